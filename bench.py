@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Benchmark of the RidgeFill hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input, resident in HBM:
+  fit : zero the statistics, accumulate every calibration chunk (rf_gram_accumulate), solve
+        the ridge maps of every filled layer (rf_solve, bf16 maps out);
+  fill: fill every prompt token of every filled layer with those maps (rf_fill).
+Default workload: the Llama-8B-shaped configuration (d=4096, 32 layers split at 16, GQA
+8 x 128, RoPE base 5e5, calibration N=65536 in 8192-row chunks, lambda=0.1, T=16384).
+
+Prints one JSON line.  ``value`` is filled tokens per second of fill time; the fit's rows
+per second, per-phase times, the dominant kernel's roofline and the CPU oracle baseline ride
+along.  Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+METRIC = "filled tokens/sec (all filled layers) + % bf16 MFMA peak; ridge-fit rows/sec"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, n_tokens: int, n_fit_rows: int):
+    """Time the oracle (fp64 NumPy) on a bounded sample of the same workload."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    cores = len(os.sched_getaffinity(0))
+    X = synth.hidden_states(cfg, n_tokens, "prompt").float().numpy().astype(np.float64)
+    layers = []
+    for l in cfg.filled_layers:
+        w = synth.layer_weights(cfg, l, maps="law")
+        f = lambda t: t.float().numpy().astype(np.float64)
+        layers.append((f(w.W_map).T, f(w.b_map), f(w.gamma), f(w.W_k).T, f(w.W_v).T))
+    t0 = time.perf_counter()
+    oracle.fill(X, 0, n_tokens, 0, layers, cfg.n_kv_heads, cfg.head_dim, cfg.rms_eps, cfg.rope_base)
+    t_fill = time.perf_counter() - t0
+    Xc = synth.hidden_states(cfg, n_fit_rows, "calib").float().numpy().astype(np.float64)
+    Ys = [synth.late_layer_inputs(cfg, torch.from_numpy(Xc).to(torch.bfloat16), l).float().numpy().astype(np.float64)
+          for l in cfg.filled_layers]
+    t0 = time.perf_counter()
+    oracle.gram_sums(Xc, Ys)
+    t_gram = time.perf_counter() - t0
+    return {
+        "value": n_tokens / t_fill, "unit": "filled tokens/s", "cores": min(cores, threads), "kind": "oracle",
+        "sample": f"fill of {n_tokens} prompt tokens x {len(cfg.filled_layers)} layers (d={cfg.d}), fp64 NumPy, "
+                  f"{t_fill:.1f} s; fit rows/s from the one-pass sums of {n_fit_rows} calibration rows "
+                  f"({t_gram:.1f} s)",
+        "fit_rows_per_s": n_fit_rows / t_gram,
+        "blas_threads": threads,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="C2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-fit-rows", type=int, default=1024)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the fit and fill run on a single MI355X; "
+              "run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import linear_kv_cache_amd as rf
+    import synth
+    from linear_kv_cache_amd.runner import Filler, GramState, alloc_cache, device_bytes
+
+    cfg = synth.CONFIGS[args.config]
+    if cfg.calib_rows == 0 or cfg.fill_tokens == 0:
+        raise SystemExit(f"{args.config} is a parity-test configuration, not a bench workload")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    d, L, T = cfg.d, cfg.n_targets, cfg.fill_tokens
+    n_chunks = cfg.calib_rows // cfg.calib_chunk
+    log(f"workload {cfg.name}: d={d} layers={L} N={cfg.calib_rows} T={T}; drawing inputs on the GPU")
+    Xc = [synth.hidden_states(cfg, cfg.calib_chunk, "calib", chunk=c, device=dev) for c in range(n_chunks)]
+    Yc = [[synth.late_layer_inputs(cfg, Xc[c], l, chunk=c) for l in cfg.filled_layers] for c in range(n_chunks)]
+    Xp = synth.hidden_states(cfg, T, "prompt", device=dev)
+    kv = [synth.kv_weights(cfg, l, device=dev) for l in cfg.filled_layers]
+    state = GramState(d, L, cfg.torch_dtype, dev)
+    solve_ws = device_bytes(rf.rf_solve_workspace_bytes(state.desc, L), dev)
+    W_lp = torch.empty(L, d, d, dtype=torch.bfloat16, device=dev)
+    b = torch.empty(L, d, dtype=torch.float32, device=dev)
+    info = torch.empty(1, dtype=torch.int32, device=dev)
+    cache = alloc_cache(L, cfg.n_kv_heads, cfg.head_dim, T, cfg.torch_dtype, dev)
+    fw = rf.FillWeights(d, cfg.n_kv_heads, cfg.head_dim, cfg.rms_eps, cfg.torch_dtype, [W_lp[i] for i in range(L)],
+                        [b[i] for i in range(L)], [g for (_, _, g) in kv], [k for (k, _, _) in kv],
+                        [v for (_, v, _) in kv])
+    filler = Filler(fw, cfg.rope_base, T, T, dev)
+    lam = cfg.lambdas[0]
+    torch.cuda.synchronize()
+
+    def step():
+        ev = {k: torch.cuda.Event(enable_timing=True) for k in ("start", "gram", "solve", "fill")}
+        gram_ev = []
+        ev["start"].record(stream)
+        rf.rf_gram_init(state.desc, state.buf, stream)
+        for c in range(n_chunks):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rf.rf_gram_accumulate(state.desc, state.buf, Xc[c], Yc[c], stream=stream)
+            e1.record(stream)
+            gram_ev.append((e0, e1))
+        ev["gram"].record(stream)
+        rf.rf_solve(state.desc, state.buf, lam, rf.RF_LAMBDA_ABSOLUTE, list(range(L)), None, W_lp, b, info,
+                    solve_ws, stream)
+        ev["solve"].record(stream)
+        filler.fill(Xp, 0, T, 0, cache, stream)
+        ev["fill"].record(stream)
+        return ev, gram_ev
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+    if int(info.item()) != 0:
+        raise SystemExit(f"solve reported a non-positive pivot: {int(info.item())}")
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    recs = [step() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"timed {args.steps} steps in {wall:.3f} s")
+
+    gram_ms = [r[0]["start"].elapsed_time(r[0]["gram"]) for r in recs]
+    solve_ms = [r[0]["gram"].elapsed_time(r[0]["solve"]) for r in recs]
+    fill_ms = [r[0]["solve"].elapsed_time(r[0]["fill"]) for r in recs]
+    launch_ms = [e0.elapsed_time(e1) for r in recs for (e0, e1) in r[1]]
+    fill_flop = T * L * cfg.fill_flop_per_token_layer()
+    gram_flop_per_launch = cfg.calib_chunk * cfg.fit_flop_per_row()
+    fill_s = sum(fill_ms) / 1e3
+    tok_s = T * args.steps / fill_s
+    fill_tflops = fill_flop * args.steps / fill_s / 1e12
+    gram_launch_ms = statistics.mean(launch_ms)
+    gram_tflops = gram_flop_per_launch / (gram_launch_ms / 1e3) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "filled tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "d": d, "filled_layers": L, "n_kv_heads": cfg.n_kv_heads,
+                   "head_dim": cfg.head_dim, "fill_tokens": T, "calib_rows": cfg.calib_rows,
+                   "calib_chunk": cfg.calib_chunk, "lambda": lam},
+        "fill": {"ms": round(statistics.mean(fill_ms), 3), "tokens_per_s": round(tok_s, 1),
+                 "tflops": round(fill_tflops, 1), "frac_bf16_peak": round(fill_tflops / BF16_PEAK_TFLOPS, 4),
+                 "flop_per_token_layer": cfg.fill_flop_per_token_layer()},
+        "fit": {"rows_per_s": round(cfg.calib_rows / (statistics.mean(gram_ms) / 1e3), 1),
+                "gram_ms": round(statistics.mean(gram_ms), 3), "solve_ms": round(statistics.mean(solve_ms), 3),
+                "rows_per_s_incl_solve": round(cfg.calib_rows / ((statistics.mean(gram_ms) +
+                                                                   statistics.mean(solve_ms)) / 1e3), 1),
+                "flop_per_row": cfg.fit_flop_per_row()},
+        "roofline": {"bound": "mfma", "kernel": "k_gram<bf16> (one rf_gram_accumulate of 8192 rows)",
+                     "achieved": round(gram_tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gram_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "launch_ms": round(gram_launch_ms, 4), "flop_per_launch": gram_flop_per_launch},
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle on {args.cpu_tokens} tokens and {args.cpu_fit_rows} calibration rows")
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens, args.cpu_fit_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,228 @@
+/*
+ * ridgefill.h -- C ABI of the RidgeFill ridge fit and late-layer KV-cache fill for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What it computes (RidgeFill project page, "Method" steps 1-4 and Figure 2(b); "Abstract"):
+ * the lower layers of a model run exactly up to a split layer; for every filled prompt row
+ * and every late layer, a per-layer ridge map fitted once in closed form predicts that
+ * layer's input from the split layer's state, and the layer's own K/V projections write its
+ * cache from the prediction.  The order of the layer's own cache path follows the KV-Lingo
+ * page, section 3.1 "Rotation and normalisation" (pre-norm storing: normalise, project,
+ * rotate keys by position, store).
+ *
+ * Conventions for every entry point
+ *  - Pointers named d_* are device memory of the current HIP device, owned by the caller.
+ *    Arrays of pointers (``const void* const*``) are host arrays of device pointers.
+ *    The library allocates no device memory and keeps no state between calls.
+ *  - ``stream`` is a hipStream_t (NULL = the null stream).  Every call only enqueues work on
+ *    it and returns without synchronising.
+ *  - Arguments are validated on the host before anything is enqueued.  On a failed check the
+ *    call returns RF_ERR_INVALID_ARG or RF_ERR_UNSUPPORTED, enqueues nothing, and
+ *    rf_last_error() (thread-local) describes the problem.
+ *  - RF_ERR_HIP means a launch failed; rf_last_error() holds the HIP error string.
+ *  - Row-vector notation: a token state is x in R^{1 x d}.  Matrices are row-major.
+ *  - Weight matrices are stored out-feature major ("Linear" layout): a map W stored as
+ *    [d_out][d_in] computes y = x W^T.  This puts the reduction dimension contiguous for
+ *    both operands of every GEMM.
+ *  - bf16 is IEEE bfloat16 stored as 16-bit words; conversions round to nearest even.
+ *  - Calls on one stream are ordered; calls that write the same buffers from different
+ *    streams race.
+ */
+#ifndef RIDGEFILL_H
+#define RIDGEFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RF_OK = 0,
+    RF_ERR_INVALID_ARG = 1,   /* a null pointer, bad size, bad range or bad stride        */
+    RF_ERR_UNSUPPORTED = 2,   /* a valid request this build does not implement (shape)    */
+    RF_ERR_HIP = 3,           /* a HIP runtime call or kernel launch failed               */
+    RF_ERR_WORKSPACE = 4      /* the workspace passed is smaller than the size query says */
+} rf_status;
+
+typedef enum { RF_F32 = 0, RF_BF16 = 1 } rf_dtype;
+typedef enum { RF_LAYOUT_CONTIGUOUS = 0, RF_LAYOUT_PAGED = 1 } rf_layout;
+typedef enum {
+    RF_LAMBDA_ABSOLUTE = 0,      /* lambda added to the centred Gram's diagonal as given       */
+    RF_LAMBDA_REL_MEAN_DIAG = 1  /* lambda x mean diagonal of the centred Gram (KV-Lingo,
+                                    Appendix B.2 "Protocol", relative ridge convention)      */
+} rf_lambda_mode;
+
+/* Library version string, e.g. "ridgefill 0.1.0 gfx950". */
+const char* rf_version(void);
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char* rf_last_error(void);
+
+/* ---------------------------------------------------------------------------------------
+ * Ridge fit, part 1: one streaming pass of second moments over calibration chunks.
+ *
+ * RidgeFill project page, "Method" step 2 and "Abstract": the map of each late layer is a
+ * ridge regression fitted once, in closed form, from one pass over calibration rows.  The
+ * pass carries, for the split-layer rows X and each target layer's input rows Y_l:
+ *     n        number of rows seen                       (int64)
+ *     S_xx   = X^T X                 [d][d]               (fp32; rows <= cols are defined,
+ *                                                          the strict lower triangle is not)
+ *     S_yx   = Y_l^T X for each l    [n_targets*d][d]     (fp32; row l*d+o, column i holds
+ *                                                          sum_r Y_l[r][o] X[r][i])
+ *     s_x    = 1^T X                 [d]                  (fp64)
+ *     s_y    = 1^T Y_l for each l    [n_targets*d]        (fp64)
+ * The state is one device buffer laid out as rf_gram_state_layout() reports; it is plain
+ * data, so it can be copied out and back to checkpoint and resume a calibration pass.
+ * ------------------------------------------------------------------------------------- */
+typedef struct {
+    int32_t d;          /* hidden width; a multiple of 256                          */
+    int32_t n_targets;  /* number of target layers whose inputs are regressed on X  */
+    rf_dtype dtype;     /* dtype of the X and Y rows passed to rf_gram_accumulate   */
+} rf_gram_desc;
+
+typedef struct {       /* byte offsets into the state buffer */
+    int64_t off_n, off_S_xx, off_S_yx, off_s_x, off_s_y, total_bytes;
+} rf_gram_layout_t;
+
+/* Host only.  Fills *out; returns RF_ERR_INVALID_ARG for a bad descriptor. */
+rf_status rf_gram_state_layout(const rf_gram_desc* desc, rf_gram_layout_t* out);
+
+/* Host only.  Bytes of the state buffer (0 for a bad descriptor). */
+size_t rf_gram_state_bytes(const rf_gram_desc* desc);
+
+/* Zero the state (n = 0, all sums 0).  d_state: rf_gram_state_bytes() bytes, 256-B aligned. */
+rf_status rf_gram_init(const rf_gram_desc* desc, void* d_state, void* stream);
+
+/* Add one chunk of ``rows`` calibration rows to the state.
+ *  d_X : [rows][ldx] split-layer rows, dtype desc->dtype, ldx >= d, 16-B aligned rows
+ *  d_Y : host array of n_targets device pointers, each [rows][ldy] target-layer input rows
+ *  rows: >= 0 (0 is a no-op).  Any row count is allowed; ragged tails are handled.
+ * Results are deterministic: the same chunks in the same order give bit-identical sums. */
+rf_status rf_gram_accumulate(const rf_gram_desc* desc, void* d_state,
+                             const void* d_X, int64_t ldx,
+                             const void* const* d_Y, int64_t ldy,
+                             int64_t rows, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Ridge fit, part 2: the closed-form solve.
+ *
+ * For each selected target l (intercept by mean-centring, rows as token states):
+ *     mu_x = s_x / n,  mu_l = s_y,l / n
+ *     C    = S_xx - n mu_x^T mu_x           (centred Gram, symmetric from the upper triangle)
+ *     B_l  = S_yx,l - n mu_l^T mu_x          (centred cross moments, [d_out][d_in])
+ *     W_l  = B_l (C + lambda I)^-1           (out-feature major: row o is the map of output o)
+ *     b_l  = mu_l - mu_x W_l^T
+ * so that the prediction is y = x W_l^T + b_l.  C + lambda I is factored by Cholesky in
+ * fp64; the triangular solves and the products run in fp64.
+ *
+ *  targets : host array of n_sel target indices in [0, n_targets)
+ *  d_W     : [n_sel][d][d] fp32 out, may be NULL
+ *  d_W_lp  : [n_sel][d][d] bf16 out (the map as the fill consumes it), may be NULL
+ *  d_b     : [n_sel][d] fp32 out, may be NULL
+ *  d_info  : one int32 out: 0 = success; k > 0 = C + lambda I is not positive definite and
+ *            the k-th leading minor (1-based) is the first that fails.  The outputs are then
+ *            meaningless (finite or not) but every write stays in bounds.
+ *  d_ws    : rf_solve_workspace_bytes(desc, n_sel) bytes, 256-B aligned
+ * lambda must be >= 0 and finite. */
+size_t rf_solve_workspace_bytes(const rf_gram_desc* desc, int32_t n_sel);
+rf_status rf_solve(const rf_gram_desc* desc, const void* d_state,
+                   double lambda, rf_lambda_mode mode,
+                   const int32_t* targets, int32_t n_sel,
+                   float* d_W, void* d_W_lp, float* d_b, int32_t* d_info,
+                   void* d_ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * KV cache layout (host only).
+ *
+ * Each filled layer has one K pool and one V pool of the same shape.
+ *  CONTIGUOUS: [max_tokens][n_kv_heads][head_dim]; token t lives in row t.
+ *  PAGED     : [n_blocks][n_kv_heads][block_size][head_dim] with
+ *              n_blocks = ceil(max_tokens / block_size); token t lives in physical block
+ *              block_table[t / block_size], slot t % block_size (serving systems keep KV in
+ *              pages: RIFT page, section 4.1, "Block-Level RIFT-stat").
+ * Strides are in elements.
+ * ------------------------------------------------------------------------------------- */
+typedef struct {
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t block_size;   /* PAGED only; ignored for CONTIGUOUS */
+    int64_t max_tokens;   /* tokens the pool holds */
+    rf_layout layout;
+    rf_dtype dtype;       /* element type of the pool */
+} rf_cache_desc;
+
+typedef struct {
+    int64_t n_blocks;         /* PAGED: physical blocks; CONTIGUOUS: max_tokens */
+    int64_t elem_bytes;
+    int64_t bytes_per_pool;   /* bytes of one K (or one V) pool of one layer */
+    int64_t stride_block;     /* PAGED only (0 for CONTIGUOUS) */
+    int64_t stride_head;
+    int64_t stride_token;
+} rf_cache_layout_t;
+
+rf_status rf_cache_layout(const rf_cache_desc* desc, rf_cache_layout_t* out);
+
+/* ---------------------------------------------------------------------------------------
+ * RoPE table.  KV-Lingo page, section 2: RoPE rotates keys by their token's position.
+ * Rotate-half convention: within each head the pair (i, i + head_dim/2) turns by
+ * pos * base^(-2i/head_dim).  Writes d_table[pos][i] = (cos, sin) as two fp32 for
+ * pos in [0, n_pos), i in [0, head_dim/2).  Angles and their cos/sin are evaluated in fp64
+ * and rounded once to fp32, so the table stays accurate at positions beyond 10^5.
+ * ------------------------------------------------------------------------------------- */
+rf_status rf_rope_table(double base, int32_t head_dim, int64_t n_pos, float* d_table,
+                        void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * The fill.  RidgeFill project page, "Method" steps 2-4 and Figure 2(b): for every token
+ * t in [t0, t1) and every listed late layer l,
+ *     h = x_t W_l^T + b_l                              (predicted layer input)
+ *     u = h / sqrt(mean_j h_j^2 + rms_eps) * gamma_l   (the layer's own RMSNorm)
+ *     k = u W_k,l^T,  v = u W_v,l^T                    (the layer's own K/V projections)
+ *     k <- RoPE(k, pos0 + t)                           (keys only)
+ * and k, v are stored in the layer's K and V pools at token t.  Rows outside [t0, t1) and
+ * layers not listed are never written: exact rows skip the map (project page, Fig. 2).
+ *
+ * Weights, per listed layer (host arrays of n_layers device pointers):
+ *   W_map[l] : [d][d]                dtype    out-feature major map
+ *   b_map[l] : [d]                   fp32
+ *   gamma[l] : [d]                   fp32
+ *   W_k[l]   : [n_kv_heads*head_dim][d] dtype  head-major output rows
+ *   W_v[l]   : [n_kv_heads*head_dim][d] dtype
+ * d_X : rows of the split-layer state for tokens t0..t1-1 (row i is token t0+i), [t1-t0][ldx]
+ * k_cache[l], v_cache[l] : pools laid out per *cache (dtype must equal weights->dtype)
+ * d_block_table : PAGED only, int32 [n_table_blocks]; entries outside [0, n_blocks) are
+ *                 skipped (their tokens are not written)
+ * d_rope : rf_rope_table() output with rope_len >= pos0 + t1 positions, head_dim of *cache
+ * d_ws   : rf_fill_workspace_bytes(weights, t1 - t0) bytes, 256-B aligned
+ * Supported: d % 256 == 0, head_dim in {64, 128}, (n_kv_heads*head_dim) % 256 == 0,
+ * dtype F32 or BF16 (all of X, maps, projections and pools share it).
+ * ------------------------------------------------------------------------------------- */
+typedef struct {
+    int32_t d;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    float rms_eps;
+    rf_dtype dtype;
+    const void* const* W_map;
+    const float* const* b_map;
+    const float* const* gamma;
+    const void* const* W_k;
+    const void* const* W_v;
+} rf_fill_weights;
+
+size_t rf_fill_workspace_bytes(const rf_fill_weights* weights, int64_t max_rows);
+rf_status rf_fill(const rf_fill_weights* weights, int32_t n_layers,
+                  const void* d_X, int64_t ldx,
+                  int64_t t0, int64_t t1, int64_t pos0,
+                  const rf_cache_desc* cache, void* const* k_cache, void* const* v_cache,
+                  const int32_t* d_block_table, int64_t n_table_blocks,
+                  const float* d_rope, int64_t rope_len,
+                  void* d_ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RIDGEFILL_H */

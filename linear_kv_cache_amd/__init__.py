@@ -1,0 +1,235 @@
+"""Python binding of libridgefill (RidgeFill ridge fit and late-layer KV-cache fill, gfx950).
+
+Argument marshalling only: every function forwards to the C entry point of the same name in
+``libridgefill.so`` (declared in ``include/ridgefill.h``).  Tensors are passed as device
+pointers, streams as ``hipStream_t`` handles; nothing is computed in Python.  PyTorch is used
+for device memory and streams only.
+
+The library must have been built (``python -m linear_kv_cache_amd.build``); importing this
+module without it raises ImportError.  There is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libridgefill.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libridgefill.so is not built ({LIB_PATH}); run `python -m linear_kv_cache_amd.build`")
+_lib = C.CDLL(LIB_PATH)
+
+# ---- enums (ridgefill.h) -------------------------------------------------------------------
+RF_OK, RF_ERR_INVALID_ARG, RF_ERR_UNSUPPORTED, RF_ERR_HIP, RF_ERR_WORKSPACE = range(5)
+RF_F32, RF_BF16 = 0, 1
+RF_LAYOUT_CONTIGUOUS, RF_LAYOUT_PAGED = 0, 1
+RF_LAMBDA_ABSOLUTE, RF_LAMBDA_REL_MEAN_DIAG = 0, 1
+
+_STATUS = {0: "RF_OK", 1: "RF_ERR_INVALID_ARG", 2: "RF_ERR_UNSUPPORTED", 3: "RF_ERR_HIP", 4: "RF_ERR_WORKSPACE"}
+
+
+class RidgeFillError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+# ---- structs -------------------------------------------------------------------------------
+class rf_gram_desc(C.Structure):
+    _fields_ = [("d", C.c_int32), ("n_targets", C.c_int32), ("dtype", C.c_int)]
+
+
+class rf_gram_layout_t(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in ("off_n", "off_S_xx", "off_S_yx", "off_s_x", "off_s_y", "total_bytes")]
+
+
+class rf_cache_desc(C.Structure):
+    _fields_ = [("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("block_size", C.c_int32),
+                ("max_tokens", C.c_int64), ("layout", C.c_int), ("dtype", C.c_int)]
+
+
+class rf_cache_layout_t(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in ("n_blocks", "elem_bytes", "bytes_per_pool", "stride_block",
+                                          "stride_head", "stride_token")]
+
+
+class rf_fill_weights(C.Structure):
+    _fields_ = [("d", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("rms_eps", C.c_float),
+                ("dtype", C.c_int), ("W_map", C.POINTER(C.c_void_p)), ("b_map", C.POINTER(C.c_void_p)),
+                ("gamma", C.POINTER(C.c_void_p)), ("W_k", C.POINTER(C.c_void_p)), ("W_v", C.POINTER(C.c_void_p))]
+
+
+_P = C.c_void_p
+_sig = {
+    "rf_version": (C.c_char_p, []),
+    "rf_last_error": (C.c_char_p, []),
+    "rf_gram_state_layout": (C.c_int, [C.POINTER(rf_gram_desc), C.POINTER(rf_gram_layout_t)]),
+    "rf_gram_state_bytes": (C.c_size_t, [C.POINTER(rf_gram_desc)]),
+    "rf_gram_init": (C.c_int, [C.POINTER(rf_gram_desc), _P, _P]),
+    "rf_gram_accumulate": (C.c_int, [C.POINTER(rf_gram_desc), _P, _P, C.c_int64, C.POINTER(_P), C.c_int64,
+                                     C.c_int64, _P]),
+    "rf_solve_workspace_bytes": (C.c_size_t, [C.POINTER(rf_gram_desc), C.c_int32]),
+    "rf_solve": (C.c_int, [C.POINTER(rf_gram_desc), _P, C.c_double, C.c_int, C.POINTER(C.c_int32), C.c_int32,
+                           _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "rf_cache_layout": (C.c_int, [C.POINTER(rf_cache_desc), C.POINTER(rf_cache_layout_t)]),
+    "rf_rope_table": (C.c_int, [C.c_double, C.c_int32, C.c_int64, _P, _P]),
+    "rf_fill_workspace_bytes": (C.c_size_t, [C.POINTER(rf_fill_weights), C.c_int64]),
+    "rf_fill": (C.c_int, [C.POINTER(rf_fill_weights), C.c_int32, _P, C.c_int64, C.c_int64, C.c_int64, C.c_int64,
+                          C.POINTER(rf_cache_desc), C.POINTER(_P), C.POINTER(_P), _P, C.c_int64, _P, C.c_int64,
+                          _P, C.c_size_t, _P]),
+}
+for _name, (_res, _args) in _sig.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTED = tuple(_sig)
+
+
+def _check(status: int):
+    if status != RF_OK:
+        raise RidgeFillError(status, _lib.rf_last_error().decode())
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s) -> Optional[int]:
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _ptr_array(xs) -> C.Array:
+    arr = (_P * max(1, len(xs)))()
+    for i, x in enumerate(xs):
+        arr[i] = _ptr(x)
+    return arr
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t == torch.float32 or t == RF_F32:
+        return RF_F32
+    if t == torch.bfloat16 or t == RF_BF16:
+        return RF_BF16
+    raise ValueError(f"unsupported dtype {t}")
+
+
+# ---- API ------------------------------------------------------------------------------------
+def rf_version() -> str:
+    return _lib.rf_version().decode()
+
+
+def rf_last_error() -> str:
+    return _lib.rf_last_error().decode()
+
+
+def gram_desc(d: int, n_targets: int, dtype) -> rf_gram_desc:
+    return rf_gram_desc(d, n_targets, _dtype_code(dtype))
+
+
+def rf_gram_state_layout(desc: rf_gram_desc) -> dict:
+    out = rf_gram_layout_t()
+    _check(_lib.rf_gram_state_layout(C.byref(desc), C.byref(out)))
+    return {n: getattr(out, n) for n, _ in rf_gram_layout_t._fields_}
+
+
+def rf_gram_state_bytes(desc: rf_gram_desc) -> int:
+    return int(_lib.rf_gram_state_bytes(C.byref(desc)))
+
+
+def rf_gram_init(desc: rf_gram_desc, state, stream=None):
+    _check(_lib.rf_gram_init(C.byref(desc), _ptr(state), _stream(stream)))
+
+
+def rf_gram_accumulate(desc: rf_gram_desc, state, X, Ys: Sequence, rows: Optional[int] = None, stream=None):
+    """X: [rows, >=d] tensor (row stride = ldx); Ys: n_targets tensors [rows, >=d] sharing one row stride."""
+    rows = X.shape[0] if rows is None else rows
+    ldy = Ys[0].stride(0) if len(Ys) else desc.d
+    if any(Y.stride(0) != ldy for Y in Ys):
+        raise ValueError("all Y tensors must share one row stride")
+    ys = _ptr_array(Ys)
+    _check(_lib.rf_gram_accumulate(C.byref(desc), _ptr(state), _ptr(X), X.stride(0), ys, ldy, rows,
+                                   _stream(stream)))
+
+
+def rf_solve_workspace_bytes(desc: rf_gram_desc, n_sel: int) -> int:
+    return int(_lib.rf_solve_workspace_bytes(C.byref(desc), n_sel))
+
+
+def rf_solve(desc: rf_gram_desc, state, lam: float, mode: int, targets: Sequence[int], W, W_lp, b, info, ws,
+             stream=None):
+    tg = (C.c_int32 * max(1, len(targets)))(*targets)
+    ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.rf_solve(C.byref(desc), _ptr(state), float(lam), int(mode), tg, len(targets), _ptr(W), _ptr(W_lp),
+                         _ptr(b), _ptr(info), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def cache_desc(n_kv_heads: int, head_dim: int, max_tokens: int, layout: int, dtype, block_size: int = 16):
+    return rf_cache_desc(n_kv_heads, head_dim, block_size, max_tokens, layout, _dtype_code(dtype))
+
+
+def rf_cache_layout(desc: rf_cache_desc) -> dict:
+    out = rf_cache_layout_t()
+    _check(_lib.rf_cache_layout(C.byref(desc), C.byref(out)))
+    return {n: getattr(out, n) for n, _ in rf_cache_layout_t._fields_}
+
+
+def rf_rope_table(base: float, head_dim: int, n_pos: int, table, stream=None):
+    _check(_lib.rf_rope_table(float(base), head_dim, n_pos, _ptr(table), _stream(stream)))
+
+
+@dataclass
+class FillWeights:
+    """Per-layer weights of the layers one rf_fill call fills (tensors on the device)."""
+
+    d: int
+    n_kv_heads: int
+    head_dim: int
+    rms_eps: float
+    dtype: object
+    W_map: list
+    b_map: list
+    gamma: list
+    W_k: list
+    W_v: list
+
+    def _c(self):
+        arrs = [_ptr_array(x) for x in (self.W_map, self.b_map, self.gamma, self.W_k, self.W_v)]
+        w = rf_fill_weights(self.d, self.n_kv_heads, self.head_dim, self.rms_eps, _dtype_code(self.dtype),
+                            *[C.cast(a, C.POINTER(_P)) for a in arrs])
+        return w, arrs
+
+
+def rf_fill_workspace_bytes(weights: FillWeights, max_rows: int) -> int:
+    w, _keep = weights._c()
+    return int(_lib.rf_fill_workspace_bytes(C.byref(w), max_rows))
+
+
+def rf_fill(weights: FillWeights, X, t0: int, t1: int, pos0: int, cache: rf_cache_desc, k_cache: Sequence,
+            v_cache: Sequence, block_table, rope, rope_len: int, ws, stream=None, n_layers: Optional[int] = None):
+    w, _keep = weights._c()
+    n_layers = len(weights.W_map) if n_layers is None else n_layers
+    kc = _ptr_array(k_cache)
+    vc = _ptr_array(v_cache)
+    n_tab = 0 if block_table is None else block_table.numel()
+    ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.rf_fill(C.byref(w), n_layers, _ptr(X), X.stride(0), t0, t1, pos0, C.byref(cache), kc, vc,
+                        _ptr(block_table), n_tab, _ptr(rope), rope_len, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+__all__ = [n for n in dir() if n.startswith("rf_") or n.startswith("RF_")] + [
+    "RidgeFillError", "FillWeights", "gram_desc", "cache_desc", "EXPORTED", "LIB_PATH"]

@@ -1,0 +1,63 @@
+// Host-only parts of the C ABI: error reporting, version, KV-cache layout arithmetic.
+#include <stdio.h>
+
+#include <string>
+
+#include "rf_internal.h"
+
+namespace rf {
+
+static thread_local std::string g_last_error;
+
+rf_status fail(rf_status st, const std::string& msg) {
+    g_last_error = msg;
+    return st;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+rf_status check_launch(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(RF_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+    return RF_OK;
+}
+
+}  // namespace rf
+
+extern "C" {
+
+const char* rf_version(void) { return "ridgefill 0.1.0 gfx950"; }
+
+const char* rf_last_error(void) { return rf::g_last_error.c_str(); }
+
+rf_status rf_cache_layout(const rf_cache_desc* desc, rf_cache_layout_t* out) {
+    rf::clear_error();
+    RF_REQUIRE(desc && out, RF_ERR_INVALID_ARG, "rf_cache_layout: null argument");
+    RF_REQUIRE(desc->n_kv_heads > 0 && desc->head_dim > 0 && desc->max_tokens >= 0, RF_ERR_INVALID_ARG,
+               "rf_cache_layout: n_kv_heads, head_dim must be > 0 and max_tokens >= 0");
+    RF_REQUIRE(rf::valid_dtype(desc->dtype), RF_ERR_INVALID_ARG, "rf_cache_layout: bad dtype");
+    const int64_t H = desc->n_kv_heads, dh = desc->head_dim;
+    rf_cache_layout_t L{};
+    L.elem_bytes = (int64_t)rf::elem_bytes(desc->dtype);
+    if (desc->layout == RF_LAYOUT_CONTIGUOUS) {
+        L.n_blocks = desc->max_tokens;
+        L.stride_block = 0;
+        L.stride_token = H * dh;
+        L.stride_head = dh;
+        L.bytes_per_pool = desc->max_tokens * H * dh * L.elem_bytes;
+    } else if (desc->layout == RF_LAYOUT_PAGED) {
+        RF_REQUIRE(desc->block_size > 0, RF_ERR_INVALID_ARG, "rf_cache_layout: block_size must be > 0");
+        const int64_t bs = desc->block_size;
+        L.n_blocks = rf::ceil_div(desc->max_tokens, bs);
+        L.stride_block = H * bs * dh;
+        L.stride_head = bs * dh;
+        L.stride_token = dh;
+        L.bytes_per_pool = L.n_blocks * L.stride_block * L.elem_bytes;
+    } else {
+        return rf::fail(RF_ERR_INVALID_ARG, "rf_cache_layout: bad layout");
+    }
+    *out = L;
+    return RF_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,348 @@
+// Late-layer cache fill (RidgeFill project page, "Method" steps 2-4 and Figure 2(b)).
+//
+// Per group of layers, two MFMA GEMM launches:
+//   map  : h = x W_map^T + b over [tokens x d]; the epilogue adds the bias, forms per-token
+//          partial sums of h^2 over its 256 features (fixed order, no atomics), multiplies by
+//          gamma and stores u' = h * gamma in the workspace (storage dtype).
+//   kv   : [k | v] = u' [W_k | W_v]^T over [tokens x 2*H*d_h]; the epilogue finishes the
+//          RMSNorm with r = 1/sqrt(sum of the partials / d + eps) (u W^T = r * (u' W^T)),
+//          rotates K pairs (i, i + d_h/2) by their token's position (KV-Lingo page, sec. 3.1,
+//          pre-norm storing) and stores K and V rows into the layer's pools.
+// MFMA operands: A = weight rows (features), B = token rows, so each lane's accumulators
+// hold 4 consecutive features of one token and a head's RoPE pairs sit in the same lane.
+#include <math.h>
+
+#include "rf_internal.h"
+#include "rf_mfma.h"
+
+namespace rf {
+
+constexpr int kMaxGroup = 32;
+constexpr int kFT = 256;  // features per tile
+constexpr int kTT = 256;  // tokens per tile
+
+struct MapArgs {
+    const void* X;
+    int64_t ldx;
+    int64_t rows;
+    int32_t d;
+    int32_t n_ps;            // partial sums per token = d / kFT
+    void* H;                 // workspace rows [rows][d] per layer slot
+    int64_t h_slot;          // elements per layer slot
+    float* psum;             // [rows][n_ps] per layer slot
+    int64_t ps_slot;
+    const void* W[kMaxGroup];
+    const float* bias[kMaxGroup];
+    const float* gamma[kMaxGroup];
+};
+
+struct KVArgs {
+    const void* H;
+    int64_t h_slot;
+    const float* psum;
+    int64_t ps_slot;
+    int32_t n_ps;
+    int32_t d;
+    int32_t kvw;             // n_kv_heads * head_dim
+    float eps;
+    int64_t rows;
+    int64_t t0;
+    int64_t pos0;
+    const float* rope;       // [pos][head_dim/2][2]
+    int32_t paged;
+    int32_t block_size;
+    int64_t stride_block, stride_head, stride_token;
+    int64_t n_blocks;
+    const int32_t* block_table;
+    int64_t n_table_blocks;
+    const void* Wk[kMaxGroup];
+    const void* Wv[kMaxGroup];
+    void* kc[kMaxGroup];
+    void* vc[kMaxGroup];
+};
+
+template <typename T>
+__device__ inline void store4(T* p, float a, float b, float c, float e);
+template <>
+__device__ inline void store4<bf16_t>(bf16_t* p, float a, float b, float c, float e) {
+    *(u32x2*)p = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, e)};
+}
+template <>
+__device__ inline void store4<float>(float* p, float a, float b, float c, float e) {
+    *(f32x4*)p = f32x4{a, b, c, e};
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_fill_map(MapArgs a) {
+    using G = TileGemm<T, kFT, kTT, false, false>;
+    __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
+    const int g = blockIdx.z;
+    const int mt = blockIdx.x;
+    const int64_t n0 = (int64_t)blockIdx.y * kTT;
+    const Operand A{(const T*)a.W[g] + (int64_t)mt * kFT * a.d, a.d, kFT};
+    const Operand B{(const T*)a.X + n0 * a.ldx, a.ldx, a.rows - n0};
+    G gm;
+    gm.run(lds, A, B, a.d / G::BK);
+
+    const int lane = threadIdx.x & 63;
+    const int wm = (threadIdx.x >> 6) >> 1;
+    float* red = (float*)lds;  // [2][kTT]; the main loop ended on a barrier
+    const float* bias = a.bias[g] + mt * kFT;
+    const float* gamma = a.gamma[g] + mt * kFT;
+    T* H = (T*)a.H + g * a.h_slot;
+#pragma unroll
+    for (int j = 0; j < G::SN; ++j) {
+        const int nl = G::col_of(j);
+        const int64_t n = n0 + nl;
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < G::SM; ++i) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int ml = G::row_of(i, 4 * q);
+                const f32x4 bb = *(const f32x4*)(bias + ml);
+                const f32x4 gg = *(const f32x4*)(gamma + ml);
+                float h[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    h[e] = gm.acc[i][j][4 * q + e] + bb[e];
+                    ss += h[e] * h[e];
+                }
+                if (n < a.rows)
+                    store4<T>(H + n * a.d + (int64_t)mt * kFT + ml, h[0] * gg[0], h[1] * gg[1],
+                              h[2] * gg[2], h[3] * gg[3]);
+            }
+        }
+        ss += __shfl_xor(ss, 32);
+        if (lane < 32) red[wm * kTT + nl] = ss;
+    }
+    __syncthreads();
+    {
+        const int nl = threadIdx.x;
+        const int64_t n = n0 + nl;
+        if (nl < kTT && n < a.rows)
+            a.psum[g * a.ps_slot + n * a.n_ps + mt] = red[nl] + red[kTT + nl];
+    }
+}
+
+template <typename T, int DH>
+__global__ __launch_bounds__(kThreads) void k_fill_kv(KVArgs a) {
+    using G = TileGemm<T, kFT, kTT, false, false>;
+    static_assert(G::WTM % DH == 0, "a wave's feature extent must hold whole heads");
+    constexpr int HALF = DH / 2;
+    constexpr int PAIR = HALF / 32;  // sub-tile distance between RoPE partners
+    __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
+    const int g = blockIdx.z;
+    const int mt = blockIdx.x;
+    const int64_t n0 = (int64_t)blockIdx.y * kTT;
+    const bool is_k = (int64_t)mt * kFT < a.kvw;
+    const int f0 = is_k ? mt * kFT : mt * kFT - a.kvw;
+    const T* Wsel = (const T*)(is_k ? a.Wk[g] : a.Wv[g]) + (int64_t)f0 * a.d;
+    const Operand A{Wsel, a.d, kFT};
+    const Operand B{(const T*)a.H + g * a.h_slot + n0 * a.d, a.d, a.rows - n0};
+    G gm;
+    gm.run(lds, A, B, a.d / G::BK);
+
+    T* pool = (T*)(is_k ? a.kc[g] : a.vc[g]);
+    const float* ps = a.psum + g * a.ps_slot;
+    const float inv_d = 1.0f / (float)a.d;
+#pragma unroll
+    for (int j = 0; j < G::SN; ++j) {
+        const int64_t n = n0 + G::col_of(j);
+        bool ok = n < a.rows;
+        const int64_t t = a.t0 + n;
+        float r = 0.f;
+        int64_t base = 0;
+        if (ok) {
+            float s = 0.f;
+            for (int p = 0; p < a.n_ps; ++p) s += ps[n * a.n_ps + p];
+            r = 1.0f / sqrtf(s * inv_d + a.eps);
+            if (a.paged) {
+                const int64_t lb = t / a.block_size;
+                int64_t phys = lb < a.n_table_blocks ? (int64_t)a.block_table[lb] : -1;
+                ok = phys >= 0 && phys < a.n_blocks;
+                base = phys * a.stride_block + (t % a.block_size) * a.stride_token;
+            } else {
+                base = t * a.stride_token;
+            }
+        }
+        if (!ok) continue;
+        const float* cs_row = a.rope + (a.pos0 + t) * (int64_t)DH;  // HALF (cos, sin) pairs
+#pragma unroll
+        for (int i = 0; i < G::SM; ++i) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int f = f0 + G::row_of(i, 4 * q);
+                const int head = f / DH;
+                const int dim = f % DH;
+                T* dst = pool + base + head * a.stride_head + dim;
+                if (!is_k) {
+                    store4<T>(dst, gm.acc[i][j][4 * q] * r, gm.acc[i][j][4 * q + 1] * r,
+                              gm.acc[i][j][4 * q + 2] * r, gm.acc[i][j][4 * q + 3] * r);
+                } else {
+                    if ((i * 32) % DH < HALF) {
+                        // this sub-tile holds dims [dim, dim+4) < HALF; partner sub-tile i+PAIR
+                        // holds dims + HALF of the same head in the same registers
+                        const f32x4 c01 = *(const f32x4*)(cs_row + 2 * dim);
+                        const f32x4 c23 = *(const f32x4*)(cs_row + 2 * dim + 4);
+                        const float cs[4] = {c01[0], c01[2], c23[0], c23[2]};
+                        const float sn[4] = {c01[1], c01[3], c23[1], c23[3]};
+                        float lo[4], hi[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float x0 = gm.acc[i][j][4 * q + e] * r;
+                            const float x1 = gm.acc[(i + PAIR) % G::SM][j][4 * q + e] * r;
+                            lo[e] = x0 * cs[e] - x1 * sn[e];
+                            hi[e] = x1 * cs[e] + x0 * sn[e];
+                        }
+                        store4<T>(dst, lo[0], lo[1], lo[2], lo[3]);
+                        store4<T>(dst + HALF, hi[0], hi[1], hi[2], hi[3]);
+                    }
+                }
+            }
+        }
+    }
+}
+
+__global__ void k_rope_table(double base, int32_t dh, int64_t n_pos, float* out) {
+    const int64_t half = dh / 2;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= n_pos * half) return;
+    const int64_t p = idx / half;
+    const int64_t i = idx % half;
+    const double theta = pow(base, -2.0 * (double)i / (double)dh);
+    const double phi = (double)p * theta;
+    out[2 * idx] = (float)cos(phi);
+    out[2 * idx + 1] = (float)sin(phi);
+}
+
+static size_t slot_bytes(const rf_fill_weights* w, int64_t rows) {
+    const size_t hb = round_up((size_t)rows * w->d * elem_bytes(w->dtype), 256);
+    const size_t pb = round_up((size_t)rows * (w->d / kFT) * sizeof(float), 256);
+    return hb + pb;
+}
+
+template <typename T>
+static rf_status launch_fill(const rf_fill_weights* w, int32_t n_layers, const void* X, int64_t ldx,
+                             int64_t t0, int64_t t1, int64_t pos0, const rf_cache_desc* cache,
+                             const rf_cache_layout_t& L, void* const* kc, void* const* vc,
+                             const int32_t* table, int64_t n_table, const float* rope, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+    const int64_t rows = t1 - t0;
+    const size_t slot = slot_bytes(w, rows);
+    const int group = (int)std::min<size_t>({(size_t)n_layers, (size_t)kMaxGroup, ws_bytes / slot});
+    const size_t hb = round_up((size_t)rows * w->d * sizeof(T), 256);
+    char* wsc = (char*)ws;
+    const int64_t h_slot = (int64_t)(slot / sizeof(T));
+    const int64_t ps_slot = (int64_t)(slot / sizeof(float));
+    const int tok_tiles = (int)ceil_div(rows, kTT);
+    for (int l0 = 0; l0 < n_layers; l0 += group) {
+        const int gsz = std::min(group, n_layers - l0);
+        MapArgs ma{};
+        ma.X = X; ma.ldx = ldx; ma.rows = rows; ma.d = w->d; ma.n_ps = w->d / kFT;
+        ma.H = wsc; ma.h_slot = h_slot; ma.psum = (float*)(wsc + hb); ma.ps_slot = ps_slot;
+        KVArgs ka{};
+        ka.H = wsc; ka.h_slot = h_slot; ka.psum = (const float*)(wsc + hb); ka.ps_slot = ps_slot;
+        ka.n_ps = w->d / kFT; ka.d = w->d; ka.kvw = w->n_kv_heads * w->head_dim; ka.eps = w->rms_eps;
+        ka.rows = rows; ka.t0 = t0; ka.pos0 = pos0; ka.rope = rope;
+        ka.paged = cache->layout == RF_LAYOUT_PAGED; ka.block_size = cache->block_size;
+        ka.stride_block = L.stride_block; ka.stride_head = L.stride_head; ka.stride_token = L.stride_token;
+        ka.n_blocks = L.n_blocks; ka.block_table = table; ka.n_table_blocks = n_table;
+        for (int g = 0; g < gsz; ++g) {
+            ma.W[g] = w->W_map[l0 + g]; ma.bias[g] = w->b_map[l0 + g]; ma.gamma[g] = w->gamma[l0 + g];
+            ka.Wk[g] = w->W_k[l0 + g]; ka.Wv[g] = w->W_v[l0 + g];
+            ka.kc[g] = kc[l0 + g]; ka.vc[g] = vc[l0 + g];
+        }
+        hipLaunchKernelGGL(k_fill_map<T>, dim3(w->d / kFT, tok_tiles, gsz), dim3(kThreads), 0, stream, ma);
+        rf_status st = check_launch("rf_fill: map kernel");
+        if (st != RF_OK) return st;
+        const dim3 kv_grid(2 * ka.kvw / kFT, tok_tiles, gsz);
+        if (w->head_dim == 128)
+            hipLaunchKernelGGL((k_fill_kv<T, 128>), kv_grid, dim3(kThreads), 0, stream, ka);
+        else
+            hipLaunchKernelGGL((k_fill_kv<T, 64>), kv_grid, dim3(kThreads), 0, stream, ka);
+        st = check_launch("rf_fill: kv kernel");
+        if (st != RF_OK) return st;
+    }
+    return RF_OK;
+}
+
+}  // namespace rf
+
+using namespace rf;
+
+extern "C" {
+
+rf_status rf_rope_table(double base, int32_t head_dim, int64_t n_pos, float* d_table, void* stream) {
+    clear_error();
+    RF_REQUIRE(d_table, RF_ERR_INVALID_ARG, "rf_rope_table: null table");
+    RF_REQUIRE(head_dim > 0 && head_dim % 2 == 0, RF_ERR_INVALID_ARG, "rf_rope_table: head_dim must be even and > 0");
+    RF_REQUIRE(n_pos >= 0, RF_ERR_INVALID_ARG, "rf_rope_table: n_pos must be >= 0");
+    RF_REQUIRE(base > 0 && isfinite(base), RF_ERR_INVALID_ARG, "rf_rope_table: base must be finite and > 0");
+    const int64_t n = n_pos * (head_dim / 2);
+    if (n == 0) return RF_OK;
+    hipLaunchKernelGGL(k_rope_table, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, (hipStream_t)stream,
+                       base, head_dim, n_pos, d_table);
+    return check_launch("rf_rope_table");
+}
+
+size_t rf_fill_workspace_bytes(const rf_fill_weights* w, int64_t max_rows) {
+    if (!w || w->d <= 0 || w->d % kFT != 0 || max_rows < 0 || !valid_dtype(w->dtype)) return 0;
+    return slot_bytes(w, max_rows);
+}
+
+rf_status rf_fill(const rf_fill_weights* w, int32_t n_layers, const void* d_X, int64_t ldx,
+                  int64_t t0, int64_t t1, int64_t pos0, const rf_cache_desc* cache,
+                  void* const* k_cache, void* const* v_cache, const int32_t* d_block_table,
+                  int64_t n_table_blocks, const float* d_rope, int64_t rope_len, void* d_ws,
+                  size_t ws_bytes, void* stream) {
+    clear_error();
+    RF_REQUIRE(w && cache, RF_ERR_INVALID_ARG, "rf_fill: null weights or cache descriptor");
+    RF_REQUIRE(n_layers >= 0, RF_ERR_INVALID_ARG, "rf_fill: n_layers must be >= 0");
+    RF_REQUIRE(t0 >= 0 && t1 >= t0 && pos0 >= 0, RF_ERR_INVALID_ARG, "rf_fill: need 0 <= t0 <= t1 and pos0 >= 0");
+    RF_REQUIRE(valid_dtype(w->dtype), RF_ERR_INVALID_ARG, "rf_fill: bad dtype");
+    RF_REQUIRE(cache->dtype == w->dtype, RF_ERR_UNSUPPORTED, "rf_fill: cache dtype must equal the weights' dtype");
+    RF_REQUIRE(w->d > 0 && w->d % kFT == 0, RF_ERR_UNSUPPORTED, "rf_fill: d must be a positive multiple of 256");
+    RF_REQUIRE(w->head_dim == 64 || w->head_dim == 128, RF_ERR_UNSUPPORTED, "rf_fill: head_dim must be 64 or 128");
+    RF_REQUIRE(w->n_kv_heads > 0 && (w->n_kv_heads * w->head_dim) % kFT == 0, RF_ERR_UNSUPPORTED,
+               "rf_fill: n_kv_heads*head_dim must be a positive multiple of 256");
+    RF_REQUIRE(cache->n_kv_heads == w->n_kv_heads && cache->head_dim == w->head_dim, RF_ERR_INVALID_ARG,
+               "rf_fill: cache heads/head_dim differ from the weights'");
+    RF_REQUIRE(w->rms_eps >= 0.f && isfinite(w->rms_eps), RF_ERR_INVALID_ARG, "rf_fill: rms_eps must be finite and >= 0");
+    rf_cache_layout_t L;
+    rf_status st = rf_cache_layout(cache, &L);
+    if (st != RF_OK) return st;
+    if (n_layers == 0 || t1 == t0) return RF_OK;
+    RF_REQUIRE(d_X && w->W_map && w->b_map && w->gamma && w->W_k && w->W_v && k_cache && v_cache && d_rope && d_ws,
+               RF_ERR_INVALID_ARG, "rf_fill: null pointer argument");
+    const size_t eb = elem_bytes(w->dtype);
+    RF_REQUIRE(ldx >= w->d && (ldx * (int64_t)eb) % 16 == 0 && aligned(d_X, 16), RF_ERR_INVALID_ARG,
+               "rf_fill: X rows must be >= d long, 16-byte aligned with a 16-byte multiple stride");
+    for (int l = 0; l < n_layers; ++l) {
+        RF_REQUIRE(w->W_map[l] && w->b_map[l] && w->gamma[l] && w->W_k[l] && w->W_v[l] && k_cache[l] && v_cache[l],
+                   RF_ERR_INVALID_ARG, "rf_fill: null per-layer pointer");
+        RF_REQUIRE(aligned(w->W_map[l], 16) && aligned(w->W_k[l], 16) && aligned(w->W_v[l], 16) &&
+                       aligned(w->b_map[l], 16) && aligned(w->gamma[l], 16) && aligned(k_cache[l], 16) &&
+                       aligned(v_cache[l], 16),
+                   RF_ERR_INVALID_ARG, "rf_fill: per-layer buffers must be 16-byte aligned");
+    }
+    RF_REQUIRE(aligned(d_rope, 16) && aligned(d_ws, 256), RF_ERR_INVALID_ARG,
+               "rf_fill: rope table must be 16-byte and workspace 256-byte aligned");
+    RF_REQUIRE(pos0 + t1 <= rope_len, RF_ERR_INVALID_ARG, "rf_fill: rope table shorter than pos0 + t1");
+    if (cache->layout == RF_LAYOUT_PAGED) {
+        RF_REQUIRE(d_block_table, RF_ERR_INVALID_ARG, "rf_fill: paged cache needs a block table");
+        RF_REQUIRE(ceil_div(t1, cache->block_size) <= n_table_blocks, RF_ERR_INVALID_ARG,
+                   "rf_fill: block table shorter than ceil(t1 / block_size)");
+    } else {
+        RF_REQUIRE(t1 <= cache->max_tokens, RF_ERR_INVALID_ARG, "rf_fill: t1 exceeds the cache's max_tokens");
+    }
+    RF_REQUIRE(ws_bytes >= slot_bytes(w, t1 - t0), RF_ERR_WORKSPACE, "rf_fill: workspace too small");
+    hipStream_t s = (hipStream_t)stream;
+    if (w->dtype == RF_BF16)
+        return launch_fill<bf16_t>(w, n_layers, d_X, ldx, t0, t1, pos0, cache, L, k_cache, v_cache, d_block_table,
+                                   n_table_blocks, d_rope, d_ws, ws_bytes, s);
+    return launch_fill<float>(w, n_layers, d_X, ldx, t0, t1, pos0, cache, L, k_cache, v_cache, d_block_table,
+                              n_table_blocks, d_rope, d_ws, ws_bytes, s);
+}
+
+}  // extern "C"

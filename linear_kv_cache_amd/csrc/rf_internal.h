@@ -1,0 +1,32 @@
+// Host-side helpers shared by the library's translation units (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "ridgefill.h"
+
+namespace rf {
+
+// Records the message for rf_last_error() on this thread and returns ``st``.
+rf_status fail(rf_status st, const std::string& msg);
+void clear_error();
+
+// Checks the last launch (hipGetLastError) and converts a failure into RF_ERR_HIP.
+rf_status check_launch(const char* what);
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
+
+inline size_t elem_bytes(rf_dtype t) { return t == RF_F32 ? 4 : 2; }
+inline bool valid_dtype(rf_dtype t) { return t == RF_F32 || t == RF_BF16; }
+
+}  // namespace rf
+
+#define RF_REQUIRE(cond, status, msg)                  \
+    do {                                               \
+        if (!(cond)) return ::rf::fail((status), (msg)); \
+    } while (0)

@@ -1,0 +1,118 @@
+"""Device-memory plumbing around the C entry points: allocate states, workspaces, caches and
+RoPE tables with torch, then call the library.  No arithmetic of the method happens here."""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import (RF_LAYOUT_CONTIGUOUS, RF_LAYOUT_PAGED, FillWeights, cache_desc, gram_desc, rf_cache_layout,
+               rf_fill, rf_fill_workspace_bytes, rf_gram_accumulate, rf_gram_init, rf_gram_state_bytes,
+               rf_gram_state_layout, rf_rope_table, rf_solve, rf_solve_workspace_bytes)
+
+
+def device_bytes(n: int, device) -> torch.Tensor:
+    """A 256-byte aligned uint8 buffer (torch's caching allocator aligns to >= 512 B)."""
+    t = torch.empty(max(int(n), 256), dtype=torch.uint8, device=device)
+    assert t.data_ptr() % 256 == 0
+    return t
+
+
+class GramState:
+    """The one-pass second-moment state of a calibration run (device buffer + layout)."""
+
+    def __init__(self, d: int, n_targets: int, dtype, device, stream=None):
+        self.desc = gram_desc(d, n_targets, dtype)
+        self.layout = rf_gram_state_layout(self.desc)
+        self.buf = device_bytes(rf_gram_state_bytes(self.desc), device)
+        self.d, self.n_targets = d, n_targets
+        rf_gram_init(self.desc, self.buf, stream)
+
+    def accumulate(self, X, Ys, stream=None):
+        rf_gram_accumulate(self.desc, self.buf, X, Ys, stream=stream)
+
+    # views of the state (plain data as laid out by rf_gram_state_layout)
+    def _view(self, off, count, dtype):
+        nbytes = count * torch.tensor([], dtype=dtype).element_size()
+        return self.buf[off:off + nbytes].view(dtype)
+
+    def n(self):
+        return self._view(self.layout["off_n"], 1, torch.int64)
+
+    def S_xx(self):
+        return self._view(self.layout["off_S_xx"], self.d * self.d, torch.float32).view(self.d, self.d)
+
+    def S_yx(self):
+        return self._view(self.layout["off_S_yx"], self.n_targets * self.d * self.d,
+                          torch.float32).view(self.n_targets, self.d, self.d)
+
+    def s_x(self):
+        return self._view(self.layout["off_s_x"], self.d, torch.float64)
+
+    def s_y(self):
+        return self._view(self.layout["off_s_y"], self.n_targets * self.d, torch.float64).view(self.n_targets, self.d)
+
+    def solve(self, lam: float, mode: int, targets: Sequence[int], want_f32=True, want_bf16=True, stream=None,
+              ws: Optional[torch.Tensor] = None):
+        dev = self.buf.device
+        n_sel = len(targets)
+        W = torch.empty(n_sel, self.d, self.d, dtype=torch.float32, device=dev) if want_f32 else None
+        Wlp = torch.empty(n_sel, self.d, self.d, dtype=torch.bfloat16, device=dev) if want_bf16 else None
+        b = torch.empty(n_sel, self.d, dtype=torch.float32, device=dev)
+        info = torch.empty(1, dtype=torch.int32, device=dev)
+        if ws is None:
+            ws = device_bytes(rf_solve_workspace_bytes(self.desc, n_sel), dev)
+        rf_solve(self.desc, self.buf, lam, mode, list(targets), W, Wlp, b, info, ws, stream)
+        return W, Wlp, b, info
+
+
+@dataclass
+class Cache:
+    desc: object
+    layout: dict
+    k: List[torch.Tensor]
+    v: List[torch.Tensor]
+    block_table: Optional[torch.Tensor]
+
+
+def alloc_cache(n_layers: int, n_kv_heads: int, head_dim: int, max_tokens: int, dtype, device,
+                paged: bool = False, block_size: int = 16, block_table: Optional[torch.Tensor] = None,
+                sentinel: float = float("nan"), n_blocks: Optional[int] = None) -> Cache:
+    desc = cache_desc(n_kv_heads, head_dim, max_tokens, RF_LAYOUT_PAGED if paged else RF_LAYOUT_CONTIGUOUS,
+                      dtype, block_size)
+    if paged and n_blocks is not None:
+        desc.max_tokens = n_blocks * block_size
+    lay = rf_cache_layout(desc)
+    n_el = lay["bytes_per_pool"] // lay["elem_bytes"]
+    k = [torch.full((n_el,), sentinel, dtype=dtype, device=device) for _ in range(n_layers)]
+    v = [torch.full((n_el,), sentinel, dtype=dtype, device=device) for _ in range(n_layers)]
+    return Cache(desc, lay, k, v, block_table)
+
+
+def gather_rows(cache: Cache, pool: torch.Tensor, t0: int, t1: int) -> torch.Tensor:
+    """Rows [t0, t1) of one pool as [t1 - t0, H, d_h] (index arithmetic only)."""
+    H, dh = cache.desc.n_kv_heads, cache.desc.head_dim
+    if cache.desc.layout == RF_LAYOUT_CONTIGUOUS:
+        return pool.view(-1, H, dh)[t0:t1]
+    bs = cache.desc.block_size
+    t = torch.arange(t0, t1, device=pool.device)
+    phys = cache.block_table.long()[t // bs]
+    blocks = pool.view(-1, H, bs, dh)
+    return blocks[phys, :, t % bs, :]
+
+
+class Filler:
+    """Holds the per-layer weights, a RoPE table and a workspace; fills token ranges."""
+
+    def __init__(self, weights: FillWeights, rope_base: float, max_pos: int, max_rows: int, device,
+                 ws_slots: int = 1, stream=None):
+        self.w = weights
+        self.rope_len = max_pos
+        self.rope = torch.empty(max_pos, weights.head_dim, dtype=torch.float32, device=device)
+        rf_rope_table(rope_base, weights.head_dim, max_pos, self.rope, stream)
+        self.ws = device_bytes(rf_fill_workspace_bytes(weights, max_rows) * max(1, ws_slots), device)
+
+    def fill(self, X, t0: int, t1: int, pos0: int, cache: Cache, stream=None):
+        rf_fill(self.w, X, t0, t1, pos0, cache.desc, cache.k, cache.v, cache.block_table, self.rope,
+                self.rope_len, self.ws, stream)

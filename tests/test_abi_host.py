@@ -1,0 +1,140 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared symbol, and its
+host-only arithmetic and argument validation behave as the header says.  No kernel is
+launched here (every call below returns before any enqueue)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+import torch
+
+import linear_kv_cache_amd as rf
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ridgefill.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rf_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 12
+    lib = C.CDLL(rf.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(rf.EXPORTED)
+    assert rf.rf_version().startswith("ridgefill")
+
+
+def test_cache_layout_contiguous_and_paged():
+    d = rf.cache_desc(8, 128, 1000, rf.RF_LAYOUT_CONTIGUOUS, torch.bfloat16)
+    L = rf.rf_cache_layout(d)
+    assert L == dict(n_blocks=1000, elem_bytes=2, bytes_per_pool=1000 * 8 * 128 * 2, stride_block=0,
+                     stride_head=128, stride_token=1024)
+    p = rf.cache_desc(8, 128, 1000, rf.RF_LAYOUT_PAGED, torch.bfloat16, block_size=16)
+    L = rf.rf_cache_layout(p)
+    assert L["n_blocks"] == 63 and L["stride_block"] == 8 * 16 * 128
+    assert L["stride_head"] == 16 * 128 and L["stride_token"] == 128
+    assert L["bytes_per_pool"] == 63 * 8 * 16 * 128 * 2
+    f = rf.cache_desc(4, 64, 512, rf.RF_LAYOUT_CONTIGUOUS, torch.float32)
+    assert rf.rf_cache_layout(f)["elem_bytes"] == 4
+
+
+def test_cache_layout_rejects_bad_descriptors():
+    with pytest.raises(rf.RidgeFillError) as e:
+        rf.rf_cache_layout(rf.cache_desc(0, 128, 10, rf.RF_LAYOUT_CONTIGUOUS, torch.bfloat16))
+    assert e.value.status == rf.RF_ERR_INVALID_ARG
+    with pytest.raises(rf.RidgeFillError):
+        rf.rf_cache_layout(rf.cache_desc(8, 128, 10, rf.RF_LAYOUT_PAGED, torch.bfloat16, block_size=0))
+
+
+def test_gram_state_layout():
+    desc = rf.gram_desc(4096, 16, torch.bfloat16)
+    L = rf.rf_gram_state_layout(desc)
+    assert L["off_n"] == 0 and L["off_S_xx"] == 256
+    assert L["off_S_yx"] == 256 + 4096 * 4096 * 4
+    assert L["off_s_x"] == L["off_S_yx"] + 16 * 4096 * 4096 * 4
+    assert L["off_s_y"] == L["off_s_x"] + 4096 * 8
+    assert L["total_bytes"] == L["off_s_y"] + 16 * 4096 * 8
+    assert all(v % 256 == 0 for v in L.values())
+    assert rf.rf_gram_state_bytes(desc) == L["total_bytes"]
+    assert rf.rf_gram_state_bytes(rf.gram_desc(100, 2, torch.float32)) == 0
+
+
+def test_gram_validation_before_enqueue():
+    with pytest.raises(rf.RidgeFillError) as e:
+        rf.rf_gram_init(rf.gram_desc(300, 1, torch.float32), 256, None)
+    assert e.value.status == rf.RF_ERR_UNSUPPORTED
+    desc = rf.gram_desc(256, 1, torch.float32)
+    with pytest.raises(rf.RidgeFillError) as e:
+        rf.rf_gram_init(desc, 255, None)  # misaligned state pointer
+    assert e.value.status == rf.RF_ERR_INVALID_ARG
+    X = torch.empty(4, 256)
+    with pytest.raises(rf.RidgeFillError):
+        rf.rf_gram_accumulate(desc, 256, X, [], rows=-1)
+    with pytest.raises(rf.RidgeFillError) as e:
+        rf.rf_gram_accumulate(rf.gram_desc(256, 65, torch.float32), 256, X, [])
+    assert e.value.status == rf.RF_ERR_UNSUPPORTED
+    rf.rf_gram_accumulate(desc, 256, X, [X], rows=0)  # zero rows: a no-op
+
+
+def test_solve_validation_before_enqueue():
+    desc = rf.gram_desc(256, 2, torch.float32)
+    ws_bytes = rf.rf_solve_workspace_bytes(desc, 2)
+    assert ws_bytes > 2 * 256 * 256 * 8
+    ws = torch.empty(16, dtype=torch.uint8)
+    for lam, targets, status in [(-1.0, [0], rf.RF_ERR_INVALID_ARG), (float("nan"), [0], rf.RF_ERR_INVALID_ARG),
+                                 (0.1, [2], rf.RF_ERR_INVALID_ARG), (0.1, [0], rf.RF_ERR_WORKSPACE)]:
+        with pytest.raises(rf.RidgeFillError) as e:
+            rf._check(rf._lib.rf_solve(C.byref(desc), 256, lam, 0, (C.c_int32 * 1)(*targets), len(targets),
+                                       None, None, None, 512, 256, 16, None))
+        assert e.value.status == status, (lam, targets)
+
+
+def _weights(d=256, H=4, dh=64, dtype=torch.float32, n=1, ptr=256):
+    return rf.FillWeights(d, H, dh, 1e-6, dtype, [ptr] * n, [ptr] * n, [ptr] * n, [ptr] * n, [ptr] * n)
+
+
+def _aligned_bytes(n, a=256):
+    buf = torch.empty(n + a, dtype=torch.uint8)
+    off = (-buf.data_ptr()) % a
+    return buf[off:off + n]
+
+
+def test_fill_validation_before_enqueue():
+    cache = rf.cache_desc(4, 64, 512, rf.RF_LAYOUT_CONTIGUOUS, torch.float32)
+    X = torch.empty(512, 256)
+    ws = _aligned_bytes(1 << 20)
+    rope = torch.empty(512, 64)
+
+    def call(w=None, t0=0, t1=512, pos0=0, cache_=cache, rope_len=512, ws_=ws, n_layers=None):
+        w = w or _weights()
+        rf.rf_fill(w, X, t0, t1, pos0, cache_, [256], [256], None, rope, rope_len, ws_, None, n_layers=n_layers)
+
+    cases = [
+        (dict(t0=5, t1=4), rf.RF_ERR_INVALID_ARG),
+        (dict(w=_weights(d=320)), rf.RF_ERR_UNSUPPORTED),
+        (dict(w=_weights(dh=96, H=8)), rf.RF_ERR_UNSUPPORTED),
+        (dict(w=_weights(dtype=torch.bfloat16)), rf.RF_ERR_UNSUPPORTED),
+        (dict(t1=513), rf.RF_ERR_INVALID_ARG),
+        (dict(pos0=1), rf.RF_ERR_INVALID_ARG),  # rope table too short
+        (dict(ws_=_aligned_bytes(256)), rf.RF_ERR_WORKSPACE),
+        (dict(cache_=rf.cache_desc(4, 64, 512, rf.RF_LAYOUT_PAGED, torch.float32)), rf.RF_ERR_INVALID_ARG),
+    ]
+    for kw, status in cases:
+        with pytest.raises(rf.RidgeFillError) as e:
+            call(**kw)
+        assert e.value.status == status, kw
+    call(t0=7, t1=7)          # empty range: nothing to do
+    call(n_layers=0)          # no layers: nothing to do
+    assert rf.rf_fill_workspace_bytes(_weights(), 512) >= 512 * 256 * 4
+
+
+def test_rope_table_validation():
+    for args in [(0.0, 64, 10), (1e4, 63, 10), (1e4, 64, -1)]:
+        with pytest.raises(rf.RidgeFillError):
+            rf.rf_rope_table(*args, 256, None)
+    rf.rf_rope_table(1e4, 64, 0, 256, None)  # zero positions: nothing to do

@@ -1,0 +1,92 @@
+"""GPU parity of rf_gram_accumulate and rf_solve against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_cases import W_TOL, FitCase, f64, fit_errors, log, run_fit_case
+
+pytestmark = pytest.mark.gpu
+
+SMALL_BF16 = synth.scaled(synth.C2, name="fit-bf16-d512", d=512, n_layers=6, split=3)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _gram_errors(res):
+    X, Ys, st = res["X"], res["Ys"], res["state"]
+    S_xx, S_xy, s_x, s_y, n = oracle.gram_sums(f64(X), [f64(Y) for Y in Ys])
+    up = np.triu(np.ones_like(S_xx, dtype=bool))
+    g_xx = f64(st.S_xx())
+    e_xx = float(np.max(np.abs(g_xx[up] - S_xx[up])) / np.max(np.abs(S_xx)))
+    g_yx = f64(st.S_yx())
+    e_yx = max(float(np.max(np.abs(g_yx[l] - S_xy[l].T)) / np.max(np.abs(S_xy[l]))) for l in range(len(Ys)))
+    e_sx = float(np.max(np.abs(f64(st.s_x()) - s_x)) / np.max(np.abs(s_x)))
+    e_sy = max(float(np.max(np.abs(f64(st.s_y())[l] - s_y[l])) / np.max(np.abs(s_y[l]))) for l in range(len(Ys)))
+    return dict(n=int(st.n().item()), n_ref=n, e_xx=e_xx, e_yx=e_yx, e_sx=e_sx, e_sy=e_sy)
+
+
+def test_fit_tiny_fp32_one_chunk_and_ragged_chunks():
+    for chunks in ([4096], [1000, 3000, 96]):
+        case = FitCase(synth.C1, 4096, chunks, 1e-2)
+        res = run_fit_case(case)
+        g = _gram_errors(res)
+        ew, eb = fit_errors(res, case)
+        log(f"[fit] C1 chunks={chunks} gram={g} W_err={np.max(ew):.3e} b_err={np.max(eb):.3e} info={res['info']}")
+        assert res["info"] == 0
+        assert g["n"] == g["n_ref"] == 4096
+        assert max(g["e_xx"], g["e_yx"]) <= 1e-5 and max(g["e_sx"], g["e_sy"]) <= 1e-12
+        assert max(ew) <= W_TOL and max(eb) <= W_TOL
+
+
+def test_fit_bf16_ragged_rows_and_relative_lambda():
+    case = FitCase(SMALL_BF16, 5000, [1024, 1024, 1024, 1024, 904], 1e-1)
+    res = run_fit_case(case)
+    g = _gram_errors(res)
+    ew, eb = fit_errors(res, case)
+    log(f"[fit] bf16 d512 gram={g} W_err={np.max(ew):.3e} b_err={np.max(eb):.3e}")
+    assert res["info"] == 0 and g["n"] == 5000
+    assert max(g["e_xx"], g["e_yx"]) <= 1e-5 and max(g["e_sx"], g["e_sy"]) <= 1e-12
+    assert max(ew) <= W_TOL and max(eb) <= W_TOL
+    case_r = FitCase(SMALL_BF16, 5000, [5000], 1e-3, mode="rel_mean_diag")
+    res_r = run_fit_case(case_r)
+    ew, eb = fit_errors(res_r, case_r)
+    log(f"[fit] bf16 d512 relative lambda W_err={np.max(ew):.3e} b_err={np.max(eb):.3e}")
+    assert res_r["info"] == 0 and max(ew) <= W_TOL and max(eb) <= W_TOL
+
+
+def test_fit_not_spd_reports_pivot():
+    case = FitCase(synth.C1, 1024, [1024], 0.0, zero_column=77, n_targets=1)
+    res = run_fit_case(case)
+    with pytest.raises(oracle.NotSPD) as e:
+        oracle.fit(f64(res["X"]), f64(res["Ys"][0]), 0.0)
+    log(f"[fit] not SPD: gpu info={res['info']} oracle pivot={e.value.pivot}")
+    assert res["info"] == e.value.pivot == 78
+
+
+def test_gram_deterministic_and_resumable():
+    import linear_kv_cache_amd as rf
+    from linear_kv_cache_amd.runner import GramState
+    cfg = SMALL_BF16
+    X = synth.hidden_states(cfg, 3000, "calib", device="cuda")
+    Ys = [synth.late_layer_inputs(cfg, X, cfg.split + l) for l in range(2)]
+    a = GramState(cfg.d, 2, cfg.torch_dtype, "cuda")
+    b = GramState(cfg.d, 2, cfg.torch_dtype, "cuda")
+    for st in (a, b):
+        st.accumulate(X[:1200], [Y[:1200] for Y in Ys])
+        st.accumulate(X[1200:], [Y[1200:] for Y in Ys])
+    # checkpoint after the first chunk, restore into a fresh state, continue
+    c = GramState(cfg.d, 2, cfg.torch_dtype, "cuda")
+    c.accumulate(X[:1200], [Y[:1200] for Y in Ys])
+    host = c.buf.cpu()
+    d = GramState(cfg.d, 2, cfg.torch_dtype, "cuda")
+    d.buf.copy_(host.to("cuda"))
+    d.accumulate(X[1200:], [Y[1200:] for Y in Ys])
+    torch.cuda.synchronize()
+    assert torch.equal(a.buf, b.buf)
+    assert torch.equal(a.buf, d.buf)
