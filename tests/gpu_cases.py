@@ -93,7 +93,6 @@ def run_fill_case(case: FillCase, device="cuda"):
         out["finite"] &= bool(torch.isfinite(filled.float()).all()) and bool(
             torch.isfinite(Vall[case.t0:case.t1].float()).all())
         for pool in (cache.k[li], cache.v[li]):
-            written = written_mask(cache, case.t0, case.t1, T)
             vals = pool.view(-1, cfg.n_kv_heads * cfg.head_dim) if not cfg.paged else pool
             if not cfg.paged:
                 outside = torch.ones(vals.shape[0], dtype=torch.bool, device=device)
@@ -101,7 +100,7 @@ def run_fill_case(case: FillCase, device="cuda"):
                 out["sentinel_ok"] &= bool(torch.isnan(vals[outside].float()).all())
             else:
                 blk = pool.view(-1, cfg.n_kv_heads, cfg.block_size, cfg.head_dim)
-                unw = ~written
+                unw = ~written_mask(cache, case.t0, case.t1, T)
                 out["sentinel_ok"] &= bool(torch.isnan(blk.permute(0, 2, 1, 3)[unw].float()).all())
     out["tol"] = tol
     out["max_err"] = max(out["k_err"] + out["v_err"])
