@@ -5,7 +5,7 @@ Argument marshalling only: every function forwards to the C entry point of the s
 pointers, streams as ``hipStream_t`` handles; nothing is computed in Python.  PyTorch is used
 for device memory and streams only.
 
-The library must have been built (``python -m linear_kv_cache_amd.build``); importing this
+The library must have been built (``python linear_kv_cache_amd/build.py``); importing this
 module without it raises ImportError.  There is no fallback path.
 """
 from __future__ import annotations
@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libridgefill.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"libridgefill.so is not built ({LIB_PATH}); run `python -m linear_kv_cache_amd.build`")
+    raise ImportError(f"libridgefill.so is not built ({LIB_PATH}); run `python linear_kv_cache_amd/build.py`")
 _lib = C.CDLL(LIB_PATH)
 
 # ---- enums (ridgefill.h) -------------------------------------------------------------------

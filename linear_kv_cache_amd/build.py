@@ -1,6 +1,6 @@
 """Build libridgefill.so for gfx950 in-tree with hipcc.
 
-    python -m linear_kv_cache_amd.build          # compile every source, link the library
+    python linear_kv_cache_amd/build.py          # compile every source, link the library
 
 Every HIP source is compiled with packed-FP32 instruction forms disabled
 (``-target-feature -packed-fp32-ops``); the library links against the HIP runtime only.
