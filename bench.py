@@ -79,6 +79,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--cpu-fit-rows", type=int, default=1024)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one 1 GiB device-to-device copy before the steps, a known-size reference "
+                         "for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the fit and fill run on a single MI355X; "
@@ -115,6 +118,14 @@ def main():
                         [v for (_, v, _) in kv])
     filler = Filler(fw, cfg.rope_base, T, T, dev)
     lam = cfg.lambdas[0]
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy probe: 1 GiB device-to-device copy (1048576 KiB read, 1048576 KiB written)")
+        del src, dst
     torch.cuda.synchronize()
 
     def step():

@@ -14,6 +14,7 @@
 
 #include "rf_internal.h"
 #include "rf_mfma.h"
+#include "rf_pipe.h"
 
 namespace rf {
 
@@ -27,6 +28,7 @@ struct MapArgs {
     int64_t rows;
     int32_t d;
     int32_t n_ps;            // partial sums per token = d / kFT
+    int32_t tok_tiles;       // ceil(rows / kTT)
     void* H;                 // workspace rows [rows][d] per layer slot
     int64_t h_slot;          // elements per layer slot
     float* psum;             // [rows][n_ps] per layer slot
@@ -44,6 +46,7 @@ struct KVArgs {
     int32_t n_ps;
     int32_t d;
     int32_t kvw;             // n_kv_heads * head_dim
+    int32_t tok_tiles;       // ceil(rows / kTT)
     float eps;
     int64_t rows;
     int64_t t0;
@@ -72,21 +75,53 @@ __device__ inline void store4<float>(float* p, float a, float b, float c, float 
     *(f32x4*)p = f32x4{a, b, c, e};
 }
 
+// The bf16 instantiation runs the software-pipelined core; fp32 runs the plain tile loop.
+template <typename T> struct FillCore { using G = TileGemm<T, kFT, kTT, false, false>; };
+template <> struct FillCore<bf16_t> { using G = PipeGemm; };
+
+// Tile of this work-group: layer slot g, feature tile mt, token tile tt.  The grid is 1-D over
+// (layer, feature tile, token tile), renumbered so that each XCD works on a compact block of
+// 4 feature tiles x 8 token tiles at a time (shared weight and token rows in its L2).
+__device__ inline void fill_tile(int n_feat, int n_tok, int& g, int& mt, int& tt) {
+    const int per_layer = n_feat * n_tok;
+    const int v = xcd_order((int)blockIdx.x, (int)gridDim.x);
+    g = v / per_layer;
+    grouped_tile(v - g * per_layer, n_feat, n_tok, 4, mt, tt);
+}
+
+template <typename G>
+__device__ inline void fill_gemm(G& gm, char* lds, const void* A, int64_t lda, int64_t va, const void* B, int64_t ldb,
+                                 int64_t vb, int nk) {
+    gm.run(lds, Operand{A, lda, va}, Operand{B, ldb, vb}, nk);
+}
+__device__ inline void fill_gemm(PipeGemm& gm, char* lds, const void* A, int64_t lda, int64_t va, const void* B,
+                                 int64_t ldb, int64_t vb, int nk) {
+    gm.run(lds, PipeOperand{A, lda, va}, PipeOperand{B, ldb, vb}, nk);
+}
+
+// bf16: the tile of u' is staged in LDS as [token][feature] (512 bytes per token, 16-byte
+// chunk c of token n in slot c ^ (n & 31)) and leaves as whole 512-byte row segments of H.
+// fp32: each lane stores its 4 consecutive features directly.
+template <typename T> struct MapStage { static constexpr bool kLds = false; static constexpr int kBytes = 0; };
+template <> struct MapStage<bf16_t> { static constexpr bool kLds = true; static constexpr int kBytes = kTT * kFT * 2; };
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_fill_map(MapArgs a) {
-    using G = TileGemm<T, kFT, kTT, false, false>;
-    __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
-    const int g = blockIdx.z;
-    const int mt = blockIdx.x;
-    const int64_t n0 = (int64_t)blockIdx.y * kTT;
-    const Operand A{(const T*)a.W[g] + (int64_t)mt * kFT * a.d, a.d, kFT};
-    const Operand B{(const T*)a.X + n0 * a.ldx, a.ldx, a.rows - n0};
+    using G = typename FillCore<T>::G;
+    constexpr int kRedOff = MapStage<T>::kBytes;  // [2][kTT] fp32 partial sums after the stage
+    constexpr int kLdsBytes = G::LDS_BYTES > kRedOff + 2 * kTT * 4 ? G::LDS_BYTES : kRedOff + 2 * kTT * 4;
+    __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+    int g, mt, tt;
+    fill_tile(a.d / kFT, a.tok_tiles, g, mt, tt);
+    const int64_t n0 = (int64_t)tt * kTT;
     G gm;
-    gm.run(lds, A, B, a.d / G::BK);
+    fill_gemm(gm, lds, (const T*)a.W[g] + (int64_t)mt * kFT * a.d, a.d, kFT, (const T*)a.X + n0 * a.ldx, a.ldx,
+              a.rows - n0, a.d / G::BK);
 
+    // the main loop ended on a barrier: LDS is free
     const int lane = threadIdx.x & 63;
     const int wm = (threadIdx.x >> 6) >> 1;
-    float* red = (float*)lds;  // [2][kTT]; the main loop ended on a barrier
+    float* red = (float*)(lds + kRedOff);
     const float* bias = a.bias[g] + mt * kFT;
     const float* gamma = a.gamma[g] + mt * kFT;
     T* H = (T*)a.H + g * a.h_slot;
@@ -108,15 +143,32 @@ __global__ __launch_bounds__(kThreads) void k_fill_map(MapArgs a) {
                     h[e] = gm.acc[i][j][4 * q + e] + bb[e];
                     ss += h[e] * h[e];
                 }
-                if (n < a.rows)
-                    store4<T>(H + n * a.d + (int64_t)mt * kFT + ml, h[0] * gg[0], h[1] * gg[1],
-                              h[2] * gg[2], h[3] * gg[3]);
+                if constexpr (MapStage<T>::kLds) {
+                    const int slot = ((ml >> 3) ^ (nl & 31)) << 4;
+                    *(u32x2*)(lds + nl * (kFT * 2) + slot + (ml & 4) * 2) =
+                        u32x2{pack_bf16x2(h[0] * gg[0], h[1] * gg[1]), pack_bf16x2(h[2] * gg[2], h[3] * gg[3])};
+                } else {
+                    if (n < a.rows)
+                        store4<T>(H + n * a.d + (int64_t)mt * kFT + ml, h[0] * gg[0], h[1] * gg[1],
+                                  h[2] * gg[2], h[3] * gg[3]);
+                }
             }
         }
         ss += __shfl_xor(ss, 32);
         if (lane < 32) red[wm * kTT + nl] = ss;
     }
     __syncthreads();
+    if constexpr (MapStage<T>::kLds) {
+        // 8 tokens per pass; the 32 lanes of a half-wave write one token's 512 bytes
+        const int c = threadIdx.x & 31;
+#pragma unroll 4
+        for (int p = 0; p < kTT / 8; ++p) {
+            const int nl = p * 8 + (threadIdx.x >> 5);
+            const int64_t n = n0 + nl;
+            const u32x4 v = *(const u32x4*)(lds + nl * (kFT * 2) + ((c ^ (nl & 31)) << 4));
+            if (n < a.rows) *(u32x4*)(H + n * a.d + (int64_t)mt * kFT + c * 8) = v;
+        }
+    }
     {
         const int nl = threadIdx.x;
         const int64_t n = n0 + nl;
@@ -127,21 +179,19 @@ __global__ __launch_bounds__(kThreads) void k_fill_map(MapArgs a) {
 
 template <typename T, int DH>
 __global__ __launch_bounds__(kThreads) void k_fill_kv(KVArgs a) {
-    using G = TileGemm<T, kFT, kTT, false, false>;
+    using G = typename FillCore<T>::G;
     static_assert(G::WTM % DH == 0, "a wave's feature extent must hold whole heads");
     constexpr int HALF = DH / 2;
     constexpr int PAIR = HALF / 32;  // sub-tile distance between RoPE partners
     __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
-    const int g = blockIdx.z;
-    const int mt = blockIdx.x;
-    const int64_t n0 = (int64_t)blockIdx.y * kTT;
+    int g, mt, tt;
+    fill_tile(2 * a.kvw / kFT, a.tok_tiles, g, mt, tt);
+    const int64_t n0 = (int64_t)tt * kTT;
     const bool is_k = (int64_t)mt * kFT < a.kvw;
     const int f0 = is_k ? mt * kFT : mt * kFT - a.kvw;
     const T* Wsel = (const T*)(is_k ? a.Wk[g] : a.Wv[g]) + (int64_t)f0 * a.d;
-    const Operand A{Wsel, a.d, kFT};
-    const Operand B{(const T*)a.H + g * a.h_slot + n0 * a.d, a.d, a.rows - n0};
     G gm;
-    gm.run(lds, A, B, a.d / G::BK);
+    fill_gemm(gm, lds, Wsel, a.d, kFT, (const T*)a.H + g * a.h_slot + n0 * a.d, a.d, a.rows - n0, a.d / G::BK);
 
     T* pool = (T*)(is_k ? a.kc[g] : a.vc[g]);
     const float* ps = a.psum + g * a.ps_slot;
@@ -253,10 +303,12 @@ static rf_status launch_fill(const rf_fill_weights* w, int32_t n_layers, const v
             ka.Wk[g] = w->W_k[l0 + g]; ka.Wv[g] = w->W_v[l0 + g];
             ka.kc[g] = kc[l0 + g]; ka.vc[g] = vc[l0 + g];
         }
-        hipLaunchKernelGGL(k_fill_map<T>, dim3(w->d / kFT, tok_tiles, gsz), dim3(kThreads), 0, stream, ma);
+        ma.tok_tiles = tok_tiles;
+        ka.tok_tiles = tok_tiles;
+        hipLaunchKernelGGL(k_fill_map<T>, dim3((w->d / kFT) * tok_tiles * gsz), dim3(kThreads), 0, stream, ma);
         rf_status st = check_launch("rf_fill: map kernel");
         if (st != RF_OK) return st;
-        const dim3 kv_grid(2 * ka.kvw / kFT, tok_tiles, gsz);
+        const dim3 kv_grid((2 * ka.kvw / kFT) * tok_tiles * gsz);
         if (w->head_dim == 128)
             hipLaunchKernelGGL((k_fill_kv<T, 128>), kv_grid, dim3(kThreads), 0, stream, ka);
         else
@@ -318,6 +370,8 @@ rf_status rf_fill(const rf_fill_weights* w, int32_t n_layers, const void* d_X, i
     const size_t eb = elem_bytes(w->dtype);
     RF_REQUIRE(ldx >= w->d && (ldx * (int64_t)eb) % 16 == 0 && aligned(d_X, 16), RF_ERR_INVALID_ARG,
                "rf_fill: X rows must be >= d long, 16-byte aligned with a 16-byte multiple stride");
+    RF_REQUIRE(ldx <= (1 << 21) && w->d <= (1 << 16), RF_ERR_UNSUPPORTED,
+               "rf_fill: ldx must be <= 2^21 and d <= 65536 (32-bit tile offsets)");
     for (int l = 0; l < n_layers; ++l) {
         RF_REQUIRE(w->W_map[l] && w->b_map[l] && w->gamma[l] && w->W_k[l] && w->W_v[l] && k_cache[l] && v_cache[l],
                    RF_ERR_INVALID_ARG, "rf_fill: null per-layer pointer");

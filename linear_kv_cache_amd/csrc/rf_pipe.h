@@ -1,0 +1,251 @@
+// Software-pipelined bf16 MFMA GEMM core for gfx950, used by the fill kernels.
+//
+// One workgroup of 256 threads (4 waves, one per SIMD, in a 2 x 2 grid) computes a 256 x 256
+// tile of  acc[m][n] = sum_k A[m][k] * B[n][k]  with both operands K-contiguous ("K-major").
+// Each wave owns a 128 x 128 sub-tile: 4 x 4 blocks of v_mfma_f32_32x32x16_bf16, whose fp32
+// accumulators fill the 256 accumulation registers.
+//
+// Data movement per k-step of 64 elements (128 bytes of every operand row):
+//   HBM/L2 -> VGPR : buffer loads of 16 bytes per lane into one of two register sets, issued
+//                    two k-steps before their LDS write (three before their use).  Rows of a
+//                    ragged tail fall outside the buffer's byte range and read as zero.
+//   VGPR -> LDS    : two LDS stages of 64 KiB.  A row of 128 bytes is 8 chunks of 16 bytes;
+//                    chunk c of row r is stored in slot c ^ ((r >> 1) & 7).  gfx950's LDS has
+//                    64 banks of 4 bytes, so a 16-byte access serves 16 lanes per cycle; the
+//                    16 rows read by 16 consecutive lanes then cover all 64 banks once, and the
+//                    two rows written by 16 consecutive lanes do too: no bank conflicts and no
+//                    padding.
+//   LDS -> VGPR    : fragments are double-buffered in registers: the reads for slice kk+1 are
+//                    in flight while the 16 MFMAs of slice kk run.
+// One barrier per k-step, placed half-way through the last slice: by then every wave has
+// written the next stage and finished reading the current one, and the fragment reads of the
+// next stage overlap the remaining MFMAs.
+//
+// MFMA lane layout (v_mfma_f32_32x32x16_bf16): lane l supplies row (l % 32) of A and of B and
+// the 16-byte half (l / 32) of a 32-byte k-slice; accumulator register i of lane l holds
+// C[m = 8*(i/4) + 4*(l/32) + i%4][n = l % 32].  The k-permutation inside a slice is the same for
+// both operands, so the sum is unchanged by it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rf_mfma.h"
+
+namespace rf {
+
+struct PipeOperand {
+    const void* ptr;   // row 0 of the tile, k = 0
+    int64_t ld;        // row stride in elements
+    int64_t valid;     // rows of the tile that exist (rows >= valid read as zero)
+};
+
+// Work-group renumbering for L2 locality.  The dispatcher deals consecutive work-groups to
+// the 8 XCDs in turn, and each XCD has its own L2.  ``xcd_order`` renumbers work-group b so
+// that every XCD receives one contiguous range of the logical order; ``grouped_tile`` then
+// walks a range in column groups of ``gf`` row tiles, so the 32 work-groups an XCD runs at
+// once share a few operand tiles (gf row tiles x 32/gf column tiles).
+__device__ inline int xcd_order(int b, int n) {
+    constexpr int kXcd = 8;
+    const int q = n / kXcd, r = n % kXcd;
+    const int x = b % kXcd, i = b / kXcd;
+    return x * q + (x < r ? x : r) + i;
+}
+__device__ inline void grouped_tile(int v, int n_rows, int n_cols, int gf, int& row, int& col) {
+    const int span = gf * n_cols;
+    const int grp = v / span;
+    const int f0 = grp * gf;
+    const int gs = (n_rows - f0) < gf ? (n_rows - f0) : gf;
+    const int w = v - grp * span;
+    row = f0 + w % gs;
+    col = w / gs;
+}
+
+struct PipeGemm {
+    static constexpr int BM = 256, BN = 256, BK = 64;
+    static constexpr int ROWB = 128;                       // bytes of one row per k-step
+    static constexpr int STAGE_BYTES = (BM + BN) * ROWB;   // 64 KiB
+    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;      // 128 KiB
+    static constexpr int WTM = BM / 2, WTN = BN / 2;
+    static constexpr int SM = WTM / 32, SN = WTN / 32;
+    static constexpr int VA = BM * 8 / kThreads;           // 16-byte vectors per thread per step
+    static constexpr int VB = BN * 8 / kThreads;
+
+    f32x16 acc[SM][SN];
+
+    __device__ static inline __amdgpu_buffer_rsrc_t rsrc(const PipeOperand& op, int rows) {
+        // byte range covers the rows that exist; a row at or past ``valid`` starts beyond it
+        int64_t nrows = op.valid < rows ? op.valid : rows;
+        if (nrows < 0) nrows = 0;
+        const int64_t bytes = nrows * op.ld * 2;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(op.ptr), (short)0, (int)bytes, 0x00020000);
+    }
+
+    struct Regs {
+        u32x4 a[VA], b[VB];
+    };
+
+    // Full K loop over ``nk`` k-steps; nk must be even (the loop is unrolled by two so that
+    // the two register sets are addressed statically).
+    __device__ inline void run(char* lds, const PipeOperand& A, const PipeOperand& B, int nk) {
+        const int t = threadIdx.x;
+        const int lane = t & 63;
+        const int wave = t >> 6;
+        const int wm = wave >> 1, wn = wave & 1;
+
+#pragma unroll
+        for (int i = 0; i < SM; ++i)
+#pragma unroll
+            for (int j = 0; j < SN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+        if (nk <= 0) return;
+
+        const __amdgpu_buffer_rsrc_t ra = rsrc(A, BM);
+        const __amdgpu_buffer_rsrc_t rb = rsrc(B, BN);
+        // global: row (t >> 3) + 32 j, logical chunk t & 7
+        const int gA = (int)((t >> 3) * A.ld * 2) + (t & 7) * 16;
+        const int gB = (int)((t >> 3) * B.ld * 2) + (t & 7) * 16;
+        const int strideA = (int)(32 * A.ld * 2);
+        const int strideB = (int)(32 * B.ld * 2);
+        // LDS write slot: row (t >> 3) + 32 j has (row >> 1) & 7 == (t >> 4) & 7
+        const int wofs = (t >> 3) * ROWB + (((t & 7) ^ ((t >> 4) & 7)) << 4);
+        // LDS fragment reads: row (lane & 31) of a 32-row block, chunk 2 kk + (lane >> 5)
+        const int rA = (wm * WTM + (lane & 31)) * ROWB;
+        const int rB = (BM + wn * WTN + (lane & 31)) * ROWB;
+        int cofs[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) cofs[kk] = ((2 * kk + (lane >> 5)) ^ ((lane >> 1) & 7)) << 4;
+
+        auto gload_a = [&](Regs& g, int kt) {
+            const int kb = (kt < nk ? kt : nk - 1) * ROWB;
+#pragma unroll
+            for (int j = 0; j < VA; ++j) g.a[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, gA + j * strideA, kb, 0);
+        };
+        auto gload_b = [&](Regs& g, int kt) {
+            const int kb = (kt < nk ? kt : nk - 1) * ROWB;
+#pragma unroll
+            for (int j = 0; j < VB; ++j) g.b[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, gB + j * strideB, kb, 0);
+        };
+        auto swrite_a = [&](const Regs& g, char* st) {
+#pragma unroll
+            for (int j = 0; j < VA; ++j) *(u32x4*)(st + wofs + j * 32 * ROWB) = g.a[j];
+        };
+        auto swrite_b = [&](const Regs& g, char* st) {
+#pragma unroll
+            for (int j = 0; j < VB; ++j) *(u32x4*)(st + BM * ROWB + wofs + j * 32 * ROWB) = g.b[j];
+        };
+        u32x4 fa[2][SM], fb[2][SN];
+        auto fread = [&](int buf, const char* st, int kk) {
+#pragma unroll
+            for (int i = 0; i < SM; ++i) fa[buf][i] = *(const u32x4*)(st + rA + i * 32 * ROWB + cofs[kk]);
+#pragma unroll
+            for (int j = 0; j < SN; ++j) fb[buf][j] = *(const u32x4*)(st + rB + j * 32 * ROWB + cofs[kk]);
+        };
+        auto mfma = [&](int buf, int i0, int i1) {
+#pragma unroll
+            for (int i = i0; i < i1; ++i)
+#pragma unroll
+                for (int j = 0; j < SN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[buf][i]),
+                                                                       __builtin_bit_cast(bf16x8, fb[buf][j]),
+                                                                       acc[i][j], 0, 0, 0);
+        };
+
+        // One k-step.  ``g`` holds step kt+1 (written to the other LDS stage here) and is then
+        // refilled with step kt+3.  Each slice is its own scheduling region (sched_barrier); the
+        // group barriers interleave its MFMAs with its memory instructions (mask 0x008 MFMA,
+        // 0x100 LDS read, 0x200 LDS write, 0x020 VMEM read).
+        auto step = [&](int kt, Regs& g) {
+            char* cur = lds + (kt & 1) * STAGE_BYTES;
+            char* nxt = lds + ((kt + 1) & 1) * STAGE_BYTES;
+            // slice 0: next slice's fragments, A half of the next stage, its refill
+            fread(1, cur, 1);
+            swrite_a(g, nxt);
+            gload_a(g, kt + 3);
+            mfma(0, 0, SM);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // slice 1: fragments, B half of the next stage, its refill
+            fread(0, cur, 2);
+            swrite_b(g, nxt);
+            gload_b(g, kt + 3);
+            mfma(1, 0, SM);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // slice 2
+            fread(1, cur, 3);
+            mfma(0, 0, SM);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            // slice 3: half, barrier, first fragments of the next stage, other half
+            mfma(1, 0, SM / 2);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            fread(0, nxt, 0);
+            mfma(1, SM / 2, SM);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+
+        // prologue: step 0 in LDS stage 0, steps 1 and 2 in flight to the register sets
+        // (fences keep the loads in step order, which the in-order load counter relies on)
+        Regs g0, g1;
+        gload_a(g0, 0);
+        gload_b(g0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        gload_a(g1, 1);
+        gload_b(g1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        swrite_a(g0, lds);
+        swrite_b(g0, lds);
+        __builtin_amdgcn_sched_barrier(0);
+        gload_a(g0, 2);
+        __builtin_amdgcn_sched_barrier(0);
+        gload_b(g0, 2);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        fread(0, lds, 0);
+
+        for (int kt = 0; kt < nk; kt += 2) {
+            step(kt, g1);       // writes step kt+1 (odd), refills with kt+3
+            step(kt + 1, g0);   // writes step kt+2 (even), refills with kt+4
+        }
+        // the last fragment reads and stage writes target LDS the caller may reuse
+        __syncthreads();
+    }
+
+    __device__ static inline int row_of(int i, int r) {
+        const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 1;
+        return wm * WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    }
+    __device__ static inline int col_of(int j) {
+        const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
+        return wn * WTN + j * 32 + (lane & 31);
+    }
+};
+
+}  // namespace rf
