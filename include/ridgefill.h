@@ -114,12 +114,15 @@ rf_status rf_gram_accumulate(const rf_gram_desc* desc, void* d_state,
  *     B_l  = S_yx,l - n mu_l^T mu_x          (centred cross moments, [d_out][d_in])
  *     W_l  = B_l (C + lambda I)^-1           (out-feature major: row o is the map of output o)
  *     b_l  = mu_l - mu_x W_l^T
- * so that the prediction is y = x W_l^T + b_l.  C + lambda I is factored by Cholesky in
- * fp64; the triangular solves and the products run in fp64.
+ * so that the prediction is y = x W_l^T + b_l.  C + lambda I is factored by Cholesky and
+ * inverted by triangular solves in fp64.  The product B_l (C + lambda I)^-1 runs on the bf16
+ * matrix cores in three-term split precision (each factor, equilibrated by the square root of
+ * the diagonal of C + lambda I, is split into two bf16 parts) with fp32 accumulation: about
+ * 1e-5 of max |W_l| from the fp64 product on well-scaled data.
  *
  *  targets : host array of n_sel target indices in [0, n_targets)
- *  d_W     : [n_sel][d][d] fp32 out, may be NULL
- *  d_W_lp  : [n_sel][d][d] bf16 out (the map as the fill consumes it), may be NULL
+ *  d_W     : [n_sel][d][d] fp32 out, may be NULL; 16-B aligned
+ *  d_W_lp  : [n_sel][d][d] bf16 out (the map as the fill consumes it), may be NULL; 16-B aligned
  *  d_b     : [n_sel][d] fp32 out, may be NULL
  *  d_info  : one int32 out: 0 = success; k > 0 = C + lambda I is not positive definite and
  *            the k-th leading minor (1-based) is the first that fails.  The outputs are then

@@ -1,17 +1,24 @@
 // Closed-form ridge solve from the one-pass statistics (RidgeFill project page, "Method"
 // step 2: a ridge regression fitted once in closed form; intercept by mean-centring).
 //
-//   C  = S_xx - s_x^T s_x / n  (+ lambda I)        fp64, symmetric from the upper triangle
-//   B  = S_yx,l - s_y,l^T s_x / n                  fp64, one row per (target, output)
-//   C = L L^T                                      blocked right-looking Cholesky, 64-wide panels
-//   C^-1 = L^-T L^-1                               blocked triangular solves on the identity
-//   W  = B C^-1,  b = s_y/n - W (s_x/n)            one GEMM, then a row-wise dot
-// Diagonal 64 x 64 blocks are factored and inverted inside one workgroup each; everything
-// else is a tiled fp64 GEMM.  All reductions run in a fixed order.
+//   A  = S_xx - s_x^T s_x / n + lambda I           fp64, symmetric from the upper triangle
+//   A = L L^T                                      blocked right-looking Cholesky, 64-wide panels
+//   A^-1 = L^-T L^-1                               blocked triangular solves on the identity
+//   B  = S_yx,l - s_y,l^T s_x / n                  fp64 per element, one row per (target, output)
+//   W  = B A^-1,  b = s_y/n - W (s_x/n)
+// The large product W = B A^-1 ([n_sel d] x d x d) runs on the bf16 MFMA pipes in three-term
+// split precision: with D = diag(A), W = (B D^-1/2)(D^1/2 A^-1 D^1/2) D^-1/2, and each
+// equilibrated factor F is split into bf16 parts F = F_hi + F_lo, so that
+//   W D^1/2 = B_hi Ah + B_hi Al + B_lo Ah        (the F_lo x F_lo term is below fp32 rounding)
+// accumulated in fp32.  The equilibrated inverse has unit-scale entries and a condition
+// number near that of the data's correlation matrix, so the result matches the fp64 product
+// to ~1e-5 of max |W|.  Diagonal 64 x 64 blocks are factored and inverted by one wave each;
+// the blocked updates are tiled fp64 GEMMs.  All reductions run in a fixed order.
 #include <math.h>
 
 #include "rf_internal.h"
 #include "rf_mfma.h"
+#include "rf_pipe.h"
 
 namespace rf {
 
@@ -122,19 +129,30 @@ __global__ __launch_bounds__(256) void k_add_lambda(double* C, int64_t d, double
     for (int64_t i = threadIdx.x; i < d; i += 256) C[i * d + i] += lam;
 }
 
+// v = hi + lo with hi = bf16(v) and lo = bf16(v - hi) (each rounded to nearest even; the
+// double rounding through fp32 is exact for hi's bf16 grid and below lo's precision).
+__device__ inline void split_bf16(double v, bf16_t& hi, bf16_t& lo) {
+    const __bf16 h = (__bf16)(float)v;
+    hi = __builtin_bit_cast(uint16_t, h);
+    lo = __builtin_bit_cast(uint16_t, (__bf16)(float)(v - (double)(float)h));
+}
+
 struct CrossArgs {
     const float* Syx;
     const double* sy;
     const double* sx;
     const int64_t* np;
+    const double* dg;
     int64_t d;
     int64_t rows;          // n_sel * d
-    double* R;             // [rows][d]
+    bf16_t* Aq;            // [rows][3d]: [hi | hi | lo] of the equilibrated centred cross moments
     double* mu_y;          // [rows]
     int32_t tsel[kMaxSel];
 };
 
-__global__ void k_centre_cross(CrossArgs a) {
+// Centred cross moments B[c][i] = S_yx[c][i] - s_y[c] s_x[i] / n (fp64), scaled by 1/dg[i]
+// and split into bf16 parts.
+__global__ void k_centre_split(CrossArgs a) {
     const double inv_n = 1.0 / (double)*a.np;
     const int64_t n = a.rows * a.d;
     for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
@@ -142,86 +160,166 @@ __global__ void k_centre_cross(CrossArgs a) {
         const int64_t s = c / a.d, o = c % a.d;
         const int64_t srow = (int64_t)a.tsel[s] * a.d + o;
         const double syv = a.sy[srow];
-        a.R[idx] = (double)a.Syx[srow * a.d + i] - syv * a.sx[i] * inv_n;
+        const double v = ((double)a.Syx[srow * a.d + i] - syv * a.sx[i] * inv_n) / a.dg[i];
+        bf16_t hi, lo;
+        split_bf16(v, hi, lo);
+        bf16_t* row = a.Aq + c * 3 * a.d;
+        row[i] = hi;
+        row[a.d + i] = hi;
+        row[2 * a.d + i] = lo;
         if (i == 0) a.mu_y[c] = syv * inv_n;
     }
 }
 
 // Factor the diagonal block J (already updated by all earlier panels) in place into L_JJ and
 // write L_JJ^-1 into Dinv.  info receives the 1-based index of the first non-positive pivot.
+// The block sits in LDS; 256 threads eliminate one column per step, then form L^-1 one row at
+// a time, four threads per column splitting each dot product (reduced in a fixed order).
 __global__ __launch_bounds__(256) void k_chol_diag(double* C, int64_t d, int J, double* Dinv, int32_t* info) {
     __shared__ double a[kNB][kNB + 1];
-    __shared__ double b[kNB][kNB + 1];
+    __shared__ double x[kNB][kNB + 1];
+    __shared__ double red[4][kNB];
     const int t = threadIdx.x;
     const int64_t off = (int64_t)J * kNB;
     for (int idx = t; idx < kNB * kNB; idx += 256) {
         const int i = idx / kNB, k = idx % kNB;
         a[i][k] = C[(off + i) * d + off + k];
     }
+    bool failed = t == 0 && *info != 0;  // an earlier block already failed: keep its pivot
     __syncthreads();
     for (int j = 0; j < kNB; ++j) {
         if (t == 0) {
             const double p = a[j][j];
-            if (!(p > 0.0) && *info == 0) *info = (int32_t)(off + j + 1);
+            if (!(p > 0.0) && !failed) {
+                *info = (int32_t)(off + j + 1);
+                failed = true;
+            }
             a[j][j] = sqrt(p);
         }
         __syncthreads();
-        for (int i = j + 1 + t; i < kNB; i += 256) a[i][j] /= a[j][j];
+        if (t > j && t < kNB) a[t][j] /= a[j][j];
         __syncthreads();
-        for (int idx = t; idx < kNB * kNB; idx += 256) {
-            const int i = idx / kNB, k = idx % kNB;
-            if (k > j && i >= k) a[i][k] -= a[i][j] * a[k][j];
+        // trailing lower triangle: rows i > j, columns j < k <= i
+        const int m = kNB - 1 - j;
+        for (int idx = t; idx < m * m; idx += 256) {
+            const int i = j + 1 + idx / m, k = j + 1 + idx % m;
+            if (k <= i) a[i][k] -= a[i][j] * a[k][j];
         }
         __syncthreads();
     }
-    // inverse of the lower triangle, one column per thread
-    if (t < kNB) {
-        const int c = t;
-        for (int i = 0; i < kNB; ++i) {
-            if (i < c) {
-                b[i][c] = 0.0;
-            } else if (i == c) {
-                b[i][c] = 1.0 / a[c][c];
-            } else {
-                double s = 0.0;
-                for (int k = c; k < i; ++k) s += a[i][k] * b[k][c];
-                b[i][c] = -s / a[i][i];
-            }
-        }
+    const int c = t & (kNB - 1), q = t >> 6;
+    for (int r = 0; r < kNB; ++r) {
+        double s = 0.0;
+        for (int k = q; k < r; k += 4) s += a[r][k] * x[k][c];
+        red[q][c] = s;
+        __syncthreads();
+        if (q == 0) x[r][c] = ((r == c ? 1.0 : 0.0) - (((red[0][c] + red[1][c]) + red[2][c]) + red[3][c])) / a[r][r];
+        __syncthreads();
     }
-    __syncthreads();
     double* D = Dinv + (int64_t)J * kNB * kNB;
     for (int idx = t; idx < kNB * kNB; idx += 256) {
         const int i = idx / kNB, k = idx % kNB;
         C[(off + i) * d + off + k] = k <= i ? a[i][k] : 0.0;
-        D[idx] = b[i][k];
+        D[idx] = x[i][k];
     }
 }
 
-// b[c] = mu_y[c] - sum_i W[c][i] s_x[i] / n ; one wave per row.
-__global__ __launch_bounds__(256) void k_bias(const double* W, const double* sx, const int64_t* np, const double* mu_y,
-                                              int64_t d, int64_t rows, float* b) {
-    const int64_t c = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+// dg[i] = sqrt(A[i][i]) before the factorisation overwrites the diagonal.
+__global__ void k_diag_sqrt(const double* A, int64_t d, double* dg) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < d) dg[i] = sqrt(fabs(A[i * d + i]));
+}
+
+// Equilibrated inverse, split: row j of Bq = [hi | lo | hi] of Ainv[j][i] dg[i] dg[j].
+__global__ void k_split_inverse(const double* Ainv, const double* dg, int64_t d, bf16_t* Bq) {
+    const int64_t n = d * d;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t j = idx / d, i = idx % d;
+        bf16_t hi, lo;
+        split_bf16(Ainv[idx] * dg[i] * dg[j], hi, lo);
+        bf16_t* row = Bq + j * 3 * d;
+        row[i] = hi;
+        row[d + i] = lo;
+        row[2 * d + i] = hi;
+    }
+}
+
+// W = Aq Bq^T over K = 3d.  MFMA operand A = Bq rows (input feature j), B = Aq rows
+// (output c), so each lane holds 4 consecutive j of one c: W[c][j..j+3] = acc / dg[j] is one
+// 16-byte (fp32) and one 8-byte (bf16) store.  The epilogue also leaves, per (c, tile of 256
+// j), the partial dot  sum_j W[c][j] s_x[j] / n  for the bias.
+struct WArgs {
+    const bf16_t* Aq;
+    const bf16_t* Bq;
+    const double* dg;
+    const double* sx;
+    const int64_t* np;
+    int64_t d;
+    int64_t rows;
+    int32_t tiles_j;
+    int32_t tiles_c;
+    float* W;          // may be null
+    bf16_t* Wlp;       // may be null
+    float* bpart;      // [rows][tiles_j]
+};
+
+__global__ __launch_bounds__(kThreads) void k_wgemm(WArgs a) {
+    using G = PipeGemm;
+    __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
+    const int v = xcd_order((int)blockIdx.x, (int)gridDim.x);
+    int jt, ct;
+    grouped_tile(v, a.tiles_j, a.tiles_c, 4, jt, ct);
+    const int64_t j0 = (int64_t)jt * 256, c0 = (int64_t)ct * 256;
+    const int64_t K = 3 * a.d;
+    G gm;
+    gm.run(lds, PipeOperand{a.Bq + j0 * K, K, 256}, PipeOperand{a.Aq + c0 * K, K, a.rows - c0}, (int)(K / G::BK));
+
+    const double inv_n = 1.0 / (double)*a.np;
     const int lane = threadIdx.x & 63;
-    if (c >= rows) return;
-    const double inv_n = 1.0 / (double)*np;
-    double s = 0.0;
-    for (int64_t i = lane; i < d; i += 64) s += W[c * d + i] * sx[i];
-    for (int w = 32; w > 0; w >>= 1) s += __shfl_xor(s, w);
-    if (lane == 0) b[c] = (float)(mu_y[c] - s * inv_n);
+    const int wm = (threadIdx.x >> 6) >> 1;
+    float* red = (float*)lds;  // [2][256]; the main loop ended on a barrier
+#pragma unroll
+    for (int jb = 0; jb < G::SN; ++jb) {
+        const int cl = G::col_of(jb);
+        const int64_t c = c0 + cl;
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < G::SM; ++i) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t j = j0 + G::row_of(i, 4 * q);
+                float w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    w[e] = (float)((double)gm.acc[i][jb][4 * q + e] / a.dg[j + e]);
+                    part += w[e] * (float)(a.sx[j + e] * inv_n);
+                }
+                if (a.W) *(f32x4*)(a.W + c * a.d + j) = f32x4{w[0], w[1], w[2], w[3]};
+                if (a.Wlp) *(u32x2*)(a.Wlp + c * a.d + j) = u32x2{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3])};
+            }
+        }
+        part += __shfl_xor(part, 32);
+        if (lane < 32) red[wm * 256 + cl] = part;
+    }
+    __syncthreads();
+    const int cl = threadIdx.x;
+    if (cl < 256) a.bpart[(c0 + cl) * a.tiles_j + jt] = red[cl] + red[256 + cl];
 }
 
-__global__ void k_store_w(const double* W, int64_t n, float* Wf, bf16_t* Wlp) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-        const double v = W[i];
-        if (Wf) Wf[i] = (float)v;
-        if (Wlp) Wlp[i] = __builtin_bit_cast(uint16_t, (__bf16)(float)v);
-    }
+// b[c] = mu_y[c] - sum over tiles of the partial dots (fixed order, fp64).
+__global__ void k_bias(const float* bpart, int tiles_j, const double* mu_y, int64_t rows, float* b) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= rows) return;
+    double s = 0.0;
+    for (int t = 0; t < tiles_j; ++t) s += (double)bpart[c * tiles_j + t];
+    b[c] = (float)(mu_y[c] - s);
 }
 
 // -------------------------------------------------------------------------------------------
 struct SolveWs {
-    double *C, *Cinv, *R, *W, *P, *Dinv, *mu_y;
+    double *C, *Cinv, *P, *Dinv, *mu_y, *dg;
+    bf16_t *Aq, *Bq;
+    float* bpart;
     size_t total;
 };
 
@@ -230,18 +328,20 @@ static SolveWs solve_ws(void* base, int64_t d, int64_t n_sel) {
     size_t off = 0;
     char* p = (char*)base;
     auto take = [&](size_t bytes) {
-        double* r = (double*)(p ? p + off : nullptr);
+        void* r = p ? (void*)(p + off) : nullptr;
         off += round_up(bytes, 256);
         return r;
     };
     const int64_t rows = n_sel * d;
-    w.C = take(d * d * 8);
-    w.Cinv = take(d * d * 8);
-    w.R = take(rows * d * 8);
-    w.W = take(rows * d * 8);
-    w.P = take(d * kNB * 8);
-    w.Dinv = take(d * kNB * 8);
-    w.mu_y = take(rows * 8);
+    w.C = (double*)take(d * d * 8);
+    w.Cinv = (double*)take(d * d * 8);
+    w.P = (double*)take(d * kNB * 8);
+    w.Dinv = (double*)take(d * kNB * 8);
+    w.mu_y = (double*)take(rows * 8);
+    w.dg = (double*)take(d * 8);
+    w.Aq = (bf16_t*)take(rows * 3 * d * 2);
+    w.Bq = (bf16_t*)take(d * 3 * d * 2);
+    w.bpart = (float*)take(rows * (d / 256) * 4);
     w.total = off;
     return w;
 }
@@ -317,6 +417,8 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, double lambda,
     for (int i = 0; i < n_sel; ++i)
         RF_REQUIRE(targets[i] >= 0 && targets[i] < desc->n_targets, RF_ERR_INVALID_ARG, "rf_solve: target index out of range");
     RF_REQUIRE(aligned(d_ws, 256), RF_ERR_INVALID_ARG, "rf_solve: workspace must be 256-B aligned");
+    RF_REQUIRE(aligned(d_W, 16) && aligned(d_W_lp, 16) && aligned(d_b, 4), RF_ERR_INVALID_ARG,
+               "rf_solve: W outputs must be 16-byte aligned");
     const int64_t d = desc->d;
     const SolveWs w = solve_ws(d_ws, d, n_sel);
     RF_REQUIRE(d_ws && ws_bytes >= w.total, RF_ERR_WORKSPACE, "rf_solve: workspace too small");
@@ -334,6 +436,8 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, double lambda,
     RF_TRY(check_launch("rf_solve: centre"));
     hipLaunchKernelGGL(k_add_lambda, dim3(1), dim3(256), 0, s, w.C, d, lambda, (int)(mode == RF_LAMBDA_REL_MEAN_DIAG));
     RF_TRY(check_launch("rf_solve: lambda"));
+    hipLaunchKernelGGL(k_diag_sqrt, dim3(grid_for(d)), dim3(256), 0, s, w.C, d, w.dg);
+    RF_TRY(check_launch("rf_solve: diagonal"));
 
     // blocked Cholesky
     const int nblk = (int)(d / kNB);
@@ -350,27 +454,32 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, double lambda,
                            (int64_t)kNB);
         RF_TRY(check_launch("rf_solve: copy"));
     }
-    // C^-1 by the two triangular solves on the identity
+    // A^-1 by the two triangular solves on the identity
     hipLaunchKernelGGL(k_identity, dim3(grid_for(d * d)), dim3(256), 0, s, w.Cinv, d);
     RF_TRY(check_launch("rf_solve: identity"));
     RF_TRY(apply_inverse(s, w, d, w.Cinv, d));
     if (n_sel == 0) return RF_OK;
 
+    // equilibrated split operands, then W on the MFMA pipes
+    hipLaunchKernelGGL(k_split_inverse, dim3(grid_for(d * d)), dim3(256), 0, s, w.Cinv, w.dg, d, w.Bq);
+    RF_TRY(check_launch("rf_solve: split inverse"));
     const int64_t rows = (int64_t)n_sel * d;
     CrossArgs ca{};
-    ca.Syx = Syx; ca.sy = sy; ca.sx = sx; ca.np = np; ca.d = d; ca.rows = rows; ca.R = w.R; ca.mu_y = w.mu_y;
+    ca.Syx = Syx; ca.sy = sy; ca.sx = sx; ca.np = np; ca.dg = w.dg; ca.d = d; ca.rows = rows; ca.Aq = w.Aq;
+    ca.mu_y = w.mu_y;
     for (int i = 0; i < n_sel; ++i) ca.tsel[i] = targets[i];
-    hipLaunchKernelGGL(k_centre_cross, dim3(grid_for(rows * d)), dim3(256), 0, s, ca);
+    hipLaunchKernelGGL(k_centre_split, dim3(grid_for(rows * d)), dim3(256), 0, s, ca);
     RF_TRY(check_launch("rf_solve: centre cross"));
-    // W = B C^-1 (C^-1 symmetric, so its rows serve as columns)
-    RF_TRY(dgemm<true>(s, rows, d, d, 1.0, w.R, d, w.Cinv, d, 0.0, w.W, d));
+    WArgs wa{};
+    wa.Aq = w.Aq; wa.Bq = w.Bq; wa.dg = w.dg; wa.sx = sx; wa.np = np; wa.d = d; wa.rows = rows;
+    wa.tiles_j = (int)(d / 256); wa.tiles_c = (int)(rows / 256); wa.W = d_W; wa.Wlp = (bf16_t*)d_W_lp;
+    wa.bpart = w.bpart;
+    hipLaunchKernelGGL(k_wgemm, dim3((unsigned)(wa.tiles_j * wa.tiles_c)), dim3(kThreads), 0, s, wa);
+    RF_TRY(check_launch("rf_solve: W product"));
     if (d_b) {
-        hipLaunchKernelGGL(k_bias, dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0, s, w.W, sx, np, w.mu_y, d, rows, d_b);
+        hipLaunchKernelGGL(k_bias, dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0, s, w.bpart, wa.tiles_j, w.mu_y,
+                           rows, d_b);
         RF_TRY(check_launch("rf_solve: bias"));
-    }
-    if (d_W || d_W_lp) {
-        hipLaunchKernelGGL(k_store_w, dim3(grid_for(rows * d)), dim3(256), 0, s, w.W, rows * d, d_W, (bf16_t*)d_W_lp);
-        RF_TRY(check_launch("rf_solve: store"));
     }
     return RF_OK;
 }
