@@ -136,7 +136,7 @@ def main():
         for c in range(n_chunks):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            rf.rf_gram_accumulate(state.desc, state.buf, Xc[c], Yc[c], stream=stream)
+            rf.rf_gram_accumulate(state.desc, state.buf, Xc[c], Yc[c], ws=state.ws, stream=stream)
             e1.record(stream)
             gram_ev.append((e0, e1))
         ev["gram"].record(stream)

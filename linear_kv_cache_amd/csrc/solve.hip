@@ -3,7 +3,7 @@
 //
 //   A  = S_xx - s_x^T s_x / n + lambda I           fp64, symmetric from the upper triangle
 //   A = L L^T                                      blocked right-looking Cholesky, 64-wide panels
-//   A^-1 = L^-T L^-1                               blocked triangular solves on the identity
+//   Z = L^-T, A^-1 = Z Z^T                          blocked forward solve on the identity, one GEMM
 //   B  = S_yx,l - s_y,l^T s_x / n                  fp64 per element, one row per (target, output)
 //   W  = B A^-1,  b = s_y/n - W (s_x/n)
 // The large product W = B A^-1 ([n_sel d] x d x d) runs on the bf16 MFMA pipes in three-term
@@ -25,10 +25,122 @@ namespace rf {
 constexpr int kNB = 64;        // Cholesky / triangular-solve block
 constexpr int kMaxSel = 64;
 
-// ---- tiled fp64 GEMM:  C = alpha * A * op(B) + beta * C -------------------------------------
+// ---- tiled fp64 GEMM on the matrix cores:  C = alpha * A * op(B) + beta * C ----------------
 // A [M][K] (lda); op(B) = B^T with B [N][K] (BT) or B [K][N] (!BT); beta == 0 never reads C.
+// 128 x 128 tile per work-group of 4 waves (2 x 2), each wave 64 x 64 as 4 x 4 blocks of
+// v_mfma_f64_16x16x4_f64 (lane l: A[l % 16][k0 + l / 16], B[k0 + l / 16][l % 16]; accumulator
+// element r of lane l is C[4 r + l / 16][l % 16], as measured on gfx950).  k-slices of 16 are staged in LDS as
+// [k][m] and [k][n], double-buffered; out-of-range rows and columns read as zero.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// Structure flags: kLowerOnly skips tiles wholly above the diagonal (the caller reads only the
+// lower triangle of C); kUpperOperands means A and B are upper triangular (A[m][k] = B[n][k] = 0
+// for k < m, k < n), so a tile's k-loop starts at max(m0, n0).
+enum { kFull = 0, kLowerOnly = 1, kUpperOperands = 2 };
+
 template <bool BT>
 __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, double alpha, const double* A,
+                                               int64_t lda, const double* B, int64_t ldb, double beta, double* C,
+                                               int64_t ldc, int structure) {
+    constexpr int BM = 128, BN = 128, BK = 16, PAD = 2;
+    __shared__ double As[2][BK][BM + PAD];
+    __shared__ double Bs[2][BK][BN + PAD];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t m0 = (int64_t)blockIdx.x * BM, n0 = (int64_t)blockIdx.y * BN;
+    if (structure == kLowerOnly && n0 > m0 + BM - 1) return;
+    const int64_t kbeg = structure == kUpperOperands ? (m0 > n0 ? m0 : n0) / BK * BK : 0;
+    // loaders: a K-contiguous operand gives each thread 8 consecutive k of one row; an
+    // N-contiguous operand gives 8 consecutive n of one k-row
+    double ra[8], rb[8];
+    auto load = [&](int64_t k0) {
+        {
+            const int64_t m = m0 + (t >> 1);
+            const int kk = (t & 1) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int64_t k = k0 + kk + e;
+                ra[e] = (m < M && k < K) ? A[m * lda + k] : 0.0;
+            }
+        }
+        if (BT) {
+            const int64_t n = n0 + (t >> 1);
+            const int kk = (t & 1) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int64_t k = k0 + kk + e;
+                rb[e] = (n < N && k < K) ? B[n * ldb + k] : 0.0;
+            }
+        } else {
+            const int64_t k = k0 + (t >> 4);
+            const int64_t nn = n0 + (t & 15) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rb[e] = (k < K && nn + e < N) ? B[k * ldb + nn + e] : 0.0;
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) As[buf][(t & 1) * 8 + e][t >> 1] = ra[e];
+        if (BT) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) Bs[buf][(t & 1) * 8 + e][t >> 1] = rb[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) Bs[buf][t >> 4][(t & 15) * 8 + e] = rb[e];
+        }
+    };
+    f64x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+    const int nk = K > kbeg ? (int)((K - kbeg + BK - 1) / BK) : 0;
+    if (nk > 0) {
+        load(kbeg);
+        store(0);
+        __syncthreads();
+        for (int kt = 0; kt < nk; ++kt) {
+            const int cur = kt & 1;
+            if (kt + 1 < nk) load(kbeg + (int64_t)(kt + 1) * BK);
+#pragma unroll
+            for (int ks = 0; ks < BK; ks += 4) {
+                const int kr = ks + (lane >> 4);
+                double a[4], b[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[i] = As[cur][kr][wm * 64 + i * 16 + (lane & 15)];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) b[j] = Bs[cur][kr][wn * 64 + j * 16 + (lane & 15)];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+            }
+            if (kt + 1 < nk) store(cur ^ 1);
+            __syncthreads();
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t n = n0 + wn * 64 + j * 16 + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t m = m0 + wm * 64 + i * 16 + 4 * r + (lane >> 4);
+                if (m < M && n < N) {
+                    double v = alpha * acc[i][j][r];
+                    if (beta != 0.0) v += beta * C[m * ldc + n];
+                    C[m * ldc + n] = v;
+                }
+            }
+        }
+    }
+}
+
+// ---- fp64 GEMM on the vector ALUs, 64 x 64 tiles: for narrow operands (N or M < 512), where
+// the matrix-core kernel's 128 x 128 tiles would leave most CUs idle.
+template <bool BT>
+__global__ __launch_bounds__(256) void k_dgemm_valu(int64_t M, int64_t N, int64_t K, double alpha, const double* A,
                                                int64_t lda, const double* B, int64_t ldb, double beta, double* C,
                                                int64_t ldc) {
     constexpr int BM = 64, BN = 64, BK = 16;
@@ -151,34 +263,46 @@ struct CrossArgs {
 };
 
 // Centred cross moments B[c][i] = S_yx[c][i] - s_y[c] s_x[i] / n (fp64), scaled by 1/dg[i]
-// and split into bf16 parts.
+// and split into bf16 parts; one thread per 8 consecutive i (16-byte stores).
 __global__ void k_centre_split(CrossArgs a) {
     const double inv_n = 1.0 / (double)*a.np;
-    const int64_t n = a.rows * a.d;
+    const int64_t per_row = a.d / 8;
+    const int64_t n = a.rows * per_row;
     for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t c = idx / a.d, i = idx % a.d;
+        const int64_t c = idx / per_row, i0 = (idx % per_row) * 8;
         const int64_t s = c / a.d, o = c % a.d;
         const int64_t srow = (int64_t)a.tsel[s] * a.d + o;
         const double syv = a.sy[srow];
-        const double v = ((double)a.Syx[srow * a.d + i] - syv * a.sx[i] * inv_n) / a.dg[i];
-        bf16_t hi, lo;
-        split_bf16(v, hi, lo);
+        const f32x4 v0 = *(const f32x4*)(a.Syx + srow * a.d + i0);
+        const f32x4 v1 = *(const f32x4*)(a.Syx + srow * a.d + i0 + 4);
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            bf16_t h0, l0, h1, l1;
+            const float x0 = e < 4 ? v0[e] : v1[e - 4], x1 = e < 4 ? v0[e + 1] : v1[e - 3];
+            split_bf16(((double)x0 - syv * a.sx[i0 + e] * inv_n) / a.dg[i0 + e], h0, l0);
+            split_bf16(((double)x1 - syv * a.sx[i0 + e + 1] * inv_n) / a.dg[i0 + e + 1], h1, l1);
+            hi[e / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            lo[e / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
         bf16_t* row = a.Aq + c * 3 * a.d;
-        row[i] = hi;
-        row[a.d + i] = hi;
-        row[2 * a.d + i] = lo;
-        if (i == 0) a.mu_y[c] = syv * inv_n;
+        const u32x4 H{hi[0], hi[1], hi[2], hi[3]}, Lo{lo[0], lo[1], lo[2], lo[3]};
+        *(u32x4*)(row + i0) = H;
+        *(u32x4*)(row + a.d + i0) = H;
+        *(u32x4*)(row + 2 * a.d + i0) = Lo;
+        if (i0 == 0) a.mu_y[c] = syv * inv_n;
     }
 }
 
 // Factor the diagonal block J (already updated by all earlier panels) in place into L_JJ and
 // write L_JJ^-1 into Dinv.  info receives the 1-based index of the first non-positive pivot.
 // The block sits in LDS; 256 threads eliminate one column per step, then form L^-1 one row at
-// a time, four threads per column splitting each dot product (reduced in a fixed order).
+// a time by forward substitution, four lanes per column splitting each dot product (reduced by
+// a fixed shuffle tree).
 __global__ __launch_bounds__(256) void k_chol_diag(double* C, int64_t d, int J, double* Dinv, int32_t* info) {
     __shared__ double a[kNB][kNB + 1];
     __shared__ double x[kNB][kNB + 1];
-    __shared__ double red[4][kNB];
+    __shared__ double rinv[kNB];   // 1 / L[j][j]
     const int t = threadIdx.x;
     const int64_t off = (int64_t)J * kNB;
     for (int idx = t; idx < kNB * kNB; idx += 256) {
@@ -194,26 +318,39 @@ __global__ __launch_bounds__(256) void k_chol_diag(double* C, int64_t d, int J, 
                 *info = (int32_t)(off + j + 1);
                 failed = true;
             }
-            a[j][j] = sqrt(p);
+            const double r = sqrt(p);
+            a[j][j] = r;
+            rinv[j] = 1.0 / r;
         }
         __syncthreads();
-        if (t > j && t < kNB) a[t][j] /= a[j][j];
+        if (t > j && t < kNB) a[t][j] *= rinv[j];
         __syncthreads();
-        // trailing lower triangle: rows i > j, columns j < k <= i
-        const int m = kNB - 1 - j;
-        for (int idx = t; idx < m * m; idx += 256) {
-            const int i = j + 1 + idx / m, k = j + 1 + idx % m;
-            if (k <= i) a[i][k] -= a[i][j] * a[k][j];
+        // trailing lower triangle: rows i > j, columns j < k <= i (thread: column t & 63, every
+        // fourth row)
+        {
+            const int k = t & (kNB - 1);
+            if (k > j) {
+                const double lkj = a[k][j];
+                for (int i = k + ((t >> 6) - k % 4 + 4) % 4; i < kNB; i += 4) a[i][k] -= a[i][j] * lkj;
+            }
         }
         __syncthreads();
     }
-    const int c = t & (kNB - 1), q = t >> 6;
+    // column c of X = L^-1:  X[r][c] = (delta_rc - sum_{k<r} L[r][k] X[k][c]) / L[r][r];
+    // lane group (4 lanes) per column, lane q of the group takes k = q, q + 4, ...
+    const int c = t >> 2, q = t & 3;
     for (int r = 0; r < kNB; ++r) {
-        double s = 0.0;
-        for (int k = q; k < r; k += 4) s += a[r][k] * x[k][c];
-        red[q][c] = s;
-        __syncthreads();
-        if (q == 0) x[r][c] = ((r == c ? 1.0 : 0.0) - (((red[0][c] + red[1][c]) + red[2][c]) + red[3][c])) / a[r][r];
+        double s0 = 0.0, s1 = 0.0;
+        int k = q;
+        for (; k + 4 < r; k += 8) {
+            s0 += a[r][k] * x[k][c];
+            s1 += a[r][k + 4] * x[k + 4][c];
+        }
+        if (k < r) s0 += a[r][k] * x[k][c];
+        double sum = s0 + s1;
+        sum += __shfl_xor(sum, 1);
+        sum += __shfl_xor(sum, 2);
+        if (q == 0) x[r][c] = ((r == c ? 1.0 : 0.0) - sum) * rinv[r];
         __syncthreads();
     }
     double* D = Dinv + (int64_t)J * kNB * kNB;
@@ -352,10 +489,14 @@ static inline unsigned grid_for(int64_t n, int64_t per = 256) {
 
 template <bool BT>
 static rf_status dgemm(hipStream_t s, int64_t M, int64_t N, int64_t K, double alpha, const double* A, int64_t lda,
-                       const double* B, int64_t ldb, double beta, double* C, int64_t ldc) {
+                       const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int structure = kFull) {
     if (M <= 0 || N <= 0) return RF_OK;
-    hipLaunchKernelGGL(k_dgemm<BT>, dim3((unsigned)ceil_div(M, 64), (unsigned)ceil_div(N, 64)), dim3(256), 0, s, M, N,
-                       K, alpha, A, lda, B, ldb, beta, C, ldc);
+    if ((M >= 512 && N >= 512) || structure != kFull)
+        hipLaunchKernelGGL(k_dgemm<BT>, dim3((unsigned)ceil_div(M, 128), (unsigned)ceil_div(N, 128)), dim3(256), 0, s,
+                           M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, structure);
+    else
+        hipLaunchKernelGGL(k_dgemm_valu<BT>, dim3((unsigned)ceil_div(M, 64), (unsigned)ceil_div(N, 64)), dim3(256), 0,
+                           s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
     return check_launch("rf_solve: dgemm");
 }
 
@@ -365,27 +506,20 @@ static rf_status dgemm(hipStream_t s, int64_t M, int64_t N, int64_t K, double al
         if (_st != RF_OK) return _st;     \
     } while (0)
 
-// R (rows x d, ld d) <- R C^-1 using L (in C's lower triangle) and the diagonal inverses.
-static rf_status apply_inverse(hipStream_t s, const SolveWs& w, int64_t d, double* R, int64_t rows) {
+// Z = L^-T by the forward solve Z L^T = I, one 64-column block at a time (L in C's lower
+// triangle, its diagonal-block inverses in Dinv).  Z is upper triangular, so block column J
+// has nonzero rows only below (J + 1) * 64 and each step touches just those rows.
+static rf_status inverse_factor(hipStream_t s, const SolveWs& w, int64_t d, double* Z) {
     const int nblk = (int)(d / kNB);
-    // forward:  Z L^T = R
     for (int J = 0; J < nblk; ++J) {
         const int64_t c0 = (int64_t)J * kNB;
-        RF_TRY(dgemm<true>(s, rows, kNB, kNB, 1.0, R + c0, d, w.Dinv + c0 * kNB, kNB, 0.0, w.P, kNB));
-        hipLaunchKernelGGL(k_copy2d, dim3(grid_for(rows * kNB)), dim3(256), 0, s, w.P, (int64_t)kNB, R + c0, d, rows,
+        const int64_t rows = c0 + kNB;
+        RF_TRY(dgemm<true>(s, rows, kNB, kNB, 1.0, Z + c0, d, w.Dinv + c0 * kNB, kNB, 0.0, w.P, kNB));
+        hipLaunchKernelGGL(k_copy2d, dim3(grid_for(rows * kNB)), dim3(256), 0, s, w.P, (int64_t)kNB, Z + c0, d, rows,
                            (int64_t)kNB);
         RF_TRY(check_launch("rf_solve: copy"));
         const int64_t rem = d - c0 - kNB;
-        RF_TRY(dgemm<true>(s, rows, rem, kNB, -1.0, w.P, kNB, w.C + (c0 + kNB) * d + c0, d, 1.0, R + c0 + kNB, d));
-    }
-    // backward: W L = Z
-    for (int J = nblk - 1; J >= 0; --J) {
-        const int64_t c0 = (int64_t)J * kNB;
-        RF_TRY(dgemm<false>(s, rows, kNB, kNB, 1.0, R + c0, d, w.Dinv + c0 * kNB, kNB, 0.0, w.P, kNB));
-        hipLaunchKernelGGL(k_copy2d, dim3(grid_for(rows * kNB)), dim3(256), 0, s, w.P, (int64_t)kNB, R + c0, d, rows,
-                           (int64_t)kNB);
-        RF_TRY(check_launch("rf_solve: copy"));
-        RF_TRY(dgemm<false>(s, rows, c0, kNB, -1.0, w.P, kNB, w.C + c0 * d, d, 1.0, R, d));
+        RF_TRY(dgemm<true>(s, rows, rem, kNB, -1.0, w.P, kNB, w.C + (c0 + kNB) * d + c0, d, 1.0, Z + c0 + kNB, d));
     }
     return RF_OK;
 }
@@ -449,26 +583,28 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, double lambda,
         if (rem <= 0) continue;
         double* panel = w.C + (c0 + kNB) * d + c0;
         RF_TRY(dgemm<true>(s, rem, kNB, kNB, 1.0, panel, d, w.Dinv + c0 * kNB, kNB, 0.0, w.P, kNB));
-        RF_TRY(dgemm<true>(s, rem, rem, kNB, -1.0, w.P, kNB, w.P, kNB, 1.0, w.C + (c0 + kNB) * d + c0 + kNB, d));
+        RF_TRY(dgemm<true>(s, rem, rem, kNB, -1.0, w.P, kNB, w.P, kNB, 1.0, w.C + (c0 + kNB) * d + c0 + kNB, d,
+                           kLowerOnly));
         hipLaunchKernelGGL(k_copy2d, dim3(grid_for(rem * kNB)), dim3(256), 0, s, w.P, (int64_t)kNB, panel, d, rem,
                            (int64_t)kNB);
         RF_TRY(check_launch("rf_solve: copy"));
     }
-    // A^-1 by the two triangular solves on the identity
+    // A^-1 = Z Z^T with Z = L^-T (the factor is no longer needed afterwards: A^-1 overwrites it)
     hipLaunchKernelGGL(k_identity, dim3(grid_for(d * d)), dim3(256), 0, s, w.Cinv, d);
     RF_TRY(check_launch("rf_solve: identity"));
-    RF_TRY(apply_inverse(s, w, d, w.Cinv, d));
+    RF_TRY(inverse_factor(s, w, d, w.Cinv));
+    RF_TRY(dgemm<true>(s, d, d, d, 1.0, w.Cinv, d, w.Cinv, d, 0.0, w.C, d, kUpperOperands));
     if (n_sel == 0) return RF_OK;
 
     // equilibrated split operands, then W on the MFMA pipes
-    hipLaunchKernelGGL(k_split_inverse, dim3(grid_for(d * d)), dim3(256), 0, s, w.Cinv, w.dg, d, w.Bq);
+    hipLaunchKernelGGL(k_split_inverse, dim3(grid_for(d * d)), dim3(256), 0, s, w.C, w.dg, d, w.Bq);
     RF_TRY(check_launch("rf_solve: split inverse"));
     const int64_t rows = (int64_t)n_sel * d;
     CrossArgs ca{};
     ca.Syx = Syx; ca.sy = sy; ca.sx = sx; ca.np = np; ca.dg = w.dg; ca.d = d; ca.rows = rows; ca.Aq = w.Aq;
     ca.mu_y = w.mu_y;
     for (int i = 0; i < n_sel; ++i) ca.tsel[i] = targets[i];
-    hipLaunchKernelGGL(k_centre_split, dim3(grid_for(rows * d)), dim3(256), 0, s, ca);
+    hipLaunchKernelGGL(k_centre_split, dim3(grid_for(rows * d / 8)), dim3(256), 0, s, ca);
     RF_TRY(check_launch("rf_solve: centre cross"));
     WArgs wa{};
     wa.Aq = w.Aq; wa.Bq = w.Bq; wa.dg = w.dg; wa.sx = sx; wa.np = np; wa.d = d; wa.rows = rows;
