@@ -25,6 +25,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+# HBM bytes of one rf_gram_accumulate call (8192 rows, d=4096, 16 targets), from two
+# rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of this benchmark, each scaled by what the
+# counter reads for a 1 GiB device copy; profiles/pmc_traffic_llama8b-shaped_d4096_T16384.md has the
+# commands and the figures; set to None whenever k_gram_transpose or k_gram_pipe change.
+GRAM_TRAFFIC = (557379 + 4278748) * 2 * 1024 + (1114656 + 1218425) * 1024
 METRIC = "filled tokens/sec (all filled layers) + % bf16 MFMA peak; ridge-fit rows/sec"
 
 
@@ -77,8 +82,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="C2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=2048)
-    ap.add_argument("--cpu-fit-rows", type=int, default=1024)
+    ap.add_argument("--cpu-tokens", type=int, default=16384)
+    ap.add_argument("--cpu-fit-rows", type=int, default=8192)
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 1 GiB device-to-device copy before the steps, a known-size reference "
                          "for HBM byte counters")
@@ -197,9 +202,12 @@ def main():
                 "rows_per_s_incl_solve": round(cfg.calib_rows / ((statistics.mean(gram_ms) +
                                                                    statistics.mean(solve_ms)) / 1e3), 1),
                 "flop_per_row": cfg.fit_flop_per_row()},
-        "roofline": {"bound": "mfma", "kernel": "k_gram<bf16> (one rf_gram_accumulate of 8192 rows)",
+        "roofline": {"bound": "mfma",
+                     "kernel": f"rf_gram_accumulate of {cfg.calib_chunk} rows x {L} targets "
+                               f"(k_gram_transpose + k_gram_pipe)",
                      "achieved": round(gram_tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gram_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(gram_tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": GRAM_TRAFFIC if args.config == "C2" else None,
                      "launch_ms": round(gram_launch_ms, 4), "flop_per_launch": gram_flop_per_launch},
     }
     if not args.no_cpu_baseline:
