@@ -106,7 +106,7 @@ template <typename T> struct MapStage { static constexpr bool kLds = false; stat
 template <> struct MapStage<bf16_t> { static constexpr bool kLds = true; static constexpr int kBytes = kTT * kFT * 2; };
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_fill_map(MapArgs a) {
+__global__ __launch_bounds__(FillCore<T>::G::kThr) void k_fill_map(MapArgs a) {
     using G = typename FillCore<T>::G;
     constexpr int kRedOff = MapStage<T>::kBytes;  // [2][kTT] fp32 partial sums after the stage
     constexpr int kLdsBytes = G::LDS_BYTES > kRedOff + 2 * kTT * 4 ? G::LDS_BYTES : kRedOff + 2 * kTT * 4;
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void k_fill_map(MapArgs a) {
 
     // the main loop ended on a barrier: LDS is free
     const int lane = threadIdx.x & 63;
-    const int wm = (threadIdx.x >> 6) >> 1;
+    const int wm = (threadIdx.x >> 6) / G::WGN;   // wave row (two per tile)
     float* red = (float*)(lds + kRedOff);
     const float* bias = a.bias[g] + mt * kFT;
     const float* gamma = a.gamma[g] + mt * kFT;
@@ -159,11 +159,12 @@ __global__ __launch_bounds__(kThreads) void k_fill_map(MapArgs a) {
     }
     __syncthreads();
     if constexpr (MapStage<T>::kLds) {
-        // 8 tokens per pass; the 32 lanes of a half-wave write one token's 512 bytes
+        // kThr / 32 tokens per pass; the 32 lanes of a half-wave write one token's 512 bytes
+        constexpr int kTok = G::kThr / 32;
         const int c = threadIdx.x & 31;
 #pragma unroll 4
-        for (int p = 0; p < kTT / 8; ++p) {
-            const int nl = p * 8 + (threadIdx.x >> 5);
+        for (int p = 0; p < kTT / kTok; ++p) {
+            const int nl = p * kTok + (threadIdx.x >> 5);
             const int64_t n = n0 + nl;
             const u32x4 v = *(const u32x4*)(lds + nl * (kFT * 2) + ((c ^ (nl & 31)) << 4));
             if (n < a.rows) *(u32x4*)(H + n * a.d + (int64_t)mt * kFT + c * 8) = v;
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void k_fill_map(MapArgs a) {
 }
 
 template <typename T, int DH>
-__global__ __launch_bounds__(kThreads) void k_fill_kv(KVArgs a) {
+__global__ __launch_bounds__(FillCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
     using G = typename FillCore<T>::G;
     static_assert(G::WTM % DH == 0, "a wave's feature extent must hold whole heads");
     constexpr int HALF = DH / 2;
@@ -196,41 +197,107 @@ __global__ __launch_bounds__(kThreads) void k_fill_kv(KVArgs a) {
     T* pool = (T*)(is_k ? a.kc[g] : a.vc[g]);
     const float* ps = a.psum + g * a.ps_slot;
     const float inv_d = 1.0f / (float)a.d;
-#pragma unroll
-    for (int j = 0; j < G::SN; ++j) {
-        const int64_t n = n0 + G::col_of(j);
-        bool ok = n < a.rows;
-        const int64_t t = a.t0 + n;
-        float r = 0.f;
-        int64_t base = 0;
-        if (ok) {
-            float s = 0.f;
+    // 1 / rms of token n from its per-feature-tile partial sums (fixed order)
+    auto rms_inv = [&](int64_t n) {
+        float s = 0.f;
+        if (a.n_ps % 4 == 0) {
+            for (int p = 0; p < a.n_ps; p += 4) {
+                const f32x4 v = *(const f32x4*)(ps + n * a.n_ps + p);
+                s += v[0]; s += v[1]; s += v[2]; s += v[3];
+            }
+        } else {
             for (int p = 0; p < a.n_ps; ++p) s += ps[n * a.n_ps + p];
-            r = 1.0f / sqrtf(s * inv_d + a.eps);
-            if (a.paged) {
-                const int64_t lb = t / a.block_size;
-                int64_t phys = lb < a.n_table_blocks ? (int64_t)a.block_table[lb] : -1;
-                ok = phys >= 0 && phys < a.n_blocks;
-                base = phys * a.stride_block + (t % a.block_size) * a.stride_token;
-            } else {
-                base = t * a.stride_token;
+        }
+        return 1.0f / sqrtf(s * inv_d + a.eps);
+    };
+    // element offset of token t's row in the pool, or -1 if it has no slot
+    auto row_base = [&](int64_t t) -> int64_t {
+        if (!a.paged) return t * a.stride_token;
+        const int64_t lb = t / a.block_size;
+        const int64_t phys = lb < a.n_table_blocks ? (int64_t)a.block_table[lb] : -1;
+        if (phys < 0 || phys >= a.n_blocks) return -1;
+        return phys * a.stride_block + (t % a.block_size) * a.stride_token;
+    };
+    // final values: scaled by r = 1/rms of their token; keys rotated by their position
+    if constexpr (sizeof(T) == 2) {
+        // bf16: stage the 256 tokens x 256 features tile in LDS ([token][feature], 16-byte
+        // chunk c of token n in slot c ^ (n & 31)), then write whole (token, head) rows
+#pragma unroll
+        for (int j = 0; j < G::SN; ++j) {
+            const int nl = G::col_of(j);
+            const int64_t n = n0 + nl;
+            const bool ok = n < a.rows;
+            const float r = ok ? rms_inv(n) : 0.f;
+            const float* cs_row = a.rope + (a.pos0 + a.t0 + (ok ? n : 0)) * (int64_t)DH;
+#pragma unroll
+            for (int i = 0; i < G::SM; ++i) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int fl = G::row_of(i, 4 * q);
+                    const int dim = (f0 + fl) % DH;
+                    float o[4];
+                    if (!is_k) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) o[e] = gm.acc[i][j][4 * q + e] * r;
+                    } else {
+                        // dims [dim, dim+4) pair with dims + HALF, held in sub-tile i +- PAIR
+                        const bool low = (i * 32) % DH < HALF;
+                        const int dlo = low ? dim : dim - HALF;
+                        const f32x4 c01 = *(const f32x4*)(cs_row + 2 * dlo);
+                        const f32x4 c23 = *(const f32x4*)(cs_row + 2 * dlo + 4);
+                        const float cs[4] = {c01[0], c01[2], c23[0], c23[2]};
+                        const float sn[4] = {c01[1], c01[3], c23[1], c23[3]};
+                        const int ip = low ? (i + PAIR) % G::SM : (i + G::SM - PAIR) % G::SM;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float x = gm.acc[i][j][4 * q + e] * r;
+                            const float y = gm.acc[ip][j][4 * q + e] * r;
+                            o[e] = low ? x * cs[e] - y * sn[e] : x * cs[e] + y * sn[e];
+                        }
+                    }
+                    const int slot = ((fl >> 3) ^ (nl & 31)) << 4;
+                    *(u32x2*)(lds + nl * (kFT * 2) + slot + (fl & 4) * 2) =
+                        u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                }
             }
         }
-        if (!ok) continue;
-        const float* cs_row = a.rope + (a.pos0 + t) * (int64_t)DH;  // HALF (cos, sin) pairs
+        __syncthreads();
+        constexpr int kTok = G::kThr / 32;
+        const int c = threadIdx.x & 31;            // 16-byte chunk: features 8c .. 8c+7
+        const int head = (f0 + c * 8) / DH, dim = (f0 + c * 8) % DH;
+#pragma unroll 2
+        for (int p = 0; p < kTT / kTok; ++p) {
+            const int nl = p * kTok + (threadIdx.x >> 5);
+            const int64_t n = n0 + nl;
+            if (n >= a.rows) continue;
+            const int64_t base = row_base(a.t0 + n);
+            if (base < 0) continue;
+            const u32x4 v = *(const u32x4*)(lds + nl * (kFT * 2) + ((c ^ (nl & 31)) << 4));
+            *(u32x4*)(pool + base + head * a.stride_head + dim) = v;
+        }
+    } else {
+        // fp32: each lane stores its 4 consecutive features directly
 #pragma unroll
-        for (int i = 0; i < G::SM; ++i) {
+        for (int j = 0; j < G::SN; ++j) {
+            const int64_t n = n0 + G::col_of(j);
+            if (n >= a.rows) continue;
+            const int64_t t = a.t0 + n;
+            const int64_t base = row_base(t);
+            if (base < 0) continue;
+            const float r = rms_inv(n);
+            const float* cs_row = a.rope + (a.pos0 + t) * (int64_t)DH;  // HALF (cos, sin) pairs
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int f = f0 + G::row_of(i, 4 * q);
-                const int head = f / DH;
-                const int dim = f % DH;
-                T* dst = pool + base + head * a.stride_head + dim;
-                if (!is_k) {
-                    store4<T>(dst, gm.acc[i][j][4 * q] * r, gm.acc[i][j][4 * q + 1] * r,
-                              gm.acc[i][j][4 * q + 2] * r, gm.acc[i][j][4 * q + 3] * r);
-                } else {
-                    if ((i * 32) % DH < HALF) {
+            for (int i = 0; i < G::SM; ++i) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int f = f0 + G::row_of(i, 4 * q);
+                    const int head = f / DH;
+                    const int dim = f % DH;
+                    T* dst = pool + base + head * a.stride_head + dim;
+                    if (!is_k) {
+                        store4<T>(dst, gm.acc[i][j][4 * q] * r, gm.acc[i][j][4 * q + 1] * r,
+                                  gm.acc[i][j][4 * q + 2] * r, gm.acc[i][j][4 * q + 3] * r);
+                    } else if ((i * 32) % DH < HALF) {
                         // this sub-tile holds dims [dim, dim+4) < HALF; partner sub-tile i+PAIR
                         // holds dims + HALF of the same head in the same registers
                         const f32x4 c01 = *(const f32x4*)(cs_row + 2 * dim);
@@ -305,14 +372,14 @@ static rf_status launch_fill(const rf_fill_weights* w, int32_t n_layers, const v
         }
         ma.tok_tiles = tok_tiles;
         ka.tok_tiles = tok_tiles;
-        hipLaunchKernelGGL(k_fill_map<T>, dim3((w->d / kFT) * tok_tiles * gsz), dim3(kThreads), 0, stream, ma);
+        hipLaunchKernelGGL(k_fill_map<T>, dim3((w->d / kFT) * tok_tiles * gsz), dim3(FillCore<T>::G::kThr), 0, stream, ma);
         rf_status st = check_launch("rf_fill: map kernel");
         if (st != RF_OK) return st;
         const dim3 kv_grid((2 * ka.kvw / kFT) * tok_tiles * gsz);
         if (w->head_dim == 128)
-            hipLaunchKernelGGL((k_fill_kv<T, 128>), kv_grid, dim3(kThreads), 0, stream, ka);
+            hipLaunchKernelGGL((k_fill_kv<T, 128>), kv_grid, dim3(FillCore<T>::G::kThr), 0, stream, ka);
         else
-            hipLaunchKernelGGL((k_fill_kv<T, 64>), kv_grid, dim3(kThreads), 0, stream, ka);
+            hipLaunchKernelGGL((k_fill_kv<T, 64>), kv_grid, dim3(FillCore<T>::G::kThr), 0, stream, ka);
         st = check_launch("rf_fill: kv kernel");
         if (st != RF_OK) return st;
     }

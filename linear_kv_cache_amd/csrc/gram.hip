@@ -235,7 +235,7 @@ struct PipeGramArgs {
 // step; [n_yx, n_yx + n_xx) are the S_xx upper triangle.  MFMA operand A = X^T rows (X column
 // tile mt), B = rows of the S tile (Y_l^T or X^T), so each lane holds 4 consecutive columns of
 // one S row: one 16-byte read-modify-write.
-__global__ __launch_bounds__(kThreads) void k_gram_pipe(PipeGramArgs a) {
+__global__ __launch_bounds__(kPipeThreads) void k_gram_pipe(PipeGramArgs a) {
     using G = PipeGemm;
     __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
     const int v = xcd_order((int)blockIdx.x, (int)gridDim.x);
@@ -403,7 +403,7 @@ rf_status rf_gram_accumulate(const rf_gram_desc* desc, void* d_state, const void
         PipeGramArgs pa{};
         pa.T = (const bf16_t*)d_ws; pa.rows_pad = ta.rows_pad; pa.d = desc->d; pa.tiles_m = tiles_m;
         pa.n_xx = n_xx; pa.n_yx = n_yx; pa.Sxx = Sxx; pa.Syx = Syx; pa.n = np; pa.rows = pr;
-        hipLaunchKernelGGL(k_gram_pipe, dim3((unsigned)(n_xx + n_yx)), dim3(kThreads), 0, strm, pa);
+        hipLaunchKernelGGL(k_gram_pipe, dim3((unsigned)(n_xx + n_yx)), dim3(kPipeThreads), 0, strm, pa);
         st = check_launch("rf_gram_accumulate: products");
         if (st != RF_OK) return st;
     }

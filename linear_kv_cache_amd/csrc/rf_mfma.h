@@ -112,6 +112,8 @@ struct Operand {
 
 template <typename T, int BM, int BN, bool A_MMAJOR, bool B_MMAJOR>
 struct TileGemm {
+    static constexpr int kThr = kThreads;
+    static constexpr int WGN = 2;  // waves per row of the 2 x 2 wave grid
     static constexpr int EPV = ElemTraits<T>::kPerVec;
     static constexpr int BK = kRowBytes / (int)sizeof(T);
     static constexpr int WTM = BM / 2, WTN = BN / 2;

@@ -400,7 +400,7 @@ struct WArgs {
     float* bpart;      // [rows][tiles_j]
 };
 
-__global__ __launch_bounds__(kThreads) void k_wgemm(WArgs a) {
+__global__ __launch_bounds__(kPipeThreads) void k_wgemm(WArgs a) {
     using G = PipeGemm;
     __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
     const int v = xcd_order((int)blockIdx.x, (int)gridDim.x);
@@ -413,7 +413,7 @@ __global__ __launch_bounds__(kThreads) void k_wgemm(WArgs a) {
 
     const double inv_n = 1.0 / (double)*a.np;
     const int lane = threadIdx.x & 63;
-    const int wm = (threadIdx.x >> 6) >> 1;
+    const int wm = (threadIdx.x >> 6) / G::WGN;   // wave row (two per tile)
     float* red = (float*)lds;  // [2][256]; the main loop ended on a barrier
 #pragma unroll
     for (int jb = 0; jb < G::SN; ++jb) {
@@ -610,7 +610,7 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, double lambda,
     wa.Aq = w.Aq; wa.Bq = w.Bq; wa.dg = w.dg; wa.sx = sx; wa.np = np; wa.d = d; wa.rows = rows;
     wa.tiles_j = (int)(d / 256); wa.tiles_c = (int)(rows / 256); wa.W = d_W; wa.Wlp = (bf16_t*)d_W_lp;
     wa.bpart = w.bpart;
-    hipLaunchKernelGGL(k_wgemm, dim3((unsigned)(wa.tiles_j * wa.tiles_c)), dim3(kThreads), 0, s, wa);
+    hipLaunchKernelGGL(k_wgemm, dim3((unsigned)(wa.tiles_j * wa.tiles_c)), dim3(kPipeThreads), 0, s, wa);
     RF_TRY(check_launch("rf_solve: W product"));
     if (d_b) {
         hipLaunchKernelGGL(k_bias, dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0, s, w.bpart, wa.tiles_j, w.mu_y,
