@@ -109,7 +109,9 @@ template <typename T>
 __global__ __launch_bounds__(FillCore<T>::G::kThr) void k_fill_map(MapArgs a) {
     using G = typename FillCore<T>::G;
     constexpr int kRedOff = MapStage<T>::kBytes;  // [2][kTT] fp32 partial sums after the stage
-    constexpr int kLdsBytes = G::LDS_BYTES > kRedOff + 2 * kTT * 4 ? G::LDS_BYTES : kRedOff + 2 * kTT * 4;
+    constexpr int kBgOff = kRedOff + 2 * kTT * 4;  // bias and gamma of the tile's features, fp32
+    constexpr int kEpi = kBgOff + 2 * kFT * 4;
+    constexpr int kLdsBytes = G::LDS_BYTES > kEpi ? G::LDS_BYTES : kEpi;
     __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
     int g, mt, tt;
     fill_tile(a.d / kFT, a.tok_tiles, g, mt, tt);
@@ -122,8 +124,13 @@ __global__ __launch_bounds__(FillCore<T>::G::kThr) void k_fill_map(MapArgs a) {
     const int lane = threadIdx.x & 63;
     const int wm = (threadIdx.x >> 6) / G::WGN;   // wave row (two per tile)
     float* red = (float*)(lds + kRedOff);
-    const float* bias = a.bias[g] + mt * kFT;
-    const float* gamma = a.gamma[g] + mt * kFT;
+    float* bias = (float*)(lds + kBgOff);
+    float* gamma = bias + kFT;
+    for (int f = threadIdx.x; f < kFT; f += G::kThr) {
+        bias[f] = a.bias[g][mt * kFT + f];
+        gamma[f] = a.gamma[g][mt * kFT + f];
+    }
+    __syncthreads();
     T* H = (T*)a.H + g * a.h_slot;
 #pragma unroll
     for (int j = 0; j < G::SN; ++j) {
@@ -184,7 +191,8 @@ __global__ __launch_bounds__(FillCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
     static_assert(G::WTM % DH == 0, "a wave's feature extent must hold whole heads");
     constexpr int HALF = DH / 2;
     constexpr int PAIR = HALF / 32;  // sub-tile distance between RoPE partners
-    __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
+    constexpr int kEpi = sizeof(T) == 2 ? kTT * kFT * 2 + kTT * 4 : 0;  // staged tile + 1/rms per token
+    __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES > kEpi ? G::LDS_BYTES : kEpi];
     int g, mt, tt;
     fill_tile(2 * a.kvw / kFT, a.tok_tiles, g, mt, tt);
     const int64_t n0 = (int64_t)tt * kTT;
@@ -220,6 +228,10 @@ __global__ __launch_bounds__(FillCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
     };
     // final values: scaled by r = 1/rms of their token; keys rotated by their position
     if constexpr (sizeof(T) == 2) {
+        // 1/rms of the tile's tokens, once per token, after the staging area
+        float* rinv = (float*)(lds + kTT * kFT * 2);
+        for (int nl = threadIdx.x; nl < kTT; nl += G::kThr) rinv[nl] = n0 + nl < a.rows ? rms_inv(n0 + nl) : 0.f;
+        __syncthreads();
         // bf16: stage the 256 tokens x 256 features tile in LDS ([token][feature], 16-byte
         // chunk c of token n in slot c ^ (n & 31)), then write whole (token, head) rows
 #pragma unroll
@@ -227,7 +239,7 @@ __global__ __launch_bounds__(FillCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
             const int nl = G::col_of(j);
             const int64_t n = n0 + nl;
             const bool ok = n < a.rows;
-            const float r = ok ? rms_inv(n) : 0.f;
+            const float r = rinv[nl];
             const float* cs_row = a.rope + (a.pos0 + a.t0 + (ok ? n : 0)) * (int64_t)DH;
 #pragma unroll
             for (int i = 0; i < G::SM; ++i) {

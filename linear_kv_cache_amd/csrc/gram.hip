@@ -177,27 +177,42 @@ __global__ __launch_bounds__(256) void k_gram_transpose(TransArgs a) {
     double cs[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) cs[i] = 0.0;
-    for (int64_t r0 = (int64_t)wave * 64; r0 < a.rows_pad; r0 += 256) {
-        u32x4 in[8], o[8];
+    // each wave takes 64-row tiles wave, wave + 4, ...; four tiles per pass keep 32 loads in
+    // flight before the first transpose
+    constexpr int U = 4;
+    for (int64_t rb0 = (int64_t)wave * 64; rb0 < a.rows_pad; rb0 += 256 * U) {
+        u32x4 in[U][8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-            in[r] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(((r0 + rb * 8 + r) * ld + c0 + cb * 8) * 2), 0, 0);
-        // o[i] = the 8 rows' values of column cb*8 + i (row 2p in the low half of dword p)
+        for (int u = 0; u < U; ++u) {
+            const int64_t r0 = rb0 + (int64_t)u * 256;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+            for (int r = 0; r < 8; ++r)
+                in[u][r] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rs, (int)(((r0 + rb * 8 + r) * ld + c0 + cb * 8) * 2), 0, 0);
+        }
 #pragma unroll
-            for (int p = 0; p < 4; ++p)
-                o[i][p] = __builtin_amdgcn_perm(in[2 * p + 1][i >> 1], in[2 * p][i >> 1], (i & 1) ? sel_hi : sel_lo);
+        for (int u = 0; u < U; ++u) {
+            const int64_t r0 = rb0 + (int64_t)u * 256;
+            if (r0 >= a.rows_pad) break;
+            // o[i] = the 8 rows' values of column cb*8 + i (row 2p in the low half of dword p)
+            u32x4 o[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            *(u32x4*)(out + (int64_t)(cb * 8 + i) * a.rows_pad + r0 + rb * 8) = o[i];
-            double s = cs[i];
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                s += (double)__uint_as_float(o[i][p] << 16);
-                s += (double)__uint_as_float(o[i][p] & 0xffff0000u);
+                for (int p = 0; p < 4; ++p)
+                    o[i][p] = __builtin_amdgcn_perm(in[u][2 * p + 1][i >> 1], in[u][2 * p][i >> 1],
+                                                    (i & 1) ? sel_hi : sel_lo);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                *(u32x4*)(out + (int64_t)(cb * 8 + i) * a.rows_pad + r0 + rb * 8) = o[i];
+                double sacc = cs[i];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    sacc += (double)__uint_as_float(o[i][p] << 16);
+                    sacc += (double)__uint_as_float(o[i][p] & 0xffff0000u);
+                }
+                cs[i] = sacc;
             }
-            cs[i] = s;
         }
     }
     // reduce over the 8 row blocks of the wave (lane bits 3..5), then over the 4 waves
@@ -385,7 +400,7 @@ rf_status rf_gram_accumulate(const rf_gram_desc* desc, void* d_state, const void
     // 32-bit byte offsets: a 256-row operand tile of the transposed piece, and a source row range
     const int64_t ld_max = std::max<int64_t>(ldx, desc->n_targets > 0 ? ldy : 0);
     const int64_t lim = (((int64_t)1 << 31) - 1);
-    cap = std::min<int64_t>(cap, std::min<int64_t>(lim / (256 * 2), lim / (ld_max * 2) - 256) / 128 * 128);
+    cap = std::min<int64_t>(cap, std::min<int64_t>(lim / (256 * 2), lim / (ld_max * 2) - 1024) / 128 * 128);
     RF_REQUIRE(cap >= 128, RF_ERR_WORKSPACE, "rf_gram_accumulate: workspace smaller than rf_gram_workspace_bytes(desc, 128)");
     for (int64_t r0 = 0; r0 < rows; r0 += cap) {
         const int64_t pr = std::min(cap, rows - r0);
