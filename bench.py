@@ -29,7 +29,7 @@ BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 # rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of this benchmark, each scaled by what the
 # counter reads for a 1 GiB device copy; profiles/pmc_traffic_llama8b-shaped_d4096_T16384.md has the
 # commands and the figures; set to None whenever k_gram_transpose or k_gram_pipe change.
-GRAM_TRAFFIC = None   # counters predate the current core; re-take them
+GRAM_TRAFFIC = (557425 + 4300414) * 2 * 1024 + (1114656 + 1224794) * 1024   # 12.34e9 B
 METRIC = "filled tokens/sec (all filled layers) + % bf16 MFMA peak; ridge-fit rows/sec"
 
 
