@@ -191,7 +191,8 @@ __global__ __launch_bounds__(FillCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
     static_assert(G::WTM % DH == 0, "a wave's feature extent must hold whole heads");
     constexpr int HALF = DH / 2;
     constexpr int PAIR = HALF / 32;  // sub-tile distance between RoPE partners
-    constexpr int kEpi = sizeof(T) == 2 ? kTT * kFT * 2 + kTT * 4 : 0;  // staged tile + 1/rms per token
+    // staged tile, then 1/rms and the cache row offset of every token of the tile
+    constexpr int kEpi = sizeof(T) == 2 ? kTT * kFT * 2 + kTT * 4 + kTT * 8 : 0;
     __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES > kEpi ? G::LDS_BYTES : kEpi];
     int g, mt, tt;
     fill_tile(2 * a.kvw / kFT, a.tok_tiles, g, mt, tt);
@@ -209,9 +210,16 @@ __global__ __launch_bounds__(FillCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
     auto rms_inv = [&](int64_t n) {
         float s = 0.f;
         if (a.n_ps % 4 == 0) {
-            for (int p = 0; p < a.n_ps; p += 4) {
-                const f32x4 v = *(const f32x4*)(ps + n * a.n_ps + p);
-                s += v[0]; s += v[1]; s += v[2]; s += v[3];
+            // four independent loads per pass, added in index order
+            for (int p = 0; p < a.n_ps; p += 16) {
+                f32x4 v[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    v[u] = p + 4 * u < a.n_ps ? *(const f32x4*)(ps + n * a.n_ps + p + 4 * u) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    s += v[u][0]; s += v[u][1]; s += v[u][2]; s += v[u][3];
+                }
             }
         } else {
             for (int p = 0; p < a.n_ps; ++p) s += ps[n * a.n_ps + p];
@@ -228,48 +236,78 @@ __global__ __launch_bounds__(FillCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
     };
     // final values: scaled by r = 1/rms of their token; keys rotated by their position
     if constexpr (sizeof(T) == 2) {
-        // 1/rms of the tile's tokens, once per token, after the staging area
+        // 1/rms and the cache row offset of the tile's tokens, once per token, after the
+        // staging area (read from LDS below, so no global load follows a cache store)
         float* rinv = (float*)(lds + kTT * kFT * 2);
-        for (int nl = threadIdx.x; nl < kTT; nl += G::kThr) rinv[nl] = n0 + nl < a.rows ? rms_inv(n0 + nl) : 0.f;
+        int64_t* rbase = (int64_t*)(lds + kTT * kFT * 2 + kTT * 4);
+        for (int nl = threadIdx.x; nl < kTT; nl += G::kThr) {
+            const bool ok = n0 + nl < a.rows;
+            rinv[nl] = ok ? rms_inv(n0 + nl) : 0.f;
+            rbase[nl] = ok ? row_base(a.t0 + n0 + nl) : -1;
+        }
         __syncthreads();
         // bf16: stage the 256 tokens x 256 features tile in LDS ([token][feature], 16-byte
         // chunk c of token n in slot c ^ (n & 31)), then write whole (token, head) rows
+        auto stage = [&](int nl, int fl, const float (&o)[4]) {
+            const int slot = ((fl >> 3) ^ (nl & 31)) << 4;
+            *(u32x2*)(lds + nl * (kFT * 2) + slot + (fl & 4) * 2) =
+                u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        };
+        if (!is_k) {
 #pragma unroll
-        for (int j = 0; j < G::SN; ++j) {
-            const int nl = G::col_of(j);
-            const int64_t n = n0 + nl;
-            const bool ok = n < a.rows;
-            const float r = rinv[nl];
-            const float* cs_row = a.rope + (a.pos0 + a.t0 + (ok ? n : 0)) * (int64_t)DH;
+            for (int j = 0; j < G::SN; ++j) {
+                const int nl = G::col_of(j);
+                const float r = rinv[nl];
 #pragma unroll
-            for (int i = 0; i < G::SM; ++i) {
+                for (int i = 0; i < G::SM; ++i)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int fl = G::row_of(i, 4 * q);
-                    const int dim = (f0 + fl) % DH;
-                    float o[4];
-                    if (!is_k) {
+                    for (int q = 0; q < 4; ++q) {
+                        float o[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) o[e] = gm.acc[i][j][4 * q + e] * r;
-                    } else {
-                        // dims [dim, dim+4) pair with dims + HALF, held in sub-tile i +- PAIR
-                        const bool low = (i * 32) % DH < HALF;
-                        const int dlo = low ? dim : dim - HALF;
-                        const f32x4 c01 = *(const f32x4*)(cs_row + 2 * dlo);
-                        const f32x4 c23 = *(const f32x4*)(cs_row + 2 * dlo + 4);
-                        const float cs[4] = {c01[0], c01[2], c23[0], c23[2]};
-                        const float sn[4] = {c01[1], c01[3], c23[1], c23[3]};
-                        const int ip = low ? (i + PAIR) % G::SM : (i + G::SM - PAIR) % G::SM;
+                        stage(nl, G::row_of(i, 4 * q), o);
+                    }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < G::SN; ++j) {
+                const int nl = G::col_of(j);
+                const int64_t n = n0 + nl;
+                const float r = rinv[nl];
+                const float* cs_row = a.rope + (a.pos0 + a.t0 + (n < a.rows ? n : 0)) * (int64_t)DH;
+                // (cos, sin) of the dims held by the low-half sub-tiles; a high-half sub-tile
+                // i holds dims + HALF of sub-tile i - PAIR and rotates with the same angles
+                f32x4 c01[G::SM][4], c23[G::SM][4];
+#pragma unroll
+                for (int i = 0; i < G::SM; ++i) {
+                    if ((i * 32) % DH >= HALF) continue;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int dlo = (f0 + G::row_of(i, 4 * q)) % DH;
+                        c01[i][q] = *(const f32x4*)(cs_row + 2 * dlo);
+                        c23[i][q] = *(const f32x4*)(cs_row + 2 * dlo + 4);
+                    }
+                }
+                // keep the loads together ahead of their uses (one wait instead of one each)
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < G::SM; ++i) {
+                    const bool low = (i * 32) % DH < HALF;
+                    const int il = low ? i : i - PAIR;            // sub-tile holding the angles
+                    const int ip = low ? i + PAIR : i - PAIR;     // RoPE partner sub-tile
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float cs[4] = {c01[il][q][0], c01[il][q][2], c23[il][q][0], c23[il][q][2]};
+                        const float sn[4] = {c01[il][q][1], c01[il][q][3], c23[il][q][1], c23[il][q][3]};
+                        float o[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const float x = gm.acc[i][j][4 * q + e] * r;
                             const float y = gm.acc[ip][j][4 * q + e] * r;
                             o[e] = low ? x * cs[e] - y * sn[e] : x * cs[e] + y * sn[e];
                         }
+                        stage(nl, G::row_of(i, 4 * q), o);
                     }
-                    const int slot = ((fl >> 3) ^ (nl & 31)) << 4;
-                    *(u32x2*)(lds + nl * (kFT * 2) + slot + (fl & 4) * 2) =
-                        u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
                 }
             }
         }
@@ -280,9 +318,7 @@ __global__ __launch_bounds__(FillCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
 #pragma unroll 2
         for (int p = 0; p < kTT / kTok; ++p) {
             const int nl = p * kTok + (threadIdx.x >> 5);
-            const int64_t n = n0 + nl;
-            if (n >= a.rows) continue;
-            const int64_t base = row_base(a.t0 + n);
+            const int64_t base = rbase[nl];     // -1: past the rows, or no cache slot
             if (base < 0) continue;
             const u32x4 v = *(const u32x4*)(lds + nl * (kFT * 2) + ((c ^ (nl & 31)) << 4));
             *(u32x4*)(pool + base + head * a.stride_head + dim) = v;

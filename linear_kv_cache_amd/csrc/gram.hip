@@ -273,21 +273,26 @@ __global__ __launch_bounds__(kPipeThreads) void k_gram_pipe(PipeGramArgs a) {
     gm.run(lds, PipeOperand{a.T + (int64_t)mt * kGT * a.rows_pad, a.rows_pad, kGT},
            PipeOperand{Bp, a.rows_pad, kGT}, (int)(a.rows_pad / G::BK));
     if (v == 0 && threadIdx.x == 0) *a.n += a.rows;
+    // Read-modify-write of the S tile, one 32-row block at a time: all 16 reads of a block are
+    // issued before its writes (a store followed by a load the compiler cannot prove disjoint
+    // would otherwise cost one full memory round trip per 16 bytes).
     float* S = is_xx ? a.Sxx : a.Syx;
 #pragma unroll
     for (int j = 0; j < G::SN; ++j) {
-        const int64_t srow = srow0 + G::col_of(j);
+        float* srow = S + (srow0 + G::col_of(j)) * a.d + (int64_t)mt * kGT;
+        f32x4 x[G::SM][4];
 #pragma unroll
-        for (int i = 0; i < G::SM; ++i) {
+        for (int i = 0; i < G::SM; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) x[i][q] = *(const f32x4*)(srow + G::row_of(i, 4 * q));
+#pragma unroll
+        for (int i = 0; i < G::SM; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                f32x4* p = (f32x4*)(S + srow * a.d + (int64_t)mt * kGT + G::row_of(i, 4 * q));
-                f32x4 x = *p;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] += gm.acc[i][j][4 * q + e];
-                *p = x;
+                for (int e = 0; e < 4; ++e) x[i][q][e] += gm.acc[i][j][4 * q + e];
+                *(f32x4*)(srow + G::row_of(i, 4 * q)) = x[i][q];
             }
-        }
     }
 }
 

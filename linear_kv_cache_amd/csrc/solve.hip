@@ -119,6 +119,20 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, 
             __syncthreads();
         }
     }
+    // all reads of C before any write: a store followed by a load the compiler cannot prove
+    // disjoint would otherwise cost a full memory round trip per element
+    double cv[4][4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t n = n0 + wn * 64 + j * 16 + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t m = m0 + wm * 64 + i * 16 + 4 * r + (lane >> 4);
+                cv[i][j][r] = (beta != 0.0 && m < M && n < N) ? C[m * ldc + n] : 0.0;
+            }
+        }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -129,7 +143,7 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, 
                 const int64_t m = m0 + wm * 64 + i * 16 + 4 * r + (lane >> 4);
                 if (m < M && n < N) {
                     double v = alpha * acc[i][j][r];
-                    if (beta != 0.0) v += beta * C[m * ldc + n];
+                    if (beta != 0.0) v += beta * cv[i][j][r];
                     C[m * ldc + n] = v;
                 }
             }
@@ -181,6 +195,14 @@ __global__ __launch_bounds__(256) void k_dgemm_valu(int64_t M, int64_t N, int64_
         }
         __syncthreads();
     }
+    double cv[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int64_t gm = m0 + ty + 16 * r, gn = n0 + tx + 16 * c;
+            cv[r][c] = (beta != 0.0 && gm < M && gn < N) ? C[gm * ldc + gn] : 0.0;
+        }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int64_t gm = m0 + ty + 16 * r;
@@ -190,7 +212,7 @@ __global__ __launch_bounds__(256) void k_dgemm_valu(int64_t M, int64_t N, int64_
             const int64_t gn = n0 + tx + 16 * c;
             if (gn >= N) continue;
             double v = alpha * acc[r][c];
-            if (beta != 0.0) v += beta * C[gm * ldc + gn];
+            if (beta != 0.0) v += beta * cv[r][c];
             C[gm * ldc + gn] = v;
         }
     }
