@@ -32,61 +32,80 @@ constexpr int kMaxSel = 64;
 // element r of lane l is C[4 r + l / 16][l % 16], as measured on gfx950).  k-slices of 16 are staged in LDS as
 // [k][m] and [k][n], double-buffered; out-of-range rows and columns read as zero.
 typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
 
 // Structure flags: kLowerOnly skips tiles wholly above the diagonal (the caller reads only the
 // lower triangle of C); kUpperOperands means A and B are upper triangular (A[m][k] = B[n][k] = 0
-// for k < m, k < n), so a tile's k-loop starts at max(m0, n0).
-enum { kFull = 0, kLowerOnly = 1, kUpperOperands = 2 };
+// for k < m, k < n), so a tile's k-loop starts at max(m0, n0); kUpperA means only A is upper
+// triangular (the k-loop starts at m0); kUpperB means B, given as [K][N], is upper triangular
+// (B[k][n] = 0 for k > n: the k-loop ends at n0 + BN).
+// The flags are bits and combine.
+// Batched launches (gridDim.z > 1) offset A, B and C by blockIdx.z times sA, sB, sC elements.
+enum { kFull = 0, kLowerOnly = 1, kUpperOperands = 2, kUpperA = 4, kUpperB = 8 };
 
 template <bool BT>
 __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, double alpha, const double* A,
                                                int64_t lda, const double* B, int64_t ldb, double beta, double* C,
-                                               int64_t ldc, int structure) {
-    constexpr int BM = 128, BN = 128, BK = 16, PAD = 2;
+                                               int64_t ldc, int structure, int64_t sA, int64_t sB, int64_t sC) {
+    constexpr int BM = 128, BN = 128, BK = 32, PAD = 2;
+    A += (int64_t)blockIdx.z * sA;
+    B += (int64_t)blockIdx.z * sB;
+    C += (int64_t)blockIdx.z * sC;
     __shared__ double As[2][BK][BM + PAD];
     __shared__ double Bs[2][BK][BN + PAD];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t m0 = (int64_t)blockIdx.x * BM, n0 = (int64_t)blockIdx.y * BN;
-    if (structure == kLowerOnly && n0 > m0 + BM - 1) return;
-    const int64_t kbeg = structure == kUpperOperands ? (m0 > n0 ? m0 : n0) / BK * BK : 0;
-    // loaders: a K-contiguous operand gives each thread 8 consecutive k of one row; an
-    // N-contiguous operand gives 8 consecutive n of one k-row
-    double ra[8], rb[8];
+    if ((structure & kLowerOnly) && n0 > m0 + BM - 1) return;
+    int64_t kbeg = 0, kend = K;
+    if (structure & kUpperOperands) kbeg = (m0 > n0 ? m0 : n0) / BK * BK;
+    if (structure & kUpperA) kbeg = m0 / BK * BK;
+    if ((structure & kUpperB) && n0 + BN < K) kend = n0 + BN;
+    // loaders: a K-contiguous operand gives each thread 16 consecutive k of one row; an
+    // N-contiguous operand gives 16 consecutive n of one k-row.  A run wholly in range and
+    // 16-byte aligned is read as eight 16-byte loads, otherwise element by element.
+    double ra[16], rb[16];
+    auto run16 = [&](const double* p, bool whole, int valid, double (&r)[16]) {
+        if (whole && ((uintptr_t)p & 15) == 0) {
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+                const f64x2 v = *(const f64x2*)(p + e);
+                r[e] = v[0];
+                r[e + 1] = v[1];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) r[e] = e < valid ? p[e] : 0.0;
+        }
+    };
     auto load = [&](int64_t k0) {
         {
             const int64_t m = m0 + (t >> 1);
-            const int kk = (t & 1) * 8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int64_t k = k0 + kk + e;
-                ra[e] = (m < M && k < K) ? A[m * lda + k] : 0.0;
-            }
+            const int64_t k = k0 + (t & 1) * 16;
+            const int valid = m < M ? (int)(K - k < 16 ? (K - k > 0 ? K - k : 0) : 16) : 0;
+            run16(A + (m < M ? m : 0) * lda + (valid > 0 ? k : 0), valid == 16, valid, ra);
         }
         if (BT) {
             const int64_t n = n0 + (t >> 1);
-            const int kk = (t & 1) * 8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int64_t k = k0 + kk + e;
-                rb[e] = (n < N && k < K) ? B[n * ldb + k] : 0.0;
-            }
+            const int64_t k = k0 + (t & 1) * 16;
+            const int valid = n < N ? (int)(K - k < 16 ? (K - k > 0 ? K - k : 0) : 16) : 0;
+            run16(B + (n < N ? n : 0) * ldb + (valid > 0 ? k : 0), valid == 16, valid, rb);
         } else {
-            const int64_t k = k0 + (t >> 4);
-            const int64_t nn = n0 + (t & 15) * 8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) rb[e] = (k < K && nn + e < N) ? B[k * ldb + nn + e] : 0.0;
+            const int64_t k = k0 + (t >> 3);
+            const int64_t nn = n0 + (t & 7) * 16;
+            const int valid = k < K ? (int)(N - nn < 16 ? (N - nn > 0 ? N - nn : 0) : 16) : 0;
+            run16(B + (k < K ? k : 0) * ldb + (valid > 0 ? nn : 0), valid == 16, valid, rb);
         }
     };
     auto store = [&](int buf) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) As[buf][(t & 1) * 8 + e][t >> 1] = ra[e];
+        for (int e = 0; e < 16; ++e) As[buf][(t & 1) * 16 + e][t >> 1] = ra[e];
         if (BT) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) Bs[buf][(t & 1) * 8 + e][t >> 1] = rb[e];
+            for (int e = 0; e < 16; ++e) Bs[buf][(t & 1) * 16 + e][t >> 1] = rb[e];
         } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) Bs[buf][t >> 4][(t & 15) * 8 + e] = rb[e];
+            for (int e = 0; e < 16; ++e) Bs[buf][t >> 3][(t & 7) * 16 + e] = rb[e];
         }
     };
     f64x4 acc[4][4];
@@ -94,7 +113,7 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, 
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
-    const int nk = K > kbeg ? (int)((K - kbeg + BK - 1) / BK) : 0;
+    const int nk = kend > kbeg ? (int)((kend - kbeg + BK - 1) / BK) : 0;
     if (nk > 0) {
         load(kbeg);
         store(0);
@@ -226,10 +245,15 @@ __global__ void k_copy2d(const double* src, int64_t lds, double* dst, int64_t ld
     }
 }
 
-__global__ void k_identity(double* R, int64_t d) {
+// Z = 0 except its diagonal 64 x 64 blocks, which are the transposed inverses of L's diagonal
+// blocks (Dinv holds L_JJ^-1 row-major): Z_JJ = (L_JJ^T)^-1.
+__global__ void k_zdiag(const double* Dinv, int64_t d, double* Z) {
     const int64_t n = d * d;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-        R[i] = (i / d == i % d) ? 1.0 : 0.0;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / d, c = i % d;
+        const int64_t J = r / kNB;
+        Z[i] = c / kNB == J ? Dinv[(J * kNB + c % kNB) * kNB + r % kNB] : 0.0;
+    }
 }
 
 __global__ void k_zero_int(int32_t* p) { *p = 0; }
@@ -390,12 +414,21 @@ __global__ void k_diag_sqrt(const double* A, int64_t d, double* dg) {
 }
 
 // Equilibrated inverse, split: row j of Bq = [hi | lo | hi] of Ainv[j][i] dg[i] dg[j].
-__global__ void k_split_inverse(const double* Ainv, const double* dg, int64_t d, bf16_t* Bq) {
-    const int64_t n = d * d;
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t j = idx / d, i = idx % d;
+// One 64 x 64 tile of A^-1 per work-group.  Only the lower triangle of A^-1 (by 64-blocks) is
+// formed; a tile above the diagonal reads its mirror image (coalesced) and transposes it
+// through LDS.
+__global__ __launch_bounds__(256) void k_split_inverse(const double* Ainv, const double* dg, int64_t d, bf16_t* Bq) {
+    __shared__ double tile[64][65];
+    const int64_t ib = blockIdx.x, jb = blockIdx.y;   // element (j, i): Bq row j, column i
+    const bool mirror = ib > jb;
+    const int64_t r0 = (mirror ? ib : jb) * 64, c0 = (mirror ? jb : ib) * 64;
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) tile[e / 64][e % 64] = Ainv[(r0 + e / 64) * d + c0 + e % 64];
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+        const int jl = e / 64, il = e % 64;
+        const int64_t j = jb * 64 + jl, i = ib * 64 + il;
         bf16_t hi, lo;
-        split_bf16(Ainv[idx] * dg[i] * dg[j], hi, lo);
+        split_bf16((mirror ? tile[il][jl] : tile[jl][il]) * dg[i] * dg[j], hi, lo);
         bf16_t* row = Bq + j * 3 * d;
         row[i] = hi;
         row[d + i] = lo;
@@ -515,7 +548,7 @@ static rf_status dgemm(hipStream_t s, int64_t M, int64_t N, int64_t K, double al
     if (M <= 0 || N <= 0) return RF_OK;
     if ((M >= 512 && N >= 512) || structure != kFull)
         hipLaunchKernelGGL(k_dgemm<BT>, dim3((unsigned)ceil_div(M, 128), (unsigned)ceil_div(N, 128)), dim3(256), 0, s,
-                           M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, structure);
+                           M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, structure, (int64_t)0, (int64_t)0, (int64_t)0);
     else
         hipLaunchKernelGGL(k_dgemm_valu<BT>, dim3((unsigned)ceil_div(M, 64), (unsigned)ceil_div(N, 64)), dim3(256), 0,
                            s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
@@ -528,20 +561,28 @@ static rf_status dgemm(hipStream_t s, int64_t M, int64_t N, int64_t K, double al
         if (_st != RF_OK) return _st;     \
     } while (0)
 
-// Z = L^-T by the forward solve Z L^T = I, one 64-column block at a time (L in C's lower
-// triangle, its diagonal-block inverses in Dinv).  Z is upper triangular, so block column J
-// has nonzero rows only below (J + 1) * 64 and each step touches just those rows.
+// Z = L^-T = R^-1 with R = L^T upper triangular, by recursive doubling over block size b =
+// 64, 128, ..., d/2: for every pair of adjacent diagonal b-blocks the inverse of the 2b-block is
+//   [[R11, R12], [0, R22]]^-1 = [[Z11, -Z11 R12 Z22], [0, Z22]],   R12 = L21^T,
+// two batched products per level (T = Z11 L21^T, then Z12 = -T Z22) instead of one dependent
+// step per 64 columns.  The diagonal 64-blocks come from the factorisation (Dinv); T lives in
+// the split-operand buffer, which is written only after the inverse is complete.
 static rf_status inverse_factor(hipStream_t s, const SolveWs& w, int64_t d, double* Z) {
-    const int nblk = (int)(d / kNB);
-    for (int J = 0; J < nblk; ++J) {
-        const int64_t c0 = (int64_t)J * kNB;
-        const int64_t rows = c0 + kNB;
-        RF_TRY(dgemm<true>(s, rows, kNB, kNB, 1.0, Z + c0, d, w.Dinv + c0 * kNB, kNB, 0.0, w.P, kNB));
-        hipLaunchKernelGGL(k_copy2d, dim3(grid_for(rows * kNB)), dim3(256), 0, s, w.P, (int64_t)kNB, Z + c0, d, rows,
-                           (int64_t)kNB);
-        RF_TRY(check_launch("rf_solve: copy"));
-        const int64_t rem = d - c0 - kNB;
-        RF_TRY(dgemm<true>(s, rows, rem, kNB, -1.0, w.P, kNB, w.C + (c0 + kNB) * d + c0, d, 1.0, Z + c0 + kNB, d));
+    hipLaunchKernelGGL(k_zdiag, dim3(grid_for(d * d)), dim3(256), 0, s, w.Dinv, d, Z);
+    RF_TRY(check_launch("rf_solve: inverse diagonal"));
+    double* T = (double*)w.Bq;
+    for (int64_t b = kNB; b < d; b *= 2) {
+        const unsigned pairs = (unsigned)(d / (2 * b));
+        const int64_t sp = 2 * b * (d + 1);   // from one pair's diagonal block to the next
+        const dim3 grid((unsigned)ceil_div(b, 128), (unsigned)ceil_div(b, 128), pairs);
+        // T_p = Z11 L21^T  (Z11 upper triangular)
+        hipLaunchKernelGGL(k_dgemm<true>, grid, dim3(256), 0, s, b, b, b, 1.0, (const double*)Z, d,
+                           (const double*)(w.C + b * d), d, 0.0, T, b, (int)kUpperA, sp, sp, b * b);
+        RF_TRY(check_launch("rf_solve: inverse T"));
+        // Z12 = -T_p Z22  (Z22 upper triangular, [K][N])
+        hipLaunchKernelGGL(k_dgemm<false>, grid, dim3(256), 0, s, b, b, b, -1.0, (const double*)T, b,
+                           (const double*)(Z + b * d + b), d, 0.0, Z + b, d, (int)kUpperB, b * b, sp, sp);
+        RF_TRY(check_launch("rf_solve: inverse Z12"));
     }
     return RF_OK;
 }
@@ -612,14 +653,13 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, double lambda,
         RF_TRY(check_launch("rf_solve: copy"));
     }
     // A^-1 = Z Z^T with Z = L^-T (the factor is no longer needed afterwards: A^-1 overwrites it)
-    hipLaunchKernelGGL(k_identity, dim3(grid_for(d * d)), dim3(256), 0, s, w.Cinv, d);
-    RF_TRY(check_launch("rf_solve: identity"));
     RF_TRY(inverse_factor(s, w, d, w.Cinv));
-    RF_TRY(dgemm<true>(s, d, d, d, 1.0, w.Cinv, d, w.Cinv, d, 0.0, w.C, d, kUpperOperands));
+    // lower triangle only (by 128-blocks): A^-1 is symmetric and its one reader mirrors it
+    RF_TRY(dgemm<true>(s, d, d, d, 1.0, w.Cinv, d, w.Cinv, d, 0.0, w.C, d, kUpperOperands | kLowerOnly));
     if (n_sel == 0) return RF_OK;
 
     // equilibrated split operands, then W on the MFMA pipes
-    hipLaunchKernelGGL(k_split_inverse, dim3(grid_for(d * d)), dim3(256), 0, s, w.C, w.dg, d, w.Bq);
+    hipLaunchKernelGGL(k_split_inverse, dim3((unsigned)(d / 64), (unsigned)(d / 64)), dim3(256), 0, s, w.C, w.dg, d, w.Bq);
     RF_TRY(check_launch("rf_solve: split inverse"));
     const int64_t rows = (int64_t)n_sel * d;
     CrossArgs ca{};
