@@ -341,70 +341,54 @@ __global__ void k_centre_split(CrossArgs a) {
 }
 
 // Factor the diagonal block J (already updated by all earlier panels) in place into L_JJ and
-// write L_JJ^-1 into Dinv.  info receives the 1-based index of the first non-positive pivot.
-// The block sits in LDS; 256 threads eliminate one column per step, then form L^-1 one row at
-// a time by forward substitution, four lanes per column splitting each dot product (reduced by
-// a fixed shuffle tree).
-__global__ __launch_bounds__(256) void k_chol_diag(double* C, int64_t d, int J, double* Dinv, int32_t* info) {
-    __shared__ double a[kNB][kNB + 1];
-    __shared__ double x[kNB][kNB + 1];
-    __shared__ double rinv[kNB];   // 1 / L[j][j]
-    const int t = threadIdx.x;
+// write L_JJ^-1 into Dinv.  info receives the 1-based index of the first non-positive pivot
+// (unless an earlier block already reported one).
+// One wave, no barriers: lane i keeps row i of the block in registers and the right-looking
+// elimination broadcasts each multiplier L[k][j] from lane k (v_readlane); entries above the
+// diagonal are never read for the lower triangle and are written as zeros.  Then lane c keeps
+// column c of L^-1 and forward-substitutes, X[r][c] = (delta_rc - sum_{k<r} L[r][k] X[k][c]) /
+// L[r][r], with L[r][k] broadcast from lane r.
+__device__ inline double bcast_lane(double v, int lane) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, lane);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__global__ __launch_bounds__(64) void k_chol_diag(double* C, int64_t d, int J, double* Dinv, int32_t* info) {
+    const int i = threadIdx.x;
     const int64_t off = (int64_t)J * kNB;
-    for (int idx = t; idx < kNB * kNB; idx += 256) {
-        const int i = idx / kNB, k = idx % kNB;
-        a[i][k] = C[(off + i) * d + off + k];
-    }
-    bool failed = t == 0 && *info != 0;  // an earlier block already failed: keep its pivot
-    __syncthreads();
+    double a[kNB];
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) a[k] = C[(off + i) * d + off + k];
+    const bool prior = *info != 0;
+    int32_t fail = 0;
+    double rinv = 0.0;   // lane i: 1 / L[i][i]
+#pragma unroll
     for (int j = 0; j < kNB; ++j) {
-        if (t == 0) {
-            const double p = a[j][j];
-            if (!(p > 0.0) && !failed) {
-                *info = (int32_t)(off + j + 1);
-                failed = true;
-            }
-            const double r = sqrt(p);
-            a[j][j] = r;
-            rinv[j] = 1.0 / r;
-        }
-        __syncthreads();
-        if (t > j && t < kNB) a[t][j] *= rinv[j];
-        __syncthreads();
-        // trailing lower triangle: rows i > j, columns j < k <= i (thread: column t & 63, every
-        // fourth row)
-        {
-            const int k = t & (kNB - 1);
-            if (k > j) {
-                const double lkj = a[k][j];
-                for (int i = k + ((t >> 6) - k % 4 + 4) % 4; i < kNB; i += 4) a[i][k] -= a[i][j] * lkj;
-            }
-        }
-        __syncthreads();
+        const double p = bcast_lane(a[j], j);
+        if (!(p > 0.0) && fail == 0) fail = (int32_t)(off + j + 1);
+        const double r = sqrt(p);
+        const double ri = 1.0 / r;
+        if (i == j) rinv = ri;
+        a[j] = i > j ? a[j] * ri : (i == j ? r : a[j]);
+#pragma unroll
+        for (int k = j + 1; k < kNB; ++k) a[k] -= a[j] * bcast_lane(a[j], k);
     }
-    // column c of X = L^-1:  X[r][c] = (delta_rc - sum_{k<r} L[r][k] X[k][c]) / L[r][r];
-    // lane group (4 lanes) per column, lane q of the group takes k = q, q + 4, ...
-    const int c = t >> 2, q = t & 3;
+    double x[kNB];
+#pragma unroll
     for (int r = 0; r < kNB; ++r) {
-        double s0 = 0.0, s1 = 0.0;
-        int k = q;
-        for (; k + 4 < r; k += 8) {
-            s0 += a[r][k] * x[k][c];
-            s1 += a[r][k + 4] * x[k + 4][c];
-        }
-        if (k < r) s0 += a[r][k] * x[k][c];
-        double sum = s0 + s1;
-        sum += __shfl_xor(sum, 1);
-        sum += __shfl_xor(sum, 2);
-        if (q == 0) x[r][c] = ((r == c ? 1.0 : 0.0) - sum) * rinv[r];
-        __syncthreads();
+        double sum = r == i ? 1.0 : 0.0;
+#pragma unroll
+        for (int k = 0; k < r; ++k) sum -= bcast_lane(a[k], r) * x[k];
+        x[r] = sum * bcast_lane(rinv, r);
     }
+    if (i == 0 && !prior && fail != 0) *info = fail;
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) C[(off + i) * d + off + k] = k <= i ? a[k] : 0.0;
     double* D = Dinv + (int64_t)J * kNB * kNB;
-    for (int idx = t; idx < kNB * kNB; idx += 256) {
-        const int i = idx / kNB, k = idx % kNB;
-        C[(off + i) * d + off + k] = k <= i ? a[i][k] : 0.0;
-        D[idx] = x[i][k];
-    }
+#pragma unroll
+    for (int r = 0; r < kNB; ++r) D[r * kNB + i] = x[r];
 }
 
 // dg[i] = sqrt(A[i][i]) before the factorisation overwrites the diagonal.
@@ -640,7 +624,7 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, double lambda,
     const int nblk = (int)(d / kNB);
     for (int J = 0; J < nblk; ++J) {
         const int64_t c0 = (int64_t)J * kNB;
-        hipLaunchKernelGGL(k_chol_diag, dim3(1), dim3(256), 0, s, w.C, d, J, w.Dinv, d_info);
+        hipLaunchKernelGGL(k_chol_diag, dim3(1), dim3(64), 0, s, w.C, d, J, w.Dinv, d_info);
         RF_TRY(check_launch("rf_solve: potrf"));
         const int64_t rem = d - c0 - kNB;
         if (rem <= 0) continue;
