@@ -545,28 +545,36 @@ static rf_status dgemm(hipStream_t s, int64_t M, int64_t N, int64_t K, double al
         if (_st != RF_OK) return _st;     \
     } while (0)
 
-// Z = L^-T = R^-1 with R = L^T upper triangular, by recursive doubling over block size b =
-// 64, 128, ..., d/2: for every pair of adjacent diagonal b-blocks the inverse of the 2b-block is
+// Z = L^-T = R^-1 with R = L^T upper triangular, by recursive doubling over unit size b =
+// 64, 128, ...: at level b the rows split into units of b (the last one possibly shorter), and
+// every pair of adjacent units (2p, 2p+1) is joined by
 //   [[R11, R12], [0, R22]]^-1 = [[Z11, -Z11 R12 Z22], [0, Z22]],   R12 = L21^T,
-// two batched products per level (T = Z11 L21^T, then Z12 = -T Z22) instead of one dependent
-// step per 64 columns.  The diagonal 64-blocks come from the factorisation (Dinv); T lives in
-// the split-operand buffer, which is written only after the inverse is complete.
+// i.e. two products, T = Z11 L21^T and Z12 = -T Z22, batched over the pairs of whole units,
+// with one more unbatched pair when the second unit of the last pair is short.  An unpaired
+// last unit is carried to the next level unchanged.  Each unit is complete when it is used
+// (by induction over the levels), and the number of dependent levels is log2(d / 64) rounded
+// up, instead of one step per 64 columns.  The diagonal 64-blocks come from the factorisation
+// (Dinv); T lives in the split-operand buffer, which is written only after the inverse.
 static rf_status inverse_factor(hipStream_t s, const SolveWs& w, int64_t d, double* Z) {
     hipLaunchKernelGGL(k_zdiag, dim3(grid_for(d * d)), dim3(256), 0, s, w.Dinv, d, Z);
     RF_TRY(check_launch("rf_solve: inverse diagonal"));
     double* T = (double*)w.Bq;
-    for (int64_t b = kNB; b < d; b *= 2) {
-        const unsigned pairs = (unsigned)(d / (2 * b));
-        const int64_t sp = 2 * b * (d + 1);   // from one pair's diagonal block to the next
-        const dim3 grid((unsigned)ceil_div(b, 128), (unsigned)ceil_div(b, 128), pairs);
-        // T_p = Z11 L21^T  (Z11 upper triangular)
-        hipLaunchKernelGGL(k_dgemm<true>, grid, dim3(256), 0, s, b, b, b, 1.0, (const double*)Z, d,
-                           (const double*)(w.C + b * d), d, 0.0, T, b, (int)kUpperA, sp, sp, b * b);
+    auto join = [&](int64_t o, int64_t b, int64_t n2, unsigned batch, int64_t sp) -> rf_status {
+        // units [o, o + b) and [o + b, o + b + n2), repeated ``batch`` times every sp elements
+        const dim3 g1((unsigned)ceil_div(b, 128), (unsigned)ceil_div(n2, 128), batch);
+        hipLaunchKernelGGL(k_dgemm<true>, g1, dim3(256), 0, s, b, n2, b, 1.0, (const double*)(Z + o * d + o), d,
+                           (const double*)(w.C + (o + b) * d + o), d, 0.0, T, n2, (int)kUpperA, sp, sp, b * n2);
         RF_TRY(check_launch("rf_solve: inverse T"));
-        // Z12 = -T_p Z22  (Z22 upper triangular, [K][N])
-        hipLaunchKernelGGL(k_dgemm<false>, grid, dim3(256), 0, s, b, b, b, -1.0, (const double*)T, b,
-                           (const double*)(Z + b * d + b), d, 0.0, Z + b, d, (int)kUpperB, b * b, sp, sp);
-        RF_TRY(check_launch("rf_solve: inverse Z12"));
+        hipLaunchKernelGGL(k_dgemm<false>, g1, dim3(256), 0, s, b, n2, n2, -1.0, (const double*)T, n2,
+                           (const double*)(Z + (o + b) * d + o + b), d, 0.0, Z + o * d + o + b, d, (int)kUpperB,
+                           b * n2, sp, sp);
+        return check_launch("rf_solve: inverse Z12");
+    };
+    for (int64_t b = kNB; b < d; b *= 2) {
+        const int64_t full = d / (2 * b);                 // pairs of whole units
+        if (full > 0) RF_TRY(join(0, b, b, (unsigned)full, 2 * b * (d + 1)));
+        const int64_t o = full * 2 * b;                   // a last pair with a short second unit
+        if (o + b < d) RF_TRY(join(o, b, d - o - b, 1u, 0));
     }
     return RF_OK;
 }

@@ -60,6 +60,19 @@ def test_fit_bf16_ragged_rows_and_relative_lambda():
     assert res_r["info"] == 0 and max(ew) <= W_TOL and max(eb) <= W_TOL
 
 
+def test_fit_bf16_widths_not_a_power_of_two_blocks():
+    # d / 64 = 12 and 20 diagonal blocks: the triangular inverse joins units of unequal size
+    # and carries unpaired ones between levels
+    for d in (768, 1280):
+        cfg = synth.scaled(synth.C2, name=f"fit-bf16-d{d}", d=d, n_layers=4, split=2)
+        case = FitCase(cfg, 3000, [2000, 1000], 1e-1)
+        res = run_fit_case(case)
+        ew, eb = fit_errors(res, case)
+        log(f"[fit] bf16 d{d} W_err={np.max(ew):.3e} b_err={np.max(eb):.3e}")
+        assert res["info"] == 0
+        assert max(ew) <= W_TOL and max(eb) <= W_TOL
+
+
 def test_fit_not_spd_reports_pivot():
     case = FitCase(synth.C1, 1024, [1024], 0.0, zero_column=77, n_targets=1)
     res = run_fit_case(case)
