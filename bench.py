@@ -28,8 +28,8 @@ BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 # HBM bytes of one rf_gram_accumulate call (8192 rows, d=4096, 16 targets), from two
 # rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of this benchmark, each scaled by what the
 # counter reads for a 1 GiB device copy; profiles/pmc_traffic_llama8b-shaped_d4096_T16384.md has the
-# commands and the figures; set to None whenever k_gram_transpose or k_gram_pipe change.
-GRAM_TRAFFIC = (557425 + 4300414) * 2 * 1024 + (1114656 + 1224794) * 1024   # 12.34e9 B
+# commands and the figures; set to None whenever k_gram_colsum or k_gram_pipe change.
+GRAM_TRAFFIC = None   # counters predate the in-place products (k_gram_colsum + k_gram_pipe); re-take them
 METRIC = "filled tokens/sec (all filled layers) + % bf16 MFMA peak; ridge-fit rows/sec"
 
 
@@ -121,7 +121,7 @@ def main():
     fw = rf.FillWeights(d, cfg.n_kv_heads, cfg.head_dim, cfg.rms_eps, cfg.torch_dtype, [W_lp[i] for i in range(L)],
                         [b[i] for i in range(L)], [g for (_, _, g) in kv], [k for (k, _, _) in kv],
                         [v for (_, v, _) in kv])
-    filler = Filler(fw, cfg.rope_base, T, T, dev)
+    filler = Filler(fw, cfg.rope_base, T, T, dev, ws_slots=8)   # 8 layers per fill launch (1 GiB of H)
     lam = cfg.lambdas[0]
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -141,7 +141,7 @@ def main():
         for c in range(n_chunks):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            rf.rf_gram_accumulate(state.desc, state.buf, Xc[c], Yc[c], ws=state.ws, stream=stream)
+            rf.rf_gram_accumulate(state.desc, state.buf, Xc[c], Yc[c], stream=stream)
             e1.record(stream)
             gram_ev.append((e0, e1))
         ev["gram"].record(stream)
@@ -204,7 +204,7 @@ def main():
                 "flop_per_row": cfg.fit_flop_per_row()},
         "roofline": {"bound": "mfma",
                      "kernel": f"rf_gram_accumulate of {cfg.calib_chunk} rows x {L} targets "
-                               f"(k_gram_transpose + k_gram_pipe)",
+                               f"(k_gram_colsum + k_gram_pipe)",
                      "achieved": round(gram_tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gram_tflops / BF16_PEAK_TFLOPS, 4),
                      "traffic": GRAM_TRAFFIC if args.config == "C2" else None,

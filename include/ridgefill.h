@@ -95,25 +95,17 @@ size_t rf_gram_state_bytes(const rf_gram_desc* desc);
 /* Zero the state (n = 0, all sums 0).  d_state: rf_gram_state_bytes() bytes, 256-B aligned. */
 rf_status rf_gram_init(const rf_gram_desc* desc, void* d_state, void* stream);
 
-/* Host only.  Workspace bytes rf_gram_accumulate needs to take a chunk of up to max_rows
- * rows in one piece (0 for fp32 states, which need none; 0 for a bad descriptor).  bf16
- * chunks are transposed into the workspace ((n_targets + 1) * d * round_up(rows, 128) bf16
- * values) so that both operands of the products read rows contiguously. */
-size_t rf_gram_workspace_bytes(const rf_gram_desc* desc, int64_t max_rows);
-
 /* Add one chunk of ``rows`` calibration rows to the state.
  *  d_X : [rows][ldx] split-layer rows, dtype desc->dtype, ldx >= d, 16-B aligned rows
  *  d_Y : host array of n_targets device pointers, each [rows][ldy] target-layer input rows
- *  rows: >= 0 (0 is a no-op).  Any row count is allowed; ragged tails are handled.
- *  d_ws: bf16: workspace of ws_bytes >= rf_gram_workspace_bytes(desc, 128), 256-B aligned;
- *        a chunk larger than the workspace holds is taken in several pieces.  fp32: unused
- *        (may be NULL).  Its contents are scratch, valid only while the call's work runs.
- * Results are deterministic: the same chunks in the same pieces and order give bit-identical
- * sums. */
+ *  rows: >= 0 (0 is a no-op).  Any row count is allowed; ragged tails are handled.  The rows
+ *        are read in place (no workspace); a chunk whose byte offsets would pass 2^31 is
+ *        taken in several pieces.
+ * Results are deterministic: the same chunks in the same order give bit-identical sums. */
 rf_status rf_gram_accumulate(const rf_gram_desc* desc, void* d_state,
                              const void* d_X, int64_t ldx,
                              const void* const* d_Y, int64_t ldy,
-                             int64_t rows, void* d_ws, size_t ws_bytes, void* stream);
+                             int64_t rows, void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * Ridge fit, part 2: the closed-form solve.

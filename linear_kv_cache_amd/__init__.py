@@ -70,9 +70,8 @@ _sig = {
     "rf_gram_state_layout": (C.c_int, [C.POINTER(rf_gram_desc), C.POINTER(rf_gram_layout_t)]),
     "rf_gram_state_bytes": (C.c_size_t, [C.POINTER(rf_gram_desc)]),
     "rf_gram_init": (C.c_int, [C.POINTER(rf_gram_desc), _P, _P]),
-    "rf_gram_workspace_bytes": (C.c_size_t, [C.POINTER(rf_gram_desc), C.c_int64]),
     "rf_gram_accumulate": (C.c_int, [C.POINTER(rf_gram_desc), _P, _P, C.c_int64, C.POINTER(_P), C.c_int64,
-                                     C.c_int64, _P, C.c_size_t, _P]),
+                                     C.c_int64, _P]),
     "rf_solve_workspace_bytes": (C.c_size_t, [C.POINTER(rf_gram_desc), C.c_int32]),
     "rf_solve": (C.c_int, [C.POINTER(rf_gram_desc), _P, C.c_double, C.c_int, C.POINTER(C.c_int32), C.c_int32,
                            _P, _P, _P, _P, _P, C.c_size_t, _P]),
@@ -156,22 +155,15 @@ def rf_gram_init(desc: rf_gram_desc, state, stream=None):
     _check(_lib.rf_gram_init(C.byref(desc), _ptr(state), _stream(stream)))
 
 
-def rf_gram_workspace_bytes(desc: rf_gram_desc, max_rows: int) -> int:
-    return int(_lib.rf_gram_workspace_bytes(C.byref(desc), max_rows))
-
-
-def rf_gram_accumulate(desc: rf_gram_desc, state, X, Ys: Sequence, rows: Optional[int] = None, ws=None,
-                       stream=None):
-    """X: [rows, >=d] tensor (row stride = ldx); Ys: n_targets tensors [rows, >=d] sharing one row stride;
-    ws: workspace tensor (bf16 states) or None (fp32 states)."""
+def rf_gram_accumulate(desc: rf_gram_desc, state, X, Ys: Sequence, rows: Optional[int] = None, stream=None):
+    """X: [rows, >=d] tensor (row stride = ldx); Ys: n_targets tensors [rows, >=d] sharing one row stride."""
     rows = X.shape[0] if rows is None else rows
     ldy = Ys[0].stride(0) if len(Ys) else desc.d
     if any(Y.stride(0) != ldy for Y in Ys):
         raise ValueError("all Y tensors must share one row stride")
     ys = _ptr_array(Ys)
-    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.rf_gram_accumulate(C.byref(desc), _ptr(state), _ptr(X), X.stride(0), ys, ldy, rows,
-                                   _ptr(ws) if ws is not None else None, ws_bytes, _stream(stream)))
+                                   _stream(stream)))
 
 
 def rf_solve_workspace_bytes(desc: rf_gram_desc, n_sel: int) -> int:

@@ -2,17 +2,13 @@
 // "Method" step 2: the maps are fitted in closed form from one pass over calibration text).
 //
 // bf16 chunks take two launches:
-//   k_gram_transpose : X and every Y_l, [rows][d], are written transposed ([d][rows_pad],
-//                      rows zero-padded to a multiple of 128) into the workspace, so that the
-//                      reduction over rows is contiguous for both operands of the products.
-//                      8 x 8 blocks are transposed in registers.  Each work-group owns 64
-//                      columns over all rows, so it also forms their exact fp64 column sums
-//                      (bf16 values have 8-bit significands: fp64 sums are exact and
-//                      independent of order) and adds them once.
+//   k_gram_colsum    : exact fp64 column sums of X and every Y_l (bf16 values have 8-bit
+//                      significands; each column is summed in one fixed order).
 //   k_gram_pipe      : S_yx tiles (Y_l^T X) and the S_xx upper triangle (X^T X, 256 x 256
-//                      tiles) on the software-pipelined bf16 MFMA core, in an XCD-aware
-//                      order; each tile adds its fp32 result into the state (one owner per
-//                      element).
+//                      tiles) on the software-pipelined bf16 MFMA core, reading X and Y_l as
+//                      they lie ([rows][d]: the reduction runs over rows, the core's M-major
+//                      operand form), in an XCD-aware order; each tile adds its fp32 result
+//                      into the state (one owner per element).
 // fp32 chunks (small widths) run one launch of the plain tile loop, which transposes 4 x 4
 // blocks on their way to LDS and sums the columns on the operand already in registers.
 #include "rf_internal.h"
@@ -150,92 +146,60 @@ __global__ __launch_bounds__(kThreads) void k_gram(GramArgs a) {
     }
 }
 
-// ---- bf16: transpose + column sums ---------------------------------------------------------
-struct TransArgs {
+// ---- bf16: column sums ------------------------------------------------------------------------
+struct ColsumArgs {
     const void* src[kMaxTargets + 1];   // [rows][ld] per matrix: X, then Y_0 .. Y_{L-1}
     int64_t ld[kMaxTargets + 1];
     double* csum[kMaxTargets + 1];      // column sums to add into: s_x, then s_y + l*d
-    int64_t rows;                       // rows present in this piece
-    int64_t rows_pad;                   // multiple of 128
-    int32_t d;
-    int32_t blocks_per_mat;             // d / 64
-    bf16_t* out;                        // [(L+1) d][rows_pad]
+    int64_t rows;
+    int32_t blocks_per_mat;             // d / 256
 };
 
-__global__ __launch_bounds__(256) void k_gram_transpose(TransArgs a) {
+// One work-group per 256 columns of one matrix: thread t sums columns 8 (t & 31) .. + 8 over
+// rows r = t >> 5 (mod 8) in ascending order (four rows in flight), then the 8 row groups are
+// added in a fixed order: the result does not depend on scheduling.
+__global__ __launch_bounds__(256) void k_gram_colsum(ColsumArgs a) {
     const int g = blockIdx.x / a.blocks_per_mat;
-    const int c0 = (blockIdx.x % a.blocks_per_mat) * 64;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int rb = lane >> 3, cb = lane & 7;   // 8 x 8 block (row block, column block) of a 64 x 64 tile
+    const int c0 = (blockIdx.x % a.blocks_per_mat) * 256;
+    const int t = threadIdx.x, ch = t & 31, rg = t >> 5;
     const int64_t ld = a.ld[g];
-    // rows past ``rows`` fall outside the byte range and read as zero (the row offset is in
-    // the vector offset, which the range check covers)
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(a.src[g]), (short)0, (int)(a.rows * ld * 2), 0x00020000);
-    bf16_t* out = a.out + ((int64_t)g * a.d + c0) * a.rows_pad;
-    const uint32_t sel_lo = 0x05040100u, sel_hi = 0x07060302u;
-    double cs[8];
+    const bf16_t* src = (const bf16_t*)a.src[g] + c0 + ch * 8;
+    double s[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) cs[i] = 0.0;
-    // each wave takes 64-row tiles wave, wave + 4, ...; four tiles per pass keep 32 loads in
-    // flight before the first transpose
-    constexpr int U = 4;
-    for (int64_t rb0 = (int64_t)wave * 64; rb0 < a.rows_pad; rb0 += 256 * U) {
-        u32x4 in[U][8];
+    for (int e = 0; e < 8; ++e) s[e] = 0.0;
+    auto add = [&](const u32x4& v) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t r0 = rb0 + (int64_t)u * 256;
-#pragma unroll
-            for (int r = 0; r < 8; ++r)
-                in[u][r] = __builtin_amdgcn_raw_buffer_load_b128(
-                    rs, (int)(((r0 + rb * 8 + r) * ld + c0 + cb * 8) * 2), 0, 0);
+        for (int w = 0; w < 4; ++w) {
+            s[2 * w] += (double)__uint_as_float(v[w] << 16);
+            s[2 * w + 1] += (double)__uint_as_float(v[w] & 0xffff0000u);
         }
+    };
+    int64_t r = rg;
+    for (; r + 24 < a.rows; r += 32) {
+        u32x4 v[4];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t r0 = rb0 + (int64_t)u * 256;
-            if (r0 >= a.rows_pad) break;
-            // o[i] = the 8 rows' values of column cb*8 + i (row 2p in the low half of dword p)
-            u32x4 o[8];
+        for (int u = 0; u < 4; ++u) v[u] = *(const u32x4*)(src + (r + 8 * u) * ld);
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int p = 0; p < 4; ++p)
-                    o[i][p] = __builtin_amdgcn_perm(in[u][2 * p + 1][i >> 1], in[u][2 * p][i >> 1],
-                                                    (i & 1) ? sel_hi : sel_lo);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                *(u32x4*)(out + (int64_t)(cb * 8 + i) * a.rows_pad + r0 + rb * 8) = o[i];
-                double sacc = cs[i];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    sacc += (double)__uint_as_float(o[i][p] << 16);
-                    sacc += (double)__uint_as_float(o[i][p] & 0xffff0000u);
-                }
-                cs[i] = sacc;
-            }
-        }
+        for (int u = 0; u < 4; ++u) add(v[u]);
     }
-    // reduce over the 8 row blocks of the wave (lane bits 3..5), then over the 4 waves
-    __shared__ double red[4][64];
+    for (; r < a.rows; r += 8) add(*(const u32x4*)(src + r * ld));
+    __shared__ double red[8][256];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        double x = cs[i];
-        x += __shfl_xor(x, 8);
-        x += __shfl_xor(x, 16);
-        x += __shfl_xor(x, 32);
-        if (rb == 0) red[wave][cb * 8 + i] = x;
-    }
+    for (int e = 0; e < 8; ++e) red[rg][ch * 8 + e] = s[e];
     __syncthreads();
-    if (threadIdx.x < 64) {
-        const int c = threadIdx.x;
-        a.csum[g][c0 + c] += ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
-    }
+    double x = 0.0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) x += red[q][t];
+    a.csum[g][c0 + t] += x;
 }
 
 // ---- bf16: products on the pipelined core ----------------------------------------------------
 struct PipeGramArgs {
-    const bf16_t* T;        // transposed chunk [(L+1) d][rows_pad]: X^T then Y_l^T
-    int64_t rows_pad;
+    const bf16_t* X;        // [rows][ldx]
+    int64_t ldx;
+    const bf16_t* Y[kMaxTargets];   // [rows][ldy] each
+    int64_t ldy;
+    int64_t rows;           // rows of this piece (the reduction extent; also added to n)
     int32_t d;
     int32_t tiles_m;        // d / 256
     int32_t n_xx;           // S_xx upper tiles
@@ -243,15 +207,16 @@ struct PipeGramArgs {
     float* Sxx;
     float* Syx;
     int64_t* n;
-    int64_t rows;           // rows of this piece (for n)
 };
 
 // Logical tiles [0, n_yx) are S_yx tiles, walked in groups of 4 X tiles x 8 Y tiles per XCD
 // step; [n_yx, n_yx + n_xx) are the S_xx upper triangle.  MFMA operand A = X^T rows (X column
 // tile mt), B = rows of the S tile (Y_l^T or X^T), so each lane holds 4 consecutive columns of
 // one S row: one 16-byte read-modify-write.
-__global__ __launch_bounds__(kPipeThreads) void k_gram_pipe(PipeGramArgs a) {
-    using G = PipeGemm;
+using GramCore = PipeGemmW<4, 2, true>;
+
+__global__ __launch_bounds__(GramCore::kThr) void k_gram_pipe(PipeGramArgs a) {
+    using G = GramCore;
     __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
     const int v = xcd_order((int)blockIdx.x, (int)gridDim.x);
     int mt, nt;
@@ -268,10 +233,19 @@ __global__ __launch_bounds__(kPipeThreads) void k_gram_pipe(PipeGramArgs a) {
         grouped_tile(v, a.tiles_m, a.n_yx / a.tiles_m, 4, mt, nt);
     }
     const int64_t srow0 = (int64_t)nt * kGT;
-    const bf16_t* Bp = a.T + ((is_xx ? 0 : (int64_t)a.d) + srow0) * a.rows_pad;
+    const bf16_t* Bp;
+    int64_t ldb;
+    if (is_xx) {
+        Bp = a.X + srow0;
+        ldb = a.ldx;
+    } else {
+        Bp = a.Y[srow0 / a.d] + srow0 % a.d;
+        ldb = a.ldy;
+    }
+    int nk = (int)((a.rows + G::BK - 1) / G::BK);
+    nk += nk & 1;   // the core takes k-steps in pairs; rows past the end read as zero
     G gm;
-    gm.run(lds, PipeOperand{a.T + (int64_t)mt * kGT * a.rows_pad, a.rows_pad, kGT},
-           PipeOperand{Bp, a.rows_pad, kGT}, (int)(a.rows_pad / G::BK));
+    gm.run(lds, PipeOperand{a.X + (int64_t)mt * kGT, a.ldx, a.rows}, PipeOperand{Bp, ldb, a.rows}, nk);
     if (v == 0 && threadIdx.x == 0) *a.n += a.rows;
     // Read-modify-write of the S tile, one 32-row block at a time: all 16 reads of a block are
     // issued before its writes (a store followed by a load the compiler cannot prove disjoint
@@ -295,8 +269,6 @@ __global__ __launch_bounds__(kPipeThreads) void k_gram_pipe(PipeGramArgs a) {
             }
     }
 }
-
-static int64_t pad_rows(int64_t rows) { return (rows + 127) / 128 * 128; }
 
 __global__ void k_zero_bytes(uint4* p, int64_t n16) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
@@ -351,16 +323,8 @@ rf_status rf_gram_init(const rf_gram_desc* desc, void* d_state, void* stream) {
     return check_launch("rf_gram_init");
 }
 
-size_t rf_gram_workspace_bytes(const rf_gram_desc* desc, int64_t max_rows) {
-    if (check_desc(desc) != RF_OK || max_rows < 0) { clear_error(); return 0; }
-    if (desc->dtype == RF_F32) return 0;
-    const int64_t rp = std::max<int64_t>(pad_rows(max_rows), 128);
-    return round_up((size_t)(desc->n_targets + 1) * desc->d * rp * 2, 256);
-}
-
 rf_status rf_gram_accumulate(const rf_gram_desc* desc, void* d_state, const void* d_X, int64_t ldx,
-                             const void* const* d_Y, int64_t ldy, int64_t rows, void* d_ws, size_t ws_bytes,
-                             void* stream) {
+                             const void* const* d_Y, int64_t ldy, int64_t rows, void* stream) {
     clear_error();
     rf_status st = check_desc(desc);
     if (st != RF_OK) return st;
@@ -398,32 +362,30 @@ rf_status rf_gram_accumulate(const rf_gram_desc* desc, void* d_state, const void
         return check_launch("rf_gram_accumulate");
     }
 
-    // bf16: pieces of as many rows as the workspace holds (at least 128)
-    const int64_t per_row = (int64_t)(desc->n_targets + 1) * desc->d * 2;
-    RF_REQUIRE(d_ws && aligned(d_ws, 256), RF_ERR_INVALID_ARG, "rf_gram_accumulate: bf16 needs a 256-B aligned workspace");
-    int64_t cap = (int64_t)(ws_bytes / (size_t)per_row) / 128 * 128;
-    // 32-bit byte offsets: a 256-row operand tile of the transposed piece, and a source row range
+    // bf16: pieces small enough for 32-bit byte offsets into X and Y (the products address a
+    // whole piece from the start of its rows)
     const int64_t ld_max = std::max<int64_t>(ldx, desc->n_targets > 0 ? ldy : 0);
     const int64_t lim = (((int64_t)1 << 31) - 1);
-    cap = std::min<int64_t>(cap, std::min<int64_t>(lim / (256 * 2), lim / (ld_max * 2) - 1024) / 128 * 128);
-    RF_REQUIRE(cap >= 128, RF_ERR_WORKSPACE, "rf_gram_accumulate: workspace smaller than rf_gram_workspace_bytes(desc, 128)");
+    const int64_t cap = (lim / (ld_max * 2) - 64) / 64 * 64;
+    RF_REQUIRE(cap >= 64, RF_ERR_UNSUPPORTED, "rf_gram_accumulate: row stride too large for 32-bit offsets");
     for (int64_t r0 = 0; r0 < rows; r0 += cap) {
         const int64_t pr = std::min(cap, rows - r0);
-        TransArgs ta{};
-        ta.src[0] = (const bf16_t*)d_X + r0 * ldx; ta.ld[0] = ldx; ta.csum[0] = sx;
+        ColsumArgs ca{};
+        ca.src[0] = (const bf16_t*)d_X + r0 * ldx; ca.ld[0] = ldx; ca.csum[0] = sx;
         for (int l = 0; l < desc->n_targets; ++l) {
-            ta.src[l + 1] = (const bf16_t*)d_Y[l] + r0 * ldy; ta.ld[l + 1] = ldy; ta.csum[l + 1] = sy + (int64_t)l * desc->d;
+            ca.src[l + 1] = (const bf16_t*)d_Y[l] + r0 * ldy; ca.ld[l + 1] = ldy; ca.csum[l + 1] = sy + (int64_t)l * desc->d;
         }
-        ta.rows = pr; ta.rows_pad = pad_rows(pr); ta.d = desc->d; ta.blocks_per_mat = desc->d / 64;
-        ta.out = (bf16_t*)d_ws;
-        hipLaunchKernelGGL(k_gram_transpose, dim3((unsigned)((desc->n_targets + 1) * ta.blocks_per_mat)), dim3(256), 0,
-                           strm, ta);
-        st = check_launch("rf_gram_accumulate: transpose");
+        ca.rows = pr; ca.blocks_per_mat = desc->d / kGT;
+        hipLaunchKernelGGL(k_gram_colsum, dim3((unsigned)((desc->n_targets + 1) * ca.blocks_per_mat)), dim3(256), 0,
+                           strm, ca);
+        st = check_launch("rf_gram_accumulate: column sums");
         if (st != RF_OK) return st;
         PipeGramArgs pa{};
-        pa.T = (const bf16_t*)d_ws; pa.rows_pad = ta.rows_pad; pa.d = desc->d; pa.tiles_m = tiles_m;
-        pa.n_xx = n_xx; pa.n_yx = n_yx; pa.Sxx = Sxx; pa.Syx = Syx; pa.n = np; pa.rows = pr;
-        hipLaunchKernelGGL(k_gram_pipe, dim3((unsigned)(n_xx + n_yx)), dim3(kPipeThreads), 0, strm, pa);
+        pa.X = (const bf16_t*)d_X + r0 * ldx; pa.ldx = ldx;
+        for (int l = 0; l < desc->n_targets; ++l) pa.Y[l] = (const bf16_t*)d_Y[l] + r0 * ldy;
+        pa.ldy = ldy; pa.rows = pr; pa.d = desc->d; pa.tiles_m = tiles_m;
+        pa.n_xx = n_xx; pa.n_yx = n_yx; pa.Sxx = Sxx; pa.Syx = Syx; pa.n = np;
+        hipLaunchKernelGGL(k_gram_pipe, dim3((unsigned)(n_xx + n_yx)), dim3(GramCore::kThr), 0, strm, pa);
         st = check_launch("rf_gram_accumulate: products");
         if (st != RF_OK) return st;
     }

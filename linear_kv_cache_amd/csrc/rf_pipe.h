@@ -26,6 +26,16 @@
 // the 16-byte half (l / 32) of a 32-byte k-slice; accumulator register i of lane l holds
 // C[m = 8*(i/4) + 4*(l/32) + i%4][n = l % 32].  The k-permutation inside a slice is the same for
 // both operands, so the sum is unchanged by it.
+//
+// M-major operands (MMAJOR): both operands are instead stored with m contiguous and k as the row
+// index (a [k][m] matrix, e.g. calibration rows x features), and the product contracts over k.
+// A k-step stages 64 rows x 256 columns (512 bytes) of each operand as they lie in memory; the
+// 16-byte chunk c of staged row k sits in slot c ^ 4 (k & 3).  Fragments come from gfx950's
+// transposing LDS read (ds_read_b64_tr_b16): in each group of 16 lanes, source lane j points at
+// row k0 + j / 4, columns m0 + 4 (j % 4), and lane i receives column m0 + i at rows k0 .. k0 + 3
+// (so two reads give a lane its 8 k of one m).  The 32 lanes served per LDS cycle cover four
+// rows x 64 bytes; the slot permutation spreads them over all 64 banks.  Rows at or past the
+// operand's ``valid`` (the k extent) read as zero.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -64,10 +74,11 @@ __device__ inline void grouped_tile(int v, int n_rows, int n_cols, int gf, int& 
     col = w / gs;
 }
 
-template <int WAVES, int NSETS = 2>
+template <int WAVES, int NSETS = 2, bool MMAJOR = false>
 struct PipeGemmW {
     static_assert(WAVES == 4 || WAVES == 8, "4 waves (one per SIMD) or 8 (two per SIMD)");
     static_assert(NSETS == 1 || NSETS == 2, "register sets of staged loads");
+    static_assert(!MMAJOR || WAVES == 4, "M-major operands: four waves");
     static constexpr int kThr = WAVES * 64;
     static constexpr int BM = 256, BN = 256, BK = 64;
     static constexpr int ROWB = 128;                       // bytes of one row per k-step
@@ -79,14 +90,15 @@ struct PipeGemmW {
     static constexpr int VA = BM * 8 / kThr;               // 16-byte vectors per thread per step
     static constexpr int VB = BN * 8 / kThr;
     static constexpr int ROWS_J = kThr / 8;                // rows between a thread's vectors
-    static constexpr int NR = SM + SN;                     // fragment reads per k-slice
+    static constexpr int NR = (MMAJOR ? 2 : 1) * (SM + SN);  // fragment reads per k-slice
     static constexpr int NM = SM * SN;                     // MFMAs per k-slice
 
     f32x16 acc[SM][SN];
 
     __device__ static inline __amdgpu_buffer_rsrc_t rsrc(const PipeOperand& op, int rows) {
         // byte range covers the rows that exist; a row at or past ``valid`` starts beyond it
-        int64_t nrows = op.valid < rows ? op.valid : rows;
+        // (M-major: the rows are k, all of them counted)
+        int64_t nrows = MMAJOR || op.valid < rows ? op.valid : rows;
         if (nrows < 0) nrows = 0;
         const int64_t bytes = nrows * op.ld * 2;
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(op.ptr), (short)0, (int)bytes, 0x00020000);
@@ -114,13 +126,17 @@ struct PipeGemmW {
 
         const __amdgpu_buffer_rsrc_t ra = rsrc(A, BM);
         const __amdgpu_buffer_rsrc_t rb = rsrc(B, BN);
-        // global: row (t >> 3) + ROWS_J j, logical chunk t & 7
-        const int gA = (int)((t >> 3) * A.ld * 2) + (t & 7) * 16;
-        const int gB = (int)((t >> 3) * B.ld * 2) + (t & 7) * 16;
-        const int strideA = (int)(ROWS_J * A.ld * 2);
-        const int strideB = (int)(ROWS_J * B.ld * 2);
-        // LDS write slot: row (t >> 3) + ROWS_J j has (row >> 1) & 7 == (t >> 4) & 7
-        const int wofs = (t >> 3) * ROWB + (((t & 7) ^ ((t >> 4) & 7)) << 4);
+        // global: row (t >> 3) + ROWS_J j, logical chunk t & 7 (M-major: row (t >> 5) + 8 j of
+        // the k-step, chunk t & 31)
+        const int gA = MMAJOR ? (int)((t >> 5) * A.ld * 2) + (t & 31) * 16 : (int)((t >> 3) * A.ld * 2) + (t & 7) * 16;
+        const int gB = MMAJOR ? (int)((t >> 5) * B.ld * 2) + (t & 31) * 16 : (int)((t >> 3) * B.ld * 2) + (t & 7) * 16;
+        const int strideA = (int)((MMAJOR ? 8 : ROWS_J) * A.ld * 2);
+        const int strideB = (int)((MMAJOR ? 8 : ROWS_J) * B.ld * 2);
+        // LDS write slot: row (t >> 3) + ROWS_J j has (row >> 1) & 7 == (t >> 4) & 7 (M-major:
+        // 512-byte rows (t >> 5) + 8 j, whose k & 3 is (t >> 5) & 3; stride 4096 bytes)
+        const int wofs = MMAJOR ? (t >> 5) * 512 + (((t & 31) ^ (4 * ((t >> 5) & 3))) << 4)
+                                : (t >> 3) * ROWB + (((t & 7) ^ ((t >> 4) & 7)) << 4);
+        const int wstep = MMAJOR ? 4096 : ROWS_J * ROWB;
         // LDS fragment reads: row (lane & 31) of a 32-row block, chunk 2 kk + (lane >> 5)
         const int rA = (wm * WTM + (lane & 31)) * ROWB;
         const int rB = (BM + wn * WTN + (lane & 31)) * ROWB;
@@ -128,30 +144,63 @@ struct PipeGemmW {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) cofs[kk] = ((2 * kk + (lane >> 5)) ^ ((lane >> 1) & 7)) << 4;
 
+        // k-step offsets: K-major steps move along the row (buffer offset), M-major steps move
+        // down 64 rows, kept in the range-checked vector offset so rows past the end read zero
         auto gload_a = [&](Regs& g, int kt) {
-            const int kb = (kt < nk ? kt : nk - 1) * ROWB;
+            const int kc = kt < nk ? kt : nk - 1;
+            const int kb = MMAJOR ? 0 : kc * ROWB;
+            const int kv = MMAJOR ? (int)(kc * 64 * A.ld * 2) : 0;
 #pragma unroll
-            for (int j = 0; j < VA; ++j) g.a[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, gA + j * strideA, kb, 0);
+            for (int j = 0; j < VA; ++j) g.a[j] = __builtin_amdgcn_raw_buffer_load_b128(ra, gA + kv + j * strideA, kb, 0);
         };
         auto gload_b = [&](Regs& g, int kt) {
-            const int kb = (kt < nk ? kt : nk - 1) * ROWB;
+            const int kc = kt < nk ? kt : nk - 1;
+            const int kb = MMAJOR ? 0 : kc * ROWB;
+            const int kv = MMAJOR ? (int)(kc * 64 * B.ld * 2) : 0;
 #pragma unroll
-            for (int j = 0; j < VB; ++j) g.b[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, gB + j * strideB, kb, 0);
+            for (int j = 0; j < VB; ++j) g.b[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, gB + kv + j * strideB, kb, 0);
         };
         auto swrite_a = [&](const Regs& g, char* st) {
 #pragma unroll
-            for (int j = 0; j < VA; ++j) *(u32x4*)(st + wofs + j * ROWS_J * ROWB) = g.a[j];
+            for (int j = 0; j < VA; ++j) *(u32x4*)(st + wofs + j * wstep) = g.a[j];
         };
         auto swrite_b = [&](const Regs& g, char* st) {
 #pragma unroll
-            for (int j = 0; j < VB; ++j) *(u32x4*)(st + BM * ROWB + wofs + j * ROWS_J * ROWB) = g.b[j];
+            for (int j = 0; j < VB; ++j) *(u32x4*)(st + BM * ROWB + wofs + j * wstep) = g.b[j];
         };
         u32x4 fa[2][SM], fb[2][SN];
+        // M-major fragments: lane l = 16 g + j reads row kk * 16 + 8 (g >> 1) + 4 h + (j >> 2),
+        // columns (g & 1) * 16 + 4 (j & 3) of its 32-column block, for h = 0, 1
+        const int tk = ((lane >> 5) << 3) + ((lane & 15) >> 2);
+        const int tm = (((lane >> 4) & 1) << 4) + 4 * (lane & 3);
+        auto tread = [&](const char* base, int k, int m) -> uint2 {
+            typedef short v4i16 __attribute__((ext_vector_type(4)));
+            typedef __attribute__((address_space(3))) v4i16 lds_v4;
+            const int off = k * 512 + ((((m >> 3) ^ (4 * (k & 3))) << 4) | ((m & 7) * 2));
+            const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4*)((__attribute__((address_space(3))) char*)base + off));
+            return __builtin_bit_cast(uint2, v);
+        };
         auto fread = [&](int buf, const char* st, int kk) {
+            if constexpr (MMAJOR) {
 #pragma unroll
-            for (int i = 0; i < SM; ++i) fa[buf][i] = *(const u32x4*)(st + rA + i * 32 * ROWB + cofs[kk]);
+                for (int i = 0; i < SM; ++i) {
+                    const uint2 lo = tread(st, kk * 16 + tk, wm * WTM + i * 32 + tm);
+                    const uint2 hi = tread(st, kk * 16 + 4 + tk, wm * WTM + i * 32 + tm);
+                    fa[buf][i] = u32x4{lo.x, lo.y, hi.x, hi.y};
+                }
 #pragma unroll
-            for (int j = 0; j < SN; ++j) fb[buf][j] = *(const u32x4*)(st + rB + j * 32 * ROWB + cofs[kk]);
+                for (int j = 0; j < SN; ++j) {
+                    const uint2 lo = tread(st + BM * ROWB, kk * 16 + tk, wn * WTN + j * 32 + tm);
+                    const uint2 hi = tread(st + BM * ROWB, kk * 16 + 4 + tk, wn * WTN + j * 32 + tm);
+                    fb[buf][j] = u32x4{lo.x, lo.y, hi.x, hi.y};
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < SM; ++i) fa[buf][i] = *(const u32x4*)(st + rA + i * 32 * ROWB + cofs[kk]);
+#pragma unroll
+                for (int j = 0; j < SN; ++j) fb[buf][j] = *(const u32x4*)(st + rB + j * 32 * ROWB + cofs[kk]);
+            }
         };
         auto mfma = [&](int buf, int i0, int i1) {
 #pragma unroll

@@ -9,7 +9,6 @@ import torch
 
 from . import (RF_LAYOUT_CONTIGUOUS, RF_LAYOUT_PAGED, FillWeights, cache_desc, gram_desc, rf_cache_layout,
                rf_fill, rf_fill_workspace_bytes, rf_gram_accumulate, rf_gram_init, rf_gram_state_bytes,
-               rf_gram_workspace_bytes,
                rf_gram_state_layout, rf_rope_table, rf_solve, rf_solve_workspace_bytes)
 
 
@@ -23,17 +22,15 @@ def device_bytes(n: int, device) -> torch.Tensor:
 class GramState:
     """The one-pass second-moment state of a calibration run (device buffer + layout)."""
 
-    def __init__(self, d: int, n_targets: int, dtype, device, stream=None, max_chunk_rows: int = 8192):
+    def __init__(self, d: int, n_targets: int, dtype, device, stream=None):
         self.desc = gram_desc(d, n_targets, dtype)
         self.layout = rf_gram_state_layout(self.desc)
         self.buf = device_bytes(rf_gram_state_bytes(self.desc), device)
-        wsb = rf_gram_workspace_bytes(self.desc, max_chunk_rows)
-        self.ws = device_bytes(wsb, device) if wsb else None
         self.d, self.n_targets = d, n_targets
         rf_gram_init(self.desc, self.buf, stream)
 
     def accumulate(self, X, Ys, stream=None):
-        rf_gram_accumulate(self.desc, self.buf, X, Ys, ws=self.ws, stream=stream)
+        rf_gram_accumulate(self.desc, self.buf, X, Ys, stream=stream)
 
     # views of the state (plain data as laid out by rf_gram_state_layout)
     def _view(self, off, count, dtype):

@@ -79,28 +79,16 @@ def test_gram_validation_before_enqueue():
         rf.rf_gram_accumulate(rf.gram_desc(256, 65, torch.float32), 256, X, [])
     assert e.value.status == rf.RF_ERR_UNSUPPORTED
     rf.rf_gram_accumulate(desc, 256, X, [X], rows=0)  # zero rows: a no-op
-    # bf16 chunks need a workspace
+    # bf16 rows: pointers and strides are checked before anything is enqueued
     db = rf.gram_desc(256, 1, torch.bfloat16)
-    Xb = torch.empty(4, 256, dtype=torch.bfloat16)
-    with pytest.raises(rf.RidgeFillError) as e:
-        rf.rf_gram_accumulate(db, 256, Xb, [Xb])
+    ys = (C.c_void_p * 1)(256)
+    for X_ptr, ldx, ldy in ((264, 256, 256), (256, 200, 256), (256, 256, 260), (0, 256, 256)):
+        with pytest.raises(rf.RidgeFillError) as e:
+            rf._check(rf._lib.rf_gram_accumulate(C.byref(db), 256, X_ptr, ldx, ys, ldy, 4, None))
+        assert e.value.status == rf.RF_ERR_INVALID_ARG
+    with pytest.raises(rf.RidgeFillError) as e:   # a null Y pointer
+        rf._check(rf._lib.rf_gram_accumulate(C.byref(db), 256, 256, 256, (C.c_void_p * 1)(0), 256, 4, None))
     assert e.value.status == rf.RF_ERR_INVALID_ARG
-    small = torch.empty(1024, dtype=torch.uint8)
-    with pytest.raises(rf.RidgeFillError) as e:
-        rf._check(rf._lib.rf_gram_accumulate(C.byref(db), 256, 256, 256, (C.c_void_p * 1)(256), 256, 4, 256,
-                                             16, None))
-    assert e.value.status == rf.RF_ERR_WORKSPACE
-
-
-def test_gram_workspace_bytes():
-    assert rf.rf_gram_workspace_bytes(rf.gram_desc(256, 4, torch.float32), 4096) == 0
-    d, L = 4096, 16
-    desc = rf.gram_desc(d, L, torch.bfloat16)
-    # (L + 1) * d * round_up(rows, 128) bf16 values, at least 128 rows
-    assert rf.rf_gram_workspace_bytes(desc, 8192) == (L + 1) * d * 8192 * 2
-    assert rf.rf_gram_workspace_bytes(desc, 8193) == (L + 1) * d * 8320 * 2
-    assert rf.rf_gram_workspace_bytes(desc, 0) == (L + 1) * d * 128 * 2
-    assert rf.rf_gram_workspace_bytes(rf.gram_desc(100, 2, torch.bfloat16), 64) == 0
 
 
 def test_solve_validation_before_enqueue():
