@@ -152,16 +152,16 @@ struct ColsumArgs {
     int64_t ld[kMaxTargets + 1];
     double* csum[kMaxTargets + 1];      // column sums to add into: s_x, then s_y + l*d
     int64_t rows;
-    int32_t blocks_per_mat;             // d / 256
+    int32_t blocks_per_mat;             // d / 64
 };
 
-// One work-group per 256 columns of one matrix: thread t sums columns 8 (t & 31) .. + 8 over
-// rows r = t >> 5 (mod 8) in ascending order (four rows in flight), then the 8 row groups are
-// added in a fixed order: the result does not depend on scheduling.
+// One work-group per 64 columns of one matrix: thread t sums columns 8 (t & 7) .. + 8 over rows
+// r = t >> 3 (mod 32) in ascending order (eight rows in flight), then the 32 row groups are added
+// in a fixed order: the result does not depend on scheduling.
 __global__ __launch_bounds__(256) void k_gram_colsum(ColsumArgs a) {
     const int g = blockIdx.x / a.blocks_per_mat;
-    const int c0 = (blockIdx.x % a.blocks_per_mat) * 256;
-    const int t = threadIdx.x, ch = t & 31, rg = t >> 5;
+    const int c0 = (blockIdx.x % a.blocks_per_mat) * 64;
+    const int t = threadIdx.x, ch = t & 7, rg = t >> 3;
     const int64_t ld = a.ld[g];
     const bf16_t* src = (const bf16_t*)a.src[g] + c0 + ch * 8;
     double s[8];
@@ -175,22 +175,23 @@ __global__ __launch_bounds__(256) void k_gram_colsum(ColsumArgs a) {
         }
     };
     int64_t r = rg;
-    for (; r + 24 < a.rows; r += 32) {
-        u32x4 v[4];
+    for (; r + 7 * 32 < a.rows; r += 8 * 32) {
+        u32x4 v[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = *(const u32x4*)(src + (r + 8 * u) * ld);
+        for (int u = 0; u < 8; ++u) v[u] = *(const u32x4*)(src + (r + 32 * u) * ld);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) add(v[u]);
+        for (int u = 0; u < 8; ++u) add(v[u]);
     }
-    for (; r < a.rows; r += 8) add(*(const u32x4*)(src + r * ld));
-    __shared__ double red[8][256];
+    for (; r < a.rows; r += 32) add(*(const u32x4*)(src + r * ld));
+    __shared__ double red[32][64 + 1];
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[rg][ch * 8 + e] = s[e];
     __syncthreads();
-    double x = 0.0;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) x += red[q][t];
-    a.csum[g][c0 + t] += x;
+    if (t < 64) {
+        double x = 0.0;
+        for (int q = 0; q < 32; ++q) x += red[q][t];
+        a.csum[g][c0 + t] += x;
+    }
 }
 
 // ---- bf16: products on the pipelined core ----------------------------------------------------
@@ -375,7 +376,7 @@ rf_status rf_gram_accumulate(const rf_gram_desc* desc, void* d_state, const void
         for (int l = 0; l < desc->n_targets; ++l) {
             ca.src[l + 1] = (const bf16_t*)d_Y[l] + r0 * ldy; ca.ld[l + 1] = ldy; ca.csum[l + 1] = sy + (int64_t)l * desc->d;
         }
-        ca.rows = pr; ca.blocks_per_mat = desc->d / kGT;
+        ca.rows = pr; ca.blocks_per_mat = desc->d / 64;
         hipLaunchKernelGGL(k_gram_colsum, dim3((unsigned)((desc->n_targets + 1) * ca.blocks_per_mat)), dim3(256), 0,
                            strm, ca);
         st = check_launch("rf_gram_accumulate: column sums");

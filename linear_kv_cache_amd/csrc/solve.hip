@@ -343,19 +343,17 @@ __global__ void k_centre_split(CrossArgs a) {
 // Factor the diagonal block J (already updated by all earlier panels) in place into L_JJ and
 // write L_JJ^-1 into Dinv.  info receives the 1-based index of the first non-positive pivot
 // (unless an earlier block already reported one).
-// One wave, no barriers: lane i keeps row i of the block in registers and the right-looking
-// elimination broadcasts each multiplier L[k][j] from lane k (v_readlane); entries above the
-// diagonal are never read for the lower triangle and are written as zeros.  Then lane c keeps
-// column c of L^-1 and forward-substitutes, X[r][c] = (delta_rc - sum_{k<r} L[r][k] X[k][c]) /
-// L[r][r], with L[r][k] broadcast from lane r.
-__device__ inline double bcast_lane(double v, int lane) {
-    const uint64_t u = __builtin_bit_cast(uint64_t, v);
-    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, lane);
-    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), lane);
-    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
-
+// One wave, no barriers (a wave's LDS operations complete in order).  Lane i keeps row i of the
+// block in registers.  Right-looking elimination: at step j lane i writes its entry of column j
+// to LDS, reads the pivot back, scales, and writes L[i][j] into the transposed copy Lt[j][i];
+// the multipliers L[k][j] then reach every lane as broadcast reads of Lt[j] (all lanes one
+// address).  Entries above the diagonal are never read for the lower triangle and are written as
+// zeros.  L^-1 by right-looking substitution, lane c holding column c: once X[k][c] is final it
+// is stored, and row k of X updates the running sums of rows r > k with L[r][k] = Lt[k][r].
 __global__ __launch_bounds__(64) void k_chol_diag(double* C, int64_t d, int J, double* Dinv, int32_t* info) {
+    __shared__ double piv[kNB];
+    __shared__ double col[2][kNB];
+    __shared__ __attribute__((aligned(16))) double Lt[kNB][kNB + 2];
     const int i = threadIdx.x;
     const int64_t off = (int64_t)J * kNB;
     double a[kNB];
@@ -366,29 +364,48 @@ __global__ __launch_bounds__(64) void k_chol_diag(double* C, int64_t d, int J, d
     double rinv = 0.0;   // lane i: 1 / L[i][i]
 #pragma unroll
     for (int j = 0; j < kNB; ++j) {
-        const double p = bcast_lane(a[j], j);
+        col[j & 1][i] = a[j];   // every lane writes (no divergent branch in the unrolled step)
+        const double p = col[j & 1][j];
         if (!(p > 0.0) && fail == 0) fail = (int32_t)(off + j + 1);
         const double r = sqrt(p);
         const double ri = 1.0 / r;
         if (i == j) rinv = ri;
-        a[j] = i > j ? a[j] * ri : (i == j ? r : a[j]);
+        const double lij = i > j ? a[j] * ri : (i == j ? r : 0.0);
+        Lt[j][i] = lij;
+        a[j] = i >= j ? lij : a[j];
+        if ((j & 1) == 0 && j + 1 < kNB) a[j + 1] -= lij * Lt[j][j + 1];   // odd first row, alone
 #pragma unroll
-        for (int k = j + 1; k < kNB; ++k) a[k] -= a[j] * bcast_lane(a[j], k);
+        for (int k = (j + 2) & ~1; k < kNB; k += 2) {
+            const f64x2 v = *(const f64x2*)(&Lt[j][k]);   // broadcast of L[k][j], L[k+1][j]
+            a[k] -= lij * v[0];
+            a[k + 1] -= lij * v[1];
+            if ((k & 15) == 14) __builtin_amdgcn_sched_barrier(0);   // at most 8 reads in flight
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep each step's broadcasts within the step
     }
-    double x[kNB];
-#pragma unroll
-    for (int r = 0; r < kNB; ++r) {
-        double sum = r == i ? 1.0 : 0.0;
-#pragma unroll
-        for (int k = 0; k < r; ++k) sum -= bcast_lane(a[k], r) * x[k];
-        x[r] = sum * bcast_lane(rinv, r);
-    }
-    if (i == 0 && !prior && fail != 0) *info = fail;
 #pragma unroll
     for (int k = 0; k < kNB; ++k) C[(off + i) * d + off + k] = k <= i ? a[k] : 0.0;
+    if (i == 0 && !prior && fail != 0) *info = fail;
+    // 1 / L[r][r] for every r, broadcast through LDS
+    piv[i] = rinv;
     double* D = Dinv + (int64_t)J * kNB * kNB;
+    double acc[kNB];   // lane c: sum_{k < r, so far} L[r][k] X[k][c]
 #pragma unroll
-    for (int r = 0; r < kNB; ++r) D[r * kNB + i] = x[r];
+    for (int r = 0; r < kNB; ++r) acc[r] = 0.0;
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) {
+        const double xk = ((k == i ? 1.0 : 0.0) - acc[k]) * piv[k];
+        D[k * kNB + i] = xk;
+        if ((k & 1) == 0 && k + 1 < kNB) acc[k + 1] += Lt[k][k + 1] * xk;
+#pragma unroll
+        for (int r = (k + 2) & ~1; r < kNB; r += 2) {
+            const f64x2 v = *(const f64x2*)(&Lt[k][r]);   // broadcast of L[r][k], L[r+1][k]
+            acc[r] += v[0] * xk;
+            acc[r + 1] += v[1] * xk;
+            if ((r & 15) == 14) __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 // dg[i] = sqrt(A[i][i]) before the factorisation overwrites the diagonal.
