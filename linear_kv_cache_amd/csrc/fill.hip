@@ -109,8 +109,7 @@ template <typename T>
 __global__ __launch_bounds__(FillCore<T>::G::kThr) void k_fill_map(MapArgs a) {
     using G = typename FillCore<T>::G;
     constexpr int kRedOff = MapStage<T>::kBytes;  // [2][kTT] fp32 partial sums after the stage
-    constexpr int kBgOff = kRedOff + 2 * kTT * 4;  // bias and gamma of the tile's features, fp32
-    constexpr int kEpi = kBgOff + 2 * kFT * 4;
+    constexpr int kEpi = kRedOff + 2 * kTT * 4;
     constexpr int kLdsBytes = G::LDS_BYTES > kEpi ? G::LDS_BYTES : kEpi;
     __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
     int g, mt, tt;
@@ -124,13 +123,17 @@ __global__ __launch_bounds__(FillCore<T>::G::kThr) void k_fill_map(MapArgs a) {
     const int lane = threadIdx.x & 63;
     const int wm = (threadIdx.x >> 6) / G::WGN;   // wave row (two per tile)
     float* red = (float*)(lds + kRedOff);
-    float* bias = (float*)(lds + kBgOff);
-    float* gamma = bias + kFT;
-    for (int f = threadIdx.x; f < kFT; f += G::kThr) {
-        bias[f] = a.bias[g][mt * kFT + f];
-        gamma[f] = a.gamma[g][mt * kFT + f];
-    }
-    __syncthreads();
+    // bias and gamma of this lane's 16 groups of 4 features, read once (16-byte loads) before any
+    // staging write, so no LDS read waits behind the writes
+    f32x4 bb[G::SM][4], gg[G::SM][4];
+#pragma unroll
+    for (int i = 0; i < G::SM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int f = mt * kFT + G::row_of(i, 4 * q);
+            bb[i][q] = *(const f32x4*)(a.bias[g] + f);
+            gg[i][q] = *(const f32x4*)(a.gamma[g] + f);
+        }
     T* H = (T*)a.H + g * a.h_slot;
 #pragma unroll
     for (int j = 0; j < G::SN; ++j) {
@@ -142,22 +145,21 @@ __global__ __launch_bounds__(FillCore<T>::G::kThr) void k_fill_map(MapArgs a) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int ml = G::row_of(i, 4 * q);
-                const f32x4 bb = *(const f32x4*)(bias + ml);
-                const f32x4 gg = *(const f32x4*)(gamma + ml);
                 float h[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    h[e] = gm.acc[i][j][4 * q + e] + bb[e];
+                    h[e] = gm.acc[i][j][4 * q + e] + bb[i][q][e];
                     ss += h[e] * h[e];
                 }
+                const f32x4 gq = gg[i][q];
                 if constexpr (MapStage<T>::kLds) {
                     const int slot = ((ml >> 3) ^ (nl & 31)) << 4;
                     *(u32x2*)(lds + nl * (kFT * 2) + slot + (ml & 4) * 2) =
-                        u32x2{pack_bf16x2(h[0] * gg[0], h[1] * gg[1]), pack_bf16x2(h[2] * gg[2], h[3] * gg[3])};
+                        u32x2{pack_bf16x2(h[0] * gq[0], h[1] * gq[1]), pack_bf16x2(h[2] * gq[2], h[3] * gq[3])};
                 } else {
                     if (n < a.rows)
-                        store4<T>(H + n * a.d + (int64_t)mt * kFT + ml, h[0] * gg[0], h[1] * gg[1],
-                                  h[2] * gg[2], h[3] * gg[3]);
+                        store4<T>(H + n * a.d + (int64_t)mt * kFT + ml, h[0] * gq[0], h[1] * gq[1],
+                                  h[2] * gq[2], h[3] * gq[3]);
                 }
             }
         }
