@@ -78,8 +78,8 @@ def cpu_baseline(cfg, n_tokens: int, n_fit_rows: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="C2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16384)
@@ -194,11 +194,16 @@ def main():
         "config": {"workload": cfg.name, "d": d, "filled_layers": L, "n_kv_heads": cfg.n_kv_heads,
                    "head_dim": cfg.head_dim, "fill_tokens": T, "calib_rows": cfg.calib_rows,
                    "calib_chunk": cfg.calib_chunk, "lambda": lam},
-        "fill": {"ms": round(statistics.mean(fill_ms), 3), "tokens_per_s": round(tok_s, 1),
+        "fill": {"ms": round(statistics.mean(fill_ms), 3), "ms_median": round(statistics.median(fill_ms), 3),
+                 "tokens_per_s": round(tok_s, 1),
                  "tflops": round(fill_tflops, 1), "frac_bf16_peak": round(fill_tflops / BF16_PEAK_TFLOPS, 4),
-                 "flop_per_token_layer": cfg.fill_flop_per_token_layer()},
+                 "flop_per_token_layer": cfg.fill_flop_per_token_layer(),
+                 # bf16 K and V rows written to the caches: 2 * H_kv * d_h * 2 B per token-layer
+                 "cache_write_GBps": round(T * L * 4 * cfg.n_kv_heads * cfg.head_dim * args.steps / fill_s / 1e9, 1)},
         "fit": {"rows_per_s": round(cfg.calib_rows / (statistics.mean(gram_ms) / 1e3), 1),
                 "gram_ms": round(statistics.mean(gram_ms), 3), "solve_ms": round(statistics.mean(solve_ms), 3),
+                "gram_ms_median": round(statistics.median(gram_ms), 3),
+                "solve_ms_median": round(statistics.median(solve_ms), 3),
                 "rows_per_s_incl_solve": round(cfg.calib_rows / ((statistics.mean(gram_ms) +
                                                                    statistics.mean(solve_ms)) / 1e3), 1),
                 "flop_per_row": cfg.fit_flop_per_row()},

@@ -237,14 +237,6 @@ __global__ __launch_bounds__(256) void k_dgemm_valu(int64_t M, int64_t N, int64_
     }
 }
 
-__global__ void k_copy2d(const double* src, int64_t lds, double* dst, int64_t ldd, int64_t rows, int64_t cols) {
-    const int64_t n = rows * cols;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = i / cols, c = i % cols;
-        dst[r * ldd + c] = src[r * lds + c];
-    }
-}
-
 // Z = 0 except its diagonal 64 x 64 blocks, which are the transposed inverses of L's diagonal
 // blocks (Dinv holds L_JJ^-1 row-major): Z_JJ = (L_JJ^T)^-1.
 __global__ void k_zdiag(const double* Dinv, int64_t d, double* Z) {
@@ -510,7 +502,7 @@ __global__ void k_bias(const float* bpart, int tiles_j, const double* mu_y, int6
 
 // -------------------------------------------------------------------------------------------
 struct SolveWs {
-    double *C, *Cinv, *P, *Dinv, *mu_y, *dg;
+    double *C, *Cinv, *Dinv, *mu_y, *dg;
     bf16_t *Aq, *Bq;
     float* bpart;
     size_t total;
@@ -528,7 +520,6 @@ static SolveWs solve_ws(void* base, int64_t d, int64_t n_sel) {
     const int64_t rows = n_sel * d;
     w.C = (double*)take(d * d * 8);
     w.Cinv = (double*)take(d * d * 8);
-    w.P = (double*)take(d * kNB * 8);
     w.Dinv = (double*)take(d * kNB * 8);
     w.mu_y = (double*)take(rows * 8);
     w.dg = (double*)take(d * 8);
@@ -653,13 +644,12 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, double lambda,
         RF_TRY(check_launch("rf_solve: potrf"));
         const int64_t rem = d - c0 - kNB;
         if (rem <= 0) continue;
+        // L21 = A21 L11^-T in place: the 64-column product runs on 64 x 64 tiles, each of which
+        // reads all of its rows of A21 before writing them
         double* panel = w.C + (c0 + kNB) * d + c0;
-        RF_TRY(dgemm<true>(s, rem, kNB, kNB, 1.0, panel, d, w.Dinv + c0 * kNB, kNB, 0.0, w.P, kNB));
-        RF_TRY(dgemm<true>(s, rem, rem, kNB, -1.0, w.P, kNB, w.P, kNB, 1.0, w.C + (c0 + kNB) * d + c0 + kNB, d,
+        RF_TRY(dgemm<true>(s, rem, kNB, kNB, 1.0, panel, d, w.Dinv + c0 * kNB, kNB, 0.0, panel, d));
+        RF_TRY(dgemm<true>(s, rem, rem, kNB, -1.0, panel, d, panel, d, 1.0, w.C + (c0 + kNB) * d + c0 + kNB, d,
                            kLowerOnly));
-        hipLaunchKernelGGL(k_copy2d, dim3(grid_for(rem * kNB)), dim3(256), 0, s, w.P, (int64_t)kNB, panel, d, rem,
-                           (int64_t)kNB);
-        RF_TRY(check_launch("rf_solve: copy"));
     }
     // A^-1 = Z Z^T with Z = L^-T (the factor is no longer needed afterwards: A^-1 overwrites it)
     RF_TRY(inverse_factor(s, w, d, w.Cinv));
