@@ -43,11 +43,16 @@ typedef double f64x2 __attribute__((ext_vector_type(2)));
 // Batched launches (gridDim.z > 1) offset A, B and C by blockIdx.z times sA, sB, sC elements.
 enum { kFull = 0, kLowerOnly = 1, kUpperOperands = 2, kUpperA = 4, kUpperB = 8 };
 
-template <bool BT>
+template <bool BT, int BM = 128>
 __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, double alpha, const double* A,
                                                int64_t lda, const double* B, int64_t ldb, double beta, double* C,
                                                int64_t ldc, int structure, int64_t sA, int64_t sB, int64_t sC) {
-    constexpr int BM = 128, BN = 128, BK = 32, PAD = 2;
+    static_assert(BM == 64 || BM == 128, "64 x 64 or 128 x 128 tiles");
+    constexpr int BN = BM, BK = 32, PAD = 2;
+    constexpr int WT = BM / 2, WB = WT / 16;   // wave tile and its 16 x 16 blocks per side
+    constexpr int EPT = BM * BK / 256;          // operand elements per thread per k-step
+    constexpr int TPR = BK / EPT;               // threads per K-contiguous row
+    constexpr int TPK = BN / EPT;               // threads per k-row of an N-contiguous operand
     A += (int64_t)blockIdx.z * sA;
     B += (int64_t)blockIdx.z * sB;
     C += (int64_t)blockIdx.z * sC;
@@ -61,58 +66,59 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, 
     if (structure & kUpperOperands) kbeg = (m0 > n0 ? m0 : n0) / BK * BK;
     if (structure & kUpperA) kbeg = m0 / BK * BK;
     if ((structure & kUpperB) && n0 + BN < K) kend = n0 + BN;
-    // loaders: a K-contiguous operand gives each thread 16 consecutive k of one row; an
-    // N-contiguous operand gives 16 consecutive n of one k-row.  A run wholly in range and
-    // 16-byte aligned is read as eight 16-byte loads, otherwise element by element.
-    double ra[16], rb[16];
-    auto run16 = [&](const double* p, bool whole, int valid, double (&r)[16]) {
+    // loaders: a K-contiguous operand gives each thread EPT consecutive k of one row; an
+    // N-contiguous operand gives EPT consecutive n of one k-row.  A run wholly in range and
+    // 16-byte aligned is read as 16-byte loads, otherwise element by element.
+    double ra[EPT], rb[EPT];
+    auto runv = [&](const double* p, bool whole, int valid, double (&r)[EPT]) {
         if (whole && ((uintptr_t)p & 15) == 0) {
 #pragma unroll
-            for (int e = 0; e < 16; e += 2) {
+            for (int e = 0; e < EPT; e += 2) {
                 const f64x2 v = *(const f64x2*)(p + e);
                 r[e] = v[0];
                 r[e + 1] = v[1];
             }
         } else {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) r[e] = e < valid ? p[e] : 0.0;
+            for (int e = 0; e < EPT; ++e) r[e] = e < valid ? p[e] : 0.0;
         }
     };
+    auto span = [&](int64_t lim, int64_t at) { return (int)(lim - at < EPT ? (lim - at > 0 ? lim - at : 0) : EPT); };
     auto load = [&](int64_t k0) {
         {
-            const int64_t m = m0 + (t >> 1);
-            const int64_t k = k0 + (t & 1) * 16;
-            const int valid = m < M ? (int)(K - k < 16 ? (K - k > 0 ? K - k : 0) : 16) : 0;
-            run16(A + (m < M ? m : 0) * lda + (valid > 0 ? k : 0), valid == 16, valid, ra);
+            const int64_t m = m0 + t / TPR;
+            const int64_t k = k0 + (t % TPR) * EPT;
+            const int valid = m < M ? span(K, k) : 0;
+            runv(A + (m < M ? m : 0) * lda + (valid > 0 ? k : 0), valid == EPT, valid, ra);
         }
         if (BT) {
-            const int64_t n = n0 + (t >> 1);
-            const int64_t k = k0 + (t & 1) * 16;
-            const int valid = n < N ? (int)(K - k < 16 ? (K - k > 0 ? K - k : 0) : 16) : 0;
-            run16(B + (n < N ? n : 0) * ldb + (valid > 0 ? k : 0), valid == 16, valid, rb);
+            const int64_t n = n0 + t / TPR;
+            const int64_t k = k0 + (t % TPR) * EPT;
+            const int valid = n < N ? span(K, k) : 0;
+            runv(B + (n < N ? n : 0) * ldb + (valid > 0 ? k : 0), valid == EPT, valid, rb);
         } else {
-            const int64_t k = k0 + (t >> 3);
-            const int64_t nn = n0 + (t & 7) * 16;
-            const int valid = k < K ? (int)(N - nn < 16 ? (N - nn > 0 ? N - nn : 0) : 16) : 0;
-            run16(B + (k < K ? k : 0) * ldb + (valid > 0 ? nn : 0), valid == 16, valid, rb);
+            const int64_t k = k0 + t / TPK;
+            const int64_t nn = n0 + (t % TPK) * EPT;
+            const int valid = k < K ? span(N, nn) : 0;
+            runv(B + (k < K ? k : 0) * ldb + (valid > 0 ? nn : 0), valid == EPT, valid, rb);
         }
     };
     auto store = [&](int buf) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) As[buf][(t & 1) * 16 + e][t >> 1] = ra[e];
+        for (int e = 0; e < EPT; ++e) As[buf][(t % TPR) * EPT + e][t / TPR] = ra[e];
         if (BT) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) Bs[buf][(t & 1) * 16 + e][t >> 1] = rb[e];
+            for (int e = 0; e < EPT; ++e) Bs[buf][(t % TPR) * EPT + e][t / TPR] = rb[e];
         } else {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) Bs[buf][t >> 3][(t & 7) * 16 + e] = rb[e];
+            for (int e = 0; e < EPT; ++e) Bs[buf][t / TPK][(t % TPK) * EPT + e] = rb[e];
         }
     };
-    f64x4 acc[4][4];
+    f64x4 acc[WB][WB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WB; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+        for (int j = 0; j < WB; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
     const int nk = kend > kbeg ? (int)((kend - kbeg + BK - 1) / BK) : 0;
     if (nk > 0) {
         load(kbeg);
@@ -124,15 +130,15 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, 
 #pragma unroll
             for (int ks = 0; ks < BK; ks += 4) {
                 const int kr = ks + (lane >> 4);
-                double a[4], b[4];
+                double a[WB], b[WB];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) a[i] = As[cur][kr][wm * 64 + i * 16 + (lane & 15)];
+                for (int i = 0; i < WB; ++i) a[i] = As[cur][kr][wm * WT + i * 16 + (lane & 15)];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) b[j] = Bs[cur][kr][wn * 64 + j * 16 + (lane & 15)];
+                for (int j = 0; j < WB; ++j) b[j] = Bs[cur][kr][wn * WT + j * 16 + (lane & 15)];
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < WB; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+                    for (int j = 0; j < WB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
             }
             if (kt + 1 < nk) store(cur ^ 1);
             __syncthreads();
@@ -140,26 +146,26 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, 
     }
     // all reads of C before any write: a store followed by a load the compiler cannot prove
     // disjoint would otherwise cost a full memory round trip per element
-    double cv[4][4][4];
+    double cv[WB][WB][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WB; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t n = n0 + wn * 64 + j * 16 + (lane & 15);
+        for (int j = 0; j < WB; ++j) {
+            const int64_t n = n0 + wn * WT + j * 16 + (lane & 15);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t m = m0 + wm * 64 + i * 16 + 4 * r + (lane >> 4);
+                const int64_t m = m0 + wm * WT + i * 16 + 4 * r + (lane >> 4);
                 cv[i][j][r] = (beta != 0.0 && m < M && n < N) ? C[m * ldc + n] : 0.0;
             }
         }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < WB; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t n = n0 + wn * 64 + j * 16 + (lane & 15);
+        for (int j = 0; j < WB; ++j) {
+            const int64_t n = n0 + wn * WT + j * 16 + (lane & 15);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t m = m0 + wm * 64 + i * 16 + 4 * r + (lane >> 4);
+                const int64_t m = m0 + wm * WT + i * 16 + 4 * r + (lane >> 4);
                 if (m < M && n < N) {
                     double v = alpha * acc[i][j][r];
                     if (beta != 0.0) v += beta * cv[i][j][r];
@@ -538,10 +544,19 @@ template <bool BT>
 static rf_status dgemm(hipStream_t s, int64_t M, int64_t N, int64_t K, double alpha, const double* A, int64_t lda,
                        const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int structure = kFull) {
     if (M <= 0 || N <= 0) return RF_OK;
-    if ((M >= 512 && N >= 512) || structure != kFull)
-        hipLaunchKernelGGL(k_dgemm<BT>, dim3((unsigned)ceil_div(M, 128), (unsigned)ceil_div(N, 128)), dim3(256), 0, s,
-                           M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, structure, (int64_t)0, (int64_t)0, (int64_t)0);
-    else
+    if ((M >= 512 && N >= 512) || structure != kFull) {
+        // 128 x 128 tiles, unless they would not fill two rounds of the 256 CUs
+        int64_t tiles = ceil_div(M, 128) * ceil_div(N, 128);
+        if (structure & kLowerOnly) tiles = (tiles + ceil_div(M, 128)) / 2;
+        if (tiles >= 512)
+            hipLaunchKernelGGL((k_dgemm<BT, 128>), dim3((unsigned)ceil_div(M, 128), (unsigned)ceil_div(N, 128)), dim3(256),
+                               0, s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, structure, (int64_t)0, (int64_t)0,
+                               (int64_t)0);
+        else
+            hipLaunchKernelGGL((k_dgemm<BT, 64>), dim3((unsigned)ceil_div(M, 64), (unsigned)ceil_div(N, 64)), dim3(256), 0,
+                               s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, structure, (int64_t)0, (int64_t)0,
+                               (int64_t)0);
+    } else
         hipLaunchKernelGGL(k_dgemm_valu<BT>, dim3((unsigned)ceil_div(M, 64), (unsigned)ceil_div(N, 64)), dim3(256), 0,
                            s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
     return check_launch("rf_solve: dgemm");
