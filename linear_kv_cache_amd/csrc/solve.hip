@@ -176,73 +176,6 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, 
     }
 }
 
-// ---- fp64 GEMM on the vector ALUs, 64 x 64 tiles: for narrow operands (N or M < 512), where
-// the matrix-core kernel's 128 x 128 tiles would leave most CUs idle.
-template <bool BT>
-__global__ __launch_bounds__(256) void k_dgemm_valu(int64_t M, int64_t N, int64_t K, double alpha, const double* A,
-                                               int64_t lda, const double* B, int64_t ldb, double beta, double* C,
-                                               int64_t ldc) {
-    constexpr int BM = 64, BN = 64, BK = 16;
-    __shared__ double As[BK][BM + 1];
-    __shared__ double Bs[BK][BN + 1];
-    const int t = threadIdx.x;
-    const int tx = t & 15, ty = t >> 4;
-    const int64_t m0 = (int64_t)blockIdx.x * BM, n0 = (int64_t)blockIdx.y * BN;
-    double acc[4][4] = {};
-    for (int64_t k0 = 0; k0 < K; k0 += BK) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int idx = t + 256 * e;
-            const int m = idx >> 4, k = idx & 15;
-            const int64_t gm = m0 + m, gk = k0 + k;
-            As[k][m] = (gm < M && gk < K) ? A[gm * lda + gk] : 0.0;
-            if (BT) {
-                const int64_t gn = n0 + m;
-                Bs[k][m] = (gn < N && gk < K) ? B[gn * ldb + gk] : 0.0;
-            } else {
-                const int kk = idx >> 6, n = idx & 63;
-                const int64_t gk2 = k0 + kk, gn = n0 + n;
-                Bs[kk][n] = (gn < N && gk2 < K) ? B[gk2 * ldb + gn] : 0.0;
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < BK; ++k) {
-            double a[4], b[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) a[r] = As[k][ty + 16 * r];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) b[c] = Bs[k][tx + 16 * c];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) acc[r][c] = fma(a[r], b[c], acc[r][c]);
-        }
-        __syncthreads();
-    }
-    double cv[4][4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int64_t gm = m0 + ty + 16 * r, gn = n0 + tx + 16 * c;
-            cv[r][c] = (beta != 0.0 && gm < M && gn < N) ? C[gm * ldc + gn] : 0.0;
-        }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int64_t gm = m0 + ty + 16 * r;
-        if (gm >= M) continue;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int64_t gn = n0 + tx + 16 * c;
-            if (gn >= N) continue;
-            double v = alpha * acc[r][c];
-            if (beta != 0.0) v += beta * cv[r][c];
-            C[gm * ldc + gn] = v;
-        }
-    }
-}
-
 // Z = 0 except its diagonal 64 x 64 blocks, which are the transposed inverses of L's diagonal
 // blocks (Dinv holds L_JJ^-1 row-major): Z_JJ = (L_JJ^T)^-1.
 __global__ void k_zdiag(const double* Dinv, int64_t d, double* Z) {
@@ -544,21 +477,15 @@ template <bool BT>
 static rf_status dgemm(hipStream_t s, int64_t M, int64_t N, int64_t K, double alpha, const double* A, int64_t lda,
                        const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int structure = kFull) {
     if (M <= 0 || N <= 0) return RF_OK;
-    if ((M >= 512 && N >= 512) || structure != kFull) {
-        // 128 x 128 tiles, unless they would not fill two rounds of the 256 CUs
-        int64_t tiles = ceil_div(M, 128) * ceil_div(N, 128);
-        if (structure & kLowerOnly) tiles = (tiles + ceil_div(M, 128)) / 2;
-        if (tiles >= 512)
-            hipLaunchKernelGGL((k_dgemm<BT, 128>), dim3((unsigned)ceil_div(M, 128), (unsigned)ceil_div(N, 128)), dim3(256),
-                               0, s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, structure, (int64_t)0, (int64_t)0,
-                               (int64_t)0);
-        else
-            hipLaunchKernelGGL((k_dgemm<BT, 64>), dim3((unsigned)ceil_div(M, 64), (unsigned)ceil_div(N, 64)), dim3(256), 0,
-                               s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, structure, (int64_t)0, (int64_t)0,
-                               (int64_t)0);
-    } else
-        hipLaunchKernelGGL(k_dgemm_valu<BT>, dim3((unsigned)ceil_div(M, 64), (unsigned)ceil_div(N, 64)), dim3(256), 0,
-                           s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+    // 128 x 128 tiles, unless they would not fill two rounds of the 256 CUs
+    int64_t tiles = ceil_div(M, 128) * ceil_div(N, 128);
+    if (structure & kLowerOnly) tiles = (tiles + ceil_div(M, 128)) / 2;
+    if (tiles >= 512)
+        hipLaunchKernelGGL((k_dgemm<BT, 128>), dim3((unsigned)ceil_div(M, 128), (unsigned)ceil_div(N, 128)), dim3(256), 0,
+                           s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, structure, (int64_t)0, (int64_t)0, (int64_t)0);
+    else
+        hipLaunchKernelGGL((k_dgemm<BT, 64>), dim3((unsigned)ceil_div(M, 64), (unsigned)ceil_div(N, 64)), dim3(256), 0, s,
+                           M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, structure, (int64_t)0, (int64_t)0, (int64_t)0);
     return check_launch("rf_solve: dgemm");
 }
 
@@ -659,10 +586,13 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, double lambda,
         RF_TRY(check_launch("rf_solve: potrf"));
         const int64_t rem = d - c0 - kNB;
         if (rem <= 0) continue;
-        // L21 = A21 L11^-T in place: the 64-column product runs on 64 x 64 tiles, each of which
+        // L21 = A21 L11^-T in place on the matrix cores: one column of 64 x 64 tiles, each of which
         // reads all of its rows of A21 before writing them
         double* panel = w.C + (c0 + kNB) * d + c0;
-        RF_TRY(dgemm<true>(s, rem, kNB, kNB, 1.0, panel, d, w.Dinv + c0 * kNB, kNB, 0.0, panel, d));
+        hipLaunchKernelGGL((k_dgemm<true, 64>), dim3((unsigned)ceil_div(rem, 64), 1u), dim3(256), 0, s, rem,
+                           (int64_t)kNB, (int64_t)kNB, 1.0, (const double*)panel, d, (const double*)(w.Dinv + c0 * kNB),
+                           (int64_t)kNB, 0.0, panel, d, (int)kFull, (int64_t)0, (int64_t)0, (int64_t)0);
+        RF_TRY(check_launch("rf_solve: panel"));
         RF_TRY(dgemm<true>(s, rem, rem, kNB, -1.0, panel, d, panel, d, 1.0, w.C + (c0 + kNB) * d + c0 + kNB, d,
                            kLowerOnly));
     }
