@@ -50,14 +50,18 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, 
     static_assert(BM == 64 || BM == 128, "64 x 64 or 128 x 128 tiles");
     constexpr int BN = BM, BK = 32, PAD = 2;
     constexpr int WT = BM / 2, WB = WT / 16;   // wave tile and its 16 x 16 blocks per side
-    constexpr int EPT = BM * BK / 256;          // operand elements per thread per k-step
-    constexpr int TPR = BK / EPT;               // threads per K-contiguous row
-    constexpr int TPK = BN / EPT;               // threads per k-row of an N-contiguous operand
+    // Loads are 16-byte chunks, and each wave instruction covers whole operand rows (coalesced).
+    // K-contiguous operands (A, and B when BT) stay row-major in LDS, [m][BK + 2]: the 272-byte
+    // row stride is 16-byte aligned for the stores and puts the 16 rows a fragment read touches
+    // (plus the next k's 16 lanes) on distinct banks.  An N-contiguous B stays [k][BN + 2].
+    constexpr int CPR_K = BK / 2, RPP_K = 256 / CPR_K, PK = BM / RPP_K;   // chunks/row, rows/pass, passes
+    constexpr int CPR_N = BN / 2, RPP_N = 256 / CPR_N, PN = BK / RPP_N;
+    constexpr int PB = BT ? PK : PN;
     A += (int64_t)blockIdx.z * sA;
     B += (int64_t)blockIdx.z * sB;
     C += (int64_t)blockIdx.z * sC;
-    __shared__ double As[2][BK][BM + PAD];
-    __shared__ double Bs[2][BK][BN + PAD];
+    __shared__ __attribute__((aligned(16))) double As[2][BM][BK + PAD];
+    __shared__ __attribute__((aligned(16))) double Bs[2][BT ? BN : BK][BT ? BK + PAD : BN + PAD];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t m0 = (int64_t)blockIdx.x * BM, n0 = (int64_t)blockIdx.y * BN;
@@ -66,52 +70,44 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, 
     if (structure & kUpperOperands) kbeg = (m0 > n0 ? m0 : n0) / BK * BK;
     if (structure & kUpperA) kbeg = m0 / BK * BK;
     if ((structure & kUpperB) && n0 + BN < K) kend = n0 + BN;
-    // loaders: a K-contiguous operand gives each thread EPT consecutive k of one row; an
-    // N-contiguous operand gives EPT consecutive n of one k-row.  A run wholly in range and
-    // 16-byte aligned is read as 16-byte loads, otherwise element by element.
-    double ra[EPT], rb[EPT];
-    auto runv = [&](const double* p, bool whole, int valid, double (&r)[EPT]) {
-        if (whole && ((uintptr_t)p & 15) == 0) {
-#pragma unroll
-            for (int e = 0; e < EPT; e += 2) {
-                const f64x2 v = *(const f64x2*)(p + e);
-                r[e] = v[0];
-                r[e + 1] = v[1];
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < EPT; ++e) r[e] = e < valid ? p[e] : 0.0;
-        }
+    f64x2 ra[PK], rb[PB];
+    // two consecutive elements of a row; a pair wholly in range and 16-byte aligned is one load
+    auto pair = [&](const double* row, bool row_ok, int64_t c, int64_t lim) -> f64x2 {
+        const double* q = row + c;
+        if (row_ok && c + 1 < lim && ((uintptr_t)q & 15) == 0) return *(const f64x2*)q;
+        return f64x2{row_ok && c < lim ? q[0] : 0.0, row_ok && c + 1 < lim ? q[1] : 0.0};
     };
-    auto span = [&](int64_t lim, int64_t at) { return (int)(lim - at < EPT ? (lim - at > 0 ? lim - at : 0) : EPT); };
     auto load = [&](int64_t k0) {
-        {
-            const int64_t m = m0 + t / TPR;
-            const int64_t k = k0 + (t % TPR) * EPT;
-            const int valid = m < M ? span(K, k) : 0;
-            runv(A + (m < M ? m : 0) * lda + (valid > 0 ? k : 0), valid == EPT, valid, ra);
+        const int64_t kc = k0 + 2 * (t % CPR_K);
+#pragma unroll
+        for (int u = 0; u < PK; ++u) {
+            const int64_t m = m0 + t / CPR_K + RPP_K * u;
+            ra[u] = pair(A + (m < M ? m : 0) * lda, m < M, kc, K);
         }
         if (BT) {
-            const int64_t n = n0 + t / TPR;
-            const int64_t k = k0 + (t % TPR) * EPT;
-            const int valid = n < N ? span(K, k) : 0;
-            runv(B + (n < N ? n : 0) * ldb + (valid > 0 ? k : 0), valid == EPT, valid, rb);
+#pragma unroll
+            for (int u = 0; u < PK; ++u) {
+                const int64_t n = n0 + t / CPR_K + RPP_K * u;
+                rb[u] = pair(B + (n < N ? n : 0) * ldb, n < N, kc, K);
+            }
         } else {
-            const int64_t k = k0 + t / TPK;
-            const int64_t nn = n0 + (t % TPK) * EPT;
-            const int valid = k < K ? span(N, nn) : 0;
-            runv(B + (k < K ? k : 0) * ldb + (valid > 0 ? nn : 0), valid == EPT, valid, rb);
+            const int64_t nc = n0 + 2 * (t % CPR_N);
+#pragma unroll
+            for (int u = 0; u < PN; ++u) {
+                const int64_t k = k0 + t / CPR_N + RPP_N * u;
+                rb[u] = pair(B + (k < K ? k : 0) * ldb, k < K, nc, N);
+            }
         }
     };
     auto store = [&](int buf) {
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) As[buf][(t % TPR) * EPT + e][t / TPR] = ra[e];
+        for (int u = 0; u < PK; ++u) *(f64x2*)&As[buf][t / CPR_K + RPP_K * u][2 * (t % CPR_K)] = ra[u];
         if (BT) {
 #pragma unroll
-            for (int e = 0; e < EPT; ++e) Bs[buf][(t % TPR) * EPT + e][t / TPR] = rb[e];
+            for (int u = 0; u < PK; ++u) *(f64x2*)&Bs[buf][t / CPR_K + RPP_K * u][2 * (t % CPR_K)] = rb[u];
         } else {
 #pragma unroll
-            for (int e = 0; e < EPT; ++e) Bs[buf][t / TPK][(t % TPK) * EPT + e] = rb[e];
+            for (int u = 0; u < PN; ++u) *(f64x2*)&Bs[buf][t / CPR_N + RPP_N * u][2 * (t % CPR_N)] = rb[u];
         }
     };
     f64x4 acc[WB][WB];
@@ -132,9 +128,10 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, 
                 const int kr = ks + (lane >> 4);
                 double a[WB], b[WB];
 #pragma unroll
-                for (int i = 0; i < WB; ++i) a[i] = As[cur][kr][wm * WT + i * 16 + (lane & 15)];
+                for (int i = 0; i < WB; ++i) a[i] = As[cur][wm * WT + i * 16 + (lane & 15)][kr];
 #pragma unroll
-                for (int j = 0; j < WB; ++j) b[j] = Bs[cur][kr][wn * WT + j * 16 + (lane & 15)];
+                for (int j = 0; j < WB; ++j)
+                    b[j] = BT ? Bs[cur][wn * WT + j * 16 + (lane & 15)][kr] : Bs[cur][kr][wn * WT + j * 16 + (lane & 15)];
 #pragma unroll
                 for (int i = 0; i < WB; ++i)
 #pragma unroll
