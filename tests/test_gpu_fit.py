@@ -73,6 +73,31 @@ def test_fit_bf16_widths_not_a_power_of_two_blocks():
         assert max(ew) <= W_TOL and max(eb) <= W_TOL
 
 
+def test_gram_strided_rows_and_no_targets():
+    """X as a column slice of a wider buffer (ldx = d + 256), the Y_l as views into one
+    layer-major buffer (ldy = L d), a ragged 700-row chunk; and a state with no targets."""
+    from linear_kv_cache_amd.runner import GramState
+    cfg = SMALL_BF16
+    d, L, rows = cfg.d, 3, 700
+    X = synth.hidden_states(cfg, rows, "calib", device="cuda")
+    Ys = [synth.late_layer_inputs(cfg, X, cfg.split + l) for l in range(L)]
+    wide = torch.zeros(rows, d + 256, dtype=X.dtype, device="cuda")
+    wide[:, 128:128 + d] = X
+    Xv = wide[:, 128:128 + d]
+    Yall = torch.cat(Ys, dim=1).contiguous()
+    Yv = [Yall[:, l * d:(l + 1) * d] for l in range(L)]
+    assert Xv.stride(0) == d + 256 and Yv[0].stride(0) == L * d
+    st = GramState(d, L, cfg.torch_dtype, "cuda")
+    st.accumulate(Xv, Yv)
+    st0 = GramState(d, 0, cfg.torch_dtype, "cuda")
+    st0.accumulate(Xv, [])
+    torch.cuda.synchronize()
+    res = _gram_errors(dict(X=X, Ys=Ys, state=st))
+    log(f"[fit] strided rows gram={res}")
+    assert res["n"] == rows and max(res["e_xx"], res["e_yx"]) <= 1e-5 and max(res["e_sx"], res["e_sy"]) <= 1e-12
+    assert torch.equal(st0.S_xx(), st.S_xx()) and torch.equal(st0.s_x(), st.s_x()) and int(st0.n().item()) == rows
+
+
 def test_fit_not_spd_reports_pivot():
     case = FitCase(synth.C1, 1024, [1024], 0.0, zero_column=77, n_targets=1)
     res = run_fit_case(case)
