@@ -116,8 +116,9 @@ rf_status rf_gram_accumulate(const rf_gram_desc* desc, void* d_state,
  *     B_l  = S_yx,l - n mu_l^T mu_x          (centred cross moments, [d_out][d_in])
  *     W_l  = B_l (C + lambda I)^-1           (out-feature major: row o is the map of output o)
  *     b_l  = mu_l - mu_x W_l^T
- * so that the prediction is y = x W_l^T + b_l.  C + lambda I is factored by Cholesky and
- * inverted by triangular solves in fp64.  The product B_l (C + lambda I)^-1 runs on the bf16
+ * so that the prediction is y = x W_l^T + b_l.  C + lambda I = L L^T is factored by Cholesky
+ * and inverted in fp64 (L^-T by recursive doubling over diagonal blocks, then the lower
+ * triangle of L^-T L^-1, mirrored where read).  The product B_l (C + lambda I)^-1 runs on the bf16
  * matrix cores in three-term split precision (each factor, equilibrated by the square root of
  * the diagonal of C + lambda I, is split into two bf16 parts) with fp32 accumulation: about
  * 1e-5 of max |W_l| from the fp64 product on well-scaled data.
