@@ -125,7 +125,8 @@ rf_status rf_gram_accumulate(const rf_gram_desc* desc, void* d_state,
  *
  *  targets : host array of n_sel target indices in [0, n_targets)
  *  d_W     : [n_sel][d][d] fp32 out, may be NULL; 16-B aligned
- *  d_W_lp  : [n_sel][d][d] bf16 out (the map as the fill consumes it), may be NULL; 16-B aligned
+ *  d_W_lp  : [n_sel][d][d] bf16 out, may be NULL; 16-B aligned.  Written in the fill's packed
+ *            layout (as rf_pack_weights with rope_head_dim 0 would leave it), ready for rf_fill
  *  d_b     : [n_sel][d] fp32 out, may be NULL
  *  d_info  : one int32 out: 0 = success; k > 0 = C + lambda I is not positive definite and
  *            the k-th leading minor (1-based) is the first that fails.  The outputs are then
@@ -191,7 +192,8 @@ rf_status rf_rope_table(double base, int32_t head_dim, int64_t n_pos, float* d_t
  * layers not listed are never written: exact rows skip the map (project page, Fig. 2).
  *
  * Weights, per listed layer (host arrays of n_layers device pointers):
- *   W_map[l] : [d][d]                dtype    out-feature major map
+ *   W_map[l] : [d][d]                dtype    out-feature major map; BF16 maps in the packed
+ *                                             layout of rf_pack_weights (rope_head_dim 0)
  *   b_map[l] : [d]                   fp32
  *   gamma[l] : [d]                   fp32
  *   W_k[l]   : [n_kv_heads*head_dim][d] dtype  head-major output rows
@@ -205,6 +207,25 @@ rf_status rf_rope_table(double base, int32_t head_dim, int64_t n_pos, float* d_t
  * Supported: d % 256 == 0, head_dim in {64, 128}, (n_kv_heads*head_dim) % 256 == 0,
  * dtype F32 or BF16 (all of X, maps, projections and pools share it).
  * ------------------------------------------------------------------------------------- */
+/* ---------------------------------------------------------------------------------------
+ * Weight packing for the fill's matrix-core products (a layout change, no arithmetic).
+ * The bf16 fill reads its map rows straight into the matrix-core operand registers, so they
+ * are stored in fragment order.  Copies a row-major [rows][ld_src] bf16 matrix into d_dst
+ * (rows * cols elements, no padding) as consecutive 256-row tiles; within a tile, element
+ * (r, k) (r the row in the tile) moves to
+ *     (k/64)*16384 + (r'/64)*4096 + ((k%64)/16)*1024 + ((r'%64)/32)*512
+ *     + (((k%16)/8)*32 + r'%32)*8 + k%8
+ * where r' is the packed position of row r: r' = r when rope_head_dim is 0.  Otherwise the
+ * rows of each tile are grouped by rotate-half pairs: packed row r' = 64w + 32i + j
+ * (w, i, j in [0,4), [0,2), [0,32)) holds tile row (q / h) * hd + q % h + i * h with
+ * q = 32w + j, hd = rope_head_dim, h = hd / 2 (pair partners i = 0, 1 share w and j).
+ * Supported: BF16, rows % 256 == 0, cols % 64 == 0, rows and cols <= 65536, rope_head_dim in
+ * {0, 64, 128}; ld_src >= cols and a multiple of 8; both buffers 16-B aligned and disjoint.
+ * Asynchronous on ``stream``; nothing is allocated.
+ * ------------------------------------------------------------------------------------- */
+rf_status rf_pack_weights(rf_dtype dtype, int64_t rows, int64_t cols, const void* d_src, int64_t ld_src,
+                          int32_t rope_head_dim, void* d_dst, void* stream);
+
 typedef struct {
     int32_t d;
     int32_t n_kv_heads;

@@ -77,6 +77,7 @@ _sig = {
                            _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "rf_cache_layout": (C.c_int, [C.POINTER(rf_cache_desc), C.POINTER(rf_cache_layout_t)]),
     "rf_rope_table": (C.c_int, [C.c_double, C.c_int32, C.c_int64, _P, _P]),
+    "rf_pack_weights": (C.c_int, [C.c_int, C.c_int64, C.c_int64, _P, C.c_int64, C.c_int32, _P, _P]),
     "rf_fill_workspace_bytes": (C.c_size_t, [C.POINTER(rf_fill_weights), C.c_int64]),
     "rf_fill": (C.c_int, [C.POINTER(rf_fill_weights), C.c_int32, _P, C.c_int64, C.c_int64, C.c_int64, C.c_int64,
                           C.POINTER(rf_cache_desc), C.POINTER(_P), C.POINTER(_P), _P, C.c_int64, _P, C.c_int64,
@@ -192,9 +193,18 @@ def rf_rope_table(base: float, head_dim: int, n_pos: int, table, stream=None):
     _check(_lib.rf_rope_table(float(base), head_dim, n_pos, _ptr(table), _stream(stream)))
 
 
+def rf_pack_weights(W, dst, rope_head_dim: int = 0, stream=None):
+    """W: [rows, >=cols] bf16 tensor (row stride = ld_src); dst: rows*cols bf16 elements."""
+    rows, cols = W.shape
+    _check(_lib.rf_pack_weights(_dtype_code(W.dtype), rows, cols, _ptr(W), W.stride(0), int(rope_head_dim), _ptr(dst),
+                                _stream(stream)))
+
+
 @dataclass
 class FillWeights:
-    """Per-layer weights of the layers one rf_fill call fills (tensors on the device)."""
+    """Per-layer weights of the layers one rf_fill call fills (tensors on the device).
+
+    BF16 maps are in the packed layout (rf_pack_weights, or rf_solve's bf16 output)."""
 
     d: int
     n_kv_heads: int

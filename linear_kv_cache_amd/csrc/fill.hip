@@ -78,6 +78,9 @@ __device__ inline void store4<float>(float* p, float a, float b, float c, float 
 // The bf16 instantiation runs the software-pipelined core; fp32 runs the plain tile loop.
 template <typename T> struct FillCore { using G = TileGemm<T, kFT, kTT, false, false>; };
 template <> struct FillCore<bf16_t> { using G = PipeGemm; };
+// The map's bf16 weights come pre-packed in fragment order and skip LDS.
+template <typename T> struct MapCore { using G = typename FillCore<T>::G; };
+template <> struct MapCore<bf16_t> { using G = PackedAGemm; };
 
 // Tile of this work-group: layer slot g, feature tile mt, token tile tt.  The grid is 1-D over
 // (layer, feature tile, token tile), renumbered so that each XCD works on a compact block of
@@ -98,6 +101,10 @@ __device__ inline void fill_gemm(PipeGemm& gm, char* lds, const void* A, int64_t
                                  int64_t ldb, int64_t vb, int nk) {
     gm.run(lds, PipeOperand{A, lda, va}, PipeOperand{B, ldb, vb}, nk);
 }
+__device__ inline void fill_gemm(PackedAGemm& gm, char* lds, const void* A, int64_t lda, int64_t va, const void* B,
+                                 int64_t ldb, int64_t vb, int nk) {
+    gm.run(lds, PipeOperand{A, lda, va}, PipeOperand{B, ldb, vb}, nk);
+}
 
 // bf16: the tile of u' is staged in LDS as [token][feature] (512 bytes per token, 16-byte
 // chunk c of token n in slot c ^ (n & 31)) and leaves as whole 512-byte row segments of H.
@@ -106,10 +113,11 @@ template <typename T> struct MapStage { static constexpr bool kLds = false; stat
 template <> struct MapStage<bf16_t> { static constexpr bool kLds = true; static constexpr int kBytes = kTT * kFT * 2; };
 
 template <typename T>
-__global__ __launch_bounds__(FillCore<T>::G::kThr) void k_fill_map(MapArgs a) {
-    using G = typename FillCore<T>::G;
-    constexpr int kRedOff = MapStage<T>::kBytes;  // [2][kTT] fp32 partial sums after the stage
-    constexpr int kEpi = kRedOff + 2 * kTT * 4;
+__global__ __launch_bounds__(MapCore<T>::G::kThr) void k_fill_map(MapArgs a) {
+    using G = typename MapCore<T>::G;
+    constexpr int kWaveRows = G::kThr / 64 / G::WGN;
+    constexpr int kRedOff = MapStage<T>::kBytes;  // [kWaveRows][kTT] fp32 partial sums after the stage
+    constexpr int kEpi = kRedOff + kWaveRows * kTT * 4;
     constexpr int kLdsBytes = G::LDS_BYTES > kEpi ? G::LDS_BYTES : kEpi;
     __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
     int g, mt, tt;
@@ -121,9 +129,9 @@ __global__ __launch_bounds__(FillCore<T>::G::kThr) void k_fill_map(MapArgs a) {
 
     // the main loop ended on a barrier: LDS is free
     const int lane = threadIdx.x & 63;
-    const int wm = (threadIdx.x >> 6) / G::WGN;   // wave row (two per tile)
+    const int wm = (threadIdx.x >> 6) / G::WGN;   // wave row
     float* red = (float*)(lds + kRedOff);
-    // bias and gamma of this lane's 16 groups of 4 features, read once (16-byte loads) before any
+    // bias and gamma of this lane's SM x 4 groups of 4 features, read once (16-byte loads) before any
     // staging write, so no LDS read waits behind the writes
     f32x4 bb[G::SM][4], gg[G::SM][4];
 #pragma unroll
@@ -182,8 +190,12 @@ __global__ __launch_bounds__(FillCore<T>::G::kThr) void k_fill_map(MapArgs a) {
     {
         const int nl = threadIdx.x;
         const int64_t n = n0 + nl;
-        if (nl < kTT && n < a.rows)
-            a.psum[g * a.ps_slot + n * a.n_ps + mt] = red[nl] + red[kTT + nl];
+        if (nl < kTT && n < a.rows) {
+            float ps = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaveRows; ++w) ps += red[w * kTT + nl];
+            a.psum[g * a.ps_slot + n * a.n_ps + mt] = ps;
+        }
     }
 }
 
@@ -383,6 +395,35 @@ __global__ void k_rope_table(double base, int32_t dh, int64_t n_pos, float* out)
     out[2 * idx + 1] = (float)sin(phi);
 }
 
+// Source row, within its 256-row tile, of packed row p.  hd == 0 keeps the order; otherwise
+// wave w's block i takes rows of pairs (f, f + hd/2) of the tile's heads: pair q = 32 w + r % 32,
+// first partner in block 0, second in block 1, so a RoPE pair meets in one lane's registers.
+__device__ inline int packed_source_row(int p, int hd) {
+    if (hd == 0) return p;
+    const int half = hd >> 1;
+    const int q = ((p >> 6) << 5) + (p & 31);
+    return (q / half) * hd + q % half + ((p >> 5) & 1) * half;
+}
+
+// One 16-byte chunk (8 consecutive k of one row) per thread, in packed order: writes are
+// contiguous, reads are 16-byte pieces of source rows.
+__global__ void k_pack_weights(const bf16_t* __restrict__ src, int64_t ld, int64_t cols, int32_t hd,
+                               int64_t n_chunks, bf16_t* __restrict__ dst) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= n_chunks) return;
+    const int64_t e = c * 8;
+    const int64_t tile_elems = 256 * cols;
+    const int64_t tile = e / tile_elems;
+    const int64_t rem = e - tile * tile_elems;
+    const int64_t kt = rem >> 14;                   // 16384 elements per k-step
+    const int r2 = (int)(rem & 16383);
+    const int w = r2 >> 12, kk = (r2 >> 10) & 3, i = (r2 >> 9) & 1, lane = (r2 >> 3) & 63;
+    const int p = (w << 6) + (i << 5) + (lane & 31);
+    const int64_t row = tile * 256 + packed_source_row(p, hd);
+    const int64_t k = kt * 64 + kk * 16 + (lane >> 5) * 8;
+    *(u32x4*)(dst + e) = *(const u32x4*)(src + row * ld + k);
+}
+
 static size_t slot_bytes(const rf_fill_weights* w, int64_t rows) {
     const size_t hb = round_up((size_t)rows * w->d * elem_bytes(w->dtype), 256);
     const size_t pb = round_up((size_t)rows * (w->d / kFT) * sizeof(float), 256);
@@ -422,7 +463,7 @@ static rf_status launch_fill(const rf_fill_weights* w, int32_t n_layers, const v
         }
         ma.tok_tiles = tok_tiles;
         ka.tok_tiles = tok_tiles;
-        hipLaunchKernelGGL(k_fill_map<T>, dim3((w->d / kFT) * tok_tiles * gsz), dim3(FillCore<T>::G::kThr), 0, stream, ma);
+        hipLaunchKernelGGL(k_fill_map<T>, dim3((w->d / kFT) * tok_tiles * gsz), dim3(MapCore<T>::G::kThr), 0, stream, ma);
         rf_status st = check_launch("rf_fill: map kernel");
         if (st != RF_OK) return st;
         const dim3 kv_grid((2 * ka.kvw / kFT) * tok_tiles * gsz);
@@ -453,6 +494,25 @@ rf_status rf_rope_table(double base, int32_t head_dim, int64_t n_pos, float* d_t
     hipLaunchKernelGGL(k_rope_table, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, (hipStream_t)stream,
                        base, head_dim, n_pos, d_table);
     return check_launch("rf_rope_table");
+}
+
+rf_status rf_pack_weights(rf_dtype dtype, int64_t rows, int64_t cols, const void* d_src, int64_t ld_src,
+                          int32_t rope_head_dim, void* d_dst, void* stream) {
+    clear_error();
+    RF_REQUIRE(dtype == RF_BF16, RF_ERR_UNSUPPORTED, "rf_pack_weights: only BF16 weights are packed");
+    RF_REQUIRE(rows >= 0 && rows % 256 == 0 && cols >= 0 && cols % 64 == 0, RF_ERR_UNSUPPORTED,
+               "rf_pack_weights: rows must be a multiple of 256 and cols a multiple of 64");
+    RF_REQUIRE(rope_head_dim == 0 || rope_head_dim == 64 || rope_head_dim == 128, RF_ERR_UNSUPPORTED,
+               "rf_pack_weights: rope_head_dim must be 0, 64 or 128");
+    RF_REQUIRE(rows <= (1 << 16) && cols <= (1 << 16), RF_ERR_UNSUPPORTED, "rf_pack_weights: rows and cols must be <= 65536");
+    if (rows == 0 || cols == 0) return RF_OK;
+    RF_REQUIRE(d_src && d_dst, RF_ERR_INVALID_ARG, "rf_pack_weights: null pointer argument");
+    RF_REQUIRE(ld_src >= cols && ld_src % 8 == 0 && aligned(d_src, 16) && aligned(d_dst, 16), RF_ERR_INVALID_ARG,
+               "rf_pack_weights: source rows must be >= cols long with a stride of 8 elements, 16-byte aligned");
+    const int64_t n_chunks = rows * cols / 8;
+    hipLaunchKernelGGL(k_pack_weights, dim3((unsigned)ceil_div(n_chunks, 256)), dim3(256), 0, (hipStream_t)stream,
+                       (const bf16_t*)d_src, ld_src, cols, rope_head_dim, n_chunks, (bf16_t*)d_dst);
+    return check_launch("rf_pack_weights");
 }
 
 size_t rf_fill_workspace_bytes(const rf_fill_weights* w, int64_t max_rows) {

@@ -327,6 +327,205 @@ struct PipeGemmW {
     }
 };
 
+// Variant with a pre-packed A operand (weights) for the fill's products.
+//
+// The four waves are stacked along m: wave w computes rows 64 w .. 64 w + 63 of the 256 x 256
+// tile against all 256 columns (2 x 8 blocks of v_mfma_f32_32x32x16_bf16, 256 accumulation
+// registers).  A wave's A rows belong to it alone, so A skips LDS: it is stored pre-packed in
+// fragment order (rf_pack_weights) and every fragment is one 1 KiB contiguous load straight
+// into registers, issued two k-steps ahead.  Only B is staged through LDS as in PipeGemmW,
+// which halves the LDS stage writes per k-step (the data movement that lowers the
+// power-limited clock most).
+//
+// Packed A, one 256-row tile of K columns: element (r, k) sits at element offset
+//   (k / 64) * 16384 + (r / 64) * 4096 + ((k % 64) / 16) * 1024 + ((r % 64) / 32) * 512
+//   + (((k % 16) / 8) * 32 + r % 32) * 8 + k % 8,
+// i.e. k-step, wave, k-slice, block, then the 64 lanes' 16-byte fragments.
+struct PackedAGemm {
+    static constexpr int kThr = 256;
+    static constexpr int BM = 256, BN = 256, BK = 64;
+    static constexpr int ROWB = 128;                       // bytes of one B row per k-step
+    static constexpr int STAGE_BYTES = BN * ROWB;          // 32 KiB
+    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+    static constexpr int WGM = 4, WGN = 1;
+    static constexpr int WTM = 64, WTN = 256;
+    static constexpr int SM = 2, SN = 8;
+    static constexpr int VB = BN * 8 / kThr;               // 16-byte vectors per thread per step
+    static constexpr int ROWS_J = kThr / 8;                // rows between a thread's vectors
+    static constexpr int kStepBytes = BM * BK * 2;         // packed A bytes per k-step
+
+    f32x16 acc[SM][SN];
+
+    struct Regs {
+        u32x4 b[VB];
+    };
+
+    // Full K loop over ``nk`` k-steps (even).  A.ptr is the packed tile; A.ld and A.valid are
+    // unused (a packed tile always holds 256 rows).
+    __device__ inline void run(char* lds, const PipeOperand& A, const PipeOperand& B, int nk) {
+        const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+#pragma unroll
+        for (int i = 0; i < SM; ++i)
+#pragma unroll
+            for (int j = 0; j < SN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+        if (nk <= 0) return;
+        const __amdgpu_buffer_rsrc_t ra =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(A.ptr), (short)0, nk * kStepBytes, 0x00020000);
+        int64_t nb = B.valid < BN ? B.valid : BN;
+        if (nb < 0) nb = 0;
+        const __amdgpu_buffer_rsrc_t rb =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(B.ptr), (short)0, (int)(nb * B.ld * 2), 0x00020000);
+        // B staging as in PipeGemmW: row (t >> 3) + 32 j, logical chunk t & 7, slot
+        // chunk ^ ((row >> 1) & 7)
+        const int gB = (int)((t >> 3) * B.ld * 2) + (t & 7) * 16;
+        const int strideB = (int)(ROWS_J * B.ld * 2);
+        const int wofs = (t >> 3) * ROWB + (((t & 7) ^ ((t >> 4) & 7)) << 4);
+        const int wstep = ROWS_J * ROWB;
+        const int rB = (lane & 31) * ROWB;
+        int cofs[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) cofs[kk] = ((2 * kk + (lane >> 5)) ^ ((lane >> 1) & 7)) << 4;
+        // the wave offset stays in the vector offset: a scalar offset must be provably uniform
+        const int av = wave * 8192 + lane * 16;
+
+        // A fragments of two k-steps (parity p), 4 slices x 2 blocks each
+        u32x4 fa[2][4][SM];
+        auto aload = [&](int p, int kk, int kt) {
+            const int kc = kt < nk ? kt : nk - 1;
+#pragma unroll
+            for (int i = 0; i < SM; ++i)
+                fa[p][kk][i] = __builtin_amdgcn_raw_buffer_load_b128(ra, av, kc * kStepBytes + (kk * 2 + i) * 1024, 0);
+        };
+        auto gload_b = [&](Regs& g, int kt, int j0, int j1) {
+            const int kc = kt < nk ? kt : nk - 1;
+#pragma unroll
+            for (int j = j0; j < j1; ++j) g.b[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, gB + j * strideB, kc * ROWB, 0);
+        };
+        auto swrite_b = [&](const Regs& g, char* st, int j0, int j1) {
+#pragma unroll
+            for (int j = j0; j < j1; ++j) *(u32x4*)(st + wofs + j * wstep) = g.b[j];
+        };
+        u32x4 fb[2][SN];
+        auto fread = [&](int buf, const char* st, int kk) {
+#pragma unroll
+            for (int j = 0; j < SN; ++j) fb[buf][j] = *(const u32x4*)(st + rB + j * 32 * ROWB + cofs[kk]);
+        };
+        auto mfma = [&](int buf, int p, int kk, int j0, int j1) {
+#pragma unroll
+            for (int j = j0; j < j1; ++j)
+#pragma unroll
+                for (int i = 0; i < SM; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[p][kk][i]),
+                                                                       __builtin_bit_cast(bf16x8, fb[buf][j]),
+                                                                       acc[i][j], 0, 0, 0);
+        };
+        // group barriers (mask 0x008 MFMA, 0x100 LDS read, 0x200 LDS write, 0x020 VMEM read)
+        auto sched_write_slice = [&]() {
+#pragma unroll
+            for (int i = 0; i < VB / 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, SN - VB / 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, SM, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        };
+        auto sched_read_slice = [&]() {
+#pragma unroll
+            for (int i = 0; i < SN; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, SM, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        };
+        // One k-step: ``g`` holds B of step kt+1 (written to the other stage here, half in each
+        // of the first two slices) and is refilled with step kt+3; each slice's A fragments are
+        // reloaded with step kt+2 once its MFMAs have read them.
+        auto step = [&](int kt, Regs& g, auto par) {
+            constexpr int P = decltype(par)::value;
+            char* cur = lds + P * STAGE_BYTES;
+            char* nxt = lds + (1 - P) * STAGE_BYTES;
+            fread(1, cur, 1);
+            swrite_b(g, nxt, 0, VB / 2);
+            gload_b(g, kt + 3, 0, VB / 2);
+            mfma(0, P, 0, 0, SN);
+            aload(P, 0, kt + 2);
+            sched_write_slice();
+            __builtin_amdgcn_sched_barrier(0);
+            fread(0, cur, 2);
+            swrite_b(g, nxt, VB / 2, VB);
+            gload_b(g, kt + 3, VB / 2, VB);
+            mfma(1, P, 1, 0, SN);
+            aload(P, 1, kt + 2);
+            sched_write_slice();
+            __builtin_amdgcn_sched_barrier(0);
+            fread(1, cur, 3);
+            mfma(0, P, 2, 0, SN);
+            aload(P, 2, kt + 2);
+            sched_read_slice();
+            __builtin_amdgcn_sched_barrier(0);
+            // last slice: half, barrier, first fragments of the next stage, other half
+            mfma(1, P, 3, 0, SN / 2);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            fread(0, nxt, 0);
+            mfma(1, P, 3, SN / 2, SN);
+            aload(P, 3, kt + 2);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // prologue: A of steps 0 and 1, B of step 0 in stage 0, B of steps 1 and 2 in flight
+        // (fences keep the loads in step order, which the in-order load counter relies on)
+        Regs g0, g1;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) aload(0, kk, 0);
+        gload_b(g0, 0, 0, VB);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) aload(1, kk, 1);
+        gload_b(g1, 1, 0, VB);
+        __builtin_amdgcn_sched_barrier(0);
+        swrite_b(g0, lds, 0, VB);
+        __builtin_amdgcn_sched_barrier(0);
+        gload_b(g0, 2, 0, VB);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        fread(0, lds, 0);
+        for (int kt = 0; kt < nk; kt += 2) {
+            step(kt, g1, std::integral_constant<int, 0>{});       // writes B of kt+1, refills kt+3
+            step(kt + 1, g0, std::integral_constant<int, 1>{});   // writes B of kt+2, refills kt+4
+        }
+        // the last fragment reads and stage writes target LDS the caller may reuse
+        __syncthreads();
+    }
+
+    __device__ static inline int row_of(int i, int r) {
+        const int lane = threadIdx.x & 63, wm = threadIdx.x >> 6;
+        return wm * WTM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    }
+    __device__ static inline int col_of(int j) { return j * 32 + (threadIdx.x & 31); }
+};
+
+// Element offset of (r, k) of a packed matrix with K columns: 256-row tiles one after the
+// other, each laid out as above.  The offset splits into the tile's base, a part of the row in
+// the tile and a part of the column (both below 2^31 for K <= 65536).
+__host__ __device__ inline int packed_row_part(int rt) {   // rt in [0, 256)
+    return ((rt >> 6) << 12) + (((rt & 63) >> 5) << 9) + ((rt & 31) << 3);
+}
+__host__ __device__ inline int packed_col_part(int k) {
+    return ((k >> 6) << 14) + (((k & 63) >> 4) << 10) + (((k & 15) >> 3) << 8) + (k & 7);
+}
+__host__ __device__ inline int64_t packed_index(int64_t r, int k, int64_t K) {
+    return (r >> 8) * 256 * K + packed_row_part((int)(r & 255)) + packed_col_part(k);
+}
+
 // One wave per SIMD with two load sets measured best on the fill and Gram products; two waves
 // per SIMD (PipeGemmW<8, 1>, one load set to fit 256 registers per wave) measured equal.
 using PipeGemm = PipeGemmW<4, 2>;

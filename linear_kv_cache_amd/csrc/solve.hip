@@ -403,6 +403,7 @@ __global__ __launch_bounds__(kPipeThreads) void k_wgemm(WArgs a) {
     for (int jb = 0; jb < G::SN; ++jb) {
         const int cl = G::col_of(jb);
         const int64_t c = c0 + cl;
+        const int64_t wl_base = c0 * a.d + packed_row_part(cl);
         float part = 0.f;
 #pragma unroll
         for (int i = 0; i < G::SM; ++i) {
@@ -416,7 +417,10 @@ __global__ __launch_bounds__(kPipeThreads) void k_wgemm(WArgs a) {
                     part += w[e] * (float)(a.sx[j + e] * inv_n);
                 }
                 if (a.W) *(f32x4*)(a.W + c * a.d + j) = f32x4{w[0], w[1], w[2], w[3]};
-                if (a.Wlp) *(u32x2*)(a.Wlp + c * a.d + j) = u32x2{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3])};
+                // the bf16 map in the fill's packed layout (256-row tiles never straddle targets)
+                if (a.Wlp)
+                    *(u32x2*)(a.Wlp + wl_base + packed_col_part((int)j)) =
+                        u32x2{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3])};
             }
         }
         part += __shfl_xor(part, 32);

@@ -9,7 +9,7 @@ import torch
 
 from . import (RF_LAYOUT_CONTIGUOUS, RF_LAYOUT_PAGED, FillWeights, cache_desc, gram_desc, rf_cache_layout,
                rf_fill, rf_fill_workspace_bytes, rf_gram_accumulate, rf_gram_init, rf_gram_state_bytes,
-               rf_gram_state_layout, rf_rope_table, rf_solve, rf_solve_workspace_bytes)
+               rf_gram_state_layout, rf_pack_weights, rf_rope_table, rf_solve, rf_solve_workspace_bytes)
 
 
 def device_bytes(n: int, device) -> torch.Tensor:
@@ -100,6 +100,23 @@ def gather_rows(cache: Cache, pool: torch.Tensor, t0: int, t1: int) -> torch.Ten
     phys = cache.block_table.long()[t // bs]
     blocks = pool.view(-1, H, bs, dh)
     return blocks[phys, :, t % bs, :]
+
+
+def pack_weights(W: torch.Tensor, rope_head_dim: int = 0, stream=None) -> torch.Tensor:
+    """A packed copy (rf_pack_weights) of a bf16 [rows, cols] weight matrix."""
+    out = torch.empty(W.shape[0], W.shape[1], dtype=W.dtype, device=W.device)
+    rf_pack_weights(W, out, rope_head_dim, stream)
+    return out
+
+
+def fill_weights(d: int, n_kv_heads: int, head_dim: int, rms_eps: float, dtype, W_map, b_map, gamma, W_k, W_v,
+                 stream=None) -> FillWeights:
+    """FillWeights from row-major weights: bf16 maps are packed first (the fp32 path reads
+    them as they are)."""
+    if dtype == torch.bfloat16:
+        W_map = [pack_weights(W, 0, stream) for W in W_map]
+    return FillWeights(d, n_kv_heads, head_dim, rms_eps, dtype, list(W_map), list(b_map), list(gamma), list(W_k),
+                       list(W_v))
 
 
 class Filler:

@@ -46,7 +46,7 @@ def run_fill_case(case: FillCase, device="cuda"):
 
     Returns a dict of per-layer relative errors and sentinel status."""
     import linear_kv_cache_amd as rf
-    from linear_kv_cache_amd.runner import Filler, alloc_cache, gather_rows
+    from linear_kv_cache_amd.runner import Filler, alloc_cache, fill_weights, gather_rows
 
     cfg = case.cfg
     layers = cfg.filled_layers[: case.n_layers] if case.n_layers else cfg.filled_layers
@@ -55,9 +55,9 @@ def run_fill_case(case: FillCase, device="cuda"):
     lws = [synth.layer_weights(cfg, l, device=gd, maps=case.maps) for l in layers]
     lws_dev = [synth.LayerWeights(*(x.to(device) for x in (w.W_map, w.b_map, w.gamma, w.W_k, w.W_v))) for w in lws]
     X = synth.hidden_states(cfg, case.t1 - case.t0, "prompt", device=gd).to(device)
-    fw = rf.FillWeights(cfg.d, cfg.n_kv_heads, cfg.head_dim, cfg.rms_eps, cfg.torch_dtype,
-                        [w.W_map for w in lws_dev], [w.b_map for w in lws_dev], [w.gamma for w in lws_dev],
-                        [w.W_k for w in lws_dev], [w.W_v for w in lws_dev])
+    fw = fill_weights(cfg.d, cfg.n_kv_heads, cfg.head_dim, cfg.rms_eps, cfg.torch_dtype,
+                      [w.W_map for w in lws_dev], [w.b_map for w in lws_dev], [w.gamma for w in lws_dev],
+                      [w.W_k for w in lws_dev], [w.W_v for w in lws_dev])
     table = None
     if cfg.paged:
         table = synth.block_table(cfg, T, device=device)

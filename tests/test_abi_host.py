@@ -148,3 +148,23 @@ def test_rope_table_validation():
         with pytest.raises(rf.RidgeFillError):
             rf.rf_rope_table(*args, 256, None)
     rf.rf_rope_table(1e4, 64, 0, 256, None)  # zero positions: nothing to do
+
+
+def test_pack_weights_validation_before_enqueue():
+    bf = torch.bfloat16
+    src = torch.zeros(256, 128, dtype=bf)
+    dst = torch.zeros(256, 128, dtype=bf)
+    cases = [
+        (dict(W=src.float(), dst=dst.float()), rf.RF_ERR_UNSUPPORTED),        # only bf16 is packed
+        (dict(W=src[:100], dst=dst), rf.RF_ERR_UNSUPPORTED),                  # rows % 256
+        (dict(W=src[:, :100], dst=dst), rf.RF_ERR_UNSUPPORTED),               # cols % 64
+        (dict(W=src, dst=dst, rope_head_dim=32), rf.RF_ERR_UNSUPPORTED),
+        (dict(W=torch.zeros(256, 68, dtype=bf)[:, :64], dst=dst), rf.RF_ERR_INVALID_ARG),  # stride % 8
+        (dict(W=src, dst=None), rf.RF_ERR_INVALID_ARG),
+        (dict(W=src, dst=dst.data_ptr() + 2), rf.RF_ERR_INVALID_ARG),         # misaligned output
+    ]
+    for kw, status in cases:
+        with pytest.raises(rf.RidgeFillError) as e:
+            rf.rf_pack_weights(stream=0, **kw)
+        assert e.value.status == status, kw
+    rf.rf_pack_weights(src[:0], dst, stream=0)   # no rows: nothing to do

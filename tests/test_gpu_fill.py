@@ -57,12 +57,11 @@ def test_fill_single_token_and_tile_edges():
 
 
 def test_fill_is_deterministic():
-    import linear_kv_cache_amd as rf
-    from linear_kv_cache_amd.runner import Filler, alloc_cache
+    from linear_kv_cache_amd.runner import Filler, alloc_cache, fill_weights
     cfg = SMALL_BF16
     ws = [synth.layer_weights(cfg, l, device="cuda") for l in cfg.filled_layers[:2]]
-    fw = rf.FillWeights(cfg.d, cfg.n_kv_heads, cfg.head_dim, cfg.rms_eps, cfg.torch_dtype, [w.W_map for w in ws],
-                        [w.b_map for w in ws], [w.gamma for w in ws], [w.W_k for w in ws], [w.W_v for w in ws])
+    fw = fill_weights(cfg.d, cfg.n_kv_heads, cfg.head_dim, cfg.rms_eps, cfg.torch_dtype, [w.W_map for w in ws],
+                      [w.b_map for w in ws], [w.gamma for w in ws], [w.W_k for w in ws], [w.W_v for w in ws])
     X = synth.hidden_states(cfg, 700, "prompt", device="cuda")
     outs = []
     for _ in range(2):
