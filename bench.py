@@ -97,11 +97,12 @@ def main():
 
     import linear_kv_cache_amd as rf
     import synth
-    from linear_kv_cache_amd.runner import Filler, GramState, alloc_cache, device_bytes
+    from linear_kv_cache_amd.runner import Filler, GramState, alloc_cache, device_bytes, pack_weights
 
     cfg = synth.CONFIGS[args.config]
-    if cfg.calib_rows == 0 or cfg.fill_tokens == 0:
-        raise SystemExit(f"{args.config} is a parity-test configuration, not a bench workload")
+    if cfg.calib_rows == 0 or cfg.fill_tokens == 0 or cfg.dtype != "bf16":
+        raise SystemExit(f"{args.config} is a parity-test configuration, not a bench workload "
+                         "(the bench times the bf16 fit-then-fill pipeline)")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
@@ -118,9 +119,11 @@ def main():
     b = torch.empty(L, d, dtype=torch.float32, device=dev)
     info = torch.empty(1, dtype=torch.int32, device=dev)
     cache = alloc_cache(L, cfg.n_kv_heads, cfg.head_dim, T, cfg.torch_dtype, dev)
+    # the K/V projections are model weights: packed once at load (rf_solve writes W_lp packed)
     fw = rf.FillWeights(d, cfg.n_kv_heads, cfg.head_dim, cfg.rms_eps, cfg.torch_dtype, [W_lp[i] for i in range(L)],
-                        [b[i] for i in range(L)], [g for (_, _, g) in kv], [k for (k, _, _) in kv],
-                        [v for (_, v, _) in kv])
+                        [b[i] for i in range(L)], [g for (_, _, g) in kv],
+                        [pack_weights(k, cfg.head_dim) for (k, _, _) in kv],
+                        [pack_weights(v, cfg.head_dim) for (_, v, _) in kv])
     filler = Filler(fw, cfg.rope_base, T, T, dev, ws_slots=8)   # 8 layers per fill launch (1 GiB of H)
     lam = cfg.lambdas[0]
     if args.copy_probe:

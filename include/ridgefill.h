@@ -196,8 +196,8 @@ rf_status rf_rope_table(double base, int32_t head_dim, int64_t n_pos, float* d_t
  *                                             layout of rf_pack_weights (rope_head_dim 0)
  *   b_map[l] : [d]                   fp32
  *   gamma[l] : [d]                   fp32
- *   W_k[l]   : [n_kv_heads*head_dim][d] dtype  head-major output rows
- *   W_v[l]   : [n_kv_heads*head_dim][d] dtype
+ *   W_k[l]   : [n_kv_heads*head_dim][d] dtype  head-major output rows; BF16 packed by
+ *   W_v[l]   : [n_kv_heads*head_dim][d] dtype  rf_pack_weights with rope_head_dim = head_dim
  * d_X : rows of the split-layer state for tokens t0..t1-1 (row i is token t0+i), [t1-t0][ldx]
  * k_cache[l], v_cache[l] : pools laid out per *cache (dtype must equal weights->dtype)
  * d_block_table : PAGED only, int32 [n_table_blocks]; entries outside [0, n_blocks) are
@@ -209,8 +209,10 @@ rf_status rf_rope_table(double base, int32_t head_dim, int64_t n_pos, float* d_t
  * ------------------------------------------------------------------------------------- */
 /* ---------------------------------------------------------------------------------------
  * Weight packing for the fill's matrix-core products (a layout change, no arithmetic).
- * The bf16 fill reads its map rows straight into the matrix-core operand registers, so they
- * are stored in fragment order.  Copies a row-major [rows][ld_src] bf16 matrix into d_dst
+ * The bf16 fill reads its weight rows (map, K and V projections) straight into the
+ * matrix-core operand registers, so they are stored in fragment order; grouping the K/V rows
+ * by rotate-half pairs puts both members of a RoPE pair (KV-Lingo page, section 2) in one
+ * thread.  Copies a row-major [rows][ld_src] bf16 matrix into d_dst
  * (rows * cols elements, no padding) as consecutive 256-row tiles; within a tile, element
  * (r, k) (r the row in the tile) moves to
  *     (k/64)*16384 + (r'/64)*4096 + ((k%64)/16)*1024 + ((r'%64)/32)*512

@@ -204,7 +204,8 @@ def rf_pack_weights(W, dst, rope_head_dim: int = 0, stream=None):
 class FillWeights:
     """Per-layer weights of the layers one rf_fill call fills (tensors on the device).
 
-    BF16 maps are in the packed layout (rf_pack_weights, or rf_solve's bf16 output)."""
+    BF16 weights are in the packed layout: maps as rf_pack_weights(rope_head_dim=0) or
+    rf_solve's bf16 output leave them, W_k and W_v as rf_pack_weights(rope_head_dim=head_dim)."""
 
     d: int
     n_kv_heads: int

@@ -9,7 +9,9 @@
 //          rotates K pairs (i, i + d_h/2) by their token's position (KV-Lingo page, sec. 3.1,
 //          pre-norm storing) and stores K and V rows into the layer's pools.
 // MFMA operands: A = weight rows (features), B = token rows, so each lane's accumulators
-// hold 4 consecutive features of one token and a head's RoPE pairs sit in the same lane.
+// hold 4 consecutive features of one token.  bf16 weights arrive packed in fragment order
+// (rf_pack_weights) and go straight to registers; K/V rows are packed in rotate-half pairs so
+// a head's RoPE partners sit in the same lane and register, one block apart.
 #include <math.h>
 
 #include "rf_internal.h"
@@ -78,9 +80,10 @@ __device__ inline void store4<float>(float* p, float a, float b, float c, float 
 // The bf16 instantiation runs the software-pipelined core; fp32 runs the plain tile loop.
 template <typename T> struct FillCore { using G = TileGemm<T, kFT, kTT, false, false>; };
 template <> struct FillCore<bf16_t> { using G = PipeGemm; };
-// The map's bf16 weights come pre-packed in fragment order and skip LDS.
+// bf16 weights come pre-packed in fragment order and skip LDS (K/V rows grouped by RoPE pairs).
 template <typename T> struct MapCore { using G = typename FillCore<T>::G; };
 template <> struct MapCore<bf16_t> { using G = PackedAGemm; };
+template <typename T> using KVCore = MapCore<T>;
 
 // Tile of this work-group: layer slot g, feature tile mt, token tile tt.  The grid is 1-D over
 // (layer, feature tile, token tile), renumbered so that each XCD works on a compact block of
@@ -200,11 +203,12 @@ __global__ __launch_bounds__(MapCore<T>::G::kThr) void k_fill_map(MapArgs a) {
 }
 
 template <typename T, int DH>
-__global__ __launch_bounds__(FillCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
-    using G = typename FillCore<T>::G;
-    static_assert(G::WTM % DH == 0, "a wave's feature extent must hold whole heads");
+__global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
+    using G = typename KVCore<T>::G;
+    static_assert(sizeof(T) == 2 || G::WTM % DH == 0, "fp32: a wave's feature extent must hold whole heads");
+    static_assert(sizeof(T) == 4 || G::SM == 2, "bf16: the two blocks of a wave hold the RoPE partners");
     constexpr int HALF = DH / 2;
-    constexpr int PAIR = HALF / 32;  // sub-tile distance between RoPE partners
+    constexpr int PAIR = HALF / 32;  // fp32: sub-tile distance between RoPE partners
     // staged tile, then 1/rms and the cache row offset of every token of the tile
     constexpr int kEpi = sizeof(T) == 2 ? kTT * kFT * 2 + kTT * 4 + kTT * 8 : 0;
     __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES > kEpi ? G::LDS_BYTES : kEpi];
@@ -267,61 +271,56 @@ __global__ __launch_bounds__(FillCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
             *(u32x2*)(lds + nl * (kFT * 2) + slot + (fl & 4) * 2) =
                 u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
         };
-        if (!is_k) {
+        // packed rows: block 0 of wave wm holds low dims of pairs 32 wm + (row % 32), block 1
+        // their partners (dims + HALF), in the same registers
+        const int wm = threadIdx.x >> 6;
+        const int qp0 = wm * 32 + 4 * ((threadIdx.x & 63) >> 5);
 #pragma unroll
-            for (int j = 0; j < G::SN; ++j) {
-                const int nl = G::col_of(j);
-                const float r = rinv[nl];
+        for (int j = 0; j < G::SN; ++j) {
+            const int nl = G::col_of(j);
+            const int64_t n = n0 + nl;
+            const float r = rinv[nl];
+            if (!is_k) {
 #pragma unroll
-                for (int i = 0; i < G::SM; ++i)
+                for (int q = 0; q < 4; ++q) {
+                    const int qp = qp0 + 8 * q;
+                    const int fl = (qp / HALF) * DH + qp % HALF;
+                    float lo[4], hi[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        float o[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) o[e] = gm.acc[i][j][4 * q + e] * r;
-                        stage(nl, G::row_of(i, 4 * q), o);
+                    for (int e = 0; e < 4; ++e) {
+                        lo[e] = gm.acc[0][j][4 * q + e] * r;
+                        hi[e] = gm.acc[1][j][4 * q + e] * r;
                     }
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < G::SN; ++j) {
-                const int nl = G::col_of(j);
-                const int64_t n = n0 + nl;
-                const float r = rinv[nl];
-                const float* cs_row = a.rope + (a.pos0 + a.t0 + (n < a.rows ? n : 0)) * (int64_t)DH;
-                // (cos, sin) of the dims held by the low-half sub-tiles; a high-half sub-tile
-                // i holds dims + HALF of sub-tile i - PAIR and rotates with the same angles
-                f32x4 c01[G::SM][4], c23[G::SM][4];
-#pragma unroll
-                for (int i = 0; i < G::SM; ++i) {
-                    if ((i * 32) % DH >= HALF) continue;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int dlo = (f0 + G::row_of(i, 4 * q)) % DH;
-                        c01[i][q] = *(const f32x4*)(cs_row + 2 * dlo);
-                        c23[i][q] = *(const f32x4*)(cs_row + 2 * dlo + 4);
-                    }
+                    stage(nl, fl, lo);
+                    stage(nl, fl + HALF, hi);
                 }
-                // keep the loads together ahead of their uses (one wait instead of one each)
+            } else {
+                const float* cs_row = a.rope + (a.pos0 + a.t0 + (n < a.rows ? n : 0)) * (int64_t)DH;
+                // (cos, sin) of the lane's 4 x 4 low dims, loaded together ahead of their uses
+                f32x4 c01[4], c23[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int dlo = (qp0 + 8 * q) % HALF;
+                    c01[q] = *(const f32x4*)(cs_row + 2 * dlo);
+                    c23[q] = *(const f32x4*)(cs_row + 2 * dlo + 4);
+                }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int i = 0; i < G::SM; ++i) {
-                    const bool low = (i * 32) % DH < HALF;
-                    const int il = low ? i : i - PAIR;            // sub-tile holding the angles
-                    const int ip = low ? i + PAIR : i - PAIR;     // RoPE partner sub-tile
+                for (int q = 0; q < 4; ++q) {
+                    const int qp = qp0 + 8 * q;
+                    const int fl = (qp / HALF) * DH + qp % HALF;
+                    const float cs[4] = {c01[q][0], c01[q][2], c23[q][0], c23[q][2]};
+                    const float sn[4] = {c01[q][1], c01[q][3], c23[q][1], c23[q][3]};
+                    float lo[4], hi[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float cs[4] = {c01[il][q][0], c01[il][q][2], c23[il][q][0], c23[il][q][2]};
-                        const float sn[4] = {c01[il][q][1], c01[il][q][3], c23[il][q][1], c23[il][q][3]};
-                        float o[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float x = gm.acc[i][j][4 * q + e] * r;
-                            const float y = gm.acc[ip][j][4 * q + e] * r;
-                            o[e] = low ? x * cs[e] - y * sn[e] : x * cs[e] + y * sn[e];
-                        }
-                        stage(nl, G::row_of(i, 4 * q), o);
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = gm.acc[0][j][4 * q + e] * r;
+                        const float y = gm.acc[1][j][4 * q + e] * r;
+                        lo[e] = x * cs[e] - y * sn[e];
+                        hi[e] = y * cs[e] + x * sn[e];
                     }
+                    stage(nl, fl, lo);
+                    stage(nl, fl + HALF, hi);
                 }
             }
         }
@@ -468,9 +467,9 @@ static rf_status launch_fill(const rf_fill_weights* w, int32_t n_layers, const v
         if (st != RF_OK) return st;
         const dim3 kv_grid((2 * ka.kvw / kFT) * tok_tiles * gsz);
         if (w->head_dim == 128)
-            hipLaunchKernelGGL((k_fill_kv<T, 128>), kv_grid, dim3(FillCore<T>::G::kThr), 0, stream, ka);
+            hipLaunchKernelGGL((k_fill_kv<T, 128>), kv_grid, dim3(KVCore<T>::G::kThr), 0, stream, ka);
         else
-            hipLaunchKernelGGL((k_fill_kv<T, 64>), kv_grid, dim3(FillCore<T>::G::kThr), 0, stream, ka);
+            hipLaunchKernelGGL((k_fill_kv<T, 64>), kv_grid, dim3(KVCore<T>::G::kThr), 0, stream, ka);
         st = check_launch("rf_fill: kv kernel");
         if (st != RF_OK) return st;
     }

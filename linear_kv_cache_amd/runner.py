@@ -111,10 +111,12 @@ def pack_weights(W: torch.Tensor, rope_head_dim: int = 0, stream=None) -> torch.
 
 def fill_weights(d: int, n_kv_heads: int, head_dim: int, rms_eps: float, dtype, W_map, b_map, gamma, W_k, W_v,
                  stream=None) -> FillWeights:
-    """FillWeights from row-major weights: bf16 maps are packed first (the fp32 path reads
-    them as they are)."""
+    """FillWeights from row-major weights: bf16 maps and projections are packed first (the
+    fp32 path reads them as they are)."""
     if dtype == torch.bfloat16:
         W_map = [pack_weights(W, 0, stream) for W in W_map]
+        W_k = [pack_weights(W, head_dim, stream) for W in W_k]
+        W_v = [pack_weights(W, head_dim, stream) for W in W_v]
     return FillWeights(d, n_kv_heads, head_dim, rms_eps, dtype, list(W_map), list(b_map), list(gamma), list(W_k),
                        list(W_v))
 
