@@ -84,6 +84,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16384)
     ap.add_argument("--cpu-fit-rows", type=int, default=8192)
+    ap.add_argument("--library-reference", action="store_true",
+                    help="also time the fill's two products per layer as plain torch.matmul (hipBLASLt) "
+                         "GEMMs on the same maps, projections and prompt states")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 1 GiB device-to-device copy before the steps, a known-size reference "
                          "for HBM byte counters")
@@ -218,6 +221,47 @@ def main():
                      "traffic": GRAM_TRAFFIC if args.config == "C2" else None,
                      "launch_ms": round(gram_launch_ms, 4), "flop_per_launch": gram_flop_per_launch},
     }
+    if args.library_reference:
+        # the same maps in plain layout: the solve's fp32 output rounded to bf16, as its packed
+        # bf16 output is; the same unpacked projections and prompt states
+        W32 = torch.empty(L, d, d, dtype=torch.float32, device=dev)
+        rf.rf_solve(state.desc, state.buf, lam, rf.RF_LAMBDA_ABSOLUTE, list(range(L)), W32, None, b, info,
+                    solve_ws, stream)
+        Wt = [W32[i].to(torch.bfloat16).t().contiguous() for i in range(L)]
+        del W32
+        Wkv = [torch.cat([k, v]).t().contiguous() for (k, v, _) in kv]
+        H = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+        KV = torch.empty(T, Wkv[0].shape[1], dtype=torch.bfloat16, device=dev)
+
+        def library_fill():
+            for i in range(L):
+                torch.matmul(Xp, Wt[i], out=H)
+                torch.matmul(H, Wkv[i], out=KV)
+
+        def timed(fn):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1)
+
+        library_fill()
+        torch.cuda.synchronize()
+        # alternate the two so both see the same clock and power state
+        lib_ms, fused_ms = [], []
+        for _ in range(args.steps):
+            fused_ms.append(timed(lambda: filler.fill(Xp, 0, T, 0, cache, stream)))
+            lib_ms.append(timed(library_fill))
+        ms, fms = statistics.median(lib_ms), statistics.median(fused_ms)
+        out["library_reference"] = {
+            "what": "torch.matmul (hipBLASLt) of the fill's map and K/V products per layer, no norm, RoPE or "
+                    "cache write, same data; alternated with the fused fill",
+            "ms_median": round(ms, 3), "tflops": round(fill_flop / (ms / 1e3) / 1e12, 1),
+            "frac_bf16_peak": round(fill_flop / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "fused_fill_ms_median": round(fms, 3),
+            "fused_fill_frac_bf16_peak": round(fill_flop / (fms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        del Wt, Wkv, H, KV
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on {args.cpu_tokens} tokens and {args.cpu_fit_rows} calibration rows")
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens, args.cpu_fit_rows)
