@@ -268,19 +268,45 @@ __global__ void k_centre_split(CrossArgs a) {
     }
 }
 
+// A double held by lane ``lane`` (a compile-time constant here) as a wave-uniform value.
+__device__ inline double readlane_f64(double x, int lane) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// sqrt(p) and 1/sqrt(p) from the hardware reciprocal square root refined by two Newton steps
+// (y <- y + y (1 - p y^2) / 2, each doubling the correct bits) and a final Newton step on the
+// square root itself (r <- r + (p - r^2) y / 2).  Non-positive p gives a non-finite pair.
+__device__ inline void sqrt_rsqrt(double p, double& r, double& ri) {
+    double y = __builtin_amdgcn_rsq(p);
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const double e = fma(-(p * y), y, 1.0);
+        y = fma(0.5 * y, e, y);
+    }
+    double s = p * y;
+    s = fma(0.5 * y, fma(-s, s, p), s);
+    r = s;
+    ri = y;
+}
+
 // Factor the diagonal block J (already updated by all earlier panels) in place into L_JJ and
 // write L_JJ^-1 into Dinv.  info receives the 1-based index of the first non-positive pivot
 // (unless an earlier block already reported one).
 // One wave, no barriers (a wave's LDS operations complete in order).  Lane i keeps row i of the
-// block in registers.  Right-looking elimination: at step j lane i writes its entry of column j
-// to LDS, reads the pivot back, scales, and writes L[i][j] into the transposed copy Lt[j][i];
-// the multipliers L[k][j] then reach every lane as broadcast reads of Lt[j] (all lanes one
-// address).  Entries above the diagonal are never read for the lower triangle and are written as
-// zeros.  L^-1 by right-looking substitution, lane c holding column c: once X[k][c] is final it
-// is stored, and row k of X updates the running sums of rows r > k with L[r][k] = Lt[k][r].
+// block in registers.  Right-looking elimination: at step j lane i scales its entry of column j
+// by the pivot's inverse square root and writes L[i][j] into the transposed copy Lt[j][i]; the
+// multipliers L[k][j] then reach every lane as broadcast reads of Lt[j] (all lanes one address).
+// The step's critical path stays in registers: the next column's entry is updated first with
+// L[j+1][j] read across lanes, and the next pivot is read from lane j+1 the same way, so its
+// square root overlaps the rest of step j's update.  Entries above the diagonal are never read
+// for the lower triangle and are written as zeros.  L^-1 by right-looking substitution, lane c
+// holding column c: once X[k][c] is final it is stored, and row k of X updates the running sums
+// of rows r > k with L[r][k] = Lt[k][r].
 __global__ __launch_bounds__(64) void k_chol_diag(double* C, int64_t d, int J, double* Dinv, int32_t* info) {
     __shared__ double piv[kNB];
-    __shared__ double col[2][kNB];
     __shared__ __attribute__((aligned(16))) double Lt[kNB][kNB + 2];
     const int i = threadIdx.x;
     const int64_t off = (int64_t)J * kNB;
@@ -290,26 +316,40 @@ __global__ __launch_bounds__(64) void k_chol_diag(double* C, int64_t d, int J, d
     const bool prior = *info != 0;
     int32_t fail = 0;
     double rinv = 0.0;   // lane i: 1 / L[i][i]
+    double r, ri;        // sqrt of the current pivot and its inverse (wave-uniform)
+    {
+        const double p = readlane_f64(a[0], 0);
+        if (!(p > 0.0)) fail = (int32_t)(off + 1);
+        sqrt_rsqrt(p, r, ri);
+    }
 #pragma unroll
     for (int j = 0; j < kNB; ++j) {
-        col[j & 1][i] = a[j];   // every lane writes (no divergent branch in the unrolled step)
-        const double p = col[j & 1][j];
-        if (!(p > 0.0) && fail == 0) fail = (int32_t)(off + j + 1);
-        const double r = sqrt(p);
-        const double ri = 1.0 / r;
-        if (i == j) rinv = ri;
         const double lij = i > j ? a[j] * ri : (i == j ? r : 0.0);
+        if (i == j) rinv = ri;
         Lt[j][i] = lij;
         a[j] = i >= j ? lij : a[j];
-        if ((j & 1) == 0 && j + 1 < kNB) a[j + 1] -= lij * Lt[j][j + 1];   // odd first row, alone
+        double rn = 0.0, rin = 0.0;
+        if (j + 1 < kNB) {
+            // next column first: L[j+1][j] from lane j+1, then the next pivot from lane j+1
+            a[j + 1] -= lij * readlane_f64(lij, j + 1);
+            const double pn = readlane_f64(a[j + 1], j + 1);
+            if (!(pn > 0.0) && fail == 0) fail = (int32_t)(off + j + 2);
+            sqrt_rsqrt(pn, rn, rin);
+        }
+        int k0 = j + 2;
+        if ((k0 & 1) && k0 < kNB) {
+            a[k0] -= lij * Lt[j][k0];
+            ++k0;
+        }
 #pragma unroll
-        for (int k = (j + 2) & ~1; k < kNB; k += 2) {
+        for (int k = k0; k < kNB; k += 2) {
             const f64x2 v = *(const f64x2*)(&Lt[j][k]);   // broadcast of L[k][j], L[k+1][j]
             a[k] -= lij * v[0];
             a[k + 1] -= lij * v[1];
-            if ((k & 15) == 14) __builtin_amdgcn_sched_barrier(0);   // at most 8 reads in flight
         }
-        __builtin_amdgcn_sched_barrier(0);   // keep each step's broadcasts within the step
+        r = rn;
+        ri = rin;
+        __builtin_amdgcn_sched_barrier(0);   // one step per scheduling region
     }
 #pragma unroll
     for (int k = 0; k < kNB; ++k) C[(off + i) * d + off + k] = k <= i ? a[k] : 0.0;
