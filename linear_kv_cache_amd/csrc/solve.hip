@@ -382,10 +382,12 @@ __global__ void k_diag_sqrt(const double* A, int64_t d, double* dg) {
     if (i < d) dg[i] = sqrt(fabs(A[i * d + i]));
 }
 
-// Equilibrated inverse, split: row j of Bq = [hi | lo | hi] of Ainv[j][i] dg[i] dg[j].
+// Equilibrated inverse, split: row j of Bq = [hi | lo | hi] of Ainv[j][i] dg[i] dg[j], stored in
+// the packed fragment order of the W product's weight operand (K = 3d columns).
 // One 64 x 64 tile of A^-1 per work-group.  Only the lower triangle of A^-1 (by 64-blocks) is
 // formed; a tile above the diagonal reads its mirror image (coalesced) and transposes it
-// through LDS.
+// through LDS.  Each thread then splits 8 consecutive columns of one row and stores them as
+// three 16-byte fragment chunks.
 __global__ __launch_bounds__(256) void k_split_inverse(const double* Ainv, const double* dg, int64_t d, bf16_t* Bq) {
     __shared__ double tile[64][65];
     const int64_t ib = blockIdx.x, jb = blockIdx.y;   // element (j, i): Bq row j, column i
@@ -393,15 +395,24 @@ __global__ __launch_bounds__(256) void k_split_inverse(const double* Ainv, const
     const int64_t r0 = (mirror ? ib : jb) * 64, c0 = (mirror ? jb : ib) * 64;
     for (int e = threadIdx.x; e < 64 * 64; e += 256) tile[e / 64][e % 64] = Ainv[(r0 + e / 64) * d + c0 + e % 64];
     __syncthreads();
-    for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-        const int jl = e / 64, il = e % 64;
-        const int64_t j = jb * 64 + jl, i = ib * 64 + il;
-        bf16_t hi, lo;
-        split_bf16((mirror ? tile[il][jl] : tile[jl][il]) * dg[i] * dg[j], hi, lo);
-        bf16_t* row = Bq + j * 3 * d;
-        row[i] = hi;
-        row[d + i] = lo;
-        row[2 * d + i] = hi;
+    const int64_t K = 3 * d;
+    for (int e = threadIdx.x; e < 64 * 8; e += 256) {
+        const int jl = e >> 3, i8 = (e & 7) * 8;
+        const int64_t j = jb * 64 + jl, i0 = ib * 64 + i8;
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int il = i8 + 2 * q;
+            bf16_t h0, l0, h1, l1;
+            split_bf16((mirror ? tile[il][jl] : tile[jl][il]) * dg[i0 + 2 * q] * dg[j], h0, l0);
+            split_bf16((mirror ? tile[il + 1][jl] : tile[jl][il + 1]) * dg[i0 + 2 * q + 1] * dg[j], h1, l1);
+            hi[q] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            lo[q] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
+        const u32x4 H{hi[0], hi[1], hi[2], hi[3]}, Lo{lo[0], lo[1], lo[2], lo[3]};
+        *(u32x4*)(Bq + packed_index(j, (int)i0, K)) = H;
+        *(u32x4*)(Bq + packed_index(j, (int)(d + i0), K)) = Lo;
+        *(u32x4*)(Bq + packed_index(j, (int)(2 * d + i0), K)) = H;
     }
 }
 
@@ -424,8 +435,8 @@ struct WArgs {
     float* bpart;      // [rows][tiles_j]
 };
 
-__global__ __launch_bounds__(kPipeThreads) void k_wgemm(WArgs a) {
-    using G = PipeGemm;
+__global__ __launch_bounds__(PackedAGemm::kThr) void k_wgemm(WArgs a) {
+    using G = PackedAGemm;   // Bq arrives packed (k_split_inverse)
     __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
     const int v = xcd_order((int)blockIdx.x, (int)gridDim.x);
     int jt, ct;
@@ -437,8 +448,9 @@ __global__ __launch_bounds__(kPipeThreads) void k_wgemm(WArgs a) {
 
     const double inv_n = 1.0 / (double)*a.np;
     const int lane = threadIdx.x & 63;
-    const int wm = (threadIdx.x >> 6) / G::WGN;   // wave row (two per tile)
-    float* red = (float*)lds;  // [2][256]; the main loop ended on a barrier
+    constexpr int kWaveRows = G::kThr / 64 / G::WGN;
+    const int wm = (threadIdx.x >> 6) / G::WGN;   // wave row
+    float* red = (float*)lds;  // [kWaveRows][256]; the main loop ended on a barrier
 #pragma unroll
     for (int jb = 0; jb < G::SN; ++jb) {
         const int cl = G::col_of(jb);
@@ -468,7 +480,12 @@ __global__ __launch_bounds__(kPipeThreads) void k_wgemm(WArgs a) {
     }
     __syncthreads();
     const int cl = threadIdx.x;
-    if (cl < 256) a.bpart[(c0 + cl) * a.tiles_j + jt] = red[cl] + red[256 + cl];
+    if (cl < 256) {
+        float ps = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaveRows; ++w) ps += red[w * 256 + cl];
+        a.bpart[(c0 + cl) * a.tiles_j + jt] = ps;
+    }
 }
 
 // b[c] = mu_y[c] - sum over tiles of the partial dots (fixed order, fp64).
@@ -657,7 +674,7 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, double lambda,
     wa.Aq = w.Aq; wa.Bq = w.Bq; wa.dg = w.dg; wa.sx = sx; wa.np = np; wa.d = d; wa.rows = rows;
     wa.tiles_j = (int)(d / 256); wa.tiles_c = (int)(rows / 256); wa.W = d_W; wa.Wlp = (bf16_t*)d_W_lp;
     wa.bpart = w.bpart;
-    hipLaunchKernelGGL(k_wgemm, dim3((unsigned)(wa.tiles_j * wa.tiles_c)), dim3(kPipeThreads), 0, s, wa);
+    hipLaunchKernelGGL(k_wgemm, dim3((unsigned)(wa.tiles_j * wa.tiles_c)), dim3(PackedAGemm::kThr), 0, s, wa);
     RF_TRY(check_launch("rf_solve: W product"));
     if (d_b) {
         hipLaunchKernelGGL(k_bias, dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0, s, w.bpart, wa.tiles_j, w.mu_y,
