@@ -361,8 +361,10 @@ struct PackedAGemm {
     };
 
     // Full K loop over ``nk`` k-steps (even).  A.ptr is the packed tile; A.ld and A.valid are
-    // unused (a packed tile always holds 256 rows).
-    __device__ inline void run(char* lds, const PipeOperand& A, const PipeOperand& B, int nk) {
+    // unused (a packed tile always holds 256 rows).  With FOLD, k-step kt of B is read from step
+    // kt < b_fold ? kt : kt - b_fold of its rows (B's first b_fold steps serve twice).
+    template <bool FOLD = false>
+    __device__ inline void run(char* lds, const PipeOperand& A, const PipeOperand& B, int nk, int b_fold = 0) {
         const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
 #pragma unroll
         for (int i = 0; i < SM; ++i)
@@ -399,7 +401,13 @@ struct PackedAGemm {
                 fa[p][kk][i] = __builtin_amdgcn_raw_buffer_load_b128(ra, av, kc * kStepBytes + (kk * 2 + i) * 1024, 0);
         };
         auto gload_b = [&](Regs& g, int kt, int j0, int j1) {
-            const int kc = kt < nk ? kt : nk - 1;
+            int kc = kt < nk ? kt : nk - 1;
+            if constexpr (FOLD) {
+                if (kc >= b_fold) kc -= b_fold;
+                // uniform by construction; said so, or the compiler wraps each load in a
+                // waterfall loop
+                kc = __builtin_amdgcn_readfirstlane(kc);
+            }
 #pragma unroll
             for (int j = j0; j < j1; ++j) g.b[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, gB + j * strideB, kc * ROWB, 0);
         };

@@ -228,44 +228,42 @@ struct CrossArgs {
     const double* sy;
     const double* sx;
     const int64_t* np;
-    const double* dg;
+    const double* rdg;     // 1 / sqrt(diag(C + lambda I))
     int64_t d;
     int64_t rows;          // n_sel * d
-    bf16_t* Aq;            // [rows][3d]: [hi | hi | lo] of the equilibrated centred cross moments
+    bf16_t* Aq;            // [rows][2d]: [hi | lo] of the equilibrated centred cross moments
     double* mu_y;          // [rows]
     int32_t tsel[kMaxSel];
 };
 
-// Centred cross moments B[c][i] = S_yx[c][i] - s_y[c] s_x[i] / n (fp64), scaled by 1/dg[i]
-// and split into bf16 parts; one thread per 8 consecutive i (16-byte stores).
-__global__ void k_centre_split(CrossArgs a) {
+// Centred cross moments B[c][i] = S_yx[c][i] - s_y[c] s_x[i] / n (fp64), scaled by rdg[i] = 1/dg[i]
+// and split into bf16 parts.  Block (c, y) covers row c, columns 2048 y .. 2048 y + 2047; one
+// thread per 8 consecutive i (16-byte stores).  The row's target and offset come from one
+// division per block.
+__global__ __launch_bounds__(256) void k_centre_split(CrossArgs a) {
+    const int64_t c = blockIdx.x;
+    const int64_t i0 = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 8;
+    if (i0 >= a.d) return;
     const double inv_n = 1.0 / (double)*a.np;
-    const int64_t per_row = a.d / 8;
-    const int64_t n = a.rows * per_row;
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t c = idx / per_row, i0 = (idx % per_row) * 8;
-        const int64_t s = c / a.d, o = c % a.d;
-        const int64_t srow = (int64_t)a.tsel[s] * a.d + o;
-        const double syv = a.sy[srow];
-        const f32x4 v0 = *(const f32x4*)(a.Syx + srow * a.d + i0);
-        const f32x4 v1 = *(const f32x4*)(a.Syx + srow * a.d + i0 + 4);
-        uint32_t hi[4], lo[4];
+    const int64_t s = c / a.d, o = c - s * a.d;
+    const int64_t srow = (int64_t)a.tsel[s] * a.d + o;
+    const double syv = a.sy[srow];
+    const f32x4 v0 = *(const f32x4*)(a.Syx + srow * a.d + i0);
+    const f32x4 v1 = *(const f32x4*)(a.Syx + srow * a.d + i0 + 4);
+    uint32_t hi[4], lo[4];
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-            bf16_t h0, l0, h1, l1;
-            const float x0 = e < 4 ? v0[e] : v1[e - 4], x1 = e < 4 ? v0[e + 1] : v1[e - 3];
-            split_bf16(((double)x0 - syv * a.sx[i0 + e] * inv_n) / a.dg[i0 + e], h0, l0);
-            split_bf16(((double)x1 - syv * a.sx[i0 + e + 1] * inv_n) / a.dg[i0 + e + 1], h1, l1);
-            hi[e / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            lo[e / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-        }
-        bf16_t* row = a.Aq + c * 3 * a.d;
-        const u32x4 H{hi[0], hi[1], hi[2], hi[3]}, Lo{lo[0], lo[1], lo[2], lo[3]};
-        *(u32x4*)(row + i0) = H;
-        *(u32x4*)(row + a.d + i0) = H;
-        *(u32x4*)(row + 2 * a.d + i0) = Lo;
-        if (i0 == 0) a.mu_y[c] = syv * inv_n;
+    for (int e = 0; e < 8; e += 2) {
+        bf16_t h0, l0, h1, l1;
+        const float x0 = e < 4 ? v0[e] : v1[e - 4], x1 = e < 4 ? v0[e + 1] : v1[e - 3];
+        split_bf16(((double)x0 - syv * a.sx[i0 + e] * inv_n) * a.rdg[i0 + e], h0, l0);
+        split_bf16(((double)x1 - syv * a.sx[i0 + e + 1] * inv_n) * a.rdg[i0 + e + 1], h1, l1);
+        hi[e / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lo[e / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
     }
+    bf16_t* row = a.Aq + c * 2 * a.d;
+    *(u32x4*)(row + i0) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    *(u32x4*)(row + a.d + i0) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    if (i0 == 0) a.mu_y[c] = syv * inv_n;
 }
 
 // A double held by lane ``lane`` (a compile-time constant here) as a wave-uniform value.
@@ -376,10 +374,14 @@ __global__ __launch_bounds__(64) void k_chol_diag(double* C, int64_t d, int J, d
     }
 }
 
-// dg[i] = sqrt(A[i][i]) before the factorisation overwrites the diagonal.
-__global__ void k_diag_sqrt(const double* A, int64_t d, double* dg) {
+// dg[i] = sqrt(A[i][i]) before the factorisation overwrites the diagonal, and rdg[i] = 1/dg[i]
+// (the unscaling steps multiply by it instead of dividing).
+__global__ void k_diag_sqrt(const double* A, int64_t d, double* dg, double* rdg) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < d) dg[i] = sqrt(fabs(A[i * d + i]));
+    if (i < d) {
+        dg[i] = sqrt(fabs(A[i * d + i]));
+        rdg[i] = 1.0 / dg[i];
+    }
 }
 
 // Equilibrated inverse, split: row j of Bq = [hi | lo | hi] of Ainv[j][i] dg[i] dg[j], stored in
@@ -417,13 +419,13 @@ __global__ __launch_bounds__(256) void k_split_inverse(const double* Ainv, const
 }
 
 // W = Aq Bq^T over K = 3d.  MFMA operand A = Bq rows (input feature j), B = Aq rows
-// (output c), so each lane holds 4 consecutive j of one c: W[c][j..j+3] = acc / dg[j] is one
+// (output c), so each lane holds 4 consecutive j of one c: W[c][j..j+3] = acc rdg[j] is one
 // 16-byte (fp32) and one 8-byte (bf16) store.  The epilogue also leaves, per (c, tile of 256
 // j), the partial dot  sum_j W[c][j] s_x[j] / n  for the bias.
 struct WArgs {
     const bf16_t* Aq;
     const bf16_t* Bq;
-    const double* dg;
+    const double* rdg;
     const double* sx;
     const int64_t* np;
     int64_t d;
@@ -444,7 +446,9 @@ __global__ __launch_bounds__(PackedAGemm::kThr) void k_wgemm(WArgs a) {
     const int64_t j0 = (int64_t)jt * 256, c0 = (int64_t)ct * 256;
     const int64_t K = 3 * a.d;
     G gm;
-    gm.run(lds, PipeOperand{a.Bq + j0 * K, K, 256}, PipeOperand{a.Aq + c0 * K, K, a.rows - c0}, (int)(K / G::BK));
+    // Aq rows are [hi | lo] (2d): the k-steps of the three K segments read hi, hi, lo
+    gm.run<true>(lds, PipeOperand{a.Bq + j0 * K, K, 256}, PipeOperand{a.Aq + c0 * 2 * a.d, 2 * a.d, a.rows - c0},
+                 (int)(K / G::BK), (int)(a.d / G::BK));
 
     const double inv_n = 1.0 / (double)*a.np;
     const int lane = threadIdx.x & 63;
@@ -465,7 +469,7 @@ __global__ __launch_bounds__(PackedAGemm::kThr) void k_wgemm(WArgs a) {
                 float w[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    w[e] = (float)((double)gm.acc[i][jb][4 * q + e] / a.dg[j + e]);
+                    w[e] = (float)((double)gm.acc[i][jb][4 * q + e] * a.rdg[j + e]);
                     part += w[e] * (float)(a.sx[j + e] * inv_n);
                 }
                 if (a.W) *(f32x4*)(a.W + c * a.d + j) = f32x4{w[0], w[1], w[2], w[3]};
@@ -499,7 +503,7 @@ __global__ void k_bias(const float* bpart, int tiles_j, const double* mu_y, int6
 
 // -------------------------------------------------------------------------------------------
 struct SolveWs {
-    double *C, *Cinv, *Dinv, *mu_y, *dg;
+    double *C, *Cinv, *Dinv, *mu_y, *dg, *rdg;
     bf16_t *Aq, *Bq;
     float* bpart;
     size_t total;
@@ -520,7 +524,8 @@ static SolveWs solve_ws(void* base, int64_t d, int64_t n_sel) {
     w.Dinv = (double*)take(d * kNB * 8);
     w.mu_y = (double*)take(rows * 8);
     w.dg = (double*)take(d * 8);
-    w.Aq = (bf16_t*)take(rows * 3 * d * 2);
+    w.rdg = (double*)take(d * 8);
+    w.Aq = (bf16_t*)take(rows * 2 * d * 2);
     w.Bq = (bf16_t*)take(d * 3 * d * 2);
     w.bpart = (float*)take(rows * (d / 256) * 4);
     w.total = off;
@@ -633,7 +638,7 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, double lambda,
     RF_TRY(check_launch("rf_solve: centre"));
     hipLaunchKernelGGL(k_add_lambda, dim3(1), dim3(256), 0, s, w.C, d, lambda, (int)(mode == RF_LAMBDA_REL_MEAN_DIAG));
     RF_TRY(check_launch("rf_solve: lambda"));
-    hipLaunchKernelGGL(k_diag_sqrt, dim3(grid_for(d)), dim3(256), 0, s, w.C, d, w.dg);
+    hipLaunchKernelGGL(k_diag_sqrt, dim3(grid_for(d)), dim3(256), 0, s, w.C, d, w.dg, w.rdg);
     RF_TRY(check_launch("rf_solve: diagonal"));
 
     // blocked Cholesky
@@ -665,13 +670,13 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, double lambda,
     RF_TRY(check_launch("rf_solve: split inverse"));
     const int64_t rows = (int64_t)n_sel * d;
     CrossArgs ca{};
-    ca.Syx = Syx; ca.sy = sy; ca.sx = sx; ca.np = np; ca.dg = w.dg; ca.d = d; ca.rows = rows; ca.Aq = w.Aq;
+    ca.Syx = Syx; ca.sy = sy; ca.sx = sx; ca.np = np; ca.rdg = w.rdg; ca.d = d; ca.rows = rows; ca.Aq = w.Aq;
     ca.mu_y = w.mu_y;
     for (int i = 0; i < n_sel; ++i) ca.tsel[i] = targets[i];
-    hipLaunchKernelGGL(k_centre_split, dim3(grid_for(rows * d / 8)), dim3(256), 0, s, ca);
+    hipLaunchKernelGGL(k_centre_split, dim3((unsigned)rows, (unsigned)ceil_div(d, 2048)), dim3(256), 0, s, ca);
     RF_TRY(check_launch("rf_solve: centre cross"));
     WArgs wa{};
-    wa.Aq = w.Aq; wa.Bq = w.Bq; wa.dg = w.dg; wa.sx = sx; wa.np = np; wa.d = d; wa.rows = rows;
+    wa.Aq = w.Aq; wa.Bq = w.Bq; wa.rdg = w.rdg; wa.sx = sx; wa.np = np; wa.d = d; wa.rows = rows;
     wa.tiles_j = (int)(d / 256); wa.tiles_c = (int)(rows / 256); wa.W = d_W; wa.Wlp = (bf16_t*)d_W_lp;
     wa.bpart = w.bpart;
     hipLaunchKernelGGL(k_wgemm, dim3((unsigned)(wa.tiles_j * wa.tiles_c)), dim3(PackedAGemm::kThr), 0, s, wa);
