@@ -44,16 +44,18 @@ typedef double f64x2 __attribute__((ext_vector_type(2)));
 enum { kFull = 0, kLowerOnly = 1, kUpperOperands = 2, kUpperA = 4, kUpperB = 8 };
 
 template <bool BT, int BM = 128>
-__global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, double alpha, const double* A,
+__global__ __launch_bounds__(256, 2) void k_dgemm(int64_t M, int64_t N, int64_t K, double alpha, const double* A,
                                                int64_t lda, const double* B, int64_t ldb, double beta, double* C,
                                                int64_t ldc, int structure, int64_t sA, int64_t sB, int64_t sC) {
     static_assert(BM == 64 || BM == 128, "64 x 64 or 128 x 128 tiles");
-    constexpr int BN = BM, BK = 32, PAD = 2;
+    constexpr int BN = BM, BK = 16, PAD = 2;
     constexpr int WT = BM / 2, WB = WT / 16;   // wave tile and its 16 x 16 blocks per side
     // Loads are 16-byte chunks, and each wave instruction covers whole operand rows (coalesced).
-    // K-contiguous operands (A, and B when BT) stay row-major in LDS, [m][BK + 2]: the 272-byte
+    // K-contiguous operands (A, and B when BT) stay row-major in LDS, [m][BK + 2]: the 144-byte
     // row stride is 16-byte aligned for the stores and puts the 16 rows a fragment read touches
     // (plus the next k's 16 lanes) on distinct banks.  An N-contiguous B stays [k][BN + 2].
+    // 16-wide k-steps keep a 128 x 128 tile's two LDS stages at 72 KiB and the registers under
+    // 256, so two work-groups share a CU and hide each other's load and LDS latency.
     constexpr int CPR_K = BK / 2, RPP_K = 256 / CPR_K, PK = BM / RPP_K;   // chunks/row, rows/pass, passes
     constexpr int CPR_N = BN / 2, RPP_N = 256 / CPR_N, PN = BK / RPP_N;
     constexpr int PB = BT ? PK : PN;
@@ -141,32 +143,35 @@ __global__ __launch_bounds__(256) void k_dgemm(int64_t M, int64_t N, int64_t K, 
             __syncthreads();
         }
     }
-    // all reads of C before any write: a store followed by a load the compiler cannot prove
-    // disjoint would otherwise cost a full memory round trip per element
-    double cv[WB][WB][4];
+    // all reads of C before any write (a store followed by a load the compiler cannot prove
+    // disjoint would otherwise cost a full memory round trip per element), half a tile at a time
 #pragma unroll
-    for (int i = 0; i < WB; ++i)
+    for (int ih = 0; ih < WB; ih += WB / 2) {
+        double cv[WB / 2][WB][4];
 #pragma unroll
-        for (int j = 0; j < WB; ++j) {
-            const int64_t n = n0 + wn * WT + j * 16 + (lane & 15);
+        for (int i = 0; i < WB / 2; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t m = m0 + wm * WT + i * 16 + 4 * r + (lane >> 4);
-                cv[i][j][r] = (beta != 0.0 && m < M && n < N) ? C[m * ldc + n] : 0.0;
+            for (int j = 0; j < WB; ++j) {
+                const int64_t n = n0 + wn * WT + j * 16 + (lane & 15);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t m = m0 + wm * WT + (ih + i) * 16 + 4 * r + (lane >> 4);
+                    cv[i][j][r] = (beta != 0.0 && m < M && n < N) ? C[m * ldc + n] : 0.0;
+                }
             }
-        }
 #pragma unroll
-    for (int i = 0; i < WB; ++i) {
+        for (int i = 0; i < WB / 2; ++i) {
 #pragma unroll
-        for (int j = 0; j < WB; ++j) {
-            const int64_t n = n0 + wn * WT + j * 16 + (lane & 15);
+            for (int j = 0; j < WB; ++j) {
+                const int64_t n = n0 + wn * WT + j * 16 + (lane & 15);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t m = m0 + wm * WT + i * 16 + 4 * r + (lane >> 4);
-                if (m < M && n < N) {
-                    double v = alpha * acc[i][j][r];
-                    if (beta != 0.0) v += beta * cv[i][j][r];
-                    C[m * ldc + n] = v;
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t m = m0 + wm * WT + (ih + i) * 16 + 4 * r + (lane >> 4);
+                    if (m < M && n < N) {
+                        double v = alpha * acc[ih + i][j][r];
+                        if (beta != 0.0) v += beta * cv[i][j][r];
+                        C[m * ldc + n] = v;
+                    }
                 }
             }
         }
