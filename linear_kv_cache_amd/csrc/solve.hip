@@ -242,13 +242,10 @@ struct CrossArgs {
 };
 
 // Centred cross moments B[c][i] = S_yx[c][i] - s_y[c] s_x[i] / n (fp64), scaled by rdg[i] = 1/dg[i]
-// and split into bf16 parts.  Block (c, y) covers row c, columns 2048 y .. 2048 y + 2047; one
-// thread per 8 consecutive i (16-byte stores).  The row's target and offset come from one
-// division per block.
-__global__ __launch_bounds__(256) void k_centre_split(CrossArgs a) {
-    const int64_t c = blockIdx.x;
-    const int64_t i0 = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 8;
-    if (i0 >= a.d) return;
+// and split into bf16 parts: the 8 consecutive columns i0 .. i0 + 7 of row c (16-byte stores).
+// Runs in the spare work-groups of the diagonal-block launches (below): it does not depend on
+// the factorisation, and those launches otherwise leave all but one CU idle.
+__device__ inline void centre_split_row(const CrossArgs& a, int64_t c, int64_t i0) {
     const double inv_n = 1.0 / (double)*a.np;
     const int64_t s = c / a.d, o = c - s * a.d;
     const int64_t srow = (int64_t)a.tsel[s] * a.d + o;
@@ -308,7 +305,18 @@ __device__ inline void sqrt_rsqrt(double p, double& r, double& ri) {
 // for the lower triangle and are written as zeros.  L^-1 by right-looking substitution, lane c
 // holding column c: once X[k][c] is final it is stored, and row k of X updates the running sums
 // of rows r > k with L[r][k] = Lt[k][r].
-__global__ __launch_bounds__(64) void k_chol_diag(double* C, int64_t d, int J, double* Dinv, int32_t* info) {
+// Work-group 0 factors the block with its first wave; work-groups 1.. centre and split rows
+// [c_begin, c_end) of the cross moments, ny work-groups of 2048 columns per row.
+__global__ __launch_bounds__(256) void k_chol_diag(double* C, int64_t d, int J, double* Dinv, int32_t* info,
+                                                   CrossArgs ca, int64_t c_begin, int64_t c_end, int ny) {
+    if (blockIdx.x > 0) {
+        const int64_t b = blockIdx.x - 1;
+        const int64_t c = c_begin + b / ny;
+        const int64_t i0 = ((b % ny) * 256 + threadIdx.x) * 8;
+        if (c < c_end && i0 < ca.d) centre_split_row(ca, c, i0);
+        return;
+    }
+    if (threadIdx.x >= 64) return;   // the factorisation is one wave's (no barriers below)
     __shared__ double piv[kNB];
     __shared__ __attribute__((aligned(16))) double Lt[kNB][kNB + 2];
     const int i = threadIdx.x;
@@ -646,11 +654,23 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, double lambda,
     hipLaunchKernelGGL(k_diag_sqrt, dim3(grid_for(d)), dim3(256), 0, s, w.C, d, w.dg, w.rdg);
     RF_TRY(check_launch("rf_solve: diagonal"));
 
+    // centred, equilibrated, split cross moments: computed in slices by the diagonal-block
+    // launches' spare work-groups
+    const int64_t rows = (int64_t)n_sel * d;
+    CrossArgs ca{};
+    ca.Syx = Syx; ca.sy = sy; ca.sx = sx; ca.np = np; ca.rdg = w.rdg; ca.d = d; ca.rows = rows; ca.Aq = w.Aq;
+    ca.mu_y = w.mu_y;
+    for (int i = 0; i < n_sel; ++i) ca.tsel[i] = targets[i];
+    const int ny = (int)ceil_div(d, 2048);
+
     // blocked Cholesky
     const int nblk = (int)(d / kNB);
+    const int64_t rows_per = ceil_div(rows, nblk);
     for (int J = 0; J < nblk; ++J) {
         const int64_t c0 = (int64_t)J * kNB;
-        hipLaunchKernelGGL(k_chol_diag, dim3(1), dim3(64), 0, s, w.C, d, J, w.Dinv, d_info);
+        const int64_t cb = std::min<int64_t>(rows, J * rows_per), ce = std::min<int64_t>(rows, cb + rows_per);
+        hipLaunchKernelGGL(k_chol_diag, dim3((unsigned)(1 + (ce - cb) * ny)), dim3(256), 0, s, w.C, d, J, w.Dinv,
+                           d_info, ca, cb, ce, ny);
         RF_TRY(check_launch("rf_solve: potrf"));
         const int64_t rem = d - c0 - kNB;
         if (rem <= 0) continue;
@@ -673,13 +693,6 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, double lambda,
     // equilibrated split operands, then W on the MFMA pipes
     hipLaunchKernelGGL(k_split_inverse, dim3((unsigned)(d / 64), (unsigned)(d / 64)), dim3(256), 0, s, w.C, w.dg, d, w.Bq);
     RF_TRY(check_launch("rf_solve: split inverse"));
-    const int64_t rows = (int64_t)n_sel * d;
-    CrossArgs ca{};
-    ca.Syx = Syx; ca.sy = sy; ca.sx = sx; ca.np = np; ca.rdg = w.rdg; ca.d = d; ca.rows = rows; ca.Aq = w.Aq;
-    ca.mu_y = w.mu_y;
-    for (int i = 0; i < n_sel; ++i) ca.tsel[i] = targets[i];
-    hipLaunchKernelGGL(k_centre_split, dim3((unsigned)rows, (unsigned)ceil_div(d, 2048)), dim3(256), 0, s, ca);
-    RF_TRY(check_launch("rf_solve: centre cross"));
     WArgs wa{};
     wa.Aq = w.Aq; wa.Bq = w.Bq; wa.rdg = w.rdg; wa.sx = sx; wa.np = np; wa.d = d; wa.rows = rows;
     wa.tiles_j = (int)(d / 256); wa.tiles_c = (int)(rows / 256); wa.W = d_W; wa.Wlp = (bf16_t*)d_W_lp;
