@@ -29,7 +29,7 @@ BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 # rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of this benchmark, each scaled by what the
 # counter reads for a 1 GiB device copy; profiles/pmc_traffic_llama8b-shaped_d4096_T16384.md has the
 # commands and the figures; set to None whenever k_gram_colsum or k_gram_pipe change.
-GRAM_TRAFFIC = (557369 + 4067395) * 2 * 1024 + (544 + 1168609) * 1024   # 10.67e9 B
+GRAM_TRAFFIC = (557359 + 4068380) * 2 * 1024 + (544 + 1166165) * 1024   # 10.67e9 B
 METRIC = "filled tokens/sec (all filled layers) + % bf16 MFMA peak; ridge-fit rows/sec"
 
 
