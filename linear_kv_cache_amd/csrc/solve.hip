@@ -549,14 +549,19 @@ static inline unsigned grid_for(int64_t n, int64_t per = 256) {
     return (unsigned)std::max<int64_t>(1, std::min<int64_t>(ceil_div(n, per), 1 << 16));
 }
 
+// 128 x 128 tiles only when they fill two rounds of the CUs at two work-groups each, else
+// 64 x 64 tiles: more work-groups in flight at half the operand reuse (measured on the d=4096
+// solve: 1024 tiles or more for 128 x 128 took 11.0 ms, 512 took 11.5 ms, and 128 x 128 tiles
+// throughout the inverse 12.1 ms; 2048 and 64 x 64 throughout matched 1024)
+constexpr int64_t kBigTiles = 1024;
+
 template <bool BT>
 static rf_status dgemm(hipStream_t s, int64_t M, int64_t N, int64_t K, double alpha, const double* A, int64_t lda,
                        const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int structure = kFull) {
     if (M <= 0 || N <= 0) return RF_OK;
-    // 128 x 128 tiles, unless they would not fill two rounds of the 256 CUs
     int64_t tiles = ceil_div(M, 128) * ceil_div(N, 128);
     if (structure & kLowerOnly) tiles = (tiles + ceil_div(M, 128)) / 2;
-    if (tiles >= 512)
+    if (tiles >= kBigTiles)
         hipLaunchKernelGGL((k_dgemm<BT, 128>), dim3((unsigned)ceil_div(M, 128), (unsigned)ceil_div(N, 128)), dim3(256), 0,
                            s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, structure, (int64_t)0, (int64_t)0, (int64_t)0);
     else
@@ -587,13 +592,24 @@ static rf_status inverse_factor(hipStream_t s, const SolveWs& w, int64_t d, doub
     double* T = (double*)w.Bq;
     auto join = [&](int64_t o, int64_t b, int64_t n2, unsigned batch, int64_t sp) -> rf_status {
         // units [o, o + b) and [o + b, o + b + n2), repeated ``batch`` times every sp elements
-        const dim3 g1((unsigned)ceil_div(b, 128), (unsigned)ceil_div(n2, 128), batch);
-        hipLaunchKernelGGL(k_dgemm<true>, g1, dim3(256), 0, s, b, n2, b, 1.0, (const double*)(Z + o * d + o), d,
-                           (const double*)(w.C + (o + b) * d + o), d, 0.0, T, n2, (int)kUpperA, sp, sp, b * n2);
+        const bool big = ceil_div(b, 128) * ceil_div(n2, 128) * (int64_t)batch >= kBigTiles;
+        const int64_t tb = big ? 128 : 64;
+        const dim3 g1((unsigned)ceil_div(b, tb), (unsigned)ceil_div(n2, tb), batch);
+        if (big)
+            hipLaunchKernelGGL((k_dgemm<true, 128>), g1, dim3(256), 0, s, b, n2, b, 1.0, (const double*)(Z + o * d + o),
+                               d, (const double*)(w.C + (o + b) * d + o), d, 0.0, T, n2, (int)kUpperA, sp, sp, b * n2);
+        else
+            hipLaunchKernelGGL((k_dgemm<true, 64>), g1, dim3(256), 0, s, b, n2, b, 1.0, (const double*)(Z + o * d + o),
+                               d, (const double*)(w.C + (o + b) * d + o), d, 0.0, T, n2, (int)kUpperA, sp, sp, b * n2);
         RF_TRY(check_launch("rf_solve: inverse T"));
-        hipLaunchKernelGGL(k_dgemm<false>, g1, dim3(256), 0, s, b, n2, n2, -1.0, (const double*)T, n2,
-                           (const double*)(Z + (o + b) * d + o + b), d, 0.0, Z + o * d + o + b, d, (int)kUpperB,
-                           b * n2, sp, sp);
+        if (big)
+            hipLaunchKernelGGL((k_dgemm<false, 128>), g1, dim3(256), 0, s, b, n2, n2, -1.0, (const double*)T, n2,
+                               (const double*)(Z + (o + b) * d + o + b), d, 0.0, Z + o * d + o + b, d, (int)kUpperB,
+                               b * n2, sp, sp);
+        else
+            hipLaunchKernelGGL((k_dgemm<false, 64>), g1, dim3(256), 0, s, b, n2, n2, -1.0, (const double*)T, n2,
+                               (const double*)(Z + (o + b) * d + o + b), d, 0.0, Z + o * d + o + b, d, (int)kUpperB,
+                               b * n2, sp, sp);
         return check_launch("rf_solve: inverse Z12");
     };
     for (int64_t b = kNB; b < d; b *= 2) {
