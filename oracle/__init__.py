@@ -7,7 +7,8 @@ it; the product path (``linear_kv_cache_amd``) never does, and the two share no 
 Everything is computed in float64 with NumPy/SciPy from the stored input values, upcast
 exactly.  Sources are the RidgeFill project page ("Method": steps 1-4 and Figure 2;
 "Abstract") and, for the pre-norm storing order and the relative ridge convention, the
-KV-Lingo page (sections 2 and 3.1, Appendix B.2 "Protocol").
+KV-Lingo page (sections 2 and 3.1, Appendix B.2 "Protocol").  ``translate`` follows the
+KV-Lingo page's token-wise linear cache translators (sections 3.1 and 3.2).
 
 Readings taken where the pages are silent (each one is listed in the design notes):
   * the map is W = (X~^T X~ + lambda I)^-1 X~^T Y~ on mean-centred rows with the intercept
@@ -23,7 +24,10 @@ forms, limits, brute force or an independent library route.
 from .ridge import (NotSPD, gram_sums, fit, fit_from_sums, ridge_objective,
                     solve_columns_from_data)
 from .fill import rope_inverse_frequencies, rope_rotate, rmsnorm, fill_layer, fill
+from .translate import (relative_depth_centre, relative_depth_sources, headwise_dense,
+                        translate_layer, translate, fit_translator)
 
 __all__ = ["NotSPD", "gram_sums", "fit", "fit_from_sums", "ridge_objective",
            "solve_columns_from_data", "rope_inverse_frequencies", "rope_rotate", "rmsnorm",
-           "fill_layer", "fill"]
+           "fill_layer", "fill", "relative_depth_centre", "relative_depth_sources",
+           "headwise_dense", "translate_layer", "translate", "fit_translator"]

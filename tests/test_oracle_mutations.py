@@ -64,3 +64,84 @@ def test_rope_pins_catch_mistakes():
 
     for bad in (wrong_sign, interleaved_pairs, wrong_frequency):
         assert not _hand_example(bad)
+
+
+def _translator_pins_hold(tl):
+    # identity map = rotation of the source (complex route); head-wise = head by head
+    rng = np.random.default_rng(8)
+    H, dh, n = 2, 8, 6
+    sk, sv = rng.standard_normal((n, H * dh)), rng.standard_normal((n, H * dh))
+    pos = 1.0 + np.arange(n) * 7
+    half = dh // 2
+    theta = np.array([1e4 ** (-(2.0 * i) / dh) for i in range(half)])
+    ok = True
+    K, V = tl(sk, sv, np.eye(H * dh), np.eye(H * dh), None, None, pos, H, dh, 1e4)
+    z = (sk.reshape(n, H, dh)[..., :half] + 1j * sk.reshape(n, H, dh)[..., half:]) * np.exp(
+        1j * pos[:, None, None] * theta)
+    ok &= np.allclose(K, np.concatenate([z.real, z.imag], -1), atol=1e-12)
+    ok &= np.allclose(V, sv.reshape(n, H, dh), atol=1e-12)
+    blocks = rng.standard_normal((H, dh, dh))
+    T = oracle.headwise_dense(blocks)
+    _, V2 = tl(sk, sv, T, T, None, None, np.zeros(n), H, dh, 1e4)
+    for g in range(H):
+        ok &= np.allclose(V2[:, g], sv[:, g * dh:(g + 1) * dh] @ blocks[g], atol=1e-12)
+    Tm = rng.standard_normal((H * dh, H * dh))
+    K3, _ = tl(sk, sv, Tm, Tm, None, None, pos, H, dh, 1e4)
+    ok &= np.allclose(K3, oracle.rope_rotate((sk @ Tm).reshape(n, H, dh), pos, 1e4), atol=1e-12)
+    return bool(ok)
+
+
+def test_translator_pins_catch_mistakes():
+    assert _translator_pins_hold(oracle.translate_layer)
+
+    def transposed_map(sk, sv, Tk, Tv, bk, bv, pos, H, dh, base):
+        return oracle.translate_layer(sk, sv, np.asarray(Tk).T, np.asarray(Tv).T, bk, bv, pos, H, dh, base)
+
+    def rotates_values_too(sk, sv, Tk, Tv, bk, bv, pos, H, dh, base):
+        K, V = oracle.translate_layer(sk, sv, Tk, Tv, bk, bv, pos, H, dh, base)
+        return K, oracle.rope_rotate(V, pos, base)
+
+    def rotates_before_the_map(sk, sv, Tk, Tv, bk, bv, pos, H, dh, base):
+        n = np.asarray(sk).shape[0]
+        rk = oracle.rope_rotate(np.asarray(sk, float).reshape(n, H, dh), pos, base).reshape(n, -1)
+        _, V = oracle.translate_layer(sk, sv, Tk, Tv, bk, bv, pos, H, dh, base)
+        return (rk @ np.asarray(Tk, float)).reshape(n, H, dh), V
+
+    for bad in (transposed_map, rotates_values_too, rotates_before_the_map):
+        assert not _translator_pins_hold(bad)
+
+
+def test_relative_depth_pins_catch_mistakes():
+    def holds(sel):
+        return (sel(28, 36, 3)[17] == [12, 13, 14] and sel(28, 36, 3)[35] == [25, 26, 27]
+                and sel(3, 5, 1)[1] == [1] and sel(7, 7, 1) == [[l] for l in range(7)])
+
+    assert holds(oracle.relative_depth_sources)
+
+    def ties_to_shallower(n_src, n_tgt, nu):
+        from fractions import Fraction
+        out = []
+        for l in range(1, n_tgt + 1):
+            c = oracle.relative_depth_centre(l, n_src, n_tgt)
+            s = min(range(1, n_src - nu + 2), key=lambda s: abs(s + Fraction(nu - 1, 2) - c))
+            out.append([s - 1 + j for j in range(nu)])
+        return out
+
+    def unshifted_at_ends(n_src, n_tgt, nu):
+        out = []
+        for l in range(1, n_tgt + 1):
+            c = oracle.relative_depth_centre(l, n_src, n_tgt)
+            s = int(np.floor(c - (nu - 1) / 2 + 0.5))
+            out.append([s - 1 + j for j in range(nu)])
+        return out
+
+    def truncates_centre(n_src, n_tgt, nu):
+        out = []
+        for l in range(1, n_tgt + 1):
+            c = 1 + (l - 1) * (n_src - 1) // max(1, n_tgt - 1)
+            s = min(max(1, c - (nu - 1) // 2), n_src - nu + 1)
+            out.append([s - 1 + j for j in range(nu)])
+        return out
+
+    for bad in (ties_to_shallower, unshifted_at_ends, truncates_centre):
+        assert not holds(bad)

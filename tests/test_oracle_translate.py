@@ -1,0 +1,185 @@
+"""Pins of the oracle's KV-cache translators (KV-Lingo page, sections 3.1-3.2) against closed
+forms, hand-worked cases and invariants (CPU only)."""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _rope_complex(k, positions, base):
+    # independent route: pair (i, i+h) as the complex number a + i c, times e^{i pos theta}
+    half = k.shape[-1] // 2
+    theta = np.array([base ** (-(2.0 * i) / k.shape[-1]) for i in range(half)])
+    z = (k[..., :half] + 1j * k[..., half:]) * np.exp(1j * positions[:, None, None] * theta)
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+# ---- relative-depth source selection ---------------------------------------------------------
+
+def test_relative_depth_hand_worked():
+    # N_src = 28, N_tgt = 36, nu = 3: c(l) = 1 + 27 (l - 1) / 35
+    #   l = 1  -> c = 1;        the centred band {0, 1, 2} (1-based) is shifted to {1, 2, 3}
+    #   l = 18 -> c = 494/35 = 14.11; band centred on 14: {13, 14, 15}
+    #   l = 36 -> c = 28;       band {27, 28, 29} shifted to {26, 27, 28}
+    E = oracle.relative_depth_sources(28, 36, 3)
+    assert oracle.relative_depth_centre(18, 28, 36) == Fraction(494, 35)
+    assert E[0] == [0, 1, 2]
+    assert E[17] == [12, 13, 14]
+    assert E[35] == [25, 26, 27]
+    # a tie: N_src = 3, N_tgt = 5 gives c(2) = 3/2, half-way between layers 1 and 2; nu = 1
+    # takes the deeper one; nu = 2 is centred exactly on it
+    assert oracle.relative_depth_centre(2, 3, 5) == Fraction(3, 2)
+    assert oracle.relative_depth_sources(3, 5, 1)[1] == [1]
+    assert oracle.relative_depth_sources(3, 5, 2)[1] == [0, 1]
+
+
+def test_relative_depth_shape_preserving_and_ends():
+    # the page: a shape-preserving pair reads its counterpart, E_l = {l}
+    for n in (1, 2, 7, 36):
+        assert oracle.relative_depth_sources(n, n, 1) == [[l] for l in range(n)]
+    for n_src, n_tgt in [(28, 36), (36, 28), (64, 32), (5, 17), (2, 2)]:
+        c_first = oracle.relative_depth_centre(1, n_src, n_tgt)
+        c_last = oracle.relative_depth_centre(n_tgt, n_src, n_tgt)
+        assert c_first == 1 and c_last == n_src
+        for nu in range(1, n_src + 1):
+            E = oracle.relative_depth_sources(n_src, n_tgt, nu)
+            assert len(E) == n_tgt
+            assert E[0] == list(range(nu))
+            assert E[-1] == list(range(n_src - nu, n_src))
+            starts = [e[0] for e in E]
+            assert starts == sorted(starts)                     # deeper targets read deeper
+            for e in E:
+                assert e == list(range(e[0], e[0] + nu)) and 0 <= e[0] and e[-1] < n_src
+
+
+def test_relative_depth_band_is_nearest_to_centre():
+    # brute force: no other band of nu layers inside the source has its middle closer to c
+    for n_src, n_tgt, nu in [(28, 36, 3), (36, 28, 4), (9, 9, 2), (12, 40, 5)]:
+        E = oracle.relative_depth_sources(n_src, n_tgt, nu)
+        for l, e in enumerate(E, start=1):
+            c = oracle.relative_depth_centre(l, n_src, n_tgt)
+            mid = e[0] + 1 + Fraction(nu - 1, 2)
+            for s in range(1, n_src - nu + 2):
+                assert abs(mid - c) <= abs(s + Fraction(nu - 1, 2) - c)
+
+
+def test_relative_depth_rejects_bad_sizes():
+    with pytest.raises(ValueError):
+        oracle.relative_depth_sources(4, 4, 5)
+    with pytest.raises(ValueError):
+        oracle.relative_depth_sources(4, 0, 1)
+
+
+# ---- translation --------------------------------------------------------------------------
+
+def test_identity_translator_is_rope_of_the_source():
+    # T = I, no intercept: the target keys are the source keys rotated, values unchanged;
+    # the rotation is checked by the complex-multiplication route
+    rng = np.random.default_rng(1)
+    H, dh, n = 3, 8, 11
+    sk = rng.standard_normal((n, H * dh))
+    sv = rng.standard_normal((n, H * dh))
+    pos = 5 + np.arange(n, dtype=float) * 1000
+    K, V = oracle.translate_layer(sk, sv, np.eye(H * dh), np.eye(H * dh), None, None, pos, H, dh, 1e4)
+    assert np.allclose(K, _rope_complex(sk.reshape(n, H, dh), pos, 1e4), rtol=0, atol=1e-12)
+    assert np.array_equal(V, sv.reshape(n, H, dh))
+
+
+def test_hand_worked_one_hot_translation():
+    # one head of d_h = 2, base 100 (theta_0 = 1): source key e_1 picks row 1 of T_k,
+    # [0.5, -2] + b [1, 1] = [1.5, -1]; at position 2 it turns by 2 rad
+    T = np.array([[9.0, 9.0], [0.5, -2.0]])
+    K, V = oracle.translate_layer([[0.0, 1.0]], [[0.0, 1.0]], T, T, [1.0, 1.0], [0.0, 0.0],
+                                  np.array([2.0]), 1, 2, 100.0)
+    a, c = 1.5, -1.0
+    assert np.allclose(K[0, 0], [a * math.cos(2) - c * math.sin(2), c * math.cos(2) + a * math.sin(2)],
+                       rtol=0, atol=1e-15)
+    assert np.allclose(V[0, 0], [0.5, -2.0], rtol=0, atol=1e-15)
+
+
+def test_headwise_translator_acts_head_by_head():
+    # block-diagonal map = each target head g computed from source head g alone
+    rng = np.random.default_rng(2)
+    H, dh, n = 4, 6, 9
+    blocks_k = rng.standard_normal((H, dh, dh))
+    blocks_v = rng.standard_normal((H, dh, dh))
+    sk = rng.standard_normal((n, H * dh))
+    sv = rng.standard_normal((n, H * dh))
+    pos = np.arange(n, dtype=float) + 17
+    K, V = oracle.translate_layer(sk, sv, oracle.headwise_dense(blocks_k), oracle.headwise_dense(blocks_v),
+                                  None, None, pos, H, dh, 5e5)
+    for g in range(H):
+        kg = sk[:, g * dh:(g + 1) * dh] @ blocks_k[g]
+        vg = sv[:, g * dh:(g + 1) * dh] @ blocks_v[g]
+        assert np.allclose(K[:, g], _rope_complex(kg[:, None, :], pos, 5e5)[:, 0], rtol=0, atol=1e-12)
+        assert np.allclose(V[:, g], vg, rtol=0, atol=1e-12)
+    # and the dense matrix has zeros off the diagonal blocks
+    T = oracle.headwise_dense(blocks_k)
+    assert np.count_nonzero(T) == H * dh * dh
+
+
+def test_multi_source_is_the_sum_of_single_sources():
+    # nu = 2: [k1 | k2] [T1; T2] + b = (k1 T1) + (k2 T2) + b, and RoPE is linear
+    rng = np.random.default_rng(3)
+    H, dh, n = 2, 8, 7
+    k1, k2, v1, v2 = (rng.standard_normal((n, H * dh)) for _ in range(4))
+    T1, T2, U1, U2 = (rng.standard_normal((H * dh, H * dh)) for _ in range(4))
+    b = rng.standard_normal(H * dh)
+    pos = np.arange(n, dtype=float) * 3
+    K, V = oracle.translate_layer(np.hstack([k1, k2]), np.hstack([v1, v2]), np.vstack([T1, T2]),
+                                  np.vstack([U1, U2]), b, b, pos, H, dh, 1e4)
+    Ka, Va = oracle.translate_layer(k1, v1, T1, U1, b, b, pos, H, dh, 1e4)
+    Kb, Vb = oracle.translate_layer(k2, v2, T2, U2, None, None, pos, H, dh, 1e4)
+    assert np.allclose(K, Ka + Kb, rtol=0, atol=1e-12)
+    assert np.allclose(V, Va + Vb, rtol=0, atol=1e-12)
+
+
+def test_positions_turn_keys_only():
+    rng = np.random.default_rng(4)
+    H, dh, n = 2, 8, 5
+    sk, sv = rng.standard_normal((n, H * dh)), rng.standard_normal((n, H * dh))
+    Tk, Tv = rng.standard_normal((H * dh, H * dh)), rng.standard_normal((H * dh, H * dh))
+    K0, V0 = oracle.translate_layer(sk, sv, Tk, Tv, None, None, np.zeros(n), H, dh, 1e4)
+    assert np.allclose(K0.reshape(n, -1), sk @ Tk, rtol=0, atol=1e-12)   # position 0: no turn
+    pos = np.array([1.0, 10, 100, 1000, 100000])
+    K1, V1 = oracle.translate_layer(sk, sv, Tk, Tv, None, None, pos, H, dh, 1e4)
+    assert np.array_equal(V0, V1)
+    assert np.allclose(K1, oracle.rope_rotate(K0, pos, 1e4), rtol=0, atol=1e-12)
+
+
+def test_translate_range_and_layers():
+    rng = np.random.default_rng(5)
+    H, dh = 2, 4
+    mk = lambda: (rng.standard_normal((6, H * dh)), rng.standard_normal((6, H * dh)),
+                  rng.standard_normal((H * dh, H * dh)), rng.standard_normal((H * dh, H * dh)), None, None)
+    layers = [mk(), mk()]
+    out = oracle.translate(10, 16, 3, layers, H, dh, 1e4)
+    pos = 3 + np.arange(10, 16, dtype=float)
+    for (K, V), lw in zip(out, layers):
+        K1, V1 = oracle.translate_layer(*lw, pos, H, dh, 1e4)
+        assert np.array_equal(K, K1) and np.array_equal(V, V1)
+    with pytest.raises(ValueError):
+        oracle.translate(10, 15, 0, layers, H, dh, 1e4)
+
+
+def test_fit_translator_recovers_a_planted_map():
+    # target rows exactly an affine map of the source rows: the closed-form first stage
+    # recovers it (lambda -> 0), and translating with it reproduces the target cache
+    rng = np.random.default_rng(6)
+    H, dh, n = 2, 8, 300
+    src = rng.standard_normal((n, H * dh)) * 2 + 0.3
+    T = rng.standard_normal((H * dh, H * dh)) / 4
+    c = rng.standard_normal(H * dh)
+    tgt = src @ T + c
+    Tf, bf = oracle.fit_translator(src, tgt, 1e-10)
+    assert np.allclose(Tf, T, rtol=0, atol=1e-8) and np.allclose(bf, c, rtol=0, atol=1e-8)
+    # head-wise planted map: the fit of each head's columns on its own source head recovers
+    # the blocks
+    blocks = rng.standard_normal((H, dh, dh))
+    tgt_h = src @ oracle.headwise_dense(blocks)
+    for g in range(H):
+        Tg, bg = oracle.fit_translator(src[:, g * dh:(g + 1) * dh], tgt_h[:, g * dh:(g + 1) * dh], 1e-10)
+        assert np.allclose(Tg, blocks[g], rtol=0, atol=1e-8) and np.allclose(bg, 0, atol=1e-8)
