@@ -10,7 +10,10 @@ Default workload: the Llama-8B-shaped configuration (d=4096, 32 layers split at 
 
 Prints one JSON line.  ``value`` is filled tokens per second of fill time; the fit's rows
 per second, per-phase times, the dominant kernel's roofline and the CPU oracle baseline ride
-along.  Progress goes to stderr.
+along.  After the timed steps, and outside them, the token-wise cache translators (KV-Lingo
+page, section 3.1) are timed on their own workload (28 -> 36 layers of 8 x 128 KV heads,
+two source layers per target layer, 16384 tokens) and reported under ``translate``.
+Progress goes to stderr.
 """
 from __future__ import annotations
 
@@ -25,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
 # HBM bytes of one rf_gram_accumulate call (8192 rows, d=4096, 16 targets), from two
 # rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of this benchmark, each scaled by what the
 # counter reads for a 1 GiB device copy; profiles/pmc_traffic_llama8b-shaped_d4096_T16384.md has the
@@ -75,6 +79,58 @@ def cpu_baseline(cfg, n_tokens: int, n_fit_rows: int):
     }
 
 
+def translate_leg(steps: int, stream, dev):
+    """Time rf_translate over every target layer of the translation workload, in one call."""
+    import torch
+
+    import linear_kv_cache_amd as rf
+    import synth
+    from linear_kv_cache_amd.runner import Translator, alloc_cache, translate_weights
+
+    tc = synth.TR_BENCH
+    T = tc.t1 - tc.t0
+    log(f"translate workload {tc.name}: {tc.n_src} -> {tc.n_tgt} layers, nu={tc.nu}, T={T}")
+    E = rf.rf_relative_depth_sources(tc.n_src, tc.n_tgt, tc.nu)
+    Ks, Vs = synth.source_cache(tc, T, device=dev)
+    maps = [synth.translator_maps(tc, l, device=dev) for l in range(tc.n_tgt)]
+    tw = translate_weights(tc.d_in, tc.n_kv_heads, tc.head_dim, tc.torch_dtype, [m[0] for m in maps],
+                           [m[1] for m in maps])
+    del maps
+    cache = alloc_cache(tc.n_tgt, tc.n_kv_heads, tc.head_dim, T, tc.torch_dtype, dev)
+    tr = Translator(tw, tc.rope_base, T, dev)
+    src_k = [Ks[0, e[0]] for e in E]
+    src_v = [Vs[0, e[0]] for e in E]
+    ld = tc.n_src * tc.d_src
+
+    def call():
+        tr.translate(src_k, src_v, ld, tc.t0, tc.t1, 0, cache, stream)
+
+    call()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    med = statistics.median(ms)
+    flop = T * tc.n_tgt * tc.flop_per_token_layer()
+    # algorithmic bytes: the nu source layers' K and V rows read, the target K and V rows written
+    nbytes = T * tc.n_tgt * (2 * tc.d_in + 2 * tc.kv_width) * 2
+    tflops = flop / (med / 1e3) / 1e12
+    gbps = nbytes / (med / 1e3) / 1e9
+    return {"workload": tc.name, "n_src": tc.n_src, "n_tgt": tc.n_tgt, "nu": tc.nu, "d_in": tc.d_in,
+            "kv_width": tc.kv_width, "tokens": T, "maps": tc.maps,
+            "ms": round(statistics.mean(ms), 3), "ms_median": round(med, 3),
+            "tokens_per_s": round(T / (med / 1e3), 1),
+            "flop_per_token_layer": tc.flop_per_token_layer(), "tflops": round(tflops, 1),
+            "frac_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+            "bytes_per_token_layer": (2 * tc.d_in + 2 * tc.kv_width) * 2, "GBps": round(gbps, 1),
+            "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -87,6 +143,7 @@ def main():
     ap.add_argument("--library-reference", action="store_true",
                     help="also time the fill's two products per layer as plain torch.matmul (hipBLASLt) "
                          "GEMMs on the same maps, projections and prompt states")
+    ap.add_argument("--no-translate", action="store_true", help="skip the cache-translator leg")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 1 GiB device-to-device copy before the steps, a known-size reference "
                          "for HBM byte counters")
@@ -262,6 +319,9 @@ def main():
             "fused_fill_ms_median": round(fms, 3),
             "fused_fill_frac_bf16_peak": round(fill_flop / (fms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
         del Wt, Wkv, H, KV
+    if not args.no_translate:
+        del Xc, Yc
+        out["translate"] = translate_leg(args.steps, stream, dev)
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on {args.cpu_tokens} tokens and {args.cpu_fit_rows} calibration rows")
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens, args.cpu_fit_rows)

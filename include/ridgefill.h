@@ -182,6 +182,29 @@ rf_status rf_rope_table(double base, int32_t head_dim, int64_t n_pos, float* d_t
                         void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Weight packing for the fill's matrix-core products (a layout change, no arithmetic).
+ * The bf16 fill reads its weight rows (map, K and V projections) straight into the
+ * matrix-core operand registers, so they are stored in fragment order; grouping the K/V rows
+ * by rotate-half pairs puts both members of a RoPE pair (KV-Lingo page, section 2) in one
+ * thread.  Copies a row-major [rows][ld_src] matrix of element type ``dtype`` (BF16 copied
+ * as is, F32 rounded to nearest even bf16) into the bf16 buffer d_dst
+ * (rows * cols elements, no padding) as consecutive 256-row tiles; within a tile, element
+ * (r, k) (r the row in the tile) moves to
+ *     (k/64)*16384 + (r'/64)*4096 + ((k%64)/16)*1024 + ((r'%64)/32)*512
+ *     + (((k%16)/8)*32 + r'%32)*8 + k%8
+ * where r' is the packed position of row r: r' = r when rope_head_dim is 0.  Otherwise the
+ * rows of each tile are grouped by rotate-half pairs: packed row r' = 64w + 32i + j
+ * (w, i, j in [0,4), [0,2), [0,32)) holds tile row (q / h) * hd + q % h + i * h with
+ * q = 32w + j, hd = rope_head_dim, h = hd / 2 (pair partners i = 0, 1 share w and j).
+ * Supported: BF16 or F32 sources, rows % 256 == 0, cols % 64 == 0, rows and cols <= 65536,
+ * rope_head_dim in {0, 64, 128}; ld_src >= cols and a multiple of 8; both buffers 16-B
+ * aligned and disjoint.
+ * Asynchronous on ``stream``; nothing is allocated.
+ * ------------------------------------------------------------------------------------- */
+rf_status rf_pack_weights(rf_dtype dtype, int64_t rows, int64_t cols, const void* d_src, int64_t ld_src,
+                          int32_t rope_head_dim, void* d_dst, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * The fill.  RidgeFill project page, "Method" steps 2-4 and Figure 2(b): for every token
  * t in [t0, t1) and every listed late layer l,
  *     h = x_t W_l^T + b_l                              (predicted layer input)
@@ -207,27 +230,6 @@ rf_status rf_rope_table(double base, int32_t head_dim, int64_t n_pos, float* d_t
  * Supported: d % 256 == 0, head_dim in {64, 128}, (n_kv_heads*head_dim) % 256 == 0,
  * dtype F32 or BF16 (all of X, maps, projections and pools share it).
  * ------------------------------------------------------------------------------------- */
-/* ---------------------------------------------------------------------------------------
- * Weight packing for the fill's matrix-core products (a layout change, no arithmetic).
- * The bf16 fill reads its weight rows (map, K and V projections) straight into the
- * matrix-core operand registers, so they are stored in fragment order; grouping the K/V rows
- * by rotate-half pairs puts both members of a RoPE pair (KV-Lingo page, section 2) in one
- * thread.  Copies a row-major [rows][ld_src] bf16 matrix into d_dst
- * (rows * cols elements, no padding) as consecutive 256-row tiles; within a tile, element
- * (r, k) (r the row in the tile) moves to
- *     (k/64)*16384 + (r'/64)*4096 + ((k%64)/16)*1024 + ((r'%64)/32)*512
- *     + (((k%16)/8)*32 + r'%32)*8 + k%8
- * where r' is the packed position of row r: r' = r when rope_head_dim is 0.  Otherwise the
- * rows of each tile are grouped by rotate-half pairs: packed row r' = 64w + 32i + j
- * (w, i, j in [0,4), [0,2), [0,32)) holds tile row (q / h) * hd + q % h + i * h with
- * q = 32w + j, hd = rope_head_dim, h = hd / 2 (pair partners i = 0, 1 share w and j).
- * Supported: BF16, rows % 256 == 0, cols % 64 == 0, rows and cols <= 65536, rope_head_dim in
- * {0, 64, 128}; ld_src >= cols and a multiple of 8; both buffers 16-B aligned and disjoint.
- * Asynchronous on ``stream``; nothing is allocated.
- * ------------------------------------------------------------------------------------- */
-rf_status rf_pack_weights(rf_dtype dtype, int64_t rows, int64_t cols, const void* d_src, int64_t ld_src,
-                          int32_t rope_head_dim, void* d_dst, void* stream);
-
 typedef struct {
     int32_t d;
     int32_t n_kv_heads;
@@ -249,6 +251,64 @@ rf_status rf_fill(const rf_fill_weights* weights, int32_t n_layers,
                   const int32_t* d_block_table, int64_t n_table_blocks,
                   const float* d_rope, int64_t rope_len,
                   void* d_ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Token-wise linear KV-cache translators.  KV-Lingo page, section 3.1 "Linear translator
+ * family": each target layer l has its own linear map for keys and its own for values, both
+ * reading the cache rows of a set of nu source layers; with pre-norm storing the maps act on
+ * the source keys before rotation, and the translated keys are rotated by their token's
+ * position before they are stored.  For every token t in [t0, t1) and listed target layer l,
+ *     k = s_k T_k,l^T + b_k,l,   v = s_v T_v,l^T + b_v,l
+ *     k <- RoPE(k, pos0 + t)                           (keys only)
+ * and k, v are stored in the layer's K and V pools at token t.  s_k (s_v) is the row of
+ * token t in d_src_k[l] (d_src_v[l]): the keys before rotation (the values) of the layer's
+ * nu source layers side by side, d_in = nu * d_src wide.  A source cache kept as
+ * [token][source layer][d_src] hands over a band of consecutive source layers (the bands of
+ * rf_relative_depth_sources) as one row segment, with ld_src = n_src_layers * d_src.
+ * Head-mixing maps are dense; a head-wise map (block-diagonal: target head g reads only
+ * source head g) is passed dense, zero blocks included, and computed as such.  The maps'
+ * closed-form first stage (KV-Lingo page, section 3.2) is a ridge fit of target rows on
+ * source rows: rf_gram_accumulate and rf_solve with X = source rows, one target of the
+ * same width; rf_pack_weights packs the solve's fp32 maps (rope_head_dim = head_dim).
+ * The per-head key normalisation of some models is not applied.
+ *
+ * Maps, per listed target layer (host arrays of n_layers device pointers):
+ *   T_k[l], T_v[l] : [n_kv_heads*head_dim][d_in] dtype, head-major output rows, out-feature
+ *                    major; BF16 packed by rf_pack_weights with rope_head_dim = head_dim
+ *   b_k, b_v       : both NULL (no intercept), or host arrays of n_layers fp32
+ *                    [n_kv_heads*head_dim] device vectors, 16-B aligned
+ * d_src_k[l], d_src_v[l] : [t1-t0][ld_src] source rows of tokens t0..t1-1 (row i is token
+ *                    t0+i), dtype of the maps, 16-B aligned, ld_src a 16-byte multiple
+ * cache, k_cache, v_cache, d_block_table, d_rope : as for rf_fill; rows outside [t0, t1)
+ *                    and layers not listed are never written
+ * No workspace.  Supported: d_in % 128 == 0 (BF16) or % 64 == 0 (F32), d_in <= 65536,
+ * ld_src <= 2^21, head_dim in {64, 128}, (n_kv_heads*head_dim) % 256 == 0.
+ * ------------------------------------------------------------------------------------- */
+typedef struct {
+    int32_t d_in;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    rf_dtype dtype;
+    const void* const* T_k;
+    const void* const* T_v;
+    const float* const* b_k;
+    const float* const* b_v;
+} rf_translate_weights;
+
+rf_status rf_translate(const rf_translate_weights* weights, int32_t n_layers,
+                       const void* const* d_src_k, const void* const* d_src_v, int64_t ld_src,
+                       int64_t t0, int64_t t1, int64_t pos0,
+                       const rf_cache_desc* cache, void* const* k_cache, void* const* v_cache,
+                       const int32_t* d_block_table, int64_t n_table_blocks,
+                       const float* d_rope, int64_t rope_len, void* stream);
+
+/* Host only.  Relative-depth match, KV-Lingo page, section 3.1 "Source-layer selection":
+ * target layer l (1-based) reads the band of nu consecutive source layers centred on
+ * c(l) = 1 + (l - 1)(n_src - 1)/(n_tgt - 1), shifted at the ends so every band holds nu
+ * layers.  The band taken is the one whose middle is nearest c(l); an exact tie goes to the
+ * deeper band; n_tgt = 1 reads c = 1.  Writes out[l * nu + j] (host int32 [n_tgt][nu]) = the
+ * 0-based source layer j of 0-based target layer l.  Needs n_tgt >= 1, 1 <= nu <= n_src. */
+rf_status rf_relative_depth_sources(int32_t n_src, int32_t n_tgt, int32_t nu, int32_t* out);
 
 #ifdef __cplusplus
 }

@@ -63,6 +63,12 @@ class rf_fill_weights(C.Structure):
                 ("gamma", C.POINTER(C.c_void_p)), ("W_k", C.POINTER(C.c_void_p)), ("W_v", C.POINTER(C.c_void_p))]
 
 
+class rf_translate_weights(C.Structure):
+    _fields_ = [("d_in", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("dtype", C.c_int),
+                ("T_k", C.POINTER(C.c_void_p)), ("T_v", C.POINTER(C.c_void_p)), ("b_k", C.POINTER(C.c_void_p)),
+                ("b_v", C.POINTER(C.c_void_p))]
+
+
 _P = C.c_void_p
 _sig = {
     "rf_version": (C.c_char_p, []),
@@ -82,6 +88,10 @@ _sig = {
     "rf_fill": (C.c_int, [C.POINTER(rf_fill_weights), C.c_int32, _P, C.c_int64, C.c_int64, C.c_int64, C.c_int64,
                           C.POINTER(rf_cache_desc), C.POINTER(_P), C.POINTER(_P), _P, C.c_int64, _P, C.c_int64,
                           _P, C.c_size_t, _P]),
+    "rf_translate": (C.c_int, [C.POINTER(rf_translate_weights), C.c_int32, C.POINTER(_P), C.POINTER(_P), C.c_int64,
+                               C.c_int64, C.c_int64, C.c_int64, C.POINTER(rf_cache_desc), C.POINTER(_P),
+                               C.POINTER(_P), _P, C.c_int64, _P, C.c_int64, _P]),
+    "rf_relative_depth_sources": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int32)]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -194,7 +204,7 @@ def rf_rope_table(base: float, head_dim: int, n_pos: int, table, stream=None):
 
 
 def rf_pack_weights(W, dst, rope_head_dim: int = 0, stream=None):
-    """W: [rows, >=cols] bf16 tensor (row stride = ld_src); dst: rows*cols bf16 elements."""
+    """W: [rows, >=cols] bf16 or fp32 tensor (row stride = ld_src); dst: rows*cols bf16 elements."""
     rows, cols = W.shape
     _check(_lib.rf_pack_weights(_dtype_code(W.dtype), rows, cols, _ptr(W), W.stride(0), int(rope_head_dim), _ptr(dst),
                                 _stream(stream)))
@@ -242,5 +252,49 @@ def rf_fill(weights: FillWeights, X, t0: int, t1: int, pos0: int, cache: rf_cach
                         _ptr(block_table), n_tab, _ptr(rope), rope_len, _ptr(ws), ws_bytes, _stream(stream)))
 
 
+@dataclass
+class TranslateWeights:
+    """Per-target-layer translator maps of one rf_translate call (tensors on the device).
+
+    T_k, T_v: [n_kv_heads*head_dim, d_in] out-feature major; BF16 maps packed by
+    rf_pack_weights(rope_head_dim=head_dim).  b_k, b_v: lists of fp32 intercepts, or None."""
+
+    d_in: int
+    n_kv_heads: int
+    head_dim: int
+    dtype: object
+    T_k: list
+    T_v: list
+    b_k: Optional[list] = None
+    b_v: Optional[list] = None
+
+    def _c(self):
+        arrs = [_ptr_array(x) for x in (self.T_k, self.T_v)]
+        barrs = [None if x is None else _ptr_array(x) for x in (self.b_k, self.b_v)]
+        cast = lambda a: C.cast(a, C.POINTER(_P)) if a is not None else C.POINTER(_P)()
+        w = rf_translate_weights(self.d_in, self.n_kv_heads, self.head_dim, _dtype_code(self.dtype),
+                                 cast(arrs[0]), cast(arrs[1]), cast(barrs[0]), cast(barrs[1]))
+        return w, (arrs, barrs)
+
+
+def rf_translate(weights: TranslateWeights, src_k: Sequence, src_v: Sequence, ld_src: int, t0: int, t1: int,
+                 pos0: int, cache: rf_cache_desc, k_cache: Sequence, v_cache: Sequence, block_table, rope,
+                 rope_len: int, stream=None, n_layers: Optional[int] = None):
+    """src_k, src_v: per target layer, device pointers (or tensors) to the source rows of token t0."""
+    w, _keep = weights._c()
+    n_layers = len(weights.T_k) if n_layers is None else n_layers
+    n_tab = 0 if block_table is None else block_table.numel()
+    _check(_lib.rf_translate(C.byref(w), n_layers, _ptr_array(src_k), _ptr_array(src_v), ld_src, t0, t1, pos0,
+                             C.byref(cache), _ptr_array(k_cache), _ptr_array(v_cache), _ptr(block_table), n_tab,
+                             _ptr(rope), rope_len, _stream(stream)))
+
+
+def rf_relative_depth_sources(n_src: int, n_tgt: int, nu: int) -> list:
+    """0-based source layers of each 0-based target layer (host only)."""
+    out = (C.c_int32 * max(1, n_tgt * nu))()
+    _check(_lib.rf_relative_depth_sources(n_src, n_tgt, nu, out))
+    return [[out[l * nu + j] for j in range(nu)] for l in range(n_tgt)]
+
+
 __all__ = [n for n in dir() if n.startswith("rf_") or n.startswith("RF_")] + [
-    "RidgeFillError", "FillWeights", "gram_desc", "cache_desc", "EXPORTED", "LIB_PATH"]
+    "RidgeFillError", "FillWeights", "TranslateWeights", "gram_desc", "cache_desc", "EXPORTED", "LIB_PATH"]

@@ -1,6 +1,7 @@
 // Host-only parts of the C ABI: error reporting, version, KV-cache layout arithmetic.
 #include <stdio.h>
 
+#include <algorithm>
 #include <string>
 
 #include "rf_internal.h"
@@ -57,6 +58,25 @@ rf_status rf_cache_layout(const rf_cache_desc* desc, rf_cache_layout_t* out) {
         return rf::fail(RF_ERR_INVALID_ARG, "rf_cache_layout: bad layout");
     }
     *out = L;
+    return RF_OK;
+}
+
+rf_status rf_relative_depth_sources(int32_t n_src, int32_t n_tgt, int32_t nu, int32_t* out) {
+    rf::clear_error();
+    RF_REQUIRE(out, RF_ERR_INVALID_ARG, "rf_relative_depth_sources: null output");
+    RF_REQUIRE(n_tgt >= 1 && nu >= 1 && nu <= n_src, RF_ERR_INVALID_ARG,
+               "rf_relative_depth_sources: need n_tgt >= 1 and 1 <= nu <= n_src");
+    // c(l) - 1 = a / q with a = (l - 1)(n_src - 1), q = n_tgt - 1 (c = 1 when n_tgt = 1).  The
+    // band start s = round-half-up(c - (nu - 1)/2) = floor((2a + q(4 - nu)) / (2q)), clamped to
+    // [1, n_src - nu + 1] (1-based).
+    const int64_t q = n_tgt > 1 ? n_tgt - 1 : 1;
+    for (int64_t l = 0; l < n_tgt; ++l) {
+        const int64_t a = n_tgt > 1 ? l * (int64_t)(n_src - 1) : 0;
+        const int64_t num = 2 * a + q * (4 - (int64_t)nu), den = 2 * q;
+        int64_t s = num >= 0 ? num / den : -((-num + den - 1) / den);
+        s = std::min<int64_t>(std::max<int64_t>(s, 1), (int64_t)n_src - nu + 1);
+        for (int32_t j = 0; j < nu; ++j) out[l * nu + j] = (int32_t)(s - 1 + j);
+    }
     return RF_OK;
 }
 

@@ -41,8 +41,6 @@ struct MapArgs {
 };
 
 struct KVArgs {
-    const void* H;
-    int64_t h_slot;
     const float* psum;
     int64_t ps_slot;
     int32_t n_ps;
@@ -60,6 +58,11 @@ struct KVArgs {
     int64_t n_blocks;
     const int32_t* block_table;
     int64_t n_table_blocks;
+    int64_t ld_in;           // row stride of the product's token operand
+    const void* in_k[kMaxGroup];  // token rows feeding the K (in_k) and V (in_v) feature tiles
+    const void* in_v[kMaxGroup];
+    const float* bk[kMaxGroup];   // per-feature intercepts (translators only)
+    const float* bv[kMaxGroup];
     const void* Wk[kMaxGroup];
     const void* Wv[kMaxGroup];
     void* kc[kMaxGroup];
@@ -202,7 +205,9 @@ __global__ __launch_bounds__(MapCore<T>::G::kThr) void k_fill_map(MapArgs a) {
     }
 }
 
-template <typename T, int DH>
+// NORM: the fill (rows scaled by 1/rms from the map's partial sums).  Otherwise the product
+// of a translator (KV-Lingo page, section 3.1): no row scale, an intercept when BIAS.
+template <typename T, int DH, bool NORM, bool BIAS>
 __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
     using G = typename KVCore<T>::G;
     static_assert(sizeof(T) == 2 || G::WTM % DH == 0, "fp32: a wave's feature extent must hold whole heads");
@@ -219,13 +224,16 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
     const int f0 = is_k ? mt * kFT : mt * kFT - a.kvw;
     const T* Wsel = (const T*)(is_k ? a.Wk[g] : a.Wv[g]) + (int64_t)f0 * a.d;
     G gm;
-    fill_gemm(gm, lds, Wsel, a.d, kFT, (const T*)a.H + g * a.h_slot + n0 * a.d, a.d, a.rows - n0, a.d / G::BK);
+    fill_gemm(gm, lds, Wsel, a.d, kFT, (const T*)(is_k ? a.in_k[g] : a.in_v[g]) + n0 * a.ld_in, a.ld_in, a.rows - n0,
+              a.d / G::BK);
 
     T* pool = (T*)(is_k ? a.kc[g] : a.vc[g]);
-    const float* ps = a.psum + g * a.ps_slot;
+    const float* ps = NORM ? a.psum + g * a.ps_slot : nullptr;
+    const float* bsel = BIAS ? (is_k ? a.bk[g] : a.bv[g]) + f0 : nullptr;
     const float inv_d = 1.0f / (float)a.d;
     // 1 / rms of token n from its per-feature-tile partial sums (fixed order)
     auto rms_inv = [&](int64_t n) {
+        if constexpr (!NORM) return 1.0f;
         float s = 0.f;
         if (a.n_ps % 4 == 0) {
             // four independent loads per pass, added in index order
@@ -260,7 +268,7 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
         int64_t* rbase = (int64_t*)(lds + kTT * kFT * 2 + kTT * 4);
         for (int nl = threadIdx.x; nl < kTT; nl += G::kThr) {
             const bool ok = n0 + nl < a.rows;
-            rinv[nl] = ok ? rms_inv(n0 + nl) : 0.f;
+            if constexpr (NORM) rinv[nl] = ok ? rms_inv(n0 + nl) : 0.f;
             rbase[nl] = ok ? row_base(a.t0 + n0 + nl) : -1;
         }
         __syncthreads();
@@ -275,21 +283,27 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
         // their partners (dims + HALF), in the same registers
         const int wm = threadIdx.x >> 6;
         const int qp0 = wm * 32 + 4 * ((threadIdx.x & 63) >> 5);
+        // intercepts of 4 features from fl (read where used: cache hits, no registers held)
+        auto bias4 = [&](int fl) {
+            if constexpr (BIAS) return *(const f32x4*)(bsel + fl);
+            return f32x4{0.f, 0.f, 0.f, 0.f};
+        };
 #pragma unroll
         for (int j = 0; j < G::SN; ++j) {
             const int nl = G::col_of(j);
             const int64_t n = n0 + nl;
-            const float r = rinv[nl];
+            const float r = NORM ? rinv[nl] : 1.f;
             if (!is_k) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int qp = qp0 + 8 * q;
                     const int fl = (qp / HALF) * DH + qp % HALF;
+                    const f32x4 blo = bias4(fl), bhi = bias4(fl + HALF);
                     float lo[4], hi[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        lo[e] = gm.acc[0][j][4 * q + e] * r;
-                        hi[e] = gm.acc[1][j][4 * q + e] * r;
+                        lo[e] = gm.acc[0][j][4 * q + e] * r + blo[e];
+                        hi[e] = gm.acc[1][j][4 * q + e] * r + bhi[e];
                     }
                     stage(nl, fl, lo);
                     stage(nl, fl + HALF, hi);
@@ -311,11 +325,12 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
                     const int fl = (qp / HALF) * DH + qp % HALF;
                     const float cs[4] = {c01[q][0], c01[q][2], c23[q][0], c23[q][2]};
                     const float sn[4] = {c01[q][1], c01[q][3], c23[q][1], c23[q][3]};
+                    const f32x4 blo = bias4(fl), bhi = bias4(fl + HALF);
                     float lo[4], hi[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float x = gm.acc[0][j][4 * q + e] * r;
-                        const float y = gm.acc[1][j][4 * q + e] * r;
+                        const float x = gm.acc[0][j][4 * q + e] * r + blo[e];
+                        const float y = gm.acc[1][j][4 * q + e] * r + bhi[e];
                         lo[e] = x * cs[e] - y * sn[e];
                         hi[e] = y * cs[e] + x * sn[e];
                     }
@@ -355,9 +370,14 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
                     const int head = f / DH;
                     const int dim = f % DH;
                     T* dst = pool + base + head * a.stride_head + dim;
+                    const int fb = f - f0;  // intercept index of this lane's first feature
+                    auto add_b = [&](float v, int idx) {
+                        if constexpr (BIAS) return v + bsel[idx];
+                        return v;
+                    };
                     if (!is_k) {
-                        store4<T>(dst, gm.acc[i][j][4 * q] * r, gm.acc[i][j][4 * q + 1] * r,
-                                  gm.acc[i][j][4 * q + 2] * r, gm.acc[i][j][4 * q + 3] * r);
+                        store4<T>(dst, add_b(gm.acc[i][j][4 * q] * r, fb), add_b(gm.acc[i][j][4 * q + 1] * r, fb + 1),
+                                  add_b(gm.acc[i][j][4 * q + 2] * r, fb + 2), add_b(gm.acc[i][j][4 * q + 3] * r, fb + 3));
                     } else if ((i * 32) % DH < HALF) {
                         // this sub-tile holds dims [dim, dim+4) < HALF; partner sub-tile i+PAIR
                         // holds dims + HALF of the same head in the same registers
@@ -368,8 +388,8 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
                         float lo[4], hi[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            const float x0 = gm.acc[i][j][4 * q + e] * r;
-                            const float x1 = gm.acc[(i + PAIR) % G::SM][j][4 * q + e] * r;
+                            const float x0 = add_b(gm.acc[i][j][4 * q + e] * r, fb + e);
+                            const float x1 = add_b(gm.acc[(i + PAIR) % G::SM][j][4 * q + e] * r, fb + HALF + e);
                             lo[e] = x0 * cs[e] - x1 * sn[e];
                             hi[e] = x1 * cs[e] + x0 * sn[e];
                         }
@@ -404,9 +424,17 @@ __device__ inline int packed_source_row(int p, int hd) {
     return (q / half) * hd + q % half + ((p >> 5) & 1) * half;
 }
 
+// 8 consecutive k of one source row as 8 bf16 (fp32 sources rounded to nearest even).
+__device__ inline u32x4 load8_bf16(const bf16_t* p) { return *(const u32x4*)p; }
+__device__ inline u32x4 load8_bf16(const float* p) {
+    const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+    return u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
+}
+
 // One 16-byte chunk (8 consecutive k of one row) per thread, in packed order: writes are
-// contiguous, reads are 16-byte pieces of source rows.
-__global__ void k_pack_weights(const bf16_t* __restrict__ src, int64_t ld, int64_t cols, int32_t hd,
+// contiguous, reads are pieces of source rows.
+template <typename S>
+__global__ void k_pack_weights(const S* __restrict__ src, int64_t ld, int64_t cols, int32_t hd,
                                int64_t n_chunks, bf16_t* __restrict__ dst) {
     const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (c >= n_chunks) return;
@@ -420,7 +448,7 @@ __global__ void k_pack_weights(const bf16_t* __restrict__ src, int64_t ld, int64
     const int p = (w << 6) + (i << 5) + (lane & 31);
     const int64_t row = tile * 256 + packed_source_row(p, hd);
     const int64_t k = kt * 64 + kk * 16 + (lane >> 5) * 8;
-    *(u32x4*)(dst + e) = *(const u32x4*)(src + row * ld + k);
+    *(u32x4*)(dst + e) = load8_bf16(src + row * ld + k);
 }
 
 static size_t slot_bytes(const rf_fill_weights* w, int64_t rows) {
@@ -449,7 +477,7 @@ static rf_status launch_fill(const rf_fill_weights* w, int32_t n_layers, const v
         ma.X = X; ma.ldx = ldx; ma.rows = rows; ma.d = w->d; ma.n_ps = w->d / kFT;
         ma.H = wsc; ma.h_slot = h_slot; ma.psum = (float*)(wsc + hb); ma.ps_slot = ps_slot;
         KVArgs ka{};
-        ka.H = wsc; ka.h_slot = h_slot; ka.psum = (const float*)(wsc + hb); ka.ps_slot = ps_slot;
+        ka.psum = (const float*)(wsc + hb); ka.ps_slot = ps_slot; ka.ld_in = w->d;
         ka.n_ps = w->d / kFT; ka.d = w->d; ka.kvw = w->n_kv_heads * w->head_dim; ka.eps = w->rms_eps;
         ka.rows = rows; ka.t0 = t0; ka.pos0 = pos0; ka.rope = rope;
         ka.paged = cache->layout == RF_LAYOUT_PAGED; ka.block_size = cache->block_size;
@@ -458,6 +486,7 @@ static rf_status launch_fill(const rf_fill_weights* w, int32_t n_layers, const v
         for (int g = 0; g < gsz; ++g) {
             ma.W[g] = w->W_map[l0 + g]; ma.bias[g] = w->b_map[l0 + g]; ma.gamma[g] = w->gamma[l0 + g];
             ka.Wk[g] = w->W_k[l0 + g]; ka.Wv[g] = w->W_v[l0 + g];
+            ka.in_k[g] = ka.in_v[g] = (const T*)wsc + g * h_slot;
             ka.kc[g] = kc[l0 + g]; ka.vc[g] = vc[l0 + g];
         }
         ma.tok_tiles = tok_tiles;
@@ -467,10 +496,54 @@ static rf_status launch_fill(const rf_fill_weights* w, int32_t n_layers, const v
         if (st != RF_OK) return st;
         const dim3 kv_grid((2 * ka.kvw / kFT) * tok_tiles * gsz);
         if (w->head_dim == 128)
-            hipLaunchKernelGGL((k_fill_kv<T, 128>), kv_grid, dim3(KVCore<T>::G::kThr), 0, stream, ka);
+            hipLaunchKernelGGL((k_fill_kv<T, 128, true, false>), kv_grid, dim3(KVCore<T>::G::kThr), 0, stream, ka);
         else
-            hipLaunchKernelGGL((k_fill_kv<T, 64>), kv_grid, dim3(KVCore<T>::G::kThr), 0, stream, ka);
+            hipLaunchKernelGGL((k_fill_kv<T, 64, true, false>), kv_grid, dim3(KVCore<T>::G::kThr), 0, stream, ka);
         st = check_launch("rf_fill: kv kernel");
+        if (st != RF_OK) return st;
+    }
+    return RF_OK;
+}
+
+template <typename T, int DH, bool BIAS>
+static void launch_translate_group(const KVArgs& ka, int gsz, hipStream_t stream) {
+    const dim3 grid((2 * ka.kvw / kFT) * ka.tok_tiles * gsz);
+    hipLaunchKernelGGL((k_fill_kv<T, DH, false, BIAS>), grid, dim3(KVCore<T>::G::kThr), 0, stream, ka);
+}
+
+template <typename T>
+static rf_status launch_translate(const rf_translate_weights* w, int32_t n_layers, const void* const* src_k,
+                                  const void* const* src_v, int64_t ld_src, int64_t t0, int64_t t1, int64_t pos0,
+                                  const rf_cache_desc* cache, const rf_cache_layout_t& L, void* const* kc,
+                                  void* const* vc, const int32_t* table, int64_t n_table, const float* rope,
+                                  hipStream_t stream) {
+    const int64_t rows = t1 - t0;
+    const bool bias = w->b_k != nullptr;
+    for (int l0 = 0; l0 < n_layers; l0 += kMaxGroup) {
+        const int gsz = std::min(kMaxGroup, n_layers - l0);
+        KVArgs ka{};
+        ka.psum = nullptr; ka.ps_slot = 0; ka.n_ps = 0;
+        ka.d = w->d_in; ka.kvw = w->n_kv_heads * w->head_dim; ka.eps = 0.f;
+        ka.tok_tiles = (int)ceil_div(rows, kTT);
+        ka.rows = rows; ka.t0 = t0; ka.pos0 = pos0; ka.rope = rope;
+        ka.paged = cache->layout == RF_LAYOUT_PAGED; ka.block_size = cache->block_size;
+        ka.stride_block = L.stride_block; ka.stride_head = L.stride_head; ka.stride_token = L.stride_token;
+        ka.n_blocks = L.n_blocks; ka.block_table = table; ka.n_table_blocks = n_table;
+        ka.ld_in = ld_src;
+        for (int g = 0; g < gsz; ++g) {
+            ka.in_k[g] = src_k[l0 + g]; ka.in_v[g] = src_v[l0 + g];
+            ka.bk[g] = bias ? w->b_k[l0 + g] : nullptr; ka.bv[g] = bias ? w->b_v[l0 + g] : nullptr;
+            ka.Wk[g] = w->T_k[l0 + g]; ka.Wv[g] = w->T_v[l0 + g];
+            ka.kc[g] = kc[l0 + g]; ka.vc[g] = vc[l0 + g];
+        }
+        if (w->head_dim == 128) {
+            if (bias) launch_translate_group<T, 128, true>(ka, gsz, stream);
+            else launch_translate_group<T, 128, false>(ka, gsz, stream);
+        } else {
+            if (bias) launch_translate_group<T, 64, true>(ka, gsz, stream);
+            else launch_translate_group<T, 64, false>(ka, gsz, stream);
+        }
+        const rf_status st = check_launch("rf_translate: kernel");
         if (st != RF_OK) return st;
     }
     return RF_OK;
@@ -498,7 +571,8 @@ rf_status rf_rope_table(double base, int32_t head_dim, int64_t n_pos, float* d_t
 rf_status rf_pack_weights(rf_dtype dtype, int64_t rows, int64_t cols, const void* d_src, int64_t ld_src,
                           int32_t rope_head_dim, void* d_dst, void* stream) {
     clear_error();
-    RF_REQUIRE(dtype == RF_BF16, RF_ERR_UNSUPPORTED, "rf_pack_weights: only BF16 weights are packed");
+    RF_REQUIRE(dtype == RF_BF16 || dtype == RF_F32, RF_ERR_UNSUPPORTED,
+               "rf_pack_weights: the source must be BF16 or F32");
     RF_REQUIRE(rows >= 0 && rows % 256 == 0 && cols >= 0 && cols % 64 == 0, RF_ERR_UNSUPPORTED,
                "rf_pack_weights: rows must be a multiple of 256 and cols a multiple of 64");
     RF_REQUIRE(rope_head_dim == 0 || rope_head_dim == 64 || rope_head_dim == 128, RF_ERR_UNSUPPORTED,
@@ -509,8 +583,13 @@ rf_status rf_pack_weights(rf_dtype dtype, int64_t rows, int64_t cols, const void
     RF_REQUIRE(ld_src >= cols && ld_src % 8 == 0 && aligned(d_src, 16) && aligned(d_dst, 16), RF_ERR_INVALID_ARG,
                "rf_pack_weights: source rows must be >= cols long with a stride of 8 elements, 16-byte aligned");
     const int64_t n_chunks = rows * cols / 8;
-    hipLaunchKernelGGL(k_pack_weights, dim3((unsigned)ceil_div(n_chunks, 256)), dim3(256), 0, (hipStream_t)stream,
-                       (const bf16_t*)d_src, ld_src, cols, rope_head_dim, n_chunks, (bf16_t*)d_dst);
+    const dim3 grid((unsigned)ceil_div(n_chunks, 256));
+    if (dtype == RF_BF16)
+        hipLaunchKernelGGL(k_pack_weights<bf16_t>, grid, dim3(256), 0, (hipStream_t)stream, (const bf16_t*)d_src,
+                           ld_src, cols, rope_head_dim, n_chunks, (bf16_t*)d_dst);
+    else
+        hipLaunchKernelGGL(k_pack_weights<float>, grid, dim3(256), 0, (hipStream_t)stream, (const float*)d_src,
+                           ld_src, cols, rope_head_dim, n_chunks, (bf16_t*)d_dst);
     return check_launch("rf_pack_weights");
 }
 
@@ -573,6 +652,64 @@ rf_status rf_fill(const rf_fill_weights* w, int32_t n_layers, const void* d_X, i
                                    n_table_blocks, d_rope, d_ws, ws_bytes, s);
     return launch_fill<float>(w, n_layers, d_X, ldx, t0, t1, pos0, cache, L, k_cache, v_cache, d_block_table,
                               n_table_blocks, d_rope, d_ws, ws_bytes, s);
+}
+
+rf_status rf_translate(const rf_translate_weights* w, int32_t n_layers, const void* const* d_src_k,
+                       const void* const* d_src_v, int64_t ld_src, int64_t t0, int64_t t1, int64_t pos0,
+                       const rf_cache_desc* cache, void* const* k_cache, void* const* v_cache,
+                       const int32_t* d_block_table, int64_t n_table_blocks, const float* d_rope,
+                       int64_t rope_len, void* stream) {
+    clear_error();
+    RF_REQUIRE(w && cache, RF_ERR_INVALID_ARG, "rf_translate: null weights or cache descriptor");
+    RF_REQUIRE(n_layers >= 0, RF_ERR_INVALID_ARG, "rf_translate: n_layers must be >= 0");
+    RF_REQUIRE(t0 >= 0 && t1 >= t0 && pos0 >= 0, RF_ERR_INVALID_ARG, "rf_translate: need 0 <= t0 <= t1 and pos0 >= 0");
+    RF_REQUIRE(valid_dtype(w->dtype), RF_ERR_INVALID_ARG, "rf_translate: bad dtype");
+    RF_REQUIRE(cache->dtype == w->dtype, RF_ERR_UNSUPPORTED, "rf_translate: cache dtype must equal the maps' dtype");
+    const int din_step = w->dtype == RF_BF16 ? 128 : 64;
+    RF_REQUIRE(w->d_in > 0 && w->d_in % din_step == 0 && w->d_in <= (1 << 16), RF_ERR_UNSUPPORTED,
+               "rf_translate: d_in must be a positive multiple of 128 (BF16) or 64 (F32), at most 65536");
+    RF_REQUIRE(w->head_dim == 64 || w->head_dim == 128, RF_ERR_UNSUPPORTED, "rf_translate: head_dim must be 64 or 128");
+    RF_REQUIRE(w->n_kv_heads > 0 && (w->n_kv_heads * w->head_dim) % kFT == 0, RF_ERR_UNSUPPORTED,
+               "rf_translate: n_kv_heads*head_dim must be a positive multiple of 256");
+    RF_REQUIRE(cache->n_kv_heads == w->n_kv_heads && cache->head_dim == w->head_dim, RF_ERR_INVALID_ARG,
+               "rf_translate: cache heads/head_dim differ from the maps'");
+    RF_REQUIRE((w->b_k == nullptr) == (w->b_v == nullptr), RF_ERR_INVALID_ARG,
+               "rf_translate: b_k and b_v must both be given or both be NULL");
+    rf_cache_layout_t L;
+    rf_status st = rf_cache_layout(cache, &L);
+    if (st != RF_OK) return st;
+    if (n_layers == 0 || t1 == t0) return RF_OK;
+    RF_REQUIRE(d_src_k && d_src_v && w->T_k && w->T_v && k_cache && v_cache && d_rope, RF_ERR_INVALID_ARG,
+               "rf_translate: null pointer argument");
+    const size_t eb = elem_bytes(w->dtype);
+    RF_REQUIRE(ld_src >= w->d_in && (ld_src * (int64_t)eb) % 16 == 0 && ld_src <= (1 << 21), RF_ERR_INVALID_ARG,
+               "rf_translate: source rows must be >= d_in long with a 16-byte multiple stride of at most 2^21 elements");
+    const bool bias = w->b_k != nullptr;
+    for (int l = 0; l < n_layers; ++l) {
+        RF_REQUIRE(d_src_k[l] && d_src_v[l] && w->T_k[l] && w->T_v[l] && k_cache[l] && v_cache[l], RF_ERR_INVALID_ARG,
+                   "rf_translate: null per-layer pointer");
+        RF_REQUIRE(aligned(d_src_k[l], 16) && aligned(d_src_v[l], 16) && aligned(w->T_k[l], 16) &&
+                       aligned(w->T_v[l], 16) && aligned(k_cache[l], 16) && aligned(v_cache[l], 16),
+                   RF_ERR_INVALID_ARG, "rf_translate: per-layer buffers must be 16-byte aligned");
+        if (bias)
+            RF_REQUIRE(w->b_k[l] && w->b_v[l] && aligned(w->b_k[l], 16) && aligned(w->b_v[l], 16), RF_ERR_INVALID_ARG,
+                       "rf_translate: intercepts must be non-null and 16-byte aligned");
+    }
+    RF_REQUIRE(aligned(d_rope, 16), RF_ERR_INVALID_ARG, "rf_translate: rope table must be 16-byte aligned");
+    RF_REQUIRE(pos0 + t1 <= rope_len, RF_ERR_INVALID_ARG, "rf_translate: rope table shorter than pos0 + t1");
+    if (cache->layout == RF_LAYOUT_PAGED) {
+        RF_REQUIRE(d_block_table, RF_ERR_INVALID_ARG, "rf_translate: paged cache needs a block table");
+        RF_REQUIRE(ceil_div(t1, cache->block_size) <= n_table_blocks, RF_ERR_INVALID_ARG,
+                   "rf_translate: block table shorter than ceil(t1 / block_size)");
+    } else {
+        RF_REQUIRE(t1 <= cache->max_tokens, RF_ERR_INVALID_ARG, "rf_translate: t1 exceeds the cache's max_tokens");
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if (w->dtype == RF_BF16)
+        return launch_translate<bf16_t>(w, n_layers, d_src_k, d_src_v, ld_src, t0, t1, pos0, cache, L, k_cache,
+                                        v_cache, d_block_table, n_table_blocks, d_rope, s);
+    return launch_translate<float>(w, n_layers, d_src_k, d_src_v, ld_src, t0, t1, pos0, cache, L, k_cache, v_cache,
+                                   d_block_table, n_table_blocks, d_rope, s);
 }
 
 }  // extern "C"

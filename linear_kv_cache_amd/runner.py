@@ -7,9 +7,10 @@ from typing import List, Optional, Sequence
 
 import torch
 
-from . import (RF_LAYOUT_CONTIGUOUS, RF_LAYOUT_PAGED, FillWeights, cache_desc, gram_desc, rf_cache_layout,
-               rf_fill, rf_fill_workspace_bytes, rf_gram_accumulate, rf_gram_init, rf_gram_state_bytes,
-               rf_gram_state_layout, rf_pack_weights, rf_rope_table, rf_solve, rf_solve_workspace_bytes)
+from . import (RF_LAYOUT_CONTIGUOUS, RF_LAYOUT_PAGED, FillWeights, TranslateWeights, cache_desc, gram_desc,
+               rf_cache_layout, rf_fill, rf_fill_workspace_bytes, rf_gram_accumulate, rf_gram_init,
+               rf_gram_state_bytes, rf_gram_state_layout, rf_pack_weights, rf_rope_table, rf_solve,
+               rf_solve_workspace_bytes, rf_translate)
 
 
 def device_bytes(n: int, device) -> torch.Tensor:
@@ -103,8 +104,8 @@ def gather_rows(cache: Cache, pool: torch.Tensor, t0: int, t1: int) -> torch.Ten
 
 
 def pack_weights(W: torch.Tensor, rope_head_dim: int = 0, stream=None) -> torch.Tensor:
-    """A packed copy (rf_pack_weights) of a bf16 [rows, cols] weight matrix."""
-    out = torch.empty(W.shape[0], W.shape[1], dtype=W.dtype, device=W.device)
+    """A packed bf16 copy (rf_pack_weights) of a bf16 or fp32 [rows, cols] weight matrix."""
+    out = torch.empty(W.shape[0], W.shape[1], dtype=torch.bfloat16, device=W.device)
     rf_pack_weights(W, out, rope_head_dim, stream)
     return out
 
@@ -135,3 +136,29 @@ class Filler:
     def fill(self, X, t0: int, t1: int, pos0: int, cache: Cache, stream=None):
         rf_fill(self.w, X, t0, t1, pos0, cache.desc, cache.k, cache.v, cache.block_table, self.rope,
                 self.rope_len, self.ws, stream)
+
+
+def translate_weights(d_in: int, n_kv_heads: int, head_dim: int, dtype, T_k, T_v, b_k=None, b_v=None,
+                      stream=None) -> TranslateWeights:
+    """TranslateWeights from row-major [kv_width, d_in] maps: for bf16 they are packed first
+    (fp32 maps are rounded to bf16 by the packing); the fp32 path reads them as they are."""
+    if dtype == torch.bfloat16:
+        T_k = [pack_weights(T, head_dim, stream) for T in T_k]
+        T_v = [pack_weights(T, head_dim, stream) for T in T_v]
+    return TranslateWeights(d_in, n_kv_heads, head_dim, dtype, list(T_k), list(T_v),
+                            None if b_k is None else list(b_k), None if b_v is None else list(b_v))
+
+
+class Translator:
+    """Holds the per-target-layer translator maps and a RoPE table; translates token ranges."""
+
+    def __init__(self, weights: TranslateWeights, rope_base: float, max_pos: int, device, stream=None):
+        self.w = weights
+        self.rope_len = max_pos
+        self.rope = torch.empty(max_pos, weights.head_dim, dtype=torch.float32, device=device)
+        rf_rope_table(rope_base, weights.head_dim, max_pos, self.rope, stream)
+
+    def translate(self, src_k: Sequence, src_v: Sequence, ld_src: int, t0: int, t1: int, pos0: int, cache: Cache,
+                  stream=None):
+        rf_translate(self.w, src_k, src_v, ld_src, t0, t1, pos0, cache.desc, cache.k, cache.v, cache.block_table,
+                     self.rope, self.rope_len, stream)

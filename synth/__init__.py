@@ -267,3 +267,110 @@ def block_table(cfg: Config, n_tokens: int, device="cpu", extra_blocks: int = 3)
     g = generator(cfg.seed, "block_table", device="cpu")
     phys = torch.randperm(n_logical + extra_blocks, generator=g)[:n_logical]
     return phys.to(torch.int32).to(device)
+
+
+# ----------------------------------------------------------------------------------------
+# KV-cache translation workloads (token-wise linear translators between two models' caches)
+# ----------------------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class TranslateConfig:
+    """One translation workload: a source cache of n_src layers, a target of n_tgt layers,
+    each target layer reading nu source layers (relative-depth bands)."""
+
+    name: str
+    n_src: int
+    src_kv_heads: int
+    src_head_dim: int
+    n_tgt: int
+    n_kv_heads: int
+    head_dim: int
+    nu: int
+    rope_base: float
+    dtype: str
+    tokens: int                 # prompt tokens held by the source cache
+    t0: int                     # translated token range [t0, t1)
+    t1: int
+    paged: bool
+    block_size: int
+    maps: str                   # 'dense' (head-mixing) | 'headwise' (block-diagonal)
+    bias: bool
+    seed: int
+
+    @property
+    def d_src(self) -> int:
+        return self.src_kv_heads * self.src_head_dim
+
+    @property
+    def d_in(self) -> int:
+        return self.nu * self.d_src
+
+    @property
+    def kv_width(self) -> int:
+        return self.n_kv_heads * self.head_dim
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def flop_per_token_layer(self) -> int:
+        """Algorithmic work of one translated (token, target layer): K and V products."""
+        return 2 * 2 * self.d_in * self.kv_width
+
+
+TR_BENCH = TranslateConfig(name="kv-translate-28to36-kv8x128-nu2-T16384", n_src=28, src_kv_heads=8,
+                           src_head_dim=128, n_tgt=36, n_kv_heads=8, head_dim=128, nu=2, rope_base=1e6,
+                           dtype="bf16", tokens=16384, t0=0, t1=16384, paged=False, block_size=16,
+                           maps="dense", bias=False, seed=1006)
+
+
+def _tstore(t: torch.Tensor, cfg: TranslateConfig) -> torch.Tensor:
+    return t.to(cfg.torch_dtype).contiguous()
+
+
+def source_cache(cfg: TranslateConfig, rows: int, device="cpu", row_offset: int = 0):
+    """Source keys (before rotation) and values of ``rows`` tokens, [rows, n_src, d_src] each
+    (token-major, source layers side by side).  Keys carry per-channel scales
+    ~ LogNormal(0, 0.5) per layer (key channels differ in magnitude); values are N(0, 1)."""
+    ks = torch.exp(0.5 * _randn((cfg.n_src, cfg.d_src), cfg.seed, "kscale", device=device))
+    K = _randn((rows, cfg.n_src, cfg.d_src), cfg.seed, "srcK", row_offset, device=device) * ks
+    V = _randn((rows, cfg.n_src, cfg.d_src), cfg.seed, "srcV", row_offset, device=device)
+    return _tstore(K, cfg), _tstore(V, cfg)
+
+
+def translator_maps(cfg: TranslateConfig, layer: int, device="cpu"):
+    """(T_k, T_v, b_k, b_v) of one target layer: T [kv_width, d_in] out-feature major with
+    entries ~ N(0, 1/d_in) (zero outside the diagonal head blocks of each source layer for
+    'headwise'); b ~ N(0, 0.1^2) or None."""
+    out = []
+    for side in ("Tk", "Tv"):
+        T = _randn((cfg.kv_width, cfg.d_in), cfg.seed, side, layer, device=device) / cfg.d_in ** 0.5
+        if cfg.maps == "headwise":
+            if cfg.src_kv_heads != cfg.n_kv_heads:
+                raise ValueError("head-wise maps need as many source as target heads")
+            oh = torch.arange(cfg.kv_width, device=device) // cfg.head_dim
+            ih = (torch.arange(cfg.d_in, device=device) % cfg.d_src) // cfg.src_head_dim
+            T = T * (oh[:, None] == ih[None, :])
+        out.append(_tstore(T, cfg))
+    bk = bv = None
+    if cfg.bias:
+        bk = (0.1 * _randn((cfg.kv_width,), cfg.seed, "bk", layer, device=device)).contiguous()
+        bv = (0.1 * _randn((cfg.kv_width,), cfg.seed, "bv", layer, device=device)).contiguous()
+    return out[0], out[1], bk, bv
+
+
+def translator_calibration(cfg: TranslateConfig, layer: int, src_rows: torch.Tensor, side: str):
+    """Synthetic target cache rows for a closed-form translator fit: Y = S A + 0.1 E with a
+    planted A ~ N(0, 1/d_in) [d_in, kv_width] (x-times-matrix) and E ~ N(0, 1).  The data law
+    of the fit workload, not a step of the method."""
+    device = src_rows.device
+    A = _randn((cfg.d_in, cfg.kv_width), cfg.seed, "Acal", side, layer, device=device) / cfg.d_in ** 0.5
+    E = _randn((src_rows.shape[0], cfg.kv_width), cfg.seed, "Ecal", side, layer, device=device)
+    return _tstore(src_rows.float() @ A + 0.1 * E, cfg)
+
+
+def translate_block_table(cfg: TranslateConfig, n_tokens: int, device="cpu", extra_blocks: int = 3) -> torch.Tensor:
+    n_logical = -(-n_tokens // cfg.block_size)
+    g = generator(cfg.seed, "block_table", device="cpu")
+    phys = torch.randperm(n_logical + extra_blocks, generator=g)[:n_logical]
+    return phys.to(torch.int32).to(device)

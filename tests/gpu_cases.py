@@ -171,3 +171,85 @@ def fit_errors(res, case: FitCase):
         errs_w.append(float(np.max(np.abs(Wg - W_ref)) / np.max(np.abs(W_ref))))
         errs_b.append(float(np.max(np.abs(f64(res["b"][l]) - b_ref)) / max(np.max(np.abs(b_ref)), 1e-30)))
     return errs_w, errs_b
+
+
+# ------------------------------------------------------------------------------------------
+@dataclass
+class TranslateCase:
+    cfg: synth.TranslateConfig
+    t0: int
+    t1: int
+    pos0: int = 0
+    chunk: Optional[int] = None
+    n_layers: Optional[int] = None
+    sample: Optional[Sequence[int]] = None     # token indices to compare (None = all translated)
+    gen_device: str = "cpu"
+
+
+def run_translate_case(case: TranslateCase, device="cuda"):
+    """Translate [t0, t1) of the selected target layers through rf_translate and compare with
+    the oracle on the same stored source rows and maps."""
+    import linear_kv_cache_amd as rf
+    from linear_kv_cache_amd.runner import Translator, alloc_cache, gather_rows, translate_weights
+
+    cfg = case.cfg
+    n_tgt = case.n_layers or cfg.n_tgt
+    E = rf.rf_relative_depth_sources(cfg.n_src, cfg.n_tgt, cfg.nu)[:n_tgt]
+    assert E == oracle.relative_depth_sources(cfg.n_src, cfg.n_tgt, cfg.nu)[:n_tgt]
+    T = max(case.t1, cfg.tokens)
+    gd = case.gen_device
+    Ks, Vs = synth.source_cache(cfg, case.t1 - case.t0, device=gd, row_offset=case.t0)
+    maps = [synth.translator_maps(cfg, l, device=gd) for l in range(n_tgt)]
+    Kd, Vd = Ks.to(device), Vs.to(device)
+    md = [tuple(None if x is None else x.to(device) for x in m) for m in maps]
+    tw = translate_weights(cfg.d_in, cfg.n_kv_heads, cfg.head_dim, cfg.torch_dtype, [m[0] for m in md],
+                           [m[1] for m in md], [m[2] for m in md] if cfg.bias else None,
+                           [m[3] for m in md] if cfg.bias else None)
+    table = synth.translate_block_table(cfg, T, device=device) if cfg.paged else None
+    cache = alloc_cache(n_tgt, cfg.n_kv_heads, cfg.head_dim, T, cfg.torch_dtype, device, paged=cfg.paged,
+                        block_size=cfg.block_size, block_table=table,
+                        n_blocks=(int(table.max()) + 1) if table is not None else None)
+    tr = Translator(tw, cfg.rope_base, case.pos0 + T, device)
+    ld = cfg.n_src * cfg.d_src
+    chunk = case.chunk or (case.t1 - case.t0)
+    for c0 in range(case.t0, case.t1, chunk):
+        c1 = min(case.t1, c0 + chunk)
+        r0 = c0 - case.t0
+        # a band of consecutive source layers is one row segment of the token-major source
+        tr.translate([Kd[r0, e[0]] for e in E], [Vd[r0, e[0]] for e in E], ld, c0, c1, case.pos0, cache)
+    torch.cuda.synchronize()
+
+    rows = np.arange(case.t0, case.t1) if case.sample is None else np.asarray(sorted(set(case.sample)))
+    ridx = torch.as_tensor(rows - case.t0)
+    Kn, Vn = f64(Ks[ridx]), f64(Vs[ridx])
+    out = {"k_err": [], "v_err": [], "sentinel_ok": True, "finite": True}
+    tol = KV_TOL_F32 if cfg.dtype == "f32" else KV_TOL_BF16
+    for li, (e, m) in enumerate(zip(E, maps)):
+        sk = Kn[:, e[0]:e[0] + cfg.nu].reshape(len(rows), -1)
+        sv = Vn[:, e[0]:e[0] + cfg.nu].reshape(len(rows), -1)
+        K_ref, V_ref = oracle.translate_layer(sk, sv, f64(m[0]).T, f64(m[1]).T,
+                                              None if m[2] is None else f64(m[2]),
+                                              None if m[3] is None else f64(m[3]),
+                                              case.pos0 + rows.astype(np.float64), cfg.n_kv_heads, cfg.head_dim,
+                                              cfg.rope_base)
+        Kall = gather_rows(cache, cache.k[li], 0, T)
+        Vall = gather_rows(cache, cache.v[li], 0, T)
+        di = torch.as_tensor(rows, device=device)
+        K, V = f64(Kall[di]), f64(Vall[di])
+        out["k_err"].append(float(np.max(np.abs(K - K_ref)) / np.sqrt(np.mean(K_ref ** 2))))
+        out["v_err"].append(float(np.max(np.abs(V - V_ref)) / np.sqrt(np.mean(V_ref ** 2))))
+        out["finite"] &= bool(torch.isfinite(Kall[case.t0:case.t1].float()).all()) and bool(
+            torch.isfinite(Vall[case.t0:case.t1].float()).all())
+        for pool in (cache.k[li], cache.v[li]):
+            if not cfg.paged:
+                vals = pool.view(-1, cfg.kv_width)
+                outside = torch.ones(vals.shape[0], dtype=torch.bool, device=device)
+                outside[case.t0:case.t1] = False
+                out["sentinel_ok"] &= bool(torch.isnan(vals[outside].float()).all())
+            else:
+                blk = pool.view(-1, cfg.n_kv_heads, cfg.block_size, cfg.head_dim)
+                unw = ~written_mask(cache, case.t0, case.t1, T)
+                out["sentinel_ok"] &= bool(torch.isnan(blk.permute(0, 2, 1, 3)[unw].float()).all())
+    out["tol"] = tol
+    out["max_err"] = max(out["k_err"] + out["v_err"])
+    return out

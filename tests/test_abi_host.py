@@ -155,7 +155,6 @@ def test_pack_weights_validation_before_enqueue():
     src = torch.zeros(256, 128, dtype=bf)
     dst = torch.zeros(256, 128, dtype=bf)
     cases = [
-        (dict(W=src.float(), dst=dst.float()), rf.RF_ERR_UNSUPPORTED),        # only bf16 is packed
         (dict(W=src[:100], dst=dst), rf.RF_ERR_UNSUPPORTED),                  # rows % 256
         (dict(W=src[:, :100], dst=dst), rf.RF_ERR_UNSUPPORTED),               # cols % 64
         (dict(W=src, dst=dst, rope_head_dim=32), rf.RF_ERR_UNSUPPORTED),
@@ -168,3 +167,59 @@ def test_pack_weights_validation_before_enqueue():
             rf.rf_pack_weights(stream=0, **kw)
         assert e.value.status == status, kw
     rf.rf_pack_weights(src[:0], dst, stream=0)   # no rows: nothing to do
+    with pytest.raises(rf.RidgeFillError) as e:    # an element type that is neither BF16 nor F32
+        rf._check(rf._lib.rf_pack_weights(7, 256, 128, src.data_ptr(), 128, 0, dst.data_ptr(), None))
+    assert e.value.status == rf.RF_ERR_UNSUPPORTED
+
+
+def test_relative_depth_sources_matches_the_oracle():
+    # host arithmetic, compared exactly with the oracle's nearest-band search
+    import oracle
+    for n_src in (1, 2, 3, 5, 12, 28, 36, 64):
+        for n_tgt in (1, 2, 3, 5, 17, 28, 36, 64):
+            for nu in sorted({1, 2, 3, 4, n_src} & set(range(1, n_src + 1))):
+                assert rf.rf_relative_depth_sources(n_src, n_tgt, nu) == \
+                    oracle.relative_depth_sources(n_src, n_tgt, nu), (n_src, n_tgt, nu)
+    for bad in [(4, 4, 5), (4, 0, 1), (4, 4, 0)]:
+        with pytest.raises(rf.RidgeFillError) as e:
+            rf.rf_relative_depth_sources(*bad)
+        assert e.value.status == rf.RF_ERR_INVALID_ARG
+
+
+def _tweights(d_in=256, H=4, dh=64, dtype=torch.float32, n=1, ptr=256, bias=False):
+    b = [ptr] * n if bias else None
+    return rf.TranslateWeights(d_in, H, dh, dtype, [ptr] * n, [ptr] * n, b, b)
+
+
+def test_translate_validation_before_enqueue():
+    cache = rf.cache_desc(4, 64, 512, rf.RF_LAYOUT_CONTIGUOUS, torch.float32)
+    rope = torch.empty(512, 64)
+
+    def call(w=None, t0=0, t1=512, pos0=0, cache_=cache, rope_len=512, ld=256, src=256, n_layers=None):
+        w = w or _tweights()
+        rf.rf_translate(w, [src], [src], ld, t0, t1, pos0, cache_, [256], [256], None, rope, rope_len,
+                        n_layers=n_layers)
+
+    w_half_bias = _tweights()
+    w_half_bias.b_k = [256]
+    cases = [
+        (dict(t0=5, t1=4), rf.RF_ERR_INVALID_ARG),
+        (dict(w=_tweights(d_in=96)), rf.RF_ERR_UNSUPPORTED),                 # F32: d_in % 64
+        (dict(w=_tweights(d_in=192, dtype=torch.bfloat16)), rf.RF_ERR_UNSUPPORTED),  # BF16: % 128
+        (dict(w=_tweights(dh=96, H=8)), rf.RF_ERR_UNSUPPORTED),
+        (dict(w=_tweights(H=2)), rf.RF_ERR_UNSUPPORTED),                     # K width % 256
+        (dict(t1=513, rope_len=600), rf.RF_ERR_INVALID_ARG),                 # past max_tokens
+        (dict(pos0=1), rf.RF_ERR_INVALID_ARG),                               # rope table too short
+        (dict(ld=200), rf.RF_ERR_INVALID_ARG),                               # ld_src < d_in
+        (dict(ld=257), rf.RF_ERR_INVALID_ARG),                               # ld_src not 16-byte
+        (dict(src=260), rf.RF_ERR_INVALID_ARG),                              # misaligned source
+        (dict(src=0), rf.RF_ERR_INVALID_ARG),
+        (dict(w=w_half_bias), rf.RF_ERR_INVALID_ARG),                        # only b_k given
+        (dict(cache_=rf.cache_desc(4, 64, 512, rf.RF_LAYOUT_PAGED, torch.float32)), rf.RF_ERR_INVALID_ARG),
+    ]
+    for kw, status in cases:
+        with pytest.raises(rf.RidgeFillError) as e:
+            call(**kw)
+        assert e.value.status == status, kw
+    call(t0=7, t1=7)          # empty range: nothing to do
+    call(n_layers=0)          # no layers: nothing to do

@@ -1,0 +1,126 @@
+"""GPU parity of rf_translate (KV-Lingo page, section 3.1: token-wise linear K/V translators with
+pre-norm storing) against the oracle, element by element at sizes the oracle finishes in
+seconds and on sampled rows at the benchmark's full size.  Every case checks the
+untouched-row contract too, and the closed-form translator fit (section 3.2) runs through
+rf_gram_accumulate + rf_solve + rf_pack_weights + rf_translate."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_cases import KV_TOL_BF16, W_TOL, TranslateCase, f64, log, run_translate_case
+
+pytestmark = pytest.mark.gpu
+
+TINY_F32 = synth.TranslateConfig(name="tr-f32-d256", n_src=4, src_kv_heads=4, src_head_dim=64, n_tgt=3,
+                                 n_kv_heads=4, head_dim=64, nu=2, rope_base=1e4, dtype="f32", tokens=300, t0=0,
+                                 t1=300, paged=False, block_size=16, maps="dense", bias=True, seed=2001)
+SMALL_PAGED = synth.TranslateConfig(name="tr-bf16-paged", n_src=5, src_kv_heads=8, src_head_dim=128, n_tgt=4,
+                                    n_kv_heads=8, head_dim=128, nu=2, rope_base=1e6, dtype="bf16", tokens=800,
+                                    t0=37, t1=737, paged=True, block_size=16, maps="dense", bias=True, seed=2002)
+SMALL_HEADWISE = synth.scaled(SMALL_PAGED, name="tr-bf16-headwise", paged=False, maps="headwise", bias=False,
+                              nu=1, n_src=3, n_tgt=6, seed=2003)
+SMALL_DH64 = synth.TranslateConfig(name="tr-bf16-dh64", n_src=2, src_kv_heads=2, src_head_dim=128, n_tgt=2,
+                                   n_kv_heads=4, head_dim=64, nu=1, rope_base=1e4, dtype="bf16", tokens=600,
+                                   t0=0, t1=600, paged=False, block_size=16, maps="dense", bias=True, seed=2004)
+
+
+def _check(res, label):
+    log(f"[translate] {label}: max_err={res['max_err']:.3e} tol={res['tol']} k={np.round(res['k_err'], 5)} "
+        f"v={np.round(res['v_err'], 5)} sentinels={res['sentinel_ok']} finite={res['finite']}")
+    assert res["finite"], label
+    assert res["sentinel_ok"], label
+    assert res["max_err"] <= res["tol"], label
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def test_translate_tiny_fp32_two_sources_with_intercept():
+    # fp32: 4 source layers of 4 x 64 -> 3 target layers of 4 x 64, nu = 2 (d_in = 512)
+    _check(run_translate_case(TranslateCase(TINY_F32, 0, 300)), "fp32 nu=2 bias")
+
+
+def test_translate_bf16_paged_ragged_chunks():
+    # bf16 8 x 128, nu = 2 (d_in = 2048), paged (block 16, shuffled), rows [37, 737) in two
+    # calls of 300 and 400 tokens, pos0 = 11, intercepts
+    _check(run_translate_case(TranslateCase(SMALL_PAGED, 37, 737, pos0=11, chunk=300)), "bf16 paged chunked")
+
+
+def test_translate_bf16_headwise_and_tile_edges():
+    # block-diagonal (head-wise) maps, nu = 1, no intercept
+    _check(run_translate_case(TranslateCase(SMALL_HEADWISE, 0, 800)), "bf16 head-wise")
+    for t0, t1 in [(5, 6), (255, 257), (511, 769)]:
+        _check(run_translate_case(TranslateCase(SMALL_HEADWISE, t0, t1, n_layers=2)), f"rows [{t0},{t1})")
+
+
+def test_translate_bf16_head_dim_64_far_positions():
+    # target heads of 64 from a 2 x 128 source, RoPE at positions near 131072
+    _check(run_translate_case(TranslateCase(SMALL_DH64, 0, 600, pos0=130000)), "bf16 dh64 far pos")
+
+
+def test_translate_full_size_sampled():
+    # the benchmark's workload (28 -> 36 layers, 8 x 128, nu = 2, 16384 tokens, one call for all
+    # 36 target layers), compared on sampled rows: tile edges, the last row and a seeded spread
+    cfg = synth.TR_BENCH
+    g = np.random.default_rng(7)
+    sample = sorted(set([0, 1, 255, 256, 8191, 8192, cfg.t1 - 1] + list(g.integers(0, cfg.t1, 40))))
+    _check(run_translate_case(TranslateCase(cfg, cfg.t0, cfg.t1, sample=sample, gen_device="cuda")),
+           "full size sampled")
+
+
+def test_translator_fit_then_translate():
+    # Closed-form first stage on the GPU: for each target layer and side, the ridge fit of the
+    # target rows on its source rows (nu = 1, same width); the fp32 maps are packed (rounded to
+    # bf16) and used to translate a prompt.  W against the oracle fit; K/V against the oracle
+    # translation with the same stored (bf16-rounded) maps.
+    from linear_kv_cache_amd.runner import GramState, Translator, alloc_cache, gather_rows, translate_weights
+    cfg = synth.scaled(SMALL_PAGED, name="tr-fit", n_src=2, n_tgt=2, nu=1, paged=False, bias=True, seed=2005)
+    N, lam, dev = 4096, 0.1, "cuda"
+    E = oracle.relative_depth_sources(cfg.n_src, cfg.n_tgt, cfg.nu)
+    Kc, Vc = synth.source_cache(cfg, N, row_offset=10 ** 6)       # calibration tokens
+    maps_f32, biases, w_errs = [], [], []
+    for l, e in enumerate(E):
+        Tl, bl = [], []
+        for side, src in (("k", Kc), ("v", Vc)):
+            S = src[:, e[0]].contiguous()
+            Y = synth.translator_calibration(cfg, l, S, side)
+            st = GramState(cfg.d_in, 1, cfg.torch_dtype, dev)
+            st.accumulate(S.to(dev), [Y.to(dev)])
+            W, _, b, info = st.solve(lam, 0, [0], want_bf16=False)
+            torch.cuda.synchronize()
+            assert int(info.item()) == 0
+            T_ref, b_ref = oracle.fit_translator(f64(S), f64(Y), lam)
+            w_errs.append(float(np.max(np.abs(f64(W[0]).T - T_ref)) / np.max(np.abs(T_ref))))
+            Tl.append(W[0])
+            bl.append(b[0])
+        maps_f32.append(Tl)
+        biases.append(bl)
+    log(f"[translate] fit W errors {np.round(w_errs, 7)} (tol {W_TOL})")
+    assert max(w_errs) <= W_TOL
+    tw = translate_weights(cfg.d_in, cfg.n_kv_heads, cfg.head_dim, torch.bfloat16, [m[0] for m in maps_f32],
+                           [m[1] for m in maps_f32], [b[0] for b in biases], [b[1] for b in biases])
+    T_tok, pos0 = 700, 3
+    Ks, Vs = synth.source_cache(cfg, T_tok)
+    Kd, Vd = Ks.to(dev), Vs.to(dev)
+    cache = alloc_cache(cfg.n_tgt, cfg.n_kv_heads, cfg.head_dim, T_tok, torch.bfloat16, dev)
+    Translator(tw, cfg.rope_base, pos0 + T_tok, dev).translate([Kd[0, e[0]] for e in E], [Vd[0, e[0]] for e in E],
+                                                              cfg.n_src * cfg.d_src, 0, T_tok, pos0, cache)
+    torch.cuda.synchronize()
+    pos = pos0 + np.arange(T_tok, dtype=np.float64)
+    for l, e in enumerate(E):
+        # the maps the kernel consumed: the solve's fp32 maps rounded to nearest even bf16
+        Tk = f64(maps_f32[l][0].cpu().to(torch.bfloat16)).T
+        Tv = f64(maps_f32[l][1].cpu().to(torch.bfloat16)).T
+        K_ref, V_ref = oracle.translate_layer(f64(Ks[:, e[0]]), f64(Vs[:, e[0]]), Tk, Tv, f64(biases[l][0]),
+                                              f64(biases[l][1]), pos, cfg.n_kv_heads, cfg.head_dim, cfg.rope_base)
+        K = f64(gather_rows(cache, cache.k[l], 0, T_tok))
+        V = f64(gather_rows(cache, cache.v[l], 0, T_tok))
+        ke = float(np.max(np.abs(K - K_ref)) / np.sqrt(np.mean(K_ref ** 2)))
+        ve = float(np.max(np.abs(V - V_ref)) / np.sqrt(np.mean(V_ref ** 2)))
+        log(f"[translate] fitted layer {l}: k_err={ke:.3e} v_err={ve:.3e}")
+        assert ke <= KV_TOL_BF16 and ve <= KV_TOL_BF16
