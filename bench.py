@@ -41,6 +41,27 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def cpu_translate_baseline(n_tokens: int):
+    """Time the oracle's translation (fp64 NumPy) of n_tokens tokens over every target layer of
+    the translation workload."""
+    import numpy as np
+
+    import oracle
+    import synth
+    tc = synth.TR_BENCH
+    Ks, Vs = synth.source_cache(tc, n_tokens)
+    Kn, Vn = Ks.float().numpy().astype(np.float64), Vs.float().numpy().astype(np.float64)
+    E = oracle.relative_depth_sources(tc.n_src, tc.n_tgt, tc.nu)
+    layers = []
+    for l, e in enumerate(E):
+        Tk, Tv, _, _ = synth.translator_maps(tc, l)
+        layers.append((Kn[:, e[0]:e[0] + tc.nu].reshape(n_tokens, -1), Vn[:, e[0]:e[0] + tc.nu].reshape(n_tokens, -1),
+                       Tk.float().numpy().astype(np.float64).T, Tv.float().numpy().astype(np.float64).T, None, None))
+    t0 = time.perf_counter()
+    oracle.translate(0, n_tokens, 0, layers, tc.n_kv_heads, tc.head_dim, tc.rope_base)
+    return n_tokens / (time.perf_counter() - t0)
+
+
 def cpu_baseline(cfg, n_tokens: int, n_fit_rows: int):
     """Time the oracle (fp64 NumPy) on a bounded sample of the same workload."""
     import numpy as np
@@ -140,6 +161,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16384)
     ap.add_argument("--cpu-fit-rows", type=int, default=8192)
+    ap.add_argument("--cpu-translate-tokens", type=int, default=4096)
     ap.add_argument("--library-reference", action="store_true",
                     help="also time the fill's two products per layer as plain torch.matmul (hipBLASLt) "
                          "GEMMs on the same maps, projections and prompt states")
@@ -325,6 +347,11 @@ def main():
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on {args.cpu_tokens} tokens and {args.cpu_fit_rows} calibration rows")
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens, args.cpu_fit_rows)
+        if not args.no_translate:
+            log(f"timing the CPU oracle's translation of {args.cpu_translate_tokens} tokens")
+            out["cpu_baseline"]["translate_tokens_per_s"] = cpu_translate_baseline(args.cpu_translate_tokens)
+            out["cpu_baseline"]["sample"] += (f"; translate tokens/s from {args.cpu_translate_tokens} tokens x "
+                                              f"{synth.TR_BENCH.n_tgt} target layers")
     print(json.dumps(out), flush=True)
 
 
