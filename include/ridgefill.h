@@ -6,7 +6,8 @@
  * the lower layers of a model run exactly up to a split layer; for every filled prompt row
  * and every late layer, a per-layer ridge map fitted once in closed form predicts that
  * layer's input from the split layer's state, and the layer's own K/V projections write its
- * cache from the prediction.  The order of the layer's own cache path follows the KV-Lingo
+ * cache from the prediction.  The same fit serves the KV-Lingo page's token-wise cache
+ * translators (section 3.2, closed-form first stage), whose maps rf_translate applies.  The order of the layer's own cache path follows the KV-Lingo
  * page, section 3.1 "Rotation and normalisation" (pre-norm storing: normalise, project,
  * rotate keys by position, store).
  *
@@ -65,21 +66,24 @@ const char* rf_last_error(void);
  *
  * RidgeFill project page, "Method" step 2 and "Abstract": the map of each late layer is a
  * ridge regression fitted once, in closed form, from one pass over calibration rows.  The
- * pass carries, for the split-layer rows X and each target layer's input rows Y_l:
+ * pass carries, for the split-layer rows X ([rows][d]) and each target's rows Y_l
+ * ([rows][m], m = d_out, or d when d_out is 0):
  *     n        number of rows seen                       (int64)
  *     S_xx   = X^T X                 [d][d]               (fp32; rows <= cols are defined,
  *                                                          the strict lower triangle is not)
- *     S_yx   = Y_l^T X for each l    [n_targets*d][d]     (fp32; row l*d+o, column i holds
+ *     S_yx   = Y_l^T X for each l    [n_targets*m][d]     (fp32; row l*m+o, column i holds
  *                                                          sum_r Y_l[r][o] X[r][i])
  *     s_x    = 1^T X                 [d]                  (fp64)
- *     s_y    = 1^T Y_l for each l    [n_targets*d]        (fp64)
+ *     s_y    = 1^T Y_l for each l    [n_targets*m]        (fp64)
  * The state is one device buffer laid out as rf_gram_state_layout() reports; it is plain
  * data, so it can be copied out and back to checkpoint and resume a calibration pass.
  * ------------------------------------------------------------------------------------- */
 typedef struct {
-    int32_t d;          /* hidden width; a multiple of 256                          */
+    int32_t d;          /* width of the X rows (the maps' input); a multiple of 256  */
     int32_t n_targets;  /* number of target layers whose inputs are regressed on X  */
     rf_dtype dtype;     /* dtype of the X and Y rows passed to rf_gram_accumulate   */
+    int32_t d_out;      /* width m of each target's Y rows (the maps' output); 0 = d,
+                           else a multiple of 256, at most 65536                    */
 } rf_gram_desc;
 
 typedef struct {       /* byte offsets into the state buffer */
@@ -97,7 +101,8 @@ rf_status rf_gram_init(const rf_gram_desc* desc, void* d_state, void* stream);
 
 /* Add one chunk of ``rows`` calibration rows to the state.
  *  d_X : [rows][ldx] split-layer rows, dtype desc->dtype, ldx >= d, 16-B aligned rows
- *  d_Y : host array of n_targets device pointers, each [rows][ldy] target-layer input rows
+ *  d_Y : host array of n_targets device pointers, each [rows][ldy] target-layer input rows,
+ *        ldy >= m
  *  rows: >= 0 (0 is a no-op).  Any row count is allowed; ragged tails are handled.  The rows
  *        are read in place (no workspace); a chunk whose byte offsets would pass 2^31 is
  *        taken in several pieces.
@@ -113,7 +118,7 @@ rf_status rf_gram_accumulate(const rf_gram_desc* desc, void* d_state,
  * For each selected target l (intercept by mean-centring, rows as token states):
  *     mu_x = s_x / n,  mu_l = s_y,l / n
  *     C    = S_xx - n mu_x^T mu_x           (centred Gram, symmetric from the upper triangle)
- *     B_l  = S_yx,l - n mu_l^T mu_x          (centred cross moments, [d_out][d_in])
+ *     B_l  = S_yx,l - n mu_l^T mu_x          (centred cross moments, [m][d])
  *     W_l  = B_l (C + lambda I)^-1           (out-feature major: row o is the map of output o)
  *     b_l  = mu_l - mu_x W_l^T
  * so that the prediction is y = x W_l^T + b_l.  C + lambda I = L L^T is factored by Cholesky
@@ -124,10 +129,10 @@ rf_status rf_gram_accumulate(const rf_gram_desc* desc, void* d_state,
  * 1e-5 of max |W_l| from the fp64 product on well-scaled data.
  *
  *  targets : host array of n_sel target indices in [0, n_targets)
- *  d_W     : [n_sel][d][d] fp32 out, may be NULL; 16-B aligned
- *  d_W_lp  : [n_sel][d][d] bf16 out, may be NULL; 16-B aligned.  Written in the fill's packed
+ *  d_W     : [n_sel][m][d] fp32 out, may be NULL; 16-B aligned
+ *  d_W_lp  : [n_sel][m][d] bf16 out, may be NULL; 16-B aligned.  Written in the fill's packed
  *            layout (as rf_pack_weights with rope_head_dim 0 would leave it), ready for rf_fill
- *  d_b     : [n_sel][d] fp32 out, may be NULL
+ *  d_b     : [n_sel][m] fp32 out, may be NULL
  *  d_info  : one int32 out: 0 = success; k > 0 = C + lambda I is not positive definite and
  *            the k-th leading minor (1-based) is the first that fails.  The outputs are then
  *            meaningless (finite or not) but every write stays in bounds.

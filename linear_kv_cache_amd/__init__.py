@@ -40,7 +40,7 @@ class RidgeFillError(RuntimeError):
 
 # ---- structs -------------------------------------------------------------------------------
 class rf_gram_desc(C.Structure):
-    _fields_ = [("d", C.c_int32), ("n_targets", C.c_int32), ("dtype", C.c_int)]
+    _fields_ = [("d", C.c_int32), ("n_targets", C.c_int32), ("dtype", C.c_int), ("d_out", C.c_int32)]
 
 
 class rf_gram_layout_t(C.Structure):
@@ -148,8 +148,9 @@ def rf_last_error() -> str:
     return _lib.rf_last_error().decode()
 
 
-def gram_desc(d: int, n_targets: int, dtype) -> rf_gram_desc:
-    return rf_gram_desc(d, n_targets, _dtype_code(dtype))
+def gram_desc(d: int, n_targets: int, dtype, d_out: int = 0) -> rf_gram_desc:
+    """d_out: width of each target's rows (0 = d)."""
+    return rf_gram_desc(d, n_targets, _dtype_code(dtype), d_out)
 
 
 def rf_gram_state_layout(desc: rf_gram_desc) -> dict:
@@ -167,7 +168,7 @@ def rf_gram_init(desc: rf_gram_desc, state, stream=None):
 
 
 def rf_gram_accumulate(desc: rf_gram_desc, state, X, Ys: Sequence, rows: Optional[int] = None, stream=None):
-    """X: [rows, >=d] tensor (row stride = ldx); Ys: n_targets tensors [rows, >=d] sharing one row stride."""
+    """X: [rows, >=d] tensor (row stride = ldx); Ys: n_targets tensors [rows, >=d_out] sharing one row stride."""
     rows = X.shape[0] if rows is None else rows
     ldy = Ys[0].stride(0) if len(Ys) else desc.d
     if any(Y.stride(0) != ldy for Y in Ys):

@@ -26,6 +26,7 @@ struct GramArgs {
     int64_t rows;
     int64_t ldy;
     int32_t d;
+    int32_t dy;        // width of each target's rows
     int32_t tiles_m;   // d / kGT
     int32_t n_xx;      // S_xx upper tiles
     float* Sxx;
@@ -40,14 +41,14 @@ struct GramLayout {
     size_t off_n, off_Sxx, off_Syx, off_sx, off_sy, total;
 };
 
-static GramLayout gram_layout(int64_t d, int64_t nt) {
+static GramLayout gram_layout(int64_t d, int64_t nt, int64_t dy) {
     GramLayout L;
     L.off_n = 0;
     L.off_Sxx = 256;
     L.off_Syx = L.off_Sxx + round_up((size_t)(d * d) * 4, 256);
-    L.off_sx = L.off_Syx + round_up((size_t)(nt * d * d) * 4, 256);
+    L.off_sx = L.off_Syx + round_up((size_t)(nt * dy * d) * 4, 256);
     L.off_sy = L.off_sx + round_up((size_t)d * 8, 256);
-    L.total = L.off_sy + round_up((size_t)(nt * d) * 8, 256);
+    L.total = L.off_sy + round_up((size_t)(nt * dy) * 8, 256);
     return L;
 }
 
@@ -103,8 +104,8 @@ __global__ __launch_bounds__(kThreads) void k_gram(GramArgs a) {
         bptr = (const T*)a.X + srow0;
         bld = a.ldx;
     } else {
-        const int l = (int)(srow0 / a.d);
-        bptr = (const T*)a.Y[l] + (srow0 % a.d);
+        const int l = (int)(srow0 / a.dy);
+        bptr = (const T*)a.Y[l] + (srow0 % a.dy);
         bld = a.ldy;
     }
     const Operand B{bptr, bld, a.rows};
@@ -150,17 +151,20 @@ __global__ __launch_bounds__(kThreads) void k_gram(GramArgs a) {
 struct ColsumArgs {
     const void* src[kMaxTargets + 1];   // [rows][ld] per matrix: X, then Y_0 .. Y_{L-1}
     int64_t ld[kMaxTargets + 1];
-    double* csum[kMaxTargets + 1];      // column sums to add into: s_x, then s_y + l*d
+    double* csum[kMaxTargets + 1];      // column sums to add into: s_x, then s_y + l*dy
     int64_t rows;
-    int32_t blocks_per_mat;             // d / 64
+    int32_t blocks_x;                   // d / 64 work-groups for X
+    int32_t blocks_y;                   // dy / 64 work-groups for each Y_l
 };
 
-// One work-group per 64 columns of one matrix: thread t sums columns 8 (t & 7) .. + 8 over rows
+// One work-group per 64 columns of one matrix (X first, then each Y_l): thread t sums columns 8 (t & 7) .. + 8 over rows
 // r = t >> 3 (mod 32) in ascending order (eight rows in flight), then the 32 row groups are added
 // in a fixed order: the result does not depend on scheduling.
 __global__ __launch_bounds__(256) void k_gram_colsum(ColsumArgs a) {
-    const int g = blockIdx.x / a.blocks_per_mat;
-    const int c0 = (blockIdx.x % a.blocks_per_mat) * 64;
+    const int b = (int)blockIdx.x;
+    const int by = b - a.blocks_x;
+    const int g = by < 0 ? 0 : 1 + by / a.blocks_y;
+    const int c0 = (by < 0 ? b : by % a.blocks_y) * 64;
     const int t = threadIdx.x, ch = t & 7, rg = t >> 3;
     const int64_t ld = a.ld[g];
     const bf16_t* src = (const bf16_t*)a.src[g] + c0 + ch * 8;
@@ -202,6 +206,7 @@ struct PipeGramArgs {
     int64_t ldy;
     int64_t rows;           // rows of this piece (the reduction extent; also added to n)
     int32_t d;
+    int32_t dy;             // width of each Y_l
     int32_t tiles_m;        // d / 256
     int32_t n_xx;           // S_xx upper tiles
     int32_t n_yx;           // S_yx tiles
@@ -240,7 +245,7 @@ __global__ __launch_bounds__(GramCore::kThr) void k_gram_pipe(PipeGramArgs a) {
         Bp = a.X + srow0;
         ldb = a.ldx;
     } else {
-        Bp = a.Y[srow0 / a.d] + srow0 % a.d;
+        Bp = a.Y[srow0 / a.dy] + srow0 % a.dy;
         ldb = a.ldy;
     }
     int nk = (int)((a.rows + G::BK - 1) / G::BK);
@@ -282,6 +287,9 @@ static rf_status check_desc(const rf_gram_desc* desc) {
     RF_REQUIRE(desc->d > 0 && desc->n_targets >= 0, RF_ERR_INVALID_ARG, "gram: d must be > 0, n_targets >= 0");
     RF_REQUIRE(desc->d % kGT == 0, RF_ERR_UNSUPPORTED, "gram: d must be a multiple of 256");
     RF_REQUIRE(desc->n_targets <= kMaxTargets, RF_ERR_UNSUPPORTED, "gram: at most 64 target layers");
+    RF_REQUIRE(desc->d_out >= 0, RF_ERR_INVALID_ARG, "gram: d_out must be >= 0");
+    RF_REQUIRE(desc->d_out % kGT == 0 && desc->d_out <= (1 << 16), RF_ERR_UNSUPPORTED,
+               "gram: d_out must be 0 or a multiple of 256, at most 65536");
     return RF_OK;
 }
 
@@ -296,7 +304,7 @@ rf_status rf_gram_state_layout(const rf_gram_desc* desc, rf_gram_layout_t* out) 
     rf_status st = check_desc(desc);
     if (st != RF_OK) return st;
     RF_REQUIRE(out, RF_ERR_INVALID_ARG, "rf_gram_state_layout: null output");
-    const GramLayout L = gram_layout(desc->d, desc->n_targets);
+    const GramLayout L = gram_layout(desc->d, desc->n_targets, gram_dy(desc));
     out->off_n = (int64_t)L.off_n;
     out->off_S_xx = (int64_t)L.off_Sxx;
     out->off_S_yx = (int64_t)L.off_Syx;
@@ -317,7 +325,7 @@ rf_status rf_gram_init(const rf_gram_desc* desc, void* d_state, void* stream) {
     rf_status st = check_desc(desc);
     if (st != RF_OK) return st;
     RF_REQUIRE(d_state && aligned(d_state, 256), RF_ERR_INVALID_ARG, "rf_gram_init: state must be non-null, 256-B aligned");
-    const GramLayout L = gram_layout(desc->d, desc->n_targets);
+    const GramLayout L = gram_layout(desc->d, desc->n_targets, gram_dy(desc));
     const int64_t n16 = (int64_t)(L.total / 16);
     const int blocks = (int)std::min<int64_t>(ceil_div(n16, 256), 4096);
     hipLaunchKernelGGL(k_zero_bytes, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (uint4*)d_state, n16);
@@ -335,13 +343,14 @@ rf_status rf_gram_accumulate(const rf_gram_desc* desc, void* d_state, const void
     const size_t eb = elem_bytes(desc->dtype);
     RF_REQUIRE(d_X && aligned(d_X, 16) && ldx >= desc->d && (ldx * (int64_t)eb) % 16 == 0, RF_ERR_INVALID_ARG,
                "rf_gram_accumulate: X must be non-null, 16-B aligned, ldx >= d with 16-B row stride");
+    const int64_t dy = gram_dy(desc);
     if (desc->n_targets > 0) {
-        RF_REQUIRE(d_Y && ldy >= desc->d && (ldy * (int64_t)eb) % 16 == 0, RF_ERR_INVALID_ARG,
-                   "rf_gram_accumulate: Y needs n_targets pointers and ldy >= d with 16-B row stride");
+        RF_REQUIRE(d_Y && ldy >= dy && (ldy * (int64_t)eb) % 16 == 0, RF_ERR_INVALID_ARG,
+                   "rf_gram_accumulate: Y needs n_targets pointers and ldy >= d_out with 16-B row stride");
         for (int l = 0; l < desc->n_targets; ++l)
             RF_REQUIRE(d_Y[l] && aligned(d_Y[l], 16), RF_ERR_INVALID_ARG, "rf_gram_accumulate: null or misaligned Y pointer");
     }
-    const GramLayout L = gram_layout(desc->d, desc->n_targets);
+    const GramLayout L = gram_layout(desc->d, desc->n_targets, dy);
     char* s = (char*)d_state;
     hipStream_t strm = (hipStream_t)stream;
     float* Sxx = (float*)(s + L.off_Sxx);
@@ -351,11 +360,11 @@ rf_status rf_gram_accumulate(const rf_gram_desc* desc, void* d_state, const void
     int64_t* np = (int64_t*)(s + L.off_n);
     const int tiles_m = desc->d / kGT;
     const int n_xx = tiles_m * (tiles_m + 1) / 2;
-    const int n_yx = tiles_m * (int)((int64_t)desc->n_targets * desc->d / kGT);
+    const int n_yx = tiles_m * (int)((int64_t)desc->n_targets * dy / kGT);
 
     if (desc->dtype == RF_F32) {
         GramArgs a{};
-        a.X = d_X; a.ldx = ldx; a.rows = rows; a.ldy = ldy; a.d = desc->d;
+        a.X = d_X; a.ldx = ldx; a.rows = rows; a.ldy = ldy; a.d = desc->d; a.dy = (int32_t)dy;
         a.tiles_m = tiles_m; a.n_xx = n_xx;
         a.Sxx = Sxx; a.Syx = Syx; a.sx = sx; a.sy = sy; a.n = np;
         for (int l = 0; l < desc->n_targets; ++l) a.Y[l] = d_Y[l];
@@ -374,17 +383,17 @@ rf_status rf_gram_accumulate(const rf_gram_desc* desc, void* d_state, const void
         ColsumArgs ca{};
         ca.src[0] = (const bf16_t*)d_X + r0 * ldx; ca.ld[0] = ldx; ca.csum[0] = sx;
         for (int l = 0; l < desc->n_targets; ++l) {
-            ca.src[l + 1] = (const bf16_t*)d_Y[l] + r0 * ldy; ca.ld[l + 1] = ldy; ca.csum[l + 1] = sy + (int64_t)l * desc->d;
+            ca.src[l + 1] = (const bf16_t*)d_Y[l] + r0 * ldy; ca.ld[l + 1] = ldy; ca.csum[l + 1] = sy + (int64_t)l * dy;
         }
-        ca.rows = pr; ca.blocks_per_mat = desc->d / 64;
-        hipLaunchKernelGGL(k_gram_colsum, dim3((unsigned)((desc->n_targets + 1) * ca.blocks_per_mat)), dim3(256), 0,
+        ca.rows = pr; ca.blocks_x = desc->d / 64; ca.blocks_y = (int32_t)(dy / 64);
+        hipLaunchKernelGGL(k_gram_colsum, dim3((unsigned)(ca.blocks_x + desc->n_targets * ca.blocks_y)), dim3(256), 0,
                            strm, ca);
         st = check_launch("rf_gram_accumulate: column sums");
         if (st != RF_OK) return st;
         PipeGramArgs pa{};
         pa.X = (const bf16_t*)d_X + r0 * ldx; pa.ldx = ldx;
         for (int l = 0; l < desc->n_targets; ++l) pa.Y[l] = (const bf16_t*)d_Y[l] + r0 * ldy;
-        pa.ldy = ldy; pa.rows = pr; pa.d = desc->d; pa.tiles_m = tiles_m;
+        pa.ldy = ldy; pa.rows = pr; pa.d = desc->d; pa.dy = (int32_t)dy; pa.tiles_m = tiles_m;
         pa.n_xx = n_xx; pa.n_yx = n_yx; pa.Sxx = Sxx; pa.Syx = Syx; pa.n = np;
         hipLaunchKernelGGL(k_gram_pipe, dim3((unsigned)(n_xx + n_yx)), dim3(GramCore::kThr), 0, strm, pa);
         st = check_launch("rf_gram_accumulate: products");

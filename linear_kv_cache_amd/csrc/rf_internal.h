@@ -22,6 +22,8 @@ __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + 
 inline size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
 
 inline size_t elem_bytes(rf_dtype t) { return t == RF_F32 ? 4 : 2; }
+// Width of each target's rows (and of its map's output): d_out, or d when d_out is 0.
+inline int64_t gram_dy(const rf_gram_desc* g) { return g->d_out > 0 ? g->d_out : g->d; }
 inline bool valid_dtype(rf_dtype t) { return t == RF_F32 || t == RF_BF16; }
 
 }  // namespace rf

@@ -235,7 +235,8 @@ struct CrossArgs {
     const int64_t* np;
     const double* rdg;     // 1 / sqrt(diag(C + lambda I))
     int64_t d;
-    int64_t rows;          // n_sel * d
+    int64_t dy;            // outputs per target
+    int64_t rows;          // n_sel * dy
     bf16_t* Aq;            // [rows][2d]: [hi | lo] of the equilibrated centred cross moments
     double* mu_y;          // [rows]
     int32_t tsel[kMaxSel];
@@ -247,8 +248,8 @@ struct CrossArgs {
 // the factorisation, and those launches otherwise leave all but one CU idle.
 __device__ inline void centre_split_row(const CrossArgs& a, int64_t c, int64_t i0) {
     const double inv_n = 1.0 / (double)*a.np;
-    const int64_t s = c / a.d, o = c - s * a.d;
-    const int64_t srow = (int64_t)a.tsel[s] * a.d + o;
+    const int64_t s = c / a.dy, o = c - s * a.dy;
+    const int64_t srow = (int64_t)a.tsel[s] * a.dy + o;
     const double syv = a.sy[srow];
     const f32x4 v0 = *(const f32x4*)(a.Syx + srow * a.d + i0);
     const f32x4 v1 = *(const f32x4*)(a.Syx + srow * a.d + i0 + 4);
@@ -522,7 +523,7 @@ struct SolveWs {
     size_t total;
 };
 
-static SolveWs solve_ws(void* base, int64_t d, int64_t n_sel) {
+static SolveWs solve_ws(void* base, int64_t d, int64_t dy, int64_t n_sel) {
     SolveWs w{};
     size_t off = 0;
     char* p = (char*)base;
@@ -531,7 +532,7 @@ static SolveWs solve_ws(void* base, int64_t d, int64_t n_sel) {
         off += round_up(bytes, 256);
         return r;
     };
-    const int64_t rows = n_sel * d;
+    const int64_t rows = n_sel * dy;
     w.C = (double*)take(d * d * 8);
     w.Cinv = (double*)take(d * d * 8);
     w.Dinv = (double*)take(d * kNB * 8);
@@ -628,8 +629,9 @@ using namespace rf;
 extern "C" {
 
 size_t rf_solve_workspace_bytes(const rf_gram_desc* desc, int32_t n_sel) {
-    if (!desc || desc->d <= 0 || desc->d % 256 != 0 || n_sel < 0) return 0;
-    return solve_ws(nullptr, desc->d, n_sel).total;
+    rf_gram_layout_t GL;
+    if (n_sel < 0 || rf_gram_state_layout(desc, &GL) != RF_OK) return 0;
+    return solve_ws(nullptr, desc->d, gram_dy(desc), n_sel).total;
 }
 
 rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, double lambda, rf_lambda_mode mode,
@@ -650,8 +652,8 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, double lambda,
     RF_REQUIRE(aligned(d_ws, 256), RF_ERR_INVALID_ARG, "rf_solve: workspace must be 256-B aligned");
     RF_REQUIRE(aligned(d_W, 16) && aligned(d_W_lp, 16) && aligned(d_b, 4), RF_ERR_INVALID_ARG,
                "rf_solve: W outputs must be 16-byte aligned");
-    const int64_t d = desc->d;
-    const SolveWs w = solve_ws(d_ws, d, n_sel);
+    const int64_t d = desc->d, dy = gram_dy(desc);
+    const SolveWs w = solve_ws(d_ws, d, dy, n_sel);
     RF_REQUIRE(d_ws && ws_bytes >= w.total, RF_ERR_WORKSPACE, "rf_solve: workspace too small");
     hipStream_t s = (hipStream_t)stream;
     const char* sp = (const char*)d_state;
@@ -672,9 +674,9 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, double lambda,
 
     // centred, equilibrated, split cross moments: computed in slices by the diagonal-block
     // launches' spare work-groups
-    const int64_t rows = (int64_t)n_sel * d;
+    const int64_t rows = (int64_t)n_sel * dy;
     CrossArgs ca{};
-    ca.Syx = Syx; ca.sy = sy; ca.sx = sx; ca.np = np; ca.rdg = w.rdg; ca.d = d; ca.rows = rows; ca.Aq = w.Aq;
+    ca.Syx = Syx; ca.sy = sy; ca.sx = sx; ca.np = np; ca.rdg = w.rdg; ca.d = d; ca.dy = dy; ca.rows = rows; ca.Aq = w.Aq;
     ca.mu_y = w.mu_y;
     for (int i = 0; i < n_sel; ++i) ca.tsel[i] = targets[i];
     const int ny = (int)ceil_div(d, 2048);

@@ -23,11 +23,12 @@ def device_bytes(n: int, device) -> torch.Tensor:
 class GramState:
     """The one-pass second-moment state of a calibration run (device buffer + layout)."""
 
-    def __init__(self, d: int, n_targets: int, dtype, device, stream=None):
-        self.desc = gram_desc(d, n_targets, dtype)
+    def __init__(self, d: int, n_targets: int, dtype, device, stream=None, d_out: int = 0):
+        self.desc = gram_desc(d, n_targets, dtype, d_out)
         self.layout = rf_gram_state_layout(self.desc)
         self.buf = device_bytes(rf_gram_state_bytes(self.desc), device)
         self.d, self.n_targets = d, n_targets
+        self.dy = d_out or d
         rf_gram_init(self.desc, self.buf, stream)
 
     def accumulate(self, X, Ys, stream=None):
@@ -45,22 +46,22 @@ class GramState:
         return self._view(self.layout["off_S_xx"], self.d * self.d, torch.float32).view(self.d, self.d)
 
     def S_yx(self):
-        return self._view(self.layout["off_S_yx"], self.n_targets * self.d * self.d,
-                          torch.float32).view(self.n_targets, self.d, self.d)
+        return self._view(self.layout["off_S_yx"], self.n_targets * self.dy * self.d,
+                          torch.float32).view(self.n_targets, self.dy, self.d)
 
     def s_x(self):
         return self._view(self.layout["off_s_x"], self.d, torch.float64)
 
     def s_y(self):
-        return self._view(self.layout["off_s_y"], self.n_targets * self.d, torch.float64).view(self.n_targets, self.d)
+        return self._view(self.layout["off_s_y"], self.n_targets * self.dy, torch.float64).view(self.n_targets, self.dy)
 
     def solve(self, lam: float, mode: int, targets: Sequence[int], want_f32=True, want_bf16=True, stream=None,
               ws: Optional[torch.Tensor] = None):
         dev = self.buf.device
         n_sel = len(targets)
-        W = torch.empty(n_sel, self.d, self.d, dtype=torch.float32, device=dev) if want_f32 else None
-        Wlp = torch.empty(n_sel, self.d, self.d, dtype=torch.bfloat16, device=dev) if want_bf16 else None
-        b = torch.empty(n_sel, self.d, dtype=torch.float32, device=dev)
+        W = torch.empty(n_sel, self.dy, self.d, dtype=torch.float32, device=dev) if want_f32 else None
+        Wlp = torch.empty(n_sel, self.dy, self.d, dtype=torch.bfloat16, device=dev) if want_bf16 else None
+        b = torch.empty(n_sel, self.dy, dtype=torch.float32, device=dev)
         info = torch.empty(1, dtype=torch.int32, device=dev)
         if ws is None:
             ws = device_bytes(rf_solve_workspace_bytes(self.desc, n_sel), dev)

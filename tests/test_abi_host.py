@@ -64,6 +64,31 @@ def test_gram_state_layout():
     assert rf.rf_gram_state_bytes(rf.gram_desc(100, 2, torch.float32)) == 0
 
 
+def test_gram_state_layout_rectangular_maps():
+    # d_out = 1024 outputs per target from d = 2048 inputs (e.g. a translator reading two
+    # source layers): S_yx is [n_targets * 1024][2048], s_y [n_targets * 1024]
+    desc = rf.gram_desc(2048, 3, torch.bfloat16, d_out=1024)
+    L = rf.rf_gram_state_layout(desc)
+    assert L["off_S_yx"] == 256 + 2048 * 2048 * 4
+    assert L["off_s_x"] == L["off_S_yx"] + 3 * 1024 * 2048 * 4
+    assert L["total_bytes"] == L["off_s_y"] + 3 * 1024 * 8
+    assert rf.rf_gram_state_layout(rf.gram_desc(512, 2, torch.float32, d_out=512)) == \
+        rf.rf_gram_state_layout(rf.gram_desc(512, 2, torch.float32))
+    for d_out, status in ((300, rf.RF_ERR_UNSUPPORTED), (-256, rf.RF_ERR_INVALID_ARG)):
+        with pytest.raises(rf.RidgeFillError) as e:
+            rf.rf_gram_state_layout(rf.gram_desc(512, 1, torch.float32, d_out=d_out))
+        assert e.value.status == status
+    assert rf.rf_solve_workspace_bytes(rf.gram_desc(512, 1, torch.float32, d_out=300), 1) == 0
+    assert rf.rf_solve_workspace_bytes(rf.gram_desc(512, 2, torch.float32, d_out=1024), 2) > \
+        rf.rf_solve_workspace_bytes(rf.gram_desc(512, 2, torch.float32), 2)
+    # Y rows shorter than d_out are refused before anything is enqueued
+    ys = (C.c_void_p * 1)(256)
+    with pytest.raises(rf.RidgeFillError) as e:
+        rf._check(rf._lib.rf_gram_accumulate(C.byref(rf.gram_desc(256, 1, torch.float32, d_out=512)), 256, 256, 256,
+                                             ys, 256, 4, None))
+    assert e.value.status == rf.RF_ERR_INVALID_ARG
+
+
 def test_gram_validation_before_enqueue():
     with pytest.raises(rf.RidgeFillError) as e:
         rf.rf_gram_init(rf.gram_desc(300, 1, torch.float32), 256, None)

@@ -148,3 +148,49 @@ def test_gram_ragged_chunks_and_row_tails():
     log(f"[fit] ragged chunks {chunks} gram={res}")
     assert res["n"] == res["n_ref"] == sum(chunks)
     assert max(res["e_xx"], res["e_yx"]) <= 1e-5 and max(res["e_sx"], res["e_sy"]) <= 1e-12
+
+
+def _rect_data(d, m, n_targets, rows, dtype, seed):
+    # X ~ N(0, 1) rows; Y_l = X A_l + 0.1 E with a planted A_l ~ N(0, 1/d) of shape [d, m]
+    g = synth.generator(seed, "rect")
+    X = torch.randn(rows, d, generator=g)
+    Ys = [(X @ (torch.randn(d, m, generator=g) / d ** 0.5) + 0.1 * torch.randn(rows, m, generator=g)).to(dtype)
+          for _ in range(n_targets)]
+    return X.to(dtype), Ys
+
+
+def test_fit_rectangular_maps():
+    # maps with more outputs than inputs (fp32, d = 256 -> m = 512) and fewer (bf16, d = 512 ->
+    # m = 256), ragged chunks; Gram sums, W and b against the oracle
+    from linear_kv_cache_amd.runner import GramState
+    for d, m, nt, dtype, chunks, lam, seed in [(256, 512, 2, torch.float32, [1500, 2596], 1e-2, 11),
+                                               (512, 256, 3, torch.bfloat16, [1024, 3000, 77], 1e-1, 12)]:
+        X, Ys = _rect_data(d, m, nt, sum(chunks), dtype, seed)
+        st = GramState(d, nt, dtype, "cuda", d_out=m)
+        Xd, Yd = X.cuda(), [Y.cuda() for Y in Ys]
+        r0 = 0
+        for c in chunks:
+            st.accumulate(Xd[r0:r0 + c], [Y[r0:r0 + c] for Y in Yd])
+            r0 += c
+        W, Wlp, b, info = st.solve(lam, 0, list(range(nt)))
+        torch.cuda.synchronize()
+        assert int(info.item()) == 0
+        S_xx, S_xy, s_x, s_y, n = oracle.gram_sums(f64(X), [f64(Y) for Y in Ys])
+        g_yx = f64(st.S_yx())
+        e_yx = max(float(np.max(np.abs(g_yx[l] - S_xy[l].T)) / np.max(np.abs(S_xy[l]))) for l in range(nt))
+        e_sy = max(float(np.max(np.abs(f64(st.s_y())[l] - s_y[l])) / np.max(np.abs(s_y[l]))) for l in range(nt))
+        ew, eb = [], []
+        for l in range(nt):
+            W_ref, b_ref = oracle.fit(f64(X), f64(Ys[l]), lam)
+            ew.append(float(np.max(np.abs(f64(W[l]).T - W_ref)) / np.max(np.abs(W_ref))))
+            eb.append(float(np.max(np.abs(f64(b[l]) - b_ref)) / np.max(np.abs(b_ref))))
+        log(f"[fit] rectangular d={d} m={m} {dtype}: e_yx={e_yx:.2e} e_sy={e_sy:.2e} W_err={max(ew):.3e} "
+            f"b_err={max(eb):.3e}")
+        assert int(st.n().item()) == sum(chunks)
+        assert e_yx <= 1e-5 and e_sy <= 1e-12
+        assert max(ew) <= W_TOL and max(eb) <= W_TOL
+        if dtype == torch.bfloat16:
+            # the packed bf16 output is the fp32 map rounded, in the packed layout
+            from linear_kv_cache_amd.runner import pack_weights
+            for l in range(nt):
+                assert torch.equal(Wlp[l].view(torch.int16), pack_weights(W[l].to(torch.bfloat16)).view(torch.int16))

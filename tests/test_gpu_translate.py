@@ -75,11 +75,11 @@ def test_translate_full_size_sampled():
 
 def test_translator_fit_then_translate():
     # Closed-form first stage on the GPU: for each target layer and side, the ridge fit of the
-    # target rows on its source rows (nu = 1, same width); the fp32 maps are packed (rounded to
-    # bf16) and used to translate a prompt.  W against the oracle fit; K/V against the oracle
-    # translation with the same stored (bf16-rounded) maps.
+    # target rows (1024 wide) on its two source layers' rows (2048 wide); the fp32 maps are
+    # packed (rounded to bf16) and used to translate a prompt.  W against the oracle fit; K/V
+    # against the oracle translation with the same stored (bf16-rounded) maps.
     from linear_kv_cache_amd.runner import GramState, Translator, alloc_cache, gather_rows, translate_weights
-    cfg = synth.scaled(SMALL_PAGED, name="tr-fit", n_src=2, n_tgt=2, nu=1, paged=False, bias=True, seed=2005)
+    cfg = synth.scaled(SMALL_PAGED, name="tr-fit", n_src=3, n_tgt=2, nu=2, paged=False, bias=True, seed=2005)
     N, lam, dev = 4096, 0.1, "cuda"
     E = oracle.relative_depth_sources(cfg.n_src, cfg.n_tgt, cfg.nu)
     Kc, Vc = synth.source_cache(cfg, N, row_offset=10 ** 6)       # calibration tokens
@@ -87,9 +87,9 @@ def test_translator_fit_then_translate():
     for l, e in enumerate(E):
         Tl, bl = [], []
         for side, src in (("k", Kc), ("v", Vc)):
-            S = src[:, e[0]].contiguous()
+            S = src[:, e[0]:e[0] + cfg.nu].reshape(N, cfg.d_in)
             Y = synth.translator_calibration(cfg, l, S, side)
-            st = GramState(cfg.d_in, 1, cfg.torch_dtype, dev)
+            st = GramState(cfg.d_in, 1, cfg.torch_dtype, dev, d_out=cfg.kv_width)
             st.accumulate(S.to(dev), [Y.to(dev)])
             W, _, b, info = st.solve(lam, 0, [0], want_bf16=False)
             torch.cuda.synchronize()
@@ -116,7 +116,9 @@ def test_translator_fit_then_translate():
         # the maps the kernel consumed: the solve's fp32 maps rounded to nearest even bf16
         Tk = f64(maps_f32[l][0].cpu().to(torch.bfloat16)).T
         Tv = f64(maps_f32[l][1].cpu().to(torch.bfloat16)).T
-        K_ref, V_ref = oracle.translate_layer(f64(Ks[:, e[0]]), f64(Vs[:, e[0]]), Tk, Tv, f64(biases[l][0]),
+        sk = f64(Ks[:, e[0]:e[0] + cfg.nu].reshape(T_tok, cfg.d_in))
+        sv = f64(Vs[:, e[0]:e[0] + cfg.nu].reshape(T_tok, cfg.d_in))
+        K_ref, V_ref = oracle.translate_layer(sk, sv, Tk, Tv, f64(biases[l][0]),
                                               f64(biases[l][1]), pos, cfg.n_kv_heads, cfg.head_dim, cfg.rope_base)
         K = f64(gather_rows(cache, cache.k[l], 0, T_tok))
         V = f64(gather_rows(cache, cache.v[l], 0, T_tok))
