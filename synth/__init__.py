@@ -318,8 +318,10 @@ class TranslateConfig:
         return 2 * 2 * self.d_in * self.kv_width
 
 
+# The KV-Lingo page's cross-layer pairs: caches of 28 and 36 layers, 8 KV heads x 128 on both
+# sides, head-mixing maps reading 2 source layers (section 4, cross-layer pairs).
 TR_BENCH = TranslateConfig(name="kv-translate-28to36-kv8x128-nu2-T16384", n_src=28, src_kv_heads=8,
-                           src_head_dim=128, n_tgt=36, n_kv_heads=8, head_dim=128, nu=2, rope_base=1e6,
+                           src_head_dim=128, n_tgt=36, n_kv_heads=8, head_dim=128, nu=2, rope_base=5e5,
                            dtype="bf16", tokens=16384, t0=0, t1=16384, paged=False, block_size=16,
                            maps="dense", bias=False, seed=1006)
 

@@ -17,7 +17,7 @@ TINY_F32 = synth.TranslateConfig(name="tr-f32-d256", n_src=4, src_kv_heads=4, sr
                                  n_kv_heads=4, head_dim=64, nu=2, rope_base=1e4, dtype="f32", tokens=300, t0=0,
                                  t1=300, paged=False, block_size=16, maps="dense", bias=True, seed=2001)
 SMALL_PAGED = synth.TranslateConfig(name="tr-bf16-paged", n_src=5, src_kv_heads=8, src_head_dim=128, n_tgt=4,
-                                    n_kv_heads=8, head_dim=128, nu=2, rope_base=1e6, dtype="bf16", tokens=800,
+                                    n_kv_heads=8, head_dim=128, nu=2, rope_base=5e5, dtype="bf16", tokens=800,
                                     t0=37, t1=737, paged=True, block_size=16, maps="dense", bias=True, seed=2002)
 SMALL_HEADWISE = synth.scaled(SMALL_PAGED, name="tr-bf16-headwise", paged=False, maps="headwise", bias=False,
                               nu=1, n_src=3, n_tgt=6, seed=2003)
@@ -71,6 +71,17 @@ def test_translate_full_size_sampled():
     sample = sorted(set([0, 1, 255, 256, 8191, 8192, cfg.t1 - 1] + list(g.integers(0, cfg.t1, 40))))
     _check(run_translate_case(TranslateCase(cfg, cfg.t0, cfg.t1, sample=sample, gen_device="cuda")),
            "full size sampled")
+
+
+def test_translate_three_sources_36_to_48_sampled():
+    # the page's dense-to-MoE hand-off pattern: 48 target layers each reading nu = 3 of 36
+    # source layers by relative depth (d_in = 3072; two launches of 32 and 16 layers), 4096
+    # tokens compared on sampled rows
+    cfg = synth.scaled(synth.TR_BENCH, name="tr-36to48-nu3", n_src=36, n_tgt=48, nu=3, tokens=4096, t1=4096,
+                       seed=2006)
+    g = np.random.default_rng(8)
+    sample = sorted(set([0, 255, 256, 4095] + list(g.integers(0, 4096, 20))))
+    _check(run_translate_case(TranslateCase(cfg, 0, 4096, sample=sample, gen_device="cuda")), "36 -> 48 nu=3")
 
 
 def test_translator_fit_then_translate():
