@@ -75,6 +75,8 @@ const char* rf_last_error(void);
  *                                                          sum_r Y_l[r][o] X[r][i])
  *     s_x    = 1^T X                 [d]                  (fp64)
  *     s_y    = 1^T Y_l for each l    [n_targets*m]        (fp64)
+ *     s_yy   = 1^T (Y_l * Y_l)       [n_targets*m]        (fp64 column sums of squares: the
+ *                                                          fit's R^2 is read off the state)
  * The state is one device buffer laid out as rf_gram_state_layout() reports; it is plain
  * data, so it can be copied out and back to checkpoint and resume a calibration pass.
  * ------------------------------------------------------------------------------------- */
@@ -87,7 +89,7 @@ typedef struct {
 } rf_gram_desc;
 
 typedef struct {       /* byte offsets into the state buffer */
-    int64_t off_n, off_S_xx, off_S_yx, off_s_x, off_s_y, total_bytes;
+    int64_t off_n, off_S_xx, off_S_yx, off_s_x, off_s_y, off_s_yy, total_bytes;
 } rf_gram_layout_t;
 
 /* Host only.  Fills *out; returns RF_ERR_INVALID_ARG for a bad descriptor. */
@@ -144,6 +146,35 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state,
                    const int32_t* targets, int32_t n_sel,
                    float* d_W, void* d_W_lp, float* d_b, int32_t* d_info,
                    void* d_ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Fit quality.  KV-Lingo page, Appendix "The R^2 assignment": the score of a map is the
+ * fraction of its target's features it explains, read off the sums the fit accumulated (no
+ * extra pass over the data).  For each selected target l, with W_l the fp32 map rf_solve
+ * returned for the same state, lambda and mode:
+ *     B_l   = S_yx,l - s_y,l s_x^T / n                 (centred cross moments, [m][d])
+ *     SST_l = sum_o (s_yy,l[o] - s_y,l[o]^2 / n)        (centred total sum of squares)
+ *     R^2_l = (sum_{o,i} W_l[o][i] B_l[o][i] + lambda' sum_{o,i} W_l[o][i]^2) / SST_l
+ * where lambda' is the absolute ridge strength (lambda, or lambda x the mean diagonal of the
+ * centred Gram).  For the exact ridge map this equals 1 - ||Y~ - X~ W_l^T||^2 / ||Y~||^2 on
+ * the centred rows.  Sums run in fp64 in a fixed order.
+ *  targets : host array of n_sel target indices in [0, n_targets)
+ *  d_W     : [n_sel][m][d] fp32, 16-B aligned
+ *  d_r2    : [n_sel] fp64 out
+ *  d_ws    : rf_fit_r2_workspace_bytes(desc, n_sel) bytes, 256-B aligned
+ * ------------------------------------------------------------------------------------- */
+size_t rf_fit_r2_workspace_bytes(const rf_gram_desc* desc, int32_t n_sel);
+rf_status rf_fit_r2(const rf_gram_desc* desc, const void* d_state, double lambda, rf_lambda_mode mode,
+                    const int32_t* targets, int32_t n_sel, const float* d_W, double* d_r2,
+                    void* d_ws, size_t ws_bytes, void* stream);
+
+/* Host only.  The R^2 assignment (KV-Lingo page, Appendix "The R^2 assignment"): for each
+ * target layer l, the nu source layers s with the highest r2[l * n_src + s] (host fp64
+ * [n_tgt][n_src], e.g. rf_fit_r2 of single-source fits), written to out[l * nu + j] (host
+ * int32 [n_tgt][nu]) in ascending layer order.  Equal scores go to the shallower layer; NaN
+ * scores rank last.
+ * Keys and values are ranked apart by calling it once per side.  Needs 1 <= nu <= n_src. */
+rf_status rf_r2_assignment(const double* r2, int32_t n_tgt, int32_t n_src, int32_t nu, int32_t* out);
 
 /* ---------------------------------------------------------------------------------------
  * KV cache layout (host only).

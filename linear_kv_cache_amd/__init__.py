@@ -44,7 +44,8 @@ class rf_gram_desc(C.Structure):
 
 
 class rf_gram_layout_t(C.Structure):
-    _fields_ = [(n, C.c_int64) for n in ("off_n", "off_S_xx", "off_S_yx", "off_s_x", "off_s_y", "total_bytes")]
+    _fields_ = [(n, C.c_int64) for n in ("off_n", "off_S_xx", "off_S_yx", "off_s_x", "off_s_y", "off_s_yy",
+                                          "total_bytes")]
 
 
 class rf_cache_desc(C.Structure):
@@ -92,6 +93,10 @@ _sig = {
                                C.c_int64, C.c_int64, C.c_int64, C.POINTER(rf_cache_desc), C.POINTER(_P),
                                C.POINTER(_P), _P, C.c_int64, _P, C.c_int64, _P]),
     "rf_relative_depth_sources": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int32)]),
+    "rf_fit_r2_workspace_bytes": (C.c_size_t, [C.POINTER(rf_gram_desc), C.c_int32]),
+    "rf_fit_r2": (C.c_int, [C.POINTER(rf_gram_desc), _P, C.c_double, C.c_int, C.POINTER(C.c_int32), C.c_int32, _P, _P,
+                            _P, C.c_size_t, _P]),
+    "rf_r2_assignment": (C.c_int, [C.POINTER(C.c_double), C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int32)]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -288,6 +293,29 @@ def rf_translate(weights: TranslateWeights, src_k: Sequence, src_v: Sequence, ld
     _check(_lib.rf_translate(C.byref(w), n_layers, _ptr_array(src_k), _ptr_array(src_v), ld_src, t0, t1, pos0,
                              C.byref(cache), _ptr_array(k_cache), _ptr_array(v_cache), _ptr(block_table), n_tab,
                              _ptr(rope), rope_len, _stream(stream)))
+
+
+def rf_fit_r2_workspace_bytes(desc: rf_gram_desc, n_sel: int) -> int:
+    return int(_lib.rf_fit_r2_workspace_bytes(C.byref(desc), n_sel))
+
+
+def rf_fit_r2(desc: rf_gram_desc, state, lam: float, mode: int, targets: Sequence[int], W, r2, ws, stream=None):
+    """W: the fp32 maps rf_solve returned for ``targets``; r2: [n_sel] fp64 device output."""
+    tg = (C.c_int32 * max(1, len(targets)))(*targets)
+    ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.rf_fit_r2(C.byref(desc), _ptr(state), float(lam), int(mode), tg, len(targets), _ptr(W), _ptr(r2),
+                          _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def rf_r2_assignment(r2_rows: Sequence[Sequence[float]], nu: int) -> list:
+    """r2_rows[l][s]: score of source s for target l (host values).  Returns the nu chosen
+    source layers of each target, ascending (host only)."""
+    n_tgt = len(r2_rows)
+    n_src = len(r2_rows[0]) if n_tgt else 0
+    flat = (C.c_double * max(1, n_tgt * n_src))(*[float(v) for row in r2_rows for v in row])
+    out = (C.c_int32 * max(1, n_tgt * nu))()
+    _check(_lib.rf_r2_assignment(flat, n_tgt, n_src, nu, out))
+    return [[out[l * nu + j] for j in range(nu)] for l in range(n_tgt)]
 
 
 def rf_relative_depth_sources(n_src: int, n_tgt: int, nu: int) -> list:

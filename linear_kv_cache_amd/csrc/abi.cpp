@@ -1,8 +1,10 @@
 // Host-only parts of the C ABI: error reporting, version, KV-cache layout arithmetic.
+#include <math.h>
 #include <stdio.h>
 
 #include <algorithm>
 #include <string>
+#include <vector>
 
 #include "rf_internal.h"
 
@@ -58,6 +60,24 @@ rf_status rf_cache_layout(const rf_cache_desc* desc, rf_cache_layout_t* out) {
         return rf::fail(RF_ERR_INVALID_ARG, "rf_cache_layout: bad layout");
     }
     *out = L;
+    return RF_OK;
+}
+
+rf_status rf_r2_assignment(const double* r2, int32_t n_tgt, int32_t n_src, int32_t nu, int32_t* out) {
+    rf::clear_error();
+    RF_REQUIRE(r2 && out, RF_ERR_INVALID_ARG, "rf_r2_assignment: null argument");
+    RF_REQUIRE(n_tgt >= 0 && nu >= 1 && nu <= n_src, RF_ERR_INVALID_ARG,
+               "rf_r2_assignment: need n_tgt >= 0 and 1 <= nu <= n_src");
+    std::vector<int32_t> idx(n_src);
+    for (int64_t l = 0; l < n_tgt; ++l) {
+        const double* row = r2 + l * n_src;
+        for (int32_t s = 0; s < n_src; ++s) idx[s] = s;
+        // highest score first (NaN ranks last); equal scores keep the shallower layer first
+        auto key = [&](int32_t s) { return std::isnan(row[s]) ? -INFINITY : row[s]; };
+        std::stable_sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) { return key(a) > key(b); });
+        std::sort(idx.begin(), idx.begin() + nu);
+        for (int32_t j = 0; j < nu; ++j) out[l * nu + j] = idx[j];
+    }
     return RF_OK;
 }
 

@@ -10,7 +10,10 @@
 //                      operand form), in an XCD-aware order; each tile adds its fp32 result
 //                      into the state (one owner per element).
 // fp32 chunks (small widths) run one launch of the plain tile loop, which transposes 4 x 4
-// blocks on their way to LDS and sums the columns on the operand already in registers.
+// blocks on their way to LDS and sums the columns on the operand already in registers, and a
+// small pass for the targets' column sums of squares.
+// The column sums of squares of every Y_l (fp64) let the fit's R^2 be read off the state
+// (rf_fit_r2) without another pass over the data.
 #include "rf_internal.h"
 #include "rf_mfma.h"
 #include "rf_pipe.h"
@@ -38,7 +41,7 @@ struct GramArgs {
 };
 
 struct GramLayout {
-    size_t off_n, off_Sxx, off_Syx, off_sx, off_sy, total;
+    size_t off_n, off_Sxx, off_Syx, off_sx, off_sy, off_syy, total;
 };
 
 static GramLayout gram_layout(int64_t d, int64_t nt, int64_t dy) {
@@ -48,7 +51,8 @@ static GramLayout gram_layout(int64_t d, int64_t nt, int64_t dy) {
     L.off_Syx = L.off_Sxx + round_up((size_t)(d * d) * 4, 256);
     L.off_sx = L.off_Syx + round_up((size_t)(nt * dy * d) * 4, 256);
     L.off_sy = L.off_sx + round_up((size_t)d * 8, 256);
-    L.total = L.off_sy + round_up((size_t)(nt * dy) * 8, 256);
+    L.off_syy = L.off_sy + round_up((size_t)(nt * dy) * 8, 256);
+    L.total = L.off_syy + round_up((size_t)(nt * dy) * 8, 256);
     return L;
 }
 
@@ -152,6 +156,7 @@ struct ColsumArgs {
     const void* src[kMaxTargets + 1];   // [rows][ld] per matrix: X, then Y_0 .. Y_{L-1}
     int64_t ld[kMaxTargets + 1];
     double* csum[kMaxTargets + 1];      // column sums to add into: s_x, then s_y + l*dy
+    double* csq[kMaxTargets + 1];       // column sums of squares (null for X): s_yy + l*dy
     int64_t rows;
     int32_t blocks_x;                   // d / 64 work-groups for X
     int32_t blocks_y;                   // dy / 64 work-groups for each Y_l
@@ -168,14 +173,20 @@ __global__ __launch_bounds__(256) void k_gram_colsum(ColsumArgs a) {
     const int t = threadIdx.x, ch = t & 7, rg = t >> 3;
     const int64_t ld = a.ld[g];
     const bf16_t* src = (const bf16_t*)a.src[g] + c0 + ch * 8;
-    double s[8];
+    const bool sq = g > 0;   // targets also carry sums of squares (uniform per work-group)
+    double s[8], s2[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] = 0.0;
+    for (int e = 0; e < 8; ++e) s[e] = s2[e] = 0.0;
     auto add = [&](const u32x4& v) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            s[2 * w] += (double)__uint_as_float(v[w] << 16);
-            s[2 * w + 1] += (double)__uint_as_float(v[w] & 0xffff0000u);
+            const double lo = (double)__uint_as_float(v[w] << 16), hi = (double)__uint_as_float(v[w] & 0xffff0000u);
+            s[2 * w] += lo;
+            s[2 * w + 1] += hi;
+            if (sq) {
+                s2[2 * w] += lo * lo;
+                s2[2 * w + 1] += hi * hi;
+            }
         }
     };
     int64_t r = rg;
@@ -187,15 +198,38 @@ __global__ __launch_bounds__(256) void k_gram_colsum(ColsumArgs a) {
         for (int u = 0; u < 8; ++u) add(v[u]);
     }
     for (; r < a.rows; r += 32) add(*(const u32x4*)(src + r * ld));
-    __shared__ double red[32][64 + 1];
+    __shared__ double red[2][32][64 + 1];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) red[rg][ch * 8 + e] = s[e];
+    for (int e = 0; e < 8; ++e) {
+        red[0][rg][ch * 8 + e] = s[e];
+        red[1][rg][ch * 8 + e] = s2[e];
+    }
     __syncthreads();
     if (t < 64) {
         double x = 0.0;
-        for (int q = 0; q < 32; ++q) x += red[q][t];
+        for (int q = 0; q < 32; ++q) x += red[0][q][t];
         a.csum[g][c0 + t] += x;
+    } else if (t < 128 && sq) {
+        double x = 0.0;
+        for (int q = 0; q < 32; ++q) x += red[1][q][t - 64];
+        a.csq[g][c0 + t - 64] += x;
     }
+}
+
+// fp32 chunks: column sums of squares of every Y_l, one thread per column, rows in order.
+__global__ void k_sqsum_f32(ColsumArgs a) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // over n_targets * dy
+    const int64_t dy = (int64_t)a.blocks_y * 64;
+    const int l = (int)(c / dy);
+    if (l >= a.blocks_x) return;   // blocks_x holds the number of targets here
+    const int64_t o = c - l * dy;
+    const float* src = (const float*)a.src[l + 1] + o;
+    double x = 0.0;
+    for (int64_t r = 0; r < a.rows; ++r) {
+        const double v = (double)src[r * a.ld[l + 1]];
+        x += v * v;
+    }
+    a.csq[l + 1][o] += x;
 }
 
 // ---- bf16: products on the pipelined core ----------------------------------------------------
@@ -310,6 +344,7 @@ rf_status rf_gram_state_layout(const rf_gram_desc* desc, rf_gram_layout_t* out) 
     out->off_S_yx = (int64_t)L.off_Syx;
     out->off_s_x = (int64_t)L.off_sx;
     out->off_s_y = (int64_t)L.off_sy;
+    out->off_s_yy = (int64_t)L.off_syy;
     out->total_bytes = (int64_t)L.total;
     return RF_OK;
 }
@@ -357,6 +392,7 @@ rf_status rf_gram_accumulate(const rf_gram_desc* desc, void* d_state, const void
     float* Syx = (float*)(s + L.off_Syx);
     double* sx = (double*)(s + L.off_sx);
     double* sy = (double*)(s + L.off_sy);
+    double* syy = (double*)(s + L.off_syy);
     int64_t* np = (int64_t*)(s + L.off_n);
     const int tiles_m = desc->d / kGT;
     const int n_xx = tiles_m * (tiles_m + 1) / 2;
@@ -369,7 +405,15 @@ rf_status rf_gram_accumulate(const rf_gram_desc* desc, void* d_state, const void
         a.Sxx = Sxx; a.Syx = Syx; a.sx = sx; a.sy = sy; a.n = np;
         for (int l = 0; l < desc->n_targets; ++l) a.Y[l] = d_Y[l];
         hipLaunchKernelGGL(k_gram<float>, dim3(n_xx + n_yx), dim3(kThreads), 0, strm, a);
-        return check_launch("rf_gram_accumulate");
+        st = check_launch("rf_gram_accumulate");
+        if (st != RF_OK || desc->n_targets == 0) return st;
+        ColsumArgs qa{};
+        for (int l = 0; l < desc->n_targets; ++l) {
+            qa.src[l + 1] = d_Y[l]; qa.ld[l + 1] = ldy; qa.csq[l + 1] = syy + (int64_t)l * dy;
+        }
+        qa.rows = rows; qa.blocks_x = desc->n_targets; qa.blocks_y = (int32_t)(dy / 64);
+        hipLaunchKernelGGL(k_sqsum_f32, dim3((unsigned)ceil_div(desc->n_targets * dy, 256)), dim3(256), 0, strm, qa);
+        return check_launch("rf_gram_accumulate: sums of squares");
     }
 
     // bf16: pieces small enough for 32-bit byte offsets into X and Y (the products address a
@@ -384,6 +428,7 @@ rf_status rf_gram_accumulate(const rf_gram_desc* desc, void* d_state, const void
         ca.src[0] = (const bf16_t*)d_X + r0 * ldx; ca.ld[0] = ldx; ca.csum[0] = sx;
         for (int l = 0; l < desc->n_targets; ++l) {
             ca.src[l + 1] = (const bf16_t*)d_Y[l] + r0 * ldy; ca.ld[l + 1] = ldy; ca.csum[l + 1] = sy + (int64_t)l * dy;
+            ca.csq[l + 1] = syy + (int64_t)l * dy;
         }
         ca.rows = pr; ca.blocks_x = desc->d / 64; ca.blocks_y = (int32_t)(dy / 64);
         hipLaunchKernelGGL(k_gram_colsum, dim3((unsigned)(ca.blocks_x + desc->n_targets * ca.blocks_y)), dim3(256), 0,

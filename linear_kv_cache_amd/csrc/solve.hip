@@ -622,11 +622,138 @@ static rf_status inverse_factor(hipStream_t s, const SolveWs& w, int64_t d, doub
     return RF_OK;
 }
 
+// ---- fit quality ------------------------------------------------------------------------
+constexpr int kR2Rows = 16;   // map rows per work-group
+
+// Per (target, block of kR2Rows rows): fp64 partial sums of W[o][i] * B[o][i] and W[o][i]^2 with
+// B = S_yx - s_y s_x^T / n, each thread over a fixed set of elements, then a fixed-order tree.
+__global__ __launch_bounds__(256) void k_r2_partial(const float* Syx, const double* sy, const double* sx,
+                                                     const int64_t* np, const float* W, int64_t d, int64_t dy,
+                                                     CrossArgs ca, int n_blk, double* part) {
+    const int l = blockIdx.y, blk = blockIdx.x;
+    const double inv_n = 1.0 / (double)*np;
+    double dot = 0.0, ww = 0.0;
+    for (int r = 0; r < kR2Rows; ++r) {
+        const int64_t o = (int64_t)blk * kR2Rows + r;
+        if (o >= dy) break;
+        const int64_t srow = (int64_t)ca.tsel[l] * dy + o;
+        const float* wrow = W + ((int64_t)l * dy + o) * d;
+        const float* brow = Syx + srow * d;
+        const double syv = sy[srow] * inv_n;
+        for (int64_t i = threadIdx.x * 4; i < d; i += 1024) {
+            const f32x4 w = *(const f32x4*)(wrow + i);
+            const f32x4 b = *(const f32x4*)(brow + i);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const double wd = (double)w[e];
+                dot += wd * ((double)b[e] - syv * sx[i + e]);
+                ww += wd * wd;
+            }
+        }
+    }
+    __shared__ double red[2][256];
+    red[0][threadIdx.x] = dot;
+    red[1][threadIdx.x] = ww;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if (threadIdx.x < h) {
+            red[0][threadIdx.x] += red[0][threadIdx.x + h];
+            red[1][threadIdx.x] += red[1][threadIdx.x + h];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        part[((int64_t)l * n_blk + blk) * 2] = red[0][0];
+        part[((int64_t)l * n_blk + blk) * 2 + 1] = red[1][0];
+    }
+}
+
+// One work-group per target: the partials in block order, SST from the column sums, the
+// absolute ridge strength, and R^2.
+__global__ __launch_bounds__(256) void k_r2_final(const float* Sxx, const double* sx, const double* sy,
+                                                   const double* syy, const int64_t* np, int64_t d, int64_t dy,
+                                                   CrossArgs ca, int n_blk, const double* part, double lambda,
+                                                   int rel, double* r2) {
+    const int l = blockIdx.x;
+    const double n = (double)*np;
+    __shared__ double red[3][256];
+    double sst = 0.0, diag = 0.0;
+    for (int64_t o = threadIdx.x; o < dy; o += 256) {
+        const int64_t srow = (int64_t)ca.tsel[l] * dy + o;
+        sst += syy[srow] - sy[srow] * sy[srow] / n;
+    }
+    if (rel)
+        for (int64_t i = threadIdx.x; i < d; i += 256) diag += (double)Sxx[i * d + i] - sx[i] * sx[i] / n;
+    red[0][threadIdx.x] = sst;
+    red[1][threadIdx.x] = diag;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if (threadIdx.x < h) {
+            red[0][threadIdx.x] += red[0][threadIdx.x + h];
+            red[1][threadIdx.x] += red[1][threadIdx.x + h];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        double dot = 0.0, ww = 0.0;
+        for (int b = 0; b < n_blk; ++b) {
+            dot += part[((int64_t)l * n_blk + b) * 2];
+            ww += part[((int64_t)l * n_blk + b) * 2 + 1];
+        }
+        const double lam = rel ? lambda * red[1][0] / (double)d : lambda;
+        r2[l] = (dot + lam * ww) / red[0][0];
+    }
+}
+
 }  // namespace rf
 
 using namespace rf;
 
 extern "C" {
+
+size_t rf_fit_r2_workspace_bytes(const rf_gram_desc* desc, int32_t n_sel) {
+    rf_gram_layout_t GL;
+    if (n_sel < 0 || rf_gram_state_layout(desc, &GL) != RF_OK) return 0;
+    return round_up((size_t)n_sel * (size_t)ceil_div(gram_dy(desc), kR2Rows) * 2 * sizeof(double), 256);
+}
+
+rf_status rf_fit_r2(const rf_gram_desc* desc, const void* d_state, double lambda, rf_lambda_mode mode,
+                    const int32_t* targets, int32_t n_sel, const float* d_W, double* d_r2, void* d_ws,
+                    size_t ws_bytes, void* stream) {
+    clear_error();
+    rf_gram_layout_t GL;
+    rf_status st = rf_gram_state_layout(desc, &GL);
+    if (st != RF_OK) return st;
+    RF_REQUIRE(d_state && aligned(d_state, 256), RF_ERR_INVALID_ARG, "rf_fit_r2: state must be non-null, 256-B aligned");
+    RF_REQUIRE(isfinite(lambda) && lambda >= 0.0, RF_ERR_INVALID_ARG, "rf_fit_r2: lambda must be finite and >= 0");
+    RF_REQUIRE(mode == RF_LAMBDA_ABSOLUTE || mode == RF_LAMBDA_REL_MEAN_DIAG, RF_ERR_INVALID_ARG,
+               "rf_fit_r2: bad lambda mode");
+    RF_REQUIRE(n_sel >= 0 && n_sel <= kMaxSel, RF_ERR_UNSUPPORTED, "rf_fit_r2: 0..64 selected targets");
+    if (n_sel == 0) return RF_OK;
+    RF_REQUIRE(targets && d_W && d_r2, RF_ERR_INVALID_ARG, "rf_fit_r2: null pointer argument");
+    for (int i = 0; i < n_sel; ++i)
+        RF_REQUIRE(targets[i] >= 0 && targets[i] < desc->n_targets, RF_ERR_INVALID_ARG,
+                   "rf_fit_r2: target index out of range");
+    RF_REQUIRE(aligned(d_W, 16) && aligned(d_r2, 8), RF_ERR_INVALID_ARG, "rf_fit_r2: W must be 16-byte aligned");
+    RF_REQUIRE(d_ws && aligned(d_ws, 256), RF_ERR_INVALID_ARG, "rf_fit_r2: workspace must be non-null, 256-B aligned");
+    RF_REQUIRE(ws_bytes >= rf_fit_r2_workspace_bytes(desc, n_sel), RF_ERR_WORKSPACE, "rf_fit_r2: workspace too small");
+    const int64_t d = desc->d, dy = gram_dy(desc);
+    const char* sp = (const char*)d_state;
+    CrossArgs ca{};
+    for (int i = 0; i < n_sel; ++i) ca.tsel[i] = targets[i];
+    const int n_blk = (int)ceil_div(dy, kR2Rows);
+    hipStream_t s = (hipStream_t)stream;
+    hipLaunchKernelGGL(k_r2_partial, dim3((unsigned)n_blk, (unsigned)n_sel), dim3(256), 0, s,
+                       (const float*)(sp + GL.off_S_yx), (const double*)(sp + GL.off_s_y),
+                       (const double*)(sp + GL.off_s_x), (const int64_t*)(sp + GL.off_n), d_W, d, dy, ca, n_blk,
+                       (double*)d_ws);
+    RF_TRY(check_launch("rf_fit_r2: partial sums"));
+    hipLaunchKernelGGL(k_r2_final, dim3((unsigned)n_sel), dim3(256), 0, s, (const float*)(sp + GL.off_S_xx),
+                       (const double*)(sp + GL.off_s_x), (const double*)(sp + GL.off_s_y),
+                       (const double*)(sp + GL.off_s_yy), (const int64_t*)(sp + GL.off_n), d, dy, ca, n_blk,
+                       (const double*)d_ws, lambda, (int)(mode == RF_LAMBDA_REL_MEAN_DIAG), d_r2);
+    return check_launch("rf_fit_r2: scores");
+}
 
 size_t rf_solve_workspace_bytes(const rf_gram_desc* desc, int32_t n_sel) {
     rf_gram_layout_t GL;

@@ -8,7 +8,8 @@ from typing import List, Optional, Sequence
 import torch
 
 from . import (RF_LAYOUT_CONTIGUOUS, RF_LAYOUT_PAGED, FillWeights, TranslateWeights, cache_desc, gram_desc,
-               rf_cache_layout, rf_fill, rf_fill_workspace_bytes, rf_gram_accumulate, rf_gram_init,
+               rf_cache_layout, rf_fill, rf_fill_workspace_bytes, rf_fit_r2, rf_fit_r2_workspace_bytes,
+               rf_gram_accumulate, rf_gram_init,
                rf_gram_state_bytes, rf_gram_state_layout, rf_pack_weights, rf_rope_table, rf_solve,
                rf_solve_workspace_bytes, rf_translate)
 
@@ -54,6 +55,18 @@ class GramState:
 
     def s_y(self):
         return self._view(self.layout["off_s_y"], self.n_targets * self.dy, torch.float64).view(self.n_targets, self.dy)
+
+    def s_yy(self):
+        return self._view(self.layout["off_s_yy"], self.n_targets * self.dy,
+                          torch.float64).view(self.n_targets, self.dy)
+
+    def r2(self, lam: float, mode: int, targets: Sequence[int], W, stream=None) -> torch.Tensor:
+        """R^2 of the maps W (rf_solve's fp32 output for ``targets``), read off the state."""
+        dev = self.buf.device
+        out = torch.empty(len(targets), dtype=torch.float64, device=dev)
+        ws = device_bytes(rf_fit_r2_workspace_bytes(self.desc, len(targets)), dev)
+        rf_fit_r2(self.desc, self.buf, lam, mode, list(targets), W, out, ws, stream)
+        return out
 
     def solve(self, lam: float, mode: int, targets: Sequence[int], want_f32=True, want_bf16=True, stream=None,
               ws: Optional[torch.Tensor] = None):

@@ -14,6 +14,8 @@ the band of nu consecutive source layers centred on c(l) = 1 + (l - 1)(N_src - 1
 shifted at the boundaries so every band has nu layers.
 Section 3.2, first training stage: the maps are fitted in closed form by minimising the
 squared error, i.e. the ridge fit of ``oracle.ridge`` on (source rows, target rows).
+Appendix "The R^2 assignment": each target layer reads the nu source layers whose
+single-layer maps explain the largest fraction of its features (keys and values ranked apart).
 
 Readings (where the page is silent):
   * nu source layers enter one map as the concatenation of their rows, so the map of a
@@ -119,3 +121,35 @@ def fit_translator(src_rows, tgt_rows, lam: float, mode: str = "absolute"):
     """First-stage closed-form translator: the ridge fit of the target rows [n, d_out] on the
     source rows [n, d_in] (mean-centred, intercept b).  Returns (T [d_in, d_out], b)."""
     return fit(src_rows, tgt_rows, lam, mode)
+
+
+def fit_r2(src_rows, tgt_rows, lam: float, mode: str = "absolute") -> float:
+    """R^2 of the closed-form map from one source layer's rows to one target layer's rows
+    (KV-Lingo page, Appendix "The R^2 assignment": the fraction of the target layer's features
+    explained by the map from source layer s alone, R^2 = 1 - r({s})).
+
+    Written from its definition on the data: the ridge map with its intercept is fitted, the
+    residual of every target feature is formed, and
+        R^2 = 1 - ||Y - (X W + 1 b)||_F^2 / ||Y - 1 mean(Y)||_F^2."""
+    X = _f64(src_rows)
+    Y = _f64(tgt_rows)
+    W, b = fit(X, Y, lam, mode)
+    R = Y - (X @ W + b)
+    Yc = Y - Y.mean(axis=0)
+    return 1.0 - float(np.sum(R * R)) / float(np.sum(Yc * Yc))
+
+
+def r2_assignment(r2, nu: int):
+    """E_l for every target layer from a score matrix r2 [n_tgt][n_src]: the nu source layers
+    with the highest R^2_l(s) (KV-Lingo page, Appendix "The R^2 assignment"), in ascending
+    layer order.  Readings: equal scores go to the shallower source layer; NaN ranks last."""
+    r2 = _f64(r2)
+    n_tgt, n_src = r2.shape
+    if not 1 <= nu <= n_src:
+        raise ValueError("need 1 <= nu <= n_src")
+    out = []
+    for l in range(n_tgt):
+        score = [(-np.inf if np.isnan(r2[l, s]) else r2[l, s]) for s in range(n_src)]
+        order = sorted(range(n_src), key=lambda s: (-score[s], s))
+        out.append(sorted(order[:nu]))
+    return out

@@ -16,7 +16,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(rf_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(rf_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -58,7 +58,8 @@ def test_gram_state_layout():
     assert L["off_S_yx"] == 256 + 4096 * 4096 * 4
     assert L["off_s_x"] == L["off_S_yx"] + 16 * 4096 * 4096 * 4
     assert L["off_s_y"] == L["off_s_x"] + 4096 * 8
-    assert L["total_bytes"] == L["off_s_y"] + 16 * 4096 * 8
+    assert L["off_s_yy"] == L["off_s_y"] + 16 * 4096 * 8
+    assert L["total_bytes"] == L["off_s_yy"] + 16 * 4096 * 8
     assert all(v % 256 == 0 for v in L.values())
     assert rf.rf_gram_state_bytes(desc) == L["total_bytes"]
     assert rf.rf_gram_state_bytes(rf.gram_desc(100, 2, torch.float32)) == 0
@@ -71,7 +72,8 @@ def test_gram_state_layout_rectangular_maps():
     L = rf.rf_gram_state_layout(desc)
     assert L["off_S_yx"] == 256 + 2048 * 2048 * 4
     assert L["off_s_x"] == L["off_S_yx"] + 3 * 1024 * 2048 * 4
-    assert L["total_bytes"] == L["off_s_y"] + 3 * 1024 * 8
+    assert L["off_s_yy"] == L["off_s_y"] + 3 * 1024 * 8
+    assert L["total_bytes"] == L["off_s_yy"] + 3 * 1024 * 8
     assert rf.rf_gram_state_layout(rf.gram_desc(512, 2, torch.float32, d_out=512)) == \
         rf.rf_gram_state_layout(rf.gram_desc(512, 2, torch.float32))
     for d_out, status in ((300, rf.RF_ERR_UNSUPPORTED), (-256, rf.RF_ERR_INVALID_ARG)):
@@ -248,3 +250,35 @@ def test_translate_validation_before_enqueue():
         assert e.value.status == status, kw
     call(t0=7, t1=7)          # empty range: nothing to do
     call(n_layers=0)          # no layers: nothing to do
+
+
+def test_r2_assignment_matches_the_oracle():
+    # host ranking, compared exactly with the oracle's (ties and NaN included)
+    import numpy as np
+    import oracle
+    g = np.random.default_rng(0)
+    cases = [np.array([[0.1, 0.9, 0.5, 0.9], [0.8, 0.2, 0.8, 0.3], [0.0, 0.0, 0.0, 0.0]]),
+             np.array([[np.nan, 0.5, 0.4], [0.3, np.nan, np.nan]]),
+             g.random((36, 28)), np.round(g.random((12, 9)), 1)]
+    for r2 in cases:
+        for nu in range(1, r2.shape[1] + 1):
+            assert rf.rf_r2_assignment(r2.tolist(), nu) == oracle.r2_assignment(r2, nu), (r2.shape, nu)
+    with pytest.raises(rf.RidgeFillError) as e:
+        rf.rf_r2_assignment([[0.5, 0.2]], 3)
+    assert e.value.status == rf.RF_ERR_INVALID_ARG
+
+
+def test_fit_r2_validation_before_enqueue():
+    desc = rf.gram_desc(256, 2, torch.float32)
+    assert rf.rf_fit_r2_workspace_bytes(desc, 2) >= 2 * (256 // 16) * 2 * 8
+    ws = _aligned_bytes(1 << 16)
+    r2 = _aligned_bytes(64)
+    for lam, targets, status in [(-1.0, [0], rf.RF_ERR_INVALID_ARG), (0.1, [2], rf.RF_ERR_INVALID_ARG),
+                                 (0.1, [0] * 65, rf.RF_ERR_UNSUPPORTED)]:
+        with pytest.raises(rf.RidgeFillError) as e:
+            rf.rf_fit_r2(desc, 256, lam, 0, targets, 256, r2, ws, stream=0)
+        assert e.value.status == status, (lam, targets)
+    with pytest.raises(rf.RidgeFillError) as e:
+        rf.rf_fit_r2(desc, 256, 0.1, 0, [0], 256, r2, _aligned_bytes(128), stream=0)
+    assert e.value.status == rf.RF_ERR_WORKSPACE
+    rf.rf_fit_r2(desc, 256, 0.1, 0, [], 256, r2, ws, stream=0)   # nothing selected: nothing to do

@@ -194,3 +194,39 @@ def test_fit_rectangular_maps():
             from linear_kv_cache_amd.runner import pack_weights
             for l in range(nt):
                 assert torch.equal(Wlp[l].view(torch.int16), pack_weights(W[l].to(torch.bfloat16)).view(torch.int16))
+
+
+R2_TOL = 1e-4   # absolute, on R^2 in [0, 1]: fp32 sums and maps against fp64 on the data
+
+
+def test_fit_r2_read_off_the_state():
+    # targets explained to different degrees (noise 0.3, 1 and 3 times the signal scale), bf16
+    # rectangular and fp32 square; absolute and relative lambda; R^2 against the oracle's
+    # definition on the data, and the column sums of squares against fp64 sums
+    from linear_kv_cache_amd.runner import GramState
+    for d, m, dtype, rows, chunks in [(512, 256, torch.bfloat16, 3000, [1000, 2000]),
+                                      (256, 256, torch.float32, 2048, [2048])]:
+        g = synth.generator(21, "r2", d, m)
+        X = torch.randn(rows, d, generator=g) * (1 + torch.rand(d, generator=g))
+        Ys = [X @ (torch.randn(d, m, generator=g) / d ** 0.5) + s * torch.randn(rows, m, generator=g)
+              for s in (0.3, 1.0, 3.0)]
+        X = X.to(dtype)
+        Ys = [Y.to(dtype) for Y in Ys]
+        st = GramState(d, 3, dtype, "cuda", d_out=m)
+        r0 = 0
+        for c in chunks:
+            st.accumulate(X[r0:r0 + c].cuda(), [Y[r0:r0 + c].cuda() for Y in Ys])
+            r0 += c
+        syy = f64(st.s_yy())
+        for l, Y in enumerate(Ys):
+            ref = np.sum(f64(Y) ** 2, axis=0)
+            assert float(np.max(np.abs(syy[l] - ref) / ref)) <= 1e-12
+        for lam, mode, mname in [(0.1, 0, "absolute"), (1e-2, 1, "rel_mean_diag")]:
+            W, _, _, info = st.solve(lam, mode, [0, 1, 2], want_bf16=False)
+            r2 = f64(st.r2(lam, mode, [0, 1, 2], W))
+            torch.cuda.synchronize()
+            ref = [oracle.fit_r2(f64(X), f64(Y), lam, mname) for Y in Ys]
+            log(f"[fit] R^2 d={d} m={m} {dtype} {mname}: gpu={np.round(r2, 6)} oracle={np.round(ref, 6)}")
+            assert int(info.item()) == 0
+            assert float(np.max(np.abs(r2 - np.array(ref)))) <= R2_TOL
+            assert ref[0] > ref[1] > ref[2]

@@ -137,3 +137,39 @@ def test_translator_fit_then_translate():
         ve = float(np.max(np.abs(V - V_ref)) / np.sqrt(np.mean(V_ref ** 2)))
         log(f"[translate] fitted layer {l}: k_err={ke:.3e} v_err={ve:.3e}")
         assert ke <= KV_TOL_BF16 and ve <= KV_TOL_BF16
+
+
+def test_r2_assignment_from_gpu_scores():
+    # KV-Lingo's R^2 assignment: each target layer keeps the nu source layers whose single-layer
+    # maps explain most of it, keys and values ranked apart.  Target rows are built from the
+    # source layers with distinct weights, so the scores are well separated; one Gram per
+    # source layer regresses every target layer on it (the scores come off those states).
+    import linear_kv_cache_amd as rf
+    from linear_kv_cache_amd.runner import GramState
+    n_src, n_tgt, d, N, lam = 4, 3, 256, 3000, 0.1
+    g = synth.generator(31, "r2-assign")
+    src = {side: [torch.randn(N, d, generator=g) for _ in range(n_src)] for side in ("k", "v")}
+    weights = {"k": [[1.0, 0.6, 0.2, 0.0], [0.0, 0.3, 1.0, 0.5], [0.2, 0.0, 0.4, 1.0]],
+               "v": [[0.1, 1.0, 0.0, 0.5], [1.0, 0.0, 0.6, 0.2], [0.0, 0.5, 0.2, 1.0]]}
+    for side in ("k", "v"):
+        S = [x.to(torch.bfloat16) for x in src[side]]
+        tgts = []
+        for l in range(n_tgt):
+            y = 0.5 * torch.randn(N, d, generator=g)
+            for s in range(n_src):
+                y += weights[side][l][s] * (src[side][s] @ (torch.randn(d, d, generator=g) / d ** 0.5))
+            tgts.append(y.to(torch.bfloat16))
+        gpu = np.zeros((n_tgt, n_src))
+        ref = np.zeros((n_tgt, n_src))
+        for s in range(n_src):
+            st = GramState(d, n_tgt, torch.bfloat16, "cuda")
+            st.accumulate(S[s].cuda(), [y.cuda() for y in tgts])
+            W, _, _, info = st.solve(lam, 0, list(range(n_tgt)), want_bf16=False)
+            gpu[:, s] = f64(st.r2(lam, 0, list(range(n_tgt)), W))
+            for l in range(n_tgt):
+                ref[l, s] = oracle.fit_r2(f64(S[s]), f64(tgts[l]), lam)
+        log(f"[translate] R^2 scores ({side}) gpu=\n{np.round(gpu, 5)}\noracle=\n{np.round(ref, 5)}")
+        assert float(np.max(np.abs(gpu - ref))) <= 1e-4
+        for nu in (1, 2, 3):
+            E = rf.rf_r2_assignment(gpu.tolist(), nu)
+            assert E == oracle.r2_assignment(ref, nu), (side, nu, E)

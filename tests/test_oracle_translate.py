@@ -183,3 +183,56 @@ def test_fit_translator_recovers_a_planted_map():
     for g in range(H):
         Tg, bg = oracle.fit_translator(src[:, g * dh:(g + 1) * dh], tgt_h[:, g * dh:(g + 1) * dh], 1e-10)
         assert np.allclose(Tg, blocks[g], rtol=0, atol=1e-8) and np.allclose(bg, 0, atol=1e-8)
+
+
+# ---- R^2 of single-layer maps and the R^2 assignment ----------------------------------------
+
+def test_r2_one_feature_is_squared_correlation():
+    # textbook identity: for one source feature and one target feature, the least-squares fit
+    # with an intercept explains corr(x, y)^2 of the target's variance
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((500, 1))
+    y = 0.7 * x + rng.standard_normal((500, 1))
+    rho = np.corrcoef(x[:, 0], y[:, 0])[0, 1]
+    assert abs(oracle.fit_r2(x, y, 0.0) - rho ** 2) <= 1e-12
+
+
+def test_r2_limits_and_monotone_in_lambda():
+    rng = np.random.default_rng(11)
+    X = rng.standard_normal((400, 12)) + 1.5
+    A = rng.standard_normal((12, 6))
+    assert abs(oracle.fit_r2(X, X @ A + 3.0, 1e-10) - 1.0) <= 1e-10       # exact affine map
+    E = rng.standard_normal((400, 6))
+    vals = [oracle.fit_r2(X, X @ A + E, lam) for lam in (0.0, 1.0, 100.0, 1e4, 1e8)]
+    assert all(0.0 <= v <= 1.0 for v in vals)
+    assert all(a > b for a, b in zip(vals, vals[1:]))                     # more shrinkage, less fit
+    assert vals[-1] < 1e-3                                                # lambda -> inf: W -> 0
+    # a target independent of the source: R^2 near 0 (expected d / n for least squares)
+    r0 = oracle.fit_r2(X, rng.standard_normal((400, 6)), 0.0)
+    assert 0.0 <= r0 < 0.1
+
+
+def test_r2_from_the_sums_equals_the_data_route():
+    # the scores can be read off the accumulated sums (the page: no extra pass over the data):
+    # SSE = SST - sum(W * B) - lambda ||W||^2 with B the centred cross moments
+    rng = np.random.default_rng(12)
+    X = rng.standard_normal((300, 10)) * np.linspace(0.5, 2, 10) + 0.3
+    Y = X @ rng.standard_normal((10, 7)) + 0.5 * rng.standard_normal((300, 7)) - 1.0
+    lam = 5.0
+    S_xx, S_xy, s_x, s_y, n = oracle.gram_sums(X, [Y])
+    (W, b), = oracle.fit_from_sums(S_xx, S_xy, s_x, s_y, n, lam)
+    B = S_xy[0] - np.outer(s_x, s_y[0]) / n
+    SST = float(np.sum(Y * Y) - np.sum(s_y[0] ** 2) / n)
+    r2_sums = (float(np.sum(W * B)) + lam * float(np.sum(W * W))) / SST
+    assert abs(r2_sums - oracle.fit_r2(X, Y, lam)) <= 1e-12
+
+
+def test_r2_assignment_hand_worked():
+    r2 = np.array([[0.1, 0.9, 0.5, 0.9],     # tie 0.9 at sources 1 and 3: both kept for nu = 2
+                   [0.8, 0.2, 0.8, 0.3],     # tie at 0 and 2 for nu = 1: the shallower, 0
+                   [0.0, 0.0, 0.0, 0.0]])
+    assert oracle.r2_assignment(r2, 1) == [[1], [0], [0]]
+    assert oracle.r2_assignment(r2, 2) == [[1, 3], [0, 2], [0, 1]]
+    assert oracle.r2_assignment(r2, 4) == [[0, 1, 2, 3]] * 3
+    with pytest.raises(ValueError):
+        oracle.r2_assignment(r2, 5)
