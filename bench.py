@@ -100,7 +100,7 @@ def cpu_baseline(cfg, n_tokens: int, n_fit_rows: int):
     }
 
 
-def translate_leg(steps: int, stream, dev):
+def translate_leg(steps: int, stream, dev, tc=None):
     """Time rf_translate over every target layer of the translation workload, in one call."""
     import torch
 
@@ -108,14 +108,14 @@ def translate_leg(steps: int, stream, dev):
     import synth
     from linear_kv_cache_amd.runner import Translator, alloc_cache, translate_weights
 
-    tc = synth.TR_BENCH
+    tc = tc or synth.TR_BENCH
     T = tc.t1 - tc.t0
     log(f"translate workload {tc.name}: {tc.n_src} -> {tc.n_tgt} layers, nu={tc.nu}, T={T}")
     E = rf.rf_relative_depth_sources(tc.n_src, tc.n_tgt, tc.nu)
     Ks, Vs = synth.source_cache(tc, T, device=dev)
     maps = [synth.translator_maps(tc, l, device=dev) for l in range(tc.n_tgt)]
     tw = translate_weights(tc.d_in, tc.n_kv_heads, tc.head_dim, tc.torch_dtype, [m[0] for m in maps],
-                           [m[1] for m in maps])
+                           [m[1] for m in maps], headwise=tc.maps == "headwise")
     del maps
     cache = alloc_cache(tc.n_tgt, tc.n_kv_heads, tc.head_dim, T, tc.torch_dtype, dev)
     tr = Translator(tw, tc.rope_base, T, dev)
@@ -344,6 +344,9 @@ def main():
     if not args.no_translate:
         del Xc, Yc
         out["translate"] = translate_leg(args.steps, stream, dev)
+        out["translate_headwise"] = translate_leg(args.steps, stream, dev,
+                                                  synth.scaled(synth.TR_BENCH, maps="headwise",
+                                                               name=synth.TR_BENCH.name + "-headwise"))
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on {args.cpu_tokens} tokens and {args.cpu_fit_rows} calibration rows")
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens, args.cpu_fit_rows)

@@ -301,8 +301,11 @@ rf_status rf_fill(const rf_fill_weights* weights, int32_t n_layers,
  * nu source layers side by side, d_in = nu * d_src wide.  A source cache kept as
  * [token][source layer][d_src] hands over a band of consecutive source layers (the bands of
  * rf_relative_depth_sources) as one row segment, with ld_src = n_src_layers * d_src.
- * Head-mixing maps are dense; a head-wise map (block-diagonal: target head g reads only
- * source head g) is passed dense, zero blocks included, and computed as such.  The maps'
+ * Head-mixing maps are dense (headwise = 0).  A head-wise map (block-diagonal: target head g
+ * reads only head g of each source layer, so the source heads match the target's and
+ * d_in = nu * n_kv_heads * head_dim) is passed dense, zero blocks included; with headwise = 1
+ * the BF16 product reads only the 256 x 256 blocks that hold a head's block (the entries
+ * outside the head blocks must be zero: they are not all read), the F32 product reads all.  The maps'
  * closed-form first stage (KV-Lingo page, section 3.2) is a ridge fit of target rows on
  * source rows: rf_gram_accumulate and rf_solve with X = source rows, one target of the
  * same width; rf_pack_weights packs the solve's fp32 maps (rope_head_dim = head_dim).
@@ -329,6 +332,7 @@ typedef struct {
     const void* const* T_v;
     const float* const* b_k;
     const float* const* b_v;
+    int32_t headwise;          /* 1: block-diagonal maps (see above); 0: dense maps */
 } rf_translate_weights;
 
 rf_status rf_translate(const rf_translate_weights* weights, int32_t n_layers,

@@ -67,7 +67,7 @@ class rf_fill_weights(C.Structure):
 class rf_translate_weights(C.Structure):
     _fields_ = [("d_in", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("dtype", C.c_int),
                 ("T_k", C.POINTER(C.c_void_p)), ("T_v", C.POINTER(C.c_void_p)), ("b_k", C.POINTER(C.c_void_p)),
-                ("b_v", C.POINTER(C.c_void_p))]
+                ("b_v", C.POINTER(C.c_void_p)), ("headwise", C.c_int32)]
 
 
 _P = C.c_void_p
@@ -263,7 +263,8 @@ class TranslateWeights:
     """Per-target-layer translator maps of one rf_translate call (tensors on the device).
 
     T_k, T_v: [n_kv_heads*head_dim, d_in] out-feature major; BF16 maps packed by
-    rf_pack_weights(rope_head_dim=head_dim).  b_k, b_v: lists of fp32 intercepts, or None."""
+    rf_pack_weights(rope_head_dim=head_dim).  b_k, b_v: lists of fp32 intercepts, or None.
+    headwise: the maps are block-diagonal by head (only the head blocks are read)."""
 
     d_in: int
     n_kv_heads: int
@@ -273,13 +274,14 @@ class TranslateWeights:
     T_v: list
     b_k: Optional[list] = None
     b_v: Optional[list] = None
+    headwise: bool = False
 
     def _c(self):
         arrs = [_ptr_array(x) for x in (self.T_k, self.T_v)]
         barrs = [None if x is None else _ptr_array(x) for x in (self.b_k, self.b_v)]
         cast = lambda a: C.cast(a, C.POINTER(_P)) if a is not None else C.POINTER(_P)()
         w = rf_translate_weights(self.d_in, self.n_kv_heads, self.head_dim, _dtype_code(self.dtype),
-                                 cast(arrs[0]), cast(arrs[1]), cast(barrs[0]), cast(barrs[1]))
+                                 cast(arrs[0]), cast(arrs[1]), cast(barrs[0]), cast(barrs[1]), int(self.headwise))
         return w, (arrs, barrs)
 
 

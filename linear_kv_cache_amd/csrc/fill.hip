@@ -206,10 +206,13 @@ __global__ __launch_bounds__(MapCore<T>::G::kThr) void k_fill_map(MapArgs a) {
 }
 
 // NORM: the fill (rows scaled by 1/rms from the map's partial sums).  Otherwise the product
-// of a translator (KV-Lingo page, section 3.1): no row scale, an intercept when BIAS.
-template <typename T, int DH, bool NORM, bool BIAS>
+// of a translator (KV-Lingo page, section 3.1): no row scale, an intercept when BIAS.  HW
+// (bf16): head-wise maps, block-diagonal by head, so a 256-feature tile reads only its own
+// 256-column block of each source layer (d = nu * kvw; the other blocks are zero).
+template <typename T, int DH, bool NORM, bool BIAS, bool HW = false>
 __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
     using G = typename KVCore<T>::G;
+    static_assert(!HW || (sizeof(T) == 2 && !NORM), "head-wise products are bf16 translators");
     static_assert(sizeof(T) == 2 || G::WTM % DH == 0, "fp32: a wave's feature extent must hold whole heads");
     static_assert(sizeof(T) == 4 || G::SM == 2, "bf16: the two blocks of a wave hold the RoPE partners");
     constexpr int HALF = DH / 2;
@@ -223,9 +226,16 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
     const bool is_k = (int64_t)mt * kFT < a.kvw;
     const int f0 = is_k ? mt * kFT : mt * kFT - a.kvw;
     const T* Wsel = (const T*)(is_k ? a.Wk[g] : a.Wv[g]) + (int64_t)f0 * a.d;
+    const T* Bsel = (const T*)(is_k ? a.in_k[g] : a.in_v[g]) + n0 * a.ld_in;
     G gm;
-    fill_gemm(gm, lds, Wsel, a.d, kFT, (const T*)(is_k ? a.in_k[g] : a.in_v[g]) + n0 * a.ld_in, a.ld_in, a.rows - n0,
-              a.d / G::BK);
+    if constexpr (HW) {
+        // segments of 4 k-steps (the tile's 256 source columns), one per source layer
+        gm.template run<false, true>(lds, PipeOperand{Wsel + (int64_t)(f0 / G::BK) * (G::kStepBytes / 2), a.d, kFT},
+                                     PipeOperand{Bsel + f0, a.ld_in, a.rows - n0}, 4 * (a.d / a.kvw), 0,
+                                     a.kvw / G::BK);
+    } else {
+        fill_gemm(gm, lds, Wsel, a.d, kFT, Bsel, a.ld_in, a.rows - n0, a.d / G::BK);
+    }
 
     T* pool = (T*)(is_k ? a.kc[g] : a.vc[g]);
     const float* ps = NORM ? a.psum + g * a.ps_slot : nullptr;
@@ -506,8 +516,15 @@ static rf_status launch_fill(const rf_fill_weights* w, int32_t n_layers, const v
 }
 
 template <typename T, int DH, bool BIAS>
-static void launch_translate_group(const KVArgs& ka, int gsz, hipStream_t stream) {
+static void launch_translate_group(const KVArgs& ka, int gsz, bool headwise, hipStream_t stream) {
     const dim3 grid((2 * ka.kvw / kFT) * ka.tok_tiles * gsz);
+    if constexpr (sizeof(T) == 2) {
+        if (headwise) {
+            hipLaunchKernelGGL((k_fill_kv<T, DH, false, BIAS, true>), grid, dim3(KVCore<T>::G::kThr), 0, stream, ka);
+            return;
+        }
+    }
+    // fp32 (tiny widths) computes head-wise maps densely: their zero blocks add nothing
     hipLaunchKernelGGL((k_fill_kv<T, DH, false, BIAS>), grid, dim3(KVCore<T>::G::kThr), 0, stream, ka);
 }
 
@@ -536,12 +553,13 @@ static rf_status launch_translate(const rf_translate_weights* w, int32_t n_layer
             ka.Wk[g] = w->T_k[l0 + g]; ka.Wv[g] = w->T_v[l0 + g];
             ka.kc[g] = kc[l0 + g]; ka.vc[g] = vc[l0 + g];
         }
+        const bool hw = w->headwise != 0;
         if (w->head_dim == 128) {
-            if (bias) launch_translate_group<T, 128, true>(ka, gsz, stream);
-            else launch_translate_group<T, 128, false>(ka, gsz, stream);
+            if (bias) launch_translate_group<T, 128, true>(ka, gsz, hw, stream);
+            else launch_translate_group<T, 128, false>(ka, gsz, hw, stream);
         } else {
-            if (bias) launch_translate_group<T, 64, true>(ka, gsz, stream);
-            else launch_translate_group<T, 64, false>(ka, gsz, stream);
+            if (bias) launch_translate_group<T, 64, true>(ka, gsz, hw, stream);
+            else launch_translate_group<T, 64, false>(ka, gsz, hw, stream);
         }
         const rf_status st = check_launch("rf_translate: kernel");
         if (st != RF_OK) return st;
@@ -675,6 +693,9 @@ rf_status rf_translate(const rf_translate_weights* w, int32_t n_layers, const vo
                "rf_translate: cache heads/head_dim differ from the maps'");
     RF_REQUIRE((w->b_k == nullptr) == (w->b_v == nullptr), RF_ERR_INVALID_ARG,
                "rf_translate: b_k and b_v must both be given or both be NULL");
+    RF_REQUIRE(w->headwise == 0 || w->headwise == 1, RF_ERR_INVALID_ARG, "rf_translate: headwise must be 0 or 1");
+    RF_REQUIRE(!w->headwise || w->d_in % (w->n_kv_heads * w->head_dim) == 0, RF_ERR_UNSUPPORTED,
+               "rf_translate: head-wise maps need d_in = nu * n_kv_heads * head_dim (source heads as the target's)");
     rf_cache_layout_t L;
     rf_status st = rf_cache_layout(cache, &L);
     if (st != RF_OK) return st;

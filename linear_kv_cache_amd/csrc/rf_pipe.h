@@ -362,9 +362,12 @@ struct PackedAGemm {
 
     // Full K loop over ``nk`` k-steps (even).  A.ptr is the packed tile; A.ld and A.valid are
     // unused (a packed tile always holds 256 rows).  With FOLD, k-step kt of B is read from step
-    // kt < b_fold ? kt : kt - b_fold of its rows (B's first b_fold steps serve twice).
-    template <bool FOLD = false>
-    __device__ inline void run(char* lds, const PipeOperand& A, const PipeOperand& B, int nk, int b_fold = 0) {
+    // kt < b_fold ? kt : kt - b_fold of its rows (B's first b_fold steps serve twice).  With SEG,
+    // the K loop visits segments of 4 k-steps (256 columns) seg_stride steps apart: logical step
+    // kt reads step (kt / 4) * seg_stride + kt % 4 of both operands.
+    template <bool FOLD = false, bool SEG = false>
+    __device__ inline void run(char* lds, const PipeOperand& A, const PipeOperand& B, int nk, int b_fold = 0,
+                               int seg_stride = 4) {
         const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
 #pragma unroll
         for (int i = 0; i < SM; ++i)
@@ -373,8 +376,13 @@ struct PackedAGemm {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
         if (nk <= 0) return;
+        // physical k-step of logical step kc (uniform by construction, said so for the compiler)
+        auto phys = [&](int kc) {
+            if constexpr (SEG) return __builtin_amdgcn_readfirstlane((kc >> 2) * seg_stride + (kc & 3));
+            return kc;
+        };
         const __amdgpu_buffer_rsrc_t ra =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(A.ptr), (short)0, nk * kStepBytes, 0x00020000);
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(A.ptr), (short)0, (phys(nk - 1) + 1) * kStepBytes, 0x00020000);
         int64_t nb = B.valid < BN ? B.valid : BN;
         if (nb < 0) nb = 0;
         const __amdgpu_buffer_rsrc_t rb =
@@ -395,7 +403,7 @@ struct PackedAGemm {
         // A fragments of two k-steps (parity p), 4 slices x 2 blocks each
         u32x4 fa[2][4][SM];
         auto aload = [&](int p, int kk, int kt) {
-            const int kc = kt < nk ? kt : nk - 1;
+            const int kc = phys(kt < nk ? kt : nk - 1);
 #pragma unroll
             for (int i = 0; i < SM; ++i)
                 fa[p][kk][i] = __builtin_amdgcn_raw_buffer_load_b128(ra, av, kc * kStepBytes + (kk * 2 + i) * 1024, 0);
@@ -408,6 +416,7 @@ struct PackedAGemm {
                 // waterfall loop
                 kc = __builtin_amdgcn_readfirstlane(kc);
             }
+            kc = phys(kc);
 #pragma unroll
             for (int j = j0; j < j1; ++j) g.b[j] = __builtin_amdgcn_raw_buffer_load_b128(rb, gB + j * strideB, kc * ROWB, 0);
         };

@@ -153,14 +153,14 @@ class Filler:
 
 
 def translate_weights(d_in: int, n_kv_heads: int, head_dim: int, dtype, T_k, T_v, b_k=None, b_v=None,
-                      stream=None) -> TranslateWeights:
+                      stream=None, headwise: bool = False) -> TranslateWeights:
     """TranslateWeights from row-major [kv_width, d_in] maps: for bf16 they are packed first
     (fp32 maps are rounded to bf16 by the packing); the fp32 path reads them as they are."""
     if dtype == torch.bfloat16:
         T_k = [pack_weights(T, head_dim, stream) for T in T_k]
         T_v = [pack_weights(T, head_dim, stream) for T in T_v]
     return TranslateWeights(d_in, n_kv_heads, head_dim, dtype, list(T_k), list(T_v),
-                            None if b_k is None else list(b_k), None if b_v is None else list(b_v))
+                            None if b_k is None else list(b_k), None if b_v is None else list(b_v), headwise)
 
 
 class Translator:

@@ -314,7 +314,10 @@ class TranslateConfig:
         return torch.float32 if self.dtype == "f32" else torch.bfloat16
 
     def flop_per_token_layer(self) -> int:
-        """Algorithmic work of one translated (token, target layer): K and V products."""
+        """Algorithmic work of one translated (token, target layer): K and V products (the
+        head blocks only, for head-wise maps)."""
+        if self.maps == "headwise":
+            return 2 * 2 * self.nu * self.n_kv_heads * self.head_dim * self.src_head_dim
         return 2 * 2 * self.d_in * self.kv_width
 
 

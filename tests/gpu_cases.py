@@ -204,7 +204,7 @@ def run_translate_case(case: TranslateCase, device="cuda"):
     md = [tuple(None if x is None else x.to(device) for x in m) for m in maps]
     tw = translate_weights(cfg.d_in, cfg.n_kv_heads, cfg.head_dim, cfg.torch_dtype, [m[0] for m in md],
                            [m[1] for m in md], [m[2] for m in md] if cfg.bias else None,
-                           [m[3] for m in md] if cfg.bias else None)
+                           [m[3] for m in md] if cfg.bias else None, headwise=cfg.maps == "headwise")
     table = synth.translate_block_table(cfg, T, device=device) if cfg.paged else None
     cache = alloc_cache(n_tgt, cfg.n_kv_heads, cfg.head_dim, T, cfg.torch_dtype, device, paged=cfg.paged,
                         block_size=cfg.block_size, block_table=table,

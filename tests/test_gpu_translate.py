@@ -58,6 +58,19 @@ def test_translate_bf16_headwise_and_tile_edges():
         _check(run_translate_case(TranslateCase(SMALL_HEADWISE, t0, t1, n_layers=2)), f"rows [{t0},{t1})")
 
 
+def test_translate_headwise_two_sources_paged_and_head_dim_64():
+    # head-wise maps read block by block (8 x 128: one 256-column block of each of the 2 source
+    # layers per tile; 4 x 64: four heads per block), paged, intercepts; fp32 computes the same
+    # maps densely
+    _check(run_translate_case(TranslateCase(synth.scaled(SMALL_PAGED, name="tr-hw-paged", maps="headwise", seed=2007),
+                                            37, 737, pos0=11, chunk=400)), "bf16 head-wise nu=2 paged")
+    cfg64 = synth.scaled(SMALL_PAGED, name="tr-hw-dh64", src_kv_heads=4, src_head_dim=64, n_kv_heads=4, head_dim=64,
+                         maps="headwise", paged=False, seed=2008)
+    _check(run_translate_case(TranslateCase(cfg64, 0, 700)), "bf16 head-wise dh64 nu=2")
+    _check(run_translate_case(TranslateCase(synth.scaled(TINY_F32, name="tr-hw-f32", maps="headwise", seed=2009),
+                                            0, 300)), "fp32 head-wise nu=2")
+
+
 def test_translate_bf16_head_dim_64_far_positions():
     # target heads of 64 from a 2 x 128 source, RoPE at positions near 131072
     _check(run_translate_case(TranslateCase(SMALL_DH64, 0, 600, pos0=130000)), "bf16 dh64 far pos")
