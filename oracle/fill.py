@@ -50,28 +50,37 @@ def rmsnorm(h, gamma, eps: float) -> np.ndarray:
 
 
 def fill_layer(X, W, b, gamma, W_K, W_V, positions, n_kv_heads: int, head_dim: int,
-               eps: float, base: float):
+               eps: float, base: float, k_norm=None, k_norm_eps: float = 1e-6):
     """K and V rows of one late layer for the token states X [T, d].
 
-    h = x W + b (predicted input); u = RMSNorm(h) * gamma; k = u W_K, v = u W_V; RoPE on k.
+    h = x W + b (predicted input); u = RMSNorm(h) * gamma; k = u W_K, v = u W_V; with
+    ``k_norm`` (gamma_k [d_h]) each head of k is RMS-normalised (KV-Lingo page, section 2: some
+    models normalise keys per head before rotating them); RoPE on k.
     Returns (K, V), each [T, H, d_h] fp64."""
     X = _f64(X)
     H = X @ _f64(W) + _f64(b)
     U = rmsnorm(H, gamma, eps)
     K = (U @ _f64(W_K)).reshape(X.shape[0], n_kv_heads, head_dim)
     V = (U @ _f64(W_V)).reshape(X.shape[0], n_kv_heads, head_dim)
+    if k_norm is not None:
+        K = rmsnorm(K, k_norm, k_norm_eps)
     return rope_rotate(K, positions, base), V
 
 
 def fill(X, t0: int, t1: int, pos0: int, layers, n_kv_heads: int, head_dim: int,
-         eps: float, base: float):
+         eps: float, base: float, k_norm_eps: float = 1e-6):
     """Fill token rows [t0, t1) of every listed layer.
 
     X holds the split-layer states of tokens t0..t1-1 (row i is token t0 + i); token t sits
-    at RoPE position pos0 + t.  ``layers`` is a sequence of (W, b, gamma, W_K, W_V).
+    at RoPE position pos0 + t.  ``layers`` is a sequence of (W, b, gamma, W_K, W_V), or of
+    (W, b, gamma, W_K, W_V, gamma_k) for layers that normalise keys per head.
     Returns a list of (K, V) per layer, each [t1 - t0, H, d_h]."""
     X = _f64(X)
     if X.shape[0] != t1 - t0:
         raise ValueError("X must hold exactly the rows [t0, t1)")
     positions = pos0 + np.arange(t0, t1, dtype=np.float64)
-    return [fill_layer(X, *lw, positions, n_kv_heads, head_dim, eps, base) for lw in layers]
+    out = []
+    for lw in layers:
+        kn = lw[5] if len(lw) > 5 else None
+        out.append(fill_layer(X, *lw[:5], positions, n_kv_heads, head_dim, eps, base, kn, k_norm_eps))
+    return out

@@ -5,10 +5,9 @@ KV-Lingo page, section 3.1 "Linear translator family":
     values (T_V^l), that read the caches of a set E_l of nu source layers;
   * head-wise translators are block-diagonal (target head h reads only source head h),
     head-mixing translators are unconstrained;
-  * pre-norm storing: the maps act on the source's keys before any rotation, and the
-    translated keys are rotated by their token's position before they are stored.  The
-    per-head key normalisation some models apply is off here (the Llama-style shapes of the
-    workloads have none), so pre-norm and post-norm coincide.
+  * pre-norm storing: the maps act on the source's keys before any normalisation or
+    rotation; the translated keys are normalised per head (for targets that normalise keys,
+    section 2) and rotated by their token's position before they are stored.
 Section 3.1 "Source-layer selection": relative-depth match gives target layer l (1-based)
 the band of nu consecutive source layers centred on c(l) = 1 + (l - 1)(N_src - 1)/(N_tgt - 1),
 shifted at the boundaries so every band has nu layers.
@@ -34,7 +33,7 @@ from fractions import Fraction
 
 import numpy as np
 
-from .fill import rope_rotate
+from .fill import rmsnorm, rope_rotate
 from .ridge import fit
 
 
@@ -81,12 +80,13 @@ def headwise_dense(blocks) -> np.ndarray:
 
 
 def translate_layer(src_k, src_v, T_k, T_v, b_k, b_v, positions, n_kv_heads: int, head_dim: int,
-                    base: float):
+                    base: float, k_norm=None, k_norm_eps: float = 1e-6):
     """Target K and V rows of one layer from its source rows.
 
     src_k, src_v [T, d_in]: the source keys (before rotation) and values of the nu source
     layers, concatenated along the row; T_k, T_v [d_in, H*d_h]; b_k, b_v [H*d_h] or None.
-    k = src_k T_k + b_k, rotated by its position; v = src_v T_v + b_v.
+    k = src_k T_k + b_k, per-head RMS-normalised with gamma_k = ``k_norm`` when given, rotated
+    by its position; v = src_v T_v + b_v.
     Returns (K, V), each [T, H, d_h] fp64."""
     src_k = _f64(src_k)
     src_v = _f64(src_v)
@@ -99,6 +99,8 @@ def translate_layer(src_k, src_v, T_k, T_v, b_k, b_v, positions, n_kv_heads: int
         V = V + _f64(b_v)
     K = K.reshape(n, n_kv_heads, head_dim)
     V = V.reshape(n, n_kv_heads, head_dim)
+    if k_norm is not None:
+        K = rmsnorm(K, k_norm, k_norm_eps)
     return rope_rotate(K, positions, base), V
 
 

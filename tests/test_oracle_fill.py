@@ -130,3 +130,38 @@ def test_layer_subset_independence():
 def test_fill_rejects_row_count_mismatch():
     with pytest.raises(ValueError):
         oracle.fill(np.zeros((3, 4)), 0, 4, 0, [], 1, 4, 0.0, 1e4)
+
+
+def test_per_head_key_norm_hand_worked_and_order():
+    # one head of d_h = 4, identity map and projections, base 100, position 1, gamma_k =
+    # [1, 2, 1, 1], eps_k = 0: x = [3, 4, 0, 0] has RMS 2.5 (the layer's RMSNorm with eps = 0
+    # gives u = [1.2, 1.6, 0, 0], RMS 1); the key norm keeps it and scales dim 1 by 2:
+    # [1.2, 3.2, 0, 0]; then the pairs (0, 2) and (1, 3) turn by 1 and 0.1 rad.  Rotating first
+    # would scale the rotated dim 1 instead: 1.6 sin(0.1) in dim 3, not 3.2 sin(0.1).
+    I = np.eye(4)
+    K, V = oracle.fill_layer(np.array([[3.0, 4.0, 0.0, 0.0]]), I, np.zeros(4), np.ones(4), I, I,
+                             np.array([1.0]), 1, 4, 0.0, 100.0, k_norm=np.array([1.0, 2.0, 1.0, 1.0]),
+                             k_norm_eps=0.0)
+    expect = [1.2 * math.cos(1.0), 3.2 * math.cos(0.1), 1.2 * math.sin(1.0), 3.2 * math.sin(0.1)]
+    assert np.allclose(K[0, 0], expect, rtol=0, atol=1e-15)
+    assert np.allclose(V[0, 0], [1.2, 1.6, 0.0, 0.0], rtol=0, atol=1e-15)
+
+
+def test_per_head_key_norm_invariants():
+    rng = np.random.default_rng(9)
+    d, H, dh, n = 16, 2, 8, 5
+    X = rng.standard_normal((n, d))
+    W, Wk, Wv = rng.standard_normal((d, d)), rng.standard_normal((d, H * dh)), rng.standard_normal((d, H * dh))
+    g, b = 1 + 0.1 * rng.standard_normal(d), rng.standard_normal(d)
+    pos = np.arange(n, dtype=float) * 5
+    K1, V1 = oracle.fill_layer(X, W, b, g, Wk, Wv, pos, H, dh, 1e-6, 1e4, k_norm=np.ones(dh), k_norm_eps=0.0)
+    # unit gamma_k, no epsilon: every head of every key has RMS 1 (rotation keeps pair norms)
+    assert np.allclose(np.sqrt(np.mean(K1 ** 2, axis=-1)), 1.0, rtol=0, atol=1e-12)
+    # values untouched; keys invariant to a scale of W_K and to the head's own scale
+    K0, V0 = oracle.fill_layer(X, W, b, g, Wk, Wv, pos, H, dh, 1e-6, 1e4)
+    assert np.array_equal(V0, V1)
+    K2, _ = oracle.fill_layer(X, W, b, g, 3.7 * Wk, Wv, pos, H, dh, 1e-6, 1e4, k_norm=np.ones(dh), k_norm_eps=0.0)
+    assert np.allclose(K1, K2, rtol=0, atol=1e-12)
+    # the normalised keys are the plain keys rescaled head by head before the rotation
+    scale = 1.0 / np.sqrt(np.mean(oracle.rope_rotate(K0, -pos, 1e4) ** 2, axis=-1, keepdims=True))
+    assert np.allclose(K1, K0 * scale, rtol=0, atol=1e-12)

@@ -236,3 +236,18 @@ def test_r2_assignment_hand_worked():
     assert oracle.r2_assignment(r2, 4) == [[0, 1, 2, 3]] * 3
     with pytest.raises(ValueError):
         oracle.r2_assignment(r2, 5)
+
+
+def test_translator_key_norm_before_rotation():
+    # pre-norm storing: map, then the target's per-head key norm, then RoPE (KV-Lingo section 3.1)
+    rng = np.random.default_rng(13)
+    H, dh, n = 2, 8, 6
+    sk, sv = rng.standard_normal((n, H * dh)), rng.standard_normal((n, H * dh))
+    Tk, Tv = rng.standard_normal((H * dh, H * dh)), rng.standard_normal((H * dh, H * dh))
+    gk = 1 + 0.2 * rng.standard_normal(dh)
+    pos = 3.0 + np.arange(n)
+    K, V = oracle.translate_layer(sk, sv, Tk, Tv, None, None, pos, H, dh, 1e4, k_norm=gk, k_norm_eps=1e-6)
+    k = (sk @ Tk).reshape(n, H, dh)
+    kn = k / np.sqrt(np.mean(k * k, axis=-1, keepdims=True) + 1e-6) * gk
+    assert np.allclose(K, _rope_complex(kn, pos, 1e4), rtol=0, atol=1e-12)
+    assert np.allclose(V, (sv @ Tv).reshape(n, H, dh), rtol=0, atol=1e-12)
