@@ -246,6 +246,8 @@ rf_status rf_pack_weights(rf_dtype dtype, int64_t rows, int64_t cols, const void
  *     h = x_t W_l^T + b_l                              (predicted layer input)
  *     u = h / sqrt(mean_j h_j^2 + rms_eps) * gamma_l   (the layer's own RMSNorm)
  *     k = u W_k,l^T,  v = u W_v,l^T                    (the layer's own K/V projections)
+ *     k <- k_g / sqrt(mean(k_g^2) + k_norm_eps) * k_norm_l  for each head g  (only when
+ *          k_norm is given: models that normalise keys per head, KV-Lingo page, section 2)
  *     k <- RoPE(k, pos0 + t)                           (keys only)
  * and k, v are stored in the layer's K and V pools at token t.  Rows outside [t0, t1) and
  * layers not listed are never written: exact rows skip the map (project page, Fig. 2).
@@ -277,6 +279,8 @@ typedef struct {
     const float* const* gamma;
     const void* const* W_k;
     const void* const* W_v;
+    const float* const* k_norm;   /* NULL, or per layer fp32 [head_dim]: per-head key norm    */
+    float k_norm_eps;             /* its epsilon (inside the root), when k_norm is given      */
 } rf_fill_weights;
 
 size_t rf_fill_workspace_bytes(const rf_fill_weights* weights, int64_t max_rows);
@@ -295,6 +299,7 @@ rf_status rf_fill(const rf_fill_weights* weights, int32_t n_layers,
  * the source keys before rotation, and the translated keys are rotated by their token's
  * position before they are stored.  For every token t in [t0, t1) and listed target layer l,
  *     k = s_k T_k,l^T + b_k,l,   v = s_v T_v,l^T + b_v,l
+ *     k <- k_g / sqrt(mean(k_g^2) + k_norm_eps) * k_norm_l  for each head g  (when given)
  *     k <- RoPE(k, pos0 + t)                           (keys only)
  * and k, v are stored in the layer's K and V pools at token t.  s_k (s_v) is the row of
  * token t in d_src_k[l] (d_src_v[l]): the keys before rotation (the values) of the layer's
@@ -309,7 +314,6 @@ rf_status rf_fill(const rf_fill_weights* weights, int32_t n_layers,
  * closed-form first stage (KV-Lingo page, section 3.2) is a ridge fit of target rows on
  * source rows: rf_gram_accumulate and rf_solve with X = source rows, one target of the
  * same width; rf_pack_weights packs the solve's fp32 maps (rope_head_dim = head_dim).
- * The per-head key normalisation of some models is not applied.
  *
  * Maps, per listed target layer (host arrays of n_layers device pointers):
  *   T_k[l], T_v[l] : [n_kv_heads*head_dim][d_in] dtype, head-major output rows, out-feature
@@ -332,7 +336,10 @@ typedef struct {
     const void* const* T_v;
     const float* const* b_k;
     const float* const* b_v;
-    int32_t headwise;          /* 1: block-diagonal maps (see above); 0: dense maps */
+    int32_t headwise;             /* 1: block-diagonal maps (see above); 0: dense maps          */
+    const float* const* k_norm;   /* NULL, or per layer fp32 [head_dim]: the target's per-head
+                                     key norm, applied after the map and before the rotation */
+    float k_norm_eps;
 } rf_translate_weights;
 
 rf_status rf_translate(const rf_translate_weights* weights, int32_t n_layers,

@@ -61,13 +61,15 @@ class rf_cache_layout_t(C.Structure):
 class rf_fill_weights(C.Structure):
     _fields_ = [("d", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("rms_eps", C.c_float),
                 ("dtype", C.c_int), ("W_map", C.POINTER(C.c_void_p)), ("b_map", C.POINTER(C.c_void_p)),
-                ("gamma", C.POINTER(C.c_void_p)), ("W_k", C.POINTER(C.c_void_p)), ("W_v", C.POINTER(C.c_void_p))]
+                ("gamma", C.POINTER(C.c_void_p)), ("W_k", C.POINTER(C.c_void_p)), ("W_v", C.POINTER(C.c_void_p)),
+                ("k_norm", C.POINTER(C.c_void_p)), ("k_norm_eps", C.c_float)]
 
 
 class rf_translate_weights(C.Structure):
     _fields_ = [("d_in", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("dtype", C.c_int),
                 ("T_k", C.POINTER(C.c_void_p)), ("T_v", C.POINTER(C.c_void_p)), ("b_k", C.POINTER(C.c_void_p)),
-                ("b_v", C.POINTER(C.c_void_p)), ("headwise", C.c_int32)]
+                ("b_v", C.POINTER(C.c_void_p)), ("headwise", C.c_int32), ("k_norm", C.POINTER(C.c_void_p)),
+                ("k_norm_eps", C.c_float)]
 
 
 _P = C.c_void_p
@@ -233,12 +235,16 @@ class FillWeights:
     gamma: list
     W_k: list
     W_v: list
+    k_norm: Optional[list] = None
+    k_norm_eps: float = 1e-6
 
     def _c(self):
         arrs = [_ptr_array(x) for x in (self.W_map, self.b_map, self.gamma, self.W_k, self.W_v)]
+        kn = None if self.k_norm is None else _ptr_array(self.k_norm)
         w = rf_fill_weights(self.d, self.n_kv_heads, self.head_dim, self.rms_eps, _dtype_code(self.dtype),
-                            *[C.cast(a, C.POINTER(_P)) for a in arrs])
-        return w, arrs
+                            *[C.cast(a, C.POINTER(_P)) for a in arrs],
+                            C.cast(kn, C.POINTER(_P)) if kn is not None else C.POINTER(_P)(), self.k_norm_eps)
+        return w, (arrs, kn)
 
 
 def rf_fill_workspace_bytes(weights: FillWeights, max_rows: int) -> int:
@@ -275,13 +281,16 @@ class TranslateWeights:
     b_k: Optional[list] = None
     b_v: Optional[list] = None
     headwise: bool = False
+    k_norm: Optional[list] = None
+    k_norm_eps: float = 1e-6
 
     def _c(self):
         arrs = [_ptr_array(x) for x in (self.T_k, self.T_v)]
-        barrs = [None if x is None else _ptr_array(x) for x in (self.b_k, self.b_v)]
+        barrs = [None if x is None else _ptr_array(x) for x in (self.b_k, self.b_v, self.k_norm)]
         cast = lambda a: C.cast(a, C.POINTER(_P)) if a is not None else C.POINTER(_P)()
         w = rf_translate_weights(self.d_in, self.n_kv_heads, self.head_dim, _dtype_code(self.dtype),
-                                 cast(arrs[0]), cast(arrs[1]), cast(barrs[0]), cast(barrs[1]), int(self.headwise))
+                                 cast(arrs[0]), cast(arrs[1]), cast(barrs[0]), cast(barrs[1]), int(self.headwise),
+                                 cast(barrs[2]), self.k_norm_eps)
         return w, (arrs, barrs)
 
 

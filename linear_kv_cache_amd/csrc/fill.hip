@@ -63,6 +63,8 @@ struct KVArgs {
     const void* in_v[kMaxGroup];
     const float* bk[kMaxGroup];   // per-feature intercepts (translators only)
     const float* bv[kMaxGroup];
+    const float* kn[kMaxGroup];   // per-head key norm weights [head_dim] (KN only)
+    float kn_eps;
     const void* Wk[kMaxGroup];
     const void* Wv[kMaxGroup];
     void* kc[kMaxGroup];
@@ -208,8 +210,9 @@ __global__ __launch_bounds__(MapCore<T>::G::kThr) void k_fill_map(MapArgs a) {
 // NORM: the fill (rows scaled by 1/rms from the map's partial sums).  Otherwise the product
 // of a translator (KV-Lingo page, section 3.1): no row scale, an intercept when BIAS.  HW
 // (bf16): head-wise maps, block-diagonal by head, so a 256-feature tile reads only its own
-// 256-column block of each source layer (d = nu * kvw; the other blocks are zero).
-template <typename T, int DH, bool NORM, bool BIAS, bool HW = false>
+// 256-column block of each source layer (d = nu * kvw; the other blocks are zero).  KN: keys
+// are RMS-normalised per head with weights kn (KV-Lingo page, section 2) before the rotation.
+template <typename T, int DH, bool NORM, bool BIAS, bool HW = false, bool KN = false>
 __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
     using G = typename KVCore<T>::G;
     static_assert(!HW || (sizeof(T) == 2 && !NORM), "head-wise products are bf16 translators");
@@ -218,7 +221,8 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
     constexpr int HALF = DH / 2;
     constexpr int PAIR = HALF / 32;  // fp32: sub-tile distance between RoPE partners
     // staged tile, then 1/rms and the cache row offset of every token of the tile
-    constexpr int kEpi = sizeof(T) == 2 ? kTT * kFT * 2 + kTT * 4 + kTT * 8 : 0;
+    // (KN: then the per-wave, per-token partial key sums of squares)
+    constexpr int kEpi = sizeof(T) == 2 ? kTT * kFT * 2 + kTT * 4 + kTT * 8 + (KN ? 4 * kTT * 4 : 0) : 0;
     __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES > kEpi ? G::LDS_BYTES : kEpi];
     int g, mt, tt;
     fill_tile(2 * a.kvw / kFT, a.tok_tiles, g, mt, tt);
@@ -298,6 +302,36 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
             if constexpr (BIAS) return *(const f32x4*)(bsel + fl);
             return f32x4{0.f, 0.f, 0.f, 0.f};
         };
+        // per-head key norm: a wave's 32 pairs are half of a 128-wide head (the other half in
+        // wave wm ^ 1) or all of a 64-wide one; each token's sum of squares over the lane's 32
+        // values, the lane holding the token's other pairs (lane ^ 32) and, for 128, the partner
+        // wave (through LDS) gives 1/rms of the head
+        float* knred = (float*)(lds + kTT * kFT * 2 + kTT * 4 + kTT * 8);
+        if constexpr (KN) {
+            if (is_k) {
+#pragma unroll
+                for (int j = 0; j < G::SN; ++j) {
+                    const int nl = G::col_of(j);
+                    const float r = NORM ? rinv[nl] : 1.f;
+                    float ss = 0.f;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int qp = qp0 + 8 * q;
+                        const int fl = (qp / HALF) * DH + qp % HALF;
+                        const f32x4 blo = bias4(fl), bhi = bias4(fl + HALF);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float x = gm.acc[0][j][4 * q + e] * r + blo[e];
+                            const float y = gm.acc[1][j][4 * q + e] * r + bhi[e];
+                            ss += x * x + y * y;
+                        }
+                    }
+                    ss += __shfl_xor(ss, 32);
+                    if ((threadIdx.x & 63) < 32) knred[wm * kTT + nl] = ss;
+                }
+                __syncthreads();
+            }
+        }
 #pragma unroll
         for (int j = 0; j < G::SN; ++j) {
             const int nl = G::col_of(j);
@@ -329,6 +363,12 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
                     c23[q] = *(const f32x4*)(cs_row + 2 * dlo + 4);
                 }
                 __builtin_amdgcn_sched_barrier(0);
+                float kinv = 1.f;
+                if constexpr (KN) {
+                    float ssh = knred[wm * kTT + nl];
+                    if constexpr (DH == 128) ssh += knred[(wm ^ 1) * kTT + nl];
+                    kinv = 1.0f / sqrtf(ssh * (1.0f / (float)DH) + a.kn_eps);
+                }
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int qp = qp0 + 8 * q;
@@ -336,11 +376,20 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
                     const float cs[4] = {c01[q][0], c01[q][2], c23[q][0], c23[q][2]};
                     const float sn[4] = {c01[q][1], c01[q][3], c23[q][1], c23[q][3]};
                     const f32x4 blo = bias4(fl), bhi = bias4(fl + HALF);
+                    f32x4 glo{1.f, 1.f, 1.f, 1.f}, ghi{1.f, 1.f, 1.f, 1.f};
+                    if constexpr (KN) {
+                        glo = *(const f32x4*)(a.kn[g] + qp % HALF);
+                        ghi = *(const f32x4*)(a.kn[g] + qp % HALF + HALF);
+                    }
                     float lo[4], hi[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float x = gm.acc[0][j][4 * q + e] * r + blo[e];
-                        const float y = gm.acc[1][j][4 * q + e] * r + bhi[e];
+                        float x = gm.acc[0][j][4 * q + e] * r + blo[e];
+                        float y = gm.acc[1][j][4 * q + e] * r + bhi[e];
+                        if constexpr (KN) {
+                            x *= kinv * glo[e];
+                            y *= kinv * ghi[e];
+                        }
                         lo[e] = x * cs[e] - y * sn[e];
                         hi[e] = y * cs[e] + x * sn[e];
                     }
@@ -372,6 +421,34 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
             if (base < 0) continue;
             const float r = rms_inv(n);
             const float* cs_row = a.rope + (a.pos0 + t) * (int64_t)DH;  // HALF (cos, sin) pairs
+            // per-head key norm: sub-tiles i of one head (DH / 32 of them, inside the wave's
+            // rows) and the token's other rows in lane ^ 32
+            float kinv[G::SM];
+#pragma unroll
+            for (int i = 0; i < G::SM; ++i) kinv[i] = 1.f;
+            if constexpr (KN) {
+                if (is_k) {
+                    constexpr int kSub = DH / 32;
+#pragma unroll
+                    for (int h0 = 0; h0 < G::SM; h0 += kSub) {
+                        float ss = 0.f;
+#pragma unroll
+                        for (int i = h0; i < h0 + kSub; ++i)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    float x = gm.acc[i][j][4 * q + e] * r;
+                                    if constexpr (BIAS) x += bsel[G::row_of(i, 4 * q) + e];
+                                    ss += x * x;
+                                }
+                        ss += __shfl_xor(ss, 32);
+                        const float inv = 1.0f / sqrtf(ss * (1.0f / (float)DH) + a.kn_eps);
+#pragma unroll
+                        for (int i = h0; i < h0 + kSub; ++i) kinv[i] = inv;
+                    }
+                }
+            }
 #pragma unroll
             for (int i = 0; i < G::SM; ++i) {
 #pragma unroll
@@ -398,8 +475,12 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
                         float lo[4], hi[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            const float x0 = add_b(gm.acc[i][j][4 * q + e] * r, fb + e);
-                            const float x1 = add_b(gm.acc[(i + PAIR) % G::SM][j][4 * q + e] * r, fb + HALF + e);
+                            float x0 = add_b(gm.acc[i][j][4 * q + e] * r, fb + e);
+                            float x1 = add_b(gm.acc[(i + PAIR) % G::SM][j][4 * q + e] * r, fb + HALF + e);
+                            if constexpr (KN) {
+                                x0 *= kinv[i] * a.kn[g][dim + e];
+                                x1 *= kinv[(i + PAIR) % G::SM] * a.kn[g][dim + HALF + e];
+                            }
                             lo[e] = x0 * cs[e] - x1 * sn[e];
                             hi[e] = x1 * cs[e] + x0 * sn[e];
                         }
@@ -493,8 +574,10 @@ static rf_status launch_fill(const rf_fill_weights* w, int32_t n_layers, const v
         ka.paged = cache->layout == RF_LAYOUT_PAGED; ka.block_size = cache->block_size;
         ka.stride_block = L.stride_block; ka.stride_head = L.stride_head; ka.stride_token = L.stride_token;
         ka.n_blocks = L.n_blocks; ka.block_table = table; ka.n_table_blocks = n_table;
+        ka.kn_eps = w->k_norm_eps;
         for (int g = 0; g < gsz; ++g) {
             ma.W[g] = w->W_map[l0 + g]; ma.bias[g] = w->b_map[l0 + g]; ma.gamma[g] = w->gamma[l0 + g];
+            ka.kn[g] = w->k_norm ? w->k_norm[l0 + g] : nullptr;
             ka.Wk[g] = w->W_k[l0 + g]; ka.Wv[g] = w->W_v[l0 + g];
             ka.in_k[g] = ka.in_v[g] = (const T*)wsc + g * h_slot;
             ka.kc[g] = kc[l0 + g]; ka.vc[g] = vc[l0 + g];
@@ -505,27 +588,47 @@ static rf_status launch_fill(const rf_fill_weights* w, int32_t n_layers, const v
         rf_status st = check_launch("rf_fill: map kernel");
         if (st != RF_OK) return st;
         const dim3 kv_grid((2 * ka.kvw / kFT) * tok_tiles * gsz);
-        if (w->head_dim == 128)
-            hipLaunchKernelGGL((k_fill_kv<T, 128, true, false>), kv_grid, dim3(KVCore<T>::G::kThr), 0, stream, ka);
-        else
-            hipLaunchKernelGGL((k_fill_kv<T, 64, true, false>), kv_grid, dim3(KVCore<T>::G::kThr), 0, stream, ka);
+        const dim3 blk(KVCore<T>::G::kThr);
+        if (w->k_norm) {
+            if (w->head_dim == 128)
+                hipLaunchKernelGGL((k_fill_kv<T, 128, true, false, false, true>), kv_grid, blk, 0, stream, ka);
+            else
+                hipLaunchKernelGGL((k_fill_kv<T, 64, true, false, false, true>), kv_grid, blk, 0, stream, ka);
+        } else {
+            if (w->head_dim == 128)
+                hipLaunchKernelGGL((k_fill_kv<T, 128, true, false>), kv_grid, blk, 0, stream, ka);
+            else
+                hipLaunchKernelGGL((k_fill_kv<T, 64, true, false>), kv_grid, blk, 0, stream, ka);
+        }
         st = check_launch("rf_fill: kv kernel");
         if (st != RF_OK) return st;
     }
     return RF_OK;
 }
 
-template <typename T, int DH, bool BIAS>
+template <typename T, int DH, bool BIAS, bool KN>
 static void launch_translate_group(const KVArgs& ka, int gsz, bool headwise, hipStream_t stream) {
     const dim3 grid((2 * ka.kvw / kFT) * ka.tok_tiles * gsz);
     if constexpr (sizeof(T) == 2) {
         if (headwise) {
-            hipLaunchKernelGGL((k_fill_kv<T, DH, false, BIAS, true>), grid, dim3(KVCore<T>::G::kThr), 0, stream, ka);
+            hipLaunchKernelGGL((k_fill_kv<T, DH, false, BIAS, true, KN>), grid, dim3(KVCore<T>::G::kThr), 0, stream,
+                               ka);
             return;
         }
     }
     // fp32 (tiny widths) computes head-wise maps densely: their zero blocks add nothing
-    hipLaunchKernelGGL((k_fill_kv<T, DH, false, BIAS>), grid, dim3(KVCore<T>::G::kThr), 0, stream, ka);
+    hipLaunchKernelGGL((k_fill_kv<T, DH, false, BIAS, false, KN>), grid, dim3(KVCore<T>::G::kThr), 0, stream, ka);
+}
+
+template <typename T, int DH>
+static void launch_translate_dh(const KVArgs& ka, int gsz, bool headwise, bool bias, bool kn, hipStream_t stream) {
+    if (bias) {
+        if (kn) launch_translate_group<T, DH, true, true>(ka, gsz, headwise, stream);
+        else launch_translate_group<T, DH, true, false>(ka, gsz, headwise, stream);
+    } else {
+        if (kn) launch_translate_group<T, DH, false, true>(ka, gsz, headwise, stream);
+        else launch_translate_group<T, DH, false, false>(ka, gsz, headwise, stream);
+    }
 }
 
 template <typename T>
@@ -547,20 +650,17 @@ static rf_status launch_translate(const rf_translate_weights* w, int32_t n_layer
         ka.stride_block = L.stride_block; ka.stride_head = L.stride_head; ka.stride_token = L.stride_token;
         ka.n_blocks = L.n_blocks; ka.block_table = table; ka.n_table_blocks = n_table;
         ka.ld_in = ld_src;
+        ka.kn_eps = w->k_norm_eps;
         for (int g = 0; g < gsz; ++g) {
             ka.in_k[g] = src_k[l0 + g]; ka.in_v[g] = src_v[l0 + g];
+            ka.kn[g] = w->k_norm ? w->k_norm[l0 + g] : nullptr;
             ka.bk[g] = bias ? w->b_k[l0 + g] : nullptr; ka.bv[g] = bias ? w->b_v[l0 + g] : nullptr;
             ka.Wk[g] = w->T_k[l0 + g]; ka.Wv[g] = w->T_v[l0 + g];
             ka.kc[g] = kc[l0 + g]; ka.vc[g] = vc[l0 + g];
         }
-        const bool hw = w->headwise != 0;
-        if (w->head_dim == 128) {
-            if (bias) launch_translate_group<T, 128, true>(ka, gsz, hw, stream);
-            else launch_translate_group<T, 128, false>(ka, gsz, hw, stream);
-        } else {
-            if (bias) launch_translate_group<T, 64, true>(ka, gsz, hw, stream);
-            else launch_translate_group<T, 64, false>(ka, gsz, hw, stream);
-        }
+        const bool hw = w->headwise != 0, kn = w->k_norm != nullptr;
+        if (w->head_dim == 128) launch_translate_dh<T, 128>(ka, gsz, hw, bias, kn, stream);
+        else launch_translate_dh<T, 64>(ka, gsz, hw, bias, kn, stream);
         const rf_status st = check_launch("rf_translate: kernel");
         if (st != RF_OK) return st;
     }
@@ -634,6 +734,8 @@ rf_status rf_fill(const rf_fill_weights* w, int32_t n_layers, const void* d_X, i
     RF_REQUIRE(cache->n_kv_heads == w->n_kv_heads && cache->head_dim == w->head_dim, RF_ERR_INVALID_ARG,
                "rf_fill: cache heads/head_dim differ from the weights'");
     RF_REQUIRE(w->rms_eps >= 0.f && isfinite(w->rms_eps), RF_ERR_INVALID_ARG, "rf_fill: rms_eps must be finite and >= 0");
+    RF_REQUIRE(!w->k_norm || (w->k_norm_eps >= 0.f && isfinite(w->k_norm_eps)), RF_ERR_INVALID_ARG,
+               "rf_fill: k_norm_eps must be finite and >= 0");
     rf_cache_layout_t L;
     rf_status st = rf_cache_layout(cache, &L);
     if (st != RF_OK) return st;
@@ -652,6 +754,9 @@ rf_status rf_fill(const rf_fill_weights* w, int32_t n_layers, const void* d_X, i
                        aligned(w->b_map[l], 16) && aligned(w->gamma[l], 16) && aligned(k_cache[l], 16) &&
                        aligned(v_cache[l], 16),
                    RF_ERR_INVALID_ARG, "rf_fill: per-layer buffers must be 16-byte aligned");
+        if (w->k_norm)
+            RF_REQUIRE(w->k_norm[l] && aligned(w->k_norm[l], 16), RF_ERR_INVALID_ARG,
+                       "rf_fill: key norm weights must be non-null and 16-byte aligned");
     }
     RF_REQUIRE(aligned(d_rope, 16) && aligned(d_ws, 256), RF_ERR_INVALID_ARG,
                "rf_fill: rope table must be 16-byte and workspace 256-byte aligned");
@@ -694,6 +799,8 @@ rf_status rf_translate(const rf_translate_weights* w, int32_t n_layers, const vo
     RF_REQUIRE((w->b_k == nullptr) == (w->b_v == nullptr), RF_ERR_INVALID_ARG,
                "rf_translate: b_k and b_v must both be given or both be NULL");
     RF_REQUIRE(w->headwise == 0 || w->headwise == 1, RF_ERR_INVALID_ARG, "rf_translate: headwise must be 0 or 1");
+    RF_REQUIRE(!w->k_norm || (w->k_norm_eps >= 0.f && isfinite(w->k_norm_eps)), RF_ERR_INVALID_ARG,
+               "rf_translate: k_norm_eps must be finite and >= 0");
     RF_REQUIRE(!w->headwise || w->d_in % (w->n_kv_heads * w->head_dim) == 0, RF_ERR_UNSUPPORTED,
                "rf_translate: head-wise maps need d_in = nu * n_kv_heads * head_dim (source heads as the target's)");
     rf_cache_layout_t L;
@@ -715,6 +822,9 @@ rf_status rf_translate(const rf_translate_weights* w, int32_t n_layers, const vo
         if (bias)
             RF_REQUIRE(w->b_k[l] && w->b_v[l] && aligned(w->b_k[l], 16) && aligned(w->b_v[l], 16), RF_ERR_INVALID_ARG,
                        "rf_translate: intercepts must be non-null and 16-byte aligned");
+        if (w->k_norm)
+            RF_REQUIRE(w->k_norm[l] && aligned(w->k_norm[l], 16), RF_ERR_INVALID_ARG,
+                       "rf_translate: key norm weights must be non-null and 16-byte aligned");
     }
     RF_REQUIRE(aligned(d_rope, 16), RF_ERR_INVALID_ARG, "rf_translate: rope table must be 16-byte aligned");
     RF_REQUIRE(pos0 + t1 <= rope_len, RF_ERR_INVALID_ARG, "rf_translate: rope table shorter than pos0 + t1");

@@ -125,7 +125,7 @@ def pack_weights(W: torch.Tensor, rope_head_dim: int = 0, stream=None) -> torch.
 
 
 def fill_weights(d: int, n_kv_heads: int, head_dim: int, rms_eps: float, dtype, W_map, b_map, gamma, W_k, W_v,
-                 stream=None) -> FillWeights:
+                 stream=None, k_norm=None, k_norm_eps: float = 1e-6) -> FillWeights:
     """FillWeights from row-major weights: bf16 maps and projections are packed first (the
     fp32 path reads them as they are)."""
     if dtype == torch.bfloat16:
@@ -133,7 +133,7 @@ def fill_weights(d: int, n_kv_heads: int, head_dim: int, rms_eps: float, dtype, 
         W_k = [pack_weights(W, head_dim, stream) for W in W_k]
         W_v = [pack_weights(W, head_dim, stream) for W in W_v]
     return FillWeights(d, n_kv_heads, head_dim, rms_eps, dtype, list(W_map), list(b_map), list(gamma), list(W_k),
-                       list(W_v))
+                       list(W_v), None if k_norm is None else list(k_norm), k_norm_eps)
 
 
 class Filler:
@@ -153,14 +153,15 @@ class Filler:
 
 
 def translate_weights(d_in: int, n_kv_heads: int, head_dim: int, dtype, T_k, T_v, b_k=None, b_v=None,
-                      stream=None, headwise: bool = False) -> TranslateWeights:
+                      stream=None, headwise: bool = False, k_norm=None, k_norm_eps: float = 1e-6) -> TranslateWeights:
     """TranslateWeights from row-major [kv_width, d_in] maps: for bf16 they are packed first
     (fp32 maps are rounded to bf16 by the packing); the fp32 path reads them as they are."""
     if dtype == torch.bfloat16:
         T_k = [pack_weights(T, head_dim, stream) for T in T_k]
         T_v = [pack_weights(T, head_dim, stream) for T in T_v]
     return TranslateWeights(d_in, n_kv_heads, head_dim, dtype, list(T_k), list(T_v),
-                            None if b_k is None else list(b_k), None if b_v is None else list(b_v), headwise)
+                            None if b_k is None else list(b_k), None if b_v is None else list(b_v), headwise,
+                            None if k_norm is None else list(k_norm), k_norm_eps)
 
 
 class Translator:

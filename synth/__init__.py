@@ -227,6 +227,12 @@ def kv_weights(cfg: Config, layer: int, device="cpu"):
     return _store(Wk, cfg), _store(Wv, cfg), gamma.float().contiguous()
 
 
+def key_norm_weights(cfg, layer: int, device="cpu") -> torch.Tensor:
+    """Per-head key norm weights gamma_k [head_dim] = 1 + N(0, 0.1^2), fp32 (for models that
+    normalise keys per head)."""
+    return (1.0 + 0.1 * _randn((cfg.head_dim,), cfg.seed, "gk", layer, device=device)).contiguous()
+
+
 def random_map(cfg: Config, layer: int, device="cpu"):
     """Random-init map centred on the identity fill: W = I + N(0, 0.02^2), b ~ N(0, 0.02^2)."""
     W = 0.02 * _randn((cfg.d, cfg.d), cfg.seed, "Wmap", layer, device=device)

@@ -39,6 +39,7 @@ class FillCase:
     sample: Optional[Sequence[int]] = None     # token indices to compare (None = all filled)
     gen_device: str = "cpu"                    # where inputs are drawn
     max_tokens: Optional[int] = None
+    k_norm: bool = False                       # per-head key norm (gamma_k, eps 1e-6)
 
 
 def run_fill_case(case: FillCase, device="cuda"):
@@ -55,9 +56,11 @@ def run_fill_case(case: FillCase, device="cuda"):
     lws = [synth.layer_weights(cfg, l, device=gd, maps=case.maps) for l in layers]
     lws_dev = [synth.LayerWeights(*(x.to(device) for x in (w.W_map, w.b_map, w.gamma, w.W_k, w.W_v))) for w in lws]
     X = synth.hidden_states(cfg, case.t1 - case.t0, "prompt", device=gd).to(device)
+    gks = [synth.key_norm_weights(cfg, l) for l in layers] if case.k_norm else None
     fw = fill_weights(cfg.d, cfg.n_kv_heads, cfg.head_dim, cfg.rms_eps, cfg.torch_dtype,
                       [w.W_map for w in lws_dev], [w.b_map for w in lws_dev], [w.gamma for w in lws_dev],
-                      [w.W_k for w in lws_dev], [w.W_v for w in lws_dev])
+                      [w.W_k for w in lws_dev], [w.W_v for w in lws_dev],
+                      k_norm=None if gks is None else [gk.to(device) for gk in gks], k_norm_eps=1e-6)
     table = None
     if cfg.paged:
         table = synth.block_table(cfg, T, device=device)
@@ -78,7 +81,8 @@ def run_fill_case(case: FillCase, device="cuda"):
     for li, w in enumerate(lws):
         K_ref, V_ref = oracle.fill_layer(Xs, f64(w.W_map).T, f64(w.b_map), f64(w.gamma), f64(w.W_k).T,
                                          f64(w.W_v).T, case.pos0 + rows.astype(np.float64), cfg.n_kv_heads,
-                                         cfg.head_dim, cfg.rms_eps, cfg.rope_base)
+                                         cfg.head_dim, cfg.rms_eps, cfg.rope_base,
+                                         None if gks is None else f64(gks[li]), 1e-6)
         Kall = gather_rows(cache, cache.k[li], 0, T)
         Vall = gather_rows(cache, cache.v[li], 0, T)
         ridx = torch.as_tensor(rows, device=device)
@@ -184,6 +188,7 @@ class TranslateCase:
     n_layers: Optional[int] = None
     sample: Optional[Sequence[int]] = None     # token indices to compare (None = all translated)
     gen_device: str = "cpu"
+    k_norm: bool = False                       # the target's per-head key norm (eps 1e-6)
 
 
 def run_translate_case(case: TranslateCase, device="cuda"):
@@ -202,9 +207,11 @@ def run_translate_case(case: TranslateCase, device="cuda"):
     maps = [synth.translator_maps(cfg, l, device=gd) for l in range(n_tgt)]
     Kd, Vd = Ks.to(device), Vs.to(device)
     md = [tuple(None if x is None else x.to(device) for x in m) for m in maps]
+    gks = [synth.key_norm_weights(cfg, l) for l in range(n_tgt)] if case.k_norm else None
     tw = translate_weights(cfg.d_in, cfg.n_kv_heads, cfg.head_dim, cfg.torch_dtype, [m[0] for m in md],
                            [m[1] for m in md], [m[2] for m in md] if cfg.bias else None,
-                           [m[3] for m in md] if cfg.bias else None, headwise=cfg.maps == "headwise")
+                           [m[3] for m in md] if cfg.bias else None, headwise=cfg.maps == "headwise",
+                           k_norm=None if gks is None else [gk.to(device) for gk in gks], k_norm_eps=1e-6)
     table = synth.translate_block_table(cfg, T, device=device) if cfg.paged else None
     cache = alloc_cache(n_tgt, cfg.n_kv_heads, cfg.head_dim, T, cfg.torch_dtype, device, paged=cfg.paged,
                         block_size=cfg.block_size, block_table=table,
@@ -231,7 +238,7 @@ def run_translate_case(case: TranslateCase, device="cuda"):
                                               None if m[2] is None else f64(m[2]),
                                               None if m[3] is None else f64(m[3]),
                                               case.pos0 + rows.astype(np.float64), cfg.n_kv_heads, cfg.head_dim,
-                                              cfg.rope_base)
+                                              cfg.rope_base, None if gks is None else f64(gks[li]), 1e-6)
         Kall = gather_rows(cache, cache.k[li], 0, T)
         Vall = gather_rows(cache, cache.v[li], 0, T)
         di = torch.as_tensor(rows, device=device)

@@ -135,6 +135,12 @@ def _weights(d=256, H=4, dh=64, dtype=torch.float32, n=1, ptr=256):
     return rf.FillWeights(d, H, dh, 1e-6, dtype, [ptr] * n, [ptr] * n, [ptr] * n, [ptr] * n, [ptr] * n)
 
 
+def _weights_kn(eps, ptr=256):
+    w = _weights()
+    w.k_norm, w.k_norm_eps = [ptr], eps
+    return w
+
+
 def _aligned_bytes(n, a=256):
     buf = torch.empty(n + a, dtype=torch.uint8)
     off = (-buf.data_ptr()) % a
@@ -158,6 +164,8 @@ def test_fill_validation_before_enqueue():
         (dict(w=_weights(dtype=torch.bfloat16)), rf.RF_ERR_UNSUPPORTED),
         (dict(t1=513), rf.RF_ERR_INVALID_ARG),
         (dict(pos0=1), rf.RF_ERR_INVALID_ARG),  # rope table too short
+        (dict(w=_weights_kn(-1.0)), rf.RF_ERR_INVALID_ARG),   # negative key-norm epsilon
+        (dict(w=_weights_kn(1e-6, ptr=0)), rf.RF_ERR_INVALID_ARG),   # null key-norm weights
         (dict(ws_=_aligned_bytes(256)), rf.RF_ERR_WORKSPACE),
         (dict(cache_=rf.cache_desc(4, 64, 512, rf.RF_LAYOUT_PAGED, torch.float32)), rf.RF_ERR_INVALID_ARG),
     ]
@@ -229,6 +237,10 @@ def test_translate_validation_before_enqueue():
 
     w_half_bias = _tweights()
     w_half_bias.b_k = [256]
+    w_kn_eps = _tweights()
+    w_kn_eps.k_norm, w_kn_eps.k_norm_eps = [256], -1.0
+    w_kn_null = _tweights()
+    w_kn_null.k_norm = [0]
     cases = [
         (dict(t0=5, t1=4), rf.RF_ERR_INVALID_ARG),
         (dict(w=_tweights(d_in=96)), rf.RF_ERR_UNSUPPORTED),                 # F32: d_in % 64
@@ -242,6 +254,8 @@ def test_translate_validation_before_enqueue():
         (dict(src=260), rf.RF_ERR_INVALID_ARG),                              # misaligned source
         (dict(src=0), rf.RF_ERR_INVALID_ARG),
         (dict(w=w_half_bias), rf.RF_ERR_INVALID_ARG),                        # only b_k given
+        (dict(w=w_kn_eps), rf.RF_ERR_INVALID_ARG),                           # negative key-norm epsilon
+        (dict(w=w_kn_null), rf.RF_ERR_INVALID_ARG),                          # null key-norm weights
         (dict(cache_=rf.cache_desc(4, 64, 512, rf.RF_LAYOUT_PAGED, torch.float32)), rf.RF_ERR_INVALID_ARG),
     ]
     for kw, status in cases:

@@ -51,6 +51,15 @@ def test_fill_paged_chunked_unaligned():
     _check(run_fill_case(FillCase(SMALL_PAGED, 19, 1100, chunk=300)), "paged chunked")
 
 
+def test_fill_per_head_key_norm():
+    # keys normalised per head before the rotation (head_dim 128: the head spans two waves of a
+    # tile; 64: one wave), bf16 and fp32
+    _check(run_fill_case(FillCase(SMALL_BF16, 37, 737, pos0=5, k_norm=True)), "bf16 dh128 key norm")
+    _check(run_fill_case(FillCase(SMALL_BF16_H64, 3, 517, maps="random", k_norm=True)), "bf16 dh64 key norm")
+    _check(run_fill_case(FillCase(synth.C1, 0, 512, k_norm=True)), "C1 fp32 key norm")
+    _check(run_fill_case(FillCase(SMALL_PAGED, 19, 1100, chunk=300, k_norm=True)), "paged key norm")
+
+
 def test_fill_single_token_and_tile_edges():
     for t0, t1 in [(5, 6), (0, 256), (255, 257), (511, 769)]:
         _check(run_fill_case(FillCase(SMALL_BF16, t0, t1, n_layers=1)), f"rows [{t0},{t1})")

@@ -71,6 +71,16 @@ def test_translate_headwise_two_sources_paged_and_head_dim_64():
                                             0, 300)), "fp32 head-wise nu=2")
 
 
+def test_translate_target_key_norm():
+    # pre-norm storing for targets that normalise keys per head: map, key norm, rotation;
+    # dense and head-wise, head_dim 128 and 64, fp32
+    _check(run_translate_case(TranslateCase(SMALL_PAGED, 37, 737, pos0=11, chunk=300, k_norm=True)),
+           "bf16 key norm paged")
+    _check(run_translate_case(TranslateCase(SMALL_HEADWISE, 0, 800, k_norm=True)), "bf16 head-wise key norm")
+    _check(run_translate_case(TranslateCase(SMALL_DH64, 0, 600, pos0=130000, k_norm=True)), "bf16 dh64 key norm")
+    _check(run_translate_case(TranslateCase(TINY_F32, 0, 300, k_norm=True)), "fp32 key norm")
+
+
 def test_translate_bf16_head_dim_64_far_positions():
     # target heads of 64 from a 2 x 128 source, RoPE at positions near 131072
     _check(run_translate_case(TranslateCase(SMALL_DH64, 0, 600, pos0=130000)), "bf16 dh64 far pos")
