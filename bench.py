@@ -10,9 +10,10 @@ Default workload: the Llama-8B-shaped configuration (d=4096, 32 layers split at 
 
 Prints one JSON line.  ``value`` is filled tokens per second of fill time; the fit's rows
 per second, per-phase times, the dominant kernel's roofline and the CPU oracle baseline ride
-along.  After the timed steps, and outside them, the token-wise cache translators (KV-Lingo
-page, section 3.1) are timed on their own workload (28 -> 36 layers of 8 x 128 KV heads,
-two source layers per target layer, 16384 tokens) and reported under ``translate``.
+along.  After the timed steps, and outside them, the fill is timed once more with its maps streamed
+from page-locked host memory (``fill_streamed``), and the token-wise cache translators
+(KV-Lingo page, section 3.1) are timed on their own workload (28 -> 36 layers of 8 x 128 KV
+heads, two source layers per target layer, 16384 tokens) and reported under ``translate``.
 Progress goes to stderr.
 """
 from __future__ import annotations
@@ -100,6 +101,44 @@ def cpu_baseline(cfg, n_tokens: int, n_fit_rows: int):
     }
 
 
+def streamed_leg(steps: int, stream, dev, cfg, fw, Xp, cache, filler, ring_slots=2, layers_per_slot=2):
+    """The same fill with its maps streamed from page-locked host memory (rf_fill_streamed),
+    alternated with the resident fill so both see the same clock and power state."""
+    import dataclasses
+
+    import torch
+
+    from linear_kv_cache_amd.runner import StreamedFiller, pinned_copy
+
+    T, L = cfg.fill_tokens, cfg.n_targets
+    host = [pinned_copy(W.cpu()) for W in fw.W_map]
+    sw = dataclasses.replace(fw, W_map=host)
+    sf = StreamedFiller(sw, cfg.rope_base, T, T, dev, ring_slots=ring_slots, layers_per_slot=layers_per_slot)
+
+    def timed(f):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        f.fill(Xp, 0, T, 0, cache, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    timed(sf)
+    res_ms, str_ms = [], []
+    for _ in range(steps):
+        res_ms.append(timed(filler))
+        str_ms.append(timed(sf))
+    rm, sm = statistics.median(res_ms), statistics.median(str_ms)
+    map_bytes = L * cfg.d * cfg.d * 2
+    return {"what": "rf_fill with the maps in page-locked host memory, streamed through a device ring; "
+                    "alternated with the resident fill", "ring_slots": ring_slots, "layers_per_slot": layers_per_slot,
+            "ring_MiB": round(ring_slots * layers_per_slot * cfg.d * cfg.d * 2 / 2 ** 20, 1),
+            "resident_maps_MiB": round(map_bytes / 2 ** 20, 1),
+            "ms_median": round(sm, 3), "resident_ms_median": round(rm, 3),
+            "tokens_per_s": round(T / (sm / 1e3), 1), "vs_resident": round(rm / sm, 4),
+            "host_to_device_GBps": round(map_bytes / (sm / 1e3) / 1e9, 1)}
+
+
 def translate_leg(steps: int, stream, dev, tc=None):
     """Time rf_translate over every target layer of the translation workload, in one call."""
     import torch
@@ -166,6 +205,7 @@ def main():
                     help="also time the fill's two products per layer as plain torch.matmul (hipBLASLt) "
                          "GEMMs on the same maps, projections and prompt states")
     ap.add_argument("--no-translate", action="store_true", help="skip the cache-translator leg")
+    ap.add_argument("--no-streamed", action="store_true", help="skip the streamed-maps leg")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 1 GiB device-to-device copy before the steps, a known-size reference "
                          "for HBM byte counters")
@@ -341,6 +381,9 @@ def main():
             "fused_fill_ms_median": round(fms, 3),
             "fused_fill_frac_bf16_peak": round(fill_flop / (fms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
         del Wt, Wkv, H, KV
+    if not args.no_streamed:
+        log("streamed maps: the fill with its maps in page-locked host memory")
+        out["fill_streamed"] = streamed_leg(args.steps, stream, dev, cfg, fw, Xp, cache, filler)
     if not args.no_translate:
         del Xc, Yc
         out["translate"] = translate_leg(args.steps, stream, dev)

@@ -293,6 +293,35 @@ rf_status rf_fill(const rf_fill_weights* weights, int32_t n_layers,
                   void* d_ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Streamed maps.  RidgeFill project page, Figure 10 and Table 8 ("streamed"): the ridge maps
+ * stay in host memory and reach the GPU layer by layer while the fill runs, for far less
+ * device memory than resident maps at nearly the same speed.  Computes exactly what rf_fill
+ * computes (the same kernels, bit-identical results), with W_map[l] HOST pointers to the
+ * maps in the layout rf_fill takes (BF16 packed), in page-locked memory (hipHostMalloc) so
+ * the copies run asynchronously.  Every other weight is a device pointer as for rf_fill.
+ *  d_ring      : device buffer of ring_bytes >= rf_fill_streamed_ring_bytes() bytes, 256-B
+ *                aligned: ring_slots slots of layers_per_slot maps
+ *  d_ws        : rf_fill_workspace_bytes(weights, t1 - t0) * layers_per_slot bytes
+ *  copy_stream : a stream other than ``stream`` (hipStream_t) for the host-to-device copies
+ * Layers go in chunks of layers_per_slot (1..32): chunk c is copied into slot
+ * c % ring_slots on copy_stream once the fill of chunk c - ring_slots has left that slot, and
+ * filled on ``stream`` once its copy has landed (HIP events order the two streams; they are
+ * created and released inside the call).  Two or more slots let the copy of one chunk run
+ * under the fill of the previous one.  The host maps must stay valid until ``stream``
+ * reaches the end of the call's work.
+ * ------------------------------------------------------------------------------------- */
+size_t rf_fill_streamed_ring_bytes(const rf_fill_weights* weights, int32_t ring_slots, int32_t layers_per_slot);
+rf_status rf_fill_streamed(const rf_fill_weights* weights, int32_t n_layers,
+                           const void* d_X, int64_t ldx,
+                           int64_t t0, int64_t t1, int64_t pos0,
+                           const rf_cache_desc* cache, void* const* k_cache, void* const* v_cache,
+                           const int32_t* d_block_table, int64_t n_table_blocks,
+                           const float* d_rope, int64_t rope_len,
+                           void* d_ws, size_t ws_bytes,
+                           void* d_ring, size_t ring_bytes, int32_t ring_slots, int32_t layers_per_slot,
+                           void* stream, void* copy_stream);
+
+/* ---------------------------------------------------------------------------------------
  * Token-wise linear KV-cache translators.  KV-Lingo page, section 3.1 "Linear translator
  * family": each target layer l has its own linear map for keys and its own for values, both
  * reading the cache rows of a set of nu source layers; with pre-norm storing the maps act on

@@ -14,6 +14,9 @@
 // a head's RoPE partners sit in the same lane and register, one block apart.
 #include <math.h>
 
+#include <string>
+#include <vector>
+
 #include "rf_internal.h"
 #include "rf_mfma.h"
 #include "rf_pipe.h"
@@ -716,65 +719,185 @@ size_t rf_fill_workspace_bytes(const rf_fill_weights* w, int64_t max_rows) {
     return slot_bytes(w, max_rows);
 }
 
+}  // extern "C"
+
+namespace rf {
+// Host checks shared by rf_fill and rf_fill_streamed ("what" names the entry point).  Sets
+// *nothing_to_do for an empty request; ws_need is the workspace the launch needs.
+static rf_status check_fill(const char* what, const rf_fill_weights* w, int32_t n_layers, const void* d_X,
+                            int64_t ldx, int64_t t0, int64_t t1, int64_t pos0, const rf_cache_desc* cache,
+                            void* const* k_cache, void* const* v_cache, const int32_t* d_block_table,
+                            int64_t n_table_blocks, const float* d_rope, int64_t rope_len, const void* d_ws,
+                            size_t ws_bytes, size_t ws_need, rf_cache_layout_t& L, bool& nothing_to_do) {
+    const std::string fn = what;
+    nothing_to_do = false;
+    RF_REQUIRE(w && cache, RF_ERR_INVALID_ARG, fn + ": null weights or cache descriptor");
+    RF_REQUIRE(n_layers >= 0, RF_ERR_INVALID_ARG, fn + ": n_layers must be >= 0");
+    RF_REQUIRE(t0 >= 0 && t1 >= t0 && pos0 >= 0, RF_ERR_INVALID_ARG, fn + ": need 0 <= t0 <= t1 and pos0 >= 0");
+    RF_REQUIRE(valid_dtype(w->dtype), RF_ERR_INVALID_ARG, fn + ": bad dtype");
+    RF_REQUIRE(cache->dtype == w->dtype, RF_ERR_UNSUPPORTED, fn + ": cache dtype must equal the weights' dtype");
+    RF_REQUIRE(w->d > 0 && w->d % kFT == 0, RF_ERR_UNSUPPORTED, fn + ": d must be a positive multiple of 256");
+    RF_REQUIRE(w->head_dim == 64 || w->head_dim == 128, RF_ERR_UNSUPPORTED, fn + ": head_dim must be 64 or 128");
+    RF_REQUIRE(w->n_kv_heads > 0 && (w->n_kv_heads * w->head_dim) % kFT == 0, RF_ERR_UNSUPPORTED,
+               fn + ": n_kv_heads*head_dim must be a positive multiple of 256");
+    RF_REQUIRE(cache->n_kv_heads == w->n_kv_heads && cache->head_dim == w->head_dim, RF_ERR_INVALID_ARG,
+               fn + ": cache heads/head_dim differ from the weights'");
+    RF_REQUIRE(w->rms_eps >= 0.f && isfinite(w->rms_eps), RF_ERR_INVALID_ARG, fn + ": rms_eps must be finite and >= 0");
+    RF_REQUIRE(!w->k_norm || (w->k_norm_eps >= 0.f && isfinite(w->k_norm_eps)), RF_ERR_INVALID_ARG,
+               fn + ": k_norm_eps must be finite and >= 0");
+    rf_status st = rf_cache_layout(cache, &L);
+    if (st != RF_OK) return st;
+    if (n_layers == 0 || t1 == t0) {
+        nothing_to_do = true;
+        return RF_OK;
+    }
+    RF_REQUIRE(d_X && w->W_map && w->b_map && w->gamma && w->W_k && w->W_v && k_cache && v_cache && d_rope && d_ws,
+               RF_ERR_INVALID_ARG, fn + ": null pointer argument");
+    const size_t eb = elem_bytes(w->dtype);
+    RF_REQUIRE(ldx >= w->d && (ldx * (int64_t)eb) % 16 == 0 && aligned(d_X, 16), RF_ERR_INVALID_ARG,
+               fn + ": X rows must be >= d long, 16-byte aligned with a 16-byte multiple stride");
+    RF_REQUIRE(ldx <= (1 << 21) && w->d <= (1 << 16), RF_ERR_UNSUPPORTED,
+               fn + ": ldx must be <= 2^21 and d <= 65536 (32-bit tile offsets)");
+    for (int l = 0; l < n_layers; ++l) {
+        RF_REQUIRE(w->W_map[l] && w->b_map[l] && w->gamma[l] && w->W_k[l] && w->W_v[l] && k_cache[l] && v_cache[l],
+                   RF_ERR_INVALID_ARG, fn + ": null per-layer pointer");
+        RF_REQUIRE(aligned(w->W_map[l], 16) && aligned(w->W_k[l], 16) && aligned(w->W_v[l], 16) &&
+                       aligned(w->b_map[l], 16) && aligned(w->gamma[l], 16) && aligned(k_cache[l], 16) &&
+                       aligned(v_cache[l], 16),
+                   RF_ERR_INVALID_ARG, fn + ": per-layer buffers must be 16-byte aligned");
+        if (w->k_norm)
+            RF_REQUIRE(w->k_norm[l] && aligned(w->k_norm[l], 16), RF_ERR_INVALID_ARG,
+                       fn + ": key norm weights must be non-null and 16-byte aligned");
+    }
+    RF_REQUIRE(aligned(d_rope, 16) && aligned(d_ws, 256), RF_ERR_INVALID_ARG,
+               fn + ": rope table must be 16-byte and workspace 256-byte aligned");
+    RF_REQUIRE(pos0 + t1 <= rope_len, RF_ERR_INVALID_ARG, fn + ": rope table shorter than pos0 + t1");
+    if (cache->layout == RF_LAYOUT_PAGED) {
+        RF_REQUIRE(d_block_table, RF_ERR_INVALID_ARG, fn + ": paged cache needs a block table");
+        RF_REQUIRE(ceil_div(t1, cache->block_size) <= n_table_blocks, RF_ERR_INVALID_ARG,
+                   fn + ": block table shorter than ceil(t1 / block_size)");
+    } else {
+        RF_REQUIRE(t1 <= cache->max_tokens, RF_ERR_INVALID_ARG, fn + ": t1 exceeds the cache's max_tokens");
+    }
+    RF_REQUIRE(ws_bytes >= ws_need, RF_ERR_WORKSPACE, fn + ": workspace too small");
+    return RF_OK;
+}
+
+// The maps of a streamed fill, layers_per_slot layers per ring slot: copy chunk c into slot
+// c % ring_slots on copy_stream once the fill of chunk c - ring_slots has released the slot,
+// and fill chunk c on stream once its copy has landed.  The events only order the two
+// streams; they are released when the work they mark completes.
+template <typename T>
+static rf_status launch_fill_streamed(const rf_fill_weights* w, int32_t n_layers, const void* X, int64_t ldx,
+                                      int64_t t0, int64_t t1, int64_t pos0, const rf_cache_desc* cache,
+                                      const rf_cache_layout_t& L, void* const* kc, void* const* vc,
+                                      const int32_t* table, int64_t n_table, const float* rope, void* ws,
+                                      size_t ws_bytes, void* ring, int32_t ring_slots, int32_t per_slot,
+                                      hipStream_t stream, hipStream_t copy_stream) {
+    const size_t map_bytes = (size_t)w->d * w->d * sizeof(T);
+    std::vector<hipEvent_t> copied(ring_slots, nullptr), freed(ring_slots, nullptr);
+    rf_status st = RF_OK;
+    auto destroy = [&]() {
+        for (auto& e : copied)
+            if (e) (void)hipEventDestroy(e);
+        for (auto& e : freed)
+            if (e) (void)hipEventDestroy(e);
+    };
+    for (int i = 0; i < ring_slots; ++i) {
+        if (hipEventCreateWithFlags(&copied[i], hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&freed[i], hipEventDisableTiming) != hipSuccess) {
+            destroy();
+            return fail(RF_ERR_HIP, "rf_fill_streamed: event creation failed");
+        }
+    }
+    const void* maps[kMaxGroup];
+    rf_fill_weights cw = *w;
+    cw.W_map = maps;
+    const int n_chunks = (int)ceil_div(n_layers, per_slot);
+    for (int c = 0; c < n_chunks && st == RF_OK; ++c) {
+        const int slot = c % ring_slots;
+        const int l0 = c * per_slot, gsz = std::min(per_slot, n_layers - l0);
+        char* base = (char*)ring + (size_t)slot * per_slot * map_bytes;
+        hipError_t e = hipSuccess;
+        if (c >= ring_slots) e = hipStreamWaitEvent(copy_stream, freed[slot], 0);
+        for (int g = 0; g < gsz && e == hipSuccess; ++g) {
+            maps[g] = base + (size_t)g * map_bytes;
+            e = hipMemcpyAsync((void*)maps[g], w->W_map[l0 + g], map_bytes, hipMemcpyHostToDevice, copy_stream);
+        }
+        if (e == hipSuccess) e = hipEventRecord(copied[slot], copy_stream);
+        if (e == hipSuccess) e = hipStreamWaitEvent(stream, copied[slot], 0);
+        if (e != hipSuccess) {
+            st = fail(RF_ERR_HIP, std::string("rf_fill_streamed: copy scheduling failed: ") + hipGetErrorString(e));
+            break;
+        }
+        cw.b_map = w->b_map + l0; cw.gamma = w->gamma + l0; cw.W_k = w->W_k + l0; cw.W_v = w->W_v + l0;
+        cw.k_norm = w->k_norm ? w->k_norm + l0 : nullptr;
+        st = launch_fill<T>(&cw, gsz, X, ldx, t0, t1, pos0, cache, L, kc + l0, vc + l0, table, n_table, rope, ws,
+                            ws_bytes, stream);
+        if (st == RF_OK && hipEventRecord(freed[slot], stream) != hipSuccess)
+            st = fail(RF_ERR_HIP, "rf_fill_streamed: event record failed");
+    }
+    destroy();
+    return st;
+}
+}  // namespace rf
+
+extern "C" {
+
 rf_status rf_fill(const rf_fill_weights* w, int32_t n_layers, const void* d_X, int64_t ldx,
                   int64_t t0, int64_t t1, int64_t pos0, const rf_cache_desc* cache,
                   void* const* k_cache, void* const* v_cache, const int32_t* d_block_table,
                   int64_t n_table_blocks, const float* d_rope, int64_t rope_len, void* d_ws,
                   size_t ws_bytes, void* stream) {
     clear_error();
-    RF_REQUIRE(w && cache, RF_ERR_INVALID_ARG, "rf_fill: null weights or cache descriptor");
-    RF_REQUIRE(n_layers >= 0, RF_ERR_INVALID_ARG, "rf_fill: n_layers must be >= 0");
-    RF_REQUIRE(t0 >= 0 && t1 >= t0 && pos0 >= 0, RF_ERR_INVALID_ARG, "rf_fill: need 0 <= t0 <= t1 and pos0 >= 0");
-    RF_REQUIRE(valid_dtype(w->dtype), RF_ERR_INVALID_ARG, "rf_fill: bad dtype");
-    RF_REQUIRE(cache->dtype == w->dtype, RF_ERR_UNSUPPORTED, "rf_fill: cache dtype must equal the weights' dtype");
-    RF_REQUIRE(w->d > 0 && w->d % kFT == 0, RF_ERR_UNSUPPORTED, "rf_fill: d must be a positive multiple of 256");
-    RF_REQUIRE(w->head_dim == 64 || w->head_dim == 128, RF_ERR_UNSUPPORTED, "rf_fill: head_dim must be 64 or 128");
-    RF_REQUIRE(w->n_kv_heads > 0 && (w->n_kv_heads * w->head_dim) % kFT == 0, RF_ERR_UNSUPPORTED,
-               "rf_fill: n_kv_heads*head_dim must be a positive multiple of 256");
-    RF_REQUIRE(cache->n_kv_heads == w->n_kv_heads && cache->head_dim == w->head_dim, RF_ERR_INVALID_ARG,
-               "rf_fill: cache heads/head_dim differ from the weights'");
-    RF_REQUIRE(w->rms_eps >= 0.f && isfinite(w->rms_eps), RF_ERR_INVALID_ARG, "rf_fill: rms_eps must be finite and >= 0");
-    RF_REQUIRE(!w->k_norm || (w->k_norm_eps >= 0.f && isfinite(w->k_norm_eps)), RF_ERR_INVALID_ARG,
-               "rf_fill: k_norm_eps must be finite and >= 0");
     rf_cache_layout_t L;
-    rf_status st = rf_cache_layout(cache, &L);
-    if (st != RF_OK) return st;
-    if (n_layers == 0 || t1 == t0) return RF_OK;
-    RF_REQUIRE(d_X && w->W_map && w->b_map && w->gamma && w->W_k && w->W_v && k_cache && v_cache && d_rope && d_ws,
-               RF_ERR_INVALID_ARG, "rf_fill: null pointer argument");
-    const size_t eb = elem_bytes(w->dtype);
-    RF_REQUIRE(ldx >= w->d && (ldx * (int64_t)eb) % 16 == 0 && aligned(d_X, 16), RF_ERR_INVALID_ARG,
-               "rf_fill: X rows must be >= d long, 16-byte aligned with a 16-byte multiple stride");
-    RF_REQUIRE(ldx <= (1 << 21) && w->d <= (1 << 16), RF_ERR_UNSUPPORTED,
-               "rf_fill: ldx must be <= 2^21 and d <= 65536 (32-bit tile offsets)");
-    for (int l = 0; l < n_layers; ++l) {
-        RF_REQUIRE(w->W_map[l] && w->b_map[l] && w->gamma[l] && w->W_k[l] && w->W_v[l] && k_cache[l] && v_cache[l],
-                   RF_ERR_INVALID_ARG, "rf_fill: null per-layer pointer");
-        RF_REQUIRE(aligned(w->W_map[l], 16) && aligned(w->W_k[l], 16) && aligned(w->W_v[l], 16) &&
-                       aligned(w->b_map[l], 16) && aligned(w->gamma[l], 16) && aligned(k_cache[l], 16) &&
-                       aligned(v_cache[l], 16),
-                   RF_ERR_INVALID_ARG, "rf_fill: per-layer buffers must be 16-byte aligned");
-        if (w->k_norm)
-            RF_REQUIRE(w->k_norm[l] && aligned(w->k_norm[l], 16), RF_ERR_INVALID_ARG,
-                       "rf_fill: key norm weights must be non-null and 16-byte aligned");
-    }
-    RF_REQUIRE(aligned(d_rope, 16) && aligned(d_ws, 256), RF_ERR_INVALID_ARG,
-               "rf_fill: rope table must be 16-byte and workspace 256-byte aligned");
-    RF_REQUIRE(pos0 + t1 <= rope_len, RF_ERR_INVALID_ARG, "rf_fill: rope table shorter than pos0 + t1");
-    if (cache->layout == RF_LAYOUT_PAGED) {
-        RF_REQUIRE(d_block_table, RF_ERR_INVALID_ARG, "rf_fill: paged cache needs a block table");
-        RF_REQUIRE(ceil_div(t1, cache->block_size) <= n_table_blocks, RF_ERR_INVALID_ARG,
-                   "rf_fill: block table shorter than ceil(t1 / block_size)");
-    } else {
-        RF_REQUIRE(t1 <= cache->max_tokens, RF_ERR_INVALID_ARG, "rf_fill: t1 exceeds the cache's max_tokens");
-    }
-    RF_REQUIRE(ws_bytes >= slot_bytes(w, t1 - t0), RF_ERR_WORKSPACE, "rf_fill: workspace too small");
+    bool none;
+    const size_t need = (w && w->d > 0 && w->d % kFT == 0 && t1 >= t0) ? slot_bytes(w, t1 - t0) : 0;
+    const rf_status st = check_fill("rf_fill", w, n_layers, d_X, ldx, t0, t1, pos0, cache, k_cache, v_cache,
+                                    d_block_table, n_table_blocks, d_rope, rope_len, d_ws, ws_bytes, need, L, none);
+    if (st != RF_OK || none) return st;
     hipStream_t s = (hipStream_t)stream;
     if (w->dtype == RF_BF16)
         return launch_fill<bf16_t>(w, n_layers, d_X, ldx, t0, t1, pos0, cache, L, k_cache, v_cache, d_block_table,
                                    n_table_blocks, d_rope, d_ws, ws_bytes, s);
     return launch_fill<float>(w, n_layers, d_X, ldx, t0, t1, pos0, cache, L, k_cache, v_cache, d_block_table,
                               n_table_blocks, d_rope, d_ws, ws_bytes, s);
+}
+
+size_t rf_fill_streamed_ring_bytes(const rf_fill_weights* w, int32_t ring_slots, int32_t layers_per_slot) {
+    if (!w || w->d <= 0 || w->d % kFT != 0 || !valid_dtype(w->dtype) || ring_slots < 1 || layers_per_slot < 1)
+        return 0;
+    return (size_t)ring_slots * layers_per_slot * w->d * w->d * elem_bytes(w->dtype);
+}
+
+rf_status rf_fill_streamed(const rf_fill_weights* w, int32_t n_layers, const void* d_X, int64_t ldx,
+                           int64_t t0, int64_t t1, int64_t pos0, const rf_cache_desc* cache,
+                           void* const* k_cache, void* const* v_cache, const int32_t* d_block_table,
+                           int64_t n_table_blocks, const float* d_rope, int64_t rope_len, void* d_ws,
+                           size_t ws_bytes, void* d_ring, size_t ring_bytes, int32_t ring_slots,
+                           int32_t layers_per_slot, void* stream, void* copy_stream) {
+    clear_error();
+    RF_REQUIRE(ring_slots >= 1 && layers_per_slot >= 1 && layers_per_slot <= kMaxGroup, RF_ERR_INVALID_ARG,
+               "rf_fill_streamed: need ring_slots >= 1 and 1 <= layers_per_slot <= 32");
+    rf_cache_layout_t L;
+    bool none;
+    const size_t need = (w && w->d > 0 && w->d % kFT == 0 && t1 >= t0) ? slot_bytes(w, t1 - t0) * layers_per_slot : 0;
+    rf_status st = check_fill("rf_fill_streamed", w, n_layers, d_X, ldx, t0, t1, pos0, cache, k_cache, v_cache,
+                              d_block_table, n_table_blocks, d_rope, rope_len, d_ws, ws_bytes, need, L, none);
+    if (st != RF_OK || none) return st;
+    RF_REQUIRE(copy_stream && copy_stream != stream, RF_ERR_INVALID_ARG,
+               "rf_fill_streamed: the copies need a stream of their own");
+    RF_REQUIRE(d_ring && aligned(d_ring, 256), RF_ERR_INVALID_ARG, "rf_fill_streamed: ring must be 256-byte aligned");
+    RF_REQUIRE(ring_bytes >= rf_fill_streamed_ring_bytes(w, ring_slots, layers_per_slot), RF_ERR_WORKSPACE,
+               "rf_fill_streamed: ring too small");
+    hipStream_t s = (hipStream_t)stream, cs = (hipStream_t)copy_stream;
+    if (w->dtype == RF_BF16)
+        return launch_fill_streamed<bf16_t>(w, n_layers, d_X, ldx, t0, t1, pos0, cache, L, k_cache, v_cache,
+                                            d_block_table, n_table_blocks, d_rope, d_ws, ws_bytes, d_ring, ring_slots,
+                                            layers_per_slot, s, cs);
+    return launch_fill_streamed<float>(w, n_layers, d_X, ldx, t0, t1, pos0, cache, L, k_cache, v_cache,
+                                       d_block_table, n_table_blocks, d_rope, d_ws, ws_bytes, d_ring, ring_slots,
+                                       layers_per_slot, s, cs);
 }
 
 rf_status rf_translate(const rf_translate_weights* w, int32_t n_layers, const void* const* d_src_k,

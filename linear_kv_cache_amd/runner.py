@@ -8,7 +8,8 @@ from typing import List, Optional, Sequence
 import torch
 
 from . import (RF_LAYOUT_CONTIGUOUS, RF_LAYOUT_PAGED, FillWeights, TranslateWeights, cache_desc, gram_desc,
-               rf_cache_layout, rf_fill, rf_fill_workspace_bytes, rf_fit_r2, rf_fit_r2_workspace_bytes,
+               rf_cache_layout, rf_fill, rf_fill_streamed, rf_fill_streamed_ring_bytes, rf_fill_workspace_bytes,
+               rf_fit_r2, rf_fit_r2_workspace_bytes,
                rf_gram_accumulate, rf_gram_init,
                rf_gram_state_bytes, rf_gram_state_layout, rf_pack_weights, rf_rope_table, rf_solve,
                rf_solve_workspace_bytes, rf_translate)
@@ -150,6 +151,30 @@ class Filler:
     def fill(self, X, t0: int, t1: int, pos0: int, cache: Cache, stream=None):
         rf_fill(self.w, X, t0, t1, pos0, cache.desc, cache.k, cache.v, cache.block_table, self.rope,
                 self.rope_len, self.ws, stream)
+
+
+class StreamedFiller(Filler):
+    """A Filler whose maps stay in page-locked host memory and stream through a device ring
+    (rf_fill_streamed); the workspace holds ``layers_per_slot`` layer slots."""
+
+    def __init__(self, weights: FillWeights, rope_base: float, max_pos: int, max_rows: int, device,
+                 ring_slots: int = 2, layers_per_slot: int = 1, stream=None):
+        super().__init__(weights, rope_base, max_pos, max_rows, device, ws_slots=layers_per_slot, stream=stream)
+        self.ring_slots, self.layers_per_slot = ring_slots, layers_per_slot
+        self.ring = device_bytes(rf_fill_streamed_ring_bytes(weights, ring_slots, layers_per_slot), device)
+        self.copy_stream = torch.cuda.Stream(device=device)
+
+    def fill(self, X, t0: int, t1: int, pos0: int, cache: Cache, stream=None):
+        rf_fill_streamed(self.w, X, t0, t1, pos0, cache.desc, cache.k, cache.v, cache.block_table, self.rope,
+                         self.rope_len, self.ws, self.ring, self.ring_slots, self.layers_per_slot,
+                         stream if stream is not None else torch.cuda.current_stream(), self.copy_stream)
+
+
+def pinned_copy(t: torch.Tensor) -> torch.Tensor:
+    """A page-locked host copy of a tensor (allocated pinned, then filled)."""
+    out = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+    out.copy_(t)
+    return out
 
 
 def translate_weights(d_in: int, n_kv_heads: int, head_dim: int, dtype, T_k, T_v, b_k=None, b_v=None,

@@ -79,3 +79,53 @@ def test_fill_is_deterministic():
         outs.append(torch.cat(cache.k + cache.v))
     torch.cuda.synchronize()
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
+def test_fill_streamed_maps_match_resident():
+    # maps in page-locked host memory streamed through a device ring: the same kernels on the
+    # same data, so the caches equal the resident fill's bit for bit; checked against the
+    # oracle too.  Ring reuse (3 chunks in 2 slots), one slot (copies wait for each fill),
+    # chunks of 2 layers; bf16 packed and fp32 maps; paged and contiguous
+    from linear_kv_cache_amd.runner import (Filler, StreamedFiller, alloc_cache, fill_weights, gather_rows,
+                                            pinned_copy)
+    import oracle
+    from gpu_cases import f64
+    for cfg, t0, t1, slots, per, paged in [(SMALL_BF16, 37, 737, 2, 1, False), (synth.C1, 0, 512, 1, 3, False),
+                                           (SMALL_PAGED, 19, 1100, 2, 2, True)]:
+        layers = cfg.filled_layers
+        ws = [synth.layer_weights(cfg, l, device="cuda") for l in layers]
+        fw = fill_weights(cfg.d, cfg.n_kv_heads, cfg.head_dim, cfg.rms_eps, cfg.torch_dtype, [w.W_map for w in ws],
+                          [w.b_map for w in ws], [w.gamma for w in ws], [w.W_k for w in ws], [w.W_v for w in ws])
+        host = [pinned_copy(W.cpu()) for W in fw.W_map]
+        fs = fill_weights(cfg.d, cfg.n_kv_heads, cfg.head_dim, cfg.rms_eps, cfg.torch_dtype, [w.W_map for w in ws],
+                          [w.b_map for w in ws], [w.gamma for w in ws], [w.W_k for w in ws], [w.W_v for w in ws])
+        fs.W_map = host
+        T = max(t1, cfg.prompt_tokens)
+        X = synth.hidden_states(cfg, t1 - t0, "prompt", device="cuda")
+        table = synth.block_table(cfg, T, device="cuda") if paged else None
+        nb = int(table.max()) + 1 if paged else None
+        outs = []
+        for filler in (Filler(fw, cfg.rope_base, T, t1 - t0, "cuda"),
+                       StreamedFiller(fs, cfg.rope_base, T, t1 - t0, "cuda", ring_slots=slots, layers_per_slot=per)):
+            cache = alloc_cache(len(layers), cfg.n_kv_heads, cfg.head_dim, T, cfg.torch_dtype, "cuda", paged=paged,
+                                block_size=cfg.block_size, block_table=table, n_blocks=nb)
+            filler.fill(X, t0, t1, 0, cache)
+            torch.cuda.synchronize()
+            outs.append(cache)
+        for li in range(len(layers)):
+            for a, b in ((outs[0].k[li], outs[1].k[li]), (outs[0].v[li], outs[1].v[li])):
+                assert torch.equal(a.view(torch.int16 if a.dtype == torch.bfloat16 else torch.int32),
+                                   b.view(torch.int16 if b.dtype == torch.bfloat16 else torch.int32)), (cfg.name, li)
+        rows = np.arange(t0, t1)
+        errs = []
+        for li, w in enumerate(ws):
+            K_ref, V_ref = oracle.fill_layer(f64(X), f64(w.W_map).T, f64(w.b_map), f64(w.gamma), f64(w.W_k).T,
+                                             f64(w.W_v).T, rows.astype(np.float64), cfg.n_kv_heads, cfg.head_dim,
+                                             cfg.rms_eps, cfg.rope_base)
+            K = f64(gather_rows(outs[1], outs[1].k[li], t0, t1))
+            V = f64(gather_rows(outs[1], outs[1].v[li], t0, t1))
+            errs.append(max(float(np.max(np.abs(K - K_ref)) / np.sqrt(np.mean(K_ref ** 2))),
+                            float(np.max(np.abs(V - V_ref)) / np.sqrt(np.mean(V_ref ** 2)))))
+        tol = 1e-4 if cfg.dtype == "f32" else 2e-2
+        log(f"[fill] streamed {cfg.name} slots={slots} per_slot={per}: bit-identical to resident, max_err={max(errs):.3e}")
+        assert max(errs) <= tol
