@@ -352,7 +352,10 @@ rf_status rf_fill_streamed(const rf_fill_weights* weights, int32_t n_layers,
  * d_src_k[l], d_src_v[l] : [t1-t0][ld_src] source rows of tokens t0..t1-1 (row i is token
  *                    t0+i), dtype of the maps, 16-B aligned, ld_src a 16-byte multiple
  * cache, k_cache, v_cache, d_block_table, d_rope : as for rf_fill; rows outside [t0, t1)
- *                    and layers not listed are never written
+ *                    and layers not listed are never written.  d_rope may be NULL: the keys
+ *                    are then stored unrotated (post-RoPE translators, section 3.1, whose
+ *                    maps act on keys the source already rotated; post-norm translators pass
+ *                    the table and no k_norm)
  * No workspace.  Supported: d_in % 128 == 0 (BF16) or % 64 == 0 (F32), d_in <= 65536,
  * ld_src <= 2^21, head_dim in {64, 128}, (n_kv_heads*head_dim) % 256 == 0.
  * ------------------------------------------------------------------------------------- */

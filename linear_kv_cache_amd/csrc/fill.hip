@@ -356,14 +356,20 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
                     stage(nl, fl + HALF, hi);
                 }
             } else {
-                const float* cs_row = a.rope + (a.pos0 + a.t0 + (n < a.rows ? n : 0)) * (int64_t)DH;
-                // (cos, sin) of the lane's 4 x 4 low dims, loaded together ahead of their uses
+                // (cos, sin) of the lane's 4 x 4 low dims, loaded together ahead of their uses;
+                // no table (translators of rotated keys): the identity turn
                 f32x4 c01[4], c23[4];
+                if (a.rope) {
+                    const float* cs_row = a.rope + (a.pos0 + a.t0 + (n < a.rows ? n : 0)) * (int64_t)DH;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int dlo = (qp0 + 8 * q) % HALF;
-                    c01[q] = *(const f32x4*)(cs_row + 2 * dlo);
-                    c23[q] = *(const f32x4*)(cs_row + 2 * dlo + 4);
+                    for (int q = 0; q < 4; ++q) {
+                        const int dlo = (qp0 + 8 * q) % HALF;
+                        c01[q] = *(const f32x4*)(cs_row + 2 * dlo);
+                        c23[q] = *(const f32x4*)(cs_row + 2 * dlo + 4);
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) c01[q] = c23[q] = f32x4{1.f, 0.f, 1.f, 0.f};
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 float kinv = 1.f;
@@ -423,7 +429,8 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
             const int64_t base = row_base(t);
             if (base < 0) continue;
             const float r = rms_inv(n);
-            const float* cs_row = a.rope + (a.pos0 + t) * (int64_t)DH;  // HALF (cos, sin) pairs
+            // HALF (cos, sin) pairs; no table: the identity turn
+            const float* cs_row = a.rope ? a.rope + (a.pos0 + t) * (int64_t)DH : nullptr;
             // per-head key norm: sub-tiles i of one head (DH / 32 of them, inside the wave's
             // rows) and the token's other rows in lane ^ 32
             float kinv[G::SM];
@@ -471,8 +478,8 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
                     } else if ((i * 32) % DH < HALF) {
                         // this sub-tile holds dims [dim, dim+4) < HALF; partner sub-tile i+PAIR
                         // holds dims + HALF of the same head in the same registers
-                        const f32x4 c01 = *(const f32x4*)(cs_row + 2 * dim);
-                        const f32x4 c23 = *(const f32x4*)(cs_row + 2 * dim + 4);
+                        const f32x4 c01 = cs_row ? *(const f32x4*)(cs_row + 2 * dim) : f32x4{1.f, 0.f, 1.f, 0.f};
+                        const f32x4 c23 = cs_row ? *(const f32x4*)(cs_row + 2 * dim + 4) : f32x4{1.f, 0.f, 1.f, 0.f};
                         const float cs[4] = {c01[0], c01[2], c23[0], c23[2]};
                         const float sn[4] = {c01[1], c01[3], c23[1], c23[3]};
                         float lo[4], hi[4];
@@ -930,7 +937,7 @@ rf_status rf_translate(const rf_translate_weights* w, int32_t n_layers, const vo
     rf_status st = rf_cache_layout(cache, &L);
     if (st != RF_OK) return st;
     if (n_layers == 0 || t1 == t0) return RF_OK;
-    RF_REQUIRE(d_src_k && d_src_v && w->T_k && w->T_v && k_cache && v_cache && d_rope, RF_ERR_INVALID_ARG,
+    RF_REQUIRE(d_src_k && d_src_v && w->T_k && w->T_v && k_cache && v_cache, RF_ERR_INVALID_ARG,
                "rf_translate: null pointer argument");
     const size_t eb = elem_bytes(w->dtype);
     RF_REQUIRE(ld_src >= w->d_in && (ld_src * (int64_t)eb) % 16 == 0 && ld_src <= (1 << 21), RF_ERR_INVALID_ARG,
@@ -949,8 +956,10 @@ rf_status rf_translate(const rf_translate_weights* w, int32_t n_layers, const vo
             RF_REQUIRE(w->k_norm[l] && aligned(w->k_norm[l], 16), RF_ERR_INVALID_ARG,
                        "rf_translate: key norm weights must be non-null and 16-byte aligned");
     }
-    RF_REQUIRE(aligned(d_rope, 16), RF_ERR_INVALID_ARG, "rf_translate: rope table must be 16-byte aligned");
-    RF_REQUIRE(pos0 + t1 <= rope_len, RF_ERR_INVALID_ARG, "rf_translate: rope table shorter than pos0 + t1");
+    if (d_rope) {
+        RF_REQUIRE(aligned(d_rope, 16), RF_ERR_INVALID_ARG, "rf_translate: rope table must be 16-byte aligned");
+        RF_REQUIRE(pos0 + t1 <= rope_len, RF_ERR_INVALID_ARG, "rf_translate: rope table shorter than pos0 + t1");
+    }
     if (cache->layout == RF_LAYOUT_PAGED) {
         RF_REQUIRE(d_block_table, RF_ERR_INVALID_ARG, "rf_translate: paged cache needs a block table");
         RF_REQUIRE(ceil_div(t1, cache->block_size) <= n_table_blocks, RF_ERR_INVALID_ARG,

@@ -190,13 +190,16 @@ def translate_weights(d_in: int, n_kv_heads: int, head_dim: int, dtype, T_k, T_v
 
 
 class Translator:
-    """Holds the per-target-layer translator maps and a RoPE table; translates token ranges."""
+    """Holds the per-target-layer translator maps and a RoPE table; translates token ranges.
+    ``rope_base=None``: no table, keys stored unrotated (post-RoPE translators)."""
 
-    def __init__(self, weights: TranslateWeights, rope_base: float, max_pos: int, device, stream=None):
+    def __init__(self, weights: TranslateWeights, rope_base, max_pos: int, device, stream=None):
         self.w = weights
-        self.rope_len = max_pos
-        self.rope = torch.empty(max_pos, weights.head_dim, dtype=torch.float32, device=device)
-        rf_rope_table(rope_base, weights.head_dim, max_pos, self.rope, stream)
+        self.rope_len = max_pos if rope_base is not None else 0
+        self.rope = None
+        if rope_base is not None:
+            self.rope = torch.empty(max_pos, weights.head_dim, dtype=torch.float32, device=device)
+            rf_rope_table(rope_base, weights.head_dim, max_pos, self.rope, stream)
 
     def translate(self, src_k: Sequence, src_v: Sequence, ld_src: int, t0: int, t1: int, pos0: int, cache: Cache,
                   stream=None):

@@ -7,7 +7,8 @@ KV-Lingo page, section 3.1 "Linear translator family":
     head-mixing translators are unconstrained;
   * pre-norm storing: the maps act on the source's keys before any normalisation or
     rotation; the translated keys are normalised per head (for targets that normalise keys,
-    section 2) and rotated by their token's position before they are stored.
+    section 2) and rotated by their token's position before they are stored.  Post-RoPE
+    translators act on keys the source already rotated and store their output unrotated.
 Section 3.1 "Source-layer selection": relative-depth match gives target layer l (1-based)
 the band of nu consecutive source layers centred on c(l) = 1 + (l - 1)(N_src - 1)/(N_tgt - 1),
 shifted at the boundaries so every band has nu layers.
@@ -86,7 +87,8 @@ def translate_layer(src_k, src_v, T_k, T_v, b_k, b_v, positions, n_kv_heads: int
     src_k, src_v [T, d_in]: the source keys (before rotation) and values of the nu source
     layers, concatenated along the row; T_k, T_v [d_in, H*d_h]; b_k, b_v [H*d_h] or None.
     k = src_k T_k + b_k, per-head RMS-normalised with gamma_k = ``k_norm`` when given, rotated
-    by its position; v = src_v T_v + b_v.
+    by its position (not when ``base`` is None: post-RoPE translators act on keys the source
+    already rotated and store their output as it is); v = src_v T_v + b_v.
     Returns (K, V), each [T, H, d_h] fp64."""
     src_k = _f64(src_k)
     src_v = _f64(src_v)
@@ -101,6 +103,8 @@ def translate_layer(src_k, src_v, T_k, T_v, b_k, b_v, positions, n_kv_heads: int
     V = V.reshape(n, n_kv_heads, head_dim)
     if k_norm is not None:
         K = rmsnorm(K, k_norm, k_norm_eps)
+    if base is None:
+        return K, V
     return rope_rotate(K, positions, base), V
 
 

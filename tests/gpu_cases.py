@@ -189,6 +189,7 @@ class TranslateCase:
     sample: Optional[Sequence[int]] = None     # token indices to compare (None = all translated)
     gen_device: str = "cpu"
     k_norm: bool = False                       # the target's per-head key norm (eps 1e-6)
+    rotate: bool = True                        # False: post-RoPE translators (no table)
 
 
 def run_translate_case(case: TranslateCase, device="cuda"):
@@ -216,7 +217,8 @@ def run_translate_case(case: TranslateCase, device="cuda"):
     cache = alloc_cache(n_tgt, cfg.n_kv_heads, cfg.head_dim, T, cfg.torch_dtype, device, paged=cfg.paged,
                         block_size=cfg.block_size, block_table=table,
                         n_blocks=(int(table.max()) + 1) if table is not None else None)
-    tr = Translator(tw, cfg.rope_base, case.pos0 + T, device)
+    base = cfg.rope_base if case.rotate else None
+    tr = Translator(tw, base, case.pos0 + T, device)
     ld = cfg.n_src * cfg.d_src
     chunk = case.chunk or (case.t1 - case.t0)
     for c0 in range(case.t0, case.t1, chunk):
@@ -238,7 +240,7 @@ def run_translate_case(case: TranslateCase, device="cuda"):
                                               None if m[2] is None else f64(m[2]),
                                               None if m[3] is None else f64(m[3]),
                                               case.pos0 + rows.astype(np.float64), cfg.n_kv_heads, cfg.head_dim,
-                                              cfg.rope_base, None if gks is None else f64(gks[li]), 1e-6)
+                                              base, None if gks is None else f64(gks[li]), 1e-6)
         Kall = gather_rows(cache, cache.k[li], 0, T)
         Vall = gather_rows(cache, cache.v[li], 0, T)
         di = torch.as_tensor(rows, device=device)

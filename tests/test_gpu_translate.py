@@ -81,6 +81,14 @@ def test_translate_target_key_norm():
     _check(run_translate_case(TranslateCase(TINY_F32, 0, 300, k_norm=True)), "fp32 key norm")
 
 
+def test_translate_post_rope_unrotated():
+    # post-RoPE translators: no table, keys stored as the map leaves them (dense, head-wise, fp32)
+    _check(run_translate_case(TranslateCase(SMALL_PAGED, 37, 737, pos0=11, chunk=300, rotate=False)),
+           "bf16 post-RoPE paged")
+    _check(run_translate_case(TranslateCase(SMALL_HEADWISE, 0, 800, rotate=False)), "bf16 head-wise post-RoPE")
+    _check(run_translate_case(TranslateCase(TINY_F32, 0, 300, rotate=False)), "fp32 post-RoPE")
+
+
 def test_translate_bf16_head_dim_64_far_positions():
     # target heads of 64 from a 2 x 128 source, RoPE at positions near 131072
     _check(run_translate_case(TranslateCase(SMALL_DH64, 0, 600, pos0=130000)), "bf16 dh64 far pos")

@@ -251,3 +251,27 @@ def test_translator_key_norm_before_rotation():
     kn = k / np.sqrt(np.mean(k * k, axis=-1, keepdims=True) + 1e-6) * gk
     assert np.allclose(K, _rope_complex(kn, pos, 1e4), rtol=0, atol=1e-12)
     assert np.allclose(V, (sv @ Tv).reshape(n, H, dh), rtol=0, atol=1e-12)
+
+
+def test_post_rope_translators_store_unrotated():
+    # post-RoPE capture: the maps act on keys the source already rotated, nothing is turned
+    # after the map; rotation commutes with a map that acts on each rotation pair as a complex
+    # scalar, so rotating then translating equals translating then rotating for such maps
+    rng = np.random.default_rng(14)
+    H, dh, n = 2, 8, 5
+    sk, sv = rng.standard_normal((n, H * dh)), rng.standard_normal((n, H * dh))
+    pos = 2.0 + np.arange(n) * 11
+    K, V = oracle.translate_layer(sk, sv, np.eye(H * dh), np.eye(H * dh), None, None, pos, H, dh, None)
+    assert np.array_equal(K, sk.reshape(n, H, dh)) and np.array_equal(V, sv.reshape(n, H, dh))
+    # per pair: (a, c) -> (alpha a - beta c, beta a + alpha c) is multiplication by alpha + i beta
+    half = dh // 2
+    alpha, beta = rng.standard_normal(half), rng.standard_normal(half)
+    blk = np.zeros((dh, dh))
+    for i in range(half):
+        blk[i, i], blk[i + half, i] = alpha[i], -beta[i]
+        blk[i, i + half], blk[i + half, i + half] = beta[i], alpha[i]
+    T = oracle.headwise_dense(np.stack([blk] * H))
+    rotated = oracle.rope_rotate(sk.reshape(n, H, dh), pos, 1e4).reshape(n, -1)
+    K_post, _ = oracle.translate_layer(rotated, sv, T, T, None, None, pos, H, dh, None)
+    K_pre, _ = oracle.translate_layer(sk, sv, T, T, None, None, pos, H, dh, 1e4)
+    assert np.allclose(K_post, K_pre, rtol=0, atol=1e-12)
