@@ -25,10 +25,11 @@ from .ridge import (NotSPD, gram_sums, fit, fit_from_sums, ridge_objective,
                     solve_columns_from_data)
 from .fill import rope_inverse_frequencies, rope_rotate, rmsnorm, fill_layer, fill
 from .translate import (relative_depth_centre, relative_depth_sources, headwise_dense,
-                        translate_layer, translate, fit_translator, fit_r2, r2_assignment)
+                        translate_layer, translate, fit_translator, fit_r2, r2_assignment,
+                        greedy_sources)
 
 __all__ = ["NotSPD", "gram_sums", "fit", "fit_from_sums", "ridge_objective",
            "solve_columns_from_data", "rope_inverse_frequencies", "rope_rotate", "rmsnorm",
            "fill_layer", "fill", "relative_depth_centre", "relative_depth_sources",
            "headwise_dense", "translate_layer", "translate", "fit_translator", "fit_r2",
-           "r2_assignment"]
+           "r2_assignment", "greedy_sources"]

@@ -159,3 +159,28 @@ def r2_assignment(r2, nu: int):
         order = sorted(range(n_src), key=lambda s: (-score[s], s))
         out.append(sorted(order[:nu]))
     return out
+
+
+def greedy_sources(src_layers, tgt_rows, nu: int, lam: float, mode: str = "absolute"):
+    """Greedy match (KV-Lingo page, section 3.1 "Source-layer selection"): forward selection
+    over source layers on the residual of the ridge fit to the target layer.  Starting from
+    no source, each step adds the source layer whose rows, taken together with those already
+    chosen, leave the smallest residual, i.e. give the largest R^2 of the joint ridge fit
+    (``fit_r2`` on the chosen layers' rows side by side, in ascending layer order).
+    Reading: equal scores go to the shallower layer.  src_layers: list of [n, d_src] arrays;
+    tgt_rows: [n, d_out].  Returns the nu chosen layers, ascending."""
+    n_src = len(src_layers)
+    if not 1 <= nu <= n_src:
+        raise ValueError("need 1 <= nu <= n_src")
+    chosen = []
+    for _ in range(nu):
+        best = None
+        for s in range(n_src):
+            if s in chosen:
+                continue
+            cand = sorted(chosen + [s])
+            score = fit_r2(np.hstack([_f64(src_layers[c]) for c in cand]), tgt_rows, lam, mode)
+            if best is None or score > best[0]:
+                best = (score, s)
+        chosen.append(best[1])
+    return sorted(chosen)

@@ -275,3 +275,22 @@ def test_post_rope_translators_store_unrotated():
     K_post, _ = oracle.translate_layer(rotated, sv, T, T, None, None, pos, H, dh, None)
     K_pre, _ = oracle.translate_layer(sk, sv, T, T, None, None, pos, H, dh, 1e4)
     assert np.allclose(K_post, K_pre, rtol=0, atol=1e-12)
+
+
+def test_greedy_match_accounts_for_redundancy():
+    # The page contrasts the two data-driven assignments: the R^2 assignment keeps two source
+    # layers that explain the same part of the target, greedy match does not.  Sources 0 and 1
+    # carry the same signal (1 is 0 plus a little noise), source 2 carries a weaker,
+    # independent one, source 3 nothing; the target is their sum plus noise.
+    rng = np.random.default_rng(15)
+    n, d = 600, 6
+    a, b = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    src = [a, a + 0.05 * rng.standard_normal((n, d)), b, rng.standard_normal((n, d))]
+    tgt = a @ rng.standard_normal((d, 4)) + 0.5 * b @ rng.standard_normal((d, 4)) + 0.1 * rng.standard_normal((n, 4))
+    r2 = np.array([[oracle.fit_r2(s, tgt, 1e-3) for s in src]])
+    assert oracle.r2_assignment(r2, 2) == [[0, 1]]              # both copies of the same signal
+    assert oracle.greedy_sources(src, tgt, 2, 1e-3) == [0, 2]   # the copy adds nothing new
+    # one source: greedy and the R^2 assignment agree (the single best fit)
+    assert oracle.greedy_sources(src, tgt, 1, 1e-3) == oracle.r2_assignment(r2, 1)[0]
+    # all sources: everything
+    assert oracle.greedy_sources(src, tgt, 4, 1e-3) == [0, 1, 2, 3]
