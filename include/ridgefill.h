@@ -114,6 +114,19 @@ rf_status rf_gram_accumulate(const rf_gram_desc* desc, void* d_state,
                              const void* const* d_Y, int64_t ldy,
                              int64_t rows, void* stream);
 
+/* Sub-state of column blocks of X, for fits from a subset of source layers (KV-Lingo page,
+ * section 3.1, greedy match: forward selection over source layers, each candidate set fitted
+ * from the one accumulated pass).  X's d columns form d / block_width blocks (block_width a
+ * multiple of 256 that divides d); blocks (host, n_sel in 1..64, strictly ascending) selects
+ * some.  d_state_out (laid out for desc_out: d = n_sel * block_width, the same n_targets,
+ * d_out and dtype; distinct from d_state) receives n, S_xx over the selected blocks (their
+ * upper triangle; the rest of the tile rows is copied as it lies), the selected columns of
+ * S_yx and s_x, and s_y, s_yy unchanged: exactly the state one pass over the selected
+ * columns alone would have left.  Solving it gives the maps from the selected blocks alone. */
+rf_status rf_gram_select(const rf_gram_desc* desc, const void* d_state, int32_t block_width,
+                         const int32_t* blocks, int32_t n_sel, const rf_gram_desc* desc_out,
+                         void* d_state_out, void* stream);
+
 /* ---------------------------------------------------------------------------------------
  * Ridge fit, part 2: the closed-form solve.
  *

@@ -81,6 +81,8 @@ _sig = {
     "rf_gram_init": (C.c_int, [C.POINTER(rf_gram_desc), _P, _P]),
     "rf_gram_accumulate": (C.c_int, [C.POINTER(rf_gram_desc), _P, _P, C.c_int64, C.POINTER(_P), C.c_int64,
                                      C.c_int64, _P]),
+    "rf_gram_select": (C.c_int, [C.POINTER(rf_gram_desc), _P, C.c_int32, C.POINTER(C.c_int32), C.c_int32,
+                                 C.POINTER(rf_gram_desc), _P, _P]),
     "rf_solve_workspace_bytes": (C.c_size_t, [C.POINTER(rf_gram_desc), C.c_int32]),
     "rf_solve": (C.c_int, [C.POINTER(rf_gram_desc), _P, C.c_double, C.c_int, C.POINTER(C.c_int32), C.c_int32,
                            _P, _P, _P, _P, _P, C.c_size_t, _P]),
@@ -187,6 +189,13 @@ def rf_gram_accumulate(desc: rf_gram_desc, state, X, Ys: Sequence, rows: Optiona
     ys = _ptr_array(Ys)
     _check(_lib.rf_gram_accumulate(C.byref(desc), _ptr(state), _ptr(X), X.stride(0), ys, ldy, rows,
                                    _stream(stream)))
+
+
+def rf_gram_select(desc: rf_gram_desc, state, block_width: int, blocks: Sequence[int], desc_out: rf_gram_desc,
+                   state_out, stream=None):
+    bl = (C.c_int32 * max(1, len(blocks)))(*blocks)
+    _check(_lib.rf_gram_select(C.byref(desc), _ptr(state), block_width, bl, len(blocks), C.byref(desc_out),
+                               _ptr(state_out), _stream(stream)))
 
 
 def rf_solve_workspace_bytes(desc: rf_gram_desc, n_sel: int) -> int:

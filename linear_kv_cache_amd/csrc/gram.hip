@@ -315,6 +315,43 @@ __global__ void k_zero_bytes(uint4* p, int64_t n16) {
         p[i] = uint4{0u, 0u, 0u, 0u};
 }
 
+// ---- sub-states of column blocks ----------------------------------------------------------
+constexpr int kMaxSelBlocks = 64;
+struct SelectArgs {
+    int32_t blk[kMaxSelBlocks];   // selected source blocks, ascending
+    int32_t bw;                   // block width (columns)
+};
+
+// dst[r][c] = src[R(r)][C(c)] with C mapping destination column block c / bw to source block
+// blk[c / bw] (and R the same for rows when map_rows), 4 columns per thread.
+__global__ void k_select_cols(const float* __restrict__ src, int64_t lds, float* __restrict__ dst, int64_t ldd,
+                              int64_t rows, int64_t cols, int map_rows, SelectArgs s) {
+    const int64_t c4 = cols / 4;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < rows * c4;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / c4, c = (i - r * c4) * 4;
+        const int64_t sr = map_rows ? (int64_t)s.blk[r / s.bw] * s.bw + r % s.bw : r;
+        const int64_t sc = (int64_t)s.blk[c / s.bw] * s.bw + c % s.bw;
+        *(f32x4*)(dst + r * ldd + c) = *(const f32x4*)(src + sr * lds + sc);
+    }
+}
+
+// n, the selected entries of s_x, and s_y, s_yy as they are.
+__global__ void k_select_vecs(const int64_t* n, const double* sx, const double* sy, const double* syy, int64_t dx,
+                              int64_t ny, int64_t* n_out, double* sx_out, double* sy_out, double* syy_out,
+                              SelectArgs s) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < dx + ny;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        if (i < dx) {
+            sx_out[i] = sx[(int64_t)s.blk[i / s.bw] * s.bw + i % s.bw];
+        } else {
+            sy_out[i - dx] = sy[i - dx];
+            syy_out[i - dx] = syy[i - dx];
+        }
+        if (i == 0) *n_out = *n;
+    }
+}
+
 static rf_status check_desc(const rf_gram_desc* desc) {
     RF_REQUIRE(desc, RF_ERR_INVALID_ARG, "gram: null descriptor");
     RF_REQUIRE(valid_dtype(desc->dtype), RF_ERR_INVALID_ARG, "gram: bad dtype");
@@ -365,6 +402,54 @@ rf_status rf_gram_init(const rf_gram_desc* desc, void* d_state, void* stream) {
     const int blocks = (int)std::min<int64_t>(ceil_div(n16, 256), 4096);
     hipLaunchKernelGGL(k_zero_bytes, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (uint4*)d_state, n16);
     return check_launch("rf_gram_init");
+}
+
+rf_status rf_gram_select(const rf_gram_desc* desc, const void* d_state, int32_t block_width, const int32_t* blocks,
+                         int32_t n_sel, const rf_gram_desc* desc_out, void* d_state_out, void* stream) {
+    clear_error();
+    rf_status st = check_desc(desc);
+    if (st != RF_OK) return st;
+    st = check_desc(desc_out);
+    if (st != RF_OK) return st;
+    RF_REQUIRE(block_width > 0 && block_width % kGT == 0 && desc->d % block_width == 0, RF_ERR_UNSUPPORTED,
+               "rf_gram_select: block_width must be a multiple of 256 that divides d");
+    RF_REQUIRE(n_sel >= 1 && n_sel <= kMaxSelBlocks && blocks, RF_ERR_INVALID_ARG,
+               "rf_gram_select: 1..64 selected blocks");
+    const int32_t n_blocks = desc->d / block_width;
+    for (int i = 0; i < n_sel; ++i)
+        RF_REQUIRE(blocks[i] >= 0 && blocks[i] < n_blocks && (i == 0 || blocks[i] > blocks[i - 1]), RF_ERR_INVALID_ARG,
+                   "rf_gram_select: block indices must ascend strictly within [0, d / block_width)");
+    RF_REQUIRE(desc_out->d == (int64_t)n_sel * block_width && desc_out->n_targets == desc->n_targets &&
+                   gram_dy(desc_out) == gram_dy(desc) && desc_out->dtype == desc->dtype,
+               RF_ERR_INVALID_ARG, "rf_gram_select: desc_out must have d = n_sel * block_width and the same targets");
+    RF_REQUIRE(d_state && d_state_out && aligned(d_state, 256) && aligned(d_state_out, 256) && d_state != d_state_out,
+               RF_ERR_INVALID_ARG, "rf_gram_select: states must be distinct, non-null and 256-B aligned");
+    const GramLayout Ls = gram_layout(desc->d, desc->n_targets, gram_dy(desc));
+    const GramLayout Ld = gram_layout(desc_out->d, desc_out->n_targets, gram_dy(desc_out));
+    const char* s = (const char*)d_state;
+    char* o = (char*)d_state_out;
+    SelectArgs sa{};
+    for (int i = 0; i < n_sel; ++i) sa.blk[i] = blocks[i];
+    sa.bw = block_width;
+    hipStream_t strm = (hipStream_t)stream;
+    const int64_t dd = desc_out->d, ny = (int64_t)desc->n_targets * gram_dy(desc);
+    auto grid = [](int64_t n) { return dim3((unsigned)std::min<int64_t>(std::max<int64_t>(ceil_div(n, 256), 1), 8192)); };
+    // ascending blocks keep every selected upper-triangle block in the source's upper triangle
+    hipLaunchKernelGGL(k_select_cols, grid(dd * dd / 4), dim3(256), 0, strm, (const float*)(s + Ls.off_Sxx),
+                       (int64_t)desc->d, (float*)(o + Ld.off_Sxx), dd, dd, dd, 1, sa);
+    st = check_launch("rf_gram_select: S_xx");
+    if (st != RF_OK) return st;
+    if (ny > 0) {
+        hipLaunchKernelGGL(k_select_cols, grid(ny * dd / 4), dim3(256), 0, strm, (const float*)(s + Ls.off_Syx),
+                           (int64_t)desc->d, (float*)(o + Ld.off_Syx), dd, ny, dd, 0, sa);
+        st = check_launch("rf_gram_select: S_yx");
+        if (st != RF_OK) return st;
+    }
+    hipLaunchKernelGGL(k_select_vecs, grid(dd + ny), dim3(256), 0, strm, (const int64_t*)(s + Ls.off_n),
+                       (const double*)(s + Ls.off_sx), (const double*)(s + Ls.off_sy), (const double*)(s + Ls.off_syy),
+                       dd, ny, (int64_t*)(o + Ld.off_n), (double*)(o + Ld.off_sx), (double*)(o + Ld.off_sy),
+                       (double*)(o + Ld.off_syy), sa);
+    return check_launch("rf_gram_select: sums");
 }
 
 rf_status rf_gram_accumulate(const rf_gram_desc* desc, void* d_state, const void* d_X, int64_t ldx,

@@ -9,7 +9,7 @@ import torch
 
 from . import (RF_LAYOUT_CONTIGUOUS, RF_LAYOUT_PAGED, FillWeights, TranslateWeights, cache_desc, gram_desc,
                rf_cache_layout, rf_fill, rf_fill_streamed, rf_fill_streamed_ring_bytes, rf_fill_workspace_bytes,
-               rf_fit_r2, rf_fit_r2_workspace_bytes,
+               rf_fit_r2, rf_fit_r2_workspace_bytes, rf_gram_select,
                rf_gram_accumulate, rf_gram_init,
                rf_gram_state_bytes, rf_gram_state_layout, rf_pack_weights, rf_rope_table, rf_solve,
                rf_solve_workspace_bytes, rf_translate)
@@ -81,6 +81,49 @@ class GramState:
             ws = device_bytes(rf_solve_workspace_bytes(self.desc, n_sel), dev)
         rf_solve(self.desc, self.buf, lam, mode, list(targets), W, Wlp, b, info, ws, stream)
         return W, Wlp, b, info
+
+
+def greedy_sources(state: GramState, block_width: int, nu: int, lam: float, mode: int,
+                   targets: Optional[Sequence[int]] = None, stream=None) -> List[List[int]]:
+    """Greedy match (KV-Lingo page, section 3.1): for each target, forward selection over the
+    column blocks of X (source layers) by the R^2 of the joint ridge fit, all of it read off
+    the one accumulated state.  Each step scores every candidate set E + {s} with
+    rf_gram_select -> rf_solve -> rf_fit_r2 (a set shared by several targets is solved once
+    for all of them) and keeps the best per target (equal scores: the shallower layer).
+    The choices are host decisions on the scores; every number comes from the library."""
+    dev = state.buf.device
+    n_blocks = state.d // block_width
+    targets = list(range(state.n_targets)) if targets is None else list(targets)
+    chosen: List[List[int]] = [[] for _ in targets]
+    for _ in range(nu):
+        sets: dict = {}
+        for ti in range(len(targets)):
+            for s in range(n_blocks):
+                if s not in chosen[ti]:
+                    sets.setdefault(tuple(sorted(chosen[ti] + [s])), []).append(ti)
+        scores: dict = {}
+        for key, users in sets.items():
+            sub = GramState.__new__(GramState)
+            sub.desc = gram_desc(len(key) * block_width, state.n_targets, state.desc.dtype, state.desc.d_out)
+            sub.layout = rf_gram_state_layout(sub.desc)
+            sub.buf = device_bytes(rf_gram_state_bytes(sub.desc), dev)
+            sub.d, sub.n_targets, sub.dy = len(key) * block_width, state.n_targets, state.dy
+            rf_gram_select(state.desc, state.buf, block_width, list(key), sub.desc, sub.buf, stream)
+            tsel = sorted(set(targets[ti] for ti in users))
+            W, _, _, info = sub.solve(lam, mode, tsel, want_bf16=False, stream=stream)
+            r2 = sub.r2(lam, mode, tsel, W, stream).cpu().tolist()
+            for t, v in zip(tsel, r2):
+                scores[(key, t)] = v
+        for ti, t in enumerate(targets):
+            best = None
+            for s in range(n_blocks):
+                if s in chosen[ti]:
+                    continue
+                v = scores[(tuple(sorted(chosen[ti] + [s])), t)]
+                if best is None or v > best[0]:
+                    best = (v, s)
+            chosen[ti].append(best[1])
+    return [sorted(c) for c in chosen]
 
 
 @dataclass

@@ -296,3 +296,21 @@ def test_fit_r2_validation_before_enqueue():
         rf.rf_fit_r2(desc, 256, 0.1, 0, [0], 256, r2, _aligned_bytes(128), stream=0)
     assert e.value.status == rf.RF_ERR_WORKSPACE
     rf.rf_fit_r2(desc, 256, 0.1, 0, [], 256, r2, ws, stream=0)   # nothing selected: nothing to do
+
+
+def test_gram_select_validation_before_enqueue():
+    src = rf.gram_desc(1024, 2, torch.bfloat16, d_out=512)
+    ok = rf.gram_desc(512, 2, torch.bfloat16, d_out=512)
+    cases = [
+        (dict(bw=300, blocks=[0]), rf.RF_ERR_UNSUPPORTED),                    # width not a multiple of 256
+        (dict(bw=768, blocks=[0]), rf.RF_ERR_UNSUPPORTED),                    # does not divide d
+        (dict(bw=256, blocks=[2, 1]), rf.RF_ERR_INVALID_ARG),                 # not ascending
+        (dict(bw=256, blocks=[1, 4]), rf.RF_ERR_INVALID_ARG),                 # out of range
+        (dict(bw=256, blocks=[1, 2, 3]), rf.RF_ERR_INVALID_ARG),              # desc_out width differs
+        (dict(bw=256, blocks=[0, 1], out=rf.gram_desc(512, 3, torch.bfloat16, d_out=512)), rf.RF_ERR_INVALID_ARG),
+        (dict(bw=256, blocks=[0, 1], sout=256), rf.RF_ERR_INVALID_ARG),       # same buffer
+    ]
+    for kw, status in cases:
+        with pytest.raises(rf.RidgeFillError) as e:
+            rf.rf_gram_select(src, 256, kw["bw"], kw["blocks"], kw.get("out", ok), kw.get("sout", 512), stream=0)
+        assert e.value.status == status, kw

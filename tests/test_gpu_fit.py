@@ -230,3 +230,28 @@ def test_fit_r2_read_off_the_state():
             assert int(info.item()) == 0
             assert float(np.max(np.abs(r2 - np.array(ref)))) <= R2_TOL
             assert ref[0] > ref[1] > ref[2]
+
+
+def test_gram_select_equals_a_pass_over_the_selected_columns():
+    # the sub-state of blocks [1, 3] of a 4-block X equals the state one pass over those columns
+    # alone leaves (the same tile products over the same rows: bit for bit)
+    from linear_kv_cache_amd.runner import GramState
+    import linear_kv_cache_amd as rf
+    g = synth.generator(51, "select")
+    n, bw = 2000, 256
+    X = torch.randn(n, 4 * bw, generator=g).to(torch.bfloat16).cuda()
+    Ys = [torch.randn(n, 512, generator=g).to(torch.bfloat16).cuda() for _ in range(2)]
+    full = GramState(4 * bw, 2, torch.bfloat16, "cuda", d_out=512)
+    full.accumulate(X, Ys)
+    sub = GramState(2 * bw, 2, torch.bfloat16, "cuda", d_out=512)
+    rf.rf_gram_select(full.desc, full.buf, bw, [1, 3], sub.desc, sub.buf)
+    direct = GramState(2 * bw, 2, torch.bfloat16, "cuda", d_out=512)
+    Xs = torch.cat([X[:, bw:2 * bw], X[:, 3 * bw:]], dim=1).contiguous()
+    direct.accumulate(Xs, Ys)
+    torch.cuda.synchronize()
+    up = torch.triu(torch.ones(2 * bw, 2 * bw, dtype=torch.bool)).cuda()
+    assert int(sub.n().item()) == int(direct.n().item()) == n
+    assert torch.equal(sub.S_xx()[up], direct.S_xx()[up])
+    assert torch.equal(sub.S_yx(), direct.S_yx())
+    assert torch.equal(sub.s_x(), direct.s_x()) and torch.equal(sub.s_y(), direct.s_y())
+    assert torch.equal(sub.s_yy(), direct.s_yy())
