@@ -21,14 +21,14 @@ Readings taken where the pages are silent (each one is listed in the design note
 Parity status: every function here is pinned by tests/test_oracle_*.py against closed
 forms, limits, brute force or an independent library route.
 """
-from .ridge import (NotSPD, gram_sums, fit, fit_from_sums, ridge_objective,
+from .ridge import (NotSPD, gram_sums, fit, fit_from_sums, fit_pinv, ridge_objective,
                     solve_columns_from_data)
 from .fill import rope_inverse_frequencies, rope_rotate, rmsnorm, fill_layer, fill
 from .translate import (relative_depth_centre, relative_depth_sources, headwise_dense,
                         translate_layer, translate, fit_translator, fit_r2, r2_assignment,
                         greedy_sources)
 
-__all__ = ["NotSPD", "gram_sums", "fit", "fit_from_sums", "ridge_objective",
+__all__ = ["NotSPD", "gram_sums", "fit", "fit_from_sums", "fit_pinv", "ridge_objective",
            "solve_columns_from_data", "rope_inverse_frequencies", "rope_rotate", "rmsnorm",
            "fill_layer", "fill", "relative_depth_centre", "relative_depth_sources",
            "headwise_dense", "translate_layer", "translate", "fit_translator", "fit_r2",

@@ -120,3 +120,25 @@ def ridge_objective(X, Y, W, lam: float) -> float:
     Yc = Y - Y.mean(axis=0)
     R = Xc @ _f64(W) - Yc
     return float(np.sum(R * R) + lam * np.sum(_f64(W) ** 2))
+
+
+def fit_pinv(X, Y, lam: float = 0.0, rel_tol: float = 1e-8, mode: str = "absolute"):
+    """The map by the symmetric eigendecomposition route (KV-Lingo page, Appendix B.2
+    "Protocol": the normal equations are solved by symmetric eigendecomposition, eigenvalues
+    below a relative tolerance of 1e-8 treated as zero).  A = X~^T X~ + lam I = V diag(mu) V^T;
+    A^+ keeps 1/mu_i for mu_i > rel_tol * max(mu) and zero otherwise; W = A^+ X~^T Y~ and
+    b = mean(Y) - mean(X) W.  For a regular A this is the ridge map of ``fit``; for a singular
+    one it is the minimum-norm least-squares map."""
+    X = _f64(X)
+    Y = _f64(Y)
+    mu_x = X.mean(axis=0)
+    mu_y = Y.mean(axis=0)
+    Xc = X - mu_x
+    Yc = Y - mu_y
+    C = Xc.T @ Xc
+    A = C + _lambda_value(C, lam, mode) * np.eye(C.shape[0])
+    mu, V = np.linalg.eigh(A)
+    keep = mu > rel_tol * np.max(mu)
+    inv = np.where(keep, 1.0 / np.where(keep, mu, 1.0), 0.0)
+    W = (V * inv) @ V.T @ (Xc.T @ Yc)
+    return W, mu_y - mu_x @ W

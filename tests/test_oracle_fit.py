@@ -206,3 +206,39 @@ def test_relative_lambda_is_scale_free():
     Wa, _ = oracle.fit(X, Y, 5.0)
     Wb, _ = oracle.fit(7.0 * X, 7.0 * Y, 5.0)
     assert not np.allclose(Wa, Wb, rtol=0, atol=1e-6)
+
+
+def test_pinv_route_regular_equals_cholesky_fit():
+    # a regular system: the eigendecomposition route and the Cholesky route agree
+    rng = np.random.default_rng(21)
+    X = rng.standard_normal((300, 12)) * np.linspace(0.3, 3, 12) + 1.0
+    Y = X @ rng.standard_normal((12, 5)) + rng.standard_normal((300, 5))
+    for lam in (0.0, 1e-2, 10.0):
+        W1, b1 = oracle.fit(X, Y, lam)
+        W2, b2 = oracle.fit_pinv(X, Y, lam)
+        assert np.max(np.abs(W1 - W2)) <= 1e-10 * np.max(np.abs(W1))
+        assert np.max(np.abs(b1 - b2)) <= 1e-10 * max(1.0, np.max(np.abs(b1)))
+
+
+def test_pinv_route_rank_deficient_is_minimum_norm_least_squares():
+    # duplicated and zero-variance columns make X~^T X~ singular: the route gives the
+    # minimum-norm least-squares map, as an SVD solver does (numpy.linalg.lstsq, an independent
+    # library route), and it leaves the null space of X~ out of W
+    rng = np.random.default_rng(22)
+    n = 400
+    base = rng.standard_normal((n, 6))
+    X = np.hstack([base, base[:, :2], np.full((n, 1), 3.0), base[:, 3:4] * 2.0])   # rank 6 of 10
+    Y = base @ rng.standard_normal((6, 4)) + 0.1 * rng.standard_normal((n, 4))
+    W, b = oracle.fit_pinv(X, Y, 0.0)
+    Xc, Yc = X - X.mean(0), Y - Y.mean(0)
+    W_ls = np.linalg.lstsq(Xc, Yc, rcond=1e-10)[0]
+    assert np.max(np.abs(W - W_ls)) <= 1e-9 * np.max(np.abs(W_ls))
+    assert np.allclose(b, Y.mean(0) - X.mean(0) @ W_ls, rtol=0, atol=1e-9)
+    # null-space directions of X~ (the duplicate differences, the constant column) get nothing
+    null = np.zeros((10, 4))
+    null[0, 0], null[6, 0] = 1.0, -1.0
+    null[1, 1], null[7, 1] = 1.0, -1.0
+    null[8, 2] = 1.0
+    null[3, 3], null[9, 3] = 2.0, -1.0
+    assert np.allclose(Xc @ null, 0.0, atol=1e-12)
+    assert np.max(np.abs(null.T @ W)) <= 1e-9 * np.max(np.abs(W))
