@@ -160,6 +160,25 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state,
                    float* d_W, void* d_W_lp, float* d_b, int32_t* d_info,
                    void* d_ws, size_t ws_bytes, void* stream);
 
+/* The same maps by the symmetric eigendecomposition route (KV-Lingo page, Appendix B.2
+ * "Protocol": the normal equations solved by symmetric eigendecomposition, eigenvalues below a
+ * relative tolerance treated as zero).  C + lambda I = V diag(mu) V^T by cyclic Jacobi in fp64
+ * (``sweeps`` sweeps of round-robin rotations; 15 reach fp64 accuracy on the widths used here);
+ * A^+ keeps 1/mu_i for mu_i > rel_tol * max mu; then W_l = B_l A^+ and b_l as in rf_solve (the
+ * same split-bf16 product).  For a regular system this is rf_solve's map; for a singular one
+ * (lambda = 0 on rank-deficient rows: low-rank caches, duplicated or constant features) it is
+ * the minimum-norm least-squares map, where rf_solve reports a failed pivot.  Outputs and
+ * their layouts as for rf_solve (no d_info: the route has no pivot to fail).
+ *  d_ws : rf_solve_pinv_workspace_bytes(desc, n_sel) bytes, 256-B aligned
+ * Needs rel_tol in [0, 1), sweeps in [1, 64]; one kernel pair per Jacobi round (d - 1 rounds
+ * per sweep), so it suits offline fits of widths up to a few thousand. */
+size_t rf_solve_pinv_workspace_bytes(const rf_gram_desc* desc, int32_t n_sel);
+rf_status rf_solve_pinv(const rf_gram_desc* desc, const void* d_state, double lambda,
+                        rf_lambda_mode mode, double rel_tol, int32_t sweeps,
+                        const int32_t* targets, int32_t n_sel,
+                        float* d_W, void* d_W_lp, float* d_b, void* d_ws, size_t ws_bytes,
+                        void* stream);
+
 /* ---------------------------------------------------------------------------------------
  * Fit quality.  KV-Lingo page, Appendix "The R^2 assignment": the score of a map is the
  * fraction of its target's features it explains, read off the sums the fit accumulated (no

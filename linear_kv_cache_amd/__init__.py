@@ -86,6 +86,9 @@ _sig = {
     "rf_solve_workspace_bytes": (C.c_size_t, [C.POINTER(rf_gram_desc), C.c_int32]),
     "rf_solve": (C.c_int, [C.POINTER(rf_gram_desc), _P, C.c_double, C.c_int, C.POINTER(C.c_int32), C.c_int32,
                            _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "rf_solve_pinv_workspace_bytes": (C.c_size_t, [C.POINTER(rf_gram_desc), C.c_int32]),
+    "rf_solve_pinv": (C.c_int, [C.POINTER(rf_gram_desc), _P, C.c_double, C.c_int, C.c_double, C.c_int32,
+                                C.POINTER(C.c_int32), C.c_int32, _P, _P, _P, _P, C.c_size_t, _P]),
     "rf_cache_layout": (C.c_int, [C.POINTER(rf_cache_desc), C.POINTER(rf_cache_layout_t)]),
     "rf_rope_table": (C.c_int, [C.c_double, C.c_int32, C.c_int64, _P, _P]),
     "rf_pack_weights": (C.c_int, [C.c_int, C.c_int64, C.c_int64, _P, C.c_int64, C.c_int32, _P, _P]),
@@ -208,6 +211,18 @@ def rf_solve(desc: rf_gram_desc, state, lam: float, mode: int, targets: Sequence
     ws_bytes = ws.numel() * ws.element_size()
     _check(_lib.rf_solve(C.byref(desc), _ptr(state), float(lam), int(mode), tg, len(targets), _ptr(W), _ptr(W_lp),
                          _ptr(b), _ptr(info), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def rf_solve_pinv_workspace_bytes(desc: rf_gram_desc, n_sel: int) -> int:
+    return int(_lib.rf_solve_pinv_workspace_bytes(C.byref(desc), n_sel))
+
+
+def rf_solve_pinv(desc: rf_gram_desc, state, lam: float, mode: int, rel_tol: float, sweeps: int,
+                  targets: Sequence[int], W, W_lp, b, ws, stream=None):
+    tg = (C.c_int32 * max(1, len(targets)))(*targets)
+    ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.rf_solve_pinv(C.byref(desc), _ptr(state), float(lam), int(mode), float(rel_tol), int(sweeps), tg,
+                              len(targets), _ptr(W), _ptr(W_lp), _ptr(b), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def cache_desc(n_kv_heads: int, head_dim: int, max_tokens: int, layout: int, dtype, block_size: int = 16):

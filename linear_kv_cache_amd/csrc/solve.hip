@@ -389,11 +389,13 @@ __global__ __launch_bounds__(256) void k_chol_diag(double* C, int64_t d, int J, 
 }
 
 // dg[i] = sqrt(A[i][i]) before the factorisation overwrites the diagonal, and rdg[i] = 1/dg[i]
-// (the unscaling steps multiply by it instead of dividing).
+// (the unscaling steps multiply by it instead of dividing).  A zero diagonal (a feature with
+// no variance: only the pseudo-inverse route gets that far) keeps the scale 1.
 __global__ void k_diag_sqrt(const double* A, int64_t d, double* dg, double* rdg) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < d) {
-        dg[i] = sqrt(fabs(A[i * d + i]));
+        const double a = fabs(A[i * d + i]);
+        dg[i] = a > 0.0 ? sqrt(a) : 1.0;
         rdg[i] = 1.0 / dg[i];
     }
 }
@@ -622,6 +624,107 @@ static rf_status inverse_factor(hipStream_t s, const SolveWs& w, int64_t d, doub
     return RF_OK;
 }
 
+// ---- eigendecomposition route (pseudo-inverse) ---------------------------------------------
+// Cyclic Jacobi in round-robin order: in round r of a sweep the d players (indices) meet in
+// d/2 disjoint pairs (player 0 fixed, the others turning one seat per round), so every pair
+// meets once per sweep and a round's rotations commute.
+
+// The player in seat ``pos`` of round r.
+__device__ inline int64_t rr_player(int64_t pos, int64_t r, int64_t d) {
+    return pos == 0 ? 0 : 1 + ((pos - 1 - r) % (d - 1) + (d - 1)) % (d - 1);
+}
+
+// Pair k of round r: (p, q) = the players in seats k and d-1-k, p < q, and the rotation (c, s)
+// that zeroes A[p][q] in J^T A J with J = I except J_pp = J_qq = c, J_pq = s, J_qp = -s
+// (the symmetric 2 x 2 Schur step).  A pair already below fp64 resolution keeps (1, 0).
+__global__ void k_jacobi_angles(const double* A, int64_t d, int64_t r, double* cs, int64_t* pq) {
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= d / 2) return;
+    int64_t p = rr_player(k, r, d), q = rr_player(d - 1 - k, r, d);
+    if (p > q) {
+        const int64_t t = p;
+        p = q;
+        q = t;
+    }
+    const double app = A[p * d + p], aqq = A[q * d + q], apq = A[p * d + q];
+    double c = 1.0, s = 0.0;
+    if (apq != 0.0 && fabs(apq) > 1e-300 + 1e-18 * sqrt(fabs(app * aqq))) {
+        const double tau = (aqq - app) / (2.0 * apq);
+        const double t = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(tau * tau + 1.0));
+        c = 1.0 / sqrt(t * t + 1.0);
+        s = t * c;
+    }
+    cs[2 * k] = c;
+    cs[2 * k + 1] = s;
+    pq[2 * k] = p;
+    pq[2 * k + 1] = q;
+}
+
+// A <- J^T A J and V <- V J for all pairs of the round: each 2 x 2 block (pair i rows, pair j
+// columns) of A changes on its own, as does each (row, pair j) couple of V.
+__global__ void k_jacobi_rotate(double* A, double* V, int64_t d, const double* cs, const int64_t* pq) {
+    const int64_t h = d / 2;
+    const int64_t na = h * h, nv = d * h;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < na + nv;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        if (t < na) {
+            const int64_t i = t / h, j = t - i * h;
+            const int64_t p = pq[2 * i], q = pq[2 * i + 1], u = pq[2 * j], w = pq[2 * j + 1];
+            const double ci = cs[2 * i], si = cs[2 * i + 1], cj = cs[2 * j], sj = cs[2 * j + 1];
+            const double a00 = A[p * d + u], a01 = A[p * d + w], a10 = A[q * d + u], a11 = A[q * d + w];
+            // rows: p' = c p - s q, q' = s p + c q; then columns the same way with pair j's turn
+            const double r00 = ci * a00 - si * a10, r01 = ci * a01 - si * a11;
+            const double r10 = si * a00 + ci * a10, r11 = si * a01 + ci * a11;
+            A[p * d + u] = cj * r00 - sj * r01;
+            A[p * d + w] = sj * r00 + cj * r01;
+            A[q * d + u] = cj * r10 - sj * r11;
+            A[q * d + w] = sj * r10 + cj * r11;
+        } else {
+            const int64_t e = t - na;
+            const int64_t row = e / h, j = e - row * h;
+            const int64_t u = pq[2 * j], w = pq[2 * j + 1];
+            const double cj = cs[2 * j], sj = cs[2 * j + 1];
+            const double v0 = V[row * d + u], v1 = V[row * d + w];
+            V[row * d + u] = cj * v0 - sj * v1;
+            V[row * d + w] = sj * v0 + cj * v1;
+        }
+    }
+}
+
+__global__ void k_identity(double* V, int64_t d) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < d * d; i += (int64_t)gridDim.x * blockDim.x)
+        V[i] = (i / d == i % d) ? 1.0 : 0.0;
+}
+
+// U = V diag(sqrt(f)) with f_i = 1/mu_i for mu_i = A[i][i] > rel_tol * max mu, else 0, so that
+// U U^T is the pseudo-inverse.  One work-group finds the largest eigenvalue; the scaling is
+// grid-strided over the elements of V (every work-group recomputes the maximum).
+__global__ __launch_bounds__(256) void k_pinv_scale(const double* A, int64_t d, double rel_tol, double* V) {
+    __shared__ double red[256];
+    double m = -INFINITY;
+    for (int64_t i = threadIdx.x; i < d; i += 256) m = fmax(m, A[i * d + i]);
+    red[threadIdx.x] = m;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if ((int)threadIdx.x < h) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + h]);
+        __syncthreads();
+    }
+    const double cut = rel_tol * red[0];
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < d * d; e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t col = e % d;
+        const double mu = A[col * d + col];
+        V[e] = (red[0] > 0.0 && mu > cut) ? V[e] / sqrt(mu) : 0.0;
+    }
+}
+
+// All rows of the centred, equilibrated, split cross moments (the Cholesky route computes them
+// in the spare work-groups of its diagonal-block launches).
+__global__ __launch_bounds__(256) void k_centre_split(CrossArgs ca, int ny) {
+    const int64_t c = blockIdx.x / ny;
+    const int64_t i0 = ((blockIdx.x % ny) * 256 + threadIdx.x) * 8;
+    if (c < ca.rows && i0 < ca.d) centre_split_row(ca, c, i0);
+}
+
 // ---- fit quality ------------------------------------------------------------------------
 constexpr int kR2Rows = 16;   // map rows per work-group
 
@@ -753,6 +856,97 @@ rf_status rf_fit_r2(const rf_gram_desc* desc, const void* d_state, double lambda
                        (const double*)(sp + GL.off_s_yy), (const int64_t*)(sp + GL.off_n), d, dy, ca, n_blk,
                        (const double*)d_ws, lambda, (int)(mode == RF_LAMBDA_REL_MEAN_DIAG), d_r2);
     return check_launch("rf_fit_r2: scores");
+}
+
+static size_t pinv_extra_bytes(int64_t d) { return round_up((size_t)(d * d * 8), 256) + round_up((size_t)d * 16, 256) * 2; }
+
+size_t rf_solve_pinv_workspace_bytes(const rf_gram_desc* desc, int32_t n_sel) {
+    rf_gram_layout_t GL;
+    if (n_sel < 0 || rf_gram_state_layout(desc, &GL) != RF_OK) return 0;
+    return solve_ws(nullptr, desc->d, gram_dy(desc), n_sel).total + pinv_extra_bytes(desc->d);
+}
+
+rf_status rf_solve_pinv(const rf_gram_desc* desc, const void* d_state, double lambda, rf_lambda_mode mode,
+                        double rel_tol, int32_t sweeps, const int32_t* targets, int32_t n_sel, float* d_W,
+                        void* d_W_lp, float* d_b, void* d_ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    rf_gram_layout_t GL;
+    rf_status st = rf_gram_state_layout(desc, &GL);
+    if (st != RF_OK) return st;
+    RF_REQUIRE(d_state && aligned(d_state, 256), RF_ERR_INVALID_ARG, "rf_solve_pinv: state must be non-null, 256-B aligned");
+    RF_REQUIRE(isfinite(lambda) && lambda >= 0.0, RF_ERR_INVALID_ARG, "rf_solve_pinv: lambda must be finite and >= 0");
+    RF_REQUIRE(mode == RF_LAMBDA_ABSOLUTE || mode == RF_LAMBDA_REL_MEAN_DIAG, RF_ERR_INVALID_ARG,
+               "rf_solve_pinv: bad lambda mode");
+    RF_REQUIRE(isfinite(rel_tol) && rel_tol >= 0.0 && rel_tol < 1.0, RF_ERR_INVALID_ARG,
+               "rf_solve_pinv: rel_tol must be in [0, 1)");
+    RF_REQUIRE(sweeps >= 1 && sweeps <= 64, RF_ERR_INVALID_ARG, "rf_solve_pinv: sweeps must be in [1, 64]");
+    RF_REQUIRE(n_sel >= 0 && n_sel <= kMaxSel, RF_ERR_UNSUPPORTED, "rf_solve_pinv: 0..64 selected targets");
+    RF_REQUIRE(n_sel == 0 || targets, RF_ERR_INVALID_ARG, "rf_solve_pinv: null targets");
+    for (int i = 0; i < n_sel; ++i)
+        RF_REQUIRE(targets[i] >= 0 && targets[i] < desc->n_targets, RF_ERR_INVALID_ARG,
+                   "rf_solve_pinv: target index out of range");
+    RF_REQUIRE(aligned(d_ws, 256), RF_ERR_INVALID_ARG, "rf_solve_pinv: workspace must be 256-B aligned");
+    RF_REQUIRE(aligned(d_W, 16) && aligned(d_W_lp, 16) && aligned(d_b, 4), RF_ERR_INVALID_ARG,
+               "rf_solve_pinv: W outputs must be 16-byte aligned");
+    const int64_t d = desc->d, dy = gram_dy(desc);
+    const SolveWs w = solve_ws(d_ws, d, dy, n_sel);
+    RF_REQUIRE(d_ws && ws_bytes >= w.total + pinv_extra_bytes(d), RF_ERR_WORKSPACE, "rf_solve_pinv: workspace too small");
+    double* V = (double*)((char*)d_ws + w.total);
+    double* cs = (double*)((char*)V + round_up((size_t)(d * d * 8), 256));
+    int64_t* pq = (int64_t*)((char*)cs + round_up((size_t)d * 16, 256));
+    hipStream_t s = (hipStream_t)stream;
+    const char* sp = (const char*)d_state;
+    const float* Sxx = (const float*)(sp + GL.off_S_xx);
+    const double* sx = (const double*)(sp + GL.off_s_x);
+    const int64_t* np = (const int64_t*)(sp + GL.off_n);
+
+    hipLaunchKernelGGL(k_centre_gram, dim3(grid_for(d * d)), dim3(256), 0, s, Sxx, sx, np, d, w.C);
+    RF_TRY(check_launch("rf_solve_pinv: centre"));
+    hipLaunchKernelGGL(k_add_lambda, dim3(1), dim3(256), 0, s, w.C, d, lambda, (int)(mode == RF_LAMBDA_REL_MEAN_DIAG));
+    RF_TRY(check_launch("rf_solve_pinv: lambda"));
+    hipLaunchKernelGGL(k_diag_sqrt, dim3(grid_for(d)), dim3(256), 0, s, w.C, d, w.dg, w.rdg);
+    RF_TRY(check_launch("rf_solve_pinv: diagonal"));
+    // A = V diag(mu) V^T by cyclic Jacobi (A becomes diag(mu) in place)
+    hipLaunchKernelGGL(k_identity, dim3(grid_for(d * d)), dim3(256), 0, s, V, d);
+    RF_TRY(check_launch("rf_solve_pinv: identity"));
+    const int64_t n_rot = (d / 2) * (d / 2) + d * (d / 2);
+    for (int sw = 0; sw < sweeps; ++sw) {
+        for (int64_t r = 0; r < d - 1; ++r) {
+            hipLaunchKernelGGL(k_jacobi_angles, dim3((unsigned)ceil_div(d / 2, 256)), dim3(256), 0, s, (const double*)w.C,
+                               d, r, cs, pq);
+            hipLaunchKernelGGL(k_jacobi_rotate, dim3(grid_for(n_rot)), dim3(256), 0, s, w.C, V, d, (const double*)cs,
+                               (const int64_t*)pq);
+        }
+        RF_TRY(check_launch("rf_solve_pinv: Jacobi sweep"));
+    }
+    // U = V diag(1/sqrt(mu)) over the kept eigenvalues; A^+ = U U^T (lower triangle, as the W
+    // product's operand preparation reads it)
+    hipLaunchKernelGGL(k_pinv_scale, dim3(grid_for(d * d)), dim3(256), 0, s, (const double*)w.C, d, rel_tol, V);
+    RF_TRY(check_launch("rf_solve_pinv: scale"));
+    RF_TRY(dgemm<true>(s, d, d, d, 1.0, V, d, V, d, 0.0, w.C, d, kLowerOnly));
+    if (n_sel == 0) return RF_OK;
+    const int64_t rows = (int64_t)n_sel * dy;
+    CrossArgs ca{};
+    ca.Syx = (const float*)(sp + GL.off_S_yx); ca.sy = (const double*)(sp + GL.off_s_y); ca.sx = sx; ca.np = np;
+    ca.rdg = w.rdg; ca.d = d; ca.dy = dy; ca.rows = rows; ca.Aq = w.Aq; ca.mu_y = w.mu_y;
+    for (int i = 0; i < n_sel; ++i) ca.tsel[i] = targets[i];
+    const int ny = (int)ceil_div(d, 2048);
+    hipLaunchKernelGGL(k_centre_split, dim3((unsigned)(rows * ny)), dim3(256), 0, s, ca, ny);
+    RF_TRY(check_launch("rf_solve_pinv: cross moments"));
+    hipLaunchKernelGGL(k_split_inverse, dim3((unsigned)(d / 64), (unsigned)(d / 64)), dim3(256), 0, s, w.C, w.dg, d, w.Bq);
+    RF_TRY(check_launch("rf_solve_pinv: split pseudo-inverse"));
+    WArgs wa{};
+    wa.Aq = w.Aq; wa.Bq = w.Bq; wa.rdg = w.rdg; wa.sx = sx; wa.np = np; wa.d = d; wa.rows = rows;
+    wa.tiles_j = (int)(d / 256); wa.tiles_c = (int)(rows / 256); wa.W = d_W; wa.Wlp = (bf16_t*)d_W_lp;
+    wa.bpart = w.bpart;
+    hipLaunchKernelGGL(k_wgemm, dim3((unsigned)(wa.tiles_j * wa.tiles_c)), dim3(PackedAGemm::kThr), 0, s, wa);
+    RF_TRY(check_launch("rf_solve_pinv: W product"));
+    if (d_b) {
+        hipLaunchKernelGGL(k_bias, dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0, s, w.bpart, wa.tiles_j, w.mu_y,
+                           rows, d_b);
+        RF_TRY(check_launch("rf_solve_pinv: bias"));
+    }
+    return RF_OK;
 }
 
 size_t rf_solve_workspace_bytes(const rf_gram_desc* desc, int32_t n_sel) {

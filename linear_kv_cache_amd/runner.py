@@ -12,7 +12,7 @@ from . import (RF_LAYOUT_CONTIGUOUS, RF_LAYOUT_PAGED, FillWeights, TranslateWeig
                rf_fit_r2, rf_fit_r2_workspace_bytes, rf_gram_select,
                rf_gram_accumulate, rf_gram_init,
                rf_gram_state_bytes, rf_gram_state_layout, rf_pack_weights, rf_rope_table, rf_solve,
-               rf_solve_workspace_bytes, rf_translate)
+               rf_solve_pinv, rf_solve_pinv_workspace_bytes, rf_solve_workspace_bytes, rf_translate)
 
 
 def device_bytes(n: int, device) -> torch.Tensor:
@@ -68,6 +68,18 @@ class GramState:
         ws = device_bytes(rf_fit_r2_workspace_bytes(self.desc, len(targets)), dev)
         rf_fit_r2(self.desc, self.buf, lam, mode, list(targets), W, out, ws, stream)
         return out
+
+    def solve_pinv(self, lam: float, mode: int, targets: Sequence[int], rel_tol: float = 1e-8, sweeps: int = 15,
+                   want_bf16=False, stream=None):
+        """The maps by the eigendecomposition pseudo-inverse route (rf_solve_pinv)."""
+        dev = self.buf.device
+        n_sel = len(targets)
+        W = torch.empty(n_sel, self.dy, self.d, dtype=torch.float32, device=dev)
+        Wlp = torch.empty(n_sel, self.dy, self.d, dtype=torch.bfloat16, device=dev) if want_bf16 else None
+        b = torch.empty(n_sel, self.dy, dtype=torch.float32, device=dev)
+        ws = device_bytes(rf_solve_pinv_workspace_bytes(self.desc, n_sel), dev)
+        rf_solve_pinv(self.desc, self.buf, lam, mode, rel_tol, sweeps, list(targets), W, Wlp, b, ws, stream)
+        return W, Wlp, b
 
     def solve(self, lam: float, mode: int, targets: Sequence[int], want_f32=True, want_bf16=True, stream=None,
               ws: Optional[torch.Tensor] = None):

@@ -314,3 +314,18 @@ def test_gram_select_validation_before_enqueue():
         with pytest.raises(rf.RidgeFillError) as e:
             rf.rf_gram_select(src, 256, kw["bw"], kw["blocks"], kw.get("out", ok), kw.get("sout", 512), stream=0)
         assert e.value.status == status, kw
+
+
+def test_solve_pinv_validation_before_enqueue():
+    desc = rf.gram_desc(256, 2, torch.float32)
+    assert rf.rf_solve_pinv_workspace_bytes(desc, 2) > rf.rf_solve_workspace_bytes(desc, 2) + 256 * 256 * 8
+    ws = torch.empty(16, dtype=torch.uint8)
+    for lam, tol, sweeps, targets, status in [(-1.0, 1e-8, 15, [0], rf.RF_ERR_INVALID_ARG),
+                                              (0.0, 1.5, 15, [0], rf.RF_ERR_INVALID_ARG),
+                                              (0.0, 1e-8, 0, [0], rf.RF_ERR_INVALID_ARG),
+                                              (0.0, 1e-8, 15, [2], rf.RF_ERR_INVALID_ARG),
+                                              (0.0, 1e-8, 15, [0], rf.RF_ERR_WORKSPACE)]:
+        with pytest.raises(rf.RidgeFillError) as e:
+            rf._check(rf._lib.rf_solve_pinv(C.byref(desc), 256, lam, 0, tol, sweeps, (C.c_int32 * 1)(*targets), 1,
+                                            None, None, None, 256, 16, None))
+        assert e.value.status == status, (lam, tol, sweeps, targets)
