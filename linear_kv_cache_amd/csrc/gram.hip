@@ -1,14 +1,14 @@
 // One streaming pass of second moments over calibration chunks (RidgeFill project page,
 // "Method" step 2: the maps are fitted in closed form from one pass over calibration text).
 //
-// bf16 chunks take two launches:
-//   k_gram_colsum    : exact fp64 column sums of X and every Y_l (bf16 values have 8-bit
-//                      significands; each column is summed in one fixed order).
-//   k_gram_pipe      : S_yx tiles (Y_l^T X) and the S_xx upper triangle (X^T X, 256 x 256
-//                      tiles) on the software-pipelined bf16 MFMA core, reading X and Y_l as
-//                      they lie ([rows][d]: the reduction runs over rows, the core's M-major
-//                      operand form), in an XCD-aware order; each tile adds its fp32 result
-//                      into the state (one owner per element).
+// bf16 chunks take one launch, k_gram_pipe:
+//   - S_yx tiles (Y_l^T X) and the S_xx upper triangle (X^T X, 256 x 256 tiles) on the
+//     software-pipelined bf16 MFMA core, reading X and Y_l as they lie ([rows][d]: the
+//     reduction runs over rows, the core's M-major operand form), in an XCD-aware order; each
+//     tile adds its fp32 result into the state (one owner per element);
+//   - then, in the launch's last work-groups, exact fp64 column sums of X and every Y_l (bf16
+//     values have 8-bit significands; each column is summed in one fixed order).  They run on
+//     the CUs the last partial round of tiles leaves idle.
 // fp32 chunks (small widths) run one launch of the plain tile loop, which transposes 4 x 4
 // blocks on their way to LDS and sums the columns on the operand already in registers, and a
 // small pass for the targets' column sums of squares.
@@ -165,8 +165,8 @@ struct ColsumArgs {
 // One work-group per 64 columns of one matrix (X first, then each Y_l): thread t sums columns 8 (t & 7) .. + 8 over rows
 // r = t >> 3 (mod 32) in ascending order (eight rows in flight), then the 32 row groups are added
 // in a fixed order: the result does not depend on scheduling.
-__global__ __launch_bounds__(256) void k_gram_colsum(ColsumArgs a) {
-    const int b = (int)blockIdx.x;
+// red: LDS of at least 2 * 32 * 65 doubles.
+__device__ inline void colsum_block(const ColsumArgs& a, int b, double (*red)[32][64 + 1]) {
     const int by = b - a.blocks_x;
     const int g = by < 0 ? 0 : 1 + by / a.blocks_y;
     const int c0 = (by < 0 ? b : by % a.blocks_y) * 64;
@@ -198,7 +198,6 @@ __global__ __launch_bounds__(256) void k_gram_colsum(ColsumArgs a) {
         for (int u = 0; u < 8; ++u) add(v[u]);
     }
     for (; r < a.rows; r += 32) add(*(const u32x4*)(src + r * ld));
-    __shared__ double red[2][32][64 + 1];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         red[0][rg][ch * 8 + e] = s[e];
@@ -255,10 +254,17 @@ struct PipeGramArgs {
 // one S row: one 16-byte read-modify-write.
 using GramCore = PipeGemmW<4, 2, true>;
 
-__global__ __launch_bounds__(GramCore::kThr) void k_gram_pipe(PipeGramArgs a) {
+// Work-groups past the product tiles compute the column sums (colsum_block): dispatched last,
+// they run on the CUs the last partial round of tiles leaves idle.
+__global__ __launch_bounds__(GramCore::kThr) void k_gram_pipe(PipeGramArgs a, ColsumArgs ca) {
     using G = GramCore;
     __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
-    const int v = xcd_order((int)blockIdx.x, (int)gridDim.x);
+    const int n_tiles = a.n_yx + a.n_xx;
+    if ((int)blockIdx.x >= n_tiles) {
+        colsum_block(ca, (int)blockIdx.x - n_tiles, (double (*)[32][64 + 1])lds);
+        return;
+    }
+    const int v = xcd_order((int)blockIdx.x, n_tiles);
     int mt, nt;
     const bool is_xx = v >= a.n_yx;
     if (is_xx) {
@@ -516,16 +522,13 @@ rf_status rf_gram_accumulate(const rf_gram_desc* desc, void* d_state, const void
             ca.csq[l + 1] = syy + (int64_t)l * dy;
         }
         ca.rows = pr; ca.blocks_x = desc->d / 64; ca.blocks_y = (int32_t)(dy / 64);
-        hipLaunchKernelGGL(k_gram_colsum, dim3((unsigned)(ca.blocks_x + desc->n_targets * ca.blocks_y)), dim3(256), 0,
-                           strm, ca);
-        st = check_launch("rf_gram_accumulate: column sums");
-        if (st != RF_OK) return st;
+        const int n_colsum = ca.blocks_x + desc->n_targets * ca.blocks_y;
         PipeGramArgs pa{};
         pa.X = (const bf16_t*)d_X + r0 * ldx; pa.ldx = ldx;
         for (int l = 0; l < desc->n_targets; ++l) pa.Y[l] = (const bf16_t*)d_Y[l] + r0 * ldy;
         pa.ldy = ldy; pa.rows = pr; pa.d = desc->d; pa.dy = (int32_t)dy; pa.tiles_m = tiles_m;
         pa.n_xx = n_xx; pa.n_yx = n_yx; pa.Sxx = Sxx; pa.Syx = Syx; pa.n = np;
-        hipLaunchKernelGGL(k_gram_pipe, dim3((unsigned)(n_xx + n_yx)), dim3(GramCore::kThr), 0, strm, pa);
+        hipLaunchKernelGGL(k_gram_pipe, dim3((unsigned)(n_xx + n_yx + n_colsum)), dim3(GramCore::kThr), 0, strm, pa, ca);
         st = check_launch("rf_gram_accumulate: products");
         if (st != RF_OK) return st;
     }
