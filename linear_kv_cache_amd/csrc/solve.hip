@@ -759,7 +759,7 @@ __global__ __launch_bounds__(256) void k_r2_partial(const float* Syx, const doub
     red[1][threadIdx.x] = ww;
     __syncthreads();
     for (int h = 128; h > 0; h >>= 1) {
-        if (threadIdx.x < h) {
+        if ((int)threadIdx.x < h) {
             red[0][threadIdx.x] += red[0][threadIdx.x + h];
             red[1][threadIdx.x] += red[1][threadIdx.x + h];
         }
@@ -791,7 +791,7 @@ __global__ __launch_bounds__(256) void k_r2_final(const float* Sxx, const double
     red[1][threadIdx.x] = diag;
     __syncthreads();
     for (int h = 128; h > 0; h >>= 1) {
-        if (threadIdx.x < h) {
+        if ((int)threadIdx.x < h) {
             red[0][threadIdx.x] += red[0][threadIdx.x + h];
             red[1][threadIdx.x] += red[1][threadIdx.x + h];
         }
