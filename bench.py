@@ -191,6 +191,62 @@ def translate_leg(steps: int, stream, dev, tc=None):
             "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
+def fill_only(cfg, steps: int, warmup: int):
+    """``--fill-only``: time rf_fill alone over a configuration's whole filled range, in its own
+    chunks (the 27B-shaped and long-context workloads have no calibration set: their maps are
+    the random-init law), and print one JSON line for it.  Not the benchmark's headline line."""
+    import torch
+
+    import synth
+    from linear_kv_cache_amd.runner import Filler, alloc_cache, fill_weights
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    layers = cfg.filled_layers
+    T = cfg.prompt_tokens
+    log(f"fill-only workload {cfg.name}: d={cfg.d} layers={len(layers)} fill [{cfg.fill_t0}, {cfg.fill_t1}) "
+        f"in chunks of {cfg.fill_chunk}{' (paged)' if cfg.paged else ''}")
+    ws = [synth.layer_weights(cfg, l, device=dev) for l in layers]
+    fw = fill_weights(cfg.d, cfg.n_kv_heads, cfg.head_dim, cfg.rms_eps, cfg.torch_dtype, [w.W_map for w in ws],
+                      [w.b_map for w in ws], [w.gamma for w in ws], [w.W_k for w in ws], [w.W_v for w in ws])
+    del ws
+    X = synth.hidden_states(cfg, cfg.fill_tokens, "prompt", device=dev)
+    table = synth.block_table(cfg, T, device=dev) if cfg.paged else None
+    cache = alloc_cache(len(layers), cfg.n_kv_heads, cfg.head_dim, T, cfg.torch_dtype, dev, paged=cfg.paged,
+                        block_size=cfg.block_size, block_table=table,
+                        n_blocks=(int(table.max()) + 1) if table is not None else None)
+    filler = Filler(fw, cfg.rope_base, T, cfg.fill_chunk, dev, ws_slots=8)
+
+    def run():
+        for c0 in range(cfg.fill_t0, cfg.fill_t1, cfg.fill_chunk):
+            c1 = min(cfg.fill_t1, c0 + cfg.fill_chunk)
+            filler.fill(X[c0 - cfg.fill_t0:c1 - cfg.fill_t0], c0, c1, 0, cache, stream)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    med = statistics.median(ms)
+    tflops = cfg.fill_tokens * len(layers) * cfg.fill_flop_per_token_layer() / (med / 1e3) / 1e12
+    print(json.dumps({"metric": "filled tokens/sec (all filled layers) + % bf16 MFMA peak, fill only",
+                      "config": {"workload": cfg.name, "d": cfg.d, "filled_layers": len(layers),
+                                 "fill_tokens": cfg.fill_tokens, "fill_chunk": cfg.fill_chunk, "paged": cfg.paged},
+                      "steps": steps, "warmup": warmup, "ms_median": round(med, 3),
+                      "tokens_per_s": round(cfg.fill_tokens / (med / 1e3), 1), "tflops": round(tflops, 1),
+                      "frac_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+                      "flop_per_token_layer": cfg.fill_flop_per_token_layer(),
+                      "cache_write_GBps": round(cfg.fill_tokens * len(layers) * 4 * cfg.kv_width / (med / 1e3) / 1e9,
+                                                1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -206,6 +262,8 @@ def main():
                          "GEMMs on the same maps, projections and prompt states")
     ap.add_argument("--no-translate", action="store_true", help="skip the cache-translator leg")
     ap.add_argument("--no-streamed", action="store_true", help="skip the streamed-maps leg")
+    ap.add_argument("--fill-only", action="store_true",
+                    help="time the fill alone over --config's filled range (e.g. C3, C5) and print its own line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 1 GiB device-to-device copy before the steps, a known-size reference "
                          "for HBM byte counters")
@@ -222,6 +280,9 @@ def main():
     from linear_kv_cache_amd.runner import Filler, GramState, alloc_cache, device_bytes, pack_weights
 
     cfg = synth.CONFIGS[args.config]
+    if args.fill_only:
+        fill_only(cfg, args.steps, args.warmup)
+        return
     if cfg.calib_rows == 0 or cfg.fill_tokens == 0 or cfg.dtype != "bf16":
         raise SystemExit(f"{args.config} is a parity-test configuration, not a bench workload "
                          "(the bench times the bf16 fit-then-fill pipeline)")
