@@ -247,6 +247,68 @@ def fill_only(cfg, steps: int, warmup: int):
                                                 1)}), flush=True)
 
 
+def fit_only(cfg, steps: int, warmup: int):
+    """``--fit-only``: time the fit alone on a configuration (e.g. the fit-heavy C4: every
+    calibration chunk through rf_gram_accumulate, then one rf_solve per lambda of the
+    configuration on the shared state) and print one JSON line for it."""
+    import torch
+
+    import linear_kv_cache_amd as rf
+    import synth
+    from linear_kv_cache_amd.runner import GramState, device_bytes
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    L, d = cfg.n_targets, cfg.d
+    layers = [cfg.split + l for l in range(L)]
+    n_chunks = cfg.calib_rows // cfg.calib_chunk
+    log(f"fit-only workload {cfg.name}: d={d} targets={L} N={cfg.calib_rows} in {n_chunks} chunks, "
+        f"lambdas={cfg.lambdas}; drawing inputs on the GPU")
+    Xc = [synth.hidden_states(cfg, cfg.calib_chunk, "calib", chunk=c, device=dev) for c in range(n_chunks)]
+    Yc = [[synth.late_layer_inputs(cfg, Xc[c], l, chunk=c) for l in layers] for c in range(n_chunks)]
+    state = GramState(d, L, cfg.torch_dtype, dev)
+    ws = device_bytes(rf.rf_solve_workspace_bytes(state.desc, L), dev)
+    W_lp = torch.empty(L, d, d, dtype=torch.bfloat16, device=dev)
+    b = torch.empty(L, d, dtype=torch.float32, device=dev)
+    info = torch.empty(1, dtype=torch.int32, device=dev)
+
+    def step():
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 + len(cfg.lambdas))]
+        ev[0].record(stream)
+        rf.rf_gram_init(state.desc, state.buf, stream)
+        for c in range(n_chunks):
+            rf.rf_gram_accumulate(state.desc, state.buf, Xc[c], Yc[c], stream=stream)
+        ev[1].record(stream)
+        for i, lam in enumerate(cfg.lambdas):
+            rf.rf_solve(state.desc, state.buf, lam, rf.RF_LAMBDA_ABSOLUTE, list(range(L)), None, W_lp, b, info, ws,
+                        stream)
+            ev[2 + i].record(stream)
+        return ev
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(info.item()) != 0:
+        raise SystemExit(f"solve reported a non-positive pivot: {int(info.item())}")
+    recs = []
+    for _ in range(steps):
+        recs.append(step())
+        torch.cuda.synchronize()
+    gram = statistics.median(r[0].elapsed_time(r[1]) for r in recs)
+    solves = [statistics.median(r[1 + i].elapsed_time(r[2 + i]) for r in recs) for i in range(len(cfg.lambdas))]
+    tflops = cfg.calib_rows * cfg.fit_flop_per_row() / (gram / 1e3) / 1e12
+    print(json.dumps({"metric": "ridge-fit rows/sec, fit only",
+                      "config": {"workload": cfg.name, "d": d, "targets": L, "calib_rows": cfg.calib_rows,
+                                 "calib_chunk": cfg.calib_chunk, "lambdas": list(cfg.lambdas)},
+                      "steps": steps, "warmup": warmup, "gram_ms_median": round(gram, 3),
+                      "rows_per_s": round(cfg.calib_rows / (gram / 1e3), 1), "gram_tflops": round(tflops, 1),
+                      "gram_frac_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+                      "solve_ms_median_per_lambda": [round(x, 3) for x in solves],
+                      "rows_per_s_incl_solves": round(cfg.calib_rows / ((gram + sum(solves)) / 1e3), 1),
+                      "flop_per_row": cfg.fit_flop_per_row()}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -264,6 +326,9 @@ def main():
     ap.add_argument("--no-streamed", action="store_true", help="skip the streamed-maps leg")
     ap.add_argument("--fill-only", action="store_true",
                     help="time the fill alone over --config's filled range (e.g. C3, C5) and print its own line")
+    ap.add_argument("--fit-only", action="store_true",
+                    help="time the fit alone on --config (e.g. C4: all chunks, one solve per lambda) and print "
+                         "its own line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 1 GiB device-to-device copy before the steps, a known-size reference "
                          "for HBM byte counters")
@@ -282,6 +347,9 @@ def main():
     cfg = synth.CONFIGS[args.config]
     if args.fill_only:
         fill_only(cfg, args.steps, args.warmup)
+        return
+    if args.fit_only:
+        fit_only(cfg, args.steps, args.warmup)
         return
     if cfg.calib_rows == 0 or cfg.fill_tokens == 0 or cfg.dtype != "bf16":
         raise SystemExit(f"{args.config} is a parity-test configuration, not a bench workload "
