@@ -510,6 +510,33 @@ def main():
             "fused_fill_ms_median": round(fms, 3),
             "fused_fill_frac_bf16_peak": round(fill_flop / (fms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
         del Wt, Wkv, H, KV
+        # the Gram's products as one library GEMM on the same chunk: [X | Y_1 .. Y_L]^T X, the
+        # shape of a linear layer's weight gradient (both operands row-major over the rows, the
+        # left one read through a transposed view), full square, bf16 output
+        XY = torch.cat([Xc[0]] + list(Yc[0]), dim=1)
+        G = torch.empty(d, XY.shape[1], dtype=torch.bfloat16, device=dev)
+        lib_gram_flop = 2 * cfg.calib_chunk * d * XY.shape[1]
+
+        def library_gram():
+            torch.matmul(Xc[0].t(), XY, out=G)
+
+        library_gram()
+        torch.cuda.synchronize()
+        lib_g, ours_g = [], []
+        for _ in range(args.steps):
+            ours_g.append(timed(lambda: rf.rf_gram_accumulate(state.desc, state.buf, Xc[0], Yc[0],
+                                                              stream=stream)))
+            lib_g.append(timed(library_gram))
+        gms, oms = statistics.median(lib_g), statistics.median(ours_g)
+        out["library_reference"]["gram"] = {
+            "what": f"torch.matmul (hipBLASLt) of X^T [X | Y] over one {cfg.calib_chunk}-row chunk, full square, "
+                    "bf16 output, no fp32 accumulation into a state or column sums; alternated with "
+                    "rf_gram_accumulate on the same chunk",
+            "ms_median": round(gms, 3), "tflops": round(lib_gram_flop / (gms / 1e3) / 1e12, 1),
+            "frac_bf16_peak": round(lib_gram_flop / (gms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "ours_ms_median": round(oms, 3),
+            "ours_frac_bf16_peak": round(gram_flop_per_launch / (oms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        del XY, G
     if not args.no_streamed:
         log("streamed maps: the fill with its maps in page-locked host memory")
         out["fill_streamed"] = streamed_leg(args.steps, stream, dev, cfg, fw, Xp, cache, filler)
