@@ -65,6 +65,29 @@ def test_fill_single_token_and_tile_edges():
         _check(run_fill_case(FillCase(SMALL_BF16, t0, t1, n_layers=1)), f"rows [{t0},{t1})")
 
 
+def test_empty_calls_change_nothing():
+    # an empty token range (t0 == t1, at the start, inside and at the end of the prompt) and a
+    # zero-row calibration chunk are no-ops: sentinel caches and an accumulated state keep every byte
+    from linear_kv_cache_amd.runner import Filler, GramState, alloc_cache, fill_weights
+    cfg = SMALL_BF16
+    ws = [synth.layer_weights(cfg, l, device="cuda") for l in cfg.filled_layers[:2]]
+    fw = fill_weights(cfg.d, cfg.n_kv_heads, cfg.head_dim, cfg.rms_eps, cfg.torch_dtype, [w.W_map for w in ws],
+                      [w.b_map for w in ws], [w.gamma for w in ws], [w.W_k for w in ws], [w.W_v for w in ws])
+    X = synth.hidden_states(cfg, 300, "prompt", device="cuda")
+    cache = alloc_cache(2, cfg.n_kv_heads, cfg.head_dim, 300, cfg.torch_dtype, "cuda", sentinel=3.0)
+    filler = Filler(fw, cfg.rope_base, 300, 300, "cuda")
+    for t in (0, 17, 300):
+        filler.fill(X, t, t, 0, cache)
+    st = GramState(cfg.d, 2, cfg.torch_dtype, "cuda")
+    Ys = [synth.late_layer_inputs(cfg, X, cfg.split + l) for l in range(2)]
+    st.accumulate(X, Ys)
+    before = st.buf.clone()
+    st.accumulate(X[:0], [Y[:0] for Y in Ys])
+    torch.cuda.synchronize()
+    assert all(bool(torch.all(t == 3.0)) for t in cache.k + cache.v)
+    assert torch.equal(st.buf, before) and int(st.n().item()) == 300
+
+
 def test_fill_is_deterministic():
     from linear_kv_cache_amd.runner import Filler, alloc_cache, fill_weights
     cfg = SMALL_BF16
