@@ -30,11 +30,11 @@ sys.path.insert(0, ROOT)
 
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
-# HBM bytes of one rf_gram_accumulate call (8192 rows, d=4096, 16 targets), from two
+# HBM bytes of one rf_gram_accumulate call (32768 rows, d=4096, 16 targets), from two
 # rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of this benchmark, each scaled by what the
 # counter reads for a 1 GiB device copy; profiles/pmc_traffic_llama8b-shaped_d4096_T16384.md has the
-# commands and the figures; set to None whenever k_gram_pipe changes.
-GRAM_TRAFFIC = (4623882 * 2 + 1170147) * 1024   # 10.67e9 B
+# commands and the figures; set to None whenever k_gram_pipe or the chunk size changes.
+GRAM_TRAFFIC = (19436865 * 2 + 1164248) * 1024   # 41.0e9 B
 METRIC = "filled tokens/sec (all filled layers) + % bf16 MFMA peak; ridge-fit rows/sec"
 
 

@@ -84,7 +84,7 @@ C1 = Config(name="tiny-fp32-d256", d=256, n_layers=8, split=4, n_kv_heads=4, hea
 
 C2 = Config(name="llama8b-shaped-d4096-T16384", d=4096, n_layers=32, split=16, n_kv_heads=8,
             head_dim=128, rms_eps=1e-6, rope_base=5e5, dtype="bf16", calib_rows=65536,
-            calib_chunk=8192, lambdas=(1e-1,), prompt_tokens=16384, fill_t0=0, fill_t1=16384,
+            calib_chunk=32768, lambdas=(1e-1,), prompt_tokens=16384, fill_t0=0, fill_t1=16384,
             fill_chunk=16384, paged=False, block_size=16, x_law="lognormal_scales",
             y_law="identity_perm", fill_maps="fitted", seed=1002)
 
