@@ -98,6 +98,33 @@ def test_gram_strided_rows_and_no_targets():
     assert torch.equal(st0.S_xx(), st.S_xx()) and torch.equal(st0.s_x(), st.s_x()) and int(st0.n().item()) == rows
 
 
+def test_gram_pieces_for_32_bit_offsets():
+    """A row stride of 2^20 elements caps one launch at 896 rows (the products address X with
+    32-bit byte offsets), so a 2000-row chunk runs as pieces of 896, 896 and 208 rows.  The state
+    equals three calls of those sizes on a contiguous copy bit for bit, and the oracle's sums
+    within the usual bounds."""
+    from linear_kv_cache_amd.runner import GramState
+    cfg = SMALL_BF16
+    d, L, rows, ld = cfg.d, 2, 2000, 1 << 20
+    X = synth.hidden_states(cfg, rows, "calib", device="cuda")
+    Ys = [synth.late_layer_inputs(cfg, X, cfg.split + l) for l in range(L)]
+    wide = torch.zeros(rows, ld, dtype=X.dtype, device="cuda")   # 4 GiB
+    wide[:, ld - d:] = X
+    Xv = wide[:, ld - d:]
+    assert Xv.stride(0) == ld
+    st = GramState(d, L, cfg.torch_dtype, "cuda")
+    st.accumulate(Xv, Ys)
+    ref = GramState(d, L, cfg.torch_dtype, "cuda")
+    for r0, r1 in ((0, 896), (896, 1792), (1792, rows)):
+        ref.accumulate(X[r0:r1], [Y[r0:r1] for Y in Ys])
+    torch.cuda.synchronize()
+    del wide, Xv
+    res = _gram_errors(dict(X=X, Ys=Ys, state=st))
+    log(f"[fit] 2^20 row stride, pieces: gram={res}")
+    assert torch.equal(st.buf, ref.buf)
+    assert res["n"] == rows and max(res["e_xx"], res["e_yx"]) <= 1e-5 and max(res["e_sx"], res["e_sy"]) <= 1e-12
+
+
 def test_fit_not_spd_reports_pivot():
     case = FitCase(synth.C1, 1024, [1024], 0.0, zero_column=77, n_targets=1)
     res = run_fit_case(case)
