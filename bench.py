@@ -6,7 +6,7 @@ One step is one pass of the whole path over one batch of synthetic input, reside
         the ridge maps of every filled layer (rf_solve, bf16 maps out);
   fill: fill every prompt token of every filled layer with those maps (rf_fill).
 Default workload: the Llama-8B-shaped configuration (d=4096, 32 layers split at 16, GQA
-8 x 128, RoPE base 5e5, calibration N=65536 in 8192-row chunks, lambda=0.1, T=16384).
+8 x 128, RoPE base 5e5, calibration N=65536 in 32768-row chunks, lambda=0.1, T=16384).
 
 Prints one JSON line.  ``value`` is filled tokens per second of fill time; the fit's rows
 per second, per-phase times, the dominant kernel's roofline and the CPU oracle baseline ride
