@@ -134,6 +134,28 @@ def test_fit_not_spd_reports_pivot():
     assert res["info"] == e.value.pivot == 78
 
 
+def test_solve_with_no_targets_reports_the_pivot_only():
+    # n_sel = 0: the factorisation runs (its info is the only output) and no map is written
+    from linear_kv_cache_amd.runner import GramState
+    cfg = synth.C1
+    X = synth.hidden_states(cfg, 1024, "calib", device="cuda")
+    Ys = [synth.late_layer_inputs(cfg, X, cfg.split)]
+    st = GramState(cfg.d, 1, cfg.torch_dtype, "cuda")
+    st.accumulate(X, Ys)
+    X0 = X.clone()
+    X0[:, 77] = 0
+    st0 = GramState(cfg.d, 1, cfg.torch_dtype, "cuda")
+    st0.accumulate(X0, Ys)
+    infos = []
+    for state, lam in ((st, 0.0), (st0, 0.0), (st0, 1e-2)):
+        W, Wlp, b, info = state.solve(lam, 0, [])
+        torch.cuda.synchronize()
+        assert W.numel() == 0 and Wlp.numel() == 0 and b.numel() == 0
+        infos.append(int(info.item()))
+    log(f"[fit] no targets: infos={infos}")
+    assert infos == [0, 78, 0]
+
+
 def test_gram_deterministic_and_resumable():
     import linear_kv_cache_amd as rf
     from linear_kv_cache_amd.runner import GramState
