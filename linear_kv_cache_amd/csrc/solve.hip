@@ -318,7 +318,6 @@ __global__ __launch_bounds__(256) void k_chol_diag(double* C, int64_t d, int J, 
         return;
     }
     if (threadIdx.x >= 64) return;   // the factorisation is one wave's (no barriers below)
-    __shared__ double piv[kNB];
     __shared__ __attribute__((aligned(16))) double Lt[kNB][kNB + 2];
     const int i = threadIdx.x;
     const int64_t off = (int64_t)J * kNB;
@@ -366,15 +365,14 @@ __global__ __launch_bounds__(256) void k_chol_diag(double* C, int64_t d, int J, 
 #pragma unroll
     for (int k = 0; k < kNB; ++k) C[(off + i) * d + off + k] = k <= i ? a[k] : 0.0;
     if (i == 0 && !prior && fail != 0) *info = fail;
-    // 1 / L[r][r] for every r, broadcast through LDS
-    piv[i] = rinv;
+    // 1 / L[k][k] is lane k's rinv, read across lanes (no LDS round trip on the chain)
     double* D = Dinv + (int64_t)J * kNB * kNB;
     double acc[kNB];   // lane c: sum_{k < r, so far} L[r][k] X[k][c]
 #pragma unroll
     for (int r = 0; r < kNB; ++r) acc[r] = 0.0;
 #pragma unroll
     for (int k = 0; k < kNB; ++k) {
-        const double xk = ((k == i ? 1.0 : 0.0) - acc[k]) * piv[k];
+        const double xk = ((k == i ? 1.0 : 0.0) - acc[k]) * readlane_f64(rinv, k);
         D[k * kNB + i] = xk;
         if ((k & 1) == 0 && k + 1 < kNB) acc[k + 1] += Lt[k][k + 1] * xk;
 #pragma unroll
