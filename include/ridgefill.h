@@ -160,9 +160,9 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state,
                    float* d_W, void* d_W_lp, float* d_b, int32_t* d_info,
                    void* d_ws, size_t ws_bytes, void* stream);
 
-/* The same maps by the symmetric eigendecomposition route (KV-Lingo page, Appendix B.2
- * "Protocol": the normal equations solved by symmetric eigendecomposition, eigenvalues below a
- * relative tolerance treated as zero).  C + lambda I = V diag(mu) V^T by cyclic Jacobi in fp64
+/* The same maps by the symmetric eigendecomposition route (KV-Lingo page, appendix on the
+ * training procedure, "Stage 1": the per-layer normal equations solved once by symmetric
+ * eigendecomposition, eigenvalues below a relative tolerance counting as zero).  C + lambda I = V diag(mu) V^T by cyclic Jacobi in fp64
  * (``sweeps`` sweeps of round-robin rotations; 15 reach fp64 accuracy on the widths used here);
  * A^+ keeps 1/mu_i for mu_i > rel_tol * max mu; then W_l = B_l A^+ and b_l as in rf_solve (the
  * same split-bf16 product).  For a regular system this is rf_solve's map; for a singular one
@@ -338,8 +338,10 @@ rf_status rf_fill(const rf_fill_weights* weights, int32_t n_layers,
  * Layers go in chunks of layers_per_slot (1..32): chunk c is copied into slot
  * c % ring_slots on copy_stream once the fill of chunk c - ring_slots has left that slot, and
  * filled on ``stream`` once its copy has landed (HIP events order the two streams; they are
- * created and released inside the call).  Two or more slots let the copy of one chunk run
- * under the fill of the previous one.  The host maps must stay valid until ``stream``
+ * created and released inside the call).  The call's first copy waits for everything enqueued
+ * on ``stream`` before the call, so consecutive calls on one stream (a long prompt filled in
+ * token chunks) are ordered like any other calls on it.  Two or more slots let the copy of one
+ * chunk run under the fill of the previous one.  The host maps must stay valid until ``stream``
  * reaches the end of the call's work.
  * ------------------------------------------------------------------------------------- */
 size_t rf_fill_streamed_ring_bytes(const rf_fill_weights* weights, int32_t ring_slots, int32_t layers_per_slot);

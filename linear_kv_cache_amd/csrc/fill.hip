@@ -792,7 +792,9 @@ static rf_status check_fill(const char* what, const rf_fill_weights* w, int32_t 
 
 // The maps of a streamed fill, layers_per_slot layers per ring slot: copy chunk c into slot
 // c % ring_slots on copy_stream once the fill of chunk c - ring_slots has released the slot,
-// and fill chunk c on stream once its copy has landed.  The events only order the two
+// and fill chunk c on stream once its copy has landed.  The first copy also waits for all
+// work enqueued on stream before the call, so back-to-back calls (a chunked prompt) never
+// overwrite a slot an earlier call's fill still reads.  The events only order the two
 // streams; they are released when the work they mark completes.
 template <typename T>
 static rf_status launch_fill_streamed(const rf_fill_weights* w, int32_t n_layers, const void* X, int64_t ldx,
@@ -816,6 +818,20 @@ static rf_status launch_fill_streamed(const rf_fill_weights* w, int32_t n_layers
             destroy();
             return fail(RF_ERR_HIP, "rf_fill_streamed: event creation failed");
         }
+    }
+    // The ring's slots may still be read by fills an earlier call (or any other work) left on
+    // ``stream``: no copy of this call starts before ``stream`` has reached this point.
+    hipEvent_t entry = nullptr;
+    if (hipEventCreateWithFlags(&entry, hipEventDisableTiming) != hipSuccess) {
+        destroy();
+        return fail(RF_ERR_HIP, "rf_fill_streamed: event creation failed");
+    }
+    hipError_t e0 = hipEventRecord(entry, stream);
+    if (e0 == hipSuccess) e0 = hipStreamWaitEvent(copy_stream, entry, 0);
+    (void)hipEventDestroy(entry);
+    if (e0 != hipSuccess) {
+        destroy();
+        return fail(RF_ERR_HIP, std::string("rf_fill_streamed: stream ordering failed: ") + hipGetErrorString(e0));
     }
     const void* maps[kMaxGroup];
     rf_fill_weights cw = *w;

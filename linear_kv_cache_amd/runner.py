@@ -2,6 +2,7 @@
 RoPE tables with torch, then call the library.  No arithmetic of the method happens here."""
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass
 from typing import List, Optional, Sequence
 
@@ -96,13 +97,18 @@ class GramState:
 
 
 def greedy_sources(state: GramState, block_width: int, nu: int, lam: float, mode: int,
-                   targets: Optional[Sequence[int]] = None, stream=None) -> List[List[int]]:
+                   targets: Optional[Sequence[int]] = None, stream=None, return_order: bool = False):
     """Greedy match (KV-Lingo page, section 3.1): for each target, forward selection over the
     column blocks of X (source layers) by the R^2 of the joint ridge fit, all of it read off
     the one accumulated state.  Each step scores every candidate set E + {s} with
     rf_gram_select -> rf_solve -> rf_fit_r2 (a set shared by several targets is solved once
     for all of them) and keeps the best per target (equal scores: the shallower layer).
-    The choices are host decisions on the scores; every number comes from the library."""
+    A candidate set whose regularised Gram is not positive definite (the solve's pivot
+    report, e.g. lambda = 0 with a source layer of constant rows) or whose score is not
+    finite ranks last; a step with no valid candidate raises.
+    The choices are host decisions on the scores; every number comes from the library.
+    Returns the chosen layers per target, ascending; with ``return_order`` also the picks in
+    the order they were made."""
     dev = state.buf.device
     n_blocks = state.d // block_width
     targets = list(range(state.n_targets)) if targets is None else list(targets)
@@ -124,18 +130,23 @@ def greedy_sources(state: GramState, block_width: int, nu: int, lam: float, mode
             tsel = sorted(set(targets[ti] for ti in users))
             W, _, _, info = sub.solve(lam, mode, tsel, want_bf16=False, stream=stream)
             r2 = sub.r2(lam, mode, tsel, W, stream).cpu().tolist()
+            ok = int(info.cpu().reshape(-1)[0].item()) == 0
             for t, v in zip(tsel, r2):
-                scores[(key, t)] = v
+                scores[(key, t)] = v if ok and math.isfinite(v) else None
         for ti, t in enumerate(targets):
             best = None
             for s in range(n_blocks):
                 if s in chosen[ti]:
                     continue
                 v = scores[(tuple(sorted(chosen[ti] + [s])), t)]
-                if best is None or v > best[0]:
+                if v is not None and (best is None or v > best[0]):
                     best = (v, s)
+            if best is None:
+                raise RuntimeError(f"greedy match: no candidate set of target {t} can be fitted "
+                                   f"(every regularised Gram failed its factorisation or scored non-finite)")
             chosen[ti].append(best[1])
-    return [sorted(c) for c in chosen]
+    sets = [sorted(c) for c in chosen]
+    return (sets, [list(c) for c in chosen]) if return_order else sets
 
 
 @dataclass

@@ -123,9 +123,9 @@ def ridge_objective(X, Y, W, lam: float) -> float:
 
 
 def fit_pinv(X, Y, lam: float = 0.0, rel_tol: float = 1e-8, mode: str = "absolute"):
-    """The map by the symmetric eigendecomposition route (KV-Lingo page, Appendix B.2
-    "Protocol": the normal equations are solved by symmetric eigendecomposition, eigenvalues
-    below a relative tolerance of 1e-8 treated as zero).  A = X~^T X~ + lam I = V diag(mu) V^T;
+    """The map by the symmetric eigendecomposition route (KV-Lingo page, appendix on the
+    training procedure, "Stage 1": the per-layer normal equations are solved once by symmetric
+    eigendecomposition, eigenvalues below a relative tolerance of 1e-8 counting as zero).  A = X~^T X~ + lam I = V diag(mu) V^T;
     A^+ keeps 1/mu_i for mu_i > rel_tol * max(mu) and zero otherwise; W = A^+ X~^T Y~ and
     b = mean(Y) - mean(X) W.  For a regular A this is the ridge map of ``fit``; for a singular
     one it is the minimum-norm least-squares map."""

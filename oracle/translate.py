@@ -35,7 +35,7 @@ from fractions import Fraction
 import numpy as np
 
 from .fill import rmsnorm, rope_rotate
-from .ridge import fit
+from .ridge import NotSPD, fit
 
 
 def _f64(a) -> np.ndarray:
@@ -167,8 +167,10 @@ def greedy_sources(src_layers, tgt_rows, nu: int, lam: float, mode: str = "absol
     no source, each step adds the source layer whose rows, taken together with those already
     chosen, leave the smallest residual, i.e. give the largest R^2 of the joint ridge fit
     (``fit_r2`` on the chosen layers' rows side by side, in ascending layer order).
-    Reading: equal scores go to the shallower layer.  src_layers: list of [n, d_src] arrays;
-    tgt_rows: [n, d_out].  Returns the nu chosen layers, ascending."""
+    Readings: equal scores go to the shallower layer; a candidate set whose regularised Gram
+    is not positive definite (lambda = 0 with a constant source layer, say) has no ridge map
+    and ranks last.  src_layers: list of [n, d_src] arrays; tgt_rows: [n, d_out].  Returns
+    the nu chosen layers, ascending."""
     n_src = len(src_layers)
     if not 1 <= nu <= n_src:
         raise ValueError("need 1 <= nu <= n_src")
@@ -179,8 +181,13 @@ def greedy_sources(src_layers, tgt_rows, nu: int, lam: float, mode: str = "absol
             if s in chosen:
                 continue
             cand = sorted(chosen + [s])
-            score = fit_r2(np.hstack([_f64(src_layers[c]) for c in cand]), tgt_rows, lam, mode)
+            try:
+                score = fit_r2(np.hstack([_f64(src_layers[c]) for c in cand]), tgt_rows, lam, mode)
+            except NotSPD:
+                continue
             if best is None or score > best[0]:
                 best = (score, s)
+        if best is None:
+            raise NotSPD(0)
         chosen.append(best[1])
     return sorted(chosen)

@@ -152,3 +152,40 @@ def test_fill_streamed_maps_match_resident():
         tol = 1e-4 if cfg.dtype == "f32" else 2e-2
         log(f"[fill] streamed {cfg.name} slots={slots} per_slot={per}: bit-identical to resident, max_err={max(errs):.3e}")
         assert max(errs) <= tol
+
+
+def test_fill_streamed_back_to_back_chunks():
+    # a long prompt filled in token chunks, one streamed call per chunk on one stream with no
+    # host synchronisation between the calls: each call's first map copies into the ring must
+    # wait for the previous call's fills, so the caches still equal the resident fill's bit for bit
+    from linear_kv_cache_amd.runner import Filler, StreamedFiller, alloc_cache, fill_weights, pinned_copy
+    cfg = SMALL_BF16
+    layers = cfg.filled_layers
+    ws = [synth.layer_weights(cfg, l, device="cuda") for l in layers]
+    args = (cfg.d, cfg.n_kv_heads, cfg.head_dim, cfg.rms_eps, cfg.torch_dtype, [w.W_map for w in ws],
+            [w.b_map for w in ws], [w.gamma for w in ws], [w.W_k for w in ws], [w.W_v for w in ws])
+    fw = fill_weights(*args)
+    fs = fill_weights(*args)
+    fs.W_map = [pinned_copy(W.cpu()) for W in fw.W_map]
+    t0, t1, chunk = 5, 1301, 256
+    X = synth.hidden_states(cfg, t1 - t0, "prompt", device="cuda")
+    outs = []
+    for streamed in (False, True):
+        cache = alloc_cache(len(layers), cfg.n_kv_heads, cfg.head_dim, t1, cfg.torch_dtype, "cuda")
+        if streamed:
+            filler = StreamedFiller(fs, cfg.rope_base, t1, chunk, "cuda", ring_slots=2, layers_per_slot=1)
+        else:
+            filler = Filler(fw, cfg.rope_base, t1, t1 - t0, "cuda")
+        torch.cuda.synchronize()
+        if streamed:
+            for c0 in range(t0, t1, chunk):
+                c1 = min(t1, c0 + chunk)
+                filler.fill(X[c0 - t0:c1 - t0], c0, c1, 0, cache)
+        else:
+            filler.fill(X, t0, t1, 0, cache)
+        torch.cuda.synchronize()
+        outs.append(cache)
+    for li in range(len(layers)):
+        for a, b in ((outs[0].k[li], outs[1].k[li]), (outs[0].v[li], outs[1].v[li])):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), li
+    log(f"[fill] streamed back-to-back chunks of {chunk}: bit-identical to the resident fill")

@@ -106,23 +106,18 @@ def _fit_full(cfg, lambdas, n_cols_per_layer=3, seed=0):
         e_sy = max(e_sy, np.max(np.abs(s_y[l][cols[l]] - Ysel[l].sum(0))) / np.max(np.abs(Ysel[l].sum(0))))
     log(f"[full-fit] {cfg.name} gram: e_xx={e_xx:.2e} e_yx={e_yx:.2e} e_sx={e_sx:.2e} e_sy={e_sy:.2e}")
     assert e_xx <= 1e-5 and e_yx <= 1e-5 and e_sx <= 1e-12 and e_sy <= 1e-12
-    # oracle: full centred Gram once, then the sampled columns for every lambda
-    mu_x = X.mean(0)
-    Xc_ = X - mu_x
-    C = Xc_.T @ Xc_
+    # oracle: the exact one-pass sums of the data (the full Gram once, the sampled target
+    # columns of every layer), then the oracle's solve from those sums for every lambda
+    # (column j of W depends only on column j of Y)
+    sums = oracle.gram_sums(X, Ysel)
     ws = device_bytes(rf.rf_solve_workspace_bytes(st.desc, L), dev)
     for lam in lambdas:
         W, _, b, info = st.solve(lam, rf.RF_LAMBDA_ABSOLUTE, list(range(L)), want_bf16=False, ws=ws)
         torch.cuda.synchronize()
         assert int(info.item()) == 0
-        import scipy.linalg
-        Lc = np.linalg.cholesky(C + lam * np.eye(d))
+        refs = oracle.fit_from_sums(*sums, lam)
         errs, berrs = [], []
-        for l in range(L):
-            Yc_ = Ysel[l] - Ysel[l].mean(0)
-            B = Xc_.T @ Yc_
-            Wref = scipy.linalg.solve_triangular(Lc.T, scipy.linalg.solve_triangular(Lc, B, lower=True), lower=False)
-            bref = Ysel[l].mean(0) - mu_x @ Wref
+        for l, (Wref, bref) in enumerate(refs):
             Wg = f64(W[l][torch.as_tensor(cols[l], device=dev)]).T   # [d, n_cols]
             errs.append(np.max(np.abs(Wg - Wref)) / np.max(np.abs(Wref)))
             berrs.append(np.max(np.abs(f64(b[l])[cols[l]] - bref)) / max(np.max(np.abs(bref)), 1e-30))

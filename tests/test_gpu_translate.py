@@ -206,13 +206,43 @@ def test_r2_assignment_from_gpu_scores():
             assert E == oracle.r2_assignment(ref, nu), (side, nu, E)
 
 
+def _check_greedy_steps(order, Sn, y, lam, label, tol=1e-4):
+    """Each forward step of the GPU's greedy match, checked against the oracle given the GPU's
+    own earlier picks: the pick's R^2 (oracle, on the data) is within ``tol`` of the best
+    candidate's, and where no other candidate comes within ``tol`` of the best it is that
+    candidate.  Candidate sets without a ridge map (NotSPD) must never be picked.  Returns
+    True when every step had a clear winner."""
+    prev, clear = [], True
+    for pick in order:
+        sc = {}
+        for s in range(len(Sn)):
+            if s in prev:
+                continue
+            try:
+                sc[s] = oracle.fit_r2(np.hstack([Sn[i] for i in sorted(prev + [s])]), y, lam)
+            except oracle.NotSPD:
+                pass
+        assert pick in sc, (label, prev, pick, "picked a set without a ridge map")
+        best = max(sc.values())
+        near = sorted(s for s, v in sc.items() if v >= best - tol)
+        log(f"[translate] greedy {label} step {len(prev) + 1}: pick {pick} ({sc[pick]:.6f}), best {best:.6f}, "
+            f"within tol {near}")
+        assert sc[pick] >= best - tol, (label, prev, pick)
+        if len(near) == 1:
+            assert pick == near[0], (label, prev, pick)
+        else:
+            clear = False
+        prev.append(pick)
+    return clear
+
+
 def test_greedy_match_from_one_joint_state():
     # greedy match on the GPU: one pass accumulates the joint state of all source layers (X =
     # the 4 source layers side by side) against 3 target layers; forward selection then reads
     # every candidate set off it (rf_gram_select).  Source 1 repeats source 0 with a little
-    # noise, so the R^2 assignment and greedy match part ways as the page says.
+    # noise, so the R^2 assignment and greedy match part ways as the page says.  Every step of
+    # the selection is checked against the oracle's scores.
     from linear_kv_cache_amd.runner import GramState, greedy_sources
-    import linear_kv_cache_amd as rf
     n, d, lam = 3000, 256, 0.1
     g = synth.generator(41, "greedy")
     a, b, c = (torch.randn(n, d, generator=g) for _ in range(3))
@@ -229,22 +259,40 @@ def test_greedy_match_from_one_joint_state():
     st = GramState(4 * d, 3, torch.bfloat16, "cuda", d_out=d)
     st.accumulate(X.cuda(), [y.cuda() for y in tgts])
     Sn = [f64(x) for x in S]
-    for nu in (1, 2, 3):
-        got = greedy_sources(st, d, nu, lam, 0)
-        torch.cuda.synchronize()
-        want = [oracle.greedy_sources(Sn, f64(y), nu, lam) for y in tgts]
-        log(f"[translate] greedy nu={nu}: gpu={got} oracle={want}")
-        for t, (gs, ws) in enumerate(zip(got, want)):
-            if gs == ws:
-                continue
-            # a near tie decided by rounding (at nu = 3 target 2 can add only a redundant copy
-            # or an unrelated source): the GPU's set must explain as much, to the R^2 tolerance
-            r_got = oracle.fit_r2(np.hstack([Sn[i] for i in gs]), f64(tgts[t]), lam)
-            r_want = oracle.fit_r2(np.hstack([Sn[i] for i in ws]), f64(tgts[t]), lam)
-            log(f"[translate] greedy nu={nu} target {t}: tie {gs} ({r_got:.6f}) vs {ws} ({r_want:.6f})")
-            assert nu == 3 and abs(r_got - r_want) <= 1e-4
+    got, order = greedy_sources(st, d, 3, lam, 0, return_order=True)
+    torch.cuda.synchronize()
+    for t, y in enumerate(tgts):
+        clear = _check_greedy_steps(order[t], Sn, f64(y), lam, f"target {t}")
+        if clear:
+            assert got[t] == oracle.greedy_sources(Sn, f64(y), 3, lam), t
+    # the first two picks of target 0 drop the redundant copy, as the oracle's do
+    assert sorted(order[0][:2]) == oracle.greedy_sources(Sn, f64(tgts[0]), 2, lam) == [0, 2]
     # the R^2 assignment on the same data keeps the redundant copy for target 0; greedy match
     # takes the independent source instead
     r2 = np.array([[oracle.fit_r2(f64(x), f64(y), lam) for x in S] for y in tgts])
     assert oracle.r2_assignment(r2, 2)[0] == [0, 1]
     assert oracle.greedy_sources([f64(x) for x in S], f64(tgts[0]), 2, lam) == [0, 2]
+
+
+def test_greedy_match_lambda_zero_skips_singular_sets():
+    # lambda = 0 with a source layer of constant rows: any candidate set holding it has a
+    # singular Gram, the solve reports its failed pivot, and the set must rank last (never
+    # chosen) on the GPU as in the oracle; with every source asked for, no set is fittable
+    from linear_kv_cache_amd.runner import GramState, greedy_sources
+    n, d = 3000, 256
+    g = synth.generator(42, "greedy-l0")
+    a, b = (torch.randn(n, d, generator=g) for _ in range(2))
+    src = [a, torch.full((n, d), 0.75), b]
+    y = a @ (torch.randn(d, d, generator=g) / d ** 0.5) + 0.4 * (b @ (torch.randn(d, d, generator=g) / d ** 0.5))
+    y = (y + 0.1 * torch.randn(n, d, generator=g)).to(torch.bfloat16)
+    S = [x.to(torch.bfloat16) for x in src]
+    st = GramState(3 * d, 1, torch.bfloat16, "cuda", d_out=d)
+    st.accumulate(torch.cat(S, dim=1).cuda(), [y.cuda()])
+    Sn = [f64(x) for x in S]
+    got, order = greedy_sources(st, d, 2, 0.0, 0, return_order=True)
+    torch.cuda.synchronize()
+    log(f"[translate] greedy lambda=0 with a constant source: gpu={got} order={order}")
+    _check_greedy_steps(order[0], Sn, f64(y), 0.0, "lambda=0")
+    assert got[0] == oracle.greedy_sources(Sn, f64(y), 2, 0.0) == [0, 2]
+    with pytest.raises(RuntimeError):
+        greedy_sources(st, d, 3, 0.0, 0)

@@ -294,3 +294,23 @@ def test_greedy_match_accounts_for_redundancy():
     assert oracle.greedy_sources(src, tgt, 1, 1e-3) == oracle.r2_assignment(r2, 1)[0]
     # all sources: everything
     assert oracle.greedy_sources(src, tgt, 4, 1e-3) == [0, 1, 2, 3]
+
+
+def test_greedy_match_skips_sets_without_a_ridge_map():
+    # lambda = 0 and a source layer of constant rows: every candidate set holding it has a
+    # singular Gram (a zero row and column after centring), so no ridge map exists and the set
+    # ranks last; the other sources are still chosen in their order of merit, and asking for
+    # every source leaves no fittable set at the last step
+    rng = np.random.default_rng(16)
+    n, d = 400, 5
+    a, b = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    src = [np.full((n, d), 0.75), a, b]
+    tgt = a @ rng.standard_normal((d, 3)) + 0.3 * b @ rng.standard_normal((d, 3)) + 0.05 * rng.standard_normal((n, 3))
+    with pytest.raises(oracle.NotSPD):
+        oracle.fit_r2(src[0], tgt, 0.0)
+    assert oracle.greedy_sources(src, tgt, 1, 0.0) == [1]
+    assert oracle.greedy_sources(src, tgt, 2, 0.0) == [1, 2]
+    with pytest.raises(oracle.NotSPD):
+        oracle.greedy_sources(src, tgt, 3, 0.0)
+    # with a ridge the constant layer is fittable again (and explains nothing)
+    assert oracle.greedy_sources(src, tgt, 3, 1e-3) == [0, 1, 2]
