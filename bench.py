@@ -268,35 +268,37 @@ def fit_only(cfg, steps: int, warmup: int):
     Xc = [synth.hidden_states(cfg, cfg.calib_chunk, "calib", chunk=c, device=dev) for c in range(n_chunks)]
     Yc = [[synth.late_layer_inputs(cfg, Xc[c], l, chunk=c) for l in layers] for c in range(n_chunks)]
     state = GramState(d, L, cfg.torch_dtype, dev)
-    ws = device_bytes(rf.rf_solve_workspace_bytes(state.desc, L), dev)
-    W_lp = torch.empty(L, d, d, dtype=torch.bfloat16, device=dev)
-    b = torch.empty(L, d, dtype=torch.float32, device=dev)
-    info = torch.empty(1, dtype=torch.int32, device=dev)
+    nl = len(cfg.lambdas)
+    ws = device_bytes(rf.rf_solve_workspace_bytes(state.desc, L, nl), dev)
+    W_lp = torch.empty(nl, L, d, d, dtype=torch.bfloat16, device=dev)
+    b = torch.empty(nl, L, d, dtype=torch.float32, device=dev)
+    info = torch.empty(nl, dtype=torch.int32, device=dev)
+    cond = torch.empty(nl, dtype=torch.float64, device=dev)
 
     def step():
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 + len(cfg.lambdas))]
+        # every lambda of the workload in one rf_solve call on the shared state
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         ev[0].record(stream)
         rf.rf_gram_init(state.desc, state.buf, stream)
         for c in range(n_chunks):
             rf.rf_gram_accumulate(state.desc, state.buf, Xc[c], Yc[c], stream=stream)
         ev[1].record(stream)
-        for i, lam in enumerate(cfg.lambdas):
-            rf.rf_solve(state.desc, state.buf, lam, rf.RF_LAMBDA_ABSOLUTE, list(range(L)), None, W_lp, b, info, ws,
-                        stream)
-            ev[2 + i].record(stream)
+        rf.rf_solve(state.desc, state.buf, list(cfg.lambdas), rf.RF_LAMBDA_ABSOLUTE, list(range(L)), None, W_lp, b,
+                    info, ws, stream, cond=cond)
+        ev[2].record(stream)
         return ev
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    if int(info.item()) != 0:
-        raise SystemExit(f"solve reported a non-positive pivot: {int(info.item())}")
+    if rf.rf_info_status(info.cpu().tolist()) != rf.RF_OK:
+        raise SystemExit(f"solve reported a non-positive pivot: {rf.rf_last_error()}")
     recs = []
     for _ in range(steps):
         recs.append(step())
         torch.cuda.synchronize()
     gram = statistics.median(r[0].elapsed_time(r[1]) for r in recs)
-    solves = [statistics.median(r[1 + i].elapsed_time(r[2 + i]) for r in recs) for i in range(len(cfg.lambdas))]
+    solves = [statistics.median(r[1].elapsed_time(r[2]) for r in recs)]
     tflops = cfg.calib_rows * cfg.fit_flop_per_row() / (gram / 1e3) / 1e12
     print(json.dumps({"metric": "ridge-fit rows/sec, fit only",
                       "config": {"workload": cfg.name, "d": d, "targets": L, "calib_rows": cfg.calib_rows,
@@ -304,7 +306,8 @@ def fit_only(cfg, steps: int, warmup: int):
                       "steps": steps, "warmup": warmup, "gram_ms_median": round(gram, 3),
                       "rows_per_s": round(cfg.calib_rows / (gram / 1e3), 1), "gram_tflops": round(tflops, 1),
                       "gram_frac_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
-                      "solve_ms_median_per_lambda": [round(x, 3) for x in solves],
+                      "solve_ms_median_all_lambdas": round(solves[0], 3),
+                      "equilibrated_inverse_max": [round(float(x), 4) for x in cond.cpu().tolist()],
                       "rows_per_s_incl_solves": round(cfg.calib_rows / ((gram + sum(solves)) / 1e3), 1),
                       "flop_per_row": cfg.fit_flop_per_row()}), flush=True)
 

@@ -44,7 +44,9 @@ typedef enum {
     RF_ERR_INVALID_ARG = 1,   /* a null pointer, bad size, bad range or bad stride        */
     RF_ERR_UNSUPPORTED = 2,   /* a valid request this build does not implement (shape)    */
     RF_ERR_HIP = 3,           /* a HIP runtime call or kernel launch failed               */
-    RF_ERR_WORKSPACE = 4      /* the workspace passed is smaller than the size query says */
+    RF_ERR_WORKSPACE = 4,     /* the workspace passed is smaller than the size query says */
+    RF_ERR_NOT_SPD = 5        /* a regularised Gram is not positive definite (reported by
+                                 rf_info_status from the pivots rf_solve left on the device) */
 } rf_status;
 
 typedef enum { RF_F32 = 0, RF_BF16 = 1 } rf_dtype;
@@ -128,44 +130,77 @@ rf_status rf_gram_select(const rf_gram_desc* desc, const void* d_state, int32_t 
                          void* d_state_out, void* stream);
 
 /* ---------------------------------------------------------------------------------------
- * Ridge fit, part 2: the closed-form solve.
+ * Ridge fit, part 2: the closed-form solve, for one Gram and a batch of ridge strengths.
  *
- * For each selected target l (intercept by mean-centring, rows as token states):
+ * For each lambda_z of the batch and each selected target l (intercept by mean-centring, rows
+ * as token states):
  *     mu_x = s_x / n,  mu_l = s_y,l / n
  *     C    = S_xx - n mu_x^T mu_x           (centred Gram, symmetric from the upper triangle)
  *     B_l  = S_yx,l - n mu_l^T mu_x          (centred cross moments, [m][d])
- *     W_l  = B_l (C + lambda I)^-1           (out-feature major: row o is the map of output o)
+ *     W_l  = B_l (C + lambda_z I)^-1         (out-feature major: row o is the map of output o)
  *     b_l  = mu_l - mu_x W_l^T
- * so that the prediction is y = x W_l^T + b_l.  C + lambda I = L L^T is factored by Cholesky
- * and inverted in fp64 (L^-T by recursive doubling over diagonal blocks, then the lower
- * triangle of L^-T L^-1, mirrored where read).  The product B_l (C + lambda I)^-1 runs on the bf16
- * matrix cores in three-term split precision (each factor, equilibrated by the square root of
- * the diagonal of C + lambda I, is split into two bf16 parts) with fp32 accumulation: about
- * 1e-5 of max |W_l| from the fp64 product on well-scaled data.
+ * so that the prediction is y = x W_l^T + b_l.  Every C + lambda_z I = L L^T is factored by
+ * Cholesky in fp64, the factorisations of the batch advancing together (one launch per
+ * diagonal block for all of them), and inverted in fp64 (L^-T by recursive doubling over
+ * diagonal blocks, then the lower triangle of L^-T L^-1, mirrored where read).
  *
+ * The product B_l (C + lambda_z I)^-1 has two routes:
+ *  - split bf16: on the bf16 matrix cores in three-term split precision (each factor,
+ *    equilibrated by D = diag(C + lambda_0 I), is split into two bf16 parts) with fp32
+ *    accumulation: about 1e-5 of max |W_l| from the fp64 product while the equilibrated
+ *    inverse D^1/2 (C + lambda I)^-1 D^1/2 has entries of order one, and worse in proportion
+ *    to its largest entry (near-collinear features with lambda far below their variance);
+ *  - fp64: the product in fp64 on the matrix cores (about 30x the time of the split route).
+ * RF_PRODUCT_AUTO takes the split route and, for each lambda whose equilibrated inverse has an
+ * entry above RF_SPLIT_COND_MAX, writes the maps again from the fp64 route; the choice is made
+ * on the device (no synchronisation), and d_cond reports the largest entry.
+ *
+ *  lambdas : host array of n_lambda (1..8) ridge strengths, each >= 0 and finite
  *  targets : host array of n_sel target indices in [0, n_targets)
- *  d_W     : [n_sel][m][d] fp32 out, may be NULL; 16-B aligned
- *  d_W_lp  : [n_sel][m][d] bf16 out, may be NULL; 16-B aligned.  Written in the fill's packed
- *            layout (as rf_pack_weights with rope_head_dim 0 would leave it), ready for rf_fill
- *  d_b     : [n_sel][m] fp32 out, may be NULL
- *  d_info  : one int32 out: 0 = success; k > 0 = C + lambda I is not positive definite and
- *            the k-th leading minor (1-based) is the first that fails.  The outputs are then
- *            meaningless (finite or not) but every write stays in bounds.
- *  d_ws    : rf_solve_workspace_bytes(desc, n_sel) bytes, 256-B aligned
- * lambda must be >= 0 and finite. */
-size_t rf_solve_workspace_bytes(const rf_gram_desc* desc, int32_t n_sel);
+ *  product : RF_PRODUCT_AUTO, RF_PRODUCT_SPLIT_BF16 or RF_PRODUCT_F64
+ *  d_W     : [n_lambda][n_sel][m][d] fp32 out, may be NULL; 16-B aligned
+ *  d_W_lp  : [n_lambda][n_sel][m][d] bf16 out, may be NULL; 16-B aligned.  Written in the
+ *            fill's packed layout (as rf_pack_weights with rope_head_dim 0 would leave it),
+ *            ready for rf_fill
+ *  d_b     : [n_lambda][n_sel][m] fp32 out, may be NULL
+ *  d_info  : [n_lambda] int32 out: 0 = success; k > 0 = C + lambda_z I is not positive
+ *            definite and the k-th leading minor (1-based) is the first that fails.  That
+ *            lambda's outputs are then meaningless (finite or not) but every write stays in
+ *            bounds.  rf_info_status() turns a host copy into RF_OK / RF_ERR_NOT_SPD.
+ *  d_cond  : [n_lambda] fp64 out, may be NULL: the largest |entry| of the equilibrated inverse
+ *            (1 for uncorrelated features; +inf when it holds a NaN)
+ *  d_resid : [n_lambda][n_sel] fp64 out, may be NULL: the stationarity residual of the maps
+ *            written, max |(C + lambda I) W_l^T - B_l^T| / max |B_l|, from d_W in fp64 against
+ *            C and B_l rebuilt from the state (needs d_W; costs one fp64 product of the
+ *            product's size per lambda)
+ *  d_ws    : rf_solve_workspace_bytes(desc, n_sel, n_lambda) bytes, 256-B aligned
+ * ------------------------------------------------------------------------------------- */
+typedef enum {
+    RF_PRODUCT_AUTO = 0,        /* split bf16; fp64 for a lambda whose d_cond > RF_SPLIT_COND_MAX */
+    RF_PRODUCT_SPLIT_BF16 = 1,  /* split bf16 always                                             */
+    RF_PRODUCT_F64 = 2          /* fp64 always                                                   */
+} rf_product;
+#define RF_SPLIT_COND_MAX 8.0
+#define RF_MAX_LAMBDAS 8
+
+size_t rf_solve_workspace_bytes(const rf_gram_desc* desc, int32_t n_sel, int32_t n_lambda);
 rf_status rf_solve(const rf_gram_desc* desc, const void* d_state,
-                   double lambda, rf_lambda_mode mode,
-                   const int32_t* targets, int32_t n_sel,
-                   float* d_W, void* d_W_lp, float* d_b, int32_t* d_info,
+                   const double* lambdas, int32_t n_lambda, rf_lambda_mode mode,
+                   const int32_t* targets, int32_t n_sel, rf_product product,
+                   float* d_W, void* d_W_lp, float* d_b,
+                   int32_t* d_info, double* d_cond, double* d_resid,
                    void* d_ws, size_t ws_bytes, void* stream);
+
+/* Host only.  RF_OK when all n pivots reports (a host copy of rf_solve's d_info) are 0, else
+ * RF_ERR_NOT_SPD with the first failing lambda and pivot in rf_last_error(). */
+rf_status rf_info_status(const int32_t* info, int32_t n);
 
 /* The same maps by the symmetric eigendecomposition route (KV-Lingo page, appendix on the
  * training procedure, "Stage 1": the per-layer normal equations solved once by symmetric
  * eigendecomposition, eigenvalues below a relative tolerance counting as zero).  C + lambda I = V diag(mu) V^T by cyclic Jacobi in fp64
  * (``sweeps`` sweeps of round-robin rotations; 15 reach fp64 accuracy on the widths used here);
- * A^+ keeps 1/mu_i for mu_i > rel_tol * max mu; then W_l = B_l A^+ and b_l as in rf_solve (the
- * same split-bf16 product).  For a regular system this is rf_solve's map; for a singular one
+ * A^+ keeps 1/mu_i for mu_i > rel_tol * max mu; then W_l = B_l A^+ and b_l as in rf_solve (its
+ * split-bf16 route).  For a regular system this is rf_solve's map; for a singular one
  * (lambda = 0 on rank-deficient rows: low-rank caches, duplicated or constant features) it is
  * the minimum-norm least-squares map, where rf_solve reports a failed pivot.  Outputs and
  * their layouts as for rf_solve (no d_info: the route has no pivot to fail).

@@ -23,12 +23,16 @@ if not os.path.exists(LIB_PATH):
 _lib = C.CDLL(LIB_PATH)
 
 # ---- enums (ridgefill.h) -------------------------------------------------------------------
-RF_OK, RF_ERR_INVALID_ARG, RF_ERR_UNSUPPORTED, RF_ERR_HIP, RF_ERR_WORKSPACE = range(5)
+RF_OK, RF_ERR_INVALID_ARG, RF_ERR_UNSUPPORTED, RF_ERR_HIP, RF_ERR_WORKSPACE, RF_ERR_NOT_SPD = range(6)
 RF_F32, RF_BF16 = 0, 1
 RF_LAYOUT_CONTIGUOUS, RF_LAYOUT_PAGED = 0, 1
 RF_LAMBDA_ABSOLUTE, RF_LAMBDA_REL_MEAN_DIAG = 0, 1
+RF_PRODUCT_AUTO, RF_PRODUCT_SPLIT_BF16, RF_PRODUCT_F64 = 0, 1, 2
+RF_SPLIT_COND_MAX = 8.0
+RF_MAX_LAMBDAS = 8
 
-_STATUS = {0: "RF_OK", 1: "RF_ERR_INVALID_ARG", 2: "RF_ERR_UNSUPPORTED", 3: "RF_ERR_HIP", 4: "RF_ERR_WORKSPACE"}
+_STATUS = {0: "RF_OK", 1: "RF_ERR_INVALID_ARG", 2: "RF_ERR_UNSUPPORTED", 3: "RF_ERR_HIP", 4: "RF_ERR_WORKSPACE",
+           5: "RF_ERR_NOT_SPD"}
 
 
 class RidgeFillError(RuntimeError):
@@ -83,9 +87,10 @@ _sig = {
                                      C.c_int64, _P]),
     "rf_gram_select": (C.c_int, [C.POINTER(rf_gram_desc), _P, C.c_int32, C.POINTER(C.c_int32), C.c_int32,
                                  C.POINTER(rf_gram_desc), _P, _P]),
-    "rf_solve_workspace_bytes": (C.c_size_t, [C.POINTER(rf_gram_desc), C.c_int32]),
-    "rf_solve": (C.c_int, [C.POINTER(rf_gram_desc), _P, C.c_double, C.c_int, C.POINTER(C.c_int32), C.c_int32,
-                           _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "rf_solve_workspace_bytes": (C.c_size_t, [C.POINTER(rf_gram_desc), C.c_int32, C.c_int32]),
+    "rf_solve": (C.c_int, [C.POINTER(rf_gram_desc), _P, C.POINTER(C.c_double), C.c_int32, C.c_int,
+                           C.POINTER(C.c_int32), C.c_int32, C.c_int, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "rf_info_status": (C.c_int, [C.POINTER(C.c_int32), C.c_int32]),
     "rf_solve_pinv_workspace_bytes": (C.c_size_t, [C.POINTER(rf_gram_desc), C.c_int32]),
     "rf_solve_pinv": (C.c_int, [C.POINTER(rf_gram_desc), _P, C.c_double, C.c_int, C.c_double, C.c_int32,
                                 C.POINTER(C.c_int32), C.c_int32, _P, _P, _P, _P, C.c_size_t, _P]),
@@ -201,16 +206,26 @@ def rf_gram_select(desc: rf_gram_desc, state, block_width: int, blocks: Sequence
                                _ptr(state_out), _stream(stream)))
 
 
-def rf_solve_workspace_bytes(desc: rf_gram_desc, n_sel: int) -> int:
-    return int(_lib.rf_solve_workspace_bytes(C.byref(desc), n_sel))
+def rf_solve_workspace_bytes(desc: rf_gram_desc, n_sel: int, n_lambda: int = 1) -> int:
+    return int(_lib.rf_solve_workspace_bytes(C.byref(desc), n_sel, n_lambda))
 
 
-def rf_solve(desc: rf_gram_desc, state, lam: float, mode: int, targets: Sequence[int], W, W_lp, b, info, ws,
-             stream=None):
+def rf_solve(desc: rf_gram_desc, state, lambdas, mode: int, targets: Sequence[int], W, W_lp, b, info, ws,
+             stream=None, product: int = RF_PRODUCT_AUTO, cond=None, resid=None):
+    """lambdas: one ridge strength or a sequence of up to 8 (the outputs gain a leading axis)."""
+    lams = [float(lambdas)] if isinstance(lambdas, (int, float)) else [float(x) for x in lambdas]
+    la = (C.c_double * max(1, len(lams)))(*lams)
     tg = (C.c_int32 * max(1, len(targets)))(*targets)
     ws_bytes = ws.numel() * ws.element_size()
-    _check(_lib.rf_solve(C.byref(desc), _ptr(state), float(lam), int(mode), tg, len(targets), _ptr(W), _ptr(W_lp),
-                         _ptr(b), _ptr(info), _ptr(ws), ws_bytes, _stream(stream)))
+    _check(_lib.rf_solve(C.byref(desc), _ptr(state), la, len(lams), int(mode), tg, len(targets), int(product), _ptr(W),
+                         _ptr(W_lp), _ptr(b), _ptr(info), _ptr(cond), _ptr(resid), _ptr(ws), ws_bytes,
+                         _stream(stream)))
+
+
+def rf_info_status(info: Sequence[int]) -> int:
+    """RF_OK, or RF_ERR_NOT_SPD (message in rf_last_error()) for a host copy of rf_solve's pivots."""
+    arr = (C.c_int32 * max(1, len(info)))(*[int(x) for x in info])
+    return int(_lib.rf_info_status(arr, len(info)))
 
 
 def rf_solve_pinv_workspace_bytes(desc: rf_gram_desc, n_sel: int) -> int:

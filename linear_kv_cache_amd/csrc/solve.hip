@@ -41,13 +41,16 @@ typedef double f64x2 __attribute__((ext_vector_type(2)));
 // (B[k][n] = 0 for k > n: the k-loop ends at n0 + BN).
 // The flags are bits and combine.
 // Batched launches (gridDim.z > 1) offset A, B and C by blockIdx.z times sA, sB, sC elements.
+// ``gate`` (device, may be null): the launch does nothing when *gate is 0.
 enum { kFull = 0, kLowerOnly = 1, kUpperOperands = 2, kUpperA = 4, kUpperB = 8 };
 
 template <bool BT, int BM = 128>
 __global__ __launch_bounds__(256, 2) void k_dgemm(int64_t M, int64_t N, int64_t K, double alpha, const double* A,
                                                int64_t lda, const double* B, int64_t ldb, double beta, double* C,
-                                               int64_t ldc, int structure, int64_t sA, int64_t sB, int64_t sC) {
+                                               int64_t ldc, int structure, int64_t sA, int64_t sB, int64_t sC,
+                                               const int32_t* gate) {
     static_assert(BM == 64 || BM == 128, "64 x 64 or 128 x 128 tiles");
+    if (gate && *gate == 0) return;   // a conditional product that is not wanted
     constexpr int BN = BM, BK = 16, PAD = 2;
     constexpr int WT = BM / 2, WB = WT / 16;   // wave tile and its 16 x 16 blocks per side
     // Loads are 16-byte chunks, and each wave instruction covers whole operand rows (coalesced).
@@ -189,10 +192,14 @@ __global__ void k_zdiag(const double* Dinv, int64_t d, double* Z) {
     }
 }
 
-__global__ void k_zero_int(int32_t* p) { *p = 0; }
+__global__ void k_zero_int(int32_t* p, int n) {
+    if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
+}
 
-// C[i][j] = S_xx[min(i,j)][max(i,j)] - s_x[i] s_x[j] / n
+// C[i][j] = S_xx[min(i,j)][max(i,j)] - s_x[i] s_x[j] / n, into every matrix of the batch
+// (blockIdx.y: one per lambda, d*d elements apart)
 __global__ void k_centre_gram(const float* Sxx, const double* sx, const int64_t* np, int64_t d, double* C) {
+    C += (int64_t)blockIdx.y * d * d;
     const double inv_n = 1.0 / (double)*np;
     const int64_t n = d * d;
     for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
@@ -202,9 +209,17 @@ __global__ void k_centre_gram(const float* Sxx, const double* sx, const int64_t*
     }
 }
 
-// Adds lambda (absolute, or times the mean diagonal) to the diagonal; one workgroup.
-__global__ __launch_bounds__(256) void k_add_lambda(double* C, int64_t d, double lambda, int rel) {
+constexpr int kMaxLambda = 8;
+struct Lambdas {
+    double v[kMaxLambda];
+};
+
+// Adds lambda (absolute, or times the mean diagonal) to the diagonal: one work-group per
+// matrix of the batch (blockIdx.x; d*d elements apart), lambda lam.v[blockIdx.x].
+__global__ __launch_bounds__(256) void k_add_lambda(double* C, int64_t d, Lambdas lams, int rel) {
     __shared__ double red[256];
+    C += (int64_t)blockIdx.x * d * d;
+    const double lambda = lams.v[blockIdx.x];
     double lam = lambda;
     if (rel) {
         double s = 0.0;
@@ -306,18 +321,23 @@ __device__ inline void sqrt_rsqrt(double p, double& r, double& ri) {
 // for the lower triangle and are written as zeros.  L^-1 by right-looking substitution, lane c
 // holding column c: once X[k][c] is final it is stored, and row k of X updates the running sums
 // of rows r > k with L[r][k] = Lt[k][r].
-// Work-group 0 factors the block with its first wave; work-groups 1.. centre and split rows
-// [c_begin, c_end) of the cross moments, ny work-groups of 2048 columns per row.
-__global__ __launch_bounds__(256) void k_chol_diag(double* C, int64_t d, int J, double* Dinv, int32_t* info,
-                                                   CrossArgs ca, int64_t c_begin, int64_t c_end, int ny) {
-    if (blockIdx.x > 0) {
-        const int64_t b = blockIdx.x - 1;
+// Work-group z < n_lam factors the block of matrix z (C + z sC, Dinv + z sD, info + z) with
+// its first wave; the work-groups after those centre and split rows [c_begin, c_end) of the
+// cross moments, ny work-groups of 2048 columns per row.
+__global__ __launch_bounds__(256) void k_chol_diag(double* C, int64_t sC, int64_t d, int J, double* Dinv, int64_t sD,
+                                                   int32_t* info, int n_lam, CrossArgs ca, int64_t c_begin,
+                                                   int64_t c_end, int ny) {
+    if ((int)blockIdx.x >= n_lam) {
+        const int64_t b = blockIdx.x - n_lam;
         const int64_t c = c_begin + b / ny;
         const int64_t i0 = ((b % ny) * 256 + threadIdx.x) * 8;
         if (c < c_end && i0 < ca.d) centre_split_row(ca, c, i0);
         return;
     }
     if (threadIdx.x >= 64) return;   // the factorisation is one wave's (no barriers below)
+    C += (int64_t)blockIdx.x * sC;
+    Dinv += (int64_t)blockIdx.x * sD;
+    info += blockIdx.x;
     __shared__ __attribute__((aligned(16))) double Lt[kNB][kNB + 2];
     const int i = threadIdx.x;
     const int64_t off = (int64_t)J * kNB;
@@ -403,9 +423,14 @@ __global__ void k_diag_sqrt(const double* A, int64_t d, double* dg, double* rdg)
 // One 64 x 64 tile of A^-1 per work-group.  Only the lower triangle of A^-1 (by 64-blocks) is
 // formed; a tile above the diagonal reads its mirror image (coalesced) and transposes it
 // through LDS.  Each thread then splits 8 consecutive columns of one row and stores them as
-// three 16-byte fragment chunks.
-__global__ __launch_bounds__(256) void k_split_inverse(const double* Ainv, const double* dg, int64_t d, bf16_t* Bq) {
+// three 16-byte fragment chunks.  hmax (may be null) receives the tile's largest |entry| of the
+// equilibrated inverse, at [blockIdx.y][blockIdx.x].
+__global__ __launch_bounds__(256) void k_split_inverse(const double* Ainv, const double* dg, int64_t d, bf16_t* Bq,
+                                                       double* hmax) {
     __shared__ double tile[64][65];
+    __shared__ double red[256];
+    double hm = 0.0;
+    bool bad = false;   // a NaN entry (fmax would drop it)
     const int64_t ib = blockIdx.x, jb = blockIdx.y;   // element (j, i): Bq row j, column i
     const bool mirror = ib > jb;
     const int64_t r0 = (mirror ? ib : jb) * 64, c0 = (mirror ? jb : ib) * 64;
@@ -420,8 +445,12 @@ __global__ __launch_bounds__(256) void k_split_inverse(const double* Ainv, const
         for (int q = 0; q < 4; ++q) {
             const int il = i8 + 2 * q;
             bf16_t h0, l0, h1, l1;
-            split_bf16((mirror ? tile[il][jl] : tile[jl][il]) * dg[i0 + 2 * q] * dg[j], h0, l0);
-            split_bf16((mirror ? tile[il + 1][jl] : tile[jl][il + 1]) * dg[i0 + 2 * q + 1] * dg[j], h1, l1);
+            const double v0 = (mirror ? tile[il][jl] : tile[jl][il]) * dg[i0 + 2 * q] * dg[j];
+            const double v1 = (mirror ? tile[il + 1][jl] : tile[jl][il + 1]) * dg[i0 + 2 * q + 1] * dg[j];
+            hm = fmax(hm, fmax(fabs(v0), fabs(v1)));
+            bad |= (v0 != v0) || (v1 != v1);
+            split_bf16(v0, h0, l0);
+            split_bf16(v1, h1, l1);
             hi[q] = (uint32_t)h0 | ((uint32_t)h1 << 16);
             lo[q] = (uint32_t)l0 | ((uint32_t)l1 << 16);
         }
@@ -429,6 +458,15 @@ __global__ __launch_bounds__(256) void k_split_inverse(const double* Ainv, const
         *(u32x4*)(Bq + packed_index(j, (int)i0, K)) = H;
         *(u32x4*)(Bq + packed_index(j, (int)(d + i0), K)) = Lo;
         *(u32x4*)(Bq + packed_index(j, (int)(2 * d + i0), K)) = H;
+    }
+    if (hmax) {
+        red[threadIdx.x] = bad ? INFINITY : hm;
+        __syncthreads();
+        for (int h = 128; h > 0; h >>= 1) {
+            if ((int)threadIdx.x < h) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + h]);
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) hmax[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = red[0];
     }
 }
 
@@ -515,15 +553,171 @@ __global__ void k_bias(const float* bpart, int tiles_j, const double* mu_y, int6
     b[c] = (float)(mu_y[c] - s);
 }
 
+
+// ---- the fp64 route of the W product and the stationarity residual ------------------------
+// Each of these does nothing when its gate (device, may be null) holds 0, so a route chosen on
+// the device from the conditioning of the system is launched without a host round trip.
+
+// One work-group per d x d tile row pair: the full symmetric A^-1 from its lower triangle
+// (element (i, j) with i >= j holds A^-1, as the Z Z^T product leaves it).
+__global__ void k_mirror_full(const double* Ainv_lower, int64_t d, double* Afull, const int32_t* gate) {
+    if (gate && *gate == 0) return;
+    const int64_t n = d * d;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i = idx / d, j = idx % d;
+        Afull[idx] = i >= j ? Ainv_lower[idx] : Ainv_lower[j * d + i];
+    }
+}
+
+// Centred cross moments in fp64 for rows [r0, r0 + nr) of the selected targets' outputs, one
+// work-group per row: Bf[r - r0][i] = S_yx[row][i] - s_y[row] s_x[i] / n; bmax (may be null)
+// receives max_i |Bf| of each row at its global row index.
+__global__ __launch_bounds__(256) void k_centre_f64(CrossArgs a, int64_t r0, double* Bf, double* bmax,
+                                                    const int32_t* gate) {
+    if (gate && *gate == 0) return;
+    __shared__ double red[256];
+    const int64_t r = r0 + blockIdx.x;
+    const double inv_n = 1.0 / (double)*a.np;
+    const int64_t srow = (int64_t)a.tsel[r / a.dy] * a.dy + r % a.dy;
+    const double syv = a.sy[srow];
+    double m = 0.0;
+    for (int64_t i = threadIdx.x; i < a.d; i += 256) {
+        const double v = (double)a.Syx[srow * a.d + i] - syv * a.sx[i] * inv_n;
+        Bf[(int64_t)blockIdx.x * a.d + i] = v;
+        m = fmax(m, fabs(v));
+    }
+    if (!bmax) return;
+    red[threadIdx.x] = m;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if ((int)threadIdx.x < h) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + h]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) bmax[r] = red[0];
+}
+
+// The maps from the fp64 product, rows [r0, r0 + nr) (one work-group per row): W (fp32,
+// may be null), the packed bf16 copy (may be null), and the intercept
+// b = s_y / n - sum_j W[j] s_x[j] / n summed in fp64 in a fixed order (may be null).
+__global__ __launch_bounds__(256) void k_store_f64(const double* Wf, int64_t r0, CrossArgs a, float* W, bf16_t* Wlp,
+                                                   float* b, const int32_t* gate) {
+    if (gate && *gate == 0) return;
+    __shared__ double red[256];
+    const int64_t r = r0 + blockIdx.x, d = a.d;
+    const double inv_n = 1.0 / (double)*a.np;
+    const double* wr = Wf + (int64_t)blockIdx.x * d;
+    const int64_t wl_base = (r >> 8) * 256 * d + packed_row_part((int)(r & 255));
+    double dot = 0.0;
+    for (int64_t j = 4 * threadIdx.x; j < d; j += 1024) {
+        const double w0 = wr[j], w1 = wr[j + 1], w2 = wr[j + 2], w3 = wr[j + 3];
+        dot += w0 * a.sx[j] + w1 * a.sx[j + 1] + w2 * a.sx[j + 2] + w3 * a.sx[j + 3];
+        if (W) *(f32x4*)(W + r * d + j) = f32x4{(float)w0, (float)w1, (float)w2, (float)w3};
+        if (Wlp)
+            *(u32x2*)(Wlp + wl_base + packed_col_part((int)j)) =
+                u32x2{pack_bf16x2((float)w0, (float)w1), pack_bf16x2((float)w2, (float)w3)};
+    }
+    if (!b) return;
+    red[threadIdx.x] = dot;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        const int64_t srow = (int64_t)a.tsel[r / a.dy] * a.dy + r % a.dy;
+        b[r] = (float)((a.sy[srow] - red[0]) * inv_n);
+    }
+}
+
+// Wf[r - r0][j] = W[r][j] for rows [r0, r0 + nr) (fp32 maps widened for the residual product).
+__global__ void k_widen_rows(const float* W, int64_t r0, int64_t nr, int64_t d, double* Wf) {
+    const int64_t n = nr * d;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x)
+        Wf[idx] = (double)W[r0 * d + idx];
+}
+
+// rmax[r0 + row] = max_j |R[row][j]| (one work-group per row); NaN gives +inf.
+__global__ __launch_bounds__(256) void k_row_absmax(const double* R, int64_t r0, int64_t d, double* rmax) {
+    __shared__ double red[256];
+    double m = 0.0;
+    bool bad = false;
+    for (int64_t j = threadIdx.x; j < d; j += 256) {
+        const double v = R[(int64_t)blockIdx.x * d + j];
+        m = fmax(m, fabs(v));
+        bad |= v != v;
+    }
+    red[threadIdx.x] = bad ? INFINITY : m;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if ((int)threadIdx.x < h) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + h]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) rmax[r0 + blockIdx.x] = red[0];
+}
+
+// Per selected target i (one work-group each): max over its dy rows of the residual row maxima
+// over the same for the centred cross moments.
+__global__ __launch_bounds__(256) void k_resid_final(const double* rmax, const double* bmax, int64_t dy, double* out) {
+    __shared__ double red[2][256];
+    double mr = 0.0, mb = 0.0;
+    for (int64_t o = threadIdx.x; o < dy; o += 256) {
+        mr = fmax(mr, rmax[(int64_t)blockIdx.x * dy + o]);
+        mb = fmax(mb, bmax[(int64_t)blockIdx.x * dy + o]);
+    }
+    red[0][threadIdx.x] = mr;
+    red[1][threadIdx.x] = mb;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if ((int)threadIdx.x < h) {
+            red[0][threadIdx.x] = fmax(red[0][threadIdx.x], red[0][threadIdx.x + h]);
+            red[1][threadIdx.x] = fmax(red[1][threadIdx.x], red[1][threadIdx.x + h]);
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[blockIdx.x] = red[0][0] / red[1][0];
+}
+
+// The route of one lambda: cond = the largest |entry| of the equilibrated inverse (from the
+// tile maxima of k_split_inverse), gate = 1 when the fp64 product is to write the maps.
+__global__ __launch_bounds__(256) void k_route(const double* hmax, int64_t n, int product, double cond_max,
+                                               int32_t* gate, double* cond) {
+    __shared__ double red[256];
+    double m = 0.0;
+    for (int64_t i = threadIdx.x; i < n; i += 256) m = fmax(m, hmax[i]);
+    red[threadIdx.x] = m;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if ((int)threadIdx.x < h) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + h]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        const double c = red[0];
+        if (cond) *cond = c;
+        *gate = product == RF_PRODUCT_F64 || (product == RF_PRODUCT_AUTO && !(c <= cond_max));
+    }
+}
+
 // -------------------------------------------------------------------------------------------
 struct SolveWs {
-    double *C, *Cinv, *Dinv, *mu_y, *dg, *rdg;
+    double *C, *Cinv, *Dinv, *mu_y, *dg, *rdg;   // C, Cinv, Dinv: one per lambda
     bf16_t *Aq, *Bq;
     float* bpart;
+    double* hmax;      // per lambda: the tile maxima of the equilibrated inverse
+    int32_t* gate;     // per lambda: 1 = the fp64 product writes the maps
+    double *Bf, *Wf;   // fp64 row blocks of rb rows
+    double *rmax, *bmax;
+    int64_t rb;
     size_t total;
 };
 
-static SolveWs solve_ws(void* base, int64_t d, int64_t dy, int64_t n_sel) {
+// Rows per fp64 block: 8 Mi elements of fp64 (64 MiB) per buffer, at least 64.
+static int64_t f64_block_rows(int64_t d, int64_t rows) {
+    int64_t rb = ((int64_t)(8 << 20) / d) / 64 * 64;
+    if (rb < 64) rb = 64;
+    return rows < rb ? rows : rb;
+}
+
+static SolveWs solve_ws(void* base, int64_t d, int64_t dy, int64_t n_sel, int64_t n_lam = 1) {
     SolveWs w{};
     size_t off = 0;
     char* p = (char*)base;
@@ -533,15 +727,22 @@ static SolveWs solve_ws(void* base, int64_t d, int64_t dy, int64_t n_sel) {
         return r;
     };
     const int64_t rows = n_sel * dy;
-    w.C = (double*)take(d * d * 8);
-    w.Cinv = (double*)take(d * d * 8);
-    w.Dinv = (double*)take(d * kNB * 8);
+    w.C = (double*)take(n_lam * d * d * 8);
+    w.Cinv = (double*)take(n_lam * d * d * 8);
+    w.Dinv = (double*)take(n_lam * d * kNB * 8);
     w.mu_y = (double*)take(rows * 8);
     w.dg = (double*)take(d * 8);
     w.rdg = (double*)take(d * 8);
     w.Aq = (bf16_t*)take(rows * 2 * d * 2);
     w.Bq = (bf16_t*)take(d * 3 * d * 2);
     w.bpart = (float*)take(rows * (d / 256) * 4);
+    w.hmax = (double*)take(n_lam * (d / 64) * (d / 64) * 8);
+    w.gate = (int32_t*)take(n_lam * 4);
+    w.rb = f64_block_rows(d, rows > 0 ? rows : 1);
+    w.Bf = (double*)take(w.rb * d * 8);
+    w.Wf = (double*)take(w.rb * d * 8);
+    w.rmax = (double*)take((rows > 0 ? rows : 1) * 8);
+    w.bmax = (double*)take((rows > 0 ? rows : 1) * 8);
     w.total = off;
     return w;
 }
@@ -556,18 +757,22 @@ static inline unsigned grid_for(int64_t n, int64_t per = 256) {
 // throughout the inverse 12.1 ms; 2048 and 64 x 64 throughout matched 1024)
 constexpr int64_t kBigTiles = 1024;
 
+// A batch of ``batch`` equal products sA, sB, sC elements apart (batch = 1: one product); the
+// tile size is chosen from the tiles of the whole batch.  ``gate``: as for k_dgemm.
 template <bool BT>
 static rf_status dgemm(hipStream_t s, int64_t M, int64_t N, int64_t K, double alpha, const double* A, int64_t lda,
-                       const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int structure = kFull) {
-    if (M <= 0 || N <= 0) return RF_OK;
+                       const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int structure = kFull,
+                       int batch = 1, int64_t sA = 0, int64_t sB = 0, int64_t sC = 0, const int32_t* gate = nullptr) {
+    if (M <= 0 || N <= 0 || batch <= 0) return RF_OK;
     int64_t tiles = ceil_div(M, 128) * ceil_div(N, 128);
     if (structure & kLowerOnly) tiles = (tiles + ceil_div(M, 128)) / 2;
+    tiles *= batch;
     if (tiles >= kBigTiles)
-        hipLaunchKernelGGL((k_dgemm<BT, 128>), dim3((unsigned)ceil_div(M, 128), (unsigned)ceil_div(N, 128)), dim3(256), 0,
-                           s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, structure, (int64_t)0, (int64_t)0, (int64_t)0);
+        hipLaunchKernelGGL((k_dgemm<BT, 128>), dim3((unsigned)ceil_div(M, 128), (unsigned)ceil_div(N, 128), (unsigned)batch),
+                           dim3(256), 0, s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, structure, sA, sB, sC, gate);
     else
-        hipLaunchKernelGGL((k_dgemm<BT, 64>), dim3((unsigned)ceil_div(M, 64), (unsigned)ceil_div(N, 64)), dim3(256), 0, s,
-                           M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, structure, (int64_t)0, (int64_t)0, (int64_t)0);
+        hipLaunchKernelGGL((k_dgemm<BT, 64>), dim3((unsigned)ceil_div(M, 64), (unsigned)ceil_div(N, 64), (unsigned)batch),
+                           dim3(256), 0, s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, structure, sA, sB, sC, gate);
     return check_launch("rf_solve: dgemm");
 }
 
@@ -587,8 +792,10 @@ static rf_status dgemm(hipStream_t s, int64_t M, int64_t N, int64_t K, double al
 // (by induction over the levels), and the number of dependent levels is log2(d / 64) rounded
 // up, instead of one step per 64 columns.  The diagonal 64-blocks come from the factorisation
 // (Dinv); T lives in the split-operand buffer, which is written only after the inverse.
-static rf_status inverse_factor(hipStream_t s, const SolveWs& w, int64_t d, double* Z) {
-    hipLaunchKernelGGL(k_zdiag, dim3(grid_for(d * d)), dim3(256), 0, s, w.Dinv, d, Z);
+// Lf holds the factor L (lower triangle), Dinv the inverses of its diagonal blocks.
+static rf_status inverse_factor(hipStream_t s, const SolveWs& w, const double* Lf, const double* Dinv, int64_t d,
+                                double* Z) {
+    hipLaunchKernelGGL(k_zdiag, dim3(grid_for(d * d)), dim3(256), 0, s, Dinv, d, Z);
     RF_TRY(check_launch("rf_solve: inverse diagonal"));
     double* T = (double*)w.Bq;
     auto join = [&](int64_t o, int64_t b, int64_t n2, unsigned batch, int64_t sp) -> rf_status {
@@ -598,19 +805,21 @@ static rf_status inverse_factor(hipStream_t s, const SolveWs& w, int64_t d, doub
         const dim3 g1((unsigned)ceil_div(b, tb), (unsigned)ceil_div(n2, tb), batch);
         if (big)
             hipLaunchKernelGGL((k_dgemm<true, 128>), g1, dim3(256), 0, s, b, n2, b, 1.0, (const double*)(Z + o * d + o),
-                               d, (const double*)(w.C + (o + b) * d + o), d, 0.0, T, n2, (int)kUpperA, sp, sp, b * n2);
+                               d, Lf + (o + b) * d + o, d, 0.0, T, n2, (int)kUpperA, sp, sp, b * n2,
+                               (const int32_t*)nullptr);
         else
             hipLaunchKernelGGL((k_dgemm<true, 64>), g1, dim3(256), 0, s, b, n2, b, 1.0, (const double*)(Z + o * d + o),
-                               d, (const double*)(w.C + (o + b) * d + o), d, 0.0, T, n2, (int)kUpperA, sp, sp, b * n2);
+                               d, Lf + (o + b) * d + o, d, 0.0, T, n2, (int)kUpperA, sp, sp, b * n2,
+                               (const int32_t*)nullptr);
         RF_TRY(check_launch("rf_solve: inverse T"));
         if (big)
             hipLaunchKernelGGL((k_dgemm<false, 128>), g1, dim3(256), 0, s, b, n2, n2, -1.0, (const double*)T, n2,
                                (const double*)(Z + (o + b) * d + o + b), d, 0.0, Z + o * d + o + b, d, (int)kUpperB,
-                               b * n2, sp, sp);
+                               b * n2, sp, sp, (const int32_t*)nullptr);
         else
             hipLaunchKernelGGL((k_dgemm<false, 64>), g1, dim3(256), 0, s, b, n2, n2, -1.0, (const double*)T, n2,
                                (const double*)(Z + (o + b) * d + o + b), d, 0.0, Z + o * d + o + b, d, (int)kUpperB,
-                               b * n2, sp, sp);
+                               b * n2, sp, sp, (const int32_t*)nullptr);
         return check_launch("rf_solve: inverse Z12");
     };
     for (int64_t b = kNB; b < d; b *= 2) {
@@ -618,6 +827,61 @@ static rf_status inverse_factor(hipStream_t s, const SolveWs& w, int64_t d, doub
         if (full > 0) RF_TRY(join(0, b, b, (unsigned)full, 2 * b * (d + 1)));
         const int64_t o = full * 2 * b;                   // a last pair with a short second unit
         if (o + b < d) RF_TRY(join(o, b, d - o - b, 1u, 0));
+    }
+    return RF_OK;
+}
+
+// The product stage for matrix z of the batch, whose inverse (or pseudo-inverse) stands in
+// the lower triangle of w.C + z d^2 and whose split cross moments stand in w.Aq: the
+// equilibrated split inverse and its largest entry (cond, may be null), the route, the split
+// bf16 product (unless the route is fp64 only) and the fp64 product (unless it is split
+// only; gated on the device under RF_PRODUCT_AUTO).  Writes W (fp32), W_lp (packed bf16) and
+// b, each of which may be null.
+static rf_status solve_products(hipStream_t s, const SolveWs& w, int z, int64_t d, int64_t rows, const CrossArgs& ca,
+                                rf_product product, float* Wz, bf16_t* Wlpz, float* bz, double* cond) {
+    const int64_t dd = d * d;
+    const int64_t nb64 = (d / 64) * (d / 64);
+    double* Cz = w.C + z * dd;
+    int32_t* gz = w.gate + z;
+    const double* sx = ca.sx;
+    const int64_t* np = ca.np;
+    // equilibrated split inverse (and its largest entry), then W on the MFMA pipes
+    hipLaunchKernelGGL(k_split_inverse, dim3((unsigned)(d / 64), (unsigned)(d / 64)), dim3(256), 0, s, Cz, w.dg, d,
+                       w.Bq, w.hmax + z * nb64);
+    RF_TRY(check_launch("rf_solve: split inverse"));
+    hipLaunchKernelGGL(k_route, dim3(1), dim3(256), 0, s, (const double*)(w.hmax + z * nb64), nb64, (int)product,
+                       (double)RF_SPLIT_COND_MAX, gz, cond);
+    RF_TRY(check_launch("rf_solve: route"));
+    if (product != RF_PRODUCT_F64) {
+        WArgs wa{};
+        wa.Aq = w.Aq; wa.Bq = w.Bq; wa.rdg = w.rdg; wa.sx = sx; wa.np = np; wa.d = d; wa.rows = rows;
+        wa.tiles_j = (int)(d / 256); wa.tiles_c = (int)(rows / 256); wa.W = Wz; wa.Wlp = Wlpz;
+        wa.bpart = w.bpart;
+        hipLaunchKernelGGL(k_wgemm, dim3((unsigned)(wa.tiles_j * wa.tiles_c)), dim3(PackedAGemm::kThr), 0, s, wa);
+        RF_TRY(check_launch("rf_solve: W product"));
+        if (bz) {
+            hipLaunchKernelGGL(k_bias, dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0, s, w.bpart, wa.tiles_j,
+                               w.mu_y, rows, bz);
+            RF_TRY(check_launch("rf_solve: bias"));
+        }
+    }
+    if (product != RF_PRODUCT_SPLIT_BF16) {
+        // the fp64 product, written over the split one when the route says so:
+        // W = B A^-1 with the full A^-1 (mirrored into the free Z buffer), rb rows at a time
+        double* Af = w.Cinv + z * dd;
+        hipLaunchKernelGGL(k_mirror_full, dim3(grid_for(dd)), dim3(256), 0, s, (const double*)Cz, d, Af,
+                           (const int32_t*)gz);
+        RF_TRY(check_launch("rf_solve: fp64 inverse"));
+        for (int64_t r0 = 0; r0 < rows; r0 += w.rb) {
+            const int64_t nr = std::min<int64_t>(w.rb, rows - r0);
+            hipLaunchKernelGGL(k_centre_f64, dim3((unsigned)nr), dim3(256), 0, s, ca, r0, w.Bf, (double*)nullptr,
+                               (const int32_t*)gz);
+            RF_TRY(check_launch("rf_solve: fp64 cross moments"));
+            RF_TRY(dgemm<false>(s, nr, d, d, 1.0, w.Bf, d, Af, d, 0.0, w.Wf, d, kFull, 1, 0, 0, 0, gz));
+            hipLaunchKernelGGL(k_store_f64, dim3((unsigned)nr), dim3(256), 0, s, (const double*)w.Wf, r0, ca, Wz,
+                               Wlpz, bz, (const int32_t*)gz);
+            RF_TRY(check_launch("rf_solve: fp64 maps"));
+        }
     }
     return RF_OK;
 }
@@ -861,7 +1125,7 @@ static size_t pinv_extra_bytes(int64_t d) { return round_up((size_t)(d * d * 8),
 size_t rf_solve_pinv_workspace_bytes(const rf_gram_desc* desc, int32_t n_sel) {
     rf_gram_layout_t GL;
     if (n_sel < 0 || rf_gram_state_layout(desc, &GL) != RF_OK) return 0;
-    return solve_ws(nullptr, desc->d, gram_dy(desc), n_sel).total + pinv_extra_bytes(desc->d);
+    return solve_ws(nullptr, desc->d, gram_dy(desc), n_sel, 1).total + pinv_extra_bytes(desc->d);
 }
 
 rf_status rf_solve_pinv(const rf_gram_desc* desc, const void* d_state, double lambda, rf_lambda_mode mode,
@@ -887,7 +1151,7 @@ rf_status rf_solve_pinv(const rf_gram_desc* desc, const void* d_state, double la
     RF_REQUIRE(aligned(d_W, 16) && aligned(d_W_lp, 16) && aligned(d_b, 4), RF_ERR_INVALID_ARG,
                "rf_solve_pinv: W outputs must be 16-byte aligned");
     const int64_t d = desc->d, dy = gram_dy(desc);
-    const SolveWs w = solve_ws(d_ws, d, dy, n_sel);
+    const SolveWs w = solve_ws(d_ws, d, dy, n_sel, 1);
     RF_REQUIRE(d_ws && ws_bytes >= w.total + pinv_extra_bytes(d), RF_ERR_WORKSPACE, "rf_solve_pinv: workspace too small");
     double* V = (double*)((char*)d_ws + w.total);
     double* cs = (double*)((char*)V + round_up((size_t)(d * d * 8), 256));
@@ -900,7 +1164,9 @@ rf_status rf_solve_pinv(const rf_gram_desc* desc, const void* d_state, double la
 
     hipLaunchKernelGGL(k_centre_gram, dim3(grid_for(d * d)), dim3(256), 0, s, Sxx, sx, np, d, w.C);
     RF_TRY(check_launch("rf_solve_pinv: centre"));
-    hipLaunchKernelGGL(k_add_lambda, dim3(1), dim3(256), 0, s, w.C, d, lambda, (int)(mode == RF_LAMBDA_REL_MEAN_DIAG));
+    Lambdas lams{};
+    lams.v[0] = lambda;
+    hipLaunchKernelGGL(k_add_lambda, dim3(1), dim3(256), 0, s, w.C, d, lams, (int)(mode == RF_LAMBDA_REL_MEAN_DIAG));
     RF_TRY(check_launch("rf_solve_pinv: lambda"));
     hipLaunchKernelGGL(k_diag_sqrt, dim3(grid_for(d)), dim3(256), 0, s, w.C, d, w.dg, w.rdg);
     RF_TRY(check_launch("rf_solve_pinv: diagonal"));
@@ -931,48 +1197,56 @@ rf_status rf_solve_pinv(const rf_gram_desc* desc, const void* d_state, double la
     const int ny = (int)ceil_div(d, 2048);
     hipLaunchKernelGGL(k_centre_split, dim3((unsigned)(rows * ny)), dim3(256), 0, s, ca, ny);
     RF_TRY(check_launch("rf_solve_pinv: cross moments"));
-    hipLaunchKernelGGL(k_split_inverse, dim3((unsigned)(d / 64), (unsigned)(d / 64)), dim3(256), 0, s, w.C, w.dg, d, w.Bq);
-    RF_TRY(check_launch("rf_solve_pinv: split pseudo-inverse"));
-    WArgs wa{};
-    wa.Aq = w.Aq; wa.Bq = w.Bq; wa.rdg = w.rdg; wa.sx = sx; wa.np = np; wa.d = d; wa.rows = rows;
-    wa.tiles_j = (int)(d / 256); wa.tiles_c = (int)(rows / 256); wa.W = d_W; wa.Wlp = (bf16_t*)d_W_lp;
-    wa.bpart = w.bpart;
-    hipLaunchKernelGGL(k_wgemm, dim3((unsigned)(wa.tiles_j * wa.tiles_c)), dim3(PackedAGemm::kThr), 0, s, wa);
-    RF_TRY(check_launch("rf_solve_pinv: W product"));
-    if (d_b) {
-        hipLaunchKernelGGL(k_bias, dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0, s, w.bpart, wa.tiles_j, w.mu_y,
-                           rows, d_b);
-        RF_TRY(check_launch("rf_solve_pinv: bias"));
-    }
+    // the maps from the pseudo-inverse: the split product, or the fp64 one where the
+    // equilibrated pseudo-inverse is too large for it (as rf_solve's RF_PRODUCT_AUTO)
+    RF_TRY(solve_products(s, w, 0, d, rows, ca, RF_PRODUCT_AUTO, d_W, (bf16_t*)d_W_lp, d_b, nullptr));
     return RF_OK;
 }
 
-size_t rf_solve_workspace_bytes(const rf_gram_desc* desc, int32_t n_sel) {
+size_t rf_solve_workspace_bytes(const rf_gram_desc* desc, int32_t n_sel, int32_t n_lambda) {
     rf_gram_layout_t GL;
-    if (n_sel < 0 || rf_gram_state_layout(desc, &GL) != RF_OK) return 0;
-    return solve_ws(nullptr, desc->d, gram_dy(desc), n_sel).total;
+    if (n_sel < 0 || n_lambda < 1 || n_lambda > kMaxLambda || rf_gram_state_layout(desc, &GL) != RF_OK) return 0;
+    return solve_ws(nullptr, desc->d, gram_dy(desc), n_sel, n_lambda).total;
 }
 
-rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, double lambda, rf_lambda_mode mode,
-                   const int32_t* targets, int32_t n_sel, float* d_W, void* d_W_lp, float* d_b, int32_t* d_info,
-                   void* d_ws, size_t ws_bytes, void* stream) {
+rf_status rf_info_status(const int32_t* info, int32_t n) {
+    clear_error();
+    RF_REQUIRE(n >= 0 && (n == 0 || info), RF_ERR_INVALID_ARG, "rf_info_status: null info");
+    for (int32_t i = 0; i < n; ++i)
+        if (info[i] != 0)
+            return fail(RF_ERR_NOT_SPD, "lambda " + std::to_string(i) + ": the regularised Gram is not positive definite "
+                                        "(first failing leading minor " + std::to_string(info[i]) + ")");
+    return RF_OK;
+}
+
+rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, const double* lambdas, int32_t n_lambda,
+                   rf_lambda_mode mode, const int32_t* targets, int32_t n_sel, rf_product product, float* d_W,
+                   void* d_W_lp, float* d_b, int32_t* d_info, double* d_cond, double* d_resid, void* d_ws,
+                   size_t ws_bytes, void* stream) {
     clear_error();
     rf_gram_layout_t GL;
     rf_status st = rf_gram_state_layout(desc, &GL);
     if (st != RF_OK) return st;
     RF_REQUIRE(d_state && aligned(d_state, 256), RF_ERR_INVALID_ARG, "rf_solve: state must be non-null, 256-B aligned");
     RF_REQUIRE(d_info, RF_ERR_INVALID_ARG, "rf_solve: null info");
-    RF_REQUIRE(isfinite(lambda) && lambda >= 0.0, RF_ERR_INVALID_ARG, "rf_solve: lambda must be finite and >= 0");
+    RF_REQUIRE(lambdas && n_lambda >= 1 && n_lambda <= kMaxLambda, RF_ERR_INVALID_ARG,
+               "rf_solve: need 1..8 lambdas (host array)");
+    for (int i = 0; i < n_lambda; ++i)
+        RF_REQUIRE(isfinite(lambdas[i]) && lambdas[i] >= 0.0, RF_ERR_INVALID_ARG, "rf_solve: lambda must be finite and >= 0");
     RF_REQUIRE(mode == RF_LAMBDA_ABSOLUTE || mode == RF_LAMBDA_REL_MEAN_DIAG, RF_ERR_INVALID_ARG, "rf_solve: bad lambda mode");
+    RF_REQUIRE(product == RF_PRODUCT_AUTO || product == RF_PRODUCT_SPLIT_BF16 || product == RF_PRODUCT_F64,
+               RF_ERR_INVALID_ARG, "rf_solve: bad product route");
     RF_REQUIRE(n_sel >= 0 && n_sel <= kMaxSel, RF_ERR_UNSUPPORTED, "rf_solve: 0..64 selected targets");
     RF_REQUIRE(n_sel == 0 || targets, RF_ERR_INVALID_ARG, "rf_solve: null targets");
     for (int i = 0; i < n_sel; ++i)
         RF_REQUIRE(targets[i] >= 0 && targets[i] < desc->n_targets, RF_ERR_INVALID_ARG, "rf_solve: target index out of range");
     RF_REQUIRE(aligned(d_ws, 256), RF_ERR_INVALID_ARG, "rf_solve: workspace must be 256-B aligned");
-    RF_REQUIRE(aligned(d_W, 16) && aligned(d_W_lp, 16) && aligned(d_b, 4), RF_ERR_INVALID_ARG,
-               "rf_solve: W outputs must be 16-byte aligned");
+    RF_REQUIRE(aligned(d_W, 16) && aligned(d_W_lp, 16) && aligned(d_b, 4) && aligned(d_cond, 8) && aligned(d_resid, 8),
+               RF_ERR_INVALID_ARG, "rf_solve: W outputs must be 16-byte aligned");
+    RF_REQUIRE(!d_resid || d_W, RF_ERR_INVALID_ARG, "rf_solve: the residual is computed from the fp32 maps (d_W)");
     const int64_t d = desc->d, dy = gram_dy(desc);
-    const SolveWs w = solve_ws(d_ws, d, dy, n_sel);
+    const int nl = n_lambda;
+    const SolveWs w = solve_ws(d_ws, d, dy, n_sel, nl);
     RF_REQUIRE(d_ws && ws_bytes >= w.total, RF_ERR_WORKSPACE, "rf_solve: workspace too small");
     hipStream_t s = (hipStream_t)stream;
     const char* sp = (const char*)d_state;
@@ -981,12 +1255,19 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, double lambda,
     const double* sx = (const double*)(sp + GL.off_s_x);
     const double* sy = (const double*)(sp + GL.off_s_y);
     const int64_t* np = (const int64_t*)(sp + GL.off_n);
+    const int64_t dd = d * d;
+    const int rel = (int)(mode == RF_LAMBDA_REL_MEAN_DIAG);
+    Lambdas lams{};
+    for (int i = 0; i < nl; ++i) lams.v[i] = lambdas[i];
 
-    hipLaunchKernelGGL(k_zero_int, dim3(1), dim3(1), 0, s, d_info);
+    // A_z = C + lambda_z I for every lambda of the batch; the equilibration D = diag(A_0) is
+    // shared by the batch (any positive diagonal scaling leaves the products exact in theory;
+    // one D lets the split cross moments serve every lambda)
+    hipLaunchKernelGGL(k_zero_int, dim3(1), dim3(64), 0, s, d_info, nl);
     RF_TRY(check_launch("rf_solve: info"));
-    hipLaunchKernelGGL(k_centre_gram, dim3(grid_for(d * d)), dim3(256), 0, s, Sxx, sx, np, d, w.C);
+    hipLaunchKernelGGL(k_centre_gram, dim3(grid_for(dd), (unsigned)nl), dim3(256), 0, s, Sxx, sx, np, d, w.C);
     RF_TRY(check_launch("rf_solve: centre"));
-    hipLaunchKernelGGL(k_add_lambda, dim3(1), dim3(256), 0, s, w.C, d, lambda, (int)(mode == RF_LAMBDA_REL_MEAN_DIAG));
+    hipLaunchKernelGGL(k_add_lambda, dim3((unsigned)nl), dim3(256), 0, s, w.C, d, lams, rel);
     RF_TRY(check_launch("rf_solve: lambda"));
     hipLaunchKernelGGL(k_diag_sqrt, dim3(grid_for(d)), dim3(256), 0, s, w.C, d, w.dg, w.rdg);
     RF_TRY(check_launch("rf_solve: diagonal"));
@@ -1000,46 +1281,69 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, double lambda,
     for (int i = 0; i < n_sel; ++i) ca.tsel[i] = targets[i];
     const int ny = (int)ceil_div(d, 2048);
 
-    // blocked Cholesky
+    // blocked Cholesky of every A_z: each step factors diagonal block J of all of them in one
+    // launch (one wave each), then updates their panels and trailing matrices in batched products
     const int nblk = (int)(d / kNB);
     const int64_t rows_per = ceil_div(rows, nblk);
     for (int J = 0; J < nblk; ++J) {
         const int64_t c0 = (int64_t)J * kNB;
         const int64_t cb = std::min<int64_t>(rows, J * rows_per), ce = std::min<int64_t>(rows, cb + rows_per);
-        hipLaunchKernelGGL(k_chol_diag, dim3((unsigned)(1 + (ce - cb) * ny)), dim3(256), 0, s, w.C, d, J, w.Dinv,
-                           d_info, ca, cb, ce, ny);
+        hipLaunchKernelGGL(k_chol_diag, dim3((unsigned)(nl + (ce - cb) * ny)), dim3(256), 0, s, w.C, dd, d, J, w.Dinv,
+                           d * kNB, d_info, nl, ca, cb, ce, ny);
         RF_TRY(check_launch("rf_solve: potrf"));
         const int64_t rem = d - c0 - kNB;
         if (rem <= 0) continue;
         // L21 = A21 L11^-T in place on the matrix cores: one column of 64 x 64 tiles, each of which
         // reads all of its rows of A21 before writing them
         double* panel = w.C + (c0 + kNB) * d + c0;
-        hipLaunchKernelGGL((k_dgemm<true, 64>), dim3((unsigned)ceil_div(rem, 64), 1u), dim3(256), 0, s, rem,
-                           (int64_t)kNB, (int64_t)kNB, 1.0, (const double*)panel, d, (const double*)(w.Dinv + c0 * kNB),
-                           (int64_t)kNB, 0.0, panel, d, (int)kFull, (int64_t)0, (int64_t)0, (int64_t)0);
+        hipLaunchKernelGGL((k_dgemm<true, 64>), dim3((unsigned)ceil_div(rem, 64), 1u, (unsigned)nl), dim3(256), 0, s,
+                           rem, (int64_t)kNB, (int64_t)kNB, 1.0, (const double*)panel, d,
+                           (const double*)(w.Dinv + c0 * kNB), (int64_t)kNB, 0.0, panel, d, (int)kFull, dd, d * kNB, dd,
+                           (const int32_t*)nullptr);
         RF_TRY(check_launch("rf_solve: panel"));
         RF_TRY(dgemm<true>(s, rem, rem, kNB, -1.0, panel, d, panel, d, 1.0, w.C + (c0 + kNB) * d + c0 + kNB, d,
-                           kLowerOnly));
+                           kLowerOnly, nl, dd, dd, dd));
     }
-    // A^-1 = Z Z^T with Z = L^-T (the factor is no longer needed afterwards: A^-1 overwrites it)
-    RF_TRY(inverse_factor(s, w, d, w.Cinv));
-    // lower triangle only (by 128-blocks): A^-1 is symmetric and its one reader mirrors it
-    RF_TRY(dgemm<true>(s, d, d, d, 1.0, w.Cinv, d, w.Cinv, d, 0.0, w.C, d, kUpperOperands | kLowerOnly));
+    for (int z = 0; z < nl; ++z) {
+        double* Cz = w.C + z * dd;
+        double* Zz = w.Cinv + z * dd;
+        // A^-1 = Z Z^T with Z = L^-T (the factor is no longer needed afterwards: A^-1 overwrites it)
+        RF_TRY(inverse_factor(s, w, Cz, w.Dinv + z * d * kNB, d, Zz));
+        // lower triangle only (by 128-blocks): A^-1 is symmetric and its readers mirror it
+        RF_TRY(dgemm<true>(s, d, d, d, 1.0, Zz, d, Zz, d, 0.0, Cz, d, kUpperOperands | kLowerOnly));
+    }
     if (n_sel == 0) return RF_OK;
 
-    // equilibrated split operands, then W on the MFMA pipes
-    hipLaunchKernelGGL(k_split_inverse, dim3((unsigned)(d / 64), (unsigned)(d / 64)), dim3(256), 0, s, w.C, w.dg, d, w.Bq);
-    RF_TRY(check_launch("rf_solve: split inverse"));
-    WArgs wa{};
-    wa.Aq = w.Aq; wa.Bq = w.Bq; wa.rdg = w.rdg; wa.sx = sx; wa.np = np; wa.d = d; wa.rows = rows;
-    wa.tiles_j = (int)(d / 256); wa.tiles_c = (int)(rows / 256); wa.W = d_W; wa.Wlp = (bf16_t*)d_W_lp;
-    wa.bpart = w.bpart;
-    hipLaunchKernelGGL(k_wgemm, dim3((unsigned)(wa.tiles_j * wa.tiles_c)), dim3(PackedAGemm::kThr), 0, s, wa);
-    RF_TRY(check_launch("rf_solve: W product"));
-    if (d_b) {
-        hipLaunchKernelGGL(k_bias, dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0, s, w.bpart, wa.tiles_j, w.mu_y,
-                           rows, d_b);
-        RF_TRY(check_launch("rf_solve: bias"));
+    for (int z = 0; z < nl; ++z) {
+        float* Wz = d_W ? d_W + z * rows * d : nullptr;
+        bf16_t* Wlpz = d_W_lp ? (bf16_t*)d_W_lp + z * rows * d : nullptr;
+        float* bz = d_b ? d_b + z * rows : nullptr;
+        RF_TRY(solve_products(s, w, z, d, rows, ca, product, Wz, Wlpz, bz, d_cond ? d_cond + z : nullptr));
+        if (d_resid) {
+            // stationarity residual in fp64: R = W A - B with A rebuilt from the state
+            double* Af = w.Cinv + z * dd;
+            hipLaunchKernelGGL(k_centre_gram, dim3(grid_for(dd), 1u), dim3(256), 0, s, Sxx, sx, np, d, Af);
+            RF_TRY(check_launch("rf_solve: residual matrix"));
+            Lambdas one{};
+            one.v[0] = lambdas[z];
+            hipLaunchKernelGGL(k_add_lambda, dim3(1), dim3(256), 0, s, Af, d, one, rel);
+            RF_TRY(check_launch("rf_solve: residual lambda"));
+            for (int64_t r0 = 0; r0 < rows; r0 += w.rb) {
+                const int64_t nr = std::min<int64_t>(w.rb, rows - r0);
+                hipLaunchKernelGGL(k_centre_f64, dim3((unsigned)nr), dim3(256), 0, s, ca, r0, w.Bf, w.bmax,
+                                   (const int32_t*)nullptr);
+                RF_TRY(check_launch("rf_solve: residual cross moments"));
+                hipLaunchKernelGGL(k_widen_rows, dim3(grid_for(nr * d)), dim3(256), 0, s, (const float*)Wz, r0, nr, d,
+                                   w.Wf);
+                RF_TRY(check_launch("rf_solve: residual maps"));
+                RF_TRY(dgemm<false>(s, nr, d, d, 1.0, w.Wf, d, Af, d, -1.0, w.Bf, d));
+                hipLaunchKernelGGL(k_row_absmax, dim3((unsigned)nr), dim3(256), 0, s, (const double*)w.Bf, r0, d, w.rmax);
+                RF_TRY(check_launch("rf_solve: residual maxima"));
+            }
+            hipLaunchKernelGGL(k_resid_final, dim3((unsigned)n_sel), dim3(256), 0, s, (const double*)w.rmax,
+                               (const double*)w.bmax, dy, d_resid + (int64_t)z * n_sel);
+            RF_TRY(check_launch("rf_solve: residual"));
+        }
     }
     return RF_OK;
 }

@@ -8,7 +8,7 @@ from typing import List, Optional, Sequence
 
 import torch
 
-from . import (RF_LAYOUT_CONTIGUOUS, RF_LAYOUT_PAGED, FillWeights, TranslateWeights, cache_desc, gram_desc,
+from . import (RF_LAYOUT_CONTIGUOUS, RF_LAYOUT_PAGED, RF_PRODUCT_AUTO, FillWeights, TranslateWeights, cache_desc, gram_desc,
                rf_cache_layout, rf_fill, rf_fill_streamed, rf_fill_streamed_ring_bytes, rf_fill_workspace_bytes,
                rf_fit_r2, rf_fit_r2_workspace_bytes, rf_gram_select,
                rf_gram_accumulate, rf_gram_init,
@@ -83,17 +83,31 @@ class GramState:
         return W, Wlp, b
 
     def solve(self, lam: float, mode: int, targets: Sequence[int], want_f32=True, want_bf16=True, stream=None,
-              ws: Optional[torch.Tensor] = None):
+              ws: Optional[torch.Tensor] = None, product: int = RF_PRODUCT_AUTO):
+        """Maps for one ridge strength: (W [n_sel, m, d] fp32, W_lp packed bf16, b, info [1])."""
+        W, Wlp, b, info, _, _ = self.solve_many([lam], mode, targets, want_f32, want_bf16, stream, ws, product)
+        return (None if W is None else W[0], None if Wlp is None else Wlp[0], b[0], info)
+
+    def solve_many(self, lambdas: Sequence[float], mode: int, targets: Sequence[int], want_f32=True, want_bf16=True,
+                   stream=None, ws: Optional[torch.Tensor] = None, product: int = RF_PRODUCT_AUTO,
+                   want_resid: bool = False):
+        """Maps for a batch of ridge strengths from one call (rf_solve): W [n_lambda, n_sel, m, d]
+        fp32, W_lp (packed bf16), b [n_lambda, n_sel, m], info [n_lambda], cond [n_lambda] (the
+        largest entry of the equilibrated inverse) and, with ``want_resid``, the stationarity
+        residual [n_lambda, n_sel] (fp64)."""
         dev = self.buf.device
-        n_sel = len(targets)
-        W = torch.empty(n_sel, self.dy, self.d, dtype=torch.float32, device=dev) if want_f32 else None
-        Wlp = torch.empty(n_sel, self.dy, self.d, dtype=torch.bfloat16, device=dev) if want_bf16 else None
-        b = torch.empty(n_sel, self.dy, dtype=torch.float32, device=dev)
-        info = torch.empty(1, dtype=torch.int32, device=dev)
+        n_sel, nl = len(targets), len(lambdas)
+        W = torch.empty(nl, n_sel, self.dy, self.d, dtype=torch.float32, device=dev) if want_f32 or want_resid else None
+        Wlp = torch.empty(nl, n_sel, self.dy, self.d, dtype=torch.bfloat16, device=dev) if want_bf16 else None
+        b = torch.empty(nl, n_sel, self.dy, dtype=torch.float32, device=dev)
+        info = torch.empty(nl, dtype=torch.int32, device=dev)
+        cond = torch.empty(nl, dtype=torch.float64, device=dev)
+        resid = torch.empty(nl, n_sel, dtype=torch.float64, device=dev) if want_resid else None
         if ws is None:
-            ws = device_bytes(rf_solve_workspace_bytes(self.desc, n_sel), dev)
-        rf_solve(self.desc, self.buf, lam, mode, list(targets), W, Wlp, b, info, ws, stream)
-        return W, Wlp, b, info
+            ws = device_bytes(rf_solve_workspace_bytes(self.desc, n_sel, nl), dev)
+        rf_solve(self.desc, self.buf, list(lambdas), mode, list(targets), W, Wlp, b, info, ws, stream,
+                 product=product, cond=cond, resid=resid)
+        return W, Wlp, b, info, cond, resid
 
 
 def greedy_sources(state: GramState, block_width: int, nu: int, lam: float, mode: int,

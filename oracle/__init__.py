@@ -22,14 +22,15 @@ Parity status: every function here is pinned by tests/test_oracle_*.py against c
 forms, limits, brute force or an independent library route.
 """
 from .ridge import (NotSPD, gram_sums, fit, fit_from_sums, fit_pinv, ridge_objective,
-                    solve_columns_from_data)
+                    solve_columns_from_data, stationarity_residual, stationarity_residual_from_sums)
 from .fill import rope_inverse_frequencies, rope_rotate, rmsnorm, fill_layer, fill
 from .translate import (relative_depth_centre, relative_depth_sources, headwise_dense,
                         translate_layer, translate, fit_translator, fit_r2, r2_assignment,
                         greedy_sources)
 
 __all__ = ["NotSPD", "gram_sums", "fit", "fit_from_sums", "fit_pinv", "ridge_objective",
-           "solve_columns_from_data", "rope_inverse_frequencies", "rope_rotate", "rmsnorm",
+           "solve_columns_from_data", "stationarity_residual", "stationarity_residual_from_sums",
+           "rope_inverse_frequencies", "rope_rotate", "rmsnorm",
            "fill_layer", "fill", "relative_depth_centre", "relative_depth_sources",
            "headwise_dense", "translate_layer", "translate", "fit_translator", "fit_r2",
            "r2_assignment", "greedy_sources"]

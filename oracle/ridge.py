@@ -112,6 +112,32 @@ def solve_columns_from_data(X, Y_cols, lam: float, mode: str = "absolute"):
     return fit(X, Y_cols, lam, mode)
 
 
+def stationarity_residual(X, Y, W, lam: float, mode: str = "absolute") -> float:
+    """How far W is from solving the ridge normal equations on the centred rows: with
+    C = X~^T X~ and B = X~^T Y~, max |(C + lam I) W - B| / max |B| (0 for the exact map).
+    The ridge map is the stationary point of the objective, where X~^T (X~ W - Y~) + lam W = 0;
+    this is that gradient, scaled by the cross moments."""
+    X = _f64(X)
+    Y = _f64(Y)
+    Xc = X - X.mean(axis=0)
+    Yc = Y - Y.mean(axis=0)
+    C = Xc.T @ Xc
+    B = Xc.T @ Yc
+    A = C + _lambda_value(C, lam, mode) * np.eye(C.shape[0])
+    return float(np.max(np.abs(A @ _f64(W) - B)) / np.max(np.abs(B)))
+
+
+def stationarity_residual_from_sums(S_xx, S_xy, s_x, s_y, n: int, W, lam: float, mode: str = "absolute") -> float:
+    """The same residual with C and B centred from raw one-pass sums (as ``fit_from_sums``):
+    C = S_xx - s_x^T s_x / n, B = S_xy - s_x^T s_y / n.  S_xx must be the full symmetric matrix."""
+    S_xx = _f64(S_xx)
+    s_x = _f64(s_x)
+    C = S_xx - np.outer(s_x, s_x) / n
+    B = _f64(S_xy) - np.outer(s_x, _f64(s_y)) / n
+    A = C + _lambda_value(C, lam, mode) * np.eye(C.shape[0])
+    return float(np.max(np.abs(A @ _f64(W) - B)) / np.max(np.abs(B)))
+
+
 def ridge_objective(X, Y, W, lam: float) -> float:
     """The ridge objective on centred rows, used to check optimality by perturbation."""
     X = _f64(X)

@@ -166,6 +166,27 @@ def hidden_states(cfg: Config, rows: int, stream: str, chunk: int = 0, device="c
     return _store(z * channel_scales(cfg, device=device), cfg)
 
 
+def low_rank_states(cfg: Config, rows: int, stream: str, chunk: int = 0, device="cpu", rank: int = 64,
+                    sigma: float = 0.2, n_dup: int = 8, dup_noise: float = 0.2) -> torch.Tensor:
+    """Rows of an anisotropic split-layer state of low effective rank with near-duplicate
+    channels, [rows, d] in the storage dtype: the shape of trained caches in the KV-Lingo
+    page's rank table (appendix B.2, Table 3: effective rank far below the width, a few
+    directions carrying most of the variance).
+        X = (F M + sigma Z) * s
+    F [rows, rank] ~ N(0, 1) per chunk; M [rank, d] a fixed seeded mixing whose row i has
+    scale 3 exp(-4 i / rank) / sqrt(rank); Z ~ N(0, 1); channel 2k + 1 is then channel 2k plus
+    dup_noise N(0, 1) for k < n_dup; s the per-channel log-normal scales."""
+    F = _randn((rows, rank), cfg.seed, "lowrank-F", stream, chunk, device=device)
+    decay = 3.0 * torch.exp(-4.0 * torch.arange(rank, dtype=torch.float32, device=device) / rank) / rank ** 0.5
+    M = _randn((rank, cfg.d), cfg.seed, "lowrank-M", device=device) * decay[:, None]
+    X = F @ M + sigma * _randn((rows, cfg.d), cfg.seed, "lowrank-Z", stream, chunk, device=device)
+    D = _randn((rows, n_dup), cfg.seed, "lowrank-dup", stream, chunk, device=device)
+    for k in range(n_dup):
+        X[:, 2 * k + 1] = X[:, 2 * k] + dup_noise * D[:, k]
+    s = torch.exp(0.5 * _randn((cfg.d,), cfg.seed, "lowrank-scale", device=device))
+    return _store(X * s, cfg)
+
+
 def planted_map(cfg: Config, layer: int, device="cpu") -> torch.Tensor:
     """Dense planted map A_l ~ N(0, 1/d), [d_in, d_out] (x-times-matrix convention)."""
     return _randn((cfg.d, cfg.d), cfg.seed, "A", layer, device=device) / cfg.d ** 0.5

@@ -122,13 +122,35 @@ def test_solve_validation_before_enqueue():
     desc = rf.gram_desc(256, 2, torch.float32)
     ws_bytes = rf.rf_solve_workspace_bytes(desc, 2)
     assert ws_bytes > 2 * 256 * 256 * 8
-    ws = torch.empty(16, dtype=torch.uint8)
-    for lam, targets, status in [(-1.0, [0], rf.RF_ERR_INVALID_ARG), (float("nan"), [0], rf.RF_ERR_INVALID_ARG),
-                                 (0.1, [2], rf.RF_ERR_INVALID_ARG), (0.1, [0], rf.RF_ERR_WORKSPACE)]:
+    # each extra lambda of a batch adds its own factor and inverse (2 d^2 fp64) and little else
+    assert rf.rf_solve_workspace_bytes(desc, 2, 3) - ws_bytes >= 2 * 2 * 256 * 256 * 8
+    assert rf.rf_solve_workspace_bytes(desc, 2, 0) == 0 and rf.rf_solve_workspace_bytes(desc, 2, 9) == 0
+
+    def call(lams, targets, product=0, W=None, resid=None):
+        la = (C.c_double * max(1, len(lams)))(*lams)
+        rf._check(rf._lib.rf_solve(C.byref(desc), 256, la, len(lams), 0, (C.c_int32 * 1)(*targets), len(targets),
+                                   product, W, None, None, 512, None, resid, 256, 16, None))
+
+    for lams, targets, kw, status in [([-1.0], [0], {}, rf.RF_ERR_INVALID_ARG),
+                                      ([float("nan")], [0], {}, rf.RF_ERR_INVALID_ARG),
+                                      ([0.1, -1.0], [0], {}, rf.RF_ERR_INVALID_ARG),
+                                      ([], [0], {}, rf.RF_ERR_INVALID_ARG),
+                                      ([0.1] * 9, [0], {}, rf.RF_ERR_INVALID_ARG),
+                                      ([0.1], [2], {}, rf.RF_ERR_INVALID_ARG),
+                                      ([0.1], [0], dict(product=3), rf.RF_ERR_INVALID_ARG),
+                                      ([0.1], [0], dict(resid=1024), rf.RF_ERR_INVALID_ARG),   # residual needs W
+                                      ([0.1], [0], {}, rf.RF_ERR_WORKSPACE),
+                                      ([1e-3, 0.1, 10.0], [0], dict(W=256, resid=1024), rf.RF_ERR_WORKSPACE)]:
         with pytest.raises(rf.RidgeFillError) as e:
-            rf._check(rf._lib.rf_solve(C.byref(desc), 256, lam, 0, (C.c_int32 * 1)(*targets), len(targets),
-                                       None, None, None, 512, 256, 16, None))
-        assert e.value.status == status, (lam, targets)
+            call(lams, targets, **kw)
+        assert e.value.status == status, (lams, targets, kw)
+
+
+def test_info_status_host():
+    assert rf.rf_info_status([0, 0, 0]) == rf.RF_OK
+    assert rf.rf_info_status([]) == rf.RF_OK
+    assert rf.rf_info_status([0, 78, 0]) == rf.RF_ERR_NOT_SPD
+    assert "lambda 1" in rf.rf_last_error() and "78" in rf.rf_last_error()
 
 
 def _weights(d=256, H=4, dh=64, dtype=torch.float32, n=1, ptr=256):

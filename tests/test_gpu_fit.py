@@ -307,36 +307,42 @@ def test_gram_select_equals_a_pass_over_the_selected_columns():
 
 
 def test_fit_pinv_route_regular_and_rank_deficient():
-    # the eigendecomposition route: on a regular system it gives rf_solve's map; with lambda = 0
-    # on rank-deficient rows (duplicated and constant columns: rf_solve reports a failed pivot)
-    # it gives the minimum-norm least-squares map of the oracle
+    # the eigendecomposition route: with lambda = 0 on rank-deficient rows (duplicated and
+    # constant columns: rf_solve reports a failed pivot) it gives the minimum-norm
+    # least-squares map of the oracle; on a regular system (the exact duplicates alone, at the
+    # workloads' lambda = 0.1) it gives rf_solve's map.  The duplicates leave the equilibrated
+    # inverse entries ~ n var / lambda, so both routes take the fp64 product there.
     from linear_kv_cache_amd.runner import GramState
     g = synth.generator(61, "pinv")
     n, d = 3000, 256
     base = torch.randn(n, 200, generator=g) * (0.5 + torch.rand(200, generator=g))
     X = torch.cat([base, base[:, :40], torch.full((n, 16), 2.0)], dim=1).to(torch.bfloat16)   # rank 200 of 256
+    Xr = torch.cat([base, base[:, :40], torch.randn(n, 16, generator=g)], dim=1).to(torch.bfloat16)   # duplicates only
     Ys = [(base @ (torch.randn(200, d, generator=g) / 15) + 0.1 * torch.randn(n, d, generator=g)).to(torch.bfloat16)
           for _ in range(2)]
-    st = GramState(d, 2, torch.bfloat16, "cuda")
-    st.accumulate(X.cuda(), [Y.cuda() for Y in Ys])
-    # (the regular case takes lambda at the scale of the features' sums of squares: with exact
-    # duplicates and lambda far below it, the equilibrated inverse holds entries ~ n var / lambda
-    # that the split-bf16 W product cannot resolve to 1e-3 on either route)
-    for lam, label in ((0.0, "rank-deficient, lambda 0"), (300.0, "regular, lambda 300")):
+    for Xs, lam, label in ((X, 0.0, "rank-deficient, lambda 0"), (Xr, 0.1, "duplicated columns, lambda 0.1")):
+        st = GramState(d, 2, torch.bfloat16, "cuda")
+        st.accumulate(Xs.cuda(), [Y.cuda() for Y in Ys])
         W, _, b = st.solve_pinv(lam, 0, [0, 1])
         torch.cuda.synchronize()
         ew, eb = [], []
         for l in range(2):
-            W_ref, b_ref = oracle.fit_pinv(f64(X), f64(Ys[l]), lam)
+            W_ref, b_ref = oracle.fit_pinv(f64(Xs), f64(Ys[l]), lam)
             ew.append(float(np.max(np.abs(f64(W[l]).T - W_ref)) / np.max(np.abs(W_ref))))
             eb.append(float(np.max(np.abs(f64(b[l]) - b_ref)) / max(np.max(np.abs(b_ref)), 1e-30)))
         log(f"[fit] pseudo-inverse route, {label}: W_err={max(ew):.3e} b_err={max(eb):.3e}")
         assert max(ew) <= W_TOL and max(eb) <= W_TOL
         if lam > 0:
-            W2, _, b2, info = st.solve(lam, 0, [0, 1], want_bf16=False)
+            W2, _, b2, info, cond, _ = st.solve_many([lam], 0, [0, 1], want_bf16=False)
             torch.cuda.synchronize()
             assert int(info.item()) == 0
-            assert float((W2 - W).abs().max() / W2.abs().max()) <= W_TOL
-    _, _, _, info = st.solve(0.0, 0, [0], want_bf16=False)
-    torch.cuda.synchronize()
-    assert int(info.item()) > 0          # the Cholesky route cannot factor the singular system
+            log(f"[fit] Cholesky route on the same system: cond={float(cond.item()):.3e}")
+            assert float(cond.item()) > 8.0
+            assert float((W2[0] - W).abs().max() / W2[0].abs().max()) <= W_TOL
+            for l in range(2):
+                W_ref, _ = oracle.fit(f64(Xs), f64(Ys[l]), lam)
+                assert float(np.max(np.abs(f64(W2[0, l]).T - W_ref)) / np.max(np.abs(W_ref))) <= W_TOL
+        else:
+            _, _, _, info = st.solve(0.0, 0, [0], want_bf16=False)
+            torch.cuda.synchronize()
+            assert int(info.item()) > 0          # the Cholesky route cannot factor the singular system

@@ -242,3 +242,43 @@ def test_pinv_route_rank_deficient_is_minimum_norm_least_squares():
     null[3, 3], null[9, 3] = 2.0, -1.0
     assert np.allclose(Xc @ null, 0.0, atol=1e-12)
     assert np.max(np.abs(null.T @ W)) <= 1e-9 * np.max(np.abs(W))
+
+
+def test_stationarity_residual_hand_worked_and_limits():
+    # one feature, three rows: X~ = (-1, 0, 1), Y~ = (-7/3, -1/3, 8/3), so C = 2, B = 5; with
+    # lambda = 1, A = 3 and the residual of w is |3 w - 5| / 5 (0.4 at w = 1, 0 at w = 5/3)
+    X = np.array([[1.0], [2.0], [3.0]])
+    Y = np.array([[2.0], [4.0], [7.0]])
+    assert abs(oracle.stationarity_residual(X, Y, np.array([[1.0]]), 1.0) - 0.4) <= 1e-15
+    assert oracle.stationarity_residual(X, Y, np.array([[5.0 / 3.0]]), 1.0) <= 1e-15
+    # W = 0 leaves all of B
+    rng = np.random.default_rng(3)
+    X = rng.standard_normal((200, 6))
+    Y = X @ rng.standard_normal((6, 4)) + 0.1 * rng.standard_normal((200, 4))
+    assert oracle.stationarity_residual(X, Y, np.zeros((6, 4)), 0.5) == 1.0
+    # the fitted map is stationary (the survey's pin: <= 1e-12)
+    W, _ = oracle.fit(X, Y, 0.5)
+    assert oracle.stationarity_residual(X, Y, W, 0.5) <= 1e-12
+    # one entry moved by delta: the residual is delta times the largest entry of that row of A
+    Xc = X - X.mean(0)
+    A = Xc.T @ Xc + 0.5 * np.eye(6)
+    B = Xc.T @ (Y - Y.mean(0))
+    W2 = W.copy()
+    W2[2, 1] += 1e-3
+    want = 1e-3 * np.max(np.abs(A[:, 2])) / np.max(np.abs(B))
+    assert abs(oracle.stationarity_residual(X, Y, W2, 0.5) - want) <= 1e-12
+    # a transposed map (a plausible layout mistake) is far from stationary
+    Ws, _ = oracle.fit(X, X @ rng.standard_normal((6, 6)), 0.5)
+    assert oracle.stationarity_residual(X, X @ Ws, Ws.T, 0.5) > 1e-2
+
+
+def test_stationarity_residual_from_sums_equals_data_route():
+    rng = np.random.default_rng(4)
+    X = rng.standard_normal((300, 8)) + 2.0
+    Y = X @ rng.standard_normal((8, 5)) + rng.standard_normal((300, 5))
+    W = rng.standard_normal((8, 5))
+    S_xx, S_xy, s_x, s_y, n = oracle.gram_sums(X, [Y])
+    for lam, mode in ((0.3, "absolute"), (1e-2, "rel_mean_diag")):
+        a = oracle.stationarity_residual(X, Y, W, lam, mode)
+        b = oracle.stationarity_residual_from_sums(S_xx, S_xy[0], s_x, s_y[0], n, W, lam, mode)
+        assert abs(a - b) <= 1e-12 * max(1.0, a)
