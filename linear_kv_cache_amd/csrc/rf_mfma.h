@@ -49,6 +49,15 @@ template <> struct ElemTraits<float> {
     __device__ static inline float to_f32(uint32_t bits) { return __uint_as_float(bits); }
 };
 
+// f as an fp32 value the compiler must materialise.  A double narrowed to fp32 and then to bf16
+// is rounded twice, as the fp32 copy of the same value is; without the barrier the compiler
+// may fuse the two narrowings into one rounding from the double (which can differ in the last
+// bf16 bit from rounding the stored fp32 value).
+__device__ inline float opaque_f32(float f) {
+    __asm__("" : "+v"(f));
+    return f;
+}
+
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
     __bf16 a = (__bf16)lo;  // round to nearest even (v_cvt_pk_bf16_f32)
     __bf16 b = (__bf16)hi;

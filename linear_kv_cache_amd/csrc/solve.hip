@@ -611,10 +611,12 @@ __global__ __launch_bounds__(256) void k_store_f64(const double* Wf, int64_t r0,
     for (int64_t j = 4 * threadIdx.x; j < d; j += 1024) {
         const double w0 = wr[j], w1 = wr[j + 1], w2 = wr[j + 2], w3 = wr[j + 3];
         dot += w0 * a.sx[j] + w1 * a.sx[j + 1] + w2 * a.sx[j + 2] + w3 * a.sx[j + 3];
-        if (W) *(f32x4*)(W + r * d + j) = f32x4{(float)w0, (float)w1, (float)w2, (float)w3};
+        // the bf16 map is the fp32 map rounded once more (not the double rounded once)
+        const float f0 = opaque_f32((float)w0), f1 = opaque_f32((float)w1);
+        const float f2 = opaque_f32((float)w2), f3 = opaque_f32((float)w3);
+        if (W) *(f32x4*)(W + r * d + j) = f32x4{f0, f1, f2, f3};
         if (Wlp)
-            *(u32x2*)(Wlp + wl_base + packed_col_part((int)j)) =
-                u32x2{pack_bf16x2((float)w0, (float)w1), pack_bf16x2((float)w2, (float)w3)};
+            *(u32x2*)(Wlp + wl_base + packed_col_part((int)j)) = u32x2{pack_bf16x2(f0, f1), pack_bf16x2(f2, f3)};
     }
     if (!b) return;
     red[threadIdx.x] = dot;
