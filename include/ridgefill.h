@@ -360,6 +360,27 @@ rf_status rf_fill(const rf_fill_weights* weights, int32_t n_layers,
                   void* d_ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * rf_fill without a workspace argument, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Computes exactly what rf_fill computes (the same kernels, bit-identical caches) with its
+ * workspace in a static device buffer of RF_FILL_STATIC_SCRATCH_MB MiB that the library holds
+ * on every GPU it runs on until the process ends; the call itself allocates nothing.  A call
+ * whose one-layer workspace (rf_fill_workspace_bytes(weights, t1 - t0)) exceeds the buffer is
+ * refused with RF_ERR_UNSUPPORTED and nothing enqueued: fill such a range in several calls.
+ * The buffer is shared by every call on one GPU and keeps the last call's contents (nothing
+ * in it needs to start at zero); calls that overlap on one GPU (different streams, different
+ * threads without ordering) race on it.  Other arguments as for rf_fill.
+ * ------------------------------------------------------------------------------------- */
+#define RF_FILL_STATIC_SCRATCH_MB 96
+size_t rf_fill_static_scratch_bytes(void);
+rf_status rf_fill_static(const rf_fill_weights* weights, int32_t n_layers,
+                         const void* d_X, int64_t ldx,
+                         int64_t t0, int64_t t1, int64_t pos0,
+                         const rf_cache_desc* cache, void* const* k_cache, void* const* v_cache,
+                         const int32_t* d_block_table, int64_t n_table_blocks,
+                         const float* d_rope, int64_t rope_len, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Streamed maps.  RidgeFill project page, Figure 10 and Table 8 ("streamed"): the ridge maps
  * stay in host memory and reach the GPU layer by layer while the fill runs, for far less
  * device memory than resident maps at nearly the same speed.  Computes exactly what rf_fill

@@ -105,6 +105,10 @@ _sig = {
                                C.c_int64, C.c_int64, C.c_int64, C.POINTER(rf_cache_desc), C.POINTER(_P),
                                C.POINTER(_P), _P, C.c_int64, _P, C.c_int64, _P]),
     "rf_relative_depth_sources": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int32)]),
+    "rf_fill_static_scratch_bytes": (C.c_size_t, []),
+    "rf_fill_static": (C.c_int, [C.POINTER(rf_fill_weights), C.c_int32, _P, C.c_int64, C.c_int64, C.c_int64,
+                                 C.c_int64, C.POINTER(rf_cache_desc), C.POINTER(_P), C.POINTER(_P), _P, C.c_int64, _P,
+                                 C.c_int64, _P]),
     "rf_fill_streamed_ring_bytes": (C.c_size_t, [C.POINTER(rf_fill_weights), C.c_int32, C.c_int32]),
     "rf_fill_streamed": (C.c_int, [C.POINTER(rf_fill_weights), C.c_int32, _P, C.c_int64, C.c_int64, C.c_int64,
                                    C.c_int64, C.POINTER(rf_cache_desc), C.POINTER(_P), C.POINTER(_P), _P, C.c_int64, _P,
@@ -305,6 +309,22 @@ def rf_fill(weights: FillWeights, X, t0: int, t1: int, pos0: int, cache: rf_cach
     ws_bytes = ws.numel() * ws.element_size()
     _check(_lib.rf_fill(C.byref(w), n_layers, _ptr(X), X.stride(0), t0, t1, pos0, C.byref(cache), kc, vc,
                         _ptr(block_table), n_tab, _ptr(rope), rope_len, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def rf_fill_static_scratch_bytes() -> int:
+    return int(_lib.rf_fill_static_scratch_bytes())
+
+
+def rf_fill_static(weights: FillWeights, X, t0: int, t1: int, pos0: int, cache: rf_cache_desc, k_cache: Sequence,
+                   v_cache: Sequence, block_table, rope, rope_len: int, stream=None, n_layers: Optional[int] = None):
+    """rf_fill with the library's static scratch buffer instead of a workspace argument."""
+    w, _keep = weights._c()
+    n_layers = len(weights.W_map) if n_layers is None else n_layers
+    kc = _ptr_array(k_cache)
+    vc = _ptr_array(v_cache)
+    n_tab = 0 if block_table is None else block_table.numel()
+    _check(_lib.rf_fill_static(C.byref(w), n_layers, _ptr(X), X.stride(0), t0, t1, pos0, C.byref(cache), kc, vc,
+                               _ptr(block_table), n_tab, _ptr(rope), rope_len, _stream(stream)))
 
 
 @dataclass

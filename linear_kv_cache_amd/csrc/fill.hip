@@ -14,6 +14,7 @@
 // a head's RoPE partners sit in the same lane and register, one block apart.
 #include <math.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -865,7 +866,68 @@ static rf_status launch_fill_streamed(const rf_fill_weights* w, int32_t n_layers
 }
 }  // namespace rf
 
+namespace rf {
+// Workspace of rf_fill_static: a file-scope device array (one per GPU the library runs on, held
+// until the process ends).  Host code uses its device address, taken once per device with
+// hipGetSymbolAddress; the array's name is not a device address on the host.
+constexpr size_t kStaticScratchBytes = (size_t)RF_FILL_STATIC_SCRATCH_MB << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mutex;
+static void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of ``scratch`` (taken on the first call on that device).
+static rf_status static_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(RF_ERR_HIP, std::string("rf_fill_static: hipGetDevice: ") + hipGetErrorString(e));
+    RF_REQUIRE(dev >= 0 && dev < kMaxDevices, RF_ERR_UNSUPPORTED, "rf_fill_static: device index above 63");
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(RF_ERR_HIP, std::string("rf_fill_static: hipGetSymbolAddress: ") + hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return RF_OK;
+}
+}  // namespace rf
+
 extern "C" {
+
+size_t rf_fill_static_scratch_bytes(void) { return rf::kStaticScratchBytes; }
+
+rf_status rf_fill_static(const rf_fill_weights* w, int32_t n_layers, const void* d_X, int64_t ldx, int64_t t0,
+                         int64_t t1, int64_t pos0, const rf_cache_desc* cache, void* const* k_cache,
+                         void* const* v_cache, const int32_t* d_block_table, int64_t n_table_blocks,
+                         const float* d_rope, int64_t rope_len, void* stream) {
+    clear_error();
+    const size_t need = (w && w->d > 0 && w->d % kFT == 0 && t1 >= t0) ? slot_bytes(w, t1 - t0) : 0;
+    RF_REQUIRE(need <= kStaticScratchBytes, RF_ERR_UNSUPPORTED,
+               "rf_fill_static: one layer of " + std::to_string(t1 - t0) + " rows needs " + std::to_string(need) +
+                   " bytes of scratch; the static buffer holds " + std::to_string(kStaticScratchBytes) +
+                   " (fill fewer rows per call)");
+    rf_cache_layout_t L;
+    bool none;
+    // the scratch pointer is validated below; check everything else first, against a stand-in
+    const void* probe = (const void*)(uintptr_t)256;
+    rf_status st = check_fill("rf_fill_static", w, n_layers, d_X, ldx, t0, t1, pos0, cache, k_cache, v_cache,
+                              d_block_table, n_table_blocks, d_rope, rope_len, probe, kStaticScratchBytes, need, L,
+                              none);
+    if (st != RF_OK || none) return st;
+    void* ws = nullptr;
+    st = static_scratch(&ws);
+    if (st != RF_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (w->dtype == RF_BF16)
+        return launch_fill<bf16_t>(w, n_layers, d_X, ldx, t0, t1, pos0, cache, L, k_cache, v_cache, d_block_table,
+                                   n_table_blocks, d_rope, ws, kStaticScratchBytes, s);
+    return launch_fill<float>(w, n_layers, d_X, ldx, t0, t1, pos0, cache, L, k_cache, v_cache, d_block_table,
+                              n_table_blocks, d_rope, ws, kStaticScratchBytes, s);
+}
 
 rf_status rf_fill(const rf_fill_weights* w, int32_t n_layers, const void* d_X, int64_t ldx,
                   int64_t t0, int64_t t1, int64_t pos0, const rf_cache_desc* cache,

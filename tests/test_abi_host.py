@@ -351,3 +351,18 @@ def test_solve_pinv_validation_before_enqueue():
             rf._check(rf._lib.rf_solve_pinv(C.byref(desc), 256, lam, 0, tol, sweeps, (C.c_int32 * 1)(*targets), 1,
                                             None, None, None, 256, 16, None))
         assert e.value.status == status, (lam, tol, sweeps, targets)
+
+
+def test_fill_static_refuses_oversized_requests_before_any_device_call():
+    # one layer of 20000 rows at d = 4096 needs 164 MB of workspace, more than the static buffer
+    assert rf.rf_fill_static_scratch_bytes() == 96 << 20
+    w = _weights(d=4096, H=8, dh=128, dtype=torch.bfloat16)
+    cd = rf.cache_desc(8, 128, 20000, rf.RF_LAYOUT_CONTIGUOUS, torch.bfloat16)
+    X = torch.empty(20000, 4096, dtype=torch.bfloat16)
+    with pytest.raises(rf.RidgeFillError) as e:
+        rf.rf_fill_static(w, X, 0, 20000, 0, cd, [256], [256], None, 256, 20000, stream=0)
+    assert e.value.status == rf.RF_ERR_UNSUPPORTED and "static buffer" in e.value.message
+    # a request that fits is still validated first (here: no RoPE table)
+    with pytest.raises(rf.RidgeFillError) as e:
+        rf.rf_fill_static(w, X[:64], 0, 64, 0, cd, [256], [256], None, None, 64, stream=0)
+    assert e.value.status == rf.RF_ERR_INVALID_ARG
