@@ -3,8 +3,12 @@
 
 One step is one pass of the whole path over one batch of synthetic input, resident in HBM:
   fit : zero the statistics, accumulate every calibration chunk (rf_gram_accumulate), solve
-        the ridge maps of every filled layer (rf_solve, bf16 maps out);
-  fill: fill every prompt token of every filled layer with those maps (rf_fill).
+        the ridge maps of every filled layer (rf_solve, bf16 maps out), and fold them into the
+        layers' K/V projections (rf_fill_compose);
+  fill: fill every prompt token of every filled layer with those maps (rf_fill_composed: the
+        same caches as rf_fill, from the composed maps).
+After the timed steps the direct fill (rf_fill: map product, then the K/V product) is timed
+alternated with the composed one and reported under ``fill_direct``.
 Default workload: the Llama-8B-shaped configuration (d=4096, 32 layers split at 16, GQA
 8 x 128, RoPE base 5e5, calibration N=65536 in 32768-row chunks, lambda=0.1, T=16384).
 
@@ -40,6 +44,34 @@ METRIC = "filled tokens/sec (all filled layers) + % bf16 MFMA peak; ridge-fit ro
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def composed_flop_per_token_layer(d: int, kvw: int) -> int:
+    """FLOP the composed fill executes per token and layer: the triangular quadratic form (each
+    256-feature tile reads the columns from its own first feature on) and the K/V product."""
+    return 2 * 256 * sum(d - 256 * i for i in range(d // 256)) + 2 * d * 2 * kvw
+
+
+def alternate(stream, fns, steps):
+    """Median milliseconds of each callable, called in turn ``steps`` times (same clock and
+    power state for all)."""
+    import torch
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    for fn in fns:
+        timed(fn)
+    ms = [[] for _ in fns]
+    for _ in range(steps):
+        for i, fn in enumerate(fns):
+            ms[i].append(timed(fn))
+    return [statistics.median(m) for m in ms]
 
 
 def cpu_translate_baseline(n_tokens: int):
@@ -198,7 +230,7 @@ def fill_only(cfg, steps: int, warmup: int):
     import torch
 
     import synth
-    from linear_kv_cache_amd.runner import Filler, alloc_cache, fill_weights
+    from linear_kv_cache_amd.runner import ComposedFiller, Filler, alloc_cache, fill_weights
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -216,35 +248,38 @@ def fill_only(cfg, steps: int, warmup: int):
     cache = alloc_cache(len(layers), cfg.n_kv_heads, cfg.head_dim, T, cfg.torch_dtype, dev, paged=cfg.paged,
                         block_size=cfg.block_size, block_table=table,
                         n_blocks=(int(table.max()) + 1) if table is not None else None)
-    filler = Filler(fw, cfg.rope_base, T, cfg.fill_chunk, dev, ws_slots=8)
+    direct = Filler(fw, cfg.rope_base, T, cfg.fill_chunk, dev, ws_slots=8)
+    composed = ComposedFiller(fw, cfg.rope_base, T, cfg.fill_chunk, dev)
 
-    def run():
-        for c0 in range(cfg.fill_t0, cfg.fill_t1, cfg.fill_chunk):
-            c1 = min(cfg.fill_t1, c0 + cfg.fill_chunk)
-            filler.fill(X[c0 - cfg.fill_t0:c1 - cfg.fill_t0], c0, c1, 0, cache, stream)
+    def runner(filler):
+        def run():
+            for c0 in range(cfg.fill_t0, cfg.fill_t1, cfg.fill_chunk):
+                c1 = min(cfg.fill_t1, c0 + cfg.fill_chunk)
+                filler.fill(X[c0 - cfg.fill_t0:c1 - cfg.fill_t0], c0, c1, 0, cache, stream)
+        return run
 
     for _ in range(warmup):
-        run()
+        runner(composed)()
+        runner(direct)()
     torch.cuda.synchronize()
-    ms = []
-    for _ in range(steps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        run()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms.append(e0.elapsed_time(e1))
-    med = statistics.median(ms)
-    tflops = cfg.fill_tokens * len(layers) * cfg.fill_flop_per_token_layer() / (med / 1e3) / 1e12
+    med, med_direct = alternate(stream, [runner(composed), runner(direct)], steps)
+    alg = cfg.fill_tokens * len(layers) * cfg.fill_flop_per_token_layer()
+    exe = cfg.fill_tokens * len(layers) * composed_flop_per_token_layer(cfg.d, cfg.kv_width)
     print(json.dumps({"metric": "filled tokens/sec (all filled layers) + % bf16 MFMA peak, fill only",
                       "config": {"workload": cfg.name, "d": cfg.d, "filled_layers": len(layers),
                                  "fill_tokens": cfg.fill_tokens, "fill_chunk": cfg.fill_chunk, "paged": cfg.paged},
-                      "steps": steps, "warmup": warmup, "ms_median": round(med, 3),
-                      "tokens_per_s": round(cfg.fill_tokens / (med / 1e3), 1), "tflops": round(tflops, 1),
-                      "frac_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+                      "steps": steps, "warmup": warmup, "path": "composed (rf_fill_composed)",
+                      "ms_median": round(med, 3), "tokens_per_s": round(cfg.fill_tokens / (med / 1e3), 1),
+                      "frac_bf16_peak": round(alg / (med / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                       "flop_per_token_layer": cfg.fill_flop_per_token_layer(),
+                      "executed_flop_per_token_layer": composed_flop_per_token_layer(cfg.d, cfg.kv_width),
+                      "executed_frac_bf16_peak": round(exe / (med / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                       "cache_write_GBps": round(cfg.fill_tokens * len(layers) * 4 * cfg.kv_width / (med / 1e3) / 1e9,
-                                                1)}), flush=True)
+                                                1),
+                      "direct": {"ms_median": round(med_direct, 3),
+                                 "tokens_per_s": round(cfg.fill_tokens / (med_direct / 1e3), 1),
+                                 "frac_bf16_peak": round(alg / (med_direct / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)}}),
+          flush=True)
 
 
 def fit_only(cfg, steps: int, warmup: int):
@@ -345,7 +380,8 @@ def main():
 
     import linear_kv_cache_amd as rf
     import synth
-    from linear_kv_cache_amd.runner import Filler, GramState, alloc_cache, device_bytes, pack_weights
+    from linear_kv_cache_amd.runner import (ComposedFiller, Filler, GramState, alloc_cache, compose_weights,
+                                            device_bytes, pack_weights)
 
     cfg = synth.CONFIGS[args.config]
     if args.fill_only:
@@ -379,6 +415,10 @@ def main():
                         [pack_weights(k, cfg.head_dim) for (k, _, _) in kv],
                         [pack_weights(v, cfg.head_dim) for (_, v, _) in kv])
     filler = Filler(fw, cfg.rope_base, T, T, dev, ws_slots=8)   # 8 layers per fill launch (1 GiB of H)
+    # the composed weights' buffers; rf_fill_compose rewrites them from each step's maps
+    cw = compose_weights(fw, slots=L)
+    compose_ws = device_bytes(rf.rf_fill_compose_workspace_bytes(fw) * L, dev)
+    cfiller = ComposedFiller(fw, cfg.rope_base, T, T, dev, composed=cw)
     lam = cfg.lambdas[0]
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -391,7 +431,7 @@ def main():
     torch.cuda.synchronize()
 
     def step():
-        ev = {k: torch.cuda.Event(enable_timing=True) for k in ("start", "gram", "solve", "fill")}
+        ev = {k: torch.cuda.Event(enable_timing=True) for k in ("start", "gram", "solve", "compose", "fill")}
         gram_ev = []
         ev["start"].record(stream)
         rf.rf_gram_init(state.desc, state.buf, stream)
@@ -405,7 +445,9 @@ def main():
         rf.rf_solve(state.desc, state.buf, lam, rf.RF_LAMBDA_ABSOLUTE, list(range(L)), None, W_lp, b, info,
                     solve_ws, stream)
         ev["solve"].record(stream)
-        filler.fill(Xp, 0, T, 0, cache, stream)
+        rf.rf_fill_compose(fw, cw, compose_ws, stream)
+        ev["compose"].record(stream)
+        cfiller.fill(Xp, 0, T, 0, cache, stream)
         ev["fill"].record(stream)
         return ev, gram_ev
 
@@ -425,13 +467,16 @@ def main():
 
     gram_ms = [r[0]["start"].elapsed_time(r[0]["gram"]) for r in recs]
     solve_ms = [r[0]["gram"].elapsed_time(r[0]["solve"]) for r in recs]
-    fill_ms = [r[0]["solve"].elapsed_time(r[0]["fill"]) for r in recs]
+    compose_ms = [r[0]["solve"].elapsed_time(r[0]["compose"]) for r in recs]
+    fill_ms = [r[0]["compose"].elapsed_time(r[0]["fill"]) for r in recs]
     launch_ms = [e0.elapsed_time(e1) for r in recs for (e0, e1) in r[1]]
     fill_flop = T * L * cfg.fill_flop_per_token_layer()
     gram_flop_per_launch = cfg.calib_chunk * cfg.fit_flop_per_row()
     fill_s = sum(fill_ms) / 1e3
     tok_s = T * args.steps / fill_s
     fill_tflops = fill_flop * args.steps / fill_s / 1e12
+    exe_flop_tl = composed_flop_per_token_layer(d, cfg.kv_width)
+    exe_tflops = T * L * exe_flop_tl * args.steps / fill_s / 1e12
     gram_launch_ms = statistics.mean(launch_ms)
     gram_tflops = gram_flop_per_launch / (gram_launch_ms / 1e3) / 1e12
 
@@ -451,14 +496,18 @@ def main():
         "config": {"workload": cfg.name, "d": d, "filled_layers": L, "n_kv_heads": cfg.n_kv_heads,
                    "head_dim": cfg.head_dim, "fill_tokens": T, "calib_rows": cfg.calib_rows,
                    "calib_chunk": cfg.calib_chunk, "lambda": lam},
-        "fill": {"ms": round(statistics.mean(fill_ms), 3), "ms_median": round(statistics.median(fill_ms), 3),
+        "fill": {"path": "composed maps (rf_fill_composed); algorithmic FLOP as the method's two products",
+                 "ms": round(statistics.mean(fill_ms), 3), "ms_median": round(statistics.median(fill_ms), 3),
                  "tokens_per_s": round(tok_s, 1),
                  "tflops": round(fill_tflops, 1), "frac_bf16_peak": round(fill_tflops / BF16_PEAK_TFLOPS, 4),
                  "flop_per_token_layer": cfg.fill_flop_per_token_layer(),
+                 "executed_flop_per_token_layer": exe_flop_tl, "executed_tflops": round(exe_tflops, 1),
+                 "executed_frac_bf16_peak": round(exe_tflops / BF16_PEAK_TFLOPS, 4),
                  # bf16 K and V rows written to the caches: 2 * H_kv * d_h * 2 B per token-layer
                  "cache_write_GBps": round(T * L * 4 * cfg.n_kv_heads * cfg.head_dim * args.steps / fill_s / 1e9, 1)},
         "fit": {"rows_per_s": round(cfg.calib_rows / (statistics.mean(gram_ms) / 1e3), 1),
                 "gram_ms": round(statistics.mean(gram_ms), 3), "solve_ms": round(statistics.mean(solve_ms), 3),
+                "compose_ms": round(statistics.mean(compose_ms), 3),
                 "gram_ms_median": round(statistics.median(gram_ms), 3),
                 "solve_ms_median": round(statistics.median(solve_ms), 3),
                 "rows_per_s_incl_solve": round(cfg.calib_rows / ((statistics.mean(gram_ms) +
@@ -540,6 +589,24 @@ def main():
             "ours_ms_median": round(oms, 3),
             "ours_frac_bf16_peak": round(gram_flop_per_launch / (oms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
         del XY, G
+    # the direct fill on the same maps, alternated with the composed one
+    log("direct fill (rf_fill) alternated with the composed fill")
+    cms, dms = alternate(stream, [lambda: cfiller.fill(Xp, 0, T, 0, cache, stream),
+                                  lambda: filler.fill(Xp, 0, T, 0, cache, stream)], args.steps)
+    out["fill_direct"] = {"what": "rf_fill (map product, RMSNorm, K/V product, RoPE, cache write) on the same maps, "
+                                  "alternated with rf_fill_composed",
+                          "ms_median": round(dms, 3), "tokens_per_s": round(T / (dms / 1e3), 1),
+                          "frac_bf16_peak": round(fill_flop / (dms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                          "composed_ms_median": round(cms, 3), "composed_speedup": round(dms / cms, 4)}
+    # the solve's accuracy on this workload: the largest entry of the equilibrated inverse and
+    # the fp64 stationarity residual of the fp32 maps (one extra call, outside the timed steps)
+    _, _, _, info_r, cond_r, resid_r = state.solve_many([lam], rf.RF_LAMBDA_ABSOLUTE, list(range(L)), want_bf16=False,
+                                                        want_resid=True)
+    torch.cuda.synchronize()
+    out["fit"]["equilibrated_inverse_max"] = round(float(cond_r[0].item()), 4)
+    out["fit"]["product_route"] = "fp64" if float(cond_r[0].item()) > rf.RF_SPLIT_COND_MAX else "split bf16"
+    out["fit"]["stationarity_residual_max"] = float(resid_r.max().item())
+    del cond_r, resid_r
     if not args.no_streamed:
         log("streamed maps: the fill with its maps in page-locked host memory")
         out["fill_streamed"] = streamed_leg(args.steps, stream, dev, cfg, fw, Xp, cache, filler)

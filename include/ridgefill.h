@@ -360,6 +360,71 @@ rf_status rf_fill(const rf_fill_weights* weights, int32_t n_layers,
                   void* d_ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * The composed fill: the same caches as rf_fill, from the maps folded into the layers' own
+ * projections once per map.  RidgeFill project page, "Method" steps 2-4: only the K/V rows
+ * of a filled layer are written, and the predicted input h = x W^T + b enters them only
+ * through its RMS and its projections, so for a map W, b and a layer's gamma, W_k, W_v
+ *     k = (x M_k^T + c_k) r,   v = (x M_v^T + c_v) r,   r = 1/sqrt(mean_o h_o^2 + rms_eps)
+ * with M_k = W_k diag(gamma) W, c_k = W_k diag(gamma) b (likewise for v), and
+ *     sum_o h_o^2 = sum_i x_i ((T x^T)_i + g_i x_i) + x q_lin^T + q_const,
+ *     T = the strict upper triangle of 2 W^T W, g = the diagonal of W^T W (kept in fp32),
+ *     q_lin = 2 W^T b, q_const = |b|^2,
+ * then the per-head key norm (if given) and RoPE on k as in rf_fill.  Per token and layer the
+ * products take 2 d (d/2 + 2 H_kv d_h) + O(d) FLOP instead of rf_fill's 2 d (d + 2 H_kv d_h):
+ * the map's own product becomes a triangular quadratic form, and the projections read the
+ * prompt states directly.
+ *
+ * rf_fill_compose forms the composed weights of n_layers layers from rf_fill's (BF16, packed)
+ * weights.  Per layer l (device buffers, caller-owned, 16-B aligned):
+ *   T[l]   : [d][d] bf16 out, packed as a map (rope_head_dim 0); only the blocks on and above
+ *            the 256 x 256 block diagonal are written or read
+ *   q[l]   : [2d + 1] fp32 out: q_lin, then g, then q_const
+ *   M_k[l], M_v[l] : [n_kv_heads*head_dim][d] bf16 out, packed as rf_pack_weights with
+ *            rope_head_dim = head_dim packs W_k, W_v
+ *   c_k[l], c_v[l] : [n_kv_heads*head_dim] fp32 out
+ * Products of bf16 weights accumulate in fp32 (W_k diag(gamma) enters in two bf16 parts, so
+ * its product with W is exact to fp32 before the one rounding of M to bf16); the vectors are
+ * summed in fp64.  d_ws: a multiple k >= 1 of rf_fill_compose_workspace_bytes(weights) bytes
+ * (one layer slot: 4 d^2 + 8 H_kv d_h d bytes), 256-B aligned; the products of up to
+ * min(k, 32) layers share one launch.
+ * Supported: BF16 weights, d % 256 == 0, as for rf_fill.
+ * ------------------------------------------------------------------------------------- */
+typedef struct {
+    int32_t d;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    float rms_eps;
+    const void* const* T;
+    const float* const* q;
+    const void* const* M_k;
+    const void* const* M_v;
+    const float* const* c_k;
+    const float* const* c_v;
+    const float* const* k_norm;   /* NULL, or per layer fp32 [head_dim] (as for rf_fill)        */
+    float k_norm_eps;
+} rf_fill_composed_weights;
+
+size_t rf_fill_compose_workspace_bytes(const rf_fill_weights* weights);
+rf_status rf_fill_compose(const rf_fill_weights* weights, int32_t n_layers,
+                          void* const* T, float* const* q, void* const* M_k, void* const* M_v,
+                          float* const* c_k, float* const* c_v,
+                          void* d_ws, size_t ws_bytes, void* stream);
+
+/* The fill from composed weights; arguments as for rf_fill (X, cache, block table, RoPE table,
+ * rows outside [t0, t1) and layers not listed never written).  BF16 only.
+ * d_ws: rf_fill_composed_workspace_bytes(weights, t1 - t0) bytes, 256-B aligned (per-token
+ * partial sums of squares: d/256 fp32 per token and layer slot; more slots, more layers per
+ * launch, up to 32). */
+size_t rf_fill_composed_workspace_bytes(const rf_fill_composed_weights* weights, int64_t max_rows);
+rf_status rf_fill_composed(const rf_fill_composed_weights* weights, int32_t n_layers,
+                           const void* d_X, int64_t ldx,
+                           int64_t t0, int64_t t1, int64_t pos0,
+                           const rf_cache_desc* cache, void* const* k_cache, void* const* v_cache,
+                           const int32_t* d_block_table, int64_t n_table_blocks,
+                           const float* d_rope, int64_t rope_len,
+                           void* d_ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * rf_fill without a workspace argument, for callers that cannot allocate device memory:
  * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Computes exactly what rf_fill computes (the same kernels, bit-identical caches) with its

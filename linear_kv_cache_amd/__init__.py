@@ -69,6 +69,13 @@ class rf_fill_weights(C.Structure):
                 ("k_norm", C.POINTER(C.c_void_p)), ("k_norm_eps", C.c_float)]
 
 
+class rf_fill_composed_weights(C.Structure):
+    _fields_ = [("d", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("rms_eps", C.c_float),
+                ("T", C.POINTER(C.c_void_p)), ("q", C.POINTER(C.c_void_p)), ("M_k", C.POINTER(C.c_void_p)),
+                ("M_v", C.POINTER(C.c_void_p)), ("c_k", C.POINTER(C.c_void_p)), ("c_v", C.POINTER(C.c_void_p)),
+                ("k_norm", C.POINTER(C.c_void_p)), ("k_norm_eps", C.c_float)]
+
+
 class rf_translate_weights(C.Structure):
     _fields_ = [("d_in", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("dtype", C.c_int),
                 ("T_k", C.POINTER(C.c_void_p)), ("T_v", C.POINTER(C.c_void_p)), ("b_k", C.POINTER(C.c_void_p)),
@@ -105,6 +112,13 @@ _sig = {
                                C.c_int64, C.c_int64, C.c_int64, C.POINTER(rf_cache_desc), C.POINTER(_P),
                                C.POINTER(_P), _P, C.c_int64, _P, C.c_int64, _P]),
     "rf_relative_depth_sources": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.POINTER(C.c_int32)]),
+    "rf_fill_compose_workspace_bytes": (C.c_size_t, [C.POINTER(rf_fill_weights)]),
+    "rf_fill_compose": (C.c_int, [C.POINTER(rf_fill_weights), C.c_int32, C.POINTER(_P), C.POINTER(_P), C.POINTER(_P),
+                                  C.POINTER(_P), C.POINTER(_P), C.POINTER(_P), _P, C.c_size_t, _P]),
+    "rf_fill_composed_workspace_bytes": (C.c_size_t, [C.POINTER(rf_fill_composed_weights), C.c_int64]),
+    "rf_fill_composed": (C.c_int, [C.POINTER(rf_fill_composed_weights), C.c_int32, _P, C.c_int64, C.c_int64,
+                                   C.c_int64, C.c_int64, C.POINTER(rf_cache_desc), C.POINTER(_P), C.POINTER(_P), _P,
+                                   C.c_int64, _P, C.c_int64, _P, C.c_size_t, _P]),
     "rf_fill_static_scratch_bytes": (C.c_size_t, []),
     "rf_fill_static": (C.c_int, [C.POINTER(rf_fill_weights), C.c_int32, _P, C.c_int64, C.c_int64, C.c_int64,
                                  C.c_int64, C.POINTER(rf_cache_desc), C.POINTER(_P), C.POINTER(_P), _P, C.c_int64, _P,
@@ -309,6 +323,66 @@ def rf_fill(weights: FillWeights, X, t0: int, t1: int, pos0: int, cache: rf_cach
     ws_bytes = ws.numel() * ws.element_size()
     _check(_lib.rf_fill(C.byref(w), n_layers, _ptr(X), X.stride(0), t0, t1, pos0, C.byref(cache), kc, vc,
                         _ptr(block_table), n_tab, _ptr(rope), rope_len, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+@dataclass
+class ComposedFillWeights:
+    """Per-layer composed weights of one rf_fill_composed call (tensors on the device), as
+    rf_fill_compose writes them: T [d, d] and M_k, M_v [H*d_h, d] packed bf16; q [2d + 1], c_k,
+    c_v [H*d_h] fp32."""
+
+    d: int
+    n_kv_heads: int
+    head_dim: int
+    rms_eps: float
+    T: list
+    q: list
+    M_k: list
+    M_v: list
+    c_k: list
+    c_v: list
+    k_norm: Optional[list] = None
+    k_norm_eps: float = 1e-6
+
+    def _c(self):
+        arrs = [_ptr_array(x) for x in (self.T, self.q, self.M_k, self.M_v, self.c_k, self.c_v)]
+        kn = None if self.k_norm is None else _ptr_array(self.k_norm)
+        w = rf_fill_composed_weights(self.d, self.n_kv_heads, self.head_dim, self.rms_eps,
+                                     *[C.cast(a, C.POINTER(_P)) for a in arrs],
+                                     C.cast(kn, C.POINTER(_P)) if kn is not None else C.POINTER(_P)(), self.k_norm_eps)
+        return w, (arrs, kn)
+
+
+def rf_fill_compose_workspace_bytes(weights: FillWeights) -> int:
+    w, _keep = weights._c()
+    return int(_lib.rf_fill_compose_workspace_bytes(C.byref(w)))
+
+
+def rf_fill_compose(weights: FillWeights, out: ComposedFillWeights, ws, stream=None, n_layers: Optional[int] = None):
+    """Composed weights of the listed layers into the buffers of ``out``."""
+    w, _keep = weights._c()
+    n_layers = len(weights.W_map) if n_layers is None else n_layers
+    arrs = [_ptr_array(x) for x in (out.T, out.q, out.M_k, out.M_v, out.c_k, out.c_v)]
+    ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.rf_fill_compose(C.byref(w), n_layers, *arrs, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def rf_fill_composed_workspace_bytes(weights: ComposedFillWeights, max_rows: int) -> int:
+    w, _keep = weights._c()
+    return int(_lib.rf_fill_composed_workspace_bytes(C.byref(w), max_rows))
+
+
+def rf_fill_composed(weights: ComposedFillWeights, X, t0: int, t1: int, pos0: int, cache: rf_cache_desc,
+                     k_cache: Sequence, v_cache: Sequence, block_table, rope, rope_len: int, ws, stream=None,
+                     n_layers: Optional[int] = None):
+    w, _keep = weights._c()
+    n_layers = len(weights.T) if n_layers is None else n_layers
+    kc = _ptr_array(k_cache)
+    vc = _ptr_array(v_cache)
+    n_tab = 0 if block_table is None else block_table.numel()
+    ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.rf_fill_composed(C.byref(w), n_layers, _ptr(X), X.stride(0), t0, t1, pos0, C.byref(cache), kc, vc,
+                                 _ptr(block_table), n_tab, _ptr(rope), rope_len, _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def rf_fill_static_scratch_bytes() -> int:

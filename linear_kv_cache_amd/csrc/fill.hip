@@ -68,6 +68,7 @@ struct KVArgs {
     const float* bk[kMaxGroup];   // per-feature intercepts (translators only)
     const float* bv[kMaxGroup];
     const float* kn[kMaxGroup];   // per-head key norm weights [head_dim] (KN only)
+    const float* qb[kMaxGroup];   // NORM: the constant added to each token's sum of squares, or null
     float kn_eps;
     const void* Wk[kMaxGroup];
     const void* Wv[kMaxGroup];
@@ -268,6 +269,7 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
         } else {
             for (int p = 0; p < a.n_ps; ++p) s += ps[n * a.n_ps + p];
         }
+        if (a.qb[g]) s += *a.qb[g];   // composed maps: the constant term of the sum of squares
         return 1.0f / sqrtf(s * inv_d + a.eps);
     };
     // element offset of token t's row in the pool, or -1 if it has no slot
@@ -325,8 +327,8 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
                         const f32x4 blo = bias4(fl), bhi = bias4(fl + HALF);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            const float x = gm.acc[0][j][4 * q + e] * r + blo[e];
-                            const float y = gm.acc[1][j][4 * q + e] * r + bhi[e];
+                            const float x = (gm.acc[0][j][4 * q + e] + blo[e]) * r;
+                            const float y = (gm.acc[1][j][4 * q + e] + bhi[e]) * r;
                             ss += x * x + y * y;
                         }
                     }
@@ -350,8 +352,8 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
                     float lo[4], hi[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        lo[e] = gm.acc[0][j][4 * q + e] * r + blo[e];
-                        hi[e] = gm.acc[1][j][4 * q + e] * r + bhi[e];
+                        lo[e] = (gm.acc[0][j][4 * q + e] + blo[e]) * r;
+                        hi[e] = (gm.acc[1][j][4 * q + e] + bhi[e]) * r;
                     }
                     stage(nl, fl, lo);
                     stage(nl, fl + HALF, hi);
@@ -394,8 +396,8 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
                     float lo[4], hi[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        float x = gm.acc[0][j][4 * q + e] * r + blo[e];
-                        float y = gm.acc[1][j][4 * q + e] * r + bhi[e];
+                        float x = (gm.acc[0][j][4 * q + e] + blo[e]) * r;
+                        float y = (gm.acc[1][j][4 * q + e] + bhi[e]) * r;
                         if constexpr (KN) {
                             x *= kinv * glo[e];
                             y *= kinv * ghi[e];
@@ -504,6 +506,117 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
     }
 }
 
+
+// ---- the composed fill: the maps folded into the layers' projections -----------------------
+// With W' = W_k,v diag(gamma) W (composed once per map, rf_fill_compose), a token's keys and
+// values are (x W'^T + c) r, where c = W_k,v diag(gamma) b and r = 1/rms(h) needs only the sum
+// of squares of h = x W^T + b:
+//     sum_o h_o^2 = x G x^T + x (2 W^T b) + |b|^2,   G = W^T W,
+// a quadratic form read with the strictly upper-triangular T (T_ij = 2 G_ij for j > i) and
+// G's diagonal kept in fp32: x G x^T = sum_i x_i ((T x)_i + G_ii x_i).  k_fill_norm forms
+// (T x)_i over 256-feature tiles, reading only columns j >= the tile's first feature (T is zero
+// to their left), and leaves the tile's partial  sum_i x_i ((T x)_i + G_ii x_i + 2 (W^T b)_i)
+// per token; the K/V launch reads X itself.
+struct NormArgs {
+    const void* X;
+    int64_t ldx;
+    int64_t rows;
+    int32_t d;
+    int32_t n_ps;            // partial sums per token = d / kFT
+    int32_t tok_tiles;
+    int32_t n_layers;
+    float* psum;             // [rows][n_ps] per layer slot
+    int64_t ps_slot;
+    const void* T[kMaxGroup];   // packed [d][d] (upper block triangle read)
+    const float* q[kMaxGroup];  // [2d + 1]: 2 W^T b, diag(W^T W), then |b|^2
+};
+
+__global__ __launch_bounds__(PackedAGemm::kThr) void k_fill_norm(NormArgs a) {
+    using G = PackedAGemm;
+    // epilogue: the tile's x values [token][feature] (bf16, 16-byte chunk c of token n in slot
+    // c ^ (n & 31)), then the [wave][token] fp32 partials
+    constexpr int kX = kTT * kFT * 2, kRed = 4 * kTT * 4;
+    constexpr int kEpi = kX + kRed;
+    __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES > kEpi ? G::LDS_BYTES : kEpi];
+    const int n_feat = a.d / kFT;
+    // the K range shrinks with the feature tile: every XCD takes a block of (layer, token tile)
+    // columns with all their feature tiles, longest first, 4 feature x 8 token tiles at a time
+    int mt, col;
+    balanced_tile(xcd_order((int)blockIdx.x, (int)gridDim.x), n_feat, a.n_layers * a.tok_tiles, mt, col);
+    const int g = col / a.tok_tiles, tt = col - g * a.tok_tiles;
+    const int64_t n0 = (int64_t)tt * kTT;
+    const int kb = mt * (kFT / G::BK);   // first k-step: column 256 mt
+    const bf16_t* X = (const bf16_t*)a.X;
+    G gm;
+    gm.run(lds, PipeOperand{(const bf16_t*)a.T[g] + (int64_t)mt * kFT * a.d + (int64_t)kb * (G::kStepBytes / 2), a.d, kFT},
+           PipeOperand{X + n0 * a.ldx + (int64_t)mt * kFT, a.ldx, a.rows - n0}, a.d / G::BK - kb);
+
+    // the main loop ended on a barrier: LDS is free.  The tile's x values come back as whole
+    // 512-byte row segments (a half-wave per token; rows past the end read as zero) and are
+    // read per lane from LDS in the accumulators' layout
+    const int lane = threadIdx.x & 63, wm = threadIdx.x >> 6;
+    {
+        const int c = threadIdx.x & 31;
+#pragma unroll 2
+        for (int p = 0; p < kTT / 8; ++p) {
+            const int nl = p * 8 + (threadIdx.x >> 5);
+            const int64_t n = n0 + nl;
+            const u32x4 v = n < a.rows ? *(const u32x4*)(X + n * a.ldx + mt * kFT + c * 8) : u32x4{0u, 0u, 0u, 0u};
+            *(u32x4*)(lds + nl * (kFT * 2) + ((c ^ (nl & 31)) << 4)) = v;
+        }
+    }
+    __syncthreads();
+    float* red = (float*)(lds + kX);
+    const float* qv = a.q[g];
+    f32x4 gq[G::SM][4], gd[G::SM][4];
+#pragma unroll
+    for (int i = 0; i < G::SM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            gq[i][q] = *(const f32x4*)(qv + mt * kFT + G::row_of(i, 4 * q));
+            gd[i][q] = *(const f32x4*)(qv + a.d + mt * kFT + G::row_of(i, 4 * q));
+        }
+#pragma unroll
+    for (int j = 0; j < G::SN; ++j) {
+        const int nl = G::col_of(j);
+        const int64_t n = n0 + nl;
+        // this lane's 32 features of the token's own row
+        u32x2 xv[G::SM][4];
+#pragma unroll
+        for (int i = 0; i < G::SM; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int ml = G::row_of(i, 4 * q);
+                xv[i][q] = *(const u32x2*)(lds + nl * (kFT * 2) + (((ml >> 3) ^ (nl & 31)) << 4) + (ml & 4) * 2);
+            }
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < G::SM; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float x0 = __builtin_bit_cast(float, xv[i][q][0] << 16);
+                const float x1 = __builtin_bit_cast(float, xv[i][q][0] & 0xffff0000u);
+                const float x2 = __builtin_bit_cast(float, xv[i][q][1] << 16);
+                const float x3 = __builtin_bit_cast(float, xv[i][q][1] & 0xffff0000u);
+                ss += x0 * (gm.acc[i][j][4 * q] + gq[i][q][0] + gd[i][q][0] * x0);
+                ss += x1 * (gm.acc[i][j][4 * q + 1] + gq[i][q][1] + gd[i][q][1] * x1);
+                ss += x2 * (gm.acc[i][j][4 * q + 2] + gq[i][q][2] + gd[i][q][2] * x2);
+                ss += x3 * (gm.acc[i][j][4 * q + 3] + gq[i][q][3] + gd[i][q][3] * x3);
+            }
+        if (n >= a.rows) ss = 0.f;
+        ss += __shfl_xor(ss, 32);
+        if (lane < 32) red[wm * kTT + nl] = ss;
+        __builtin_amdgcn_sched_barrier(0);   // one token column at a time (register pressure)
+    }
+    __syncthreads();
+    const int nl = threadIdx.x;
+    const int64_t n = n0 + nl;
+    if (nl < kTT && n < a.rows) {
+        const float ps = ((red[nl] + red[kTT + nl]) + red[2 * kTT + nl]) + red[3 * kTT + nl];
+        a.psum[g * a.ps_slot + n * a.n_ps + mt] = ps;
+    }
+}
+
 __global__ void k_rope_table(double base, int32_t dh, int64_t n_pos, float* out) {
     const int64_t half = dh / 2;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -516,15 +629,6 @@ __global__ void k_rope_table(double base, int32_t dh, int64_t n_pos, float* out)
     out[2 * idx + 1] = (float)sin(phi);
 }
 
-// Source row, within its 256-row tile, of packed row p.  hd == 0 keeps the order; otherwise
-// wave w's block i takes rows of pairs (f, f + hd/2) of the tile's heads: pair q = 32 w + r % 32,
-// first partner in block 0, second in block 1, so a RoPE pair meets in one lane's registers.
-__device__ inline int packed_source_row(int p, int hd) {
-    if (hd == 0) return p;
-    const int half = hd >> 1;
-    const int q = ((p >> 6) << 5) + (p & 31);
-    return (q / half) * hd + q % half + ((p >> 5) & 1) * half;
-}
 
 // 8 consecutive k of one source row as 8 bf16 (fp32 sources rounded to nearest even).
 __device__ inline u32x4 load8_bf16(const bf16_t* p) { return *(const u32x4*)p; }
@@ -612,6 +716,69 @@ static rf_status launch_fill(const rf_fill_weights* w, int32_t n_layers, const v
                 hipLaunchKernelGGL((k_fill_kv<T, 64, true, false>), kv_grid, blk, 0, stream, ka);
         }
         st = check_launch("rf_fill: kv kernel");
+        if (st != RF_OK) return st;
+    }
+    return RF_OK;
+}
+
+
+static size_t composed_slot_bytes(const rf_fill_composed_weights* w, int64_t rows) {
+    return round_up((size_t)rows * (w->d / kFT) * sizeof(float), 256);
+}
+
+// Per group of layers: the quadratic-form launch, then the K/V launch reading the prompt
+// states directly (the composed maps make the predicted inputs unnecessary).
+static rf_status launch_fill_composed(const rf_fill_composed_weights* w, int32_t n_layers, const void* X, int64_t ldx,
+                                      int64_t t0, int64_t t1, int64_t pos0, const rf_cache_desc* cache,
+                                      const rf_cache_layout_t& L, void* const* kc, void* const* vc,
+                                      const int32_t* table, int64_t n_table, const float* rope, void* ws,
+                                      size_t ws_bytes, hipStream_t stream) {
+    const int64_t rows = t1 - t0;
+    const size_t slot = composed_slot_bytes(w, rows);
+    const int group = (int)std::min<size_t>({(size_t)n_layers, (size_t)kMaxGroup, ws_bytes / slot});
+    const int64_t ps_slot = (int64_t)(slot / sizeof(float));
+    const int tok_tiles = (int)ceil_div(rows, kTT);
+    const int kvw = w->n_kv_heads * w->head_dim;
+    for (int l0 = 0; l0 < n_layers; l0 += group) {
+        const int gsz = std::min(group, n_layers - l0);
+        NormArgs na{};
+        na.X = X; na.ldx = ldx; na.rows = rows; na.d = w->d; na.n_ps = w->d / kFT; na.tok_tiles = tok_tiles;
+        na.n_layers = gsz; na.psum = (float*)ws; na.ps_slot = ps_slot;
+        KVArgs ka{};
+        ka.psum = (const float*)ws; ka.ps_slot = ps_slot; ka.ld_in = ldx;
+        ka.n_ps = w->d / kFT; ka.d = w->d; ka.kvw = kvw; ka.eps = w->rms_eps;
+        ka.rows = rows; ka.t0 = t0; ka.pos0 = pos0; ka.rope = rope;
+        ka.paged = cache->layout == RF_LAYOUT_PAGED; ka.block_size = cache->block_size;
+        ka.stride_block = L.stride_block; ka.stride_head = L.stride_head; ka.stride_token = L.stride_token;
+        ka.n_blocks = L.n_blocks; ka.block_table = table; ka.n_table_blocks = n_table;
+        ka.kn_eps = w->k_norm_eps;
+        for (int g = 0; g < gsz; ++g) {
+            na.T[g] = w->T[l0 + g]; na.q[g] = w->q[l0 + g];
+            ka.qb[g] = w->q[l0 + g] + 2 * w->d;
+            ka.kn[g] = w->k_norm ? w->k_norm[l0 + g] : nullptr;
+            ka.Wk[g] = w->M_k[l0 + g]; ka.Wv[g] = w->M_v[l0 + g];
+            ka.bk[g] = w->c_k[l0 + g]; ka.bv[g] = w->c_v[l0 + g];
+            ka.in_k[g] = ka.in_v[g] = X;
+            ka.kc[g] = kc[l0 + g]; ka.vc[g] = vc[l0 + g];
+        }
+        ka.tok_tiles = tok_tiles;
+        hipLaunchKernelGGL(k_fill_norm, dim3((w->d / kFT) * tok_tiles * gsz), dim3(PackedAGemm::kThr), 0, stream, na);
+        rf_status st = check_launch("rf_fill_composed: quadratic-form kernel");
+        if (st != RF_OK) return st;
+        const dim3 kv_grid((2 * kvw / kFT) * tok_tiles * gsz);
+        const dim3 blk(PackedAGemm::kThr);
+        if (w->k_norm) {
+            if (w->head_dim == 128)
+                hipLaunchKernelGGL((k_fill_kv<bf16_t, 128, true, true, false, true>), kv_grid, blk, 0, stream, ka);
+            else
+                hipLaunchKernelGGL((k_fill_kv<bf16_t, 64, true, true, false, true>), kv_grid, blk, 0, stream, ka);
+        } else {
+            if (w->head_dim == 128)
+                hipLaunchKernelGGL((k_fill_kv<bf16_t, 128, true, true>), kv_grid, blk, 0, stream, ka);
+            else
+                hipLaunchKernelGGL((k_fill_kv<bf16_t, 64, true, true>), kv_grid, blk, 0, stream, ka);
+        }
+        st = check_launch("rf_fill_composed: kv kernel");
         if (st != RF_OK) return st;
     }
     return RF_OK;
@@ -897,6 +1064,37 @@ static rf_status static_scratch(void** out) {
 }  // namespace rf
 
 extern "C" {
+
+
+size_t rf_fill_composed_workspace_bytes(const rf_fill_composed_weights* w, int64_t max_rows) {
+    if (!w || w->d <= 0 || w->d % kFT != 0 || max_rows < 0) return 0;
+    return composed_slot_bytes(w, max_rows);
+}
+
+rf_status rf_fill_composed(const rf_fill_composed_weights* w, int32_t n_layers, const void* d_X, int64_t ldx,
+                           int64_t t0, int64_t t1, int64_t pos0, const rf_cache_desc* cache, void* const* k_cache,
+                           void* const* v_cache, const int32_t* d_block_table, int64_t n_table_blocks,
+                           const float* d_rope, int64_t rope_len, void* d_ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    RF_REQUIRE(w && cache, RF_ERR_INVALID_ARG, "rf_fill_composed: null weights or cache descriptor");
+    // the shared checks, on the composed weights seen through the fill's descriptor
+    rf_fill_weights fw{};
+    fw.d = w->d; fw.n_kv_heads = w->n_kv_heads; fw.head_dim = w->head_dim; fw.rms_eps = w->rms_eps; fw.dtype = RF_BF16;
+    fw.W_map = w->T; fw.b_map = w->q; fw.gamma = w->c_k; fw.W_k = w->M_k; fw.W_v = w->M_v;
+    fw.k_norm = w->k_norm; fw.k_norm_eps = w->k_norm_eps;
+    rf_cache_layout_t L;
+    bool none;
+    const size_t need = (w->d > 0 && w->d % kFT == 0 && t1 >= t0) ? composed_slot_bytes(w, t1 - t0) : 0;
+    rf_status st = check_fill("rf_fill_composed", &fw, n_layers, d_X, ldx, t0, t1, pos0, cache, k_cache, v_cache,
+                              d_block_table, n_table_blocks, d_rope, rope_len, d_ws, ws_bytes, need, L, none);
+    if (st != RF_OK || none) return st;
+    RF_REQUIRE(w->c_v, RF_ERR_INVALID_ARG, "rf_fill_composed: null value intercepts");
+    for (int l = 0; l < n_layers; ++l)
+        RF_REQUIRE(w->c_v[l] && aligned(w->c_v[l], 16), RF_ERR_INVALID_ARG,
+                   "rf_fill_composed: per-layer intercepts must be non-null and 16-byte aligned");
+    return launch_fill_composed(w, n_layers, d_X, ldx, t0, t1, pos0, cache, L, k_cache, v_cache, d_block_table,
+                                n_table_blocks, d_rope, d_ws, ws_bytes, (hipStream_t)stream);
+}
 
 size_t rf_fill_static_scratch_bytes(void) { return rf::kStaticScratchBytes; }
 

@@ -74,6 +74,26 @@ __device__ inline void grouped_tile(int v, int n_rows, int n_cols, int gf, int& 
     col = w / gs;
 }
 
+// A tile order for launches whose row tiles have unequal K lengths (longer for lower rows):
+// logical index l (after xcd_order, so each XCD receives one contiguous range) walks the n_cols
+// columns in 8 blocks of ceil(n_cols / 8), one per XCD range when n_cols divides by 8; within a
+// block, row tiles in groups of 4 go slowest (longest first), then the block's columns, then
+// the 4 rows of the group.  Every XCD so gets the same mix of long and short tiles, starts on
+// its long ones, and runs 4 row tiles x 8 columns at a time.
+__device__ inline void balanced_tile(int l, int n_rows, int n_cols, int& row, int& col) {
+    const int cb = (n_cols + 7) / 8;
+    const int blk = l / (n_rows * cb);
+    const int r = l - blk * n_rows * cb;
+    const int ck = (n_cols - blk * cb) < cb ? (n_cols - blk * cb) : cb;
+    const int n_grp = (n_rows + 3) / 4;
+    int grp = r / (4 * ck);
+    if (grp > n_grp - 1) grp = n_grp - 1;
+    const int w = r - grp * 4 * ck;
+    const int gs = (n_rows - 4 * grp) < 4 ? (n_rows - 4 * grp) : 4;
+    row = 4 * grp + w % gs;
+    col = blk * cb + w / gs;
+}
+
 template <int WAVES, int NSETS = 2, bool MMAJOR = false>
 struct PipeGemmW {
     static_assert(WAVES == 4 || WAVES == 8, "4 waves (one per SIMD) or 8 (two per SIMD)");
@@ -541,6 +561,16 @@ __host__ __device__ inline int packed_col_part(int k) {
 }
 __host__ __device__ inline int64_t packed_index(int64_t r, int k, int64_t K) {
     return (r >> 8) * 256 * K + packed_row_part((int)(r & 255)) + packed_col_part(k);
+}
+
+// Source row, within its 256-row tile, of packed row p.  hd == 0 keeps the order; otherwise
+// wave w's block i takes rows of pairs (f, f + hd/2) of the tile's heads: pair q = 32 w + r % 32,
+// first partner in block 0, second in block 1, so a RoPE pair meets in one lane's registers.
+__host__ __device__ inline int packed_source_row(int p, int hd) {
+    if (hd == 0) return p;
+    const int half = hd >> 1;
+    const int q = ((p >> 6) << 5) + (p & 31);
+    return (q / half) * hd + q % half + ((p >> 5) & 1) * half;
 }
 
 // One wave per SIMD with two load sets measured best on the fill and Gram products; two waves

@@ -8,8 +8,9 @@ from typing import List, Optional, Sequence
 
 import torch
 
-from . import (RF_LAYOUT_CONTIGUOUS, RF_LAYOUT_PAGED, RF_PRODUCT_AUTO, FillWeights, TranslateWeights, cache_desc, gram_desc,
-               rf_cache_layout, rf_fill, rf_fill_streamed, rf_fill_streamed_ring_bytes, rf_fill_workspace_bytes,
+from . import (RF_LAYOUT_CONTIGUOUS, RF_LAYOUT_PAGED, RF_PRODUCT_AUTO, ComposedFillWeights, FillWeights, TranslateWeights, cache_desc, gram_desc,
+               rf_cache_layout, rf_fill, rf_fill_compose, rf_fill_compose_workspace_bytes, rf_fill_composed,
+               rf_fill_composed_workspace_bytes, rf_fill_streamed, rf_fill_streamed_ring_bytes, rf_fill_workspace_bytes,
                rf_fit_r2, rf_fit_r2_workspace_bytes, rf_gram_select,
                rf_gram_accumulate, rf_gram_init,
                rf_gram_state_bytes, rf_gram_state_layout, rf_pack_weights, rf_rope_table, rf_solve,
@@ -231,6 +232,41 @@ class Filler:
     def fill(self, X, t0: int, t1: int, pos0: int, cache: Cache, stream=None):
         rf_fill(self.w, X, t0, t1, pos0, cache.desc, cache.k, cache.v, cache.block_table, self.rope,
                 self.rope_len, self.ws, stream)
+
+
+def compose_weights(weights: FillWeights, stream=None, slots: int = 8) -> ComposedFillWeights:
+    """The composed weights (rf_fill_compose) of every layer of a bf16 FillWeights, in fresh
+    device buffers (``slots`` layers per product launch)."""
+    dev = weights.W_map[0].device
+    L, d, kvw = len(weights.W_map), weights.d, weights.n_kv_heads * weights.head_dim
+    T = [torch.empty(d, d, dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    q = [torch.empty(2 * d + 4, dtype=torch.float32, device=dev) for _ in range(L)]
+    Mk = [torch.empty(kvw, d, dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    Mv = [torch.empty(kvw, d, dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    ck = [torch.empty(kvw, dtype=torch.float32, device=dev) for _ in range(L)]
+    cv = [torch.empty(kvw, dtype=torch.float32, device=dev) for _ in range(L)]
+    out = ComposedFillWeights(d, weights.n_kv_heads, weights.head_dim, weights.rms_eps, T, q, Mk, Mv, ck, cv,
+                              weights.k_norm, weights.k_norm_eps)
+    ws = device_bytes(rf_fill_compose_workspace_bytes(weights) * max(1, min(slots, L)), dev)
+    rf_fill_compose(weights, out, ws, stream)
+    return out
+
+
+class ComposedFiller:
+    """Composed weights (rf_fill_compose), a RoPE table and a workspace; fills token ranges
+    with rf_fill_composed."""
+
+    def __init__(self, weights: FillWeights, rope_base: float, max_pos: int, max_rows: int, device, ws_slots: int = 32,
+                 stream=None, composed: Optional[ComposedFillWeights] = None):
+        self.w = composed if composed is not None else compose_weights(weights, stream)
+        self.rope_len = max_pos
+        self.rope = torch.empty(max_pos, weights.head_dim, dtype=torch.float32, device=device)
+        rf_rope_table(rope_base, weights.head_dim, max_pos, self.rope, stream)
+        self.ws = device_bytes(rf_fill_composed_workspace_bytes(self.w, max_rows) * max(1, ws_slots), device)
+
+    def fill(self, X, t0: int, t1: int, pos0: int, cache: Cache, stream=None):
+        rf_fill_composed(self.w, X, t0, t1, pos0, cache.desc, cache.k, cache.v, cache.block_table, self.rope,
+                         self.rope_len, self.ws, stream)
 
 
 class StreamedFiller(Filler):

@@ -40,6 +40,7 @@ class FillCase:
     gen_device: str = "cpu"                    # where inputs are drawn
     max_tokens: Optional[int] = None
     k_norm: bool = False                       # per-head key norm (gamma_k, eps 1e-6)
+    composed: bool = False                     # rf_fill_compose + rf_fill_composed instead of rf_fill
 
 
 def run_fill_case(case: FillCase, device="cuda"):
@@ -47,7 +48,7 @@ def run_fill_case(case: FillCase, device="cuda"):
 
     Returns a dict of per-layer relative errors and sentinel status."""
     import linear_kv_cache_amd as rf
-    from linear_kv_cache_amd.runner import Filler, alloc_cache, fill_weights, gather_rows
+    from linear_kv_cache_amd.runner import ComposedFiller, Filler, alloc_cache, fill_weights, gather_rows
 
     cfg = case.cfg
     layers = cfg.filled_layers[: case.n_layers] if case.n_layers else cfg.filled_layers
@@ -68,7 +69,10 @@ def run_fill_case(case: FillCase, device="cuda"):
                         block_size=cfg.block_size, block_table=table,
                         n_blocks=(int(table.max()) + 1) if table is not None else None)
     chunk = case.chunk or (case.t1 - case.t0)
-    filler = Filler(fw, cfg.rope_base, case.pos0 + T, chunk, device)
+    if case.composed:
+        filler = ComposedFiller(fw, cfg.rope_base, case.pos0 + T, chunk, device)
+    else:
+        filler = Filler(fw, cfg.rope_base, case.pos0 + T, chunk, device)
     for c0 in range(case.t0, case.t1, chunk):
         c1 = min(case.t1, c0 + chunk)
         filler.fill(X[c0 - case.t0: c1 - case.t0], c0, c1, case.pos0, cache)
