@@ -19,11 +19,14 @@ Readings taken where the pages are silent (each one is listed in the design note
     projections, then rotate-half RoPE on K with 0-based absolute positions.
 
 Parity status: every function here is pinned by tests/test_oracle_*.py against closed
-forms, limits, brute force or an independent library route.
+forms, limits, brute force or an independent library route.  ``gdn_state`` (the Gated
+DeltaNet state update, a published recurrence the pages name but do not write out) is pinned
+by the recurrence's own closed forms; against the pages its parity is unpinned.
 """
 from .ridge import (NotSPD, gram_sums, fit, fit_from_sums, fit_pinv, ridge_objective,
                     solve_columns_from_data, stationarity_residual, stationarity_residual_from_sums)
 from .fill import rope_inverse_frequencies, rope_rotate, rmsnorm, fill_layer, fill
+from .gdn import gdn_state, l2_normalise
 from .translate import (relative_depth_centre, relative_depth_sources, headwise_dense,
                         translate_layer, translate, fit_translator, fit_r2, r2_assignment,
                         greedy_sources)
@@ -33,4 +36,4 @@ __all__ = ["NotSPD", "gram_sums", "fit", "fit_from_sums", "fit_pinv", "ridge_obj
            "rope_inverse_frequencies", "rope_rotate", "rmsnorm",
            "fill_layer", "fill", "relative_depth_centre", "relative_depth_sources",
            "headwise_dense", "translate_layer", "translate", "fit_translator", "fit_r2",
-           "r2_assignment", "greedy_sources"]
+           "r2_assignment", "greedy_sources", "gdn_state", "l2_normalise"]

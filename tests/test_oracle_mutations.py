@@ -145,3 +145,38 @@ def test_relative_depth_pins_catch_mistakes():
 
     for bad in (ties_to_shallower, unshifted_at_ends, truncates_centre):
         assert not holds(bad)
+
+
+def _gdn_pins_hold(gdn):
+    # the hand-worked token and the exact write of the delta rule
+    ok = np.allclose(gdn(np.array([[[0.6, 0.8]]]), np.array([[[3.0]]]), np.log([[0.5]]), np.array([[0.5]]),
+                         S0=np.array([[[1.0, 2.0]]])), [[[1.07, 1.76]]], atol=1e-12)
+    rng = np.random.default_rng(9)
+    S0 = rng.standard_normal((1, 3, 4))
+    k = np.array([0.5, 0.5, 0.5, 0.5])
+    v = rng.standard_normal(3)
+    S = gdn(k[None, None, :], v[None, None, :], np.log([[0.6]]), np.ones((1, 1)), S0=S0)
+    return ok and np.allclose(S[0] @ k, v, atol=1e-12)
+
+
+def test_gdn_pins_catch_mistakes():
+    assert _gdn_pins_hold(oracle.gdn_state)
+
+    def decay_after_write(K, V, g, beta, S0=None, normalise_k=False):
+        S = np.array(S0, float)
+        for t in range(K.shape[0]):
+            for h in range(K.shape[1]):
+                k, a, b = K[t, h], np.exp(g[t, h]), beta[t, h]
+                S[h] = a * (S[h] - b * np.outer(S[h] @ k, k) + b * np.outer(V[t, h], k))
+        return S
+
+    def erase_without_beta(K, V, g, beta, S0=None, normalise_k=False):
+        S = np.array(S0, float)
+        for t in range(K.shape[0]):
+            for h in range(K.shape[1]):
+                k, a, b = K[t, h], np.exp(g[t, h]), beta[t, h]
+                S[h] = a * (S[h] - np.outer(S[h] @ k, k)) + b * np.outer(V[t, h], k)
+        return S
+
+    for bad in (decay_after_write, erase_without_beta):
+        assert not _gdn_pins_hold(bad)
