@@ -477,6 +477,38 @@ rf_status rf_fill_streamed(const rf_fill_weights* weights, int32_t n_layers,
                            void* stream, void* copy_stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Gated DeltaNet state update.  RidgeFill project page, "Method" step 3 and Figure 2(b): on a
+ * Gated DeltaNet (linear-attention) layer the filled rows also run the layer's own state
+ * update, from the keys, values and gates its projections make of the predicted input.  The
+ * page does not write the update out; this is the published Gated DeltaNet recurrence (Yang,
+ * Kautz and Hatamizadeh, "Gated Delta Networks", 2024), per layer and head:
+ *     S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ * with S in R^{d_v x d_k} (fp32), over tokens t = 0 .. n_tokens-1 in order, starting from the
+ * state in d_state and leaving the final state there: a prompt filled in chunks continues
+ * from the previous chunk's state.  With normalise_k the keys are first scaled to unit length
+ * per head, k / sqrt(|k|^2 + eps).  Arithmetic in fp32 (keys and values upcast exactly).
+ * Per listed layer (host arrays of n_layers device pointers):
+ *   d_k[l], d_v[l]   : [n_tokens][ld_k], [n_tokens][ld_v] rows, dtype; head h's key is
+ *                      elements h d_k .. h d_k + d_k - 1 of its row (values likewise)
+ *   d_g[l], d_beta[l]: [n_tokens][n_heads] fp32 log decay (<= 0) and write strength
+ *   d_state[l]       : [n_heads][d_v][d_k] fp32, in and out, 16-B aligned
+ * Supported: d_k in {64, 128}, d_v <= 4096, up to 64 layers per call.
+ * ------------------------------------------------------------------------------------- */
+typedef struct {
+    int32_t n_heads;
+    int32_t d_k;
+    int32_t d_v;
+    rf_dtype dtype;        /* of the key and value rows                       */
+    int32_t normalise_k;   /* 1: unit-length keys per head before the update  */
+    float eps;             /* inside the root of the key norm                 */
+} rf_gdn_desc;
+
+rf_status rf_gdn_state(const rf_gdn_desc* desc, int32_t n_layers,
+                       const void* const* d_k, const void* const* d_v, int64_t ld_k, int64_t ld_v,
+                       const float* const* d_g, const float* const* d_beta, int64_t n_tokens,
+                       float* const* d_state, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * Token-wise linear KV-cache translators.  KV-Lingo page, section 3.1 "Linear translator
  * family": each target layer l has its own linear map for keys and its own for values, both
  * reading the cache rows of a set of nu source layers; with pre-norm storing the maps act on

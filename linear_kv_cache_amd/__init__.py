@@ -76,6 +76,11 @@ class rf_fill_composed_weights(C.Structure):
                 ("k_norm", C.POINTER(C.c_void_p)), ("k_norm_eps", C.c_float)]
 
 
+class rf_gdn_desc(C.Structure):
+    _fields_ = [("n_heads", C.c_int32), ("d_k", C.c_int32), ("d_v", C.c_int32), ("dtype", C.c_int),
+                ("normalise_k", C.c_int32), ("eps", C.c_float)]
+
+
 class rf_translate_weights(C.Structure):
     _fields_ = [("d_in", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("dtype", C.c_int),
                 ("T_k", C.POINTER(C.c_void_p)), ("T_v", C.POINTER(C.c_void_p)), ("b_k", C.POINTER(C.c_void_p)),
@@ -119,6 +124,8 @@ _sig = {
     "rf_fill_composed": (C.c_int, [C.POINTER(rf_fill_composed_weights), C.c_int32, _P, C.c_int64, C.c_int64,
                                    C.c_int64, C.c_int64, C.POINTER(rf_cache_desc), C.POINTER(_P), C.POINTER(_P), _P,
                                    C.c_int64, _P, C.c_int64, _P, C.c_size_t, _P]),
+    "rf_gdn_state": (C.c_int, [C.POINTER(rf_gdn_desc), C.c_int32, C.POINTER(_P), C.POINTER(_P), C.c_int64, C.c_int64,
+                               C.POINTER(_P), C.POINTER(_P), C.c_int64, C.POINTER(_P), _P]),
     "rf_fill_static_scratch_bytes": (C.c_size_t, []),
     "rf_fill_static": (C.c_int, [C.POINTER(rf_fill_weights), C.c_int32, _P, C.c_int64, C.c_int64, C.c_int64,
                                  C.c_int64, C.POINTER(rf_cache_desc), C.POINTER(_P), C.POINTER(_P), _P, C.c_int64, _P,
@@ -383,6 +390,20 @@ def rf_fill_composed(weights: ComposedFillWeights, X, t0: int, t1: int, pos0: in
     ws_bytes = ws.numel() * ws.element_size()
     _check(_lib.rf_fill_composed(C.byref(w), n_layers, _ptr(X), X.stride(0), t0, t1, pos0, C.byref(cache), kc, vc,
                                  _ptr(block_table), n_tab, _ptr(rope), rope_len, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def gdn_desc(n_heads: int, d_k: int, d_v: int, dtype, normalise_k: bool = True, eps: float = 1e-6) -> rf_gdn_desc:
+    return rf_gdn_desc(n_heads, d_k, d_v, _dtype_code(dtype), int(bool(normalise_k)), eps)
+
+
+def rf_gdn_state(desc: rf_gdn_desc, K: Sequence, V: Sequence, g: Sequence, beta: Sequence, states: Sequence,
+                 n_tokens: Optional[int] = None, stream=None):
+    """K, V: per layer [n_tokens, >= n_heads*d_k] / [n_tokens, >= n_heads*d_v] tensors (one row
+    stride for all K, one for all V); g, beta: per layer [n_tokens, n_heads] fp32; states: per
+    layer [n_heads, d_v, d_k] fp32, updated in place."""
+    n = K[0].shape[0] if n_tokens is None else n_tokens
+    _check(_lib.rf_gdn_state(C.byref(desc), len(K), _ptr_array(K), _ptr_array(V), K[0].stride(0), V[0].stride(0),
+                             _ptr_array(g), _ptr_array(beta), n, _ptr_array(states), _stream(stream)))
 
 
 def rf_fill_static_scratch_bytes() -> int:

@@ -406,3 +406,23 @@ def translate_block_table(cfg: TranslateConfig, n_tokens: int, device="cpu", ext
     g = generator(cfg.seed, "block_table", device="cpu")
     phys = torch.randperm(n_logical + extra_blocks, generator=g)[:n_logical]
     return phys.to(torch.int32).to(device)
+
+
+# ----------------------------------------------------------------------------------------
+# Gated DeltaNet inputs (keys, values, gates, write strengths of a linear-attention layer)
+# ----------------------------------------------------------------------------------------
+
+def gdn_inputs(seed: int, layer: int, tokens: int, n_heads: int, d_k: int, d_v: int, dtype=torch.bfloat16,
+               device="cpu", row_offset: int = 0):
+    """Synthetic per-token inputs of one Gated DeltaNet layer's state update: keys and values
+    N(0, 1) [tokens, n_heads * d], stored in ``dtype``; log decays g = -softplus(z) a_h with
+    z ~ N(0, 1) and a per-head rate a_h ~ U(0.02, 0.5) (per-token decays around 0.7-0.99);
+    write strengths beta = sigmoid(N(0, 1)).  Both fp32 [tokens, n_heads].  Drawn in blocks
+    keyed by ``row_offset`` so a prompt can be drawn in chunks."""
+    K = _randn((tokens, n_heads * d_k), seed, "gdn-k", layer, row_offset, device=device).to(dtype)
+    V = _randn((tokens, n_heads * d_v), seed, "gdn-v", layer, row_offset, device=device).to(dtype)
+    g_rate = 0.02 + 0.48 * torch.rand(n_heads, generator=generator(seed, "gdn-rate", layer), device="cpu")
+    z = _randn((tokens, n_heads), seed, "gdn-g", layer, row_offset, device=device)
+    g = -torch.nn.functional.softplus(z) * g_rate.to(device)
+    beta = torch.sigmoid(_randn((tokens, n_heads), seed, "gdn-b", layer, row_offset, device=device))
+    return K.contiguous(), V.contiguous(), g.contiguous(), beta.contiguous()
