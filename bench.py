@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector, published
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
 # HBM bytes of one rf_gram_accumulate call (32768 rows, d=4096, 16 targets), from two
 # rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of this benchmark, each scaled by what the
@@ -223,7 +224,36 @@ def translate_leg(steps: int, stream, dev, tc=None):
             "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
-def fill_only(cfg, steps: int, warmup: int):
+def gdn_leg(steps: int, stream, dev, n_layers=12, n_heads=16, d_k=128, d_v=128, T=16384):
+    """Time rf_gdn_state (the Gated DeltaNet state update of filled hybrid layers) over a
+    16384-token prompt: 12 layers (the linear-attention three quarters of 16 filled layers) of
+    16 heads with 128 x 128 states, bf16 keys and values, unit-length keys."""
+    import torch
+
+    import linear_kv_cache_amd as rf
+    import synth
+    log(f"gated deltanet state update: {n_layers} layers x {n_heads} heads x ({d_v} x {d_k}), T={T}")
+    ins = [synth.gdn_inputs(11, l, T, n_heads, d_k, d_v, torch.bfloat16, device=dev) for l in range(n_layers)]
+    S = [torch.zeros(n_heads, d_v, d_k, dtype=torch.float32, device=dev) for _ in range(n_layers)]
+    desc = rf.gdn_desc(n_heads, d_k, d_v, torch.bfloat16, True)
+
+    def call():
+        for s in S:
+            s.zero_()
+        rf.rf_gdn_state(desc, [x[0] for x in ins], [x[1] for x in ins], [x[2] for x in ins], [x[3] for x in ins], S,
+                        stream=stream)
+
+    (ms,) = alternate(stream, [call], steps)
+    # per token, head and state element: the row's dot product (2 FLOP) and the update
+    # a s + c k (3 FLOP)
+    flop = 5 * T * n_layers * n_heads * d_k * d_v
+    return {"workload": f"gdn-{n_layers}x{n_heads}h-{d_v}x{d_k}-T{T}", "ms_median": round(ms, 3),
+            "tokens_per_s": round(T / (ms / 1e3), 1), "tflops_fp32": round(flop / (ms / 1e3) / 1e12, 2),
+            "frac_fp32_vector_peak": round(flop / (ms / 1e3) / 1e12 / FP32_PEAK_TFLOPS, 4),
+            "bound": "latency: each head's state advances one token after the other"}
+
+
+def fill_only(cfg, steps: int, warmup: int, streamed: bool = False):
     """``--fill-only``: time rf_fill alone over a configuration's whole filled range, in its own
     chunks (the 27B-shaped and long-context workloads have no calibration set: their maps are
     the random-init law), and print one JSON line for it.  Not the benchmark's headline line."""
@@ -258,11 +288,24 @@ def fill_only(cfg, steps: int, warmup: int):
                 filler.fill(X[c0 - cfg.fill_t0:c1 - cfg.fill_t0], c0, c1, 0, cache, stream)
         return run
 
+    fns = [runner(composed), runner(direct)]
+    if streamed:
+        # the maps in page-locked host memory, one call over the whole range: each map crosses
+        # the host link once, the range is filled in steps of the workload's chunk inside each
+        # ring slot (rf_fill_streamed with rows_per_fill)
+        import dataclasses
+
+        from linear_kv_cache_amd.runner import StreamedFiller, pinned_copy
+        sw = dataclasses.replace(fw, W_map=[pinned_copy(W.cpu()) for W in fw.W_map])
+        sf = StreamedFiller(sw, cfg.rope_base, T, cfg.fill_chunk, dev, ring_slots=2, layers_per_slot=2,
+                            rows_per_fill=cfg.fill_chunk)
+        fns.append(lambda: sf.fill(X, cfg.fill_t0, cfg.fill_t1, 0, cache, stream))
     for _ in range(warmup):
-        runner(composed)()
-        runner(direct)()
+        for f in fns:
+            f()
     torch.cuda.synchronize()
-    med, med_direct = alternate(stream, [runner(composed), runner(direct)], steps)
+    meds = alternate(stream, fns, steps)
+    med, med_direct = meds[0], meds[1]
     alg = cfg.fill_tokens * len(layers) * cfg.fill_flop_per_token_layer()
     exe = cfg.fill_tokens * len(layers) * composed_flop_per_token_layer(cfg.d, cfg.kv_width)
     print(json.dumps({"metric": "filled tokens/sec (all filled layers) + % bf16 MFMA peak, fill only",
@@ -278,7 +321,12 @@ def fill_only(cfg, steps: int, warmup: int):
                                                 1),
                       "direct": {"ms_median": round(med_direct, 3),
                                  "tokens_per_s": round(cfg.fill_tokens / (med_direct / 1e3), 1),
-                                 "frac_bf16_peak": round(alg / (med_direct / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)}}),
+                                 "frac_bf16_peak": round(alg / (med_direct / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+                      **({"streamed": {"what": "rf_fill_streamed, one call, maps in page-locked host memory "
+                                               "(2 slots x 2 layers), steps of the workload's chunk",
+                                       "ms_median": round(meds[2], 3),
+                                       "tokens_per_s": round(cfg.fill_tokens / (meds[2] / 1e3), 1),
+                                       "vs_resident_direct": round(med_direct / meds[2], 4)}} if streamed else {})}),
           flush=True)
 
 
@@ -362,6 +410,9 @@ def main():
                          "GEMMs on the same maps, projections and prompt states")
     ap.add_argument("--no-translate", action="store_true", help="skip the cache-translator leg")
     ap.add_argument("--no-streamed", action="store_true", help="skip the streamed-maps leg")
+    ap.add_argument("--no-gdn", action="store_true", help="skip the Gated DeltaNet state-update leg")
+    ap.add_argument("--streamed", action="store_true",
+                    help="with --fill-only: also time the fill with streamed maps over the whole range in one call")
     ap.add_argument("--fill-only", action="store_true",
                     help="time the fill alone over --config's filled range (e.g. C3, C5) and print its own line")
     ap.add_argument("--fit-only", action="store_true",
@@ -385,7 +436,7 @@ def main():
 
     cfg = synth.CONFIGS[args.config]
     if args.fill_only:
-        fill_only(cfg, args.steps, args.warmup)
+        fill_only(cfg, args.steps, args.warmup, streamed=args.streamed)
         return
     if args.fit_only:
         fit_only(cfg, args.steps, args.warmup)
@@ -616,6 +667,8 @@ def main():
         out["translate_headwise"] = translate_leg(args.steps, stream, dev,
                                                   synth.scaled(synth.TR_BENCH, maps="headwise",
                                                                name=synth.TR_BENCH.name + "-headwise"))
+    if not args.no_gdn:
+        out["gdn_state"] = gdn_leg(args.steps, stream, dev)
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on {args.cpu_tokens} tokens and {args.cpu_fit_rows} calibration rows")
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens, args.cpu_fit_rows)

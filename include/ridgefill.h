@@ -454,7 +454,11 @@ rf_status rf_fill_static(const rf_fill_weights* weights, int32_t n_layers,
  * the copies run asynchronously.  Every other weight is a device pointer as for rf_fill.
  *  d_ring      : device buffer of ring_bytes >= rf_fill_streamed_ring_bytes() bytes, 256-B
  *                aligned: ring_slots slots of layers_per_slot maps
- *  d_ws        : rf_fill_workspace_bytes(weights, t1 - t0) * layers_per_slot bytes
+ *  d_ws        : rf_fill_workspace_bytes(weights, rows) * layers_per_slot bytes, rows = the
+ *                tokens filled per step: rows_per_fill, or t1 - t0 when it is 0 (or larger)
+ *  rows_per_fill : 0, or the tokens of [t0, t1) filled per step: a long prompt is filled in
+ *                steps of this many tokens inside each layer chunk, so each map is copied once
+ *                per call however many steps the range takes (the workspace covers one step)
  *  copy_stream : a stream other than ``stream`` (hipStream_t) for the host-to-device copies
  * Layers go in chunks of layers_per_slot (1..32): chunk c is copied into slot
  * c % ring_slots on copy_stream once the fill of chunk c - ring_slots has left that slot, and
@@ -474,7 +478,7 @@ rf_status rf_fill_streamed(const rf_fill_weights* weights, int32_t n_layers,
                            const float* d_rope, int64_t rope_len,
                            void* d_ws, size_t ws_bytes,
                            void* d_ring, size_t ring_bytes, int32_t ring_slots, int32_t layers_per_slot,
-                           void* stream, void* copy_stream);
+                           int64_t rows_per_fill, void* stream, void* copy_stream);
 
 /* ---------------------------------------------------------------------------------------
  * Gated DeltaNet state update.  RidgeFill project page, "Method" step 3 and Figure 2(b): on a

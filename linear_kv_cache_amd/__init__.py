@@ -133,7 +133,7 @@ _sig = {
     "rf_fill_streamed_ring_bytes": (C.c_size_t, [C.POINTER(rf_fill_weights), C.c_int32, C.c_int32]),
     "rf_fill_streamed": (C.c_int, [C.POINTER(rf_fill_weights), C.c_int32, _P, C.c_int64, C.c_int64, C.c_int64,
                                    C.c_int64, C.POINTER(rf_cache_desc), C.POINTER(_P), C.POINTER(_P), _P, C.c_int64, _P,
-                                   C.c_int64, _P, C.c_size_t, _P, C.c_size_t, C.c_int32, C.c_int32, _P, _P]),
+                                   C.c_int64, _P, C.c_size_t, _P, C.c_size_t, C.c_int32, C.c_int32, C.c_int64, _P, _P]),
     "rf_fit_r2_workspace_bytes": (C.c_size_t, [C.POINTER(rf_gram_desc), C.c_int32]),
     "rf_fit_r2": (C.c_int, [C.POINTER(rf_gram_desc), _P, C.c_double, C.c_int, C.POINTER(C.c_int32), C.c_int32, _P, _P,
                             _P, C.c_size_t, _P]),
@@ -471,16 +471,17 @@ def rf_fill_streamed_ring_bytes(weights: FillWeights, ring_slots: int, layers_pe
 
 def rf_fill_streamed(weights: FillWeights, X, t0: int, t1: int, pos0: int, cache: rf_cache_desc, k_cache: Sequence,
                      v_cache: Sequence, block_table, rope, rope_len: int, ws, ring, ring_slots: int,
-                     layers_per_slot: int, stream, copy_stream, n_layers: Optional[int] = None):
-    """weights.W_map: pinned host tensors (the maps); everything else on the device."""
+                     layers_per_slot: int, stream, copy_stream, n_layers: Optional[int] = None, rows_per_fill: int = 0):
+    """weights.W_map: pinned host tensors (the maps); everything else on the device.
+    rows_per_fill: tokens per fill step inside each layer chunk (0 = the whole range)."""
     w, _keep = weights._c()
     n_layers = len(weights.W_map) if n_layers is None else n_layers
     n_tab = 0 if block_table is None else block_table.numel()
     _check(_lib.rf_fill_streamed(C.byref(w), n_layers, _ptr(X), X.stride(0), t0, t1, pos0, C.byref(cache),
                                  _ptr_array(k_cache), _ptr_array(v_cache), _ptr(block_table), n_tab, _ptr(rope),
                                  rope_len, _ptr(ws), ws.numel() * ws.element_size(), _ptr(ring),
-                                 ring.numel() * ring.element_size(), ring_slots, layers_per_slot, _stream(stream),
-                                 _stream(copy_stream)))
+                                 ring.numel() * ring.element_size(), ring_slots, layers_per_slot, rows_per_fill,
+                                 _stream(stream), _stream(copy_stream)))
 
 
 def rf_fit_r2_workspace_bytes(desc: rf_gram_desc, n_sel: int) -> int:

@@ -960,7 +960,9 @@ static rf_status check_fill(const char* what, const rf_fill_weights* w, int32_t 
 
 // The maps of a streamed fill, layers_per_slot layers per ring slot: copy chunk c into slot
 // c % ring_slots on copy_stream once the fill of chunk c - ring_slots has released the slot,
-// and fill chunk c on stream once its copy has landed.  The first copy also waits for all
+// and fill chunk c on stream once its copy has landed, over the whole token range in steps of
+// ``rows_per_fill`` tokens (each map crosses the host link once per call, however long the
+// prompt).  The first copy also waits for all
 // work enqueued on stream before the call, so back-to-back calls (a chunked prompt) never
 // overwrite a slot an earlier call's fill still reads.  The events only order the two
 // streams; they are released when the work they mark completes.
@@ -970,7 +972,7 @@ static rf_status launch_fill_streamed(const rf_fill_weights* w, int32_t n_layers
                                       const rf_cache_layout_t& L, void* const* kc, void* const* vc,
                                       const int32_t* table, int64_t n_table, const float* rope, void* ws,
                                       size_t ws_bytes, void* ring, int32_t ring_slots, int32_t per_slot,
-                                      hipStream_t stream, hipStream_t copy_stream) {
+                                      int64_t rows_per_fill, hipStream_t stream, hipStream_t copy_stream) {
     const size_t map_bytes = (size_t)w->d * w->d * sizeof(T);
     std::vector<hipEvent_t> copied(ring_slots, nullptr), freed(ring_slots, nullptr);
     rf_status st = RF_OK;
@@ -1023,8 +1025,11 @@ static rf_status launch_fill_streamed(const rf_fill_weights* w, int32_t n_layers
         }
         cw.b_map = w->b_map + l0; cw.gamma = w->gamma + l0; cw.W_k = w->W_k + l0; cw.W_v = w->W_v + l0;
         cw.k_norm = w->k_norm ? w->k_norm + l0 : nullptr;
-        st = launch_fill<T>(&cw, gsz, X, ldx, t0, t1, pos0, cache, L, kc + l0, vc + l0, table, n_table, rope, ws,
-                            ws_bytes, stream);
+        for (int64_t r0 = t0; r0 < t1 && st == RF_OK; r0 += rows_per_fill) {
+            const int64_t r1 = std::min(t1, r0 + rows_per_fill);
+            st = launch_fill<T>(&cw, gsz, (const T*)X + (r0 - t0) * ldx, ldx, r0, r1, pos0, cache, L, kc + l0, vc + l0,
+                                table, n_table, rope, ws, ws_bytes, stream);
+        }
         if (st == RF_OK && hipEventRecord(freed[slot], stream) != hipSuccess)
             st = fail(RF_ERR_HIP, "rf_fill_streamed: event record failed");
     }
@@ -1158,13 +1163,15 @@ rf_status rf_fill_streamed(const rf_fill_weights* w, int32_t n_layers, const voi
                            void* const* k_cache, void* const* v_cache, const int32_t* d_block_table,
                            int64_t n_table_blocks, const float* d_rope, int64_t rope_len, void* d_ws,
                            size_t ws_bytes, void* d_ring, size_t ring_bytes, int32_t ring_slots,
-                           int32_t layers_per_slot, void* stream, void* copy_stream) {
+                           int32_t layers_per_slot, int64_t rows_per_fill, void* stream, void* copy_stream) {
     clear_error();
     RF_REQUIRE(ring_slots >= 1 && layers_per_slot >= 1 && layers_per_slot <= kMaxGroup, RF_ERR_INVALID_ARG,
                "rf_fill_streamed: need ring_slots >= 1 and 1 <= layers_per_slot <= 32");
+    RF_REQUIRE(rows_per_fill >= 0, RF_ERR_INVALID_ARG, "rf_fill_streamed: rows_per_fill must be >= 0");
+    const int64_t rpf = rows_per_fill == 0 || rows_per_fill > t1 - t0 ? std::max<int64_t>(t1 - t0, 1) : rows_per_fill;
     rf_cache_layout_t L;
     bool none;
-    const size_t need = (w && w->d > 0 && w->d % kFT == 0 && t1 >= t0) ? slot_bytes(w, t1 - t0) * layers_per_slot : 0;
+    const size_t need = (w && w->d > 0 && w->d % kFT == 0 && t1 >= t0) ? slot_bytes(w, rpf) * layers_per_slot : 0;
     rf_status st = check_fill("rf_fill_streamed", w, n_layers, d_X, ldx, t0, t1, pos0, cache, k_cache, v_cache,
                               d_block_table, n_table_blocks, d_rope, rope_len, d_ws, ws_bytes, need, L, none);
     if (st != RF_OK || none) return st;
@@ -1177,10 +1184,10 @@ rf_status rf_fill_streamed(const rf_fill_weights* w, int32_t n_layers, const voi
     if (w->dtype == RF_BF16)
         return launch_fill_streamed<bf16_t>(w, n_layers, d_X, ldx, t0, t1, pos0, cache, L, k_cache, v_cache,
                                             d_block_table, n_table_blocks, d_rope, d_ws, ws_bytes, d_ring, ring_slots,
-                                            layers_per_slot, s, cs);
+                                            layers_per_slot, rpf, s, cs);
     return launch_fill_streamed<float>(w, n_layers, d_X, ldx, t0, t1, pos0, cache, L, k_cache, v_cache,
                                        d_block_table, n_table_blocks, d_rope, d_ws, ws_bytes, d_ring, ring_slots,
-                                       layers_per_slot, s, cs);
+                                       layers_per_slot, rpf, s, cs);
 }
 
 rf_status rf_translate(const rf_translate_weights* w, int32_t n_layers, const void* const* d_src_k,

@@ -274,16 +274,20 @@ class StreamedFiller(Filler):
     (rf_fill_streamed); the workspace holds ``layers_per_slot`` layer slots."""
 
     def __init__(self, weights: FillWeights, rope_base: float, max_pos: int, max_rows: int, device,
-                 ring_slots: int = 2, layers_per_slot: int = 1, stream=None):
-        super().__init__(weights, rope_base, max_pos, max_rows, device, ws_slots=layers_per_slot, stream=stream)
-        self.ring_slots, self.layers_per_slot = ring_slots, layers_per_slot
+                 ring_slots: int = 2, layers_per_slot: int = 1, stream=None, rows_per_fill: int = 0):
+        """rows_per_fill: tokens per fill step inside each layer chunk (0: a call's whole range,
+        which must then fit ``max_rows``); the workspace covers one step."""
+        step_rows = rows_per_fill if rows_per_fill > 0 else max_rows
+        super().__init__(weights, rope_base, max_pos, step_rows, device, ws_slots=layers_per_slot, stream=stream)
+        self.ring_slots, self.layers_per_slot, self.rows_per_fill = ring_slots, layers_per_slot, rows_per_fill
         self.ring = device_bytes(rf_fill_streamed_ring_bytes(weights, ring_slots, layers_per_slot), device)
         self.copy_stream = torch.cuda.Stream(device=device)
 
     def fill(self, X, t0: int, t1: int, pos0: int, cache: Cache, stream=None):
         rf_fill_streamed(self.w, X, t0, t1, pos0, cache.desc, cache.k, cache.v, cache.block_table, self.rope,
                          self.rope_len, self.ws, self.ring, self.ring_slots, self.layers_per_slot,
-                         stream if stream is not None else torch.cuda.current_stream(), self.copy_stream)
+                         stream if stream is not None else torch.cuda.current_stream(), self.copy_stream,
+                         rows_per_fill=self.rows_per_fill)
 
 
 def pinned_copy(t: torch.Tensor) -> torch.Tensor:

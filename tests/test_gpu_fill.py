@@ -189,3 +189,35 @@ def test_fill_streamed_back_to_back_chunks():
         for a, b in ((outs[0].k[li], outs[1].k[li]), (outs[0].v[li], outs[1].v[li])):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), li
     log(f"[fill] streamed back-to-back chunks of {chunk}: bit-identical to the resident fill")
+
+
+def test_fill_streamed_long_prompt_in_steps():
+    # one streamed call over a long range, filled in steps of 256 tokens inside each layer chunk
+    # (each map copied once), paged: the caches equal the resident fill's bit for bit
+    from linear_kv_cache_amd.runner import Filler, StreamedFiller, alloc_cache, fill_weights, pinned_copy
+    cfg = SMALL_PAGED
+    layers = cfg.filled_layers
+    ws = [synth.layer_weights(cfg, l, device="cuda") for l in layers]
+    args = (cfg.d, cfg.n_kv_heads, cfg.head_dim, cfg.rms_eps, cfg.torch_dtype, [w.W_map for w in ws],
+            [w.b_map for w in ws], [w.gamma for w in ws], [w.W_k for w in ws], [w.W_v for w in ws])
+    fw = fill_weights(*args)
+    fs = fill_weights(*args)
+    fs.W_map = [pinned_copy(W.cpu()) for W in fw.W_map]
+    t0, t1 = 19, 1100
+    T = cfg.prompt_tokens
+    X = synth.hidden_states(cfg, t1 - t0, "prompt", device="cuda")
+    table = synth.block_table(cfg, T, device="cuda")
+    nb = int(table.max()) + 1
+    outs = []
+    for filler in (Filler(fw, cfg.rope_base, T, t1 - t0, "cuda"),
+                   StreamedFiller(fs, cfg.rope_base, T, t1 - t0, "cuda", ring_slots=2, layers_per_slot=1,
+                                  rows_per_fill=256)):
+        cache = alloc_cache(len(layers), cfg.n_kv_heads, cfg.head_dim, T, cfg.torch_dtype, "cuda", paged=True,
+                            block_size=cfg.block_size, block_table=table, n_blocks=nb)
+        filler.fill(X, t0, t1, 0, cache)
+        torch.cuda.synchronize()
+        outs.append(cache)
+    for li in range(len(layers)):
+        for a, b in ((outs[0].k[li], outs[1].k[li]), (outs[0].v[li], outs[1].v[li])):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), li
+    log("[fill] streamed in steps of 256 tokens: bit-identical to the resident fill")
