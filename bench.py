@@ -35,12 +35,30 @@ sys.path.insert(0, ROOT)
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector, published
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
-# HBM bytes of one rf_gram_accumulate call (32768 rows, d=4096, 16 targets), from two
-# rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of this benchmark, each scaled by what the
-# counter reads for a 1 GiB device copy; profiles/pmc_traffic_llama8b-shaped_d4096_T16384.md has the
-# commands and the figures; set to None whenever k_gram_pipe or the chunk size changes.
-GRAM_TRAFFIC = (19436865 * 2 + 1164248) * 1024   # 41.0e9 B
+# HBM bytes of one rf_gram_accumulate call (32768 rows, d=4096, 16 targets): the per-launch
+# means (KiB) of two rocprofv3 --pmc runs of this benchmark (FETCH_SIZE, then WRITE_SIZE), and
+# the factors that turn each counter into bytes (what it reads for a 1 GiB device copy: 524308
+# KiB fetched, 1048576 KiB written).  The traffic profile under profiles/ gives the commands.
+# The figures belong to the kernel sources they were taken on: once those hash differently the
+# traffic is reported as null until the counters are taken again.
+GRAM_COUNTERS = {"fetch_kib": 18740900.7, "write_kib": 1173062.7, "fetch_scale": 2.0, "write_scale": 1.0,
+                 "sources": ("gram.hip", "rf_pipe.h", "rf_mfma.h", "rf_internal.h"),
+                 "sources_sha256": "f506a57d4c821f42d51f342f0b88f0a62b164cb90ca7533e8bb5d65040a680aa"}
 METRIC = "filled tokens/sec (all filled layers) + % bf16 MFMA peak; ridge-fit rows/sec"
+
+
+def gram_traffic():
+    """Scaled HBM bytes of one Gram launch, or None when the kernel's sources have changed since
+    the counters were read."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in GRAM_COUNTERS["sources"]:
+        with open(os.path.join(ROOT, "linear_kv_cache_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != GRAM_COUNTERS["sources_sha256"]:
+        return None
+    return int((GRAM_COUNTERS["fetch_kib"] * GRAM_COUNTERS["fetch_scale"] +
+                GRAM_COUNTERS["write_kib"] * GRAM_COUNTERS["write_scale"]) * 1024)
 
 
 def log(msg):
@@ -569,7 +587,7 @@ def main():
                                f"(k_gram_pipe, column sums in its last work-groups)",
                      "achieved": round(gram_tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gram_tflops / BF16_PEAK_TFLOPS, 4),
-                     "traffic": GRAM_TRAFFIC if args.config == "C2" else None,
+                     "traffic": gram_traffic() if args.config == "C2" else None,
                      "launch_ms": round(gram_launch_ms, 4), "flop_per_launch": gram_flop_per_launch},
     }
     if args.library_reference:

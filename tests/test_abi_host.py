@@ -366,3 +366,98 @@ def test_fill_static_refuses_oversized_requests_before_any_device_call():
     with pytest.raises(rf.RidgeFillError) as e:
         rf.rf_fill_static(w, X[:64], 0, 64, 0, cd, [256], [256], None, None, 64, stream=0)
     assert e.value.status == rf.RF_ERR_INVALID_ARG
+
+
+def _cweights(d=256, H=4, dh=64, n=1, ptr=256, c_v=None):
+    c_v = [ptr] * n if c_v is None else c_v
+    return rf.ComposedFillWeights(d, H, dh, 1e-6, [ptr] * n, [ptr] * n, [ptr] * n, [ptr] * n, [ptr] * n, c_v)
+
+
+def test_fill_compose_validation_before_enqueue():
+    bf = torch.bfloat16
+    w = _weights(dtype=bf)
+    assert rf.rf_fill_compose_workspace_bytes(w) == 4 * 256 * 256 + 8 * 256 * 256
+    ws = _aligned_bytes(rf.rf_fill_compose_workspace_bytes(w))
+    cases = [
+        (dict(w=_weights(dtype=torch.float32)), rf.RF_ERR_UNSUPPORTED),           # BF16 only
+        (dict(w=_weights(d=320, dtype=bf)), rf.RF_ERR_UNSUPPORTED),
+        (dict(w=_weights(dh=96, H=8, dtype=bf)), rf.RF_ERR_UNSUPPORTED),
+        (dict(w=_weights(H=1, dh=64, dtype=bf)), rf.RF_ERR_UNSUPPORTED),        # kv width 64, not a tile
+        (dict(out=_cweights(ptr=264)), rf.RF_ERR_INVALID_ARG),                     # outputs 8-byte aligned
+        (dict(out=_cweights(ptr=0)), rf.RF_ERR_INVALID_ARG),                       # null outputs
+        (dict(ws=_aligned_bytes(256)), rf.RF_ERR_WORKSPACE),
+        (dict(ws=_aligned_bytes(len(ws) + 512)[8:]), rf.RF_ERR_INVALID_ARG),      # misaligned workspace
+    ]
+    for kw, status in cases:
+        args = dict(w=w, out=_cweights(), ws=ws)
+        args.update(kw)
+        with pytest.raises(rf.RidgeFillError) as e:
+            rf.rf_fill_compose(args["w"], args["out"], args["ws"], stream=0)
+        assert e.value.status == status, kw
+    rf.rf_fill_compose(w, _cweights(), ws, stream=0, n_layers=0)   # no layers: nothing to do
+
+
+def test_fill_composed_validation_before_enqueue():
+    bf = torch.bfloat16
+    cache = rf.cache_desc(4, 64, 512, rf.RF_LAYOUT_CONTIGUOUS, bf)
+    X = torch.empty(512, 256, dtype=bf)
+    rope = torch.empty(512, 64)
+    w = _cweights()
+    need = rf.rf_fill_composed_workspace_bytes(w, 512)
+    assert need >= 512 * (256 // 256) * 4
+    ws = _aligned_bytes(need)
+
+    def call(w=w, t0=0, t1=512, pos0=0, cache_=cache, ws_=ws, n_layers=None):
+        rf.rf_fill_composed(w, X, t0, t1, pos0, cache_, [256], [256], None, rope, 512, ws_, stream=0,
+                            n_layers=n_layers)
+
+    cases = [
+        (dict(t0=5, t1=4), rf.RF_ERR_INVALID_ARG),
+        (dict(w=_cweights(d=320)), rf.RF_ERR_UNSUPPORTED),
+        (dict(w=_cweights(dh=96, H=8)), rf.RF_ERR_UNSUPPORTED),
+        (dict(t1=513), rf.RF_ERR_INVALID_ARG),
+        (dict(pos0=1), rf.RF_ERR_INVALID_ARG),                                    # rope table too short
+        (dict(w=_cweights(c_v=[0])), rf.RF_ERR_INVALID_ARG),                       # null value intercepts
+        (dict(ws_=_aligned_bytes(256)), rf.RF_ERR_WORKSPACE),
+        (dict(cache_=rf.cache_desc(4, 64, 512, rf.RF_LAYOUT_PAGED, bf)), rf.RF_ERR_INVALID_ARG),  # no table
+    ]
+    for kw, status in cases:
+        with pytest.raises(rf.RidgeFillError) as e:
+            call(**kw)
+        assert e.value.status == status, kw
+    call(t0=7, t1=7)          # empty range: nothing to do
+    call(n_layers=0)          # no layers: nothing to do
+
+
+def test_gdn_state_validation_before_enqueue():
+    P = C.POINTER(C.c_void_p)
+
+    def call(n_heads=4, d_k=128, d_v=128, dtype=rf.RF_BF16, normalise=1, eps=1e-6, n_layers=1, ld_k=None,
+             ld_v=None, n_tokens=16, state=256):
+        desc = rf.rf_gdn_desc(n_heads, d_k, d_v, dtype, normalise, eps)
+        ptrs = (C.c_void_p * 64)(*([256] * 64))
+        states = (C.c_void_p * 64)(*([state] * 64))
+        rf._check(rf._lib.rf_gdn_state(C.byref(desc), n_layers, ptrs, ptrs, n_heads * d_k if ld_k is None else ld_k,
+                                       n_heads * d_v if ld_v is None else ld_v, C.cast(ptrs, P), C.cast(ptrs, P),
+                                       n_tokens, C.cast(states, P), None))
+
+    cases = [
+        (dict(d_k=96), rf.RF_ERR_UNSUPPORTED),
+        (dict(n_layers=65), rf.RF_ERR_UNSUPPORTED),
+        (dict(n_layers=-1), rf.RF_ERR_INVALID_ARG),
+        (dict(d_v=4097), rf.RF_ERR_INVALID_ARG),
+        (dict(n_heads=0), rf.RF_ERR_INVALID_ARG),
+        (dict(dtype=7), rf.RF_ERR_INVALID_ARG),
+        (dict(normalise=2), rf.RF_ERR_INVALID_ARG),
+        (dict(eps=-1.0), rf.RF_ERR_INVALID_ARG),
+        (dict(ld_k=4 * 128 - 8), rf.RF_ERR_INVALID_ARG),                           # rows shorter than the heads
+        (dict(ld_v=4 * 128 - 8), rf.RF_ERR_INVALID_ARG),
+        (dict(state=264), rf.RF_ERR_INVALID_ARG),                                  # states 8-byte aligned
+        (dict(state=0), rf.RF_ERR_INVALID_ARG),
+    ]
+    for kw, status in cases:
+        with pytest.raises(rf.RidgeFillError) as e:
+            call(**kw)
+        assert e.value.status == status, kw
+    call(n_tokens=0)          # no tokens: nothing to do
+    call(n_layers=0)          # no layers: nothing to do
