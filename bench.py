@@ -400,6 +400,15 @@ def fit_only(cfg, steps: int, warmup: int):
         torch.cuda.synchronize()
     gram = statistics.median(r[0].elapsed_time(r[1]) for r in recs)
     solves = [statistics.median(r[1].elapsed_time(r[2]) for r in recs)]
+    # the batched call against one lambda alone, alternated on the same state
+    ws1 = device_bytes(rf.rf_solve_workspace_bytes(state.desc, L, 1), dev)
+    mid = cfg.lambdas[len(cfg.lambdas) // 2]
+    one, alln = alternate(stream, [
+        lambda: rf.rf_solve(state.desc, state.buf, mid, rf.RF_LAMBDA_ABSOLUTE, list(range(L)), None, W_lp[0], b[0],
+                            info[:1], ws1, stream),
+        lambda: rf.rf_solve(state.desc, state.buf, list(cfg.lambdas), rf.RF_LAMBDA_ABSOLUTE, list(range(L)), None,
+                            W_lp, b, info, ws, stream)], max(steps, 3))
+    del ws1
     tflops = cfg.calib_rows * cfg.fit_flop_per_row() / (gram / 1e3) / 1e12
     print(json.dumps({"metric": "ridge-fit rows/sec, fit only",
                       "config": {"workload": cfg.name, "d": d, "targets": L, "calib_rows": cfg.calib_rows,
@@ -408,6 +417,8 @@ def fit_only(cfg, steps: int, warmup: int):
                       "rows_per_s": round(cfg.calib_rows / (gram / 1e3), 1), "gram_tflops": round(tflops, 1),
                       "gram_frac_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
                       "solve_ms_median_all_lambdas": round(solves[0], 3),
+                      "solve_alternated": {"one_lambda_ms": round(one, 3), "all_lambdas_ms": round(alln, 3),
+                                           "ratio": round(alln / one, 3), "lambda_alone": mid},
                       "equilibrated_inverse_max": [round(float(x), 4) for x in cond.cpu().tolist()],
                       "rows_per_s_incl_solves": round(cfg.calib_rows / ((gram + sum(solves)) / 1e3), 1),
                       "flop_per_row": cfg.fit_flop_per_row()}), flush=True)

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libridgefill.so")
-SOURCES = ["abi.cpp", "compose.hip", "fill.hip", "gdn.hip", "gram.hip", "solve.hip"]
+SOURCES = ["abi.cpp", "compose.hip", "fill.hip", "gdn.hip", "gram.hip", "headwise.hip", "solve.hip"]
 ARCH = os.environ.get("RIDGEFILL_ARCH", "gfx950")
 
 

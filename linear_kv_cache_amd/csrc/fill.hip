@@ -1251,6 +1251,9 @@ rf_status rf_translate(const rf_translate_weights* w, int32_t n_layers, const vo
         RF_REQUIRE(t1 <= cache->max_tokens, RF_ERR_INVALID_ARG, "rf_translate: t1 exceeds the cache's max_tokens");
     }
     hipStream_t s = (hipStream_t)stream;
+    if (translate_headwise_supported(w))
+        return launch_translate_headwise(w, n_layers, d_src_k, d_src_v, ld_src, t0, t1, pos0, cache, L, k_cache,
+                                         v_cache, d_block_table, n_table_blocks, d_rope, s);
     if (w->dtype == RF_BF16)
         return launch_translate<bf16_t>(w, n_layers, d_src_k, d_src_v, ld_src, t0, t1, pos0, cache, L, k_cache,
                                         v_cache, d_block_table, n_table_blocks, d_rope, s);

@@ -26,6 +26,15 @@ inline size_t elem_bytes(rf_dtype t) { return t == RF_F32 ? 4 : 2; }
 inline int64_t gram_dy(const rf_gram_desc* g) { return g->d_out > 0 ? g->d_out : g->d; }
 inline bool valid_dtype(rf_dtype t) { return t == RF_F32 || t == RF_BF16; }
 
+// Head-wise translators on their own kernel (headwise.hip): BF16 maps with headwise = 1 and
+// d_in = nu * n_kv_heads * head_dim, nu in 1..2.  Arguments validated by rf_translate.
+bool translate_headwise_supported(const rf_translate_weights* w);
+rf_status launch_translate_headwise(const rf_translate_weights* w, int32_t n_layers, const void* const* src_k,
+                                    const void* const* src_v, int64_t ld_src, int64_t t0, int64_t t1, int64_t pos0,
+                                    const rf_cache_desc* cache, const rf_cache_layout_t& L, void* const* kc,
+                                    void* const* vc, const int32_t* table, int64_t n_table, const float* rope,
+                                    hipStream_t stream);
+
 }  // namespace rf
 
 #define RF_REQUIRE(cond, status, msg)                  \

@@ -296,3 +296,80 @@ def test_greedy_match_lambda_zero_skips_singular_sets():
     assert got[0] == oracle.greedy_sources(Sn, f64(y), 2, 0.0) == [0, 2]
     with pytest.raises(RuntimeError):
         greedy_sources(st, d, 3, 0.0, 0)
+
+
+def _translate_caches(cfg, headwise: bool, t0: int, t1: int, pos0: int = 0, k_norm: bool = False):
+    """rf_translate of [t0, t1) with the config's maps passed as head-wise or as dense maps."""
+    import linear_kv_cache_amd as rf
+    from linear_kv_cache_amd.runner import Translator, alloc_cache, gather_rows, translate_weights
+
+    dev = "cuda"
+    E = rf.rf_relative_depth_sources(cfg.n_src, cfg.n_tgt, cfg.nu)
+    Ks, Vs = synth.source_cache(cfg, t1 - t0, device=dev, row_offset=t0)
+    maps = [synth.translator_maps(cfg, l, device=dev) for l in range(cfg.n_tgt)]
+    gks = [synth.key_norm_weights(cfg, l).to(dev) for l in range(cfg.n_tgt)] if k_norm else None
+    tw = translate_weights(cfg.d_in, cfg.n_kv_heads, cfg.head_dim, cfg.torch_dtype, [m[0] for m in maps],
+                           [m[1] for m in maps], [m[2] for m in maps] if cfg.bias else None,
+                           [m[3] for m in maps] if cfg.bias else None, headwise=headwise, k_norm=gks)
+    table = synth.translate_block_table(cfg, t1, device=dev) if cfg.paged else None
+    cache = alloc_cache(cfg.n_tgt, cfg.n_kv_heads, cfg.head_dim, t1, cfg.torch_dtype, dev, paged=cfg.paged,
+                        block_size=cfg.block_size, block_table=table,
+                        n_blocks=(int(table.max()) + 1) if table is not None else None)
+    tr = Translator(tw, cfg.rope_base, pos0 + t1, dev)
+    ld = cfg.n_src * cfg.d_src
+    tr.translate([Ks[0, e[0]] for e in E], [Vs[0, e[0]] for e in E], ld, t0, t1, pos0, cache)
+    torch.cuda.synchronize()
+    return [(gather_rows(cache, cache.k[l], 0, t1), gather_rows(cache, cache.v[l], 0, t1)) for l in range(cfg.n_tgt)]
+
+
+@pytest.mark.parametrize("dh,nu,paged,bias,k_norm", [(128, 2, False, False, False), (128, 1, True, True, True),
+                                                      (64, 2, True, True, False), (64, 1, False, False, True)])
+def test_headwise_kernel_equals_dense_kernel_on_block_diagonal_maps(dh, nu, paged, bias, k_norm):
+    # The head-wise kernel computes only the diagonal head blocks; the dense kernel reads every
+    # column of the same maps, whose other entries are zero.  Adding exact zeros leaves fp32
+    # sums unchanged and the nonzero terms come in the same order, so the products agree; the
+    # epilogues may contract the rotation's multiply-adds differently, so a stored key may sit
+    # one bf16 rounding step away (values, never rotated, are equal).
+    heads = 1024 // dh
+    cfg = synth.scaled(SMALL_PAGED, name=f"tr-hw-vs-dense-{dh}-{nu}", src_kv_heads=heads, src_head_dim=dh,
+                       n_kv_heads=heads, head_dim=dh, nu=nu, n_src=3, n_tgt=3, paged=paged, bias=bias,
+                       maps="headwise", seed=2100 + dh + nu)
+    t0, t1 = 19, 19 + 1000
+    hw = _translate_caches(cfg, True, t0, t1, pos0=5, k_norm=k_norm)
+    dn = _translate_caches(cfg, False, t0, t1, pos0=5, k_norm=k_norm)
+    for l, ((kh, vh), (kd, vd)) in enumerate(zip(hw, dn)):
+        # the translated rows (the others keep the allocation's sentinels in both)
+        kh, vh, kd, vd = kh[t0:t1], vh[t0:t1], kd[t0:t1], vd[t0:t1]
+        dk = (kh.float() - kd.float()).abs()
+        dv = (vh.float() - vd.float()).abs().max().item()
+        # one bf16 step of the larger value (2^-7 of its power-of-two floor), plus the fp32
+        # rounding of the rotation's two products for keys that nearly cancel (~2^-24 of the
+        # operands, bounded here by 2^-20 of the layer's largest key)
+        step = torch.exp2(torch.floor(torch.log2(torch.maximum(kh.float().abs(), kd.float().abs()) + 1e-30)) - 7)
+        step = step + 2.0 ** -20 * kd.float().abs().max()
+        log(f"[translate] head-wise vs dense dh={dh} nu={nu} layer {l}: max |dK|={dk.max().item():.3e} "
+            f"({int((dk > 0).sum())} keys differ) |dV|={dv:.3e}")
+        over = (dk > step).nonzero()
+        if over.numel():
+            i = tuple(over[0].tolist())
+            log(f"[translate]   {over.shape[0]} keys beyond one step; first at {i}: head-wise "
+                f"{kh[i].item():.6e} dense {kd[i].item():.6e} step {step[i].item():.3e}")
+        assert over.numel() == 0, (l, dk.max().item())
+        assert torch.equal(vh, vd), (l, dv)
+
+
+def test_translate_headwise_full_size_sampled():
+    # the benchmark's head-wise workload (28 -> 36 layers, 8 x 128, nu = 2, 16384 tokens; one call,
+    # launches of 32 and 4 target layers), compared with the oracle on sampled rows
+    cfg = synth.scaled(synth.TR_BENCH, name="kv-translate-headwise-full", maps="headwise")
+    g = np.random.default_rng(9)
+    sample = sorted(set([0, 31, 32, 4095, 4096, 8191, 8192, cfg.t1 - 1] + list(g.integers(0, cfg.t1, 40))))
+    _check(run_translate_case(TranslateCase(cfg, cfg.t0, cfg.t1, sample=sample, gen_device="cuda")),
+           "head-wise full size sampled")
+
+
+def test_translate_headwise_three_sources():
+    # nu = 3 head-wise maps keep the dense kernel's block-by-block reading (the head-wise kernel
+    # takes nu <= 2); paged, intercepts, ragged range
+    cfg = synth.scaled(SMALL_PAGED, name="tr-hw-nu3", n_src=6, n_tgt=5, nu=3, maps="headwise", seed=2011)
+    _check(run_translate_case(TranslateCase(cfg, 37, 737, pos0=11, chunk=350)), "bf16 head-wise nu=3 paged")
