@@ -191,6 +191,24 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state,
                    int32_t* d_info, double* d_cond, double* d_resid,
                    void* d_ws, size_t ws_bytes, void* stream);
 
+/* Head-wise maps.  KV-Lingo page, section 3.1 "Head mixing" (a head-wise translator maps each
+ * source head only onto the same target head: its map is block-diagonal by head) and section
+ * 3.2 (the first stage fits the maps in closed form).  The ridge fit restricted to such maps is
+ * one independent ridge fit per head: target head h on head h of every source layer.  Computed
+ * as rf_solve with the centred moments between different heads taken as zero, so that the
+ * regularised system is block-diagonal by head and its solution is those per-head maps; the
+ * blocks between heads of the output are exactly zero.  Features are numbered as the state
+ * has them: target output o belongs to head o / head_dim; source feature i, of source layer
+ * i / d_out, to head (i % d_out) / head_dim (source layers of the targets' layout side by side).
+ *  head_dim : a positive multiple of 8 dividing the targets' width d_out; d a multiple of d_out
+ * Every other argument, output and workspace as for rf_solve (rf_solve_workspace_bytes). */
+rf_status rf_solve_headwise(const rf_gram_desc* desc, const void* d_state,
+                            const double* lambdas, int32_t n_lambda, rf_lambda_mode mode, int32_t head_dim,
+                            const int32_t* targets, int32_t n_sel, rf_product product,
+                            float* d_W, void* d_W_lp, float* d_b,
+                            int32_t* d_info, double* d_cond, double* d_resid,
+                            void* d_ws, size_t ws_bytes, void* stream);
+
 /* Host only.  RF_OK when all n pivots reports (a host copy of rf_solve's d_info) are 0, else
  * RF_ERR_NOT_SPD with the first failing lambda and pivot in rf_last_error(). */
 rf_status rf_info_status(const int32_t* info, int32_t n);

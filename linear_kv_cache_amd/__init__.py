@@ -102,6 +102,9 @@ _sig = {
     "rf_solve_workspace_bytes": (C.c_size_t, [C.POINTER(rf_gram_desc), C.c_int32, C.c_int32]),
     "rf_solve": (C.c_int, [C.POINTER(rf_gram_desc), _P, C.POINTER(C.c_double), C.c_int32, C.c_int,
                            C.POINTER(C.c_int32), C.c_int32, C.c_int, _P, _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "rf_solve_headwise": (C.c_int, [C.POINTER(rf_gram_desc), _P, C.POINTER(C.c_double), C.c_int32, C.c_int,
+                                    C.c_int32, C.POINTER(C.c_int32), C.c_int32, C.c_int, _P, _P, _P, _P, _P, _P, _P,
+                                    C.c_size_t, _P]),
     "rf_info_status": (C.c_int, [C.POINTER(C.c_int32), C.c_int32]),
     "rf_solve_pinv_workspace_bytes": (C.c_size_t, [C.POINTER(rf_gram_desc), C.c_int32]),
     "rf_solve_pinv": (C.c_int, [C.POINTER(rf_gram_desc), _P, C.c_double, C.c_int, C.c_double, C.c_int32,
@@ -245,6 +248,18 @@ def rf_solve(desc: rf_gram_desc, state, lambdas, mode: int, targets: Sequence[in
     _check(_lib.rf_solve(C.byref(desc), _ptr(state), la, len(lams), int(mode), tg, len(targets), int(product), _ptr(W),
                          _ptr(W_lp), _ptr(b), _ptr(info), _ptr(cond), _ptr(resid), _ptr(ws), ws_bytes,
                          _stream(stream)))
+
+
+def rf_solve_headwise(desc: rf_gram_desc, state, lambdas, mode: int, head_dim: int, targets: Sequence[int], W, W_lp,
+                      b, info, ws, stream=None, product: int = RF_PRODUCT_AUTO, cond=None, resid=None):
+    """rf_solve for maps block-diagonal by head (one ridge fit per head); arguments as rf_solve."""
+    lams = [float(lambdas)] if isinstance(lambdas, (int, float)) else [float(x) for x in lambdas]
+    la = (C.c_double * max(1, len(lams)))(*lams)
+    tg = (C.c_int32 * max(1, len(targets)))(*targets)
+    ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib.rf_solve_headwise(C.byref(desc), _ptr(state), la, len(lams), int(mode), int(head_dim), tg,
+                                  len(targets), int(product), _ptr(W), _ptr(W_lp), _ptr(b), _ptr(info), _ptr(cond),
+                                  _ptr(resid), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def rf_info_status(info: Sequence[int]) -> int:

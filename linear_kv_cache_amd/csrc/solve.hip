@@ -196,16 +196,24 @@ __global__ void k_zero_int(int32_t* p, int n) {
     if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
 }
 
-// C[i][j] = S_xx[min(i,j)][max(i,j)] - s_x[i] s_x[j] / n, into every matrix of the batch
-// (blockIdx.y: one per lambda, d*d elements apart)
-__global__ void k_centre_gram(const float* Sxx, const double* sx, const int64_t* np, int64_t d, double* C) {
+// Head-wise maps: with hdim > 0, feature i belongs to head (i % hper) / hdim (hper = the
+// targets' width; the sources are whole multiples of it), and the centred moments between
+// different heads are taken as zero, so the system is block-diagonal by head.
+__device__ inline bool cross_head(int32_t hdim, int32_t hper, int64_t i, int64_t j) {
+    return hdim > 0 && (i % hper) / hdim != (j % hper) / hdim;
+}
+
+// C[i][j] = S_xx[min(i,j)][max(i,j)] - s_x[i] s_x[j] / n (0 between heads), into every matrix
+// of the batch (blockIdx.y: one per lambda, d*d elements apart)
+__global__ void k_centre_gram(const float* Sxx, const double* sx, const int64_t* np, int64_t d, double* C,
+                              int32_t hdim, int32_t hper) {
     C += (int64_t)blockIdx.y * d * d;
     const double inv_n = 1.0 / (double)*np;
     const int64_t n = d * d;
     for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
         const int64_t i = idx / d, j = idx % d;
         const int64_t lo = i < j ? i : j, hi = i < j ? j : i;
-        C[idx] = (double)Sxx[lo * d + hi] - sx[i] * sx[j] * inv_n;
+        C[idx] = cross_head(hdim, hper, i, j) ? 0.0 : (double)Sxx[lo * d + hi] - sx[i] * sx[j] * inv_n;
     }
 }
 
@@ -254,6 +262,7 @@ struct CrossArgs {
     int64_t rows;          // n_sel * dy
     bf16_t* Aq;            // [rows][2d]: [hi | lo] of the equilibrated centred cross moments
     double* mu_y;          // [rows]
+    int32_t hdim, hper;    // head-wise maps (hdim > 0): moments between heads taken as zero
     int32_t tsel[kMaxSel];
 };
 
@@ -268,13 +277,15 @@ __device__ inline void centre_split_row(const CrossArgs& a, int64_t c, int64_t i
     const double syv = a.sy[srow];
     const f32x4 v0 = *(const f32x4*)(a.Syx + srow * a.d + i0);
     const f32x4 v1 = *(const f32x4*)(a.Syx + srow * a.d + i0 + 4);
+    // the 8 columns lie in one head (head widths are multiples of 8)
+    const double keep = cross_head(a.hdim, a.hper, o, i0) ? 0.0 : 1.0;
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
         bf16_t h0, l0, h1, l1;
         const float x0 = e < 4 ? v0[e] : v1[e - 4], x1 = e < 4 ? v0[e + 1] : v1[e - 3];
-        split_bf16(((double)x0 - syv * a.sx[i0 + e] * inv_n) * a.rdg[i0 + e], h0, l0);
-        split_bf16(((double)x1 - syv * a.sx[i0 + e + 1] * inv_n) * a.rdg[i0 + e + 1], h1, l1);
+        split_bf16(keep * (((double)x0 - syv * a.sx[i0 + e] * inv_n) * a.rdg[i0 + e]), h0, l0);
+        split_bf16(keep * (((double)x1 - syv * a.sx[i0 + e + 1] * inv_n) * a.rdg[i0 + e + 1]), h1, l1);
         hi[e / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
         lo[e / 2] = (uint32_t)l0 | ((uint32_t)l1 << 16);
     }
@@ -581,8 +592,9 @@ __global__ __launch_bounds__(256) void k_centre_f64(CrossArgs a, int64_t r0, dou
     const int64_t srow = (int64_t)a.tsel[r / a.dy] * a.dy + r % a.dy;
     const double syv = a.sy[srow];
     double m = 0.0;
+    const int64_t o = r % a.dy;
     for (int64_t i = threadIdx.x; i < a.d; i += 256) {
-        const double v = (double)a.Syx[srow * a.d + i] - syv * a.sx[i] * inv_n;
+        const double v = cross_head(a.hdim, a.hper, o, i) ? 0.0 : (double)a.Syx[srow * a.d + i] - syv * a.sx[i] * inv_n;
         Bf[(int64_t)blockIdx.x * a.d + i] = v;
         m = fmax(m, fabs(v));
     }
@@ -1164,7 +1176,7 @@ rf_status rf_solve_pinv(const rf_gram_desc* desc, const void* d_state, double la
     const double* sx = (const double*)(sp + GL.off_s_x);
     const int64_t* np = (const int64_t*)(sp + GL.off_n);
 
-    hipLaunchKernelGGL(k_centre_gram, dim3(grid_for(d * d)), dim3(256), 0, s, Sxx, sx, np, d, w.C);
+    hipLaunchKernelGGL(k_centre_gram, dim3(grid_for(d * d)), dim3(256), 0, s, Sxx, sx, np, d, w.C, 0, 0);
     RF_TRY(check_launch("rf_solve_pinv: centre"));
     Lambdas lams{};
     lams.v[0] = lambda;
@@ -1221,11 +1233,14 @@ rf_status rf_info_status(const int32_t* info, int32_t n) {
     return RF_OK;
 }
 
-rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, const double* lambdas, int32_t n_lambda,
-                   rf_lambda_mode mode, const int32_t* targets, int32_t n_sel, rf_product product, float* d_W,
-                   void* d_W_lp, float* d_b, int32_t* d_info, double* d_cond, double* d_resid, void* d_ws,
-                   size_t ws_bytes, void* stream) {
-    clear_error();
+}  // extern "C"
+
+namespace rf {
+// rf_solve, and rf_solve_headwise with hdim = the head width (0: dense maps).
+static rf_status solve_impl(const rf_gram_desc* desc, const void* d_state, const double* lambdas, int32_t n_lambda,
+                            rf_lambda_mode mode, const int32_t* targets, int32_t n_sel, rf_product product,
+                            float* d_W, void* d_W_lp, float* d_b, int32_t* d_info, double* d_cond, double* d_resid,
+                            void* d_ws, size_t ws_bytes, void* stream, int32_t hdim) {
     rf_gram_layout_t GL;
     rf_status st = rf_gram_state_layout(desc, &GL);
     if (st != RF_OK) return st;
@@ -1267,7 +1282,9 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, const double* 
     // one D lets the split cross moments serve every lambda)
     hipLaunchKernelGGL(k_zero_int, dim3(1), dim3(64), 0, s, d_info, nl);
     RF_TRY(check_launch("rf_solve: info"));
-    hipLaunchKernelGGL(k_centre_gram, dim3(grid_for(dd), (unsigned)nl), dim3(256), 0, s, Sxx, sx, np, d, w.C);
+    const int32_t hper = (int32_t)dy;
+    hipLaunchKernelGGL(k_centre_gram, dim3(grid_for(dd), (unsigned)nl), dim3(256), 0, s, Sxx, sx, np, d, w.C, hdim,
+                       hper);
     RF_TRY(check_launch("rf_solve: centre"));
     hipLaunchKernelGGL(k_add_lambda, dim3((unsigned)nl), dim3(256), 0, s, w.C, d, lams, rel);
     RF_TRY(check_launch("rf_solve: lambda"));
@@ -1279,7 +1296,7 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, const double* 
     const int64_t rows = (int64_t)n_sel * dy;
     CrossArgs ca{};
     ca.Syx = Syx; ca.sy = sy; ca.sx = sx; ca.np = np; ca.rdg = w.rdg; ca.d = d; ca.dy = dy; ca.rows = rows; ca.Aq = w.Aq;
-    ca.mu_y = w.mu_y;
+    ca.mu_y = w.mu_y; ca.hdim = hdim; ca.hper = hper;
     for (int i = 0; i < n_sel; ++i) ca.tsel[i] = targets[i];
     const int ny = (int)ceil_div(d, 2048);
 
@@ -1324,7 +1341,7 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, const double* 
         if (d_resid) {
             // stationarity residual in fp64: R = W A - B with A rebuilt from the state
             double* Af = w.Cinv + z * dd;
-            hipLaunchKernelGGL(k_centre_gram, dim3(grid_for(dd), 1u), dim3(256), 0, s, Sxx, sx, np, d, Af);
+            hipLaunchKernelGGL(k_centre_gram, dim3(grid_for(dd), 1u), dim3(256), 0, s, Sxx, sx, np, d, Af, hdim, hper);
             RF_TRY(check_launch("rf_solve: residual matrix"));
             Lambdas one{};
             one.v[0] = lambdas[z];
@@ -1348,6 +1365,33 @@ rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, const double* 
         }
     }
     return RF_OK;
+}
+}  // namespace rf
+
+extern "C" {
+
+rf_status rf_solve(const rf_gram_desc* desc, const void* d_state, const double* lambdas, int32_t n_lambda,
+                   rf_lambda_mode mode, const int32_t* targets, int32_t n_sel, rf_product product, float* d_W,
+                   void* d_W_lp, float* d_b, int32_t* d_info, double* d_cond, double* d_resid, void* d_ws,
+                   size_t ws_bytes, void* stream) {
+    clear_error();
+    return solve_impl(desc, d_state, lambdas, n_lambda, mode, targets, n_sel, product, d_W, d_W_lp, d_b, d_info, d_cond,
+                      d_resid, d_ws, ws_bytes, stream, 0);
+}
+
+rf_status rf_solve_headwise(const rf_gram_desc* desc, const void* d_state, const double* lambdas, int32_t n_lambda,
+                            rf_lambda_mode mode, int32_t head_dim, const int32_t* targets, int32_t n_sel,
+                            rf_product product, float* d_W, void* d_W_lp, float* d_b, int32_t* d_info, double* d_cond,
+                            double* d_resid, void* d_ws, size_t ws_bytes, void* stream) {
+    clear_error();
+    RF_REQUIRE(desc, RF_ERR_INVALID_ARG, "rf_solve_headwise: null descriptor");
+    const int64_t dy = gram_dy(desc);
+    RF_REQUIRE(head_dim > 0 && head_dim % 8 == 0 && dy > 0 && dy % head_dim == 0 && desc->d % dy == 0,
+               RF_ERR_INVALID_ARG,
+               "rf_solve_headwise: head_dim must be a positive multiple of 8 dividing the targets' width, and d a "
+               "multiple of that width (whole source layers of the same heads)");
+    return solve_impl(desc, d_state, lambdas, n_lambda, mode, targets, n_sel, product, d_W, d_W_lp, d_b, d_info, d_cond,
+                      d_resid, d_ws, ws_bytes, stream, head_dim);
 }
 
 }  // extern "C"

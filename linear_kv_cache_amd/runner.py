@@ -14,7 +14,8 @@ from . import (RF_LAYOUT_CONTIGUOUS, RF_LAYOUT_PAGED, RF_PRODUCT_AUTO, ComposedF
                rf_fit_r2, rf_fit_r2_workspace_bytes, rf_gram_select,
                rf_gram_accumulate, rf_gram_init,
                rf_gram_state_bytes, rf_gram_state_layout, rf_pack_weights, rf_rope_table, rf_solve,
-               rf_solve_pinv, rf_solve_pinv_workspace_bytes, rf_solve_workspace_bytes, rf_translate)
+               rf_solve_headwise, rf_solve_pinv, rf_solve_pinv_workspace_bytes, rf_solve_workspace_bytes,
+               rf_translate)
 
 
 def device_bytes(n: int, device) -> torch.Tensor:
@@ -109,6 +110,21 @@ class GramState:
         rf_solve(self.desc, self.buf, list(lambdas), mode, list(targets), W, Wlp, b, info, ws, stream,
                  product=product, cond=cond, resid=resid)
         return W, Wlp, b, info, cond, resid
+
+
+def solve_headwise(state: GramState, lam: float, mode: int, head_dim: int, targets: Sequence[int], stream=None,
+                   product: int = RF_PRODUCT_AUTO):
+    """Head-wise maps from one state (rf_solve_headwise): W [n_sel, m, d] fp32 (block-diagonal by
+    head, zero between heads), b [n_sel, m], info [1]."""
+    dev = state.buf.device
+    n_sel = len(targets)
+    W = torch.empty(n_sel, state.dy, state.d, dtype=torch.float32, device=dev)
+    b = torch.empty(n_sel, state.dy, dtype=torch.float32, device=dev)
+    info = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = device_bytes(rf_solve_workspace_bytes(state.desc, n_sel, 1), dev)
+    rf_solve_headwise(state.desc, state.buf, lam, mode, head_dim, list(targets), W, None, b, info, ws, stream,
+                      product=product)
+    return W, b, info
 
 
 def greedy_sources(state: GramState, block_width: int, nu: int, lam: float, mode: int,

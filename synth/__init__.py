@@ -393,10 +393,15 @@ def translator_maps(cfg: TranslateConfig, layer: int, device="cpu"):
 
 def translator_calibration(cfg: TranslateConfig, layer: int, src_rows: torch.Tensor, side: str):
     """Synthetic target cache rows for a closed-form translator fit: Y = S A + 0.1 E with a
-    planted A ~ N(0, 1/d_in) [d_in, kv_width] (x-times-matrix) and E ~ N(0, 1).  The data law
-    of the fit workload, not a step of the method."""
+    planted A ~ N(0, 1/d_in) [d_in, kv_width] (x-times-matrix) and E ~ N(0, 1); for head-wise
+    configurations A links only the same head of every source layer and the target.  The data
+    law of the fit workload, not a step of the method."""
     device = src_rows.device
     A = _randn((cfg.d_in, cfg.kv_width), cfg.seed, "Acal", side, layer, device=device) / cfg.d_in ** 0.5
+    if cfg.maps == "headwise":
+        hi = (torch.arange(cfg.d_in, device=device) % cfg.kv_width) // cfg.head_dim
+        ho = torch.arange(cfg.kv_width, device=device) // cfg.head_dim
+        A = A * (hi[:, None] == ho[None, :])
     E = _randn((src_rows.shape[0], cfg.kv_width), cfg.seed, "Ecal", side, layer, device=device)
     return _tstore(src_rows.float() @ A + 0.1 * E, cfg)
 

@@ -461,3 +461,21 @@ def test_gdn_state_validation_before_enqueue():
         assert e.value.status == status, kw
     call(n_tokens=0)          # no tokens: nothing to do
     call(n_layers=0)          # no layers: nothing to do
+
+
+def test_solve_headwise_validation_before_enqueue():
+    # head_dim must divide the targets' width and d must be whole source layers of that width
+    desc = rf.gram_desc(512, 1, torch.bfloat16, d_out=256)
+    ws = _aligned_bytes(rf.rf_solve_workspace_bytes(desc, 1, 1))
+    info = torch.zeros(1, dtype=torch.int32)
+    for hd in (0, -8, 12, 96, 512):
+        with pytest.raises(rf.RidgeFillError) as e:
+            rf.rf_solve_headwise(desc, 256, 0.1, 0, hd, [0], None, None, None, info, ws, stream=0)
+        assert e.value.status == rf.RF_ERR_INVALID_ARG, hd
+    odd = rf.gram_desc(768, 1, torch.bfloat16, d_out=512)     # 768 is not a multiple of 512
+    with pytest.raises(rf.RidgeFillError) as e:
+        rf.rf_solve_headwise(odd, 256, 0.1, 0, 128, [0], None, None, None, info, ws, stream=0)
+    assert e.value.status == rf.RF_ERR_INVALID_ARG
+    with pytest.raises(rf.RidgeFillError) as e:              # then the rf_solve checks: lambda
+        rf.rf_solve_headwise(desc, 256, -1.0, 0, 128, [0], None, None, None, info, ws, stream=0)
+    assert e.value.status == rf.RF_ERR_INVALID_ARG

@@ -373,3 +373,72 @@ def test_translate_headwise_three_sources():
     # takes nu <= 2); paged, intercepts, ragged range
     cfg = synth.scaled(SMALL_PAGED, name="tr-hw-nu3", n_src=6, n_tgt=5, nu=3, maps="headwise", seed=2011)
     _check(run_translate_case(TranslateCase(cfg, 37, 737, pos0=11, chunk=350)), "bf16 head-wise nu=3 paged")
+
+
+def test_headwise_fit_on_gpu_then_translate():
+    # Closed-form head-wise first stage on the GPU (KV-Lingo page, section 3.1 "Head mixing",
+    # section 3.2): for each target layer and side, rf_solve_headwise on the joint state of the
+    # layer's two source layers (2 x 1024 wide) and its target rows (1024 wide) gives one ridge
+    # fit per head (8 heads of 128: 256 inputs -> 128 outputs each).  Checked head by head against
+    # the oracle's fit of that head's rows, the blocks between heads exactly zero; the maps then
+    # translate a prompt through the head-wise kernel, against the oracle with the same maps.
+    from linear_kv_cache_amd.runner import GramState, Translator, alloc_cache, gather_rows, solve_headwise, \
+        translate_weights
+    cfg = synth.scaled(SMALL_PAGED, name="tr-hw-fit", n_src=3, n_tgt=2, nu=2, paged=False, bias=True,
+                       maps="headwise", seed=2012)
+    N, lam, dev, dh, H, kvw = 4096, 0.1, "cuda", cfg.head_dim, cfg.n_kv_heads, cfg.kv_width
+    E = oracle.relative_depth_sources(cfg.n_src, cfg.n_tgt, cfg.nu)
+    Kc, Vc = synth.source_cache(cfg, N, row_offset=10 ** 6)       # calibration tokens
+    maps_f32, biases, w_errs, b_errs = [], [], [], []
+    for l, e in enumerate(E):
+        Tl, bl = [], []
+        for side, src in (("k", Kc), ("v", Vc)):
+            S = src[:, e[0]:e[0] + cfg.nu].reshape(N, cfg.d_in)
+            Y = synth.translator_calibration(cfg, l, S, side)
+            st = GramState(cfg.d_in, 1, cfg.torch_dtype, dev, d_out=kvw)
+            st.accumulate(S.to(dev), [Y.to(dev)])
+            W, b, info = solve_headwise(st, lam, 0, dh, [0])
+            torch.cuda.synchronize()
+            assert int(info.item()) == 0
+            Wn, bn = f64(W[0]), f64(b[0])
+            W_ref, b_ref = np.zeros((kvw, cfg.d_in)), np.zeros(kvw)
+            Sn, Yn = f64(S), f64(Y)
+            for h in range(H):
+                cols = np.concatenate([s * kvw + h * dh + np.arange(dh) for s in range(cfg.nu)])
+                outs = h * dh + np.arange(dh)
+                T_h, b_h = oracle.fit_translator(Sn[:, cols], Yn[:, outs], lam)
+                W_ref[np.ix_(outs, cols)] = T_h.T
+                b_ref[outs] = b_h
+            off = W_ref == 0
+            assert bool(np.all(Wn[off] == 0.0)), "maps must be zero between heads"
+            w_errs.append(float(np.max(np.abs(Wn - W_ref)) / np.max(np.abs(W_ref))))
+            b_errs.append(float(np.max(np.abs(bn - b_ref)) / np.max(np.abs(b_ref))))
+            Tl.append(W[0])
+            bl.append(b[0])
+        maps_f32.append(Tl)
+        biases.append(bl)
+    log(f"[translate] head-wise fit W errors {np.round(w_errs, 7)}, b errors {np.round(b_errs, 7)} (tol {W_TOL})")
+    assert max(w_errs) <= W_TOL and max(b_errs) <= W_TOL
+    tw = translate_weights(cfg.d_in, cfg.n_kv_heads, cfg.head_dim, torch.bfloat16, [m[0] for m in maps_f32],
+                           [m[1] for m in maps_f32], [b[0] for b in biases], [b[1] for b in biases], headwise=True)
+    T_tok, pos0 = 700, 3
+    Ks, Vs = synth.source_cache(cfg, T_tok)
+    Kd, Vd = Ks.to(dev), Vs.to(dev)
+    cache = alloc_cache(cfg.n_tgt, cfg.n_kv_heads, cfg.head_dim, T_tok, torch.bfloat16, dev)
+    Translator(tw, cfg.rope_base, pos0 + T_tok, dev).translate([Kd[0, e[0]] for e in E], [Vd[0, e[0]] for e in E],
+                                                              cfg.n_src * cfg.d_src, 0, T_tok, pos0, cache)
+    torch.cuda.synchronize()
+    pos = pos0 + np.arange(T_tok, dtype=np.float64)
+    for l, e in enumerate(E):
+        Tk = f64(maps_f32[l][0].cpu().to(torch.bfloat16)).T
+        Tv = f64(maps_f32[l][1].cpu().to(torch.bfloat16)).T
+        sk = f64(Ks[:, e[0]:e[0] + cfg.nu].reshape(T_tok, cfg.d_in))
+        sv = f64(Vs[:, e[0]:e[0] + cfg.nu].reshape(T_tok, cfg.d_in))
+        K_ref, V_ref = oracle.translate_layer(sk, sv, Tk, Tv, f64(biases[l][0]), f64(biases[l][1]), pos,
+                                              cfg.n_kv_heads, cfg.head_dim, cfg.rope_base)
+        K = f64(gather_rows(cache, cache.k[l], 0, T_tok))
+        V = f64(gather_rows(cache, cache.v[l], 0, T_tok))
+        ke = float(np.max(np.abs(K - K_ref)) / np.sqrt(np.mean(K_ref ** 2)))
+        ve = float(np.max(np.abs(V - V_ref)) / np.sqrt(np.mean(V_ref ** 2)))
+        log(f"[translate] head-wise fitted layer {l}: k_err={ke:.3e} v_err={ve:.3e}")
+        assert ke <= KV_TOL_BF16 and ve <= KV_TOL_BF16
