@@ -268,7 +268,8 @@ def gdn_leg(steps: int, stream, dev, n_layers=12, n_heads=16, d_k=128, d_v=128, 
     return {"workload": f"gdn-{n_layers}x{n_heads}h-{d_v}x{d_k}-T{T}", "ms_median": round(ms, 3),
             "tokens_per_s": round(T / (ms / 1e3), 1), "tflops_fp32": round(flop / (ms / 1e3) / 1e12, 2),
             "frac_fp32_vector_peak": round(flop / (ms / 1e3) / 1e12 / FP32_PEAK_TFLOPS, 4),
-            "bound": "latency: each head's state advances one token after the other"}
+            "bound": "vector ALU issue: each head's state advances one token after the other, so the "
+                     "update runs on the vector units (no packed fp32: half the published fp32 peak)"}
 
 
 def fill_only(cfg, steps: int, warmup: int, streamed: bool = False):

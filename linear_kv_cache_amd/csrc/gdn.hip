@@ -5,10 +5,12 @@
 // with k_t optionally L2-normalised.  Row r of S evolves on its own:
 //     s_r <- a s_r + c k,   c = beta (v_r - a (s_r . k)),   a = exp(g)
 // (with normalised keys k -> k rn, rn = 1/sqrt(|k|^2 + eps): c = beta (v_r - a (s_r . k) rn) rn).
-// Each row is held by 8 consecutive lanes (d_k / 8 fp32 registers each, the row's dot product
-// reduced over them by lane exchanges), 32 rows per work-group of 256 threads.  Tokens go in
-// blocks of 32: a block's keys, values, gates and key norms are staged in LDS (fp32) while the
-// next block's rows are in flight in registers, so the sequential token loop reads only LDS.
+// Each row is held by d_k / 8 consecutive lanes (8 fp32 registers each; the row's dot product
+// reduced over them by DPP lane moves, no LDS round trip), 256 / (d_k / 8) rows per
+// work-group of 256 threads.  Tokens go in blocks of 32: a block's keys, values and gates are
+// staged in LDS (keys as stored) while the next block's rows are in flight in registers,
+// so the sequential token loop reads only LDS (a block's reads issued ahead of the chain);
+// each block's key norms are computed once, 8 lanes per token, when it is staged.
 #include <math.h>
 
 #include <string>
@@ -19,9 +21,11 @@
 namespace rf {
 
 constexpr int kGdnMaxLayers = 64;
-constexpr int kGdnLanes = 8;          // lanes per state row
-constexpr int kGdnRows = 256 / kGdnLanes;   // rows per work-group
+constexpr int kGdnElems = 8;          // state elements per lane
 constexpr int kGdnBlock = 32;         // tokens per staged block
+// lanes per state row and rows per work-group for a key width
+__host__ __device__ constexpr int gdn_lanes(int dk) { return dk / kGdnElems; }
+__host__ __device__ constexpr int gdn_rows(int dk) { return 256 / gdn_lanes(dk); }
 
 struct GdnArgs {
     int32_t n_heads, d_v, wg_per_head;
@@ -35,27 +39,53 @@ struct GdnArgs {
     float* S[kGdnMaxLayers];
 };
 
-template <typename T> __device__ inline float ld_elem(const T* p, int64_t i);
-template <> __device__ inline float ld_elem<float>(const float* p, int64_t i) { return p[i]; }
-template <> __device__ inline float ld_elem<bf16_t>(const bf16_t* p, int64_t i) {
-    return __builtin_bit_cast(float, (uint32_t)p[i] << 16);
+// Element i's stored bits, and their fp32 value (kept apart so that a prefetch holds the raw
+// bits and converts them only where they are staged).
+template <typename T> __device__ inline uint32_t ld_bits(const T* p, int64_t i);
+template <> __device__ inline uint32_t ld_bits<float>(const float* p, int64_t i) {
+    return __builtin_bit_cast(uint32_t, p[i]);
+}
+template <> __device__ inline uint32_t ld_bits<bf16_t>(const bf16_t* p, int64_t i) { return (uint32_t)p[i]; }
+template <typename T> __device__ inline float bits_f32(uint32_t b) {
+    return sizeof(T) == 2 ? __builtin_bit_cast(float, b << 16) : __builtin_bit_cast(float, b);
+}
+
+// A DPP lane move within each row of 16 lanes (dpp_ctrl CTRL), every lane a source.
+template <int CTRL>
+__device__ inline float dpp_move(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+// The sum over each group of LANES (8 or 16) consecutive lanes, in every lane of the group:
+// lane ^ 1, lane ^ 2 (quad permutes), then the mirrored lane of the other quad (half-row
+// mirror) and, for 16, of the other half-row (row mirror).  A fixed order.
+template <int LANES>
+__device__ inline float group_sum(float x) {
+    x += dpp_move<0xB1>(x);     // quad_perm [1, 0, 3, 2]
+    x += dpp_move<0x4E>(x);     // quad_perm [2, 3, 0, 1]
+    x += dpp_move<0x141>(x);    // row_half_mirror
+    if constexpr (LANES == 16) x += dpp_move<0x140>(x);   // row_mirror
+    return x;
 }
 
 template <typename T, int DK>
-__global__ __launch_bounds__(256) void k_gdn_state(GdnArgs a) {
-    constexpr int E = DK / kGdnLanes;   // state elements per lane
-    // per block: keys [32][DK], values [32][32 rows of this work-group], gate a, beta, 1/|k|
-    __shared__ float sk[2][kGdnBlock][DK];
-    __shared__ float sv[2][kGdnBlock][kGdnRows];
-    __shared__ float sa[2][kGdnBlock], sb[2][kGdnBlock], sn[2][kGdnBlock];
+__device__ inline void gdn_state(const GdnArgs& a) {
+    constexpr int E = kGdnElems, LANES = gdn_lanes(DK), ROWS = gdn_rows(DK);
+    static_assert(LANES == 8 || LANES == 16, "8 or 16 lanes per state row");
+    // the staged block: keys [32][DK] (fp32), values [32][ROWS rows of this work-group], gate a,
+    // beta, key norm factor.  One buffer: the next block waits in registers until every lane is
+    // done with this one.
+    __shared__ __attribute__((aligned(16))) float sk[kGdnBlock][DK];
+    __shared__ float sv[kGdnBlock][ROWS];
+    __shared__ float sa[kGdnBlock], sb[kGdnBlock], sn[kGdnBlock];
     const int per_layer = a.n_heads * a.wg_per_head;
     const int l = blockIdx.x / per_layer;
     const int rem = blockIdx.x - l * per_layer;
     const int h = rem / a.wg_per_head;
-    const int r0 = (rem - h * a.wg_per_head) * kGdnRows;
+    const int r0 = (rem - h * a.wg_per_head) * ROWS;
     const int t = threadIdx.x;
-    const int row = r0 + t / kGdnLanes;          // this lane's state row
-    const int j0 = (t % kGdnLanes) * E;          // and its columns
+    const int rl = t / LANES;                    // this lane's state row within the work-group
+    const int row = r0 + rl;
+    const int j0 = (t % LANES) * E;              // and its columns
     const bool live = row < a.d_v;
     const T* K = (const T*)a.k[l] + (int64_t)h * DK;
     const T* V = (const T*)a.v[l] + (int64_t)h * a.d_v;
@@ -67,85 +97,110 @@ __global__ __launch_bounds__(256) void k_gdn_state(GdnArgs a) {
     for (int e = 0; e < E; ++e) s[e] = live ? S[e] : 0.f;
 
     // staging: key elements of the block (32 * DK), one value per (token, row), per-token scalars
-    constexpr int KPER = kGdnBlock * DK / 256;
-    float rk[KPER], rv[kGdnBlock * kGdnRows / 256], rg = 0.f, rb = 0.f;
+    constexpr int KVEC = 16 / (int)sizeof(T);                 // key elements per 16-byte load
+    constexpr int KPER = kGdnBlock * DK / (256 * KVEC);       // key loads per thread per block
+    constexpr int VPER = kGdnBlock * ROWS / 256;
+    // Every load is issued unconditionally at an in-range index (tokens past the range read the
+    // last token, rows past d_v the last row) and masked when staged: a load guarded by a
+    // branch would be waited for on the spot instead of under the next block's token loop.
+    u32x4 rk[KPER];
+    uint32_t rv[VPER];
+    float rg = 0.f, rb = 0.f;
     auto fetch = [&](int64_t tb) {
 #pragma unroll
         for (int i = 0; i < KPER; ++i) {
-            const int e = t + 256 * i, tt = e / DK, jj = e % DK;
-            rk[i] = tb + tt < a.T ? ld_elem<T>(K, (tb + tt) * a.ld_k + jj) : 0.f;
+            const int e = (t + 256 * i) * KVEC, tt = e / DK, jj = e % DK;
+            const int64_t tok = tb + tt < a.T ? tb + tt : a.T - 1;
+            rk[i] = *(const u32x4*)(K + tok * a.ld_k + jj);
         }
 #pragma unroll
-        for (int i = 0; i < kGdnBlock * kGdnRows / 256; ++i) {
-            const int e = t + 256 * i, tt = e / kGdnRows, rr = e % kGdnRows;
-            rv[i] = (tb + tt < a.T && r0 + rr < a.d_v) ? ld_elem<T>(V, (tb + tt) * a.ld_v + r0 + rr) : 0.f;
+        for (int i = 0; i < VPER; ++i) {
+            const int e = t + 256 * i, tt = e / ROWS, rr = e % ROWS;
+            const int64_t tok = tb + tt < a.T ? tb + tt : a.T - 1;
+            const int r = r0 + rr < a.d_v ? r0 + rr : a.d_v - 1;
+            rv[i] = ld_bits<T>(V, tok * a.ld_v + r);
+        }
+        if (t < kGdnBlock) {
+            const int64_t tok = tb + t < a.T ? tb + t : a.T - 1;
+            rg = G[tok * a.n_heads];
+            rb = B[tok * a.n_heads];
+        }
+    };
+    auto stage = [&](int64_t tb) {
+#pragma unroll
+        for (int i = 0; i < KPER; ++i) {
+            const int e = (t + 256 * i) * KVEC;
+            const u32x4 v = tb + e / DK < a.T ? rk[i] : u32x4{0u, 0u, 0u, 0u};
+            float* dst = &sk[e / DK][e % DK];
+            if constexpr (sizeof(T) == 2) {
+                *(f32x4*)dst = f32x4{__builtin_bit_cast(float, v[0] << 16), __builtin_bit_cast(float, v[0] & 0xffff0000u),
+                                     __builtin_bit_cast(float, v[1] << 16), __builtin_bit_cast(float, v[1] & 0xffff0000u)};
+                *(f32x4*)(dst + 4) =
+                    f32x4{__builtin_bit_cast(float, v[2] << 16), __builtin_bit_cast(float, v[2] & 0xffff0000u),
+                          __builtin_bit_cast(float, v[3] << 16), __builtin_bit_cast(float, v[3] & 0xffff0000u)};
+            } else {
+                *(u32x4*)dst = v;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VPER; ++i) {
+            const int e = t + 256 * i;
+            sv[e / ROWS][e % ROWS] = tb + e / ROWS < a.T ? bits_f32<T>(rv[i]) : 0.f;
         }
         if (t < kGdnBlock) {
             const bool ok = tb + t < a.T;
-            rg = ok ? G[(tb + t) * a.n_heads] : 0.f;
-            rb = ok ? B[(tb + t) * a.n_heads] : 0.f;
+            sa[t] = ok ? expf(rg) : 1.f;
+            sb[t] = ok ? rb : 0.f;
         }
     };
-    auto stage = [&](int buf) {
+    // key norm factors of a staged block: 8 lanes per token, each summing DK / 8 squares, then
+    // over the 8 lanes; 1 / sqrt(|k|^2 + eps), 1 without normalisation, 0 past the range
+    auto norms = [&](int64_t tb) {
+        constexpr int PART = DK / 8;
+        const int tt = t / 8, p0 = (t % 8) * PART;
+        float q = 0.f;
 #pragma unroll
-        for (int i = 0; i < KPER; ++i) {
-            const int e = t + 256 * i;
-            sk[buf][e / DK][e % DK] = rk[i];
+        for (int c = 0; c < PART; c += 4) {
+            const f32x4 v = *(const f32x4*)&sk[tt][p0 + c];
+            q += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
         }
-#pragma unroll
-        for (int i = 0; i < kGdnBlock * kGdnRows / 256; ++i) {
-            const int e = t + 256 * i;
-            sv[buf][e / kGdnRows][e % kGdnRows] = rv[i];
-        }
-        if (t < kGdnBlock) {
-            sa[buf][t] = expf(rg);
-            sb[buf][t] = rb;
-        }
+        q = group_sum<8>(q);
+        if (t % 8 == 0) sn[tt] = tb + tt >= a.T ? 0.f : (a.normalise ? 1.0f / sqrtf(q + a.eps) : 1.0f);
     };
     const int n_blocks = (int)((a.T + kGdnBlock - 1) / kGdnBlock);
     fetch(0);
     stage(0);
     __syncthreads();
+    norms(0);
+    __syncthreads();
     for (int blk = 0; blk < n_blocks; ++blk) {
-        const int buf = blk & 1;
         const int64_t tb = (int64_t)blk * kGdnBlock;
         if (blk + 1 < n_blocks) fetch(tb + kGdnBlock);
-        // the block's key norms (a wave's lane per token; the other lanes idle here)
-        if (t < kGdnBlock) {
-            float q = 0.f;
-            if (a.normalise) {
-#pragma unroll 8
-                for (int jj = 0; jj < DK; ++jj) q += sk[buf][t][jj] * sk[buf][t][jj];
-                sn[buf][t] = 1.0f / sqrtf(q + a.eps);
-            } else {
-                sn[buf][t] = 1.0f;
-            }
-        }
-        __syncthreads();
-        const int nt = (int)((a.T - tb) < kGdnBlock ? (a.T - tb) : kGdnBlock);
-        for (int tt = 0; tt < nt; ++tt) {
-            float k[E];
+        // a fixed trip count, unrolled, so each token's LDS reads are issued ahead of the chain.
+        // Tokens past the range were staged as zero keys and values with gate 1, strength 0
+        // and norm factor 0: their update is exactly s <- s.
+#pragma unroll 4
+        for (int tt = 0; tt < kGdnBlock; ++tt) {
+            const f32x4 k0 = *(const f32x4*)&sk[tt][j0], k1 = *(const f32x4*)&sk[tt][j0 + 4];
+            const float k[E] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+            const float av = sa[tt], bv = sb[tt], rn = sn[tt], vr = sv[tt][rl];
+            // the row's dot product: two partial sums, then over the row's lanes
+            float d0 = s[0] * k[0], d1 = s[1] * k[1];
 #pragma unroll
-            for (int e = 0; e < E; e += 4) {
-                const f32x4 q4 = *(const f32x4*)&sk[buf][tt][j0 + e];
-                k[e] = q4[0]; k[e + 1] = q4[1]; k[e + 2] = q4[2]; k[e + 3] = q4[3];
+            for (int e = 2; e < E; e += 2) {
+                d0 += s[e] * k[e];
+                d1 += s[e + 1] * k[e + 1];
             }
-            float dot = 0.f;
-#pragma unroll
-            for (int e = 0; e < E; ++e) dot += s[e] * k[e];
-            // the row's dot product over its 8 lanes (fixed order: xor 1, 2, 4)
-            dot += __shfl_xor(dot, 1);
-            dot += __shfl_xor(dot, 2);
-            dot += __shfl_xor(dot, 4);
-            const float av = sa[buf][tt], bv = sb[buf][tt], rn = sn[buf][tt];
-            const float vr = sv[buf][tt][t / kGdnLanes];
+            const float dot = group_sum<LANES>(d0 + d1);
             const float c = bv * (vr - av * dot * rn) * rn;
 #pragma unroll
             for (int e = 0; e < E; ++e) s[e] = av * s[e] + c * k[e];
         }
         __syncthreads();   // every lane is done with this block's buffer
         if (blk + 1 < n_blocks) {
-            stage(buf ^ 1);
+            stage(tb + kGdnBlock);
+            __syncthreads();
+            norms(tb + kGdnBlock);
             __syncthreads();
         }
     }
@@ -153,6 +208,17 @@ __global__ __launch_bounds__(256) void k_gdn_state(GdnArgs a) {
 #pragma unroll
         for (int e = 0; e < E; ++e) S[e] = s[e];
     }
+}
+
+// Six waves per SIMD for bf16 keys (at most 85 registers): 16-row work-groups of a 16-head set
+// of layers are then resident at once, not in one and a half rounds.
+template <int DK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void k_gdn_state_bf16(GdnArgs a) {
+    gdn_state<bf16_t, DK>(a);
+}
+template <int DK>
+__global__ __launch_bounds__(256) void k_gdn_state_f32(GdnArgs a) {
+    gdn_state<float, DK>(a);
 }
 
 }  // namespace rf
@@ -177,15 +243,18 @@ rf_status rf_gdn_state(const rf_gdn_desc* desc, int32_t n_layers, const void* co
     RF_REQUIRE(desc->eps >= 0.f && isfinite(desc->eps), RF_ERR_INVALID_ARG, "rf_gdn_state: eps must be finite and >= 0");
     RF_REQUIRE(ld_k >= (int64_t)desc->n_heads * desc->d_k && ld_v >= (int64_t)desc->n_heads * desc->d_v,
                RF_ERR_INVALID_ARG, "rf_gdn_state: key and value rows shorter than n_heads * d_k (d_v)");
+    RF_REQUIRE(ld_k * (int64_t)elem_bytes(desc->dtype) % 16 == 0, RF_ERR_INVALID_ARG,
+               "rf_gdn_state: the key row stride must be a multiple of 16 bytes");
     if (n_layers == 0 || n_tokens == 0) return RF_OK;
     RF_REQUIRE(d_k && d_v && d_g && d_beta && d_state, RF_ERR_INVALID_ARG, "rf_gdn_state: null pointer argument");
     for (int l = 0; l < n_layers; ++l) {
         RF_REQUIRE(d_k[l] && d_v[l] && d_g[l] && d_beta[l] && d_state[l], RF_ERR_INVALID_ARG,
                    "rf_gdn_state: null per-layer pointer");
-        RF_REQUIRE(aligned(d_state[l], 16), RF_ERR_INVALID_ARG, "rf_gdn_state: states must be 16-byte aligned");
+        RF_REQUIRE(aligned(d_state[l], 16) && aligned(d_k[l], 16), RF_ERR_INVALID_ARG,
+                   "rf_gdn_state: states and key rows must be 16-byte aligned");
     }
     GdnArgs a{};
-    a.n_heads = desc->n_heads; a.d_v = desc->d_v; a.wg_per_head = (int32_t)ceil_div(desc->d_v, kGdnRows);
+    a.n_heads = desc->n_heads; a.d_v = desc->d_v; a.wg_per_head = (int32_t)ceil_div(desc->d_v, gdn_rows(desc->d_k));
     a.T = n_tokens; a.ld_k = ld_k; a.ld_v = ld_v; a.normalise = desc->normalise_k; a.eps = desc->eps;
     for (int l = 0; l < n_layers; ++l) {
         a.k[l] = d_k[l]; a.v[l] = d_v[l]; a.g[l] = d_g[l]; a.beta[l] = d_beta[l]; a.S[l] = d_state[l];
@@ -193,11 +262,11 @@ rf_status rf_gdn_state(const rf_gdn_desc* desc, int32_t n_layers, const void* co
     const dim3 grid((unsigned)(n_layers * desc->n_heads * a.wg_per_head));
     hipStream_t s = (hipStream_t)stream;
     if (desc->dtype == RF_BF16) {
-        if (desc->d_k == 128) hipLaunchKernelGGL((k_gdn_state<bf16_t, 128>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((k_gdn_state<bf16_t, 64>), grid, dim3(256), 0, s, a);
+        if (desc->d_k == 128) hipLaunchKernelGGL((k_gdn_state_bf16<128>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((k_gdn_state_bf16<64>), grid, dim3(256), 0, s, a);
     } else {
-        if (desc->d_k == 128) hipLaunchKernelGGL((k_gdn_state<float, 128>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((k_gdn_state<float, 64>), grid, dim3(256), 0, s, a);
+        if (desc->d_k == 128) hipLaunchKernelGGL((k_gdn_state_f32<128>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((k_gdn_state_f32<64>), grid, dim3(256), 0, s, a);
     }
     return check_launch("rf_gdn_state");
 }
