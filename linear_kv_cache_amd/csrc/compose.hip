@@ -31,8 +31,26 @@ namespace rf {
 
 constexpr int kCT = 256;   // tile
 
+constexpr int kComposeGroup = 32;   // layers per launch at most
+
+// Per-layer operands of the preparation launches (layer g = the launch's last grid index).
+struct PrepArgs {
+    const bf16_t* W[kComposeGroup];      // packed map
+    const bf16_t* Wk[kComposeGroup];
+    const bf16_t* Wv[kComposeGroup];
+    const float* gamma[kComposeGroup];
+    const float* b[kComposeGroup];
+    bf16_t* A2[kComposeGroup];
+    bf16_t* B2[kComposeGroup];
+    float* ck[kComposeGroup];
+    float* cv[kComposeGroup];
+    float* q[kComposeGroup];
+};
+
 // A2 = [W^T | W^T] from the packed map, one 64 x 64 block per work-group through LDS.
-__global__ __launch_bounds__(256) void k_unpack_transpose(const bf16_t* Wp, int64_t d, bf16_t* A2) {
+__global__ __launch_bounds__(256) void k_unpack_transpose(PrepArgs pa, int64_t d) {
+    const bf16_t* Wp = pa.W[blockIdx.z];
+    bf16_t* A2 = pa.A2[blockIdx.z];
     __shared__ uint16_t tile[64][64 + 2];   // [o][i]
     const int64_t ib = blockIdx.x, ob = blockIdx.y;
     for (int c = threadIdx.x; c < 512; c += 256) {
@@ -61,9 +79,12 @@ __device__ inline float bf16_to_f32(uint32_t bits16) { return __builtin_bit_cast
 // One work-group per packed row p of [W_k; W_v]: B2[p] = [hi | lo] of the row scaled by gamma
 // (the product rounded to fp32, then split into two bf16 parts), and the row's intercept
 // c = sum_o W[p][o] gamma_o b_o (fp64, fixed order) at its source row's index.
-__global__ __launch_bounds__(256) void k_kv_split(const bf16_t* Wk, const bf16_t* Wv, const float* gamma,
-                                                  const float* b, int64_t d, int kvw, int hd, bf16_t* B2,
-                                                  float* ck, float* cv) {
+__global__ __launch_bounds__(256) void k_kv_split(PrepArgs pa, int64_t d, int kvw, int hd) {
+    const int g = blockIdx.y;
+    const bf16_t *Wk = pa.Wk[g], *Wv = pa.Wv[g];
+    const float *gamma = pa.gamma[g], *b = pa.b[g];
+    bf16_t* B2 = pa.B2[g];
+    float *ck = pa.ck[g], *cv = pa.cv[g];
     __shared__ double red[256];
     const int p = blockIdx.x;
     const bool is_k = p < kvw;
@@ -101,8 +122,6 @@ __global__ __launch_bounds__(256) void k_kv_split(const bf16_t* Wk, const bf16_t
         (is_k ? ck : cv)[f] = (float)red[0];
     }
 }
-
-constexpr int kComposeGroup = 32;   // layers per product launch at most
 
 struct ComposeArgs {
     int64_t d;
@@ -182,7 +201,10 @@ __global__ __launch_bounds__(PipeGemm::kThr) void k_compose_gemm(ComposeArgs a) 
 
 // q[i] = 2 sum_o W[o][i] b[o] (one wave per i, reading row i of W^T), q[2d] = |b|^2 (the last
 // work-group); fp64 sums in a fixed order.
-__global__ __launch_bounds__(256) void k_qvec(const bf16_t* A2, const float* b, int64_t d, float* q) {
+__global__ __launch_bounds__(256) void k_qvec(PrepArgs pa, int64_t d) {
+    const bf16_t* A2 = pa.A2[blockIdx.y];
+    const float* b = pa.b[blockIdx.y];
+    float* q = pa.q[blockIdx.y];
     __shared__ double red[256];
     if ((int64_t)blockIdx.x * 4 >= d) {
         double s = 0.0;
@@ -264,23 +286,26 @@ rf_status rf_fill_compose(const rf_fill_weights* w, int32_t n_layers, void* cons
     ca.n_tiles = ca.n_t + (int32_t)(ca.nf * (2 * kvw / kCT));
     for (int l0 = 0; l0 < n_layers; l0 += group) {
         const int gsz = std::min(group, n_layers - l0);
+        PrepArgs pa{};
         for (int g = 0; g < gsz; ++g) {
             const int l = l0 + g;
             bf16_t* A2 = (bf16_t*)((char*)d_ws + (size_t)g * slot);
             bf16_t* B2 = (bf16_t*)((char*)A2 + off_b2);
-            hipLaunchKernelGGL(k_unpack_transpose, dim3((unsigned)(d / 64), (unsigned)(d / 64)), dim3(256), 0, s,
-                               (const bf16_t*)w->W_map[l], d, A2);
-            RF_TRY_LAUNCH("rf_fill_compose: transpose");
-            hipLaunchKernelGGL(k_kv_split, dim3((unsigned)(2 * kvw)), dim3(256), 0, s, (const bf16_t*)w->W_k[l],
-                               (const bf16_t*)w->W_v[l], w->gamma[l], w->b_map[l], d, (int)kvw, w->head_dim, B2,
-                               c_k[l], c_v[l]);
-            RF_TRY_LAUNCH("rf_fill_compose: scaled projections");
-            hipLaunchKernelGGL(k_qvec, dim3((unsigned)(d / 4 + 1)), dim3(256), 0, s, (const bf16_t*)A2, w->b_map[l], d,
-                               q[l]);
-            RF_TRY_LAUNCH("rf_fill_compose: sum-of-squares vector");
+            pa.W[g] = (const bf16_t*)w->W_map[l]; pa.Wk[g] = (const bf16_t*)w->W_k[l];
+            pa.Wv[g] = (const bf16_t*)w->W_v[l]; pa.gamma[g] = w->gamma[l]; pa.b[g] = w->b_map[l];
+            pa.A2[g] = A2; pa.B2[g] = B2; pa.ck[g] = c_k[l]; pa.cv[g] = c_v[l]; pa.q[g] = q[l];
             ca.A2[g] = A2; ca.B2[g] = B2;
             ca.T[g] = (bf16_t*)T[l]; ca.gdiag[g] = q[l] + d; ca.Mk[g] = (bf16_t*)M_k[l]; ca.Mv[g] = (bf16_t*)M_v[l];
         }
+        // the layers' preparations, each one launch over the group
+        hipLaunchKernelGGL(k_unpack_transpose, dim3((unsigned)(d / 64), (unsigned)(d / 64), (unsigned)gsz), dim3(256),
+                           0, s, pa, d);
+        RF_TRY_LAUNCH("rf_fill_compose: transpose");
+        hipLaunchKernelGGL(k_kv_split, dim3((unsigned)(2 * kvw), (unsigned)gsz), dim3(256), 0, s, pa, d, (int)kvw,
+                           w->head_dim);
+        RF_TRY_LAUNCH("rf_fill_compose: scaled projections");
+        hipLaunchKernelGGL(k_qvec, dim3((unsigned)(d / 4 + 1), (unsigned)gsz), dim3(256), 0, s, pa, d);
+        RF_TRY_LAUNCH("rf_fill_compose: sum-of-squares vector");
         hipLaunchKernelGGL(k_compose_gemm, dim3((unsigned)(gsz * ca.n_tiles)), dim3(PipeGemm::kThr), 0, s, ca);
         RF_TRY_LAUNCH("rf_fill_compose: products");
     }
