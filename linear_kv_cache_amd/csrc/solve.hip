@@ -581,65 +581,74 @@ __global__ void k_mirror_full(const double* Ainv_lower, int64_t d, double* Afull
 }
 
 // Centred cross moments in fp64 for rows [r0, r0 + nr) of the selected targets' outputs, one
-// work-group per row: Bf[r - r0][i] = S_yx[row][i] - s_y[row] s_x[i] / n; bmax (may be null)
-// receives max_i |Bf| of each row at its global row index.
-__global__ __launch_bounds__(256) void k_centre_f64(CrossArgs a, int64_t r0, double* Bf, double* bmax,
+// row per work-group at a time (rows strided by the grid, so a gated-off launch stays small):
+// Bf[r - r0][i] = S_yx[row][i] - s_y[row] s_x[i] / n; bmax (may be null) receives max_i |Bf| of
+// each row at its global row index.
+__global__ __launch_bounds__(256) void k_centre_f64(CrossArgs a, int64_t r0, int64_t nr, double* Bf, double* bmax,
                                                     const int32_t* gate) {
     if (gate && *gate == 0) return;
     __shared__ double red[256];
-    const int64_t r = r0 + blockIdx.x;
     const double inv_n = 1.0 / (double)*a.np;
-    const int64_t srow = (int64_t)a.tsel[r / a.dy] * a.dy + r % a.dy;
-    const double syv = a.sy[srow];
-    double m = 0.0;
-    const int64_t o = r % a.dy;
-    for (int64_t i = threadIdx.x; i < a.d; i += 256) {
-        const double v = cross_head(a.hdim, a.hper, o, i) ? 0.0 : (double)a.Syx[srow * a.d + i] - syv * a.sx[i] * inv_n;
-        Bf[(int64_t)blockIdx.x * a.d + i] = v;
-        m = fmax(m, fabs(v));
-    }
-    if (!bmax) return;
-    red[threadIdx.x] = m;
-    __syncthreads();
-    for (int h = 128; h > 0; h >>= 1) {
-        if ((int)threadIdx.x < h) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + h]);
+    for (int64_t rl = blockIdx.x; rl < nr; rl += gridDim.x) {
+        const int64_t r = r0 + rl;
+        const int64_t srow = (int64_t)a.tsel[r / a.dy] * a.dy + r % a.dy;
+        const double syv = a.sy[srow];
+        double m = 0.0;
+        const int64_t o = r % a.dy;
+        for (int64_t i = threadIdx.x; i < a.d; i += 256) {
+            const double v =
+                cross_head(a.hdim, a.hper, o, i) ? 0.0 : (double)a.Syx[srow * a.d + i] - syv * a.sx[i] * inv_n;
+            Bf[rl * a.d + i] = v;
+            m = fmax(m, fabs(v));
+        }
+        if (!bmax) continue;
+        red[threadIdx.x] = m;
         __syncthreads();
+        for (int h = 128; h > 0; h >>= 1) {
+            if ((int)threadIdx.x < h) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + h]);
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) bmax[r] = red[0];
+        __syncthreads();   // red is rewritten by the next row
     }
-    if (threadIdx.x == 0) bmax[r] = red[0];
 }
 
-// The maps from the fp64 product, rows [r0, r0 + nr) (one work-group per row): W (fp32,
-// may be null), the packed bf16 copy (may be null), and the intercept
-// b = s_y / n - sum_j W[j] s_x[j] / n summed in fp64 in a fixed order (may be null).
-__global__ __launch_bounds__(256) void k_store_f64(const double* Wf, int64_t r0, CrossArgs a, float* W, bf16_t* Wlp,
-                                                   float* b, const int32_t* gate) {
+// The maps from the fp64 product, rows [r0, r0 + nr) (one row per work-group at a time, rows
+// strided by the grid): W (fp32, may be null), the packed bf16 copy (may be null), and the
+// intercept b = s_y / n - sum_j W[j] s_x[j] / n summed in fp64 in a fixed order (may be null).
+__global__ __launch_bounds__(256) void k_store_f64(const double* Wf, int64_t r0, int64_t nr, CrossArgs a, float* W,
+                                                   bf16_t* Wlp, float* b, const int32_t* gate) {
     if (gate && *gate == 0) return;
     __shared__ double red[256];
-    const int64_t r = r0 + blockIdx.x, d = a.d;
+    const int64_t d = a.d;
     const double inv_n = 1.0 / (double)*a.np;
-    const double* wr = Wf + (int64_t)blockIdx.x * d;
-    const int64_t wl_base = (r >> 8) * 256 * d + packed_row_part((int)(r & 255));
-    double dot = 0.0;
-    for (int64_t j = 4 * threadIdx.x; j < d; j += 1024) {
-        const double w0 = wr[j], w1 = wr[j + 1], w2 = wr[j + 2], w3 = wr[j + 3];
-        dot += w0 * a.sx[j] + w1 * a.sx[j + 1] + w2 * a.sx[j + 2] + w3 * a.sx[j + 3];
-        // the bf16 map is the fp32 map rounded once more (not the double rounded once)
-        const float f0 = opaque_f32((float)w0), f1 = opaque_f32((float)w1);
-        const float f2 = opaque_f32((float)w2), f3 = opaque_f32((float)w3);
-        if (W) *(f32x4*)(W + r * d + j) = f32x4{f0, f1, f2, f3};
-        if (Wlp)
-            *(u32x2*)(Wlp + wl_base + packed_col_part((int)j)) = u32x2{pack_bf16x2(f0, f1), pack_bf16x2(f2, f3)};
-    }
-    if (!b) return;
-    red[threadIdx.x] = dot;
-    __syncthreads();
-    for (int h = 128; h > 0; h >>= 1) {
-        if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+    for (int64_t rl = blockIdx.x; rl < nr; rl += gridDim.x) {
+        const int64_t r = r0 + rl;
+        const double* wr = Wf + rl * d;
+        const int64_t wl_base = (r >> 8) * 256 * d + packed_row_part((int)(r & 255));
+        double dot = 0.0;
+        for (int64_t j = 4 * threadIdx.x; j < d; j += 1024) {
+            const double w0 = wr[j], w1 = wr[j + 1], w2 = wr[j + 2], w3 = wr[j + 3];
+            dot += w0 * a.sx[j] + w1 * a.sx[j + 1] + w2 * a.sx[j + 2] + w3 * a.sx[j + 3];
+            // the bf16 map is the fp32 map rounded once more (not the double rounded once)
+            const float f0 = opaque_f32((float)w0), f1 = opaque_f32((float)w1);
+            const float f2 = opaque_f32((float)w2), f3 = opaque_f32((float)w3);
+            if (W) *(f32x4*)(W + r * d + j) = f32x4{f0, f1, f2, f3};
+            if (Wlp)
+                *(u32x2*)(Wlp + wl_base + packed_col_part((int)j)) = u32x2{pack_bf16x2(f0, f1), pack_bf16x2(f2, f3)};
+        }
+        if (!b) continue;
+        red[threadIdx.x] = dot;
         __syncthreads();
-    }
-    if (threadIdx.x == 0) {
-        const int64_t srow = (int64_t)a.tsel[r / a.dy] * a.dy + r % a.dy;
-        b[r] = (float)((a.sy[srow] - red[0]) * inv_n);
+        for (int h = 128; h > 0; h >>= 1) {
+            if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) {
+            const int64_t srow = (int64_t)a.tsel[r / a.dy] * a.dy + r % a.dy;
+            b[r] = (float)((a.sy[srow] - red[0]) * inv_n);
+        }
+        __syncthreads();   // red is rewritten by the next row
     }
 }
 
@@ -765,6 +774,11 @@ static inline unsigned grid_for(int64_t n, int64_t per = 256) {
     return (unsigned)std::max<int64_t>(1, std::min<int64_t>(ceil_div(n, per), 1 << 16));
 }
 
+// Work-groups of the row-strided fp64 route kernels: two per CU, few enough that a launch whose
+// gate is off costs little.
+constexpr unsigned kRowGrid = 512;
+static inline unsigned row_grid(int64_t nr) { return (unsigned)std::max<int64_t>(1, std::min<int64_t>(nr, kRowGrid)); }
+
 // 128 x 128 tiles only when they fill two rounds of the CUs at two work-groups each, else
 // 64 x 64 tiles: more work-groups in flight at half the operand reuse (measured on the d=4096
 // solve: 1024 tiles or more for 128 x 128 took 11.0 ms, 512 took 11.5 ms, and 128 x 128 tiles
@@ -883,16 +897,16 @@ static rf_status solve_products(hipStream_t s, const SolveWs& w, int z, int64_t 
         // the fp64 product, written over the split one when the route says so:
         // W = B A^-1 with the full A^-1 (mirrored into the free Z buffer), rb rows at a time
         double* Af = w.Cinv + z * dd;
-        hipLaunchKernelGGL(k_mirror_full, dim3(grid_for(dd)), dim3(256), 0, s, (const double*)Cz, d, Af,
-                           (const int32_t*)gz);
+        hipLaunchKernelGGL(k_mirror_full, dim3(std::min(grid_for(dd), kRowGrid * 4)), dim3(256), 0, s,
+                           (const double*)Cz, d, Af, (const int32_t*)gz);
         RF_TRY(check_launch("rf_solve: fp64 inverse"));
         for (int64_t r0 = 0; r0 < rows; r0 += w.rb) {
             const int64_t nr = std::min<int64_t>(w.rb, rows - r0);
-            hipLaunchKernelGGL(k_centre_f64, dim3((unsigned)nr), dim3(256), 0, s, ca, r0, w.Bf, (double*)nullptr,
-                               (const int32_t*)gz);
+            hipLaunchKernelGGL(k_centre_f64, dim3(row_grid(nr)), dim3(256), 0, s, ca, r0, nr, w.Bf,
+                               (double*)nullptr, (const int32_t*)gz);
             RF_TRY(check_launch("rf_solve: fp64 cross moments"));
             RF_TRY(dgemm<false>(s, nr, d, d, 1.0, w.Bf, d, Af, d, 0.0, w.Wf, d, kFull, 1, 0, 0, 0, gz));
-            hipLaunchKernelGGL(k_store_f64, dim3((unsigned)nr), dim3(256), 0, s, (const double*)w.Wf, r0, ca, Wz,
+            hipLaunchKernelGGL(k_store_f64, dim3(row_grid(nr)), dim3(256), 0, s, (const double*)w.Wf, r0, nr, ca, Wz,
                                Wlpz, bz, (const int32_t*)gz);
             RF_TRY(check_launch("rf_solve: fp64 maps"));
         }
@@ -1349,7 +1363,7 @@ static rf_status solve_impl(const rf_gram_desc* desc, const void* d_state, const
             RF_TRY(check_launch("rf_solve: residual lambda"));
             for (int64_t r0 = 0; r0 < rows; r0 += w.rb) {
                 const int64_t nr = std::min<int64_t>(w.rb, rows - r0);
-                hipLaunchKernelGGL(k_centre_f64, dim3((unsigned)nr), dim3(256), 0, s, ca, r0, w.Bf, w.bmax,
+                hipLaunchKernelGGL(k_centre_f64, dim3(row_grid(nr)), dim3(256), 0, s, ca, r0, nr, w.Bf, w.bmax,
                                    (const int32_t*)nullptr);
                 RF_TRY(check_launch("rf_solve: residual cross moments"));
                 hipLaunchKernelGGL(k_widen_rows, dim3(grid_for(nr * d)), dim3(256), 0, s, (const float*)Wz, r0, nr, d,
