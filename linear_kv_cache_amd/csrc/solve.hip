@@ -44,13 +44,12 @@ typedef double f64x2 __attribute__((ext_vector_type(2)));
 // ``gate`` (device, may be null): the launch does nothing when *gate is 0.
 enum { kFull = 0, kLowerOnly = 1, kUpperOperands = 2, kUpperA = 4, kUpperB = 8 };
 
-template <bool BT, int BM = 128>
-__global__ __launch_bounds__(256, 2) void k_dgemm(int64_t M, int64_t N, int64_t K, double alpha, const double* A,
-                                               int64_t lda, const double* B, int64_t ldb, double beta, double* C,
-                                               int64_t ldc, int structure, int64_t sA, int64_t sB, int64_t sC,
-                                               const int32_t* gate) {
+// One tile (bx, by) of product bz; the whole work-group takes part (it has barriers).
+template <bool BT, int BM>
+__device__ __attribute__((always_inline)) inline void dgemm_tile(int64_t bx, int64_t by, int64_t bz, int64_t M, int64_t N, int64_t K, double alpha,
+                                  const double* A, int64_t lda, const double* B, int64_t ldb, double beta, double* C,
+                                  int64_t ldc, int structure, int64_t sA, int64_t sB, int64_t sC) {
     static_assert(BM == 64 || BM == 128, "64 x 64 or 128 x 128 tiles");
-    if (gate && *gate == 0) return;   // a conditional product that is not wanted
     constexpr int BN = BM, BK = 16, PAD = 2;
     constexpr int WT = BM / 2, WB = WT / 16;   // wave tile and its 16 x 16 blocks per side
     // Loads are 16-byte chunks, and each wave instruction covers whole operand rows (coalesced).
@@ -62,14 +61,14 @@ __global__ __launch_bounds__(256, 2) void k_dgemm(int64_t M, int64_t N, int64_t 
     constexpr int CPR_K = BK / 2, RPP_K = 256 / CPR_K, PK = BM / RPP_K;   // chunks/row, rows/pass, passes
     constexpr int CPR_N = BN / 2, RPP_N = 256 / CPR_N, PN = BK / RPP_N;
     constexpr int PB = BT ? PK : PN;
-    A += (int64_t)blockIdx.z * sA;
-    B += (int64_t)blockIdx.z * sB;
-    C += (int64_t)blockIdx.z * sC;
+    A += bz * sA;
+    B += bz * sB;
+    C += bz * sC;
     __shared__ __attribute__((aligned(16))) double As[2][BM][BK + PAD];
     __shared__ __attribute__((aligned(16))) double Bs[2][BT ? BN : BK][BT ? BK + PAD : BN + PAD];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = (int64_t)blockIdx.x * BM, n0 = (int64_t)blockIdx.y * BN;
+    const int64_t m0 = bx * BM, n0 = by * BN;
     if ((structure & kLowerOnly) && n0 > m0 + BM - 1) return;
     int64_t kbeg = 0, kend = K;
     if (structure & kUpperOperands) kbeg = (m0 > n0 ? m0 : n0) / BK * BK;
@@ -179,6 +178,16 @@ __global__ __launch_bounds__(256, 2) void k_dgemm(int64_t M, int64_t N, int64_t 
             }
         }
     }
+}
+
+template <bool BT, int BM = 128>
+__global__ __launch_bounds__(256, 2) void k_dgemm(int64_t M, int64_t N, int64_t K, double alpha, const double* A,
+                                               int64_t lda, const double* B, int64_t ldb, double beta, double* C,
+                                               int64_t ldc, int structure, int64_t sA, int64_t sB, int64_t sC,
+                                               const int32_t* gate) {
+    if (gate && *gate == 0) return;   // a conditional product that is not wanted
+    dgemm_tile<BT, BM>(blockIdx.x, blockIdx.y, blockIdx.z, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, structure,
+                       sA, sB, sC);
 }
 
 // Z = 0 except its diagonal 64 x 64 blocks, which are the transposed inverses of L's diagonal
@@ -332,23 +341,8 @@ __device__ inline void sqrt_rsqrt(double p, double& r, double& ri) {
 // for the lower triangle and are written as zeros.  L^-1 by right-looking substitution, lane c
 // holding column c: once X[k][c] is final it is stored, and row k of X updates the running sums
 // of rows r > k with L[r][k] = Lt[k][r].
-// Work-group z < n_lam factors the block of matrix z (C + z sC, Dinv + z sD, info + z) with
-// its first wave; the work-groups after those centre and split rows [c_begin, c_end) of the
-// cross moments, ny work-groups of 2048 columns per row.
-__global__ __launch_bounds__(256) void k_chol_diag(double* C, int64_t sC, int64_t d, int J, double* Dinv, int64_t sD,
-                                                   int32_t* info, int n_lam, CrossArgs ca, int64_t c_begin,
-                                                   int64_t c_end, int ny) {
-    if ((int)blockIdx.x >= n_lam) {
-        const int64_t b = blockIdx.x - n_lam;
-        const int64_t c = c_begin + b / ny;
-        const int64_t i0 = ((b % ny) * 256 + threadIdx.x) * 8;
-        if (c < c_end && i0 < ca.d) centre_split_row(ca, c, i0);
-        return;
-    }
-    if (threadIdx.x >= 64) return;   // the factorisation is one wave's (no barriers below)
-    C += (int64_t)blockIdx.x * sC;
-    Dinv += (int64_t)blockIdx.x * sD;
-    info += blockIdx.x;
+// Called by the first wave of a work-group only.
+__device__ __attribute__((always_inline)) inline void chol_diag_block(double* C, int64_t d, int J, double* Dinv, int32_t* info) {
     __shared__ __attribute__((aligned(16))) double Lt[kNB][kNB + 2];
     const int i = threadIdx.x;
     const int64_t off = (int64_t)J * kNB;
@@ -415,6 +409,61 @@ __global__ __launch_bounds__(256) void k_chol_diag(double* C, int64_t sC, int64_
         }
         __builtin_amdgcn_sched_barrier(0);
     }
+}
+
+// Work-group z < n_lam factors the block of matrix z (C + z sC, Dinv + z sD, info + z) with
+// its first wave; the work-groups after those centre and split rows [c_begin, c_end) of the
+// cross moments, ny work-groups of 2048 columns per row.
+__global__ __launch_bounds__(256) void k_chol_diag(double* C, int64_t sC, int64_t d, int J, double* Dinv, int64_t sD,
+                                                   int32_t* info, int n_lam, CrossArgs ca, int64_t c_begin,
+                                                   int64_t c_end, int ny) {
+    if ((int)blockIdx.x >= n_lam) {
+        const int64_t b = blockIdx.x - n_lam;
+        const int64_t c = c_begin + b / ny;
+        const int64_t i0 = ((b % ny) * 256 + threadIdx.x) * 8;
+        if (c < c_end && i0 < ca.d) centre_split_row(ca, c, i0);
+        return;
+    }
+    if (threadIdx.x >= 64) return;   // the factorisation is one wave's (no barriers in it)
+    chol_diag_block(C + (int64_t)blockIdx.x * sC, d, J, Dinv + (int64_t)blockIdx.x * sD, info + blockIdx.x);
+}
+
+// The rest of a step's trailing update: P = the step's panel rows below the next block (ld d),
+// C = the trailing matrix below and right of the next block, m x m, lower 64 x 64 tiles only
+// (tiles of them per matrix, in the order t = bx (bx + 1) / 2 + by, by <= bx).
+struct TrailArgs {
+    const double* P;
+    double* C;
+    int64_t m;
+    int64_t tiles;
+};
+
+// Step J of the blocked Cholesky beside the end of step J - 1: block column J was updated by
+// step J - 1 first, so its diagonal block (work-groups z < n_lam, as k_chol_diag) is factored
+// in the same launch as the rest of step J - 1's trailing update (the next tiles x n_lam
+// work-groups; those never touch block row or column J), then the centring slices.
+__global__ __launch_bounds__(256, 2) void k_chol_step(double* C, int64_t sC, int64_t d, int J, double* Dinv,
+                                                      int64_t sD, int32_t* info, int n_lam, TrailArgs u, CrossArgs ca,
+                                                      int64_t c_begin, int64_t c_end, int ny) {
+    int64_t b = blockIdx.x;
+    if (b < n_lam) {
+        if (threadIdx.x < 64) chol_diag_block(C + b * sC, d, J, Dinv + b * sD, info + b);
+        return;
+    }
+    b -= n_lam;
+    if (b < u.tiles * n_lam) {
+        const int64_t z = b / u.tiles, t = b % u.tiles;
+        int64_t bx = (int64_t)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
+        while (bx * (bx + 1) / 2 > t) --bx;
+        while ((bx + 1) * (bx + 2) / 2 <= t) ++bx;
+        const int64_t by = t - bx * (bx + 1) / 2;
+        dgemm_tile<true, 64>(bx, by, z, u.m, u.m, kNB, -1.0, u.P, d, u.P, d, 1.0, u.C, d, kLowerOnly, sC, sC, sC);
+        return;
+    }
+    b -= u.tiles * n_lam;
+    const int64_t c = c_begin + b / ny;
+    const int64_t i0 = ((b % ny) * 256 + threadIdx.x) * 8;
+    if (c < c_end && i0 < ca.d) centre_split_row(ca, c, i0);
 }
 
 // dg[i] = sqrt(A[i][i]) before the factorisation overwrites the diagonal, and rdg[i] = 1/dg[i]
@@ -1314,18 +1363,26 @@ static rf_status solve_impl(const rf_gram_desc* desc, const void* d_state, const
     for (int i = 0; i < n_sel; ++i) ca.tsel[i] = targets[i];
     const int ny = (int)ceil_div(d, 2048);
 
-    // blocked Cholesky of every A_z: each step factors diagonal block J of all of them in one
-    // launch (one wave each), then updates their panels and trailing matrices in batched products
+    // blocked Cholesky of every A_z (batched over the lambdas): step J factors diagonal block J,
+    // solves its panel, updates block column J + 1, then factors diagonal block J + 1 in the same
+    // launch as the rest of step J's trailing update, so the diagonal factorisations (one wave
+    // each, a serial chain) run beside the trailing updates instead of between them
     const int nblk = (int)(d / kNB);
     const int64_t rows_per = ceil_div(rows, nblk);
-    for (int J = 0; J < nblk; ++J) {
-        const int64_t c0 = (int64_t)J * kNB;
-        const int64_t cb = std::min<int64_t>(rows, J * rows_per), ce = std::min<int64_t>(rows, cb + rows_per);
-        hipLaunchKernelGGL(k_chol_diag, dim3((unsigned)(nl + (ce - cb) * ny)), dim3(256), 0, s, w.C, dd, d, J, w.Dinv,
+    auto slice = [&](int J, int64_t& cb, int64_t& ce) {
+        cb = std::min<int64_t>(rows, J * rows_per);
+        ce = std::min<int64_t>(rows, cb + rows_per);
+    };
+    {
+        int64_t cb, ce;
+        slice(0, cb, ce);
+        hipLaunchKernelGGL(k_chol_diag, dim3((unsigned)(nl + (ce - cb) * ny)), dim3(256), 0, s, w.C, dd, d, 0, w.Dinv,
                            d * kNB, d_info, nl, ca, cb, ce, ny);
         RF_TRY(check_launch("rf_solve: potrf"));
+    }
+    for (int J = 0; J + 1 < nblk; ++J) {
+        const int64_t c0 = (int64_t)J * kNB;
         const int64_t rem = d - c0 - kNB;
-        if (rem <= 0) continue;
         // L21 = A21 L11^-T in place on the matrix cores: one column of 64 x 64 tiles, each of which
         // reads all of its rows of A21 before writing them
         double* panel = w.C + (c0 + kNB) * d + c0;
@@ -1334,8 +1391,17 @@ static rf_status solve_impl(const rf_gram_desc* desc, const void* d_state, const
                            (const double*)(w.Dinv + c0 * kNB), (int64_t)kNB, 0.0, panel, d, (int)kFull, dd, d * kNB, dd,
                            (const int32_t*)nullptr);
         RF_TRY(check_launch("rf_solve: panel"));
-        RF_TRY(dgemm<true>(s, rem, rem, kNB, -1.0, panel, d, panel, d, 1.0, w.C + (c0 + kNB) * d + c0 + kNB, d,
-                           kLowerOnly, nl, dd, dd, dd));
+        // block column J + 1 of the trailing update (all rows below block J)
+        RF_TRY(dgemm<true>(s, rem, kNB, kNB, -1.0, panel, d, panel, d, 1.0, w.C + (c0 + kNB) * d + c0 + kNB, d, kFull,
+                           nl, dd, dd, dd));
+        // diagonal block J + 1 beside the rest of the update (rows and columns past block J + 1)
+        const int64_t m = rem - kNB, tm = ceil_div(m, 64);
+        const TrailArgs u{panel + kNB * d, w.C + (c0 + 2 * kNB) * d + c0 + 2 * kNB, m, m > 0 ? tm * (tm + 1) / 2 : 0};
+        int64_t cb, ce;
+        slice(J + 1, cb, ce);
+        hipLaunchKernelGGL(k_chol_step, dim3((unsigned)(nl + u.tiles * nl + (ce - cb) * ny)), dim3(256), 0, s, w.C, dd,
+                           d, J + 1, w.Dinv, d * kNB, d_info, nl, u, ca, cb, ce, ny);
+        RF_TRY(check_launch("rf_solve: potrf step"));
     }
     for (int z = 0; z < nl; ++z) {
         double* Cz = w.C + z * dd;
