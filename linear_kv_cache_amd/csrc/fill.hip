@@ -338,29 +338,10 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
                 __syncthreads();
             }
         }
-        // (cos, sin) of the lane's 4 x 4 low dims for token column j, one column ahead of its
-        // use, so each column's table loads wait behind the previous column's work; no table
-        // (translators of rotated keys): the identity turn
-        f32x4 c01[2][4], c23[2][4];
-        auto rope_load = [&](int j, f32x4 (&o01)[4], f32x4 (&o23)[4]) {
-            if (a.rope) {
-                const int64_t n = n0 + G::col_of(j);
-                const float* cs_row = a.rope + (a.pos0 + a.t0 + (n < a.rows ? n : 0)) * (int64_t)DH;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int dlo = (qp0 + 8 * q) % HALF;
-                    o01[q] = *(const f32x4*)(cs_row + 2 * dlo);
-                    o23[q] = *(const f32x4*)(cs_row + 2 * dlo + 4);
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) o01[q] = o23[q] = f32x4{1.f, 0.f, 1.f, 0.f};
-            }
-        };
-        if (is_k) rope_load(0, c01[0], c23[0]);
 #pragma unroll
         for (int j = 0; j < G::SN; ++j) {
             const int nl = G::col_of(j);
+            const int64_t n = n0 + nl;
             const float r = NORM ? rinv[nl] : 1.f;
             if (!is_k) {
 #pragma unroll
@@ -378,7 +359,21 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
                     stage(nl, fl + HALF, hi);
                 }
             } else {
-                if (j + 1 < G::SN) rope_load(j + 1, c01[(j + 1) & 1], c23[(j + 1) & 1]);
+                // (cos, sin) of the lane's 4 x 4 low dims, loaded together ahead of their uses;
+                // no table (translators of rotated keys): the identity turn
+                f32x4 c01[4], c23[4];
+                if (a.rope) {
+                    const float* cs_row = a.rope + (a.pos0 + a.t0 + (n < a.rows ? n : 0)) * (int64_t)DH;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int dlo = (qp0 + 8 * q) % HALF;
+                        c01[q] = *(const f32x4*)(cs_row + 2 * dlo);
+                        c23[q] = *(const f32x4*)(cs_row + 2 * dlo + 4);
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) c01[q] = c23[q] = f32x4{1.f, 0.f, 1.f, 0.f};
+                }
                 __builtin_amdgcn_sched_barrier(0);
                 float kinv = 1.f;
                 if constexpr (KN) {
@@ -390,9 +385,8 @@ __global__ __launch_bounds__(KVCore<T>::G::kThr) void k_fill_kv(KVArgs a) {
                 for (int q = 0; q < 4; ++q) {
                     const int qp = qp0 + 8 * q;
                     const int fl = (qp / HALF) * DH + qp % HALF;
-                    const f32x4 u01 = c01[j & 1][q], u23 = c23[j & 1][q];
-                    const float cs[4] = {u01[0], u01[2], u23[0], u23[2]};
-                    const float sn[4] = {u01[1], u01[3], u23[1], u23[3]};
+                    const float cs[4] = {c01[q][0], c01[q][2], c23[q][0], c23[q][2]};
+                    const float sn[4] = {c01[q][1], c01[q][3], c23[q][1], c23[q][3]};
                     const f32x4 blo = bias4(fl), bhi = bias4(fl + HALF);
                     f32x4 glo{1.f, 1.f, 1.f, 1.f}, ghi{1.f, 1.f, 1.f, 1.f};
                     if constexpr (KN) {
@@ -561,16 +555,6 @@ __global__ __launch_bounds__(PackedAGemm::kThr) void k_fill_norm(NormArgs a) {
     // 512-byte row segments (a half-wave per token; rows past the end read as zero) and are
     // read per lane from LDS in the accumulators' layout
     const int lane = threadIdx.x & 63, wm = threadIdx.x >> 6;
-    // the lane's features' linear and diagonal coefficients, in flight with the x block
-    const float* qv = a.q[g];
-    f32x4 gq[G::SM][4], gd[G::SM][4];
-#pragma unroll
-    for (int i = 0; i < G::SM; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            gq[i][q] = *(const f32x4*)(qv + mt * kFT + G::row_of(i, 4 * q));
-            gd[i][q] = *(const f32x4*)(qv + a.d + mt * kFT + G::row_of(i, 4 * q));
-        }
     {
         const int c = threadIdx.x & 31;
 #pragma unroll 2
@@ -583,6 +567,15 @@ __global__ __launch_bounds__(PackedAGemm::kThr) void k_fill_norm(NormArgs a) {
     }
     __syncthreads();
     float* red = (float*)(lds + kX);
+    const float* qv = a.q[g];
+    f32x4 gq[G::SM][4], gd[G::SM][4];
+#pragma unroll
+    for (int i = 0; i < G::SM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            gq[i][q] = *(const f32x4*)(qv + mt * kFT + G::row_of(i, 4 * q));
+            gd[i][q] = *(const f32x4*)(qv + a.d + mt * kFT + G::row_of(i, 4 * q));
+        }
 #pragma unroll
     for (int j = 0; j < G::SN; ++j) {
         const int nl = G::col_of(j);
