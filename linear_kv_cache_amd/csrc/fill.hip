@@ -552,17 +552,30 @@ __global__ __launch_bounds__(PackedAGemm::kThr) void k_fill_norm(NormArgs a) {
            PipeOperand{X + n0 * a.ldx + (int64_t)mt * kFT, a.ldx, a.rows - n0}, a.d / G::BK - kb);
 
     // the main loop ended on a barrier: LDS is free.  The tile's x values come back as whole
-    // 512-byte row segments (a half-wave per token; rows past the end read as zero) and are
-    // read per lane from LDS in the accumulators' layout
+    // 512-byte row segments (a half-wave per token; rows past the end read as zero through the
+    // buffer's range) and are read per lane from LDS in the accumulators' layout.  Sixteen loads
+    // per thread are issued before the first LDS write: a load-then-write loop waits one memory
+    // round trip per row pass, which cost more than the rest of the epilogue
     const int lane = threadIdx.x & 63, wm = threadIdx.x >> 6;
     {
         const int c = threadIdx.x & 31;
-#pragma unroll 2
-        for (int p = 0; p < kTT / 8; ++p) {
-            const int nl = p * 8 + (threadIdx.x >> 5);
-            const int64_t n = n0 + nl;
-            const u32x4 v = n < a.rows ? *(const u32x4*)(X + n * a.ldx + mt * kFT + c * 8) : u32x4{0u, 0u, 0u, 0u};
-            *(u32x4*)(lds + nl * (kFT * 2) + ((c ^ (nl & 31)) << 4)) = v;
+        const int64_t nv = a.rows - n0 < kTT ? a.rows - n0 : kTT;
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16_t*>(X + n0 * a.ldx), (short)0, (int)(nv * a.ldx * 2), 0x00020000);
+        constexpr int kInFlight = 16;
+#pragma unroll
+        for (int p0 = 0; p0 < kTT / 8; p0 += kInFlight) {
+            u32x4 v[kInFlight];
+#pragma unroll
+            for (int u = 0; u < kInFlight; ++u) {
+                const int nl = (p0 + u) * 8 + (threadIdx.x >> 5);
+                v[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)((nl * a.ldx + mt * kFT + c * 8) * 2), 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < kInFlight; ++u) {
+                const int nl = (p0 + u) * 8 + (threadIdx.x >> 5);
+                *(u32x4*)(lds + nl * (kFT * 2) + ((c ^ (nl & 31)) << 4)) = v[u];
+            }
         }
     }
     __syncthreads();
