@@ -11,6 +11,15 @@
 // staged in LDS (keys as stored) while the next block's rows are in flight in registers,
 // so the sequential token loop reads only LDS (a block's reads issued ahead of the chain);
 // each block's key norms are computed once, 8 lanes per token, when it is staged.
+// Within a block the state is carried scaled, u = s / A_t with A_t the product of the block's
+// decays up to token t, so a token's update is u <- u + c' k (one fused multiply-add per
+// element instead of a multiply and a fused multiply-add):
+//     s_{t-1} . k = A_{t-1} (u . k),   c' = c / A_t = p_t (v_r - q_t (u . k)),
+//     q_t = rn A_t,   p_t = beta rn / A_t,
+// and s = A_31 u at the block's end.  This is the same recurrence regrouped (the rounding of
+// the sum is relative to the same magnitudes after the final scaling); it is used for a block
+// only when every A_t lies in [2^-60, 2^60], so that neither u nor 1 / A_t can overflow, and
+// the block runs the direct form otherwise.
 #include <math.h>
 
 #include <string>
@@ -76,7 +85,10 @@ __device__ inline void gdn_state(const GdnArgs& a) {
     // done with this one.
     __shared__ __attribute__((aligned(16))) float sk[kGdnBlock][DK];
     __shared__ float sv[kGdnBlock][ROWS];
-    __shared__ float sa[kGdnBlock], sb[kGdnBlock], sn[kGdnBlock];
+    __shared__ float sa[kGdnBlock], sb[kGdnBlock], sn[kGdnBlock], sg[kGdnBlock];
+    __shared__ __attribute__((aligned(16))) float sqp[kGdnBlock][2];   // scaled form: q_t, p_t
+    __shared__ __attribute__((aligned(16))) int32_t sok[kGdnBlock];     // A_t in range
+    __shared__ float sA;                                                // A_31
     const int per_layer = a.n_heads * a.wg_per_head;
     const int l = blockIdx.x / per_layer;
     const int rem = blockIdx.x - l * per_layer;
@@ -151,6 +163,7 @@ __device__ inline void gdn_state(const GdnArgs& a) {
             const bool ok = tb + t < a.T;
             sa[t] = ok ? expf(rg) : 1.f;
             sb[t] = ok ? rb : 0.f;
+            sg[t] = ok ? rg : 0.f;
         }
     };
     // key norm factors of a staged block: 8 lanes per token, each summing DK / 8 squares, then
@@ -165,7 +178,19 @@ __device__ inline void gdn_state(const GdnArgs& a) {
             q += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
         }
         q = group_sum<8>(q);
-        if (t % 8 == 0) sn[tt] = tb + tt >= a.T ? 0.f : (a.normalise ? 1.0f / sqrtf(q + a.eps) : 1.0f);
+        if (t % 8 == 0) {
+            const float rn = tb + tt >= a.T ? 0.f : (a.normalise ? 1.0f / sqrtf(q + a.eps) : 1.0f);
+            sn[tt] = rn;
+            // the scaled form's factors: the block's log-decay up to this token, summed in
+            // token order (the same order in every thread that needs it)
+            float G = 0.f;
+            for (int i = 0; i <= tt; ++i) G += sg[i];
+            const float At = expf(G);
+            sok[tt] = G >= -41.0f && G <= 41.0f;   // |G| <= 60 ln 2
+            sqp[tt][0] = rn * At;
+            sqp[tt][1] = sb[tt] * rn / At;
+            if (tt == kGdnBlock - 1) sA = At;
+        }
     };
     const int n_blocks = (int)((a.T + kGdnBlock - 1) / kGdnBlock);
     fetch(0);
@@ -179,22 +204,51 @@ __device__ inline void gdn_state(const GdnArgs& a) {
         // a fixed trip count, unrolled, so each token's LDS reads are issued ahead of the chain.
         // Tokens past the range were staged as zero keys and values with gate 1, strength 0
         // and norm factor 0: their update is exactly s <- s.
+        // the block's form, the same in every thread (all read the same flags)
+        bool scaled = true;
+#pragma unroll
+        for (int i = 0; i < kGdnBlock; i += 4) {
+            const int4 f = *(const int4*)&sok[i];
+            scaled = scaled && f.x && f.y && f.z && f.w;
+        }
+        if (scaled) {
 #pragma unroll 4
-        for (int tt = 0; tt < kGdnBlock; ++tt) {
-            const f32x4 k0 = *(const f32x4*)&sk[tt][j0], k1 = *(const f32x4*)&sk[tt][j0 + 4];
-            const float k[E] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
-            const float av = sa[tt], bv = sb[tt], rn = sn[tt], vr = sv[tt][rl];
-            // the row's dot product: two partial sums, then over the row's lanes
-            float d0 = s[0] * k[0], d1 = s[1] * k[1];
+            for (int tt = 0; tt < kGdnBlock; ++tt) {
+                const f32x4 k0 = *(const f32x4*)&sk[tt][j0], k1 = *(const f32x4*)&sk[tt][j0 + 4];
+                const float k[E] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+                const float qv = sqp[tt][0], pv = sqp[tt][1], vr = sv[tt][rl];
+                float d0 = s[0] * k[0], d1 = s[1] * k[1];
 #pragma unroll
-            for (int e = 2; e < E; e += 2) {
-                d0 += s[e] * k[e];
-                d1 += s[e + 1] * k[e + 1];
+                for (int e = 2; e < E; e += 2) {
+                    d0 += s[e] * k[e];
+                    d1 += s[e + 1] * k[e + 1];
+                }
+                const float dot = group_sum<LANES>(d0 + d1);
+                const float c = pv * (vr - qv * dot);
+#pragma unroll
+                for (int e = 0; e < E; ++e) s[e] += c * k[e];
             }
-            const float dot = group_sum<LANES>(d0 + d1);
-            const float c = bv * (vr - av * dot * rn) * rn;
+            const float Ab = sA;
 #pragma unroll
-            for (int e = 0; e < E; ++e) s[e] = av * s[e] + c * k[e];
+            for (int e = 0; e < E; ++e) s[e] *= Ab;
+        } else {
+#pragma unroll 4
+            for (int tt = 0; tt < kGdnBlock; ++tt) {
+                const f32x4 k0 = *(const f32x4*)&sk[tt][j0], k1 = *(const f32x4*)&sk[tt][j0 + 4];
+                const float k[E] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+                const float av = sa[tt], bv = sb[tt], rn = sn[tt], vr = sv[tt][rl];
+                // the row's dot product: two partial sums, then over the row's lanes
+                float d0 = s[0] * k[0], d1 = s[1] * k[1];
+#pragma unroll
+                for (int e = 2; e < E; e += 2) {
+                    d0 += s[e] * k[e];
+                    d1 += s[e + 1] * k[e + 1];
+                }
+                const float dot = group_sum<LANES>(d0 + d1);
+                const float c = bv * (vr - av * dot * rn) * rn;
+#pragma unroll
+                for (int e = 0; e < E; ++e) s[e] = av * s[e] + c * k[e];
+            }
         }
         __syncthreads();   // every lane is done with this block's buffer
         if (blk + 1 < n_blocks) {

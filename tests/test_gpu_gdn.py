@@ -68,6 +68,28 @@ def test_gdn_state_chunked_continuation_and_initial_state():
     assert max(errs) <= GDN_TOL
 
 
+def test_gdn_state_strong_and_mild_decay_blocks():
+    # the kernel carries a block's state scaled by its running decay only while that decay stays
+    # within 2^-60..2^60, and runs the direct form otherwise: 32-token blocks alternate between
+    # mild decays (scaled) and decays of e^-3 per token (direct), a ragged tail ends mild, and
+    # one block mixes both near its end (the bound reached inside the block), from a given state
+    import linear_kv_cache_amd as rf
+    H, dk, dv, T = 2, 128, 64, 32 * 7 + 13
+    K, V, g, b = synth.gdn_inputs(13, 0, T, H, dk, dv, torch.bfloat16)
+    blk = torch.arange(T) // 32
+    g = torch.where((blk % 2 == 1)[:, None], torch.full_like(g, -3.0), g)
+    g[32 * 4 + 20:32 * 5] = -4.0        # block 4: mild, then strong from token 20 on
+    S0 = torch.randn(H, dv, dk, generator=synth.generator(13, "gdn-S0")) * 0.3
+    S = [S0.clone().cuda()]
+    rf.rf_gdn_state(rf.gdn_desc(H, dk, dv, torch.bfloat16, True), [K.cuda()], [V.cuda()], [g.cuda()], [b.cuda()], S)
+    torch.cuda.synchronize()
+    ref = oracle.gdn_state(f64(K).reshape(T, H, dk), f64(V).reshape(T, H, dv), f64(g), f64(b), f64(S0),
+                           normalise_k=True)
+    err = float(np.max(np.abs(f64(S[0]) - ref)) / np.max(np.abs(ref)))
+    log(f"[gdn] strong and mild decay blocks: err={err:.3g}")
+    assert bool(torch.isfinite(S[0]).all()) and err <= GDN_TOL
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(300)
 def test_gdn_state_full_prompt_sampled_heads():
