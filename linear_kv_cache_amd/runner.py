@@ -137,32 +137,53 @@ def greedy_sources(state: GramState, block_width: int, nu: int, lam: float, mode
     A candidate set whose regularised Gram is not positive definite (the solve's pivot
     report, e.g. lambda = 0 with a source layer of constant rows) or whose score is not
     finite ranks last; a step with no valid candidate raises.
-    The choices are host decisions on the scores; every number comes from the library.
-    Returns the chosen layers per target, ascending; with ``return_order`` also the picks in
-    the order they were made."""
+    The sub-state, the solve and R^2 workspaces and the maps are allocated once, for the
+    largest set (nu blocks), and reused by every candidate; each candidate's scores and pivot
+    report stay on the device until the step's candidates are all enqueued, then come back in
+    one copy.  The choices are host decisions on the scores; every number comes from the
+    library.  Returns the chosen layers per target, ascending; with ``return_order`` also the
+    picks in the order they were made."""
     dev = state.buf.device
     n_blocks = state.d // block_width
     targets = list(range(state.n_targets)) if targets is None else list(targets)
     chosen: List[List[int]] = [[] for _ in targets]
+    n_t = len(set(targets))
+    # buffers for the largest candidate set, reused by all of them
+    big = gram_desc(nu * block_width, state.n_targets, state.desc.dtype, state.desc.d_out)
+    sub_buf = device_bytes(max(rf_gram_state_bytes(gram_desc(k * block_width, state.n_targets, state.desc.dtype,
+                                                             state.desc.d_out)) for k in range(1, nu + 1)), dev)
+    solve_ws = device_bytes(max(rf_solve_workspace_bytes(gram_desc(k * block_width, state.n_targets,
+                                                                   state.desc.dtype, state.desc.d_out), n_t, 1)
+                                for k in range(1, nu + 1)), dev)
+    r2_ws = device_bytes(max(rf_fit_r2_workspace_bytes(gram_desc(k * block_width, state.n_targets, state.desc.dtype,
+                                                                 state.desc.d_out), n_t) for k in range(1, nu + 1)), dev)
+    W_buf = torch.empty(n_t * state.dy * big.d, dtype=torch.float32, device=dev)
+    b_buf = torch.empty(n_t * state.dy, dtype=torch.float32, device=dev)
     for _ in range(nu):
         sets: dict = {}
         for ti in range(len(targets)):
             for s in range(n_blocks):
                 if s not in chosen[ti]:
                     sets.setdefault(tuple(sorted(chosen[ti] + [s])), []).append(ti)
+        keys = list(sets)
+        r2_dev = torch.empty(len(keys), n_t, dtype=torch.float64, device=dev)
+        info_dev = torch.empty(len(keys), dtype=torch.int32, device=dev)
+        tsels = []
+        for c, key in enumerate(keys):
+            sub_desc = gram_desc(len(key) * block_width, state.n_targets, state.desc.dtype, state.desc.d_out)
+            rf_gram_select(state.desc, state.buf, block_width, list(key), sub_desc, sub_buf, stream)
+            tsel = sorted(set(targets[ti] for ti in sets[key]))
+            tsels.append(tsel)
+            W = W_buf[:len(tsel) * state.dy * sub_desc.d]
+            rf_solve(sub_desc, sub_buf, lam, mode, tsel, W, None, b_buf[:len(tsel) * state.dy], info_dev[c:c + 1],
+                     solve_ws, stream)
+            rf_fit_r2(sub_desc, sub_buf, lam, mode, tsel, W, r2_dev[c, :len(tsel)], r2_ws, stream)
+        r2_host = r2_dev.cpu().tolist()
+        info_host = info_dev.cpu().tolist()
         scores: dict = {}
-        for key, users in sets.items():
-            sub = GramState.__new__(GramState)
-            sub.desc = gram_desc(len(key) * block_width, state.n_targets, state.desc.dtype, state.desc.d_out)
-            sub.layout = rf_gram_state_layout(sub.desc)
-            sub.buf = device_bytes(rf_gram_state_bytes(sub.desc), dev)
-            sub.d, sub.n_targets, sub.dy = len(key) * block_width, state.n_targets, state.dy
-            rf_gram_select(state.desc, state.buf, block_width, list(key), sub.desc, sub.buf, stream)
-            tsel = sorted(set(targets[ti] for ti in users))
-            W, _, _, info = sub.solve(lam, mode, tsel, want_bf16=False, stream=stream)
-            r2 = sub.r2(lam, mode, tsel, W, stream).cpu().tolist()
-            ok = int(info.cpu().reshape(-1)[0].item()) == 0
-            for t, v in zip(tsel, r2):
+        for c, key in enumerate(keys):
+            ok = info_host[c] == 0
+            for t, v in zip(tsels[c], r2_host[c]):
                 scores[(key, t)] = v if ok and math.isfinite(v) else None
         for ti, t in enumerate(targets):
             best = None
