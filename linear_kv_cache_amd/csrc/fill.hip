@@ -548,8 +548,12 @@ __global__ __launch_bounds__(PackedAGemm::kThr) void k_fill_norm(NormArgs a) {
     const int kb = mt * (kFT / G::BK);   // first k-step: column 256 mt
     const bf16_t* X = (const bf16_t*)a.X;
     G gm;
-    gm.run(lds, PipeOperand{(const bf16_t*)a.T[g] + (int64_t)mt * kFT * a.d + (int64_t)kb * (G::kStepBytes / 2), a.d, kFT},
-           PipeOperand{X + n0 * a.ldx + (int64_t)mt * kFT, a.ldx, a.rows - n0}, a.d / G::BK - kb);
+    // the K loop from the last column down: the row tiles of one token tile that run together
+    // then read the same prompt-state columns at the same time (they all end at column d), and
+    // the tile's own x block, read last, is still in the L2 for the epilogue
+    gm.template run<false, false, true>(
+        lds, PipeOperand{(const bf16_t*)a.T[g] + (int64_t)mt * kFT * a.d + (int64_t)kb * (G::kStepBytes / 2), a.d, kFT},
+        PipeOperand{X + n0 * a.ldx + (int64_t)mt * kFT, a.ldx, a.rows - n0}, a.d / G::BK - kb);
 
     // the main loop ended on a barrier: LDS is free.  The tile's x values come back as whole
     // 512-byte row segments (a half-wave per token; rows past the end read as zero through the

@@ -384,10 +384,13 @@ struct PackedAGemm {
     // unused (a packed tile always holds 256 rows).  With FOLD, k-step kt of B is read from step
     // kt < b_fold ? kt : kt - b_fold of its rows (B's first b_fold steps serve twice).  With SEG,
     // the K loop visits segments of 4 k-steps (256 columns) seg_stride steps apart: logical step
-    // kt reads step (kt / 4) * seg_stride + kt % 4 of both operands.
-    template <bool FOLD = false, bool SEG = false>
+    // kt reads step (kt / 4) * seg_stride + kt % 4 of both operands.  With REV the K loop runs
+    // from the last step down (logical step kt reads step nk - 1 - kt), so tiles of different
+    // lengths that end at the same column read the same columns at the same time.
+    template <bool FOLD = false, bool SEG = false, bool REV = false>
     __device__ inline void run(char* lds, const PipeOperand& A, const PipeOperand& B, int nk, int b_fold = 0,
                                int seg_stride = 4) {
+        static_assert(!(REV && (FOLD || SEG)), "a reversed K loop reads plain steps");
         const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
 #pragma unroll
         for (int i = 0; i < SM; ++i)
@@ -399,10 +402,11 @@ struct PackedAGemm {
         // physical k-step of logical step kc (uniform by construction, said so for the compiler)
         auto phys = [&](int kc) {
             if constexpr (SEG) return __builtin_amdgcn_readfirstlane((kc >> 2) * seg_stride + (kc & 3));
+            if constexpr (REV) return __builtin_amdgcn_readfirstlane(nk - 1 - kc);
             return kc;
         };
-        const __amdgpu_buffer_rsrc_t ra =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(A.ptr), (short)0, (phys(nk - 1) + 1) * kStepBytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<void*>(A.ptr), (short)0, ((REV ? nk - 1 : phys(nk - 1)) + 1) * kStepBytes, 0x00020000);
         int64_t nb = B.valid < BN ? B.valid : BN;
         if (nb < 0) nb = 0;
         const __amdgpu_buffer_rsrc_t rb =
