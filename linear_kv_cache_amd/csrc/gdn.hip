@@ -26,6 +26,7 @@
 
 #include "rf_internal.h"
 #include "rf_mfma.h"
+#include "rf_pipe.h"
 
 namespace rf {
 
@@ -90,8 +91,11 @@ __device__ inline void gdn_state(const GdnArgs& a) {
     __shared__ __attribute__((aligned(16))) int32_t sok[kGdnBlock];     // A_t in range
     __shared__ float sA;                                                // A_31
     const int per_layer = a.n_heads * a.wg_per_head;
-    const int l = blockIdx.x / per_layer;
-    const int rem = blockIdx.x - l * per_layer;
+    // the work-groups of one head on one XCD, so the head's key rows, which every one of them
+    // reads, come from that XCD's L2 after the first
+    const int bid = xcd_order((int)blockIdx.x, (int)gridDim.x);
+    const int l = bid / per_layer;
+    const int rem = bid - l * per_layer;
     const int h = rem / a.wg_per_head;
     const int r0 = (rem - h * a.wg_per_head) * ROWS;
     const int t = threadIdx.x;
