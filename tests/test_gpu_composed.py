@@ -87,6 +87,29 @@ def test_composed_fill_single_token_and_tile_edges():
         _check(run_fill_case(FillCase(SMALL_BF16, t0, t1, composed=True)), f"d512 [{t0},{t1})")
 
 
+def test_composed_fill_deterministic_and_empty_ranges():
+    # the composition and the composed fill are bitwise deterministic (fixed-order reductions,
+    # no atomics), and an empty token range writes nothing
+    from linear_kv_cache_amd.runner import ComposedFiller, alloc_cache, fill_weights
+    cfg = SMALL_BF16
+    ws = [synth.layer_weights(cfg, l, device="cuda") for l in cfg.filled_layers[:2]]
+    fw = fill_weights(cfg.d, cfg.n_kv_heads, cfg.head_dim, cfg.rms_eps, cfg.torch_dtype, [w.W_map for w in ws],
+                      [w.b_map for w in ws], [w.gamma for w in ws], [w.W_k for w in ws], [w.W_v for w in ws])
+    X = synth.hidden_states(cfg, 700, "prompt", device="cuda")
+    outs = []
+    for _ in range(2):
+        cache = alloc_cache(2, cfg.n_kv_heads, cfg.head_dim, 700, cfg.torch_dtype, "cuda", sentinel=3.0)
+        filler = ComposedFiller(fw, cfg.rope_base, 700, 700, "cuda")
+        for t in (0, 350, 700):
+            filler.fill(X, t, t, 0, cache)
+        torch.cuda.synchronize()
+        assert all(bool(torch.all(t == 3.0)) for t in cache.k + cache.v)
+        filler.fill(X, 0, 700, 0, cache)
+        outs.append(torch.cat(cache.k + cache.v))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(300)
 def test_composed_fill_llama8b_shaped_full():
