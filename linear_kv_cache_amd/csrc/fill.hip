@@ -21,6 +21,7 @@
 #include "rf_internal.h"
 #include "rf_mfma.h"
 #include "rf_pipe.h"
+#include "rf_pipe4.h"
 
 namespace rf {
 
@@ -209,6 +210,234 @@ __global__ __launch_bounds__(MapCore<T>::G::kThr) void k_fill_map(MapArgs a) {
             for (int w = 0; w < kWaveRows; ++w) ps += red[w * kTT + nl];
             a.psum[g * a.ps_slot + n * a.n_ps + mt] = ps;
         }
+    }
+}
+
+// The bf16 K/V product on 512-feature x 128-token tiles (PackedAGemm4), for widths whose K
+// and V halves are whole 512-feature tiles: the same epilogue as k_fill_kv below (row scale,
+// intercept, per-head key norm, RoPE, LDS-staged cache rows).  Wave w holds pairs of blocks
+// (2p, 2p + 1), p = 0, 1, of the packed 64-row group ow = 2 (w % 2) + p of the 256-feature
+// half w / 2: block 2p the low dims of the group's 32 RoPE pairs, block 2p + 1 their partners.
+// A 128-wide head is one wave's two groups; a 64-wide head one group.
+constexpr int kFT4 = 512, kTT4 = 128;
+template <int DH, bool NORM, bool BIAS, bool KN>
+__global__ __launch_bounds__(PackedAGemm4::kThr) void k_fill_kv4(KVArgs a) {
+    using G = PackedAGemm4;
+    constexpr int HALF = DH / 2;
+    // LDS after the main loop: the staged rows of 64 tokens [token][feature] (1 KiB per token;
+    // the tile is written in two halves), the tile's RoPE rows (DH floats per token, filled
+    // during the main loop: the pipeline uses only the first 32 KiB), then 1/rms and the cache
+    // row offset of every token of the tile
+    constexpr int kHalfTok = kTT4 / 2;
+    constexpr int kTab = kHalfTok * kFT4 * 2;
+    constexpr int kTabRow = DH * 4;                        // bytes per token
+    constexpr int kRinv = kTab + kTT4 * kTabRow;
+    constexpr int kEpi = kRinv + kTT4 * 4 + kTT4 * 8;
+    static_assert(G::LDS_BYTES <= kTab, "the RoPE rows must not overlap the pipeline stages");
+    static_assert(kEpi <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(16))) char lds[kEpi];
+    const int n_feat = 2 * a.kvw / kFT4;
+    const int per_layer = n_feat * a.tok_tiles;
+    const int v = xcd_order((int)blockIdx.x, (int)gridDim.x);
+    const int g = v / per_layer;
+    int mt, tt;
+    grouped_tile(v - g * per_layer, n_feat, a.tok_tiles, 4, mt, tt);
+    const int64_t n0 = (int64_t)tt * kTT4;
+    const bool is_k = (int64_t)mt * kFT4 < a.kvw;
+    const int f0 = is_k ? mt * kFT4 : mt * kFT4 - a.kvw;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t nv = a.rows - n0 < kTT4 ? a.rows - n0 : kTT4;
+    // RoPE rows of the tile's tokens straight into LDS (no registers, no wait here: the main
+    // loop's first wait covers them).  16-byte chunk c of token n sits in slot c ^ (n % CPR); a
+    // wave's load fills 1 KiB, TPB whole token rows; tokens past the end read as zero
+    constexpr int CPR = DH / 4, TPB = 64 / CPR;
+    if (is_k && a.rope) {
+        const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(a.rope + (a.pos0 + a.t0 + n0) * (int64_t)DH), (short)0, (int)(nv * kTabRow), 0x00020000);
+        const int sl = lane % CPR;
+#pragma unroll
+        for (int u = 0; u < kTT4 / TPB / 4; ++u) {
+            const int blk = w * (kTT4 / TPB / 4) + u;
+            const int nl = blk * TPB + lane / CPR;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rr, (__attribute__((address_space(3))) void*)(lds + kTab + blk * 1024), 16,
+                nl * kTabRow + ((sl ^ (nl % CPR)) << 4), 0, 0, 0);
+        }
+    }
+    const bf16_t* Wsel = (const bf16_t*)(is_k ? a.Wk[g] : a.Wv[g]) + (int64_t)f0 * a.d;
+    const bf16_t* Bsel = (const bf16_t*)(is_k ? a.in_k[g] : a.in_v[g]) + n0 * a.ld_in;
+    G gm;
+    gm.run(lds, PipeOperand{Wsel, a.d, kFT4}, PipeOperand{Bsel, a.ld_in, a.rows - n0}, a.d / G::BK);
+
+    bf16_t* pool = (bf16_t*)(is_k ? a.kc[g] : a.vc[g]);
+    const float* ps = NORM ? a.psum + g * a.ps_slot : nullptr;
+    const float* bsel = BIAS ? (is_k ? a.bk[g] : a.bv[g]) + f0 : nullptr;
+    const float inv_d = 1.0f / (float)a.d;
+    auto rms_inv = [&](int64_t n) {
+        if constexpr (!NORM) return 1.0f;
+        float s = 0.f;
+        if (a.n_ps % 4 == 0) {
+            for (int p = 0; p < a.n_ps; p += 16) {
+                f32x4 vv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    vv[u] = p + 4 * u < a.n_ps ? *(const f32x4*)(ps + n * a.n_ps + p + 4 * u) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    s += vv[u][0]; s += vv[u][1]; s += vv[u][2]; s += vv[u][3];
+                }
+            }
+        } else {
+            for (int p = 0; p < a.n_ps; ++p) s += ps[n * a.n_ps + p];
+        }
+        if (a.qb[g]) s += *a.qb[g];
+        return 1.0f / sqrtf(s * inv_d + a.eps);
+    };
+    auto row_base = [&](int64_t t) -> int64_t {
+        if (!a.paged) return t * a.stride_token;
+        const int64_t lb = t / a.block_size;
+        const int64_t phys = lb < a.n_table_blocks ? (int64_t)a.block_table[lb] : -1;
+        if (phys < 0 || phys >= a.n_blocks) return -1;
+        return phys * a.stride_block + (t % a.block_size) * a.stride_token;
+    };
+    float* rinv = (float*)(lds + kRinv);
+    int64_t* rbase = (int64_t*)(lds + kRinv + kTT4 * 4);
+    for (int nl = threadIdx.x; nl < kTT4; nl += G::kThr) {
+        const bool ok = nl < nv;
+        if constexpr (NORM) rinv[nl] = ok ? rms_inv(n0 + nl) : 0.f;
+        rbase[nl] = ok ? row_base(a.t0 + n0 + nl) : -1;
+    }
+    __syncthreads();
+    // [token][feature] for the 64 tokens of one half, 16-byte chunk c of token n in slot c ^ n
+    auto stage = [&](int nh, int fl, const float (&o)[4]) {
+        const int slot = ((fl >> 3) ^ nh) << 4;
+        *(u32x2*)(lds + nh * (kFT4 * 2) + slot + (fl & 4) * 2) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    };
+    const int half = w >> 1;                               // 256-feature half of the tile
+    auto bias4 = [&](int fl) {
+        if constexpr (BIAS) return *(const f32x4*)(bsel + fl);
+        return f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    // lane's first RoPE pair of group p (within its 256-feature half) and the feature of pair qp
+    auto qpair0 = [&](int p) { return (2 * (w & 1) + p) * 32 + 4 * (lane >> 5); };
+    auto feat = [&](int qp) { return half * 256 + (qp / HALF) * DH + qp % HALF; };
+    // per-head key norm weights of the lane's pairs (for the whole tile)
+    f32x4 glo[2][4], ghi[2][4];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) glo[p][q] = ghi[p][q] = f32x4{1.f, 1.f, 1.f, 1.f};
+    if constexpr (KN) {
+        if (is_k) {
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int qp = qpair0(p) + 8 * q;
+                    glo[p][q] = *(const f32x4*)(a.kn[g] + qp % HALF);
+                    ghi[p][q] = *(const f32x4*)(a.kn[g] + qp % HALF + HALF);
+                }
+        }
+    }
+    // whole 16-byte pieces of (token, head) rows: chunk c = features 8c .. 8c + 7 of the tile
+    const int c = threadIdx.x & 63;
+    const int head = (f0 + c * 8) / DH, dim = (f0 + c * 8) % DH;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int jj = 0; jj < G::SN / 2; ++jj) {
+            const int j = h * (G::SN / 2) + jj;
+            const int nh = jj * 32 + (lane & 31);          // token within the half
+            const int nl = h * kHalfTok + nh;
+            const float r = NORM ? rinv[nl] : 1.f;
+            // the block pairs' values, scaled and with their intercepts
+            float xlo[2][4][4], xhi[2][4][4];
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int fl = feat(qpair0(p) + 8 * q);
+                    const f32x4 blo = bias4(fl), bhi = bias4(fl + HALF);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        xlo[p][q][e] = (gm.acc[2 * p][j][4 * q + e] + blo[e]) * r;
+                        xhi[p][q][e] = (gm.acc[2 * p + 1][j][4 * q + e] + bhi[e]) * r;
+                    }
+                }
+            if (!is_k) {
+#pragma unroll
+                for (int p = 0; p < 2; ++p)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int fl = feat(qpair0(p) + 8 * q);
+                        stage(nh, fl, xlo[p][q]);
+                        stage(nh, fl + HALF, xhi[p][q]);
+                    }
+                continue;
+            }
+            // keys: per-head norm (a 128-wide head: both groups of the wave; 64-wide: one
+            // group), over the lane, the lane holding the token's other pairs (lane ^ 32)
+            float kinv[2] = {1.f, 1.f};
+            if constexpr (KN) {
+                float ss[2] = {0.f, 0.f};
+#pragma unroll
+                for (int p = 0; p < 2; ++p)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) ss[p] += xlo[p][q][e] * xlo[p][q][e] + xhi[p][q][e] * xhi[p][q][e];
+                ss[0] += __shfl_xor(ss[0], 32);
+                ss[1] += __shfl_xor(ss[1], 32);
+                if constexpr (DH == 128) {
+                    const float t = 1.0f / sqrtf((ss[0] + ss[1]) * (1.0f / (float)DH) + a.kn_eps);
+                    kinv[0] = kinv[1] = t;
+                } else {
+                    kinv[0] = 1.0f / sqrtf(ss[0] * (1.0f / (float)DH) + a.kn_eps);
+                    kinv[1] = 1.0f / sqrtf(ss[1] * (1.0f / (float)DH) + a.kn_eps);
+                }
+            }
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int qp = qpair0(p) + 8 * q;
+                    const int fl = feat(qp);
+                    // (cos, sin) of the lane's four pairs from the tile's RoPE rows; no table:
+                    // the identity turn
+                    f32x4 c01{1.f, 0.f, 1.f, 0.f}, c23{1.f, 0.f, 1.f, 0.f};
+                    if (a.rope) {
+                        const int c0 = (qp % HALF) / 2;
+                        const char* row = lds + kTab + nl * kTabRow;
+                        c01 = *(const f32x4*)(row + ((c0 ^ (nl % CPR)) << 4));
+                        c23 = *(const f32x4*)(row + (((c0 + 1) ^ (nl % CPR)) << 4));
+                    }
+                    const float cs[4] = {c01[0], c01[2], c23[0], c23[2]};
+                    const float sn[4] = {c01[1], c01[3], c23[1], c23[3]};
+                    float lo[4], hi[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float x = xlo[p][q][e], y = xhi[p][q][e];
+                        if constexpr (KN) {
+                            x *= kinv[p] * glo[p][q][e];
+                            y *= kinv[p] * ghi[p][q][e];
+                        }
+                        lo[e] = x * cs[e] - y * sn[e];
+                        hi[e] = y * cs[e] + x * sn[e];
+                    }
+                    stage(nh, fl, lo);
+                    stage(nh, fl + HALF, hi);
+                }
+        }
+        __syncthreads();
+#pragma unroll 2
+        for (int pz = 0; pz < kHalfTok / 4; ++pz) {
+            const int nh = pz * 4 + w;
+            const int64_t base = rbase[h * kHalfTok + nh];
+            if (base < 0) continue;
+            const u32x4 val = *(const u32x4*)(lds + nh * (kFT4 * 2) + ((c ^ nh) << 4));
+            *(u32x4*)(pool + base + head * a.stride_head + dim) = val;
+        }
+        if (h == 0) __syncthreads();
     }
 }
 
@@ -680,6 +909,23 @@ static size_t slot_bytes(const rf_fill_weights* w, int64_t rows) {
     return hb + pb;
 }
 
+// The K/V launch of a group of layers: the 512-feature x 128-token tile kernel for bf16 when
+// the K and V halves are whole 512-feature tiles, else the 256 x 256 one.
+template <typename T, int DH, bool NORM, bool BIAS, bool KN>
+static void launch_kv(KVArgs ka, int64_t rows, int gsz, hipStream_t stream) {
+    if constexpr (sizeof(T) == 2) {
+        if (ka.kvw % kFT4 == 0) {
+            ka.tok_tiles = (int32_t)ceil_div(rows, (int64_t)kTT4);
+            hipLaunchKernelGGL((k_fill_kv4<DH, NORM, BIAS, KN>), dim3((unsigned)((2 * ka.kvw / kFT4) * ka.tok_tiles * gsz)),
+                               dim3(PackedAGemm4::kThr), 0, stream, ka);
+            return;
+        }
+    }
+    ka.tok_tiles = (int32_t)ceil_div(rows, (int64_t)kTT);
+    hipLaunchKernelGGL((k_fill_kv<T, DH, NORM, BIAS, false, KN>), dim3((unsigned)((2 * ka.kvw / kFT) * ka.tok_tiles * gsz)),
+                       dim3(KVCore<T>::G::kThr), 0, stream, ka);
+}
+
 template <typename T>
 static rf_status launch_fill(const rf_fill_weights* w, int32_t n_layers, const void* X, int64_t ldx,
                              int64_t t0, int64_t t1, int64_t pos0, const rf_cache_desc* cache,
@@ -719,18 +965,12 @@ static rf_status launch_fill(const rf_fill_weights* w, int32_t n_layers, const v
         hipLaunchKernelGGL(k_fill_map<T>, dim3((w->d / kFT) * tok_tiles * gsz), dim3(MapCore<T>::G::kThr), 0, stream, ma);
         rf_status st = check_launch("rf_fill: map kernel");
         if (st != RF_OK) return st;
-        const dim3 kv_grid((2 * ka.kvw / kFT) * tok_tiles * gsz);
-        const dim3 blk(KVCore<T>::G::kThr);
         if (w->k_norm) {
-            if (w->head_dim == 128)
-                hipLaunchKernelGGL((k_fill_kv<T, 128, true, false, false, true>), kv_grid, blk, 0, stream, ka);
-            else
-                hipLaunchKernelGGL((k_fill_kv<T, 64, true, false, false, true>), kv_grid, blk, 0, stream, ka);
+            if (w->head_dim == 128) launch_kv<T, 128, true, false, true>(ka, rows, gsz, stream);
+            else launch_kv<T, 64, true, false, true>(ka, rows, gsz, stream);
         } else {
-            if (w->head_dim == 128)
-                hipLaunchKernelGGL((k_fill_kv<T, 128, true, false>), kv_grid, blk, 0, stream, ka);
-            else
-                hipLaunchKernelGGL((k_fill_kv<T, 64, true, false>), kv_grid, blk, 0, stream, ka);
+            if (w->head_dim == 128) launch_kv<T, 128, true, false, false>(ka, rows, gsz, stream);
+            else launch_kv<T, 64, true, false, false>(ka, rows, gsz, stream);
         }
         st = check_launch("rf_fill: kv kernel");
         if (st != RF_OK) return st;
@@ -782,18 +1022,12 @@ static rf_status launch_fill_composed(const rf_fill_composed_weights* w, int32_t
         hipLaunchKernelGGL(k_fill_norm, dim3((w->d / kFT) * tok_tiles * gsz), dim3(PackedAGemm::kThr), 0, stream, na);
         rf_status st = check_launch("rf_fill_composed: quadratic-form kernel");
         if (st != RF_OK) return st;
-        const dim3 kv_grid((2 * kvw / kFT) * tok_tiles * gsz);
-        const dim3 blk(PackedAGemm::kThr);
         if (w->k_norm) {
-            if (w->head_dim == 128)
-                hipLaunchKernelGGL((k_fill_kv<bf16_t, 128, true, true, false, true>), kv_grid, blk, 0, stream, ka);
-            else
-                hipLaunchKernelGGL((k_fill_kv<bf16_t, 64, true, true, false, true>), kv_grid, blk, 0, stream, ka);
+            if (w->head_dim == 128) launch_kv<bf16_t, 128, true, true, true>(ka, rows, gsz, stream);
+            else launch_kv<bf16_t, 64, true, true, true>(ka, rows, gsz, stream);
         } else {
-            if (w->head_dim == 128)
-                hipLaunchKernelGGL((k_fill_kv<bf16_t, 128, true, true>), kv_grid, blk, 0, stream, ka);
-            else
-                hipLaunchKernelGGL((k_fill_kv<bf16_t, 64, true, true>), kv_grid, blk, 0, stream, ka);
+            if (w->head_dim == 128) launch_kv<bf16_t, 128, true, true, false>(ka, rows, gsz, stream);
+            else launch_kv<bf16_t, 64, true, true, false>(ka, rows, gsz, stream);
         }
         st = check_launch("rf_fill_composed: kv kernel");
         if (st != RF_OK) return st;
@@ -812,7 +1046,7 @@ static void launch_translate_group(const KVArgs& ka, int gsz, bool headwise, hip
         }
     }
     // fp32 (tiny widths) computes head-wise maps densely: their zero blocks add nothing
-    hipLaunchKernelGGL((k_fill_kv<T, DH, false, BIAS, false, KN>), grid, dim3(KVCore<T>::G::kThr), 0, stream, ka);
+    launch_kv<T, DH, false, BIAS, KN>(ka, ka.rows, gsz, stream);
 }
 
 template <typename T, int DH>

@@ -15,6 +15,17 @@ SMALL_BF16_H64 = synth.scaled(synth.C2, name="bf16-d256-dh64", d=256, n_layers=3
                               head_dim=64, prompt_tokens=600, rope_base=1e4)
 SMALL_PAGED = synth.scaled(synth.C5, name="paged-d512", d=512, n_layers=4, split=1, n_kv_heads=2, head_dim=128,
                            prompt_tokens=1200)
+# K/V widths that are whole 512-feature tiles run the K/V product on 512 x 128 tiles (the
+# configs above, 256 wide, the 256 x 256 kernel): 4 x 128 and 8 x 64 heads
+WIDE_BF16 = synth.scaled(synth.C2, name="bf16-d512-kv512", d=512, n_layers=4, split=2, n_kv_heads=4, head_dim=128,
+                         prompt_tokens=900)
+WIDE_BF16_H64 = synth.scaled(synth.C2, name="bf16-d512-kv8x64", d=512, n_layers=3, split=1, n_kv_heads=8,
+                             head_dim=64, prompt_tokens=600, rope_base=1e4)
+# (the Llama-8B-shaped input law, paged: at d = 512 the long-context law's five 20x outlier
+# channels make K heavy-tailed enough that bf16 storage alone reaches 2.2e-2 of RMS, with the
+# 256 x 256 kernel and this one alike)
+WIDE_PAGED = synth.scaled(synth.C2, name="paged-d512-kv1024", d=512, n_layers=3, split=1, n_kv_heads=8,
+                          head_dim=128, prompt_tokens=1200, paged=True, block_size=16)
 
 
 def _check(res, label):
@@ -49,6 +60,23 @@ def test_fill_bf16_head_dim_64_and_identity_maps():
 def test_fill_paged_chunked_unaligned():
     # paged cache (block 16, shuffled table), fill [19, 1100) in chunks of 300 tokens
     _check(run_fill_case(FillCase(SMALL_PAGED, 19, 1100, chunk=300)), "paged chunked")
+
+
+@pytest.mark.parametrize("composed", [False, True])
+def test_fill_512_wide_kv_tiles(composed):
+    # ragged range across several 128-token tiles, far positions, identity maps, paged in
+    # chunks, both head widths, per-head key norm.  Each case keeps a side of a layer under
+    # about 0.7 M values: the bar is a maximum over every value, and the bf16 rounding of the
+    # stored cache alone (half an ulp, up to 2^-8 of a value) reaches it for the largest values
+    # of a few million Gaussian draws (about 5.4 RMS)
+    for case, label in ((FillCase(WIDE_BF16, 37, 737, pos0=5, composed=composed), "kv512 ragged"),
+                        (FillCase(WIDE_BF16, 0, 129, composed=composed), "kv512 [0,129)"),
+                        (FillCase(WIDE_BF16, 5, 700, pos0=70000, k_norm=True, composed=composed), "kv512 key norm"),
+                        (FillCase(WIDE_BF16_H64, 3, 517, maps="identity", composed=composed), "kv8x64 identity"),
+                        (FillCase(WIDE_BF16_H64, 0, 600, k_norm=True, composed=composed), "kv8x64 key norm"),
+                        (FillCase(WIDE_PAGED, 19, 619, chunk=200, composed=composed), "kv1024 paged chunks"),
+                        (FillCase(WIDE_PAGED, 0, 600, chunk=250, k_norm=True, composed=composed), "kv1024 paged key norm")):
+        _check(run_fill_case(case), f"{label}{' composed' if composed else ''}")
 
 
 def test_fill_per_head_key_norm():
