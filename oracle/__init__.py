@@ -8,7 +8,9 @@ Everything is computed in float64 with NumPy/SciPy from the stored input values,
 exactly.  Sources are the RidgeFill project page ("Method": steps 1-4 and Figure 2;
 "Abstract") and, for the pre-norm storing order and the relative ridge convention, the
 KV-Lingo page (sections 2 and 3.1, Appendix B.2 "Protocol").  ``translate`` follows the
-KV-Lingo page's token-wise linear cache translators (sections 3.1 and 3.2).
+KV-Lingo page's token-wise linear cache translators (sections 3.1 and 3.2).  ``quantize_rows``
+is the reading of the project page's int8 maps ("Code, data and maps") as row-wise
+symmetric weight-only codes.
 
 Readings taken where the pages are silent (each one is listed in the design notes):
   * the map is W = (X~^T X~ + lambda I)^-1 X~^T Y~ on mean-centred rows with the intercept
@@ -27,6 +29,7 @@ from .ridge import (NotSPD, gram_sums, fit, fit_from_sums, fit_pinv, ridge_objec
                     solve_columns_from_data, stationarity_residual, stationarity_residual_from_sums)
 from .fill import rope_inverse_frequencies, rope_rotate, rmsnorm, fill_layer, fill
 from .gdn import gdn_state, l2_normalise
+from .quant import quantize_rows, dequantize_rows
 from .translate import (relative_depth_centre, relative_depth_sources, headwise_dense,
                         translate_layer, translate, fit_translator, fit_r2, r2_assignment,
                         greedy_sources)
@@ -36,4 +39,5 @@ __all__ = ["NotSPD", "gram_sums", "fit", "fit_from_sums", "fit_pinv", "ridge_obj
            "rope_inverse_frequencies", "rope_rotate", "rmsnorm",
            "fill_layer", "fill", "relative_depth_centre", "relative_depth_sources",
            "headwise_dense", "translate_layer", "translate", "fit_translator", "fit_r2",
-           "r2_assignment", "greedy_sources", "gdn_state", "l2_normalise"]
+           "r2_assignment", "greedy_sources", "gdn_state", "l2_normalise", "quantize_rows",
+           "dequantize_rows"]
