@@ -152,14 +152,15 @@ def cpu_baseline(cfg, n_tokens: int, n_fit_rows: int):
     }
 
 
-def streamed_leg(steps: int, stream, dev, cfg, fw, Xp, cache, filler, ring_slots=2, layers_per_slot=2):
+def streamed_leg(steps: int, stream, dev, cfg, fw, Xp, cache, filler, ring_slots=2, layers_per_slot=2, w32=None):
     """The same fill with its maps streamed from page-locked host memory (rf_fill_streamed),
-    alternated with the resident fill so both see the same clock and power state."""
+    alternated with the resident fill so both see the same clock and power state.  With the
+    fp32 maps ``w32`` also the weight-only int8 maps (rf_quantize_map), resident and streamed."""
     import dataclasses
 
     import torch
 
-    from linear_kv_cache_amd.runner import StreamedFiller, pinned_copy
+    from linear_kv_cache_amd.runner import Filler, StreamedFiller, pinned_copy, quantize_map
 
     T, L = cfg.fill_tokens, cfg.n_targets
     host = [pinned_copy(W.cpu()) for W in fw.W_map]
@@ -181,13 +182,53 @@ def streamed_leg(steps: int, stream, dev, cfg, fw, Xp, cache, filler, ring_slots
         str_ms.append(timed(sf))
     rm, sm = statistics.median(res_ms), statistics.median(str_ms)
     map_bytes = L * cfg.d * cfg.d * 2
-    return {"what": "rf_fill with the maps in page-locked host memory, streamed through a device ring; "
-                    "alternated with the resident fill", "ring_slots": ring_slots, "layers_per_slot": layers_per_slot,
-            "ring_MiB": round(ring_slots * layers_per_slot * cfg.d * cfg.d * 2 / 2 ** 20, 1),
-            "resident_maps_MiB": round(map_bytes / 2 ** 20, 1),
-            "ms_median": round(sm, 3), "resident_ms_median": round(rm, 3),
-            "tokens_per_s": round(T / (sm / 1e3), 1), "vs_resident": round(rm / sm, 4),
-            "host_to_device_GBps": round(map_bytes / (sm / 1e3) / 1e9, 1)}
+    out = {"what": "rf_fill with the maps in page-locked host memory, streamed through a device ring; "
+                   "alternated with the resident fill", "ring_slots": ring_slots, "layers_per_slot": layers_per_slot,
+           "ring_MiB": round(ring_slots * layers_per_slot * cfg.d * cfg.d * 2 / 2 ** 20, 1),
+           "resident_maps_MiB": round(map_bytes / 2 ** 20, 1),
+           "ms_median": round(sm, 3), "resident_ms_median": round(rm, 3),
+           "tokens_per_s": round(T / (sm / 1e3), 1), "vs_resident": round(rm / sm, 4),
+           "host_to_device_GBps": round(map_bytes / (sm / 1e3) / 1e9, 1)}
+    if w32 is not None:
+        qs = [quantize_map(W) for W in w32]
+        qw = dataclasses.replace(fw, W_map=[q for q, _ in qs], map_scale=[s_ for _, s_ in qs])
+        qf = Filler(qw, cfg.rope_base, T, T, dev, ws_slots=8)
+        qsf = StreamedFiller(dataclasses.replace(qw, W_map=[pinned_copy(q.cpu()) for q, _ in qs]), cfg.rope_base, T,
+                             T, dev, ring_slots=ring_slots, layers_per_slot=layers_per_slot)
+        timed(qf)
+        timed(qsf)
+        bf_ms, qr_ms, qs_ms = [], [], []
+        for _ in range(steps):
+            bf_ms.append(timed(filler))
+            qr_ms.append(timed(qf))
+            qs_ms.append(timed(qsf))
+        bm, qrm, qsm = statistics.median(bf_ms), statistics.median(qr_ms), statistics.median(qs_ms)
+        qbytes = L * cfg.d * cfg.d
+        # what the int8 codes change: the caches of both fills of the last layer, K and V, their
+        # largest and RMS difference relative to the RMS of the bf16-map caches (a property of
+        # the quantisation, outside the parity bar, which holds against the dequantised codes)
+        from linear_kv_cache_amd.runner import alloc_cache
+        c2 = alloc_cache(L, cfg.n_kv_heads, cfg.head_dim, T, cfg.torch_dtype, dev)
+        filler.fill(Xp, 0, T, 0, cache, stream)
+        qf.fill(Xp, 0, T, 0, c2, stream)
+        torch.cuda.synchronize()
+        dev_max, dev_rms = 0.0, 0.0
+        for a, b_ in ((cache.k[L - 1], c2.k[L - 1]), (cache.v[L - 1], c2.v[L - 1])):
+            a, b_ = a.float(), b_.float()   # contiguous pools of exactly the T filled tokens
+            r = float(a.pow(2).mean().sqrt())
+            dev_max = max(dev_max, float((a - b_).abs().max()) / r)
+            dev_rms = max(dev_rms, float((a - b_).pow(2).mean().sqrt()) / r)
+        del c2
+        out["int8_maps"] = {
+            "what": "weight-only int8 maps (rf_quantize_map: row-wise symmetric codes and fp32 row scales), "
+                    "resident and streamed, alternated with the bf16 resident fill",
+            "maps_MiB": round(qbytes / 2 ** 20, 1), "resident_ms_median": round(qrm, 3),
+            "streamed_ms_median": round(qsm, 3), "bf16_resident_ms_median": round(bm, 3),
+            "streamed_tokens_per_s": round(T / (qsm / 1e3), 1), "streamed_vs_int8_resident": round(qrm / qsm, 4),
+            "streamed_vs_bf16_resident": round(bm / qsm, 4), "resident_vs_bf16_resident": round(bm / qrm, 4),
+            "host_to_device_GBps": round(qbytes / (qsm / 1e3) / 1e9, 1),
+            "kv_vs_bf16_maps_max_rel_rms": round(dev_max, 4), "kv_vs_bf16_maps_rms_rel_rms": round(dev_rms, 4)}
+    return out
 
 
 def translate_leg(steps: int, stream, dev, tc=None):
@@ -689,8 +730,14 @@ def main():
     out["fit"]["stationarity_residual_max"] = float(resid_r.max().item())
     del cond_r, resid_r
     if not args.no_streamed:
-        log("streamed maps: the fill with its maps in page-locked host memory")
-        out["fill_streamed"] = streamed_leg(args.steps, stream, dev, cfg, fw, Xp, cache, filler)
+        log("streamed maps: the fill with its maps in page-locked host memory (bf16, then int8)")
+        # the fp32 maps of one more solve (outside the timed steps) feed the int8 quantiser
+        W32 = torch.empty(L, d, d, dtype=torch.float32, device=dev)
+        rf.rf_solve(state.desc, state.buf, lam, rf.RF_LAMBDA_ABSOLUTE, list(range(L)), W32, None, b, info,
+                    solve_ws, stream)
+        out["fill_streamed"] = streamed_leg(args.steps, stream, dev, cfg, fw, Xp, cache, filler,
+                                            w32=[W32[i] for i in range(L)])
+        del W32
     if not args.no_translate:
         del Xc, Yc
         out["translate"] = translate_leg(args.steps, stream, dev)

@@ -326,6 +326,23 @@ rf_status rf_pack_weights(rf_dtype dtype, int64_t rows, int64_t cols, const void
                           int32_t rope_head_dim, void* d_dst, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Weight-only int8 maps.  RidgeFill project page, "Code, data and maps" (the ridge maps on
+ * Hugging Face): some published maps are int8; the page gives no scheme, and this is the
+ * reading taken: symmetric codes per output row.  For each row o of the fp32 map d_W
+ * ([rows][ld], row-major, out-feature major as rf_solve writes it), in fp32:
+ *     s_o = max_i |W[o][i]| / 127,   q[o][i] = round_half_even(W[o][i] / s_o) in [-127, 127]
+ * (a row of zeros: s_o = 0, q_o = 0).  The codes go to d_q (rows * cols bytes) in the packed
+ * order of rf_pack_weights with rope_head_dim 0, one byte per element; the scales to
+ * d_scale ([rows] fp32).  Half the bytes of a bf16 map for the fill's map product (which then
+ * applies diag(s) q): the streamed fill copies half as much.  Maps must be finite.
+ * Supported: rows % 256 == 0, cols % 64 == 0, rows and cols <= 65536, ld >= cols and a multiple
+ * of 4, d_W and d_scale 16-B aligned, d_q 16-B aligned.  Asynchronous on ``stream``; nothing
+ * is allocated.
+ * ------------------------------------------------------------------------------------- */
+rf_status rf_quantize_map(int64_t rows, int64_t cols, const float* d_W, int64_t ld, void* d_q, float* d_scale,
+                          void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * The fill.  RidgeFill project page, "Method" steps 2-4 and Figure 2(b): for every token
  * t in [t0, t1) and every listed late layer l,
  *     h = x_t W_l^T + b_l                              (predicted layer input)
@@ -352,6 +369,11 @@ rf_status rf_pack_weights(rf_dtype dtype, int64_t rows, int64_t cols, const void
  * d_ws   : rf_fill_workspace_bytes(weights, t1 - t0) bytes, 256-B aligned
  * Supported: d % 256 == 0, head_dim in {64, 128}, (n_kv_heads*head_dim) % 256 == 0,
  * dtype F32 or BF16 (all of X, maps, projections and pools share it).
+ * Weight-only int8 maps (map_scale non-NULL, BF16 only): W_map[l] holds int8 codes in the
+ * packed order of rf_quantize_map (one byte per element) and map_scale[l] ([d] fp32, 16-B
+ * aligned) their row scales; the fill applies the map diag(map_scale[l]) codes, i.e.
+ *     h = (x codes^T) * map_scale + b_map        (the codes widened to bf16 exactly)
+ * and everything after h is as above.
  * ------------------------------------------------------------------------------------- */
 typedef struct {
     int32_t d;
@@ -366,6 +388,7 @@ typedef struct {
     const void* const* W_v;
     const float* const* k_norm;   /* NULL, or per layer fp32 [head_dim]: per-head key norm    */
     float k_norm_eps;             /* its epsilon (inside the root), when k_norm is given      */
+    const float* const* map_scale; /* NULL, or per layer fp32 [d]: W_map are int8 codes       */
 } rf_fill_weights;
 
 size_t rf_fill_workspace_bytes(const rf_fill_weights* weights, int64_t max_rows);
@@ -468,8 +491,8 @@ rf_status rf_fill_static(const rf_fill_weights* weights, int32_t n_layers,
  * stay in host memory and reach the GPU layer by layer while the fill runs, for far less
  * device memory than resident maps at nearly the same speed.  Computes exactly what rf_fill
  * computes (the same kernels, bit-identical results), with W_map[l] HOST pointers to the
- * maps in the layout rf_fill takes (BF16 packed), in page-locked memory (hipHostMalloc) so
- * the copies run asynchronously.  Every other weight is a device pointer as for rf_fill.
+ * maps in the layout rf_fill takes (BF16 packed, or int8 codes with device map_scale), in
+ * page-locked memory (hipHostMalloc) so the copies run asynchronously.  Every other weight is a device pointer as for rf_fill.
  *  d_ring      : device buffer of ring_bytes >= rf_fill_streamed_ring_bytes() bytes, 256-B
  *                aligned: ring_slots slots of layers_per_slot maps
  *  d_ws        : rf_fill_workspace_bytes(weights, rows) * layers_per_slot bytes, rows = the

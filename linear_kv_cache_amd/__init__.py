@@ -66,7 +66,7 @@ class rf_fill_weights(C.Structure):
     _fields_ = [("d", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("rms_eps", C.c_float),
                 ("dtype", C.c_int), ("W_map", C.POINTER(C.c_void_p)), ("b_map", C.POINTER(C.c_void_p)),
                 ("gamma", C.POINTER(C.c_void_p)), ("W_k", C.POINTER(C.c_void_p)), ("W_v", C.POINTER(C.c_void_p)),
-                ("k_norm", C.POINTER(C.c_void_p)), ("k_norm_eps", C.c_float)]
+                ("k_norm", C.POINTER(C.c_void_p)), ("k_norm_eps", C.c_float), ("map_scale", C.POINTER(C.c_void_p))]
 
 
 class rf_fill_composed_weights(C.Structure):
@@ -112,6 +112,7 @@ _sig = {
     "rf_cache_layout": (C.c_int, [C.POINTER(rf_cache_desc), C.POINTER(rf_cache_layout_t)]),
     "rf_rope_table": (C.c_int, [C.c_double, C.c_int32, C.c_int64, _P, _P]),
     "rf_pack_weights": (C.c_int, [C.c_int, C.c_int64, C.c_int64, _P, C.c_int64, C.c_int32, _P, _P]),
+    "rf_quantize_map": (C.c_int, [C.c_int64, C.c_int64, _P, C.c_int64, _P, _P, _P]),
     "rf_fill_workspace_bytes": (C.c_size_t, [C.POINTER(rf_fill_weights), C.c_int64]),
     "rf_fill": (C.c_int, [C.POINTER(rf_fill_weights), C.c_int32, _P, C.c_int64, C.c_int64, C.c_int64, C.c_int64,
                           C.POINTER(rf_cache_desc), C.POINTER(_P), C.POINTER(_P), _P, C.c_int64, _P, C.c_int64,
@@ -301,12 +302,20 @@ def rf_pack_weights(W, dst, rope_head_dim: int = 0, stream=None):
                                 _stream(stream)))
 
 
+def rf_quantize_map(W, q, scale, stream=None):
+    """W: [rows, >=cols] fp32 map (row stride = ld); q: rows*cols int8 codes out (packed);
+    scale: [rows] fp32 out."""
+    rows, cols = W.shape
+    _check(_lib.rf_quantize_map(rows, cols, _ptr(W), W.stride(0), _ptr(q), _ptr(scale), _stream(stream)))
+
+
 @dataclass
 class FillWeights:
     """Per-layer weights of the layers one rf_fill call fills (tensors on the device).
 
     BF16 weights are in the packed layout: maps as rf_pack_weights(rope_head_dim=0) or
-    rf_solve's bf16 output leave them, W_k and W_v as rf_pack_weights(rope_head_dim=head_dim)."""
+    rf_solve's bf16 output leave them, W_k and W_v as rf_pack_weights(rope_head_dim=head_dim).
+    With ``map_scale`` (a list of [d] fp32 tensors) the maps are int8 codes of rf_quantize_map."""
 
     d: int
     n_kv_heads: int
@@ -320,14 +329,17 @@ class FillWeights:
     W_v: list
     k_norm: Optional[list] = None
     k_norm_eps: float = 1e-6
+    map_scale: Optional[list] = None
 
     def _c(self):
         arrs = [_ptr_array(x) for x in (self.W_map, self.b_map, self.gamma, self.W_k, self.W_v)]
         kn = None if self.k_norm is None else _ptr_array(self.k_norm)
+        ms = None if self.map_scale is None else _ptr_array(self.map_scale)
         w = rf_fill_weights(self.d, self.n_kv_heads, self.head_dim, self.rms_eps, _dtype_code(self.dtype),
                             *[C.cast(a, C.POINTER(_P)) for a in arrs],
-                            C.cast(kn, C.POINTER(_P)) if kn is not None else C.POINTER(_P)(), self.k_norm_eps)
-        return w, (arrs, kn)
+                            C.cast(kn, C.POINTER(_P)) if kn is not None else C.POINTER(_P)(), self.k_norm_eps,
+                            C.cast(ms, C.POINTER(_P)) if ms is not None else C.POINTER(_P)())
+        return w, (arrs, kn, ms)
 
 
 def rf_fill_workspace_bytes(weights: FillWeights, max_rows: int) -> int:

@@ -255,6 +255,7 @@ rf_status rf_fill_compose(const rf_fill_weights* w, int32_t n_layers, void* cons
     RF_REQUIRE(w, RF_ERR_INVALID_ARG, "rf_fill_compose: null weights");
     RF_REQUIRE(n_layers >= 0, RF_ERR_INVALID_ARG, "rf_fill_compose: n_layers must be >= 0");
     RF_REQUIRE(w->dtype == RF_BF16, RF_ERR_UNSUPPORTED, "rf_fill_compose: BF16 weights only");
+    RF_REQUIRE(!w->map_scale, RF_ERR_UNSUPPORTED, "rf_fill_compose: int8 maps are not composed (use bf16 maps)");
     RF_REQUIRE(w->d > 0 && w->d % kCT == 0 && w->d <= (1 << 16), RF_ERR_UNSUPPORTED,
                "rf_fill_compose: d must be a positive multiple of 256, at most 65536");
     RF_REQUIRE(w->head_dim == 64 || w->head_dim == 128, RF_ERR_UNSUPPORTED, "rf_fill_compose: head_dim must be 64 or 128");

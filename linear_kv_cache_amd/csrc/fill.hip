@@ -43,6 +43,7 @@ struct MapArgs {
     const void* W[kMaxGroup];
     const float* bias[kMaxGroup];
     const float* gamma[kMaxGroup];
+    const float* scale[kMaxGroup];   // Q8: the map rows' scales (W = diag(scale) codes)
 };
 
 struct KVArgs {
@@ -126,9 +127,13 @@ __device__ inline void fill_gemm(PackedAGemm& gm, char* lds, const void* A, int6
 template <typename T> struct MapStage { static constexpr bool kLds = false; static constexpr int kBytes = 0; };
 template <> struct MapStage<bf16_t> { static constexpr bool kLds = true; static constexpr int kBytes = kTT * kFT * 2; };
 
-template <typename T>
+// Q8 (bf16 only): the map is weight-only int8, codes packed like the bf16 map with one byte per
+// element and one fp32 scale per row: the product runs on the codes (widened to bf16 in
+// registers, exactly) and each row of it is multiplied by its scale before the intercept.
+template <typename T, bool Q8 = false>
 __global__ __launch_bounds__(MapCore<T>::G::kThr) void k_fill_map(MapArgs a) {
     using G = typename MapCore<T>::G;
+    static_assert(!Q8 || std::is_same<T, bf16_t>::value, "int8 maps with bf16 prompt states");
     constexpr int kWaveRows = G::kThr / 64 / G::WGN;
     constexpr int kRedOff = MapStage<T>::kBytes;  // [kWaveRows][kTT] fp32 partial sums after the stage
     constexpr int kEpi = kRedOff + kWaveRows * kTT * 4;
@@ -138,8 +143,13 @@ __global__ __launch_bounds__(MapCore<T>::G::kThr) void k_fill_map(MapArgs a) {
     fill_tile(a.d / kFT, a.tok_tiles, g, mt, tt);
     const int64_t n0 = (int64_t)tt * kTT;
     G gm;
-    fill_gemm(gm, lds, (const T*)a.W[g] + (int64_t)mt * kFT * a.d, a.d, kFT, (const T*)a.X + n0 * a.ldx, a.ldx,
-              a.rows - n0, a.d / G::BK);
+    if constexpr (Q8)
+        gm.template run<false, false, false, true>(
+            lds, PipeOperand{(const int8_t*)a.W[g] + (int64_t)mt * kFT * a.d, a.d, kFT},
+            PipeOperand{(const T*)a.X + n0 * a.ldx, a.ldx, a.rows - n0}, a.d / G::BK);
+    else
+        fill_gemm(gm, lds, (const T*)a.W[g] + (int64_t)mt * kFT * a.d, a.d, kFT, (const T*)a.X + n0 * a.ldx, a.ldx,
+                  a.rows - n0, a.d / G::BK);
 
     // the main loop ended on a barrier: LDS is free
     const int lane = threadIdx.x & 63;
@@ -147,7 +157,7 @@ __global__ __launch_bounds__(MapCore<T>::G::kThr) void k_fill_map(MapArgs a) {
     float* red = (float*)(lds + kRedOff);
     // bias and gamma of this lane's SM x 4 groups of 4 features, read once (16-byte loads) before any
     // staging write, so no LDS read waits behind the writes
-    f32x4 bb[G::SM][4], gg[G::SM][4];
+    f32x4 bb[G::SM][4], gg[G::SM][4], sc[G::SM][4];
 #pragma unroll
     for (int i = 0; i < G::SM; ++i)
 #pragma unroll
@@ -155,6 +165,7 @@ __global__ __launch_bounds__(MapCore<T>::G::kThr) void k_fill_map(MapArgs a) {
             const int f = mt * kFT + G::row_of(i, 4 * q);
             bb[i][q] = *(const f32x4*)(a.bias[g] + f);
             gg[i][q] = *(const f32x4*)(a.gamma[g] + f);
+            if constexpr (Q8) sc[i][q] = *(const f32x4*)(a.scale[g] + f);
         }
     T* H = (T*)a.H + g * a.h_slot;
 #pragma unroll
@@ -170,7 +181,8 @@ __global__ __launch_bounds__(MapCore<T>::G::kThr) void k_fill_map(MapArgs a) {
                 float h[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    h[e] = gm.acc[i][j][4 * q + e] + bb[i][q][e];
+                    if constexpr (Q8) h[e] = gm.acc[i][j][4 * q + e] * sc[i][q][e] + bb[i][q][e];
+                    else h[e] = gm.acc[i][j][4 * q + e] + bb[i][q][e];
                     ss += h[e] * h[e];
                 }
                 const f32x4 gq = gg[i][q];
@@ -903,6 +915,41 @@ __global__ void k_pack_weights(const S* __restrict__ src, int64_t ld, int64_t co
     *(u32x4*)(dst + e) = load8_bf16(src + row * ld + k);
 }
 
+// Row-wise symmetric int8 codes of an fp32 map: one work-group per row; the row's absolute
+// maximum by a work-group reduction, then each thread codes chunks of 8 consecutive columns
+// and writes them as 8 bytes in packed order.  The code is rint(w / s) in fp32 (IEEE
+// division, ties to even), clamped to [-127, 127].
+__global__ __launch_bounds__(256) void k_quantize_map(const float* __restrict__ W, int64_t ld, int64_t cols,
+                                                      int8_t* __restrict__ q, float* __restrict__ scale) {
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const float* src = W + row * ld;
+    float m = 0.f;
+    for (int64_t c = threadIdx.x * 4; c < cols; c += 256 * 4) {
+        const f32x4 v = *(const f32x4*)(src + c);
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = amax / 127.0f;
+    if (threadIdx.x == 0) scale[row] = s;
+    const int64_t base = (row >> 8) * 256 * cols + packed_row_part((int)(row & 255));
+    for (int64_t c = threadIdx.x * 8; c < cols; c += 256 * 8) {
+        const f32x4 a = *(const f32x4*)(src + c), b = *(const f32x4*)(src + c + 4);
+        const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        uint32_t wd[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float r = s > 0.f ? fminf(fmaxf(rintf(x[e] / s), -127.f), 127.f) : 0.f;
+            wd[e >> 2] |= ((uint32_t)(int)r & 0xffu) << (8 * (e & 3));
+        }
+        *(u32x2*)(q + base + packed_col_part((int)c)) = u32x2{wd[0], wd[1]};
+    }
+}
+
 static size_t slot_bytes(const rf_fill_weights* w, int64_t rows) {
     const size_t hb = round_up((size_t)rows * w->d * elem_bytes(w->dtype), 256);
     const size_t pb = round_up((size_t)rows * (w->d / kFT) * sizeof(float), 256);
@@ -957,6 +1004,7 @@ static rf_status launch_fill(const rf_fill_weights* w, int32_t n_layers, const v
         ka.kn_eps = w->k_norm_eps;
         for (int g = 0; g < gsz; ++g) {
             ma.W[g] = w->W_map[l0 + g]; ma.bias[g] = w->b_map[l0 + g]; ma.gamma[g] = w->gamma[l0 + g];
+            ma.scale[g] = w->map_scale ? w->map_scale[l0 + g] : nullptr;
             ka.kn[g] = w->k_norm ? w->k_norm[l0 + g] : nullptr;
             ka.Wk[g] = w->W_k[l0 + g]; ka.Wv[g] = w->W_v[l0 + g];
             ka.in_k[g] = ka.in_v[g] = (const T*)wsc + g * h_slot;
@@ -964,7 +1012,16 @@ static rf_status launch_fill(const rf_fill_weights* w, int32_t n_layers, const v
         }
         ma.tok_tiles = tok_tiles;
         ka.tok_tiles = tok_tiles;
-        hipLaunchKernelGGL(k_fill_map<T>, dim3((w->d / kFT) * tok_tiles * gsz), dim3(MapCore<T>::G::kThr), 0, stream, ma);
+        bool launched = false;
+        if constexpr (std::is_same<T, bf16_t>::value) {
+            if (w->map_scale) {
+                hipLaunchKernelGGL((k_fill_map<T, true>), dim3((w->d / kFT) * tok_tiles * gsz), dim3(MapCore<T>::G::kThr),
+                                   0, stream, ma);
+                launched = true;
+            }
+        }
+        if (!launched)
+            hipLaunchKernelGGL(k_fill_map<T>, dim3((w->d / kFT) * tok_tiles * gsz), dim3(MapCore<T>::G::kThr), 0, stream, ma);
         rf_status st = check_launch("rf_fill: map kernel");
         if (st != RF_OK) return st;
         if (w->k_norm) {
@@ -1142,6 +1199,21 @@ rf_status rf_pack_weights(rf_dtype dtype, int64_t rows, int64_t cols, const void
     return check_launch("rf_pack_weights");
 }
 
+rf_status rf_quantize_map(int64_t rows, int64_t cols, const float* d_W, int64_t ld, void* d_q, float* d_scale,
+                          void* stream) {
+    clear_error();
+    RF_REQUIRE(rows >= 0 && rows % 256 == 0 && cols >= 0 && cols % 64 == 0, RF_ERR_UNSUPPORTED,
+               "rf_quantize_map: rows must be a multiple of 256 and cols a multiple of 64");
+    RF_REQUIRE(rows <= (1 << 16) && cols <= (1 << 16), RF_ERR_UNSUPPORTED, "rf_quantize_map: rows and cols must be <= 65536");
+    if (rows == 0 || cols == 0) return RF_OK;
+    RF_REQUIRE(d_W && d_q && d_scale, RF_ERR_INVALID_ARG, "rf_quantize_map: null pointer argument");
+    RF_REQUIRE(ld >= cols && ld % 4 == 0 && aligned(d_W, 16) && aligned(d_q, 16) && aligned(d_scale, 16),
+               RF_ERR_INVALID_ARG, "rf_quantize_map: rows must be >= cols long with a stride of 4 floats; buffers 16-byte aligned");
+    hipLaunchKernelGGL(k_quantize_map, dim3((unsigned)rows), dim3(256), 0, (hipStream_t)stream, d_W, ld, cols,
+                       (int8_t*)d_q, d_scale);
+    return check_launch("rf_quantize_map");
+}
+
 size_t rf_fill_workspace_bytes(const rf_fill_weights* w, int64_t max_rows) {
     if (!w || w->d <= 0 || w->d % kFT != 0 || max_rows < 0 || !valid_dtype(w->dtype)) return 0;
     return slot_bytes(w, max_rows);
@@ -1173,6 +1245,7 @@ static rf_status check_fill(const char* what, const rf_fill_weights* w, int32_t 
     RF_REQUIRE(w->rms_eps >= 0.f && isfinite(w->rms_eps), RF_ERR_INVALID_ARG, fn + ": rms_eps must be finite and >= 0");
     RF_REQUIRE(!w->k_norm || (w->k_norm_eps >= 0.f && isfinite(w->k_norm_eps)), RF_ERR_INVALID_ARG,
                fn + ": k_norm_eps must be finite and >= 0");
+    RF_REQUIRE(!w->map_scale || w->dtype == RF_BF16, RF_ERR_UNSUPPORTED, fn + ": int8 maps need BF16 weights");
     rf_status st = rf_cache_layout(cache, &L);
     if (st != RF_OK) return st;
     if (n_layers == 0 || t1 == t0) {
@@ -1196,6 +1269,9 @@ static rf_status check_fill(const char* what, const rf_fill_weights* w, int32_t 
         if (w->k_norm)
             RF_REQUIRE(w->k_norm[l] && aligned(w->k_norm[l], 16), RF_ERR_INVALID_ARG,
                        fn + ": key norm weights must be non-null and 16-byte aligned");
+        if (w->map_scale)
+            RF_REQUIRE(w->map_scale[l] && aligned(w->map_scale[l], 16), RF_ERR_INVALID_ARG,
+                       fn + ": int8 map scales must be non-null and 16-byte aligned");
     }
     RF_REQUIRE(aligned(d_rope, 16) && aligned(d_ws, 256), RF_ERR_INVALID_ARG,
                fn + ": rope table must be 16-byte and workspace 256-byte aligned");
@@ -1226,7 +1302,7 @@ static rf_status launch_fill_streamed(const rf_fill_weights* w, int32_t n_layers
                                       const int32_t* table, int64_t n_table, const float* rope, void* ws,
                                       size_t ws_bytes, void* ring, int32_t ring_slots, int32_t per_slot,
                                       int64_t rows_per_fill, hipStream_t stream, hipStream_t copy_stream) {
-    const size_t map_bytes = (size_t)w->d * w->d * sizeof(T);
+    const size_t map_bytes = (size_t)w->d * w->d * (w->map_scale ? 1 : sizeof(T));
     std::vector<hipEvent_t> copied(ring_slots, nullptr), freed(ring_slots, nullptr);
     rf_status st = RF_OK;
     auto destroy = [&]() {
@@ -1278,6 +1354,7 @@ static rf_status launch_fill_streamed(const rf_fill_weights* w, int32_t n_layers
         }
         cw.b_map = w->b_map + l0; cw.gamma = w->gamma + l0; cw.W_k = w->W_k + l0; cw.W_v = w->W_v + l0;
         cw.k_norm = w->k_norm ? w->k_norm + l0 : nullptr;
+        cw.map_scale = w->map_scale ? w->map_scale + l0 : nullptr;
         for (int64_t r0 = t0; r0 < t1 && st == RF_OK; r0 += rows_per_fill) {
             const int64_t r1 = std::min(t1, r0 + rows_per_fill);
             st = launch_fill<T>(&cw, gsz, (const T*)X + (r0 - t0) * ldx, ldx, r0, r1, pos0, cache, L, kc + l0, vc + l0,
@@ -1408,7 +1485,7 @@ rf_status rf_fill(const rf_fill_weights* w, int32_t n_layers, const void* d_X, i
 size_t rf_fill_streamed_ring_bytes(const rf_fill_weights* w, int32_t ring_slots, int32_t layers_per_slot) {
     if (!w || w->d <= 0 || w->d % kFT != 0 || !valid_dtype(w->dtype) || ring_slots < 1 || layers_per_slot < 1)
         return 0;
-    return (size_t)ring_slots * layers_per_slot * w->d * w->d * elem_bytes(w->dtype);
+    return (size_t)ring_slots * layers_per_slot * w->d * w->d * (w->map_scale ? 1 : elem_bytes(w->dtype));
 }
 
 rf_status rf_fill_streamed(const rf_fill_weights* w, int32_t n_layers, const void* d_X, int64_t ldx,

@@ -361,6 +361,21 @@ struct PipeGemmW {
 //   (k / 64) * 16384 + (r / 64) * 4096 + ((k % 64) / 16) * 1024 + ((r % 64) / 32) * 512
 //   + (((k % 16) / 8) * 32 + r % 32) * 8 + k % 8,
 // i.e. k-step, wave, k-slice, block, then the 64 lanes' 16-byte fragments.
+// Eight int8 codes (byte e of the pair of words = element e) as eight bf16 values: each code
+// sign-extended, converted to fp32 and cut to its upper half, which is exact for |code| <= 127.
+__device__ inline bf16x8 i8x8_to_bf16x8(u32x2 v) {
+    u32x4 r;
+#pragma unroll
+    for (int w = 0; w < 2; ++w)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float f0 = (float)((int)(v[w] << (24 - 16 * h)) >> 24);
+            const float f1 = (float)((int)(v[w] << (16 - 16 * h)) >> 24);
+            r[2 * w + h] = (__builtin_bit_cast(uint32_t, f1) & 0xffff0000u) | (__builtin_bit_cast(uint32_t, f0) >> 16);
+        }
+    return __builtin_bit_cast(bf16x8, r);
+}
+
 struct PackedAGemm {
     static constexpr int kThr = 256;
     static constexpr int BM = 256, BN = 256, BK = 64;
@@ -386,11 +401,15 @@ struct PackedAGemm {
     // the K loop visits segments of 4 k-steps (256 columns) seg_stride steps apart: logical step
     // kt reads step (kt / 4) * seg_stride + kt % 4 of both operands.  With REV the K loop runs
     // from the last step down (logical step kt reads step nk - 1 - kt), so tiles of different
-    // lengths that end at the same column read the same columns at the same time.
-    template <bool FOLD = false, bool SEG = false, bool REV = false>
+    // lengths that end at the same column read the same columns at the same time.  With I8 the
+    // packed tile holds int8 codes (the same element order, one byte each): each fragment is an
+    // 8-byte load, widened to bf16 in registers (exact: |code| <= 127 needs 7 bits) just before
+    // its MFMAs.
+    template <bool FOLD = false, bool SEG = false, bool REV = false, bool I8 = false>
     __device__ inline void run(char* lds, const PipeOperand& A, const PipeOperand& B, int nk, int b_fold = 0,
                                int seg_stride = 4) {
         static_assert(!(REV && (FOLD || SEG)), "a reversed K loop reads plain steps");
+        constexpr int AB = I8 ? 1 : 2;   // bytes per A element
         const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
 #pragma unroll
         for (int i = 0; i < SM; ++i)
@@ -406,7 +425,7 @@ struct PackedAGemm {
             return kc;
         };
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<void*>(A.ptr), (short)0, ((REV ? nk - 1 : phys(nk - 1)) + 1) * kStepBytes, 0x00020000);
+            const_cast<void*>(A.ptr), (short)0, ((REV ? nk - 1 : phys(nk - 1)) + 1) * (kStepBytes / 2 * AB), 0x00020000);
         int64_t nb = B.valid < BN ? B.valid : BN;
         if (nb < 0) nb = 0;
         const __amdgpu_buffer_rsrc_t rb =
@@ -422,15 +441,24 @@ struct PackedAGemm {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) cofs[kk] = ((2 * kk + (lane >> 5)) ^ ((lane >> 1) & 7)) << 4;
         // the wave offset stays in the vector offset: a scalar offset must be provably uniform
-        const int av = wave * 8192 + lane * 16;
+        const int av = (wave * 8192 + lane * 16) / 2 * AB;
 
         // A fragments of two k-steps (parity p), 4 slices x 2 blocks each
-        u32x4 fa[2][4][SM];
+        using AFrag = std::conditional_t<I8, u32x2, u32x4>;
+        AFrag fa[2][4][SM];
         auto aload = [&](int p, int kk, int kt) {
             const int kc = phys(kt < nk ? kt : nk - 1);
 #pragma unroll
-            for (int i = 0; i < SM; ++i)
-                fa[p][kk][i] = __builtin_amdgcn_raw_buffer_load_b128(ra, av, kc * kStepBytes + (kk * 2 + i) * 1024, 0);
+            for (int i = 0; i < SM; ++i) {
+                if constexpr (I8)
+                    fa[p][kk][i] = __builtin_amdgcn_raw_buffer_load_b64(ra, av, kc * (kStepBytes / 2) + (kk * 2 + i) * 512, 0);
+                else
+                    fa[p][kk][i] = __builtin_amdgcn_raw_buffer_load_b128(ra, av, kc * kStepBytes + (kk * 2 + i) * 1024, 0);
+            }
+        };
+        auto afrag = [&](int p, int kk, int i) -> bf16x8 {
+            if constexpr (I8) return i8x8_to_bf16x8(fa[p][kk][i]);
+            else return __builtin_bit_cast(bf16x8, fa[p][kk][i]);
         };
         auto gload_b = [&](Regs& g, int kt, int j0, int j1) {
             int kc = kt < nk ? kt : nk - 1;
@@ -454,12 +482,14 @@ struct PackedAGemm {
             for (int j = 0; j < SN; ++j) fb[buf][j] = *(const u32x4*)(st + rB + j * 32 * ROWB + cofs[kk]);
         };
         auto mfma = [&](int buf, int p, int kk, int j0, int j1) {
+            bf16x8 a[SM];
+#pragma unroll
+            for (int i = 0; i < SM; ++i) a[i] = afrag(p, kk, i);
 #pragma unroll
             for (int j = j0; j < j1; ++j)
 #pragma unroll
                 for (int i = 0; i < SM; ++i)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[p][kk][i]),
-                                                                       __builtin_bit_cast(bf16x8, fb[buf][j]),
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], __builtin_bit_cast(bf16x8, fb[buf][j]),
                                                                        acc[i][j], 0, 0, 0);
         };
         // group barriers (mask 0x008 MFMA, 0x100 LDS read, 0x200 LDS write, 0x020 VMEM read)

@@ -13,7 +13,7 @@ from . import (RF_LAYOUT_CONTIGUOUS, RF_LAYOUT_PAGED, RF_PRODUCT_AUTO, ComposedF
                rf_fill_composed_workspace_bytes, rf_fill_streamed, rf_fill_streamed_ring_bytes, rf_fill_workspace_bytes,
                rf_fit_r2, rf_fit_r2_workspace_bytes, rf_gram_select,
                rf_gram_accumulate, rf_gram_init,
-               rf_gram_state_bytes, rf_gram_state_layout, rf_pack_weights, rf_rope_table, rf_solve,
+               rf_gram_state_bytes, rf_gram_state_layout, rf_pack_weights, rf_quantize_map, rf_rope_table, rf_solve,
                rf_solve_headwise, rf_solve_pinv, rf_solve_pinv_workspace_bytes, rf_solve_workspace_bytes,
                rf_translate)
 
@@ -243,16 +243,34 @@ def pack_weights(W: torch.Tensor, rope_head_dim: int = 0, stream=None) -> torch.
     return out
 
 
+def quantize_map(W: torch.Tensor, stream=None):
+    """(codes, scales) of rf_quantize_map for a [rows, cols] map (fp32, or upcast to it): int8
+    codes in packed order and [rows] fp32 row scales."""
+    W32 = W.float().contiguous()
+    q = torch.empty(W.shape[0], W.shape[1], dtype=torch.int8, device=W.device)
+    s = torch.empty(W.shape[0], dtype=torch.float32, device=W.device)
+    rf_quantize_map(W32, q, s, stream)
+    return q, s
+
+
 def fill_weights(d: int, n_kv_heads: int, head_dim: int, rms_eps: float, dtype, W_map, b_map, gamma, W_k, W_v,
-                 stream=None, k_norm=None, k_norm_eps: float = 1e-6) -> FillWeights:
+                 stream=None, k_norm=None, k_norm_eps: float = 1e-6, int8_maps: bool = False) -> FillWeights:
     """FillWeights from row-major weights: bf16 maps and projections are packed first (the
-    fp32 path reads them as they are)."""
+    fp32 path reads them as they are); with ``int8_maps`` (bf16 only) the maps become
+    weight-only int8 codes with row scales (rf_quantize_map)."""
+    scales = None
     if dtype == torch.bfloat16:
-        W_map = [pack_weights(W, 0, stream) for W in W_map]
+        if int8_maps:
+            qs = [quantize_map(W, stream) for W in W_map]
+            W_map, scales = [q for q, _ in qs], [s for _, s in qs]
+        else:
+            W_map = [pack_weights(W, 0, stream) for W in W_map]
         W_k = [pack_weights(W, head_dim, stream) for W in W_k]
         W_v = [pack_weights(W, head_dim, stream) for W in W_v]
+    elif int8_maps:
+        raise ValueError("int8 maps need bf16 weights")
     return FillWeights(d, n_kv_heads, head_dim, rms_eps, dtype, list(W_map), list(b_map), list(gamma), list(W_k),
-                       list(W_v), None if k_norm is None else list(k_norm), k_norm_eps)
+                       list(W_v), None if k_norm is None else list(k_norm), k_norm_eps, scales)
 
 
 class Filler:

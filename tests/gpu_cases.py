@@ -41,6 +41,7 @@ class FillCase:
     max_tokens: Optional[int] = None
     k_norm: bool = False                       # per-head key norm (gamma_k, eps 1e-6)
     composed: bool = False                     # rf_fill_compose + rf_fill_composed instead of rf_fill
+    int8_maps: bool = False                    # weight-only int8 maps (rf_quantize_map)
 
 
 def run_fill_case(case: FillCase, device="cuda"):
@@ -61,7 +62,8 @@ def run_fill_case(case: FillCase, device="cuda"):
     fw = fill_weights(cfg.d, cfg.n_kv_heads, cfg.head_dim, cfg.rms_eps, cfg.torch_dtype,
                       [w.W_map for w in lws_dev], [w.b_map for w in lws_dev], [w.gamma for w in lws_dev],
                       [w.W_k for w in lws_dev], [w.W_v for w in lws_dev],
-                      k_norm=None if gks is None else [gk.to(device) for gk in gks], k_norm_eps=1e-6)
+                      k_norm=None if gks is None else [gk.to(device) for gk in gks], k_norm_eps=1e-6,
+                      int8_maps=case.int8_maps)
     table = None
     if cfg.paged:
         table = synth.block_table(cfg, T, device=device)
@@ -83,7 +85,9 @@ def run_fill_case(case: FillCase, device="cuda"):
     out = {"k_err": [], "v_err": [], "sentinel_ok": True, "finite": True}
     tol = KV_TOL_F32 if cfg.dtype == "f32" else KV_TOL_BF16
     for li, w in enumerate(lws):
-        K_ref, V_ref = oracle.fill_layer(Xs, f64(w.W_map).T, f64(w.b_map), f64(w.gamma), f64(w.W_k).T,
+        # int8 maps: the oracle's own codes of the same fp32 map values, dequantised exactly
+        W_ref = oracle.dequantize_rows(*oracle.quantize_rows(f64(w.W_map))) if case.int8_maps else f64(w.W_map)
+        K_ref, V_ref = oracle.fill_layer(Xs, W_ref.T, f64(w.b_map), f64(w.gamma), f64(w.W_k).T,
                                          f64(w.W_v).T, case.pos0 + rows.astype(np.float64), cfg.n_kv_heads,
                                          cfg.head_dim, cfg.rms_eps, cfg.rope_base,
                                          None if gks is None else f64(gks[li]), 1e-6)

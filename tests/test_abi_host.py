@@ -163,6 +163,12 @@ def _weights_kn(eps, ptr=256):
     return w
 
 
+def _weights_q8(ptr=256, dtype=torch.float32):
+    w = _weights(dtype=dtype)
+    w.map_scale = [ptr]
+    return w
+
+
 def _aligned_bytes(n, a=256):
     buf = torch.empty(n + a, dtype=torch.uint8)
     off = (-buf.data_ptr()) % a
@@ -190,6 +196,7 @@ def test_fill_validation_before_enqueue():
         (dict(w=_weights_kn(1e-6, ptr=0)), rf.RF_ERR_INVALID_ARG),   # null key-norm weights
         (dict(ws_=_aligned_bytes(256)), rf.RF_ERR_WORKSPACE),
         (dict(cache_=rf.cache_desc(4, 64, 512, rf.RF_LAYOUT_PAGED, torch.float32)), rf.RF_ERR_INVALID_ARG),
+        (dict(w=_weights_q8(ptr=256)), rf.RF_ERR_UNSUPPORTED),    # int8 maps need bf16 weights
     ]
     for kw, status in cases:
         with pytest.raises(rf.RidgeFillError) as e:
@@ -227,6 +234,24 @@ def test_pack_weights_validation_before_enqueue():
     with pytest.raises(rf.RidgeFillError) as e:    # an element type that is neither BF16 nor F32
         rf._check(rf._lib.rf_pack_weights(7, 256, 128, src.data_ptr(), 128, 0, dst.data_ptr(), None))
     assert e.value.status == rf.RF_ERR_UNSUPPORTED
+
+
+def test_quantize_map_validation_before_enqueue():
+    W = torch.zeros(256, 128)
+    q = torch.zeros(256 * 128, dtype=torch.int8)
+    s = torch.zeros(256)
+    cases = [
+        (dict(W=W[:100], q=q, scale=s), rf.RF_ERR_UNSUPPORTED),               # rows % 256
+        (dict(W=W[:, :100], q=q, scale=s), rf.RF_ERR_UNSUPPORTED),            # cols % 64
+        (dict(W=torch.zeros(256, 66)[:, :64], q=q, scale=s), rf.RF_ERR_INVALID_ARG),   # stride % 4
+        (dict(W=W, q=None, scale=s), rf.RF_ERR_INVALID_ARG),
+        (dict(W=W, q=q.data_ptr() + 8, scale=s), rf.RF_ERR_INVALID_ARG),     # misaligned codes
+    ]
+    for kw, status in cases:
+        with pytest.raises(rf.RidgeFillError) as e:
+            rf.rf_quantize_map(stream=0, **kw)
+        assert e.value.status == status, kw
+    rf.rf_quantize_map(W[:0], q, s, stream=0)   # no rows: nothing to do
 
 
 def test_relative_depth_sources_matches_the_oracle():
@@ -387,6 +412,7 @@ def test_fill_compose_validation_before_enqueue():
         (dict(out=_cweights(ptr=0)), rf.RF_ERR_INVALID_ARG),                       # null outputs
         (dict(ws=_aligned_bytes(256)), rf.RF_ERR_WORKSPACE),
         (dict(ws=_aligned_bytes(len(ws) + 512)[8:]), rf.RF_ERR_INVALID_ARG),      # misaligned workspace
+        (dict(w=_weights_q8(dtype=bf)), rf.RF_ERR_UNSUPPORTED),                   # int8 maps are not composed
     ]
     for kw, status in cases:
         args = dict(w=w, out=_cweights(), ws=ws)
