@@ -301,6 +301,8 @@ rf_status rf_cache_layout(const rf_cache_desc* desc, rf_cache_layout_t* out);
  * ------------------------------------------------------------------------------------- */
 rf_status rf_rope_table(double base, int32_t head_dim, int64_t n_pos, float* d_table,
                         void* stream);
+/* Workspace bytes a fill given no RoPE table uses for the table of n_tokens positions. */
+size_t rf_rope_workspace_bytes(int32_t head_dim, int64_t n_tokens);
 
 /* ---------------------------------------------------------------------------------------
  * Weight packing for the fill's matrix-core products (a layout change, no arithmetic).
@@ -365,7 +367,11 @@ rf_status rf_quantize_map(int64_t rows, int64_t cols, const float* d_W, int64_t 
  * k_cache[l], v_cache[l] : pools laid out per *cache (dtype must equal weights->dtype)
  * d_block_table : PAGED only, int32 [n_table_blocks]; entries outside [0, n_blocks) are
  *                 skipped (their tokens are not written)
- * d_rope : rf_rope_table() output with rope_len >= pos0 + t1 positions, head_dim of *cache
+ * d_rope : rf_rope_table() output with rope_len >= pos0 + t1 positions, head_dim of *cache;
+ *          or NULL: the table of positions pos0 + t0 .. pos0 + t1 - 1 is then built from
+ *          weights->rope_base (the same fp64 angles as rf_rope_table) at the end of d_ws, which
+ *          must hold rf_rope_workspace_bytes(head_dim, t1 - t0) bytes more (likewise for
+ *          rf_fill_composed, rf_fill_static and rf_fill_streamed; rope_len is then unused)
  * d_ws   : rf_fill_workspace_bytes(weights, t1 - t0) bytes, 256-B aligned
  * Supported: d % 256 == 0, head_dim in {64, 128}, (n_kv_heads*head_dim) % 256 == 0,
  * dtype F32 or BF16 (all of X, maps, projections and pools share it).
@@ -389,6 +395,7 @@ typedef struct {
     const float* const* k_norm;   /* NULL, or per layer fp32 [head_dim]: per-head key norm    */
     float k_norm_eps;             /* its epsilon (inside the root), when k_norm is given      */
     const float* const* map_scale; /* NULL, or per layer fp32 [d]: W_map are int8 codes       */
+    double rope_base;             /* RoPE base: used only when a fill is given no rope table   */
 } rf_fill_weights;
 
 size_t rf_fill_workspace_bytes(const rf_fill_weights* weights, int64_t max_rows);
@@ -443,6 +450,7 @@ typedef struct {
     const float* const* c_v;
     const float* const* k_norm;   /* NULL, or per layer fp32 [head_dim] (as for rf_fill)        */
     float k_norm_eps;
+    double rope_base;             /* RoPE base: used only when a fill is given no rope table   */
 } rf_fill_composed_weights;
 
 size_t rf_fill_compose_workspace_bytes(const rf_fill_weights* weights);
@@ -471,7 +479,8 @@ rf_status rf_fill_composed(const rf_fill_composed_weights* weights, int32_t n_la
  * Computes exactly what rf_fill computes (the same kernels, bit-identical caches) with its
  * workspace in a static device buffer of RF_FILL_STATIC_SCRATCH_MB MiB that the library holds
  * on every GPU it runs on until the process ends; the call itself allocates nothing.  A call
- * whose one-layer workspace (rf_fill_workspace_bytes(weights, t1 - t0)) exceeds the buffer is
+ * whose one-layer workspace (rf_fill_workspace_bytes(weights, t1 - t0), plus
+ * rf_rope_workspace_bytes(head_dim, t1 - t0) without a rope table) exceeds the buffer is
  * refused with RF_ERR_UNSUPPORTED and nothing enqueued: fill such a range in several calls.
  * The buffer is shared by every call on one GPU and keeps the last call's contents (nothing
  * in it needs to start at zero); calls that overlap on one GPU (different streams, different

@@ -66,14 +66,15 @@ class rf_fill_weights(C.Structure):
     _fields_ = [("d", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("rms_eps", C.c_float),
                 ("dtype", C.c_int), ("W_map", C.POINTER(C.c_void_p)), ("b_map", C.POINTER(C.c_void_p)),
                 ("gamma", C.POINTER(C.c_void_p)), ("W_k", C.POINTER(C.c_void_p)), ("W_v", C.POINTER(C.c_void_p)),
-                ("k_norm", C.POINTER(C.c_void_p)), ("k_norm_eps", C.c_float), ("map_scale", C.POINTER(C.c_void_p))]
+                ("k_norm", C.POINTER(C.c_void_p)), ("k_norm_eps", C.c_float), ("map_scale", C.POINTER(C.c_void_p)),
+                ("rope_base", C.c_double)]
 
 
 class rf_fill_composed_weights(C.Structure):
     _fields_ = [("d", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("rms_eps", C.c_float),
                 ("T", C.POINTER(C.c_void_p)), ("q", C.POINTER(C.c_void_p)), ("M_k", C.POINTER(C.c_void_p)),
                 ("M_v", C.POINTER(C.c_void_p)), ("c_k", C.POINTER(C.c_void_p)), ("c_v", C.POINTER(C.c_void_p)),
-                ("k_norm", C.POINTER(C.c_void_p)), ("k_norm_eps", C.c_float)]
+                ("k_norm", C.POINTER(C.c_void_p)), ("k_norm_eps", C.c_float), ("rope_base", C.c_double)]
 
 
 class rf_gdn_desc(C.Structure):
@@ -113,6 +114,7 @@ _sig = {
     "rf_rope_table": (C.c_int, [C.c_double, C.c_int32, C.c_int64, _P, _P]),
     "rf_pack_weights": (C.c_int, [C.c_int, C.c_int64, C.c_int64, _P, C.c_int64, C.c_int32, _P, _P]),
     "rf_quantize_map": (C.c_int, [C.c_int64, C.c_int64, _P, C.c_int64, _P, _P, _P]),
+    "rf_rope_workspace_bytes": (C.c_size_t, [C.c_int32, C.c_int64]),
     "rf_fill_workspace_bytes": (C.c_size_t, [C.POINTER(rf_fill_weights), C.c_int64]),
     "rf_fill": (C.c_int, [C.POINTER(rf_fill_weights), C.c_int32, _P, C.c_int64, C.c_int64, C.c_int64, C.c_int64,
                           C.POINTER(rf_cache_desc), C.POINTER(_P), C.POINTER(_P), _P, C.c_int64, _P, C.c_int64,
@@ -302,6 +304,10 @@ def rf_pack_weights(W, dst, rope_head_dim: int = 0, stream=None):
                                 _stream(stream)))
 
 
+def rf_rope_workspace_bytes(head_dim: int, n_tokens: int) -> int:
+    return int(_lib.rf_rope_workspace_bytes(head_dim, n_tokens))
+
+
 def rf_quantize_map(W, q, scale, stream=None):
     """W: [rows, >=cols] fp32 map (row stride = ld); q: rows*cols int8 codes out (packed);
     scale: [rows] fp32 out."""
@@ -330,6 +336,7 @@ class FillWeights:
     k_norm: Optional[list] = None
     k_norm_eps: float = 1e-6
     map_scale: Optional[list] = None
+    rope_base: float = 0.0   # used only by fills given no RoPE table
 
     def _c(self):
         arrs = [_ptr_array(x) for x in (self.W_map, self.b_map, self.gamma, self.W_k, self.W_v)]
@@ -338,7 +345,7 @@ class FillWeights:
         w = rf_fill_weights(self.d, self.n_kv_heads, self.head_dim, self.rms_eps, _dtype_code(self.dtype),
                             *[C.cast(a, C.POINTER(_P)) for a in arrs],
                             C.cast(kn, C.POINTER(_P)) if kn is not None else C.POINTER(_P)(), self.k_norm_eps,
-                            C.cast(ms, C.POINTER(_P)) if ms is not None else C.POINTER(_P)())
+                            C.cast(ms, C.POINTER(_P)) if ms is not None else C.POINTER(_P)(), float(self.rope_base))
         return w, (arrs, kn, ms)
 
 
@@ -377,13 +384,15 @@ class ComposedFillWeights:
     c_v: list
     k_norm: Optional[list] = None
     k_norm_eps: float = 1e-6
+    rope_base: float = 0.0   # used only by fills given no RoPE table
 
     def _c(self):
         arrs = [_ptr_array(x) for x in (self.T, self.q, self.M_k, self.M_v, self.c_k, self.c_v)]
         kn = None if self.k_norm is None else _ptr_array(self.k_norm)
         w = rf_fill_composed_weights(self.d, self.n_kv_heads, self.head_dim, self.rms_eps,
                                      *[C.cast(a, C.POINTER(_P)) for a in arrs],
-                                     C.cast(kn, C.POINTER(_P)) if kn is not None else C.POINTER(_P)(), self.k_norm_eps)
+                                     C.cast(kn, C.POINTER(_P)) if kn is not None else C.POINTER(_P)(), self.k_norm_eps,
+                                     float(self.rope_base))
         return w, (arrs, kn)
 
 

@@ -875,14 +875,14 @@ __global__ __launch_bounds__(PackedAGemm::kThr) void k_fill_norm(NormArgs a) {
     }
 }
 
-__global__ void k_rope_table(double base, int32_t dh, int64_t n_pos, float* out) {
+__global__ void k_rope_table(double base, int32_t dh, int64_t p0, int64_t n_pos, float* out) {
     const int64_t half = dh / 2;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= n_pos * half) return;
     const int64_t p = idx / half;
     const int64_t i = idx % half;
     const double theta = pow(base, -2.0 * (double)i / (double)dh);
-    const double phi = (double)p * theta;
+    const double phi = (double)(p0 + p) * theta;   // row p holds position p0 + p
     out[2 * idx] = (float)cos(phi);
     out[2 * idx + 1] = (float)sin(phi);
 }
@@ -948,6 +948,12 @@ __global__ __launch_bounds__(256) void k_quantize_map(const float* __restrict__ 
         }
         *(u32x2*)(q + base + packed_col_part((int)c)) = u32x2{wd[0], wd[1]};
     }
+}
+
+// Bytes at the end of a fill's workspace that hold the RoPE table of a call's tokens when the
+// caller passes none.
+static size_t rope_ws_bytes(int32_t head_dim, int64_t n_tokens) {
+    return round_up((size_t)n_tokens * head_dim * sizeof(float), 256);
 }
 
 static size_t slot_bytes(const rf_fill_weights* w, int64_t rows) {
@@ -1170,8 +1176,13 @@ rf_status rf_rope_table(double base, int32_t head_dim, int64_t n_pos, float* d_t
     const int64_t n = n_pos * (head_dim / 2);
     if (n == 0) return RF_OK;
     hipLaunchKernelGGL(k_rope_table, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, (hipStream_t)stream,
-                       base, head_dim, n_pos, d_table);
+                       base, head_dim, (int64_t)0, n_pos, d_table);
     return check_launch("rf_rope_table");
+}
+
+size_t rf_rope_workspace_bytes(int32_t head_dim, int64_t n_tokens) {
+    if (head_dim <= 0 || n_tokens < 0) return 0;
+    return rope_ws_bytes(head_dim, n_tokens);
 }
 
 rf_status rf_pack_weights(rf_dtype dtype, int64_t rows, int64_t cols, const void* d_src, int64_t ld_src,
@@ -1224,6 +1235,29 @@ size_t rf_fill_workspace_bytes(const rf_fill_weights* w, int64_t max_rows) {
 namespace rf {
 // Host checks shared by rf_fill and rf_fill_streamed ("what" names the entry point).  Sets
 // *nothing_to_do for an empty request; ws_need is the workspace the launch needs.
+// The table a fill reads: the caller's (positions from 0), or -- with none given -- the table of
+// the call's positions pos0 + t0 .. pos0 + t1 - 1 built at the end of the workspace, which the
+// kernels then index from the call's first token (pos0 -> -t0); the workspace left for the rest
+// shrinks by the table.
+static rf_status prepare_rope(const float* d_rope, double base, int32_t head_dim, int64_t pos0, int64_t t0,
+                              int64_t t1, void* ws, size_t& ws_bytes, const float*& rope, int64_t& pos0_eff,
+                              hipStream_t stream) {
+    rope = d_rope;
+    pos0_eff = pos0;
+    if (d_rope) return RF_OK;
+    const size_t tb = rope_ws_bytes(head_dim, t1 - t0);
+    const size_t off = (ws_bytes - tb) / 256 * 256;
+    float* tab = (float*)((char*)ws + off);
+    ws_bytes = off;
+    const int64_t n = (t1 - t0) * (head_dim / 2);
+    if (n > 0)
+        hipLaunchKernelGGL(k_rope_table, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream, base, head_dim,
+                           pos0 + t0, t1 - t0, tab);
+    rope = tab;
+    pos0_eff = -t0;
+    return check_launch("rope table in the workspace");
+}
+
 static rf_status check_fill(const char* what, const rf_fill_weights* w, int32_t n_layers, const void* d_X,
                             int64_t ldx, int64_t t0, int64_t t1, int64_t pos0, const rf_cache_desc* cache,
                             void* const* k_cache, void* const* v_cache, const int32_t* d_block_table,
@@ -1252,8 +1286,10 @@ static rf_status check_fill(const char* what, const rf_fill_weights* w, int32_t 
         nothing_to_do = true;
         return RF_OK;
     }
-    RF_REQUIRE(d_X && w->W_map && w->b_map && w->gamma && w->W_k && w->W_v && k_cache && v_cache && d_rope && d_ws,
+    RF_REQUIRE(d_X && w->W_map && w->b_map && w->gamma && w->W_k && w->W_v && k_cache && v_cache && d_ws,
                RF_ERR_INVALID_ARG, fn + ": null pointer argument");
+    RF_REQUIRE(d_rope || (w->rope_base > 0 && isfinite(w->rope_base)), RF_ERR_INVALID_ARG,
+               fn + ": without a rope table the weights' rope_base must be finite and > 0");
     const size_t eb = elem_bytes(w->dtype);
     RF_REQUIRE(ldx >= w->d && (ldx * (int64_t)eb) % 16 == 0 && aligned(d_X, 16), RF_ERR_INVALID_ARG,
                fn + ": X rows must be >= d long, 16-byte aligned with a 16-byte multiple stride");
@@ -1275,7 +1311,7 @@ static rf_status check_fill(const char* what, const rf_fill_weights* w, int32_t 
     }
     RF_REQUIRE(aligned(d_rope, 16) && aligned(d_ws, 256), RF_ERR_INVALID_ARG,
                fn + ": rope table must be 16-byte and workspace 256-byte aligned");
-    RF_REQUIRE(pos0 + t1 <= rope_len, RF_ERR_INVALID_ARG, fn + ": rope table shorter than pos0 + t1");
+    if (d_rope) RF_REQUIRE(pos0 + t1 <= rope_len, RF_ERR_INVALID_ARG, fn + ": rope table shorter than pos0 + t1");
     if (cache->layout == RF_LAYOUT_PAGED) {
         RF_REQUIRE(d_block_table, RF_ERR_INVALID_ARG, fn + ": paged cache needs a block table");
         RF_REQUIRE(ceil_div(t1, cache->block_size) <= n_table_blocks, RF_ERR_INVALID_ARG,
@@ -1283,7 +1319,9 @@ static rf_status check_fill(const char* what, const rf_fill_weights* w, int32_t 
     } else {
         RF_REQUIRE(t1 <= cache->max_tokens, RF_ERR_INVALID_ARG, fn + ": t1 exceeds the cache's max_tokens");
     }
-    RF_REQUIRE(ws_bytes >= ws_need, RF_ERR_WORKSPACE, fn + ": workspace too small");
+    const size_t tab = d_rope ? 0 : rope_ws_bytes(w->head_dim, t1 - t0);
+    RF_REQUIRE(ws_bytes >= ws_need + tab, RF_ERR_WORKSPACE,
+               fn + (d_rope ? ": workspace too small" : ": workspace too small (with the rope table it builds)"));
     return RF_OK;
 }
 
@@ -1416,7 +1454,7 @@ rf_status rf_fill_composed(const rf_fill_composed_weights* w, int32_t n_layers, 
     rf_fill_weights fw{};
     fw.d = w->d; fw.n_kv_heads = w->n_kv_heads; fw.head_dim = w->head_dim; fw.rms_eps = w->rms_eps; fw.dtype = RF_BF16;
     fw.W_map = w->T; fw.b_map = w->q; fw.gamma = w->c_k; fw.W_k = w->M_k; fw.W_v = w->M_v;
-    fw.k_norm = w->k_norm; fw.k_norm_eps = w->k_norm_eps;
+    fw.k_norm = w->k_norm; fw.k_norm_eps = w->k_norm_eps; fw.rope_base = w->rope_base;
     rf_cache_layout_t L;
     bool none;
     const size_t need = (w->d > 0 && w->d % kFT == 0 && t1 >= t0) ? composed_slot_bytes(w, t1 - t0) : 0;
@@ -1427,8 +1465,13 @@ rf_status rf_fill_composed(const rf_fill_composed_weights* w, int32_t n_layers, 
     for (int l = 0; l < n_layers; ++l)
         RF_REQUIRE(w->c_v[l] && aligned(w->c_v[l], 16), RF_ERR_INVALID_ARG,
                    "rf_fill_composed: per-layer intercepts must be non-null and 16-byte aligned");
-    return launch_fill_composed(w, n_layers, d_X, ldx, t0, t1, pos0, cache, L, k_cache, v_cache, d_block_table,
-                                n_table_blocks, d_rope, d_ws, ws_bytes, (hipStream_t)stream);
+    size_t wsb = ws_bytes;
+    const float* rope = nullptr;
+    int64_t p0e = pos0;
+    st = prepare_rope(d_rope, w->rope_base, w->head_dim, pos0, t0, t1, d_ws, wsb, rope, p0e, (hipStream_t)stream);
+    if (st != RF_OK) return st;
+    return launch_fill_composed(w, n_layers, d_X, ldx, t0, t1, p0e, cache, L, k_cache, v_cache, d_block_table,
+                                n_table_blocks, rope, d_ws, wsb, (hipStream_t)stream);
 }
 
 size_t rf_fill_static_scratch_bytes(void) { return rf::kStaticScratchBytes; }
@@ -1439,8 +1482,9 @@ rf_status rf_fill_static(const rf_fill_weights* w, int32_t n_layers, const void*
                          const float* d_rope, int64_t rope_len, void* stream) {
     clear_error();
     const size_t need = (w && w->d > 0 && w->d % kFT == 0 && t1 >= t0) ? slot_bytes(w, t1 - t0) : 0;
-    RF_REQUIRE(need <= kStaticScratchBytes, RF_ERR_UNSUPPORTED,
-               "rf_fill_static: one layer of " + std::to_string(t1 - t0) + " rows needs " + std::to_string(need) +
+    const size_t tab = (w && !d_rope && w->head_dim > 0 && t1 >= t0) ? rope_ws_bytes(w->head_dim, t1 - t0) : 0;
+    RF_REQUIRE(need + tab <= kStaticScratchBytes, RF_ERR_UNSUPPORTED,
+               "rf_fill_static: one layer of " + std::to_string(t1 - t0) + " rows needs " + std::to_string(need + tab) +
                    " bytes of scratch; the static buffer holds " + std::to_string(kStaticScratchBytes) +
                    " (fill fewer rows per call)");
     rf_cache_layout_t L;
@@ -1455,11 +1499,16 @@ rf_status rf_fill_static(const rf_fill_weights* w, int32_t n_layers, const void*
     st = static_scratch(&ws);
     if (st != RF_OK) return st;
     hipStream_t s = (hipStream_t)stream;
+    size_t wsb = kStaticScratchBytes;
+    const float* rope = nullptr;
+    int64_t p0e = pos0;
+    st = prepare_rope(d_rope, w->rope_base, w->head_dim, pos0, t0, t1, ws, wsb, rope, p0e, s);
+    if (st != RF_OK) return st;
     if (w->dtype == RF_BF16)
-        return launch_fill<bf16_t>(w, n_layers, d_X, ldx, t0, t1, pos0, cache, L, k_cache, v_cache, d_block_table,
-                                   n_table_blocks, d_rope, ws, kStaticScratchBytes, s);
-    return launch_fill<float>(w, n_layers, d_X, ldx, t0, t1, pos0, cache, L, k_cache, v_cache, d_block_table,
-                              n_table_blocks, d_rope, ws, kStaticScratchBytes, s);
+        return launch_fill<bf16_t>(w, n_layers, d_X, ldx, t0, t1, p0e, cache, L, k_cache, v_cache, d_block_table,
+                                   n_table_blocks, rope, ws, wsb, s);
+    return launch_fill<float>(w, n_layers, d_X, ldx, t0, t1, p0e, cache, L, k_cache, v_cache, d_block_table,
+                              n_table_blocks, rope, ws, wsb, s);
 }
 
 rf_status rf_fill(const rf_fill_weights* w, int32_t n_layers, const void* d_X, int64_t ldx,
@@ -1475,11 +1524,16 @@ rf_status rf_fill(const rf_fill_weights* w, int32_t n_layers, const void* d_X, i
                                     d_block_table, n_table_blocks, d_rope, rope_len, d_ws, ws_bytes, need, L, none);
     if (st != RF_OK || none) return st;
     hipStream_t s = (hipStream_t)stream;
+    size_t wsb = ws_bytes;
+    const float* rope = nullptr;
+    int64_t p0e = pos0;
+    rf_status rs = prepare_rope(d_rope, w->rope_base, w->head_dim, pos0, t0, t1, d_ws, wsb, rope, p0e, s);
+    if (rs != RF_OK) return rs;
     if (w->dtype == RF_BF16)
-        return launch_fill<bf16_t>(w, n_layers, d_X, ldx, t0, t1, pos0, cache, L, k_cache, v_cache, d_block_table,
-                                   n_table_blocks, d_rope, d_ws, ws_bytes, s);
-    return launch_fill<float>(w, n_layers, d_X, ldx, t0, t1, pos0, cache, L, k_cache, v_cache, d_block_table,
-                              n_table_blocks, d_rope, d_ws, ws_bytes, s);
+        return launch_fill<bf16_t>(w, n_layers, d_X, ldx, t0, t1, p0e, cache, L, k_cache, v_cache, d_block_table,
+                                   n_table_blocks, rope, d_ws, wsb, s);
+    return launch_fill<float>(w, n_layers, d_X, ldx, t0, t1, p0e, cache, L, k_cache, v_cache, d_block_table,
+                              n_table_blocks, rope, d_ws, wsb, s);
 }
 
 size_t rf_fill_streamed_ring_bytes(const rf_fill_weights* w, int32_t ring_slots, int32_t layers_per_slot) {
@@ -1511,12 +1565,17 @@ rf_status rf_fill_streamed(const rf_fill_weights* w, int32_t n_layers, const voi
     RF_REQUIRE(ring_bytes >= rf_fill_streamed_ring_bytes(w, ring_slots, layers_per_slot), RF_ERR_WORKSPACE,
                "rf_fill_streamed: ring too small");
     hipStream_t s = (hipStream_t)stream, cs = (hipStream_t)copy_stream;
+    size_t wsb = ws_bytes;
+    const float* rope = nullptr;
+    int64_t p0e = pos0;
+    st = prepare_rope(d_rope, w->rope_base, w->head_dim, pos0, t0, t1, d_ws, wsb, rope, p0e, s);
+    if (st != RF_OK) return st;
     if (w->dtype == RF_BF16)
-        return launch_fill_streamed<bf16_t>(w, n_layers, d_X, ldx, t0, t1, pos0, cache, L, k_cache, v_cache,
-                                            d_block_table, n_table_blocks, d_rope, d_ws, ws_bytes, d_ring, ring_slots,
+        return launch_fill_streamed<bf16_t>(w, n_layers, d_X, ldx, t0, t1, p0e, cache, L, k_cache, v_cache,
+                                            d_block_table, n_table_blocks, rope, d_ws, wsb, d_ring, ring_slots,
                                             layers_per_slot, rpf, s, cs);
-    return launch_fill_streamed<float>(w, n_layers, d_X, ldx, t0, t1, pos0, cache, L, k_cache, v_cache,
-                                       d_block_table, n_table_blocks, d_rope, d_ws, ws_bytes, d_ring, ring_slots,
+    return launch_fill_streamed<float>(w, n_layers, d_X, ldx, t0, t1, p0e, cache, L, k_cache, v_cache,
+                                       d_block_table, n_table_blocks, rope, d_ws, wsb, d_ring, ring_slots,
                                        layers_per_slot, rpf, s, cs);
 }
 

@@ -301,7 +301,7 @@ def compose_weights(weights: FillWeights, stream=None, slots: int = 8) -> Compos
     ck = [torch.empty(kvw, dtype=torch.float32, device=dev) for _ in range(L)]
     cv = [torch.empty(kvw, dtype=torch.float32, device=dev) for _ in range(L)]
     out = ComposedFillWeights(d, weights.n_kv_heads, weights.head_dim, weights.rms_eps, T, q, Mk, Mv, ck, cv,
-                              weights.k_norm, weights.k_norm_eps)
+                              weights.k_norm, weights.k_norm_eps, weights.rope_base)
     ws = device_bytes(rf_fill_compose_workspace_bytes(weights) * max(1, min(slots, L)), dev)
     rf_fill_compose(weights, out, ws, stream)
     return out

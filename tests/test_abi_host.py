@@ -181,9 +181,17 @@ def test_fill_validation_before_enqueue():
     ws = _aligned_bytes(1 << 20)
     rope = torch.empty(512, 64)
 
-    def call(w=None, t0=0, t1=512, pos0=0, cache_=cache, rope_len=512, ws_=ws, n_layers=None):
+    def call(w=None, t0=0, t1=512, pos0=0, cache_=cache, rope_len=512, ws_=ws, n_layers=None, rope_=rope):
         w = w or _weights()
-        rf.rf_fill(w, X, t0, t1, pos0, cache_, [256], [256], None, rope, rope_len, ws_, None, n_layers=n_layers)
+        rf.rf_fill(w, X, t0, t1, pos0, cache_, [256], [256], None, rope_, rope_len, ws_, None, n_layers=n_layers)
+
+    def based(base):
+        w = _weights()
+        w.rope_base = base
+        return w
+
+    need = rf.rf_fill_workspace_bytes(_weights(), 512)
+    assert rf.rf_rope_workspace_bytes(64, 512) == 512 * 64 * 4
 
     cases = [
         (dict(t0=5, t1=4), rf.RF_ERR_INVALID_ARG),
@@ -197,6 +205,9 @@ def test_fill_validation_before_enqueue():
         (dict(ws_=_aligned_bytes(256)), rf.RF_ERR_WORKSPACE),
         (dict(cache_=rf.cache_desc(4, 64, 512, rf.RF_LAYOUT_PAGED, torch.float32)), rf.RF_ERR_INVALID_ARG),
         (dict(w=_weights_q8(ptr=256)), rf.RF_ERR_UNSUPPORTED),    # int8 maps need bf16 weights
+        (dict(rope_=None), rf.RF_ERR_INVALID_ARG),                 # no table and no rope_base
+        (dict(rope_=None, w=based(float("inf"))), rf.RF_ERR_INVALID_ARG),
+        (dict(rope_=None, w=based(1e4), ws_=_aligned_bytes(need)), rf.RF_ERR_WORKSPACE),   # no room for the table
     ]
     for kw, status in cases:
         with pytest.raises(rf.RidgeFillError) as e:

@@ -249,3 +249,65 @@ def test_fill_streamed_long_prompt_in_steps():
         for a, b in ((outs[0].k[li], outs[1].k[li]), (outs[0].v[li], outs[1].v[li])):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), li
     log("[fill] streamed in steps of 256 tokens: bit-identical to the resident fill")
+
+
+def test_fill_without_rope_table_builds_it_in_the_workspace():
+    # d_rope NULL: the library builds the table of the call's positions at the end of the
+    # workspace (from the weights' rope_base, the same fp64 angles) and the caches equal those
+    # of the caller's table bit for bit: rf_fill on both K/V kernels, rf_fill_static,
+    # rf_fill_composed and rf_fill_streamed in token steps, at t0 > 0 and pos0 > 0
+    import dataclasses
+
+    import linear_kv_cache_amd as rf
+    from linear_kv_cache_amd.runner import (ComposedFiller, Filler, StreamedFiller, alloc_cache, device_bytes,
+                                            fill_weights, pinned_copy)
+    for cfg in (SMALL_BF16, WIDE_BF16):
+        t0, t1, pos0 = 37, 737, 1234
+        layers = cfg.filled_layers
+        ws_ = [synth.layer_weights(cfg, l, device="cuda") for l in layers]
+        fw = fill_weights(cfg.d, cfg.n_kv_heads, cfg.head_dim, cfg.rms_eps, cfg.torch_dtype, [w.W_map for w in ws_],
+                          [w.b_map for w in ws_], [w.gamma for w in ws_], [w.W_k for w in ws_], [w.W_v for w in ws_])
+        fw.rope_base = cfg.rope_base
+        T = max(t1, cfg.prompt_tokens)
+        X = synth.hidden_states(cfg, t1 - t0, "prompt", device="cuda")
+        rope_extra = rf.rf_rope_workspace_bytes(cfg.head_dim, t1 - t0)
+        pairs = []
+        # rf_fill
+        f = Filler(fw, cfg.rope_base, pos0 + T, t1 - t0, "cuda")
+        wsn = device_bytes(f.ws.numel() + rope_extra, "cuda")
+        for rope in (f.rope, None):
+            c = alloc_cache(len(layers), cfg.n_kv_heads, cfg.head_dim, T, cfg.torch_dtype, "cuda")
+            rf.rf_fill(fw, X, t0, t1, pos0, c.desc, c.k, c.v, None, rope, f.rope_len, f.ws if rope is not None else wsn)
+            pairs.append(("rf_fill", c))
+        # rf_fill_static
+        for rope in (f.rope, None):
+            c = alloc_cache(len(layers), cfg.n_kv_heads, cfg.head_dim, T, cfg.torch_dtype, "cuda")
+            rf.rf_fill_static(fw, X, t0, t1, pos0, c.desc, c.k, c.v, None, rope, f.rope_len)
+            pairs.append(("rf_fill_static", c))
+        # rf_fill_composed
+        cf = ComposedFiller(fw, cfg.rope_base, pos0 + T, t1 - t0, "cuda")
+        wsc = device_bytes(cf.ws.numel() + rope_extra, "cuda")
+        for rope in (cf.rope, None):
+            c = alloc_cache(len(layers), cfg.n_kv_heads, cfg.head_dim, T, cfg.torch_dtype, "cuda")
+            rf.rf_fill_composed(cf.w, X, t0, t1, pos0, c.desc, c.k, c.v, None, rope, cf.rope_len,
+                                cf.ws if rope is not None else wsc)
+            pairs.append(("rf_fill_composed", c))
+        # rf_fill_streamed in steps of 256 tokens
+        sw = dataclasses.replace(fw, W_map=[pinned_copy(W.cpu()) for W in fw.W_map])
+        sf = StreamedFiller(sw, cfg.rope_base, pos0 + T, t1 - t0, "cuda", ring_slots=2, layers_per_slot=1,
+                            rows_per_fill=256)
+        wss = device_bytes(sf.ws.numel() + rope_extra, "cuda")
+        for rope in (sf.rope, None):
+            c = alloc_cache(len(layers), cfg.n_kv_heads, cfg.head_dim, T, cfg.torch_dtype, "cuda")
+            rf.rf_fill_streamed(sw, X, t0, t1, pos0, c.desc, c.k, c.v, None, rope, sf.rope_len,
+                                sf.ws if rope is not None else wss, sf.ring, sf.ring_slots, sf.layers_per_slot,
+                                torch.cuda.current_stream(), sf.copy_stream, rows_per_fill=256)
+            pairs.append(("rf_fill_streamed", c))
+        torch.cuda.synchronize()
+        for i in range(0, len(pairs), 2):
+            (name, a), (_, b) = pairs[i], pairs[i + 1]
+            for li in range(len(layers)):
+                for x, y in ((a.k[li], b.k[li]), (a.v[li], b.v[li])):
+                    assert torch.equal(x.view(torch.int16), y.view(torch.int16)), (cfg.name, name, li)
+        log(f"[fill] {cfg.name}: no rope table given -> built in the workspace, bit-identical (fill, static, "
+            f"composed, streamed)")
