@@ -106,3 +106,19 @@ def test_int8_streamed_and_static_equal_resident():
             for a, b in ((caches[0].k[li], c.k[li]), (caches[0].v[li], c.v[li])):
                 assert torch.equal(a.view(torch.int16), b.view(torch.int16)), (kind, li)
     log("[quant] int8 maps: streamed and static fills bit-identical to the resident fill")
+
+
+@pytest.mark.timeout(300)
+def test_fill_int8_maps_llama8b_shaped_full_sampled():
+    # the benchmark's launch configuration (16 layers x 16384 tokens, d = 4096), sampled rows:
+    # every 256-token tile edge and seeded random rows
+    cfg = synth.C2
+    rng = np.random.default_rng(31)
+    edges = {0, 1, cfg.fill_t1 - 1, cfg.fill_t1 - 2}
+    for b in range(256, cfg.fill_t1, 256):
+        edges.update({b - 1, b})
+    sample = sorted(edges | set(rng.integers(0, cfg.fill_t1, 24).tolist()))
+    res = run_fill_case(FillCase(cfg, 0, cfg.fill_t1, maps="law", sample=sample, gen_device="cuda", int8_maps=True))
+    log(f"[quant] full-size int8 fill: max_err={res['max_err']:.3e} (tol {res['tol']})")
+    assert res["finite"] and res["sentinel_ok"]
+    assert res["max_err"] <= res["tol"], res
