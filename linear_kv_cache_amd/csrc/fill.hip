@@ -11,7 +11,12 @@
 // MFMA operands: A = weight rows (features), B = token rows, so each lane's accumulators
 // hold 4 consecutive features of one token.  bf16 weights arrive packed in fragment order
 // (rf_pack_weights) and go straight to registers; K/V rows are packed in rotate-half pairs so
-// a head's RoPE partners sit in the same lane and register, one block apart.
+// a head's RoPE partners sit in the same lane and register, one block apart.  The map may be
+// weight-only int8 codes (rf_quantize_map), widened to bf16 in registers.  The bf16 fills run
+// the K/V product on 512-feature x 128-token tiles (k_fill_kv4) when the K and V halves are
+// whole such tiles, on 256 x 256 tiles (k_fill_kv) otherwise.  The composed fill
+// (rf_fill_composed) replaces the map launch by the quadratic form of the RMS (k_fill_norm)
+// and runs the K/V product on the prompt states with the composed weights.
 #include <math.h>
 
 #include <mutex>
