@@ -180,3 +180,50 @@ def test_gdn_pins_catch_mistakes():
 
     for bad in (decay_after_write, erase_without_beta):
         assert not _gdn_pins_hold(bad)
+
+
+def _quant_pins_hold(qr):
+    # the hand-worked grid and tie rows of tests/test_oracle_quant.py, and the half-step bound
+    s0 = np.float32(2.0 ** -7)
+    grid = s0 * np.array([[127, -64, 3, 0, -127, 1]], dtype=np.float32)
+    ties = s0 * np.array([[127, 2.5, 3.5, -2.5, -0.5, 0.5, 1.5, -126.5]], dtype=np.float32)
+    neg = np.zeros((1, 5), dtype=np.float32)
+    neg[0, 3] = -0.75
+    q1, s1 = qr(grid)
+    q2, _ = qr(ties)
+    q3, _ = qr(neg)
+    ok = (np.array_equal(q1, [[127, -64, 3, 0, -127, 1]]) and float(s1[0]) == float(s0)
+          and np.array_equal(q2, [[127, 2, 4, -2, 0, 0, 2, -126]]) and np.array_equal(q3, [[0, 0, 0, -127, 0]]))
+    rng = np.random.default_rng(11)
+    W = rng.standard_normal((8, 64)).astype(np.float32)
+    q, s = qr(W)
+    err = np.abs(np.asarray(s, np.float64)[:, None] * np.asarray(q, np.float64) - W)
+    return bool(ok and np.all(err <= np.asarray(s, np.float64)[:, None] * (0.5 + 1e-5)))
+
+
+def test_quantiser_pins_catch_mistakes():
+    assert _quant_pins_hold(oracle.quantize_rows)
+
+    def truncates(W):
+        W = np.asarray(W, np.float32)
+        s = (np.max(np.abs(W), axis=1) / np.float32(127)).astype(np.float32)
+        return np.trunc(W / np.where(s > 0, s, 1)[:, None]).astype(np.int8), s
+
+    def ties_away(W):
+        W = np.asarray(W, np.float32)
+        s = (np.max(np.abs(W), axis=1) / np.float32(127)).astype(np.float32)
+        x = W / np.where(s > 0, s, 1)[:, None]
+        return (np.sign(x) * np.floor(np.abs(x) + 0.5)).astype(np.int8), s
+
+    def scale_by_128(W):
+        W = np.asarray(W, np.float32)
+        s = (np.max(np.abs(W), axis=1) / np.float32(128)).astype(np.float32)
+        return np.clip(np.rint(W / np.where(s > 0, s, 1)[:, None]), -127, 127).astype(np.int8), s
+
+    def signed_maximum(W):
+        W = np.asarray(W, np.float32)
+        s = np.abs(np.max(W, axis=1) / np.float32(127)).astype(np.float32)
+        return np.clip(np.rint(W / np.where(s > 0, s, 1)[:, None]), -127, 127).astype(np.int8), s
+
+    for bad in (truncates, ties_away, scale_by_128, signed_maximum):
+        assert not _quant_pins_hold(bad), bad.__name__
