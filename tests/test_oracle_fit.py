@@ -256,7 +256,7 @@ def test_stationarity_residual_hand_worked_and_limits():
     X = rng.standard_normal((200, 6))
     Y = X @ rng.standard_normal((6, 4)) + 0.1 * rng.standard_normal((200, 4))
     assert oracle.stationarity_residual(X, Y, np.zeros((6, 4)), 0.5) == 1.0
-    # the fitted map is stationary (the survey's pin: <= 1e-12)
+    # the fitted map is stationary to fp64 rounding (<= 1e-12)
     W, _ = oracle.fit(X, Y, 0.5)
     assert oracle.stationarity_residual(X, Y, W, 0.5) <= 1e-12
     # one entry moved by delta: the residual is delta times the largest entry of that row of A
