@@ -42,7 +42,7 @@ extern "C" {
 typedef enum {
     RF_OK = 0,
     RF_ERR_INVALID_ARG = 1,   /* a null pointer, bad size, bad range or bad stride        */
-    RF_ERR_UNSUPPORTED = 2,   /* a valid request this build does not implement (shape)    */
+    RF_ERR_UNSUPPORTED = 2,   /* a valid request the library does not implement (shape)  */
     RF_ERR_HIP = 3,           /* a HIP runtime call or kernel launch failed               */
     RF_ERR_WORKSPACE = 4,     /* the workspace passed is smaller than the size query says */
     RF_ERR_NOT_SPD = 5        /* a regularised Gram is not positive definite (reported by
