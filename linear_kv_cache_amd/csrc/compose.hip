@@ -146,13 +146,26 @@ __global__ __launch_bounds__(PipeGemm::kThr) void k_compose_gemm(ComposeArgs a) 
     const bf16_t* A2 = a.A2[l];
     G gm;
     if (v < a.n_t) {
-        // T tile (I, J), J >= I: acc[j][i] = (W^T W)[j][i]; rows j are A, rows i are B
-        int I = 0, rem = v;
-        while (rem >= a.nf - I) {
-            rem -= a.nf - I;
-            ++I;
+        // T tile (I, J), J >= I: acc[j][i] = (W^T W)[j][i]; rows j are A, rows i are B.
+        // Row tiles I in groups of 4; within a group, columns J in order and the group's rows
+        // with I <= J fastest, so the 32 tiles an XCD runs at once read about 4 + 8 strips of W
+        // instead of 2 + 16
+        int I = 0, J = 0, rem = v;
+        for (int i0 = 0; i0 < a.nf; i0 += 4) {
+            const int gs = a.nf - i0 < 4 ? a.nf - i0 : 4;
+            int size = 0;
+            for (int j = i0; j < a.nf; ++j) size += (j - i0 + 1) < gs ? (j - i0 + 1) : gs;
+            if (rem < size) {
+                for (J = i0;; ++J) {
+                    const int c = (J - i0 + 1) < gs ? (J - i0 + 1) : gs;
+                    if (rem < c) break;
+                    rem -= c;
+                }
+                I = i0 + rem;
+                break;
+            }
+            rem -= size;
         }
-        const int J = I + rem;
         gm.run(lds, PipeOperand{A2 + (int64_t)J * kCT * 2 * d, 2 * d, kCT},
                PipeOperand{A2 + (int64_t)I * kCT * 2 * d, 2 * d, kCT}, (int)(d / G::BK));
 #pragma unroll
@@ -177,8 +190,9 @@ __global__ __launch_bounds__(PipeGemm::kThr) void k_compose_gemm(ComposeArgs a) 
         }
     } else {
         // M tile: acc[i][p] = sum_o W[o][i] (W_kv diag(gamma))[p][o] over K = 2d (hi, lo)
-        const int w = v - a.n_t;
-        const int I = w % a.nf, F = w / a.nf;
+        // in groups of 4 row tiles F of W_kv, each against all d / 256 column tiles I of W
+        int F, I;
+        grouped_tile(v - a.n_t, 2 * a.kvw / kCT, a.nf, 4, F, I);
         gm.run(lds, PipeOperand{A2 + (int64_t)I * kCT * 2 * d, 2 * d, kCT},
                PipeOperand{a.B2[l] + (int64_t)F * kCT * 2 * d, 2 * d, kCT}, (int)(2 * d / G::BK));
 #pragma unroll
