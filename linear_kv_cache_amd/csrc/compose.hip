@@ -76,23 +76,25 @@ __global__ __launch_bounds__(256) void k_unpack_transpose(PrepArgs pa, int64_t d
 
 __device__ inline float bf16_to_f32(uint32_t bits16) { return __builtin_bit_cast(float, bits16 << 16); }
 
-// One work-group per packed row p of [W_k; W_v]: B2[p] = [hi | lo] of the row scaled by gamma
-// (the product rounded to fp32, then split into two bf16 parts), and the row's intercept
-// c = sum_o W[p][o] gamma_o b_o (fp64, fixed order) at its source row's index.
+// One wave per packed row p of [W_k; W_v] (4 rows per work-group): B2[p] = [hi | lo] of the row
+// scaled by gamma (the product rounded to fp32, then split into two bf16 parts), and the row's
+// intercept c = sum_o W[p][o] gamma_o b_o (fp64: each lane's 8-column chunks in order, then a
+// fixed shuffle tree) at its source row's index.
 __global__ __launch_bounds__(256) void k_kv_split(PrepArgs pa, int64_t d, int kvw, int hd) {
     const int g = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (p >= 2 * kvw) return;
     const bf16_t *Wk = pa.Wk[g], *Wv = pa.Wv[g];
     const float *gamma = pa.gamma[g], *b = pa.b[g];
     bf16_t* B2 = pa.B2[g];
     float *ck = pa.ck[g], *cv = pa.cv[g];
-    __shared__ double red[256];
-    const int p = blockIdx.x;
     const bool is_k = p < kvw;
     const int pr = is_k ? p : p - kvw;
     const bf16_t* src = is_k ? Wk : Wv;
     bf16_t* row = B2 + (int64_t)p * 2 * d;
     double acc = 0.0;
-    for (int64_t o = 8 * threadIdx.x; o < d; o += 8 * 256) {
+    for (int64_t o = 8 * lane; o < d; o += 8 * 64) {
         const u32x4 v = *(const u32x4*)(src + packed_index(pr, (int)o, d));
         uint32_t hi[4], lo[4];
 #pragma unroll
@@ -111,15 +113,10 @@ __global__ __launch_bounds__(256) void k_kv_split(PrepArgs pa, int64_t d, int kv
         *(u32x4*)(row + o) = u32x4{hi[0], hi[1], hi[2], hi[3]};
         *(u32x4*)(row + d + o) = u32x4{lo[0], lo[1], lo[2], lo[3]};
     }
-    red[threadIdx.x] = acc;
-    __syncthreads();
-    for (int h = 128; h > 0; h >>= 1) {
-        if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) {
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) {
         const int f = (pr / kCT) * kCT + packed_source_row(pr % kCT, hd);
-        (is_k ? ck : cv)[f] = (float)red[0];
+        (is_k ? ck : cv)[f] = (float)acc;
     }
 }
 
@@ -234,9 +231,17 @@ __global__ __launch_bounds__(256) void k_qvec(PrepArgs pa, int64_t d) {
     }
     const int lane = threadIdx.x & 63;
     const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const uint16_t* row = (const uint16_t*)(A2 + i * 2 * d);
+    const bf16_t* row = A2 + i * 2 * d;
     double s = 0.0;
-    for (int64_t o = lane; o < d; o += 64) s += (double)bf16_to_f32(row[o]) * (double)b[o];
+    // 8 consecutive columns per lane and load
+    for (int64_t o = 8 * lane; o < d; o += 8 * 64) {
+        const u32x4 v = *(const u32x4*)(row + o);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            s += (double)bf16_to_f32(v[k] & 0xffffu) * (double)b[o + 2 * k];
+            s += (double)bf16_to_f32(v[k] >> 16) * (double)b[o + 2 * k + 1];
+        }
+    }
     for (int off = 32; off > 0; off >>= 1) {
         const double t = __shfl_xor(s, off);
         s += t;
@@ -316,7 +321,7 @@ rf_status rf_fill_compose(const rf_fill_weights* w, int32_t n_layers, void* cons
         hipLaunchKernelGGL(k_unpack_transpose, dim3((unsigned)(d / 64), (unsigned)(d / 64), (unsigned)gsz), dim3(256),
                            0, s, pa, d);
         RF_TRY_LAUNCH("rf_fill_compose: transpose");
-        hipLaunchKernelGGL(k_kv_split, dim3((unsigned)(2 * kvw), (unsigned)gsz), dim3(256), 0, s, pa, d, (int)kvw,
+        hipLaunchKernelGGL(k_kv_split, dim3((unsigned)ceil_div(2 * kvw, 4), (unsigned)gsz), dim3(256), 0, s, pa, d, (int)kvw,
                            w->head_dim);
         RF_TRY_LAUNCH("rf_fill_compose: scaled projections");
         hipLaunchKernelGGL(k_qvec, dim3((unsigned)(d / 4 + 1), (unsigned)gsz), dim3(256), 0, s, pa, d);
