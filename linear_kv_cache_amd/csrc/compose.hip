@@ -47,7 +47,7 @@ struct PrepArgs {
     float* q[kComposeGroup];
 };
 
-// A2 = [W^T | W^T] from the packed map, one 64 x 64 block per work-group through LDS.
+// A2 = W^T from the packed map, one 64 x 64 block per work-group through LDS.
 __global__ __launch_bounds__(256) void k_unpack_transpose(PrepArgs pa, int64_t d) {
     const bf16_t* Wp = pa.W[blockIdx.z];
     bf16_t* A2 = pa.A2[blockIdx.z];
@@ -68,9 +68,7 @@ __global__ __launch_bounds__(256) void k_unpack_transpose(PrepArgs pa, int64_t d
         u32x4 v;
 #pragma unroll
         for (int k = 0; k < 4; ++k) v[k] = (uint32_t)tile[oc + 2 * k][il] | ((uint32_t)tile[oc + 2 * k + 1][il] << 16);
-        bf16_t* row = A2 + (ib * 64 + il) * 2 * d + ob * 64 + oc;
-        *(u32x4*)row = v;
-        *(u32x4*)(row + d) = v;
+        *(u32x4*)(A2 + (ib * 64 + il) * d + ob * 64 + oc) = v;
     }
 }
 
@@ -126,7 +124,7 @@ struct ComposeArgs {
     int32_t nf;            // d / 256
     int32_t n_t;           // tiles of T per layer: nf (nf + 1) / 2
     int32_t n_tiles;       // tiles per layer: n_t + nf * 2 kvw / 256
-    const bf16_t* A2[kComposeGroup];   // [d][2d] per layer
+    const bf16_t* A2[kComposeGroup];   // [d][d] per layer: W^T
     const bf16_t* B2[kComposeGroup];   // [2 kvw][2d] per layer
     bf16_t* T[kComposeGroup];
     float* gdiag[kComposeGroup];       // q + d: the diagonal of W^T W
@@ -163,8 +161,8 @@ __global__ __launch_bounds__(PipeGemm::kThr) void k_compose_gemm(ComposeArgs a) 
             }
             rem -= size;
         }
-        gm.run(lds, PipeOperand{A2 + (int64_t)J * kCT * 2 * d, 2 * d, kCT},
-               PipeOperand{A2 + (int64_t)I * kCT * 2 * d, 2 * d, kCT}, (int)(d / G::BK));
+        gm.run(lds, PipeOperand{A2 + (int64_t)J * kCT * d, d, kCT}, PipeOperand{A2 + (int64_t)I * kCT * d, d, kCT},
+               (int)(d / G::BK));
 #pragma unroll
         for (int jb = 0; jb < G::SN; ++jb) {
             const int64_t i = (int64_t)I * kCT + G::col_of(jb);
@@ -190,8 +188,9 @@ __global__ __launch_bounds__(PipeGemm::kThr) void k_compose_gemm(ComposeArgs a) 
         // in groups of 4 row tiles F of W_kv, each against all d / 256 column tiles I of W
         int F, I;
         grouped_tile(v - a.n_t, 2 * a.kvw / kCT, a.nf, 4, F, I);
-        gm.run(lds, PipeOperand{A2 + (int64_t)I * kCT * 2 * d, 2 * d, kCT},
-               PipeOperand{a.B2[l] + (int64_t)F * kCT * 2 * d, 2 * d, kCT}, (int)(2 * d / G::BK));
+        // K = 2d: the hi and lo halves of B2 against the same W^T rows (A's k-steps fold back)
+        gm.run(lds, PipeOperand{A2 + (int64_t)I * kCT * d, d, kCT},
+               PipeOperand{a.B2[l] + (int64_t)F * kCT * 2 * d, 2 * d, kCT}, (int)(2 * d / G::BK), (int)(d / G::BK));
 #pragma unroll
         for (int jb = 0; jb < G::SN; ++jb) {
             const int p = F * kCT + G::col_of(jb);
@@ -231,7 +230,7 @@ __global__ __launch_bounds__(256) void k_qvec(PrepArgs pa, int64_t d) {
     }
     const int lane = threadIdx.x & 63;
     const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const bf16_t* row = A2 + i * 2 * d;
+    const bf16_t* row = A2 + i * d;
     double s = 0.0;
     // 8 consecutive columns per lane and load
     for (int64_t o = 8 * lane; o < d; o += 8 * 64) {
@@ -251,7 +250,7 @@ __global__ __launch_bounds__(256) void k_qvec(PrepArgs pa, int64_t d) {
 
 // One layer slot of the workspace: A2, then B2.
 static size_t compose_ws(int64_t d, int64_t kvw, size_t* off_b2) {
-    const size_t a2 = round_up((size_t)d * 2 * d * 2, 256);
+    const size_t a2 = round_up((size_t)d * d * 2, 256);
     if (off_b2) *off_b2 = a2;
     return a2 + round_up((size_t)2 * kvw * 2 * d * 2, 256);
 }

@@ -129,8 +129,10 @@ struct PipeGemmW {
     };
 
     // Full K loop over ``nk`` k-steps; nk must be even (the loop is unrolled by two so that
-    // the two register sets are addressed statically).
-    __device__ inline void run(char* lds, const PipeOperand& A, const PipeOperand& B, int nk) {
+    // the two register sets are addressed statically).  With a_fold > 0 (K-contiguous operands),
+    // k-step kt of A is read from step kt - a_fold once kt reaches a_fold: A's first a_fold
+    // steps serve twice.
+    __device__ inline void run(char* lds, const PipeOperand& A, const PipeOperand& B, int nk, int a_fold = 0) {
         const int t = threadIdx.x;
         const int lane = t & 63;
         const int wave = t >> 6;
@@ -167,7 +169,8 @@ struct PipeGemmW {
         // k-step offsets: K-major steps move along the row (buffer offset), M-major steps move
         // down 64 rows, kept in the range-checked vector offset so rows past the end read zero
         auto gload_a = [&](Regs& g, int kt) {
-            const int kc = kt < nk ? kt : nk - 1;
+            int kc = kt < nk ? kt : nk - 1;
+            if (a_fold > 0 && kc >= a_fold) kc -= a_fold;
             const int kb = MMAJOR ? 0 : kc * ROWB;
             const int kv = MMAJOR ? (int)(kc * 64 * A.ld * 2) : 0;
 #pragma unroll
