@@ -433,7 +433,7 @@ rf_status rf_fill(const rf_fill_weights* weights, int32_t n_layers,
  * Products of bf16 weights accumulate in fp32 (W_k diag(gamma) enters in two bf16 parts, so
  * its product with W is exact to fp32 before the one rounding of M to bf16); the vectors are
  * summed in fp64.  d_ws: a multiple k >= 1 of rf_fill_compose_workspace_bytes(weights) bytes
- * (one layer slot: 4 d^2 + 8 H_kv d_h d bytes), 256-B aligned; the products of up to
+ * (one layer slot: 2 d^2 + 8 H_kv d_h d bytes), 256-B aligned; the products of up to
  * min(k, 32) layers share one launch.
  * Supported: BF16 weights, d % 256 == 0, as for rf_fill.
  * ------------------------------------------------------------------------------------- */

@@ -412,7 +412,8 @@ def _cweights(d=256, H=4, dh=64, n=1, ptr=256, c_v=None):
 def test_fill_compose_validation_before_enqueue():
     bf = torch.bfloat16
     w = _weights(dtype=bf)
-    assert rf.rf_fill_compose_workspace_bytes(w) == 4 * 256 * 256 + 8 * 256 * 256
+    # one layer slot: W^T [d][d] bf16, then [W_kv diag(gamma)] as [hi | lo], [2 kvw][2d] bf16 (d = kvw = 256)
+    assert rf.rf_fill_compose_workspace_bytes(w) == 2 * 256 * 256 + 8 * 256 * 256
     ws = _aligned_bytes(rf.rf_fill_compose_workspace_bytes(w))
     cases = [
         (dict(w=_weights(dtype=torch.float32)), rf.RF_ERR_UNSUPPORTED),           # BF16 only
